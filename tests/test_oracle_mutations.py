@@ -1,0 +1,125 @@
+"""Each test plants one plausible mistake in the oracle (CPU only) and checks
+that at least one pin of tests/test_oracle_pins.py then fails."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import sks_oracle as orc
+from tests import test_oracle_pins as pins
+from tests.golden_util import load_examples
+
+EXAMPLES = load_examples()
+
+
+def golden_all():
+    for ex in EXAMPLES:
+        pins.test_golden_worked_examples(ex)
+
+
+def dense_all():
+    for w, k in [(64, 10 ** 6), (1000, 5), (0, 1000)]:
+        pins.test_dense_equivalence_against_sdpa(w, k)
+
+
+def expect_caught(monkeypatch, name, fake, *checks):
+    monkeypatch.setattr(orc, name, fake)
+    caught = 0
+    for chk in checks:
+        try:
+            chk()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake in {name}"
+
+
+def test_caught_tie_break_by_higher_index(monkeypatch):
+    def bad(sc, k):
+        sc = np.asarray(sc, np.int64)
+        order = np.lexsort((-np.arange(sc.shape[0]), -sc))
+        return np.sort(order[:min(k, sc.shape[0])])
+    expect_caught(monkeypatch, "select_topk", bad, golden_all,
+                  lambda: pins.test_topk_brute_force_with_dense_ties(50, 10))
+
+
+def test_caught_smallest_instead_of_largest(monkeypatch):
+    def bad(sc, k):
+        sc = np.asarray(sc, np.int64)
+        order = np.lexsort((np.arange(sc.shape[0]), sc))
+        return np.sort(order[:min(k, sc.shape[0])])
+    expect_caught(monkeypatch, "select_topk", bad, golden_all)
+
+
+def test_caught_wrong_softmax_scale(monkeypatch):
+    real = orc.attend
+    expect_caught(monkeypatch, "attend", lambda q, K, V, s: real(q, K, V, s / math.sqrt(128)),
+                  dense_all)
+
+
+def test_caught_transposed_value_operand(monkeypatch):
+    def bad(q, K, V, s):
+        z = (q @ K.T) * s
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        return (p @ K), np.log(np.exp(z).sum(axis=1))      # uses K in place of V
+    expect_caught(monkeypatch, "attend", bad, dense_all, golden_all)
+
+
+def test_caught_dropped_window(monkeypatch):
+    def bad(L_i, window, r):
+        if L_i <= window:
+            return 0, 0
+        n_far = (L_i - window) // r
+        return n_far, L_i                       # window attended nowhere
+    expect_caught(monkeypatch, "row_geometry", bad, golden_all, dense_all)
+
+
+def test_caught_pool_tail_dropped(monkeypatch):
+    def bad(L_i, window, r):
+        if L_i <= window:
+            return 0, 0
+        n_far = (L_i - window) // r
+        return n_far, L_i - window              # the < r tail is attended by nobody
+    expect_caught(monkeypatch, "row_geometry", bad, golden_all)
+
+
+def test_caught_pool_without_bf16_rounding(monkeypatch):
+    def bad(x, r):
+        x = np.asarray(x, np.float64)
+        nb = x.shape[0] // r
+        return x[: nb * r].reshape(nb, r, x.shape[1]).mean(axis=1)
+    expect_caught(monkeypatch, "pool_mean", bad, pins.test_pool_mean_closed_form)
+
+
+def test_caught_truncating_quantizer(monkeypatch):
+    def bad(y, scale):
+        return np.clip(np.trunc(np.asarray(y) / scale), -127, 127).astype(np.int8)
+    expect_caught(monkeypatch, "quantize_codes", bad,
+                  pins.test_key_sketch_coordinate_basis_closed_form, golden_all)
+
+
+def test_caught_round_half_away_from_zero(monkeypatch):
+    def bad(y, scale):
+        v = np.asarray(y) / scale
+        return np.clip(np.sign(v) * np.floor(np.abs(v) + 0.5), -127, 127).astype(np.int8)
+    expect_caught(monkeypatch, "quantize_codes", bad, pins.test_key_sketch_coordinate_basis_closed_form)
+
+
+def test_caught_projection_with_transposed_basis(monkeypatch):
+    def bad(x, basis):
+        P = np.asarray(basis, np.float64)
+        return np.asarray(x, np.float64)[:, ::-1][:, : P.shape[0]] @ np.eye(P.shape[0])
+    expect_caught(monkeypatch, "project", bad, pins.test_key_sketch_coordinate_basis_closed_form,
+                  pins.test_key_sketch_orthonormal_projection_invariants)
+
+
+def test_caught_score_sign_flip(monkeypatch):
+    expect_caught(monkeypatch, "scores", lambda qc, kc: -(np.asarray(kc, np.int64) @ np.asarray(qc, np.int64)),
+                  golden_all, pins.test_scores_extremes_and_brute_force)
+
+
+def test_caught_bf16_decode_wrong_shift(monkeypatch):
+    def bad(bits):
+        u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 15
+        return u32.view(np.float32).astype(np.float64)
+    expect_caught(monkeypatch, "bf16_to_f64", bad, pins.test_bf16_decode_closed_form)
