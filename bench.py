@@ -1,0 +1,240 @@
+"""Decode-attention benchmark of the sparse-sketch path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config multi_agent_250k]
+
+One step = one decode-attention layer for the whole batch: the APPEND key
+sketch of the rows' own tokens, the query sketch, scoring every far token,
+top-k selection and the gathered merged-softmax attention (all calls of the
+C ABI on one stream).  Inputs are seeded synthetic caches resident in HBM
+before timing starts.  `--replicas` distinct copies of the cache (standing in
+for consecutive layers) are visited round-robin so that no step finds the
+previous step's data in the last-level cache.
+
+Prints ONE JSON line with steps/s, the roofline of the dominant kernel
+(sketch_score, HBM-bound) measured with HIP events on the launch stream, and
+the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="multi_agent_250k")
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(cfg):
+    """Bytes the method must move per step (per the row geometry of row 0..R-1).
+
+    sketch: 64 B per far token/block per (b, KV head), one pass for all rows;
+    gathered: one K and one V row per attended entry per (b, row, KV head);
+    plus q in, out and idx out.
+    """
+    B, R, Hkv, Hq = cfg.B, cfg.R, cfg.Hkv, cfg.Hq
+    row_bytes = 128 * (2 if cfg.kv_dtype == 0 else 1) + (0 if cfg.kv_dtype == 0 else 2)
+    n_far_max = cfg.n_far(R - 1)
+    sketch = B * Hkv * n_far_max * 64
+    gathered = sum(B * Hkv * cfg.n_attended(i) * 2 * row_bytes for i in range(R))
+    small = B * R * Hq * 128 * 2 + B * R * Hq * 128 * 4 + B * R * Hkv * cfg.topk * 4
+    return sketch, gathered, small
+
+
+def cpu_baseline(cfg, case, seconds):
+    """Time the oracle's per-step functions on sequence 0 (a bounded sample)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import sks_oracle as orc
+
+    g = cfg.g
+    with threadpool_limits(limits=1):
+        qf = orc.bf16_to_f64(case.q)
+        prep = []
+        for h in range(cfg.Hkv):             # bulk key sketch: outside the timed region
+            Kf, Vf = orc.cache_rows(case.K, case.V, case.K_scale, case.V_scale, 0, h,
+                                    cfg.kv_dtype == 1)
+            Kp, Vp = orc.pool_mean(Kf, cfg.pool), orc.pool_mean(Vf, cfg.pool)
+            _, kc = orc.key_sketch(Kp, case.basis, float(case.key_scale[h]))
+            prep.append((Kf, Vf, Kp, Vp, kc))
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for h in range(cfg.Hkv):
+                Kf, Vf, Kp, Vp, kc = prep[h]
+                for i in range(cfg.R):
+                    Li = int(case.seq_len[0]) + i
+                    n_far, ws = orc.row_geometry(Li, cfg.window, cfg.pool)
+                    qc, _, _ = orc.query_sketch(qf[0, i, h * g:(h + 1) * g], case.basis)
+                    sc = orc.scores(qc, kc[:n_far])
+                    sel = orc.select_topk(sc, cfg.topk)
+                    orc.attend(qf[0, i, h * g:(h + 1) * g],
+                               np.concatenate([Kp[sel], Kf[ws:Li]]),
+                               np.concatenate([Vp[sel], Vf[ws:Li]]), 1.0 / np.sqrt(128.0))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    per_seq = el / reps
+    return {"value": 1.0 / (per_seq * cfg.B), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequence 0 of {cfg.B} ({cfg.Hkv} KV heads x {cfg.R} rows), "
+                      f"{reps} repetitions in {el:.1f} s; steps/s = 1 / ({cfg.B} x time per "
+                      "sequence); bulk key sketch excluded as on the GPU"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the sparse-sketch path here has no multi-GPU "
+              "mode (each (sequence, KV head) pair would shard without communication).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from long_context_sparse_sketch_amd import binding as sks
+    from long_context_sparse_sketch_amd import configs as C
+    from long_context_sparse_sketch_amd.runtime import SparseDecodeLayer, to_device
+    from long_context_sparse_sketch_amd.synth import make_case
+
+    cfg = C.BY_NAME[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sks.lib()
+    t_gen = time.perf_counter()
+    case = make_case(cfg)
+    print(f"[bench] generated {cfg.name} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
+          flush=True)
+
+    i8 = cfg.kv_dtype == C.KV_I8
+    K0 = torch.from_numpy(case.K).to(dev) if i8 else to_device(case.K, dev, bf16=True)
+    V0 = torch.from_numpy(case.V).to(dev) if i8 else to_device(case.V, dev, bf16=True)
+    Ks0 = to_device(case.K_scale, dev) if i8 else None
+    Vs0 = to_device(case.V_scale, dev) if i8 else None
+    q = to_device(case.q, dev, bf16=True)
+    sl = torch.from_numpy(case.seq_len.copy()).to(dev)
+    basis = torch.from_numpy(case.basis).to(dev)
+    kscale = torch.from_numpy(case.key_scale).to(dev)
+
+    layers = []
+    for r in range(args.replicas):
+        K = K0 if r == 0 else K0.clone()
+        V = V0 if r == 0 else V0.clone()
+        Ks = Ks0 if (r == 0 or Ks0 is None) else Ks0.clone()
+        Vs = Vs0 if (r == 0 or Vs0 is None) else Vs0.clone()
+        cache = sks.Cache(K, V, sl, Ks, Vs)
+        lay = SparseDecodeLayer(cfg.B, cfg.R, cfg.Hq, cfg.Hkv, cfg.T_max, cfg.window, cfg.topk,
+                                cfg.pool, cfg.kv_dtype, dev).bind(cache, basis, kscale)
+        lay.build_sketch(0, cfg.T_max)
+        layers.append(lay)
+    torch.cuda.synchronize()
+    print(f"[bench] {args.replicas} cache replicas resident, sketches built", file=sys.stderr,
+          flush=True)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    stream = torch.cuda.current_stream()
+    for k in range(args.warmup):
+        layers[k % len(layers)].step(q)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, events around the dominant kernel of each
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        lay = layers[k % len(layers)]
+        lay.build_sketch(sks.APPEND, 0)
+        lay.query_sketch(q)
+        ev_a[2 * k].record(stream)
+        lay.score()
+        ev_a[2 * k + 1].record(stream)
+        lay.select()
+        lay.attend(q)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    score_ms = [ev_a[2 * k].elapsed_time(ev_a[2 * k + 1]) for k in range(args.steps)]
+
+    # attention kernel timing in its own pass (same stream, same rotation)
+    ev_t = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for k in range(args.steps):
+        lay = layers[k % len(layers)]
+        lay.score()
+        lay.select()
+        ev_t[2 * k].record(stream)
+        lay.attend(q)
+        ev_t[2 * k + 1].record(stream)
+    torch.cuda.synchronize()
+    attn_ms = [ev_t[2 * k].elapsed_time(ev_t[2 * k + 1]) for k in range(args.steps)]
+
+    ms_per_step = total_ms / args.steps
+    sketch_b, gather_b, small_b = algorithmic_bytes(cfg)
+    score_avg_ms = float(np.mean(score_ms))
+    attn_avg_ms = float(np.mean(attn_ms))
+    achieved = sketch_b / (score_avg_ms * 1e-3) / 1e9
+    line = {
+        "metric": "decode-attn steps/s and achieved HBM GB/s (% peak) at 250K ctx, top-k 2048",
+        "value": 1000.0 / ms_per_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8 sketch / bf16 KV / f32 accumulate" if not i8 else "i8 sketch / i8 KV / f32 accumulate",
+        "data": "synthetic (seeded N(0,1) caches with planted needles)",
+        "config": {"workload": cfg.name, "batch": cfg.B, "context": cfg.L, "rows": cfg.R,
+                   "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "window": cfg.window,
+                   "topk": cfg.topk, "pool": cfg.pool, "replicas": args.replicas},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "sketch_score", "algorithmic_bytes": sketch_b,
+                     "avg_ms": score_avg_ms},
+        "detail": {
+            "algorithmic_bytes_per_step": sketch_b + gather_b + small_b,
+            "gathered_kv_bytes": gather_b,
+            "attn_avg_ms": attn_avg_ms,
+            "attn_GBps": gather_b / (attn_avg_ms * 1e-3) / 1e9,
+            "score_plus_attn_GBps": (sketch_b + gather_b) / ((score_avg_ms + attn_avg_ms) * 1e-3) / 1e9,
+            "step_GBps": (sketch_b + gather_b + small_b) / (ms_per_step * 1e-3) / 1e9,
+        },
+    }
+    line["detail"]["score_plus_attn_frac"] = line["detail"]["score_plus_attn_GBps"] / HBM_PEAK_GBPS
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, case, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * sks.h -- C ABI of libsks, sparse-sketch long-context decode attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One decode-attention step over one layer, as described on the page
+ * "8 agents x 250K context, concurrently, on two 3090s" (claims list: every
+ * decode step each attention layer reads ~1% of the tokens, picked with a tiny
+ * rank-64 key sketch; "What it took": build the sketch, score every token,
+ * pick the top ~2K and pack them for attention, CUDA-graph safe) and on the
+ * "Agens SGLang" README ("What it adds": a 4,096-token sliding window plus a
+ * 4:1 mean-pooled far field merged under one softmax; "Quick start": the
+ * speculative-decoding verify step served as a chain).
+ *
+ * A step is:  sks_sketch_build (append the current tokens' key sketches)
+ *             -> sks_sketch_build_query -> sks_sketch_score -> sks_topk_select
+ *             -> sks_sparse_decode_attn (gathers the picked rows itself);
+ *             sks_gather_pack materialises the same rows as a packed copy.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor argument is a DEVICE pointer to caller-owned, contiguous,
+ *   row-major memory; 16-byte alignment is required for K, V, S, Kp, Vp,
+ *   K_out, V_out, out, scores and the workspace, 4-byte for the rest.
+ * - The library allocates nothing, frees nothing and never synchronises: a
+ *   call validates its host-visible arguments, enqueues kernels on `stream`
+ *   (NULL = the null stream of the current device) and returns.  All calls
+ *   can therefore be captured into a HIP graph.  Lengths are read on the
+ *   device (`seq_len`), so one captured step serves every decode position.
+ * - Errors: a call whose arguments are invalid returns SKS_ERR_ARG (or
+ *   SKS_ERR_UNSUPPORTED / SKS_ERR_WORKSPACE) BEFORE launching anything, and
+ *   sks_last_error() describes it.  SKS_ERR_HIP reports a failed launch; the
+ *   outputs may then be partly written.
+ * - Device lengths are clamped to [0, T_max - rows + 1] inside the kernels,
+ *   so a bad length gives unspecified but memory-safe results.
+ * - Results are bit-deterministic for identical inputs, whatever the batch
+ *   composition: no floating-point atomics, split counts fixed by the shape,
+ *   fixed merge order.
+ *
+ * Geometry of query row i (0 <= i < rows) of sequence b, with r = pool:
+ *   L_i   = seq_len[b] + i        tokens visible to the row (its own included;
+ *                                  row i sits at position seq_len[b]-1+i)
+ *   n_far = L_i > window ? (L_i - window) / r : 0       far tokens / r-blocks
+ *   ws    = n_far * r              first token of the exact window
+ *   k_eff = min(topk, n_far)
+ *   The row attends to its k_eff selected far entries (pooled rows when r > 1)
+ *   and to every token in [ws, L_i), under one softmax.  Query head h uses KV
+ *   head h / (Hq / Hkv); the selection is per (sequence, row, KV head).
+ */
+#ifndef SKS_H
+#define SKS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *sks_stream_t; /* a hipStream_t */
+
+enum sks_status {
+  SKS_OK = 0,
+  SKS_ERR_ARG = 1,          /* invalid argument; nothing was launched          */
+  SKS_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. int8 + pooling)  */
+  SKS_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required       */
+  SKS_ERR_HIP = 4           /* a HIP launch failed                              */
+};
+
+enum sks_kv_dtype {
+  SKS_KV_BF16 = 0,          /* K, V hold bfloat16                               */
+  SKS_KV_I8 = 1             /* K, V hold int8 codes; x = code * fp16 row scale  */
+};
+
+#define SKS_HEAD_DIM 128
+#define SKS_RANK 64
+#define SKS_MAX_ROWS 8
+#define SKS_MAX_POOL 64
+#define SKS_APPEND (-1)     /* t_begin value: sketch the current rows' tokens  */
+
+/* One layer's KV cache. */
+typedef struct sks_kv {
+  int32_t B;                /* sequences                                        */
+  int32_t Hkv;              /* KV heads                                         */
+  int32_t D;                /* head dim, must be 128                            */
+  int32_t T_max;            /* cache capacity in tokens                         */
+  int32_t dtype;            /* enum sks_kv_dtype                                */
+  const void *K;            /* [B][Hkv][T_max][D] bf16 or int8                  */
+  const void *V;            /* [B][Hkv][T_max][D]                               */
+  const uint16_t *K_scale;  /* [B][Hkv][T_max] fp16 bits, int8 only, else NULL  */
+  const uint16_t *V_scale;  /* [B][Hkv][T_max] fp16 bits, int8 only, else NULL  */
+  const int32_t *seq_len;   /* [B] device: L of query row 0 (own token included) */
+} sks_kv;
+
+/* Selection parameters of the step. */
+typedef struct sks_params {
+  int32_t window;           /* exact sliding window W >= 0                      */
+  int32_t topk;             /* k >= 1 far entries per (sequence, row, KV head)  */
+  int32_t pool;             /* far-field pooling ratio r, 1 <= r <= 64          */
+  int32_t rank;             /* sketch rank, must be 64                          */
+  int32_t rows;             /* query rows per sequence R, 1 <= R <= 8           */
+} sks_params;
+
+/* Number of sketch rows (tokens, or r-blocks) per (sequence, KV head):
+ * NB = T_max / pool.  S, Kp, Vp and each scores row have NB entries. */
+
+/* Text of the last error returned on this thread ("" if none). */
+const char *sks_last_error(void);
+
+/* HIP runtime version seen by the library (hipRuntimeGetVersion). */
+int32_t sks_runtime_version(void);
+
+/* Workspace bytes that sks_topk_select and sks_sparse_decode_attn need for
+ * this shape (the same buffer may serve both; contents need no
+ * initialisation and are clobbered).  Returns 0 on invalid arguments. */
+size_t sks_workspace_bytes(const sks_kv *kv, const sks_params *p, int32_t Hq);
+
+/* Key sketch build.  "What it took" (build the sketch) and the claims list
+ * (rank-64 key sketch) of "8 agents x 250K context ...", plus the frozen
+ * sketch basis of the same list; pooling from "What it adds" of
+ * "Agens SGLang".
+ *
+ * For every sequence b, KV head h and sketch row j:
+ *   pool == 1: rows are tokens t in the position range;
+ *              S[b][h][t][c] = clamp(rne((P_h . x_t)_c / key_scale[h]), +-127)
+ *              with x_t the (dequantised) key; Kp, Vp must be NULL.
+ *   pool  > 1: rows are blocks j whose LAST token r*j + r - 1 lies in the
+ *              position range; Kp/Vp[b][h][j] = bf16(rne(mean of the block's
+ *              r keys / values)) and S[b][h][j] is the sketch of Kp[b][h][j].
+ *              bf16 caches only (SKS_ERR_UNSUPPORTED otherwise).
+ * basis: [1][64][128] (basis_per_head == 0) or [Hkv][64][128] fp32, row c of
+ *        P_h being the c-th basis vector.  key_scale: [Hkv] fp32, > 0.
+ * Position range: [t_begin, t_end) clamped to [0, T_max) for every sequence,
+ *   or, with t_begin == SKS_APPEND, the current rows' own tokens
+ *   [seq_len[b] - 1, seq_len[b] - 1 + rows) read on the device (t_end ignored).
+ * S: [B][Hkv][NB][64] int8.  Kp, Vp: [B][Hkv][NB][128] bf16 (pool > 1). */
+int sks_sketch_build(const sks_kv *kv, const sks_params *p, const float *basis,
+                     int32_t basis_per_head, const float *key_scale, int32_t t_begin,
+                     int32_t t_end, int8_t *S, uint16_t *Kp, uint16_t *Vp,
+                     sks_stream_t stream);
+
+/* Query sketch.  Same passages as the key sketch; under grouped-query
+ * attention the query side of KV head h is the mean qbar of its g = Hq/Hkv
+ * query vectors:  y = P_h qbar,  qscale = max|y| / 127,
+ *   qsk = clamp(rne(y / qscale), +-127)   (all zero and qscale 0 if y == 0).
+ * q: [B][R][Hq][128] bf16.  qsk: [B][R][Hkv][64] int8.  qscale: [B][R][Hkv]
+ * fp32 (may be NULL). */
+int sks_sketch_build_query(const uint16_t *q, int32_t B, int32_t R, int32_t Hq, int32_t Hkv,
+                           const float *basis, int32_t basis_per_head, int8_t *qsk,
+                           float *qscale, sks_stream_t stream);
+
+/* Score every far token ("What it took": score every token):
+ *   scores[b][i][h][t] = sum_c qsk[b][i][h][c] * S[b][h][t][c]   (exact int32)
+ * for t < n_far of the row with the most far entries; one pass over S serves
+ * all rows.  Entries past that are not written.
+ * scores: [B][R][Hkv][NB] int32. */
+int sks_sketch_score(const int8_t *qsk, const int8_t *S, const sks_kv *kv,
+                     const sks_params *p, int32_t *scores, sks_stream_t stream);
+
+/* Top-k selection ("What it took": pick the top ~2K).  For every (b, i, h):
+ * the k_eff far entries with the largest scores[b][i][h][0 .. n_far), the
+ * lower index first among equal scores, written in ascending order to
+ * idx[b][i][h][0 .. k_eff) and padded with -1 up to topk.
+ * n_sel: [B][R][Hkv] int32 receives k_eff (may be NULL).
+ * ws: at least sks_workspace_bytes(). */
+int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p,
+                    int32_t *idx, int32_t *n_sel, void *ws, size_t ws_bytes,
+                    sks_stream_t stream);
+
+/* Gather/pack ("What it took": pack the picked tokens for the attention
+ * kernel).  For every (b, i, h) writes the row's attention set, selected far
+ * entries first (ascending, rows of Kp/Vp when pool > 1, else of K/V), then
+ * the window tokens [ws, L_i) ascending, into
+ *   K_out, V_out: [B][R][Hkv][C][128] with C = topk + window + pool - 1,
+ * same element type as the cache (int8 caches also write the fp16 row scales
+ * to Ks_out, Vs_out [B][R][Hkv][C]; NULL for bf16), and the entry count to
+ * n_out [B][R][Hkv].  Slots past n_out are not written. */
+int sks_gather_pack(const sks_kv *kv, const sks_params *p, const int32_t *idx,
+                    const uint16_t *Kp, const uint16_t *Vp, void *K_out, void *V_out,
+                    uint16_t *Ks_out, uint16_t *Vs_out, int32_t *n_out,
+                    sks_stream_t stream);
+
+/* Sparse decode attention, one merged softmax over the selected far entries
+ * and the exact window ("What it adds" of "Agens SGLang"; "int8 attention"
+ * of "What it took" for int8 caches, dequantised in registers).  For query
+ * head hq of row i of sequence b, with U its row's attention set:
+ *   z_j = sm_scale * (q . K_j),  out = sum_j softmax(z)_j V_j,
+ *   lse = log sum_j exp(z_j)     (U empty: out = 0, lse = -inf).
+ * The rows are gathered from K/V (and Kp/Vp for selected blocks when
+ * pool > 1) by idx [B][R][Hkv][topk] as written by sks_topk_select.
+ * q: [B][R][Hq][128] bf16.  out: [B][R][Hq][128] fp32.  lse: [B][R][Hq] fp32
+ * (may be NULL).  ws: at least sks_workspace_bytes(). */
+int sks_sparse_decode_attn(const uint16_t *q, int32_t Hq, const sks_kv *kv,
+                           const sks_params *p, const int32_t *idx, const uint16_t *Kp,
+                           const uint16_t *Vp, float sm_scale, float *out, float *lse,
+                           void *ws, size_t ws_bytes, sks_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKS_H */

@@ -1,0 +1,164 @@
+"""ctypes binding of libsks (include/sks.h): argument marshalling only.
+
+Every function here forwards torch tensors' device pointers and the current
+HIP stream to the C ABI of the same name; all computation happens in the HIP
+kernels.  The library is loaded after torch so that both share one HIP
+runtime.  There is no fallback: a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB = None
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsks.so")
+
+SKS_OK, SKS_ERR_ARG, SKS_ERR_UNSUPPORTED, SKS_ERR_WORKSPACE, SKS_ERR_HIP = range(5)
+KV_BF16, KV_I8 = 0, 1
+APPEND = -1
+HEAD_DIM, RANK = 128, 64
+
+EXPORTS = ("sks_last_error", "sks_runtime_version", "sks_workspace_bytes", "sks_sketch_build",
+           "sks_sketch_build_query", "sks_sketch_score", "sks_topk_select", "sks_gather_pack",
+           "sks_sparse_decode_attn")
+
+
+class SksError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"sks error {code}: {msg}")
+        self.code = code
+
+
+class KVDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("T_max", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("K", ctypes.c_void_p), ("V", ctypes.c_void_p),
+                ("K_scale", ctypes.c_void_p), ("V_scale", ctypes.c_void_p),
+                ("seq_len", ctypes.c_void_p)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("topk", ctypes.c_int32), ("pool", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("rows", ctypes.c_int32)]
+
+
+def params(window: int, topk: int, pool: int = 1, rows: int = 1, rank: int = RANK) -> Params:
+    return Params(window, topk, pool, rank, rows)
+
+
+def lib():
+    """Load libsks.so (built in-tree by build.py); raise if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m "
+                               "long_context_sparse_sketch_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        kvp, pp = ctypes.POINTER(KVDesc), ctypes.POINTER(Params)
+        L.sks_last_error.restype = ctypes.c_char_p
+        L.sks_last_error.argtypes = []
+        L.sks_runtime_version.restype = i32
+        L.sks_runtime_version.argtypes = []
+        L.sks_workspace_bytes.restype = sz
+        L.sks_workspace_bytes.argtypes = [kvp, pp, i32]
+        L.sks_sketch_build.restype = ctypes.c_int
+        L.sks_sketch_build.argtypes = [kvp, pp, vp, i32, vp, i32, i32, vp, vp, vp, vp]
+        L.sks_sketch_build_query.restype = ctypes.c_int
+        L.sks_sketch_build_query.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp]
+        L.sks_sketch_score.restype = ctypes.c_int
+        L.sks_sketch_score.argtypes = [vp, vp, kvp, pp, vp, vp]
+        L.sks_topk_select.restype = ctypes.c_int
+        L.sks_topk_select.argtypes = [vp, kvp, pp, vp, vp, vp, sz, vp]
+        L.sks_gather_pack.restype = ctypes.c_int
+        L.sks_gather_pack.argtypes = [kvp, pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.sks_sparse_decode_attn.restype = ctypes.c_int
+        L.sks_sparse_decode_attn.argtypes = [vp, i32, kvp, pp, vp, vp, vp, ctypes.c_float, vp,
+                                             vp, vp, sz, vp]
+        _LIB = L
+    return _LIB
+
+
+def last_error() -> str:
+    return lib().sks_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != SKS_OK:
+        raise SksError(rc, last_error())
+
+
+def ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Cache:
+    """Descriptor of one layer's KV cache; keeps the tensors alive."""
+
+    def __init__(self, K, V, seq_len, K_scale=None, V_scale=None):
+        self.K, self.V, self.seq_len, self.K_scale, self.V_scale = K, V, seq_len, K_scale, V_scale
+        B, Hkv, T, D = K.shape
+        dtype = KV_I8 if K.dtype == torch.int8 else KV_BF16
+        self.desc = KVDesc(B, Hkv, D, T, dtype, ptr(K), ptr(V), ptr(K_scale), ptr(V_scale),
+                           ptr(seq_len))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def workspace_bytes(cache: Cache, p: Params, Hq: int) -> int:
+    return lib().sks_workspace_bytes(cache.ref, ctypes.byref(p), Hq)
+
+
+def sketch_build(cache: Cache, p: Params, basis, key_scale, S, t_begin=0, t_end=None, Kp=None,
+                 Vp=None, basis_per_head=False, stream=None):
+    if t_end is None:
+        t_end = cache.desc.T_max
+    _check(lib().sks_sketch_build(cache.ref, ctypes.byref(p), ptr(basis), int(basis_per_head),
+                                  ptr(key_scale), t_begin, t_end, ptr(S), ptr(Kp), ptr(Vp),
+                                  _stream(stream)))
+
+
+def sketch_build_query(q, Hkv: int, basis, qsk, qscale=None, basis_per_head=False, stream=None):
+    B, R, Hq, _ = q.shape
+    _check(lib().sks_sketch_build_query(ptr(q), B, R, Hq, Hkv, ptr(basis), int(basis_per_head),
+                                        ptr(qsk), ptr(qscale), _stream(stream)))
+
+
+def sketch_score(qsk, S, cache: Cache, p: Params, scores, stream=None):
+    _check(lib().sks_sketch_score(ptr(qsk), ptr(S), cache.ref, ctypes.byref(p), ptr(scores),
+                                  _stream(stream)))
+
+
+def topk_select(scores, cache: Cache, p: Params, idx, n_sel, ws, stream=None):
+    _check(lib().sks_topk_select(ptr(scores), cache.ref, ctypes.byref(p), ptr(idx), ptr(n_sel),
+                                 ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                 _stream(stream)))
+
+
+def gather_pack(cache: Cache, p: Params, idx, K_out, V_out, n_out, Kp=None, Vp=None,
+                Ks_out=None, Vs_out=None, stream=None):
+    _check(lib().sks_gather_pack(cache.ref, ctypes.byref(p), ptr(idx), ptr(Kp), ptr(Vp),
+                                 ptr(K_out), ptr(V_out), ptr(Ks_out), ptr(Vs_out), ptr(n_out),
+                                 _stream(stream)))
+
+
+def sparse_decode_attn(q, cache: Cache, p: Params, idx, out, ws, lse=None, Kp=None, Vp=None,
+                       sm_scale=None, stream=None):
+    Hq = q.shape[2]
+    sm = 1.0 / math.sqrt(q.shape[3]) if sm_scale is None else sm_scale
+    _check(lib().sks_sparse_decode_attn(ptr(q), Hq, cache.ref, ctypes.byref(p), ptr(idx),
+                                        ptr(Kp), ptr(Vp), ctypes.c_float(sm), ptr(out), ptr(lse),
+                                        ptr(ws),
+                                        0 if ws is None else ws.numel() * ws.element_size(),
+                                        _stream(stream)))

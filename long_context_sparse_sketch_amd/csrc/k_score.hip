@@ -1,0 +1,110 @@
+// Score every far token against the query sketch ("What it took" on the page
+// "8 agents x 250K context, concurrently, on two 3090s": score every token).
+//
+// scores[b][i][h][t] = sum_c qsk[b][i][h][c] * S[b][h][t][c], exact int32.
+//
+// The pass is a pure HBM stream of 64-byte int8 rows.  Layout: a quad of
+// lanes owns one token row, each lane 16 bytes, so one dwordx4 load of a wave
+// covers 16 consecutive rows (1 KiB, fully coalesced).  Each lane keeps 8
+// loads in flight, does v_dot4 on its 16 bytes for every query row, and the
+// quad sums by DPP.  Lane p of a quad then writes the scores of unroll slots
+// p and p+4, so every store instruction writes 64 consecutive int32.
+#include "sks_internal.h"
+
+namespace sks {
+namespace {
+
+constexpr int SC_THREADS = 256;
+constexpr int SC_UNROLL = 8;                        // rows per lane-quad per step
+constexpr int SC_WAVE_STEP = 16 * SC_UNROLL;        // 128 rows per wave step
+constexpr int SC_BLOCK_STEP = SC_WAVE_STEP * (SC_THREADS / 64);   // 512
+
+template <int R>
+__global__ __launch_bounds__(SC_THREADS) void score_kernel(
+    const int8_t *__restrict__ qsk, const int8_t *__restrict__ S,
+    const int32_t *__restrict__ seq_len, int32_t *__restrict__ scores, int Hkv, int T_max,
+    int NB, int window, int pool) {
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
+  const int L0 = clamp_len(seq_len[b], T_max, R);
+  const int Lmax = L0 + R - 1;
+  const int n_far = Lmax > window ? (Lmax - window) / pool : 0;
+  const int c0 = blockIdx.x * SCORE_CHUNK;
+  if (c0 >= n_far) return;
+  const int c1 = min(n_far, c0 + SCORE_CHUNK);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int quad = lane >> 2, part = lane & 3;
+
+  int4 qv[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    qv[i] = *reinterpret_cast<const int4 *>(qsk + ((size_t)(b * R + i) * Hkv + h) * RANK + part * 16);
+
+  const int4 *Sbh = reinterpret_cast<const int4 *>(S + (size_t)bh * NB * RANK) + part;
+  int32_t *out[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) out[i] = scores + ((size_t)(b * R + i) * Hkv + h) * NB;
+
+  for (int base = c0 + wave * SC_WAVE_STEP; base < c1; base += SC_BLOCK_STEP) {
+    int4 sv[SC_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SC_UNROLL; ++u) {
+      const int t = base + u * 16 + quad;
+      sv[u] = t < c1 ? Sbh[(size_t)t * 4] : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      int acc[SC_UNROLL];
+#pragma unroll
+      for (int u = 0; u < SC_UNROLL; ++u) {
+        int a = __builtin_amdgcn_sdot4(sv[u].x, qv[i].x, 0, false);
+        a = __builtin_amdgcn_sdot4(sv[u].y, qv[i].y, a, false);
+        a = __builtin_amdgcn_sdot4(sv[u].z, qv[i].z, a, false);
+        a = __builtin_amdgcn_sdot4(sv[u].w, qv[i].w, a, false);
+        acc[u] = quad_sum_i(a);
+      }
+      // lane `part` stores slots part and part + 4
+      int lo = acc[0], hi = acc[4];
+#pragma unroll
+      for (int u = 1; u < 4; ++u) {
+        lo = part == u ? acc[u] : lo;
+        hi = part == u ? acc[u + 4] : hi;
+      }
+      const int t_lo = base + part * 16 + quad;
+      const int t_hi = t_lo + 64;
+      if (t_lo < c1) out[i][t_lo] = lo;
+      if (t_hi < c1) out[i][t_hi] = hi;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
+                        const Shape &s, int32_t *scores, hipStream_t st) {
+  // the largest far count any row can have is (T_max - window) / pool <= NB
+  long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
+  if (max_far <= 0) return hipSuccess;
+  dim3 grid(ceil_div(max_far, SCORE_CHUNK), s.B * s.Hkv);
+  switch (s.R) {
+#define SKS_SCORE_CASE(RR)                                                                     \
+  case RR:                                                                                     \
+    score_kernel<RR><<<grid, SC_THREADS, 0, st>>>(qsk, S, seq_len, scores, s.Hkv, s.T_max,     \
+                                                  s.NB, s.window, s.pool);                     \
+    break;
+    SKS_SCORE_CASE(1)
+    SKS_SCORE_CASE(2)
+    SKS_SCORE_CASE(3)
+    SKS_SCORE_CASE(4)
+    SKS_SCORE_CASE(5)
+    SKS_SCORE_CASE(6)
+    SKS_SCORE_CASE(7)
+    SKS_SCORE_CASE(8)
+#undef SKS_SCORE_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sks

@@ -1,0 +1,257 @@
+// Host side of the libsks C ABI: argument validation (before any launch),
+// workspace sizing, thread-local error text and kernel dispatch.  Every entry
+// point only enqueues work on the caller's stream; nothing is allocated,
+// freed or synchronised here.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "sks_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SKS_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE(cond, ...)                          \
+  do {                                              \
+    if (!(cond)) return fail(SKS_ERR_ARG, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(ptr, align)                                                          \
+  do {                                                                                   \
+    if (!(ptr)) return fail(SKS_ERR_ARG, "%s must not be NULL", #ptr);                   \
+    if (!aligned((ptr), (align)))                                                        \
+      return fail(SKS_ERR_ARG, "%s must be %d-byte aligned", #ptr, (int)(align));        \
+  } while (0)
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(SKS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Shape checks shared by every call that takes the cache description.
+int check_shape(const sks_kv *kv, const sks_params *p, sks::Shape &s) {
+  REQUIRE(kv != nullptr, "kv must not be NULL");
+  REQUIRE(p != nullptr, "params must not be NULL");
+  REQUIRE(kv->D == SKS_HEAD_DIM, "D must be %d (got %d)", SKS_HEAD_DIM, kv->D);
+  REQUIRE(p->rank == SKS_RANK, "rank must be %d (got %d)", SKS_RANK, p->rank);
+  REQUIRE(kv->B >= 1 && kv->Hkv >= 1, "B and Hkv must be >= 1 (got %d, %d)", kv->B, kv->Hkv);
+  REQUIRE(kv->dtype == SKS_KV_BF16 || kv->dtype == SKS_KV_I8, "unknown KV dtype %d", kv->dtype);
+  REQUIRE(p->rows >= 1 && p->rows <= SKS_MAX_ROWS, "rows must be in [1, %d] (got %d)",
+          SKS_MAX_ROWS, p->rows);
+  REQUIRE(kv->T_max >= p->rows, "T_max (%d) must be >= rows (%d)", kv->T_max, p->rows);
+  REQUIRE(p->pool >= 1 && p->pool <= SKS_MAX_POOL, "pool must be in [1, %d] (got %d)",
+          SKS_MAX_POOL, p->pool);
+  REQUIRE(kv->T_max / p->pool >= 1, "T_max / pool must be >= 1");
+  REQUIRE(p->window >= 0 && p->window <= kv->T_max, "window must be in [0, T_max] (got %d)",
+          p->window);
+  REQUIRE(p->topk >= 1 && p->topk <= kv->T_max, "topk must be in [1, T_max] (got %d)", p->topk);
+  REQUIRE(kv->seq_len != nullptr, "kv->seq_len must not be NULL");
+  REQUIRE(aligned(kv->seq_len, 4), "kv->seq_len must be 4-byte aligned");
+  const long nseg = (long)kv->B * p->rows * kv->Hkv;
+  REQUIRE(nseg <= 65535, "B * rows * Hkv must be <= 65535 (got %ld)", nseg);
+  if (p->pool > 1 && kv->dtype != SKS_KV_BF16)
+    return fail(SKS_ERR_UNSUPPORTED, "pooling (pool > 1) needs a bf16 cache");
+  s.B = kv->B;
+  s.R = p->rows;
+  s.Hkv = kv->Hkv;
+  s.T_max = kv->T_max;
+  s.NB = kv->T_max / p->pool;
+  s.window = p->window;
+  s.topk = p->topk;
+  s.pool = p->pool;
+  s.dtype = kv->dtype;
+  return SKS_OK;
+}
+
+int check_cache(const sks_kv *kv, bool need_v) {
+  REQUIRE_PTR(kv->K, 16);
+  if (need_v) REQUIRE_PTR(kv->V, 16);
+  if (kv->dtype == SKS_KV_I8) {
+    REQUIRE_PTR(kv->K_scale, 2);
+    if (need_v) REQUIRE_PTR(kv->V_scale, 2);
+  }
+  return SKS_OK;
+}
+
+int check_heads(int Hq, int Hkv) {
+  REQUIRE(Hq >= 1 && Hq % Hkv == 0, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  REQUIRE(Hq / Hkv <= sks::ATTN_MAX_G, "Hq / Hkv must be <= %d (got %d)", sks::ATTN_MAX_G,
+          Hq / Hkv);
+  return SKS_OK;
+}
+
+#define TRY(x)                   \
+  do {                           \
+    int rc_ = (x);               \
+    if (rc_ != SKS_OK) return rc_; \
+  } while (0)
+
+size_t ws_bytes(const sks::Shape &s, int G) {
+  return std::max(sks::topk_ws_bytes(s), sks::attn_ws_bytes(s, G));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sks_last_error(void) { return g_err; }
+
+int32_t sks_runtime_version(void) {
+  int v = 0;
+  if (hipRuntimeGetVersion(&v) != hipSuccess) return -1;
+  return v;
+}
+
+size_t sks_workspace_bytes(const sks_kv *kv, const sks_params *p, int32_t Hq) {
+  sks::Shape s;
+  if (check_shape(kv, p, s) != SKS_OK) return 0;
+  if (check_heads(Hq, kv->Hkv) != SKS_OK) return 0;
+  return ws_bytes(s, Hq / kv->Hkv);
+}
+
+int sks_sketch_build(const sks_kv *kv, const sks_params *p, const float *basis,
+                     int32_t basis_per_head, const float *key_scale, int32_t t_begin,
+                     int32_t t_end, int8_t *S, uint16_t *Kp, uint16_t *Vp, sks_stream_t stream) {
+  sks::Shape s;
+  TRY(check_shape(kv, p, s));
+  TRY(check_cache(kv, p->pool > 1));
+  REQUIRE_PTR(basis, 4);
+  REQUIRE_PTR(key_scale, 4);
+  REQUIRE_PTR(S, 16);
+  REQUIRE(basis_per_head == 0 || basis_per_head == 1, "basis_per_head must be 0 or 1");
+  REQUIRE(t_begin == SKS_APPEND || (t_begin >= 0 && t_end >= t_begin),
+          "position range [%d, %d) is invalid", t_begin, t_end);
+  if (p->pool > 1) {
+    REQUIRE_PTR(Kp, 16);
+    REQUIRE_PTR(Vp, 16);
+  } else {
+    REQUIRE(Kp == nullptr && Vp == nullptr, "Kp and Vp must be NULL when pool == 1");
+  }
+  if (t_begin != SKS_APPEND) {
+    t_begin = std::min(t_begin, s.T_max);
+    t_end = std::min(t_end, s.T_max);
+    if (t_end <= t_begin) return ok();
+  }
+  return hip_status(sks::launch_sketch_keys(*kv, s, basis, basis_per_head, key_scale, t_begin,
+                                            t_end, S, Kp, Vp, (hipStream_t)stream),
+                    "sks_sketch_build");
+}
+
+int sks_sketch_build_query(const uint16_t *q, int32_t B, int32_t R, int32_t Hq, int32_t Hkv,
+                           const float *basis, int32_t basis_per_head, int8_t *qsk,
+                           float *qscale, sks_stream_t stream) {
+  REQUIRE(B >= 1 && R >= 1 && R <= SKS_MAX_ROWS && Hkv >= 1, "bad B/R/Hkv (%d, %d, %d)", B, R,
+          Hkv);
+  REQUIRE(Hq >= 1 && Hq % Hkv == 0, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  REQUIRE((long)B * R * Hkv <= 0x7fffffffL, "too many segments");
+  REQUIRE(basis_per_head == 0 || basis_per_head == 1, "basis_per_head must be 0 or 1");
+  REQUIRE_PTR(q, 4);
+  REQUIRE_PTR(basis, 4);
+  REQUIRE_PTR(qsk, 16);
+  if (qscale) REQUIRE(aligned(qscale, 4), "qscale must be 4-byte aligned");
+  return hip_status(sks::launch_sketch_query(q, B, R, Hq, Hkv, basis, basis_per_head, qsk, qscale,
+                                             (hipStream_t)stream),
+                    "sks_sketch_build_query");
+}
+
+int sks_sketch_score(const int8_t *qsk, const int8_t *S, const sks_kv *kv, const sks_params *p,
+                     int32_t *scores, sks_stream_t stream) {
+  sks::Shape s;
+  TRY(check_shape(kv, p, s));
+  REQUIRE_PTR(qsk, 16);
+  REQUIRE_PTR(S, 16);
+  REQUIRE_PTR(scores, 4);
+  return hip_status(sks::launch_score(qsk, S, kv->seq_len, s, scores, (hipStream_t)stream),
+                    "sks_sketch_score");
+}
+
+int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p, int32_t *idx,
+                    int32_t *n_sel, void *ws, size_t ws_bytes_given, sks_stream_t stream) {
+  sks::Shape s;
+  TRY(check_shape(kv, p, s));
+  REQUIRE_PTR(scores, 4);
+  REQUIRE_PTR(idx, 4);
+  if (n_sel) REQUIRE(aligned(n_sel, 4), "n_sel must be 4-byte aligned");
+  if (sks::ceil_div(s.NB, sks::TK_SUB) > sks::TK_MAX_SUBS)
+    return fail(SKS_ERR_UNSUPPORTED, "T_max / pool above %d is not supported by the selection",
+                sks::TK_MAX_SUBS * sks::TK_SUB);
+  const size_t need = sks::topk_ws_bytes(s);
+  if (!ws || ws_bytes_given < need)
+    return fail(SKS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                ws ? ws_bytes_given : (size_t)0);
+  if (!aligned(ws, 256)) return fail(SKS_ERR_ARG, "ws must be 256-byte aligned");
+  const sks::TopkWs w = sks::topk_ws_carve(s, ws);
+  return hip_status(sks::launch_topk(scores, kv->seq_len, s, idx, n_sel, w, (hipStream_t)stream),
+                    "sks_topk_select");
+}
+
+int sks_gather_pack(const sks_kv *kv, const sks_params *p, const int32_t *idx, const uint16_t *Kp,
+                    const uint16_t *Vp, void *K_out, void *V_out, uint16_t *Ks_out,
+                    uint16_t *Vs_out, int32_t *n_out, sks_stream_t stream) {
+  sks::Shape s;
+  TRY(check_shape(kv, p, s));
+  TRY(check_cache(kv, true));
+  REQUIRE_PTR(idx, 4);
+  REQUIRE_PTR(K_out, 16);
+  REQUIRE_PTR(V_out, 16);
+  REQUIRE_PTR(n_out, 4);
+  if (s.pool > 1) {
+    REQUIRE_PTR(Kp, 16);
+    REQUIRE_PTR(Vp, 16);
+  }
+  if (s.dtype == SKS_KV_I8) {
+    REQUIRE_PTR(Ks_out, 2);
+    REQUIRE_PTR(Vs_out, 2);
+  } else {
+    REQUIRE(Ks_out == nullptr && Vs_out == nullptr, "Ks_out/Vs_out must be NULL for bf16");
+  }
+  return hip_status(sks::launch_gather(*kv, s, idx, Kp, Vp, K_out, V_out, Ks_out, Vs_out, n_out,
+                                       (hipStream_t)stream),
+                    "sks_gather_pack");
+}
+
+int sks_sparse_decode_attn(const uint16_t *q, int32_t Hq, const sks_kv *kv, const sks_params *p,
+                           const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp,
+                           float sm_scale, float *out, float *lse, void *ws,
+                           size_t ws_bytes_given, sks_stream_t stream) {
+  sks::Shape s;
+  TRY(check_shape(kv, p, s));
+  TRY(check_cache(kv, true));
+  TRY(check_heads(Hq, kv->Hkv));
+  REQUIRE_PTR(q, 16);
+  REQUIRE_PTR(idx, 4);
+  REQUIRE_PTR(out, 16);
+  if (lse) REQUIRE(aligned(lse, 4), "lse must be 4-byte aligned");
+  if (s.pool > 1) {
+    REQUIRE_PTR(Kp, 16);
+    REQUIRE_PTR(Vp, 16);
+  }
+  REQUIRE(sm_scale > 0.f && sm_scale < 1e30f, "sm_scale must be positive and finite");
+  const size_t need = sks::attn_ws_bytes(s, Hq / kv->Hkv);
+  if (!ws || ws_bytes_given < need)
+    return fail(SKS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                ws ? ws_bytes_given : (size_t)0);
+  if (!aligned(ws, 256)) return fail(SKS_ERR_ARG, "ws must be 256-byte aligned");
+  return hip_status(sks::launch_attn(q, Hq, *kv, s, idx, Kp, Vp, sm_scale, out, lse, ws,
+                                     (hipStream_t)stream),
+                    "sks_sparse_decode_attn");
+}
+
+}  // extern "C"

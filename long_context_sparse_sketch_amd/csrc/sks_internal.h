@@ -1,0 +1,152 @@
+// Internal declarations of libsks: device helpers, tile constants, launchers.
+// gfx950 (CDNA4) only: 64-lane wavefronts, DPP row operations, v_dot4 int8.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sks.h"
+
+namespace sks {
+
+// ---------------------------------------------------------------- constants
+constexpr int D = SKS_HEAD_DIM;          // 128
+constexpr int RANK = SKS_RANK;           // 64
+constexpr int SCORE_BIAS = 1 << 20;      // |score| <= 64*127*127 < 2^20
+constexpr int HIST1_BITS = 11;           // top bits of the 21-bit biased score
+constexpr int HIST1_BINS = 1 << HIST1_BITS;
+constexpr int HIST2_BITS = 10;           // low bits
+constexpr int HIST2_BINS = 1 << HIST2_BITS;
+constexpr int SCORE_CHUNK = 2048;        // tokens per score workgroup
+constexpr int TK_CHUNK = 4096;           // tokens per top-k filter workgroup
+constexpr int TK_SUB = 1024;             // tokens per filter wave (one candidate sub-list)
+constexpr int TK_MAX_SUBS = 8192;        // sub-lists per segment the final pass can index
+constexpr int ATTN_SPLIT = 256;          // attention entries per workgroup
+constexpr int ATTN_MAX_G = 8;            // query heads per KV head supported
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+// ---------------------------------------------------------------- geometry
+// Per-row geometry of the step (see sks.h): clamp the device length, then
+// derive far count, window start and effective k.
+struct RowGeom {
+  int L;      // tokens visible to the row
+  int n_far;  // far tokens / blocks
+  int ws;     // first exact-window token
+  int k_eff;  // selected far entries
+  int n_ent;  // k_eff + (L - ws): size of the attention set
+};
+
+__device__ __forceinline__ int clamp_len(int raw, int T_max, int R) {
+  int hi = T_max - R + 1;
+  if (hi < 0) hi = 0;
+  return raw < 0 ? 0 : (raw > hi ? hi : raw);
+}
+
+__device__ __forceinline__ RowGeom row_geom(int L0, int i, int window, int pool, int topk) {
+  RowGeom g;
+  g.L = L0 + i;
+  g.n_far = g.L > window ? (g.L - window) / pool : 0;
+  g.ws = g.n_far * pool;
+  g.k_eff = g.n_far < topk ? g.n_far : topk;
+  g.n_ent = g.k_eff + (g.L - g.ws);
+  return g;
+}
+
+// ---------------------------------------------------------------- numerics
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float f16_bits_to_float(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Round a finite double in the normal bf16 range to bfloat16, ties to even:
+// keep the top 7 explicit mantissa bits of the binary64 encoding.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned long long drop = 45;            // 52 - 7 explicit bits kept
+  unsigned long long lsb = (u >> drop) & 1ull;
+  u += ((1ull << (drop - 1)) - 1ull) + lsb;
+  u &= ~((1ull << drop) - 1ull);
+  float f = (float)__longlong_as_double((long long)u);   // exact
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+__device__ __forceinline__ int8_t quant_code(float y, float scale) {
+  float v = __builtin_rintf(y / scale);
+  v = fminf(fmaxf(v, -127.0f), 127.0f);
+  return (int8_t)(int)v;
+}
+
+// DPP lane permutations inside a row of 16 lanes (gfx9 encodings).
+constexpr int DPP_QUAD_XOR1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_MIRROR = 0x140;  // lane i <-> 15 - i
+constexpr int DPP_ROW_HMIRROR = 0x141; // lane i <-> 7 - i within each half row
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 4 lanes of a quad; every lane gets the total.
+__device__ __forceinline__ int quad_sum_i(int x) {
+  x += dpp_i<DPP_QUAD_XOR1>(x);
+  x += dpp_i<DPP_QUAD_XOR2>(x);
+  return x;
+}
+
+// Sum over the 16 lanes of a row; every lane gets the total.  The mirror
+// steps pair lanes into 4 classes {a, 7-a, 8+a, 15-a}; the quad steps then
+// combine one lane of each class.
+__device__ __forceinline__ float row16_sum_f(float x) {
+  x += dpp_f<DPP_ROW_MIRROR>(x);
+  x += dpp_f<DPP_ROW_HMIRROR>(x);
+  x += dpp_f<DPP_QUAD_XOR1>(x);
+  x += dpp_f<DPP_QUAD_XOR2>(x);
+  return x;
+}
+
+// ---------------------------------------------------------------- launchers
+struct Shape {
+  int B, R, Hkv, T_max, NB, window, topk, pool, dtype;
+};
+
+hipError_t launch_sketch_keys(const sks_kv &kv, const Shape &s, const float *basis,
+                              int basis_per_head, const float *key_scale, int t_begin,
+                              int t_end, int8_t *S, uint16_t *Kp, uint16_t *Vp,
+                              hipStream_t st);
+hipError_t launch_sketch_query(const uint16_t *q, int B, int R, int Hq, int Hkv,
+                               const float *basis, int basis_per_head, int8_t *qsk,
+                               float *qscale, hipStream_t st);
+hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
+                        const Shape &s, int32_t *scores, hipStream_t st);
+
+struct TopkWs {
+  int32_t *hist1;   // [nseg][HIST1_BINS]
+  int32_t *cnt;     // [nseg][nchunk]
+  int2 *cand;       // [nseg][nchunk * TK_CHUNK]
+  int nchunk;
+};
+size_t topk_ws_bytes(const Shape &s);
+TopkWs topk_ws_carve(const Shape &s, void *ws);
+hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shape &s,
+                       int32_t *idx, int32_t *n_sel, const TopkWs &w, hipStream_t st);
+
+size_t attn_ws_bytes(const Shape &s, int G);
+hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
+                       const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp,
+                       float sm_scale, float *out, float *lse, void *ws, hipStream_t st);
+
+hipError_t launch_gather(const sks_kv &kv, const Shape &s, const int32_t *idx,
+                         const uint16_t *Kp, const uint16_t *Vp, void *K_out, void *V_out,
+                         uint16_t *Ks_out, uint16_t *Vs_out, int32_t *n_out, hipStream_t st);
+
+}  // namespace sks

@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/sks.h declares, sizes workspaces, and rejects
+invalid arguments with an error code and text before launching anything.
+Only argument combinations that fail validation are called here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_sparse_sketch_amd import binding as sks
+from long_context_sparse_sketch_amd import configs as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sks.h")
+FAKE = 0x100000            # a non-NULL, aligned address: never dereferenced on failure paths
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sks.LIB_PATH):
+        from long_context_sparse_sketch_amd.build import build
+        build()
+    return sks.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sks_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("sks_sketch_build", "sks_sketch_score", "sks_topk_select", "sks_gather_pack",
+              "sks_sparse_decode_attn"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert names and set(names) == set(sks.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def kv(B=2, Hkv=4, D=128, T=1000, dtype=sks.KV_BF16, K=FAKE, V=FAKE, Ks=0, Vs=0, sl=FAKE):
+    return sks.KVDesc(B, Hkv, D, T, dtype, K, V, Ks or None, Vs or None, sl)
+
+
+def call_attn(L, k, p, Hq=8, ws_bytes=1 << 30, q=FAKE, out=FAKE, idx=FAKE, ws=FAKE):
+    return L.sks_sparse_decode_attn(q, Hq, ctypes.byref(k), ctypes.byref(p), idx, None, None,
+                                    ctypes.c_float(0.088), out, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("mut,code,word", [
+    (dict(D=64), sks.SKS_ERR_ARG, "D must be"),
+    (dict(B=0), sks.SKS_ERR_ARG, "B and Hkv"),
+    (dict(K=0), sks.SKS_ERR_ARG, "kv->K"),
+    (dict(K=FAKE + 4), sks.SKS_ERR_ARG, "aligned"),
+    (dict(sl=0), sks.SKS_ERR_ARG, "seq_len"),
+    (dict(dtype=7), sks.SKS_ERR_ARG, "dtype"),
+    (dict(dtype=sks.KV_I8), sks.SKS_ERR_ARG, "K_scale"),
+])
+def test_cache_description_errors(L, mut, code, word):
+    k = kv(**mut)
+    rc = call_attn(L, k, sks.params(64, 32))
+    assert rc == code
+    assert word in sks.last_error()
+
+
+@pytest.mark.parametrize("p,Hq,word", [
+    (sks.params(64, 32, rank=32), 8, "rank"),
+    (sks.params(64, 0), 8, "topk"),
+    (sks.params(64, 5000), 8, "topk"),
+    (sks.params(-1, 32), 8, "window"),
+    (sks.params(64, 32, pool=0), 8, "pool"),
+    (sks.params(64, 32, pool=65), 8, "pool"),
+    (sks.params(64, 32, rows=9), 8, "rows"),
+    (sks.params(64, 32), 6, "multiple"),
+    (sks.params(64, 32), 4 * 9, "<= 8"),
+])
+def test_parameter_errors(L, p, Hq, word):
+    assert call_attn(L, kv(), p, Hq=Hq) == sks.SKS_ERR_ARG
+    assert word in sks.last_error()
+
+
+def test_workspace_errors(L):
+    rc = call_attn(L, kv(), sks.params(64, 32), ws_bytes=16)
+    assert rc == sks.SKS_ERR_WORKSPACE and "workspace" in sks.last_error()
+    rc = call_attn(L, kv(), sks.params(64, 32), ws=0)
+    assert rc == sks.SKS_ERR_WORKSPACE
+
+
+def test_unsupported_int8_pooling(L):
+    k = kv(dtype=sks.KV_I8, Ks=FAKE, Vs=FAKE)
+    rc = call_attn(L, k, sks.params(64, 32, pool=4))
+    assert rc == sks.SKS_ERR_UNSUPPORTED
+
+
+def test_sketch_build_argument_errors(L):
+    k = kv()
+    p = sks.params(64, 32)
+    rc = L.sks_sketch_build(ctypes.byref(k), ctypes.byref(p), FAKE, 0, FAKE, 5, 2, FAKE, None,
+                            None, None)
+    assert rc == sks.SKS_ERR_ARG and "range" in sks.last_error()
+    rc = L.sks_sketch_build(ctypes.byref(k), ctypes.byref(p), FAKE, 0, FAKE, 0, 10, FAKE, FAKE,
+                            FAKE, None)
+    assert rc == sks.SKS_ERR_ARG and "NULL when pool == 1" in sks.last_error()
+    p4 = sks.params(64, 32, pool=4)
+    rc = L.sks_sketch_build(ctypes.byref(k), ctypes.byref(p4), FAKE, 0, FAKE, 0, 10, FAKE, None,
+                            None, None)
+    assert rc == sks.SKS_ERR_ARG and "Kp" in sks.last_error()
+
+
+def test_score_topk_query_gather_argument_errors(L):
+    k, p = kv(), sks.params(64, 32)
+    assert L.sks_sketch_score(None, FAKE, ctypes.byref(k), ctypes.byref(p), FAKE, None) == 1
+    assert "qsk" in sks.last_error()
+    assert L.sks_topk_select(FAKE, ctypes.byref(k), ctypes.byref(p), FAKE, None, FAKE, 8,
+                             None) == sks.SKS_ERR_WORKSPACE
+    assert L.sks_sketch_build_query(FAKE, 1, 1, 6, 4, FAKE, 0, FAKE, None, None) == 1
+    assert "multiple" in sks.last_error()
+    assert L.sks_gather_pack(ctypes.byref(k), ctypes.byref(p), FAKE, None, None, FAKE, FAKE,
+                             FAKE, None, FAKE, None) == 1
+    assert "NULL for bf16" in sks.last_error()
+
+
+@pytest.mark.parametrize("cfg", C.ALL, ids=lambda c: c.name)
+def test_workspace_sizes_cover_selection_and_attention(L, cfg):
+    k = kv(B=cfg.B, Hkv=cfg.Hkv, T=cfg.T_max,
+           dtype=sks.KV_I8 if cfg.kv_dtype == C.KV_I8 else sks.KV_BF16, Ks=FAKE, Vs=FAKE)
+    if cfg.kv_dtype != C.KV_I8:
+        k.K_scale = k.V_scale = None
+    p = sks.params(cfg.window, cfg.topk, cfg.pool, cfg.R)
+    nb = L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), cfg.Hq)
+    nseg = cfg.B * cfg.R * cfg.Hkv
+    NB = cfg.T_max // cfg.pool
+    # candidates (8 B per sketch row) dominate the selection workspace
+    assert nb >= nseg * NB * 8
+    nsplit = -(-(cfg.topk + cfg.window + cfg.pool - 1) // 256)
+    assert nb >= nseg * nsplit * cfg.g * (128 + 2) * 4
+    assert L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 0) == 0
+    assert L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 9 * cfg.Hkv) == 0

@@ -1,0 +1,26 @@
+"""bench.py's host-side contract (no GPU): more than one GPU is refused with a
+message, and the algorithmic byte count follows the row geometry."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_multi_gpu_request_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_bytes_of_the_250k_workload():
+    sys.path.insert(0, ROOT)
+    import bench
+    from long_context_sparse_sketch_amd import configs as C
+    sketch, gathered, small = bench.algorithmic_bytes(C.C3)
+    assert sketch == 8 * 4 * 245904 * 64                      # 503.6 MB
+    assert gathered == 8 * 4 * (2048 + 4096) * 2 * 256        # 100.7 MB
+    s5, g5, _ = bench.algorithmic_bytes(C.C5)
+    assert s5 == 4 * 8 * (65539 - 4096) * 64                  # one pass for the 3 rows
+    assert g5 == sum(4 * 8 * 6144 * 2 * 130 for _ in range(3))
