@@ -161,42 +161,63 @@ def main():
         layers[k % len(layers)].step(q)
     torch.cuda.synchronize()
 
-    # timed region: K whole steps, events around the dominant kernel of each
-    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # timed region: exactly K whole steps, nothing else on the stream
+    start, stop = ev(), ev()
     torch.cuda.synchronize()
     start.record(stream)
     for k in range(args.steps):
-        lay = layers[k % len(layers)]
-        lay.build_sketch(sks.APPEND, 0)
-        lay.query_sketch(q)
-        ev_a[2 * k].record(stream)
-        lay.score()
-        ev_a[2 * k + 1].record(stream)
-        lay.select()
-        lay.attend(q)
+        layers[k % len(layers)].step(q)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    score_ms = [ev_a[2 * k].elapsed_time(ev_a[2 * k + 1]) for k in range(args.steps)]
 
-    # attention kernel timing in its own pass (same stream, same rotation)
-    ev_t = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    # dominant kernel: K back-to-back launches (rotating replicas) between two
+    # events on the launch stream -> average launch duration
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for k in range(args.steps):
+        layers[k % len(layers)].score()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    score_avg_ms = e0.elapsed_time(e1) / args.steps
+    for lay in layers:                       # the extra histograms: back to zero at rest
+        sks.workspace_init(lay.ws)
+    # attention (gather + merged softmax) the same way, on each layer's last selection
+    e2, e3 = ev(), ev()
+    e2.record(stream)
+    for k in range(args.steps):
+        layers[k % len(layers)].attend(q)
+    e3.record(stream)
+    torch.cuda.synchronize()
+    attn_avg_ms = e2.elapsed_time(e3) / args.steps
+
+    # per-phase breakdown (events between the calls of each step; includes
+    # the events' own small overhead)
+    names = ("append_sketch", "query_sketch", "score", "topk", "attention")
+    evs = [[ev() for _ in range(len(names) + 1)] for _ in range(args.steps)]
     for k in range(args.steps):
         lay = layers[k % len(layers)]
+        e = evs[k]
+        e[0].record(stream)
+        lay.build_sketch(sks.APPEND, 0)
+        e[1].record(stream)
+        lay.query_sketch(q)
+        e[2].record(stream)
         lay.score()
+        e[3].record(stream)
         lay.select()
-        ev_t[2 * k].record(stream)
+        e[4].record(stream)
         lay.attend(q)
-        ev_t[2 * k + 1].record(stream)
+        e[5].record(stream)
     torch.cuda.synchronize()
-    attn_ms = [ev_t[2 * k].elapsed_time(ev_t[2 * k + 1]) for k in range(args.steps)]
+    phase_ms = {n: float(np.median([evs[k][j].elapsed_time(evs[k][j + 1])
+                                     for k in range(args.steps)])) for j, n in enumerate(names)}
 
     ms_per_step = total_ms / args.steps
     sketch_b, gather_b, small_b = algorithmic_bytes(cfg)
-    score_avg_ms = float(np.mean(score_ms))
-    attn_avg_ms = float(np.mean(attn_ms))
     achieved = sketch_b / (score_avg_ms * 1e-3) / 1e9
     line = {
         "metric": "decode-attn steps/s and achieved HBM GB/s (% peak) at 250K ctx, top-k 2048",
@@ -225,6 +246,7 @@ def main():
             "attn_GBps": gather_b / (attn_avg_ms * 1e-3) / 1e9,
             "score_plus_attn_GBps": (sketch_b + gather_b) / ((score_avg_ms + attn_avg_ms) * 1e-3) / 1e9,
             "step_GBps": (sketch_b + gather_b + small_b) / (ms_per_step * 1e-3) / 1e9,
+            "phase_ms_median": phase_ms,
         },
     }
     line["detail"]["score_plus_attn_frac"] = line["detail"]["score_plus_attn_GBps"] / HBM_PEAK_GBPS

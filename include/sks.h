@@ -76,6 +76,7 @@ enum sks_kv_dtype {
 #define SKS_MAX_ROWS 8
 #define SKS_MAX_POOL 64
 #define SKS_APPEND (-1)     /* t_begin value: sketch the current rows' tokens  */
+#define SKS_MAX_EXTENT (1 << 24) /* upper bound of window and topk               */
 
 /* One layer's KV cache. */
 typedef struct sks_kv {
@@ -93,8 +94,9 @@ typedef struct sks_kv {
 
 /* Selection parameters of the step. */
 typedef struct sks_params {
-  int32_t window;           /* exact sliding window W >= 0                      */
-  int32_t topk;             /* k >= 1 far entries per (sequence, row, KV head)  */
+  int32_t window;           /* exact sliding window, 0 <= W <= SKS_MAX_EXTENT   */
+  int32_t topk;             /* far entries per (sequence, row, KV head),
+                               1 <= k <= SKS_MAX_EXTENT (k >= n_far: all)      */
   int32_t pool;             /* far-field pooling ratio r, 1 <= r <= 64          */
   int32_t rank;             /* sketch rank, must be 64                          */
   int32_t rows;             /* query rows per sequence R, 1 <= R <= 8           */
@@ -109,10 +111,21 @@ const char *sks_last_error(void);
 /* HIP runtime version seen by the library (hipRuntimeGetVersion). */
 int32_t sks_runtime_version(void);
 
-/* Workspace bytes that sks_topk_select and sks_sparse_decode_attn need for
- * this shape (the same buffer may serve both; contents need no
- * initialisation and are clobbered).  Returns 0 on invalid arguments. */
+/* Workspace bytes that sks_sketch_score, sks_topk_select and
+ * sks_sparse_decode_attn need for this shape; one buffer serves the whole
+ * step.  Returns 0 on invalid arguments.
+ * The workspace starts with a region that must be ZERO AT REST (per-segment
+ * selection histograms): sks_sketch_score (with a workspace) and the
+ * selection add into it, and sks_topk_select returns it to zero.  Zero a new
+ * workspace once with sks_workspace_init.  A workspace that is not zero at
+ * rest costs time (the selection then falls back to a full pass over the
+ * scores), never correctness.  The rest is scratch, clobbered by each call.
+ * Calls that share one workspace must be ordered (same stream). */
 size_t sks_workspace_bytes(const sks_kv *kv, const sks_params *p, int32_t Hq);
+
+/* Zero-fill ws_bytes of a workspace on `stream` (a fill kernel, no memset
+ * node, so it may be captured in a graph). */
+int sks_workspace_init(void *ws, size_t ws_bytes, sks_stream_t stream);
 
 /* Key sketch build.  "What it took" (build the sketch) and the claims list
  * (rank-64 key sketch) of "8 agents x 250K context ...", plus the frozen
@@ -152,18 +165,26 @@ int sks_sketch_build_query(const uint16_t *q, int32_t B, int32_t R, int32_t Hq, 
  *   scores[b][i][h][t] = sum_c qsk[b][i][h][c] * S[b][h][t][c]   (exact int32)
  * for t < n_far of the row with the most far entries; one pass over S serves
  * all rows.  Entries past that are not written.
- * scores: [B][R][Hkv][NB] int32. */
+ * scores: [B][R][Hkv][NB] int32.
+ * ws (optional, may be NULL): a step workspace; when given, the call also
+ * accumulates the selection's level-1 histogram into it, and the following
+ * sks_topk_select on these scores is called with SKS_TOPK_HIST_READY. */
 int sks_sketch_score(const int8_t *qsk, const int8_t *S, const sks_kv *kv,
-                     const sks_params *p, int32_t *scores, sks_stream_t stream);
+                     const sks_params *p, int32_t *scores, void *ws, size_t ws_bytes,
+                     sks_stream_t stream);
 
 /* Top-k selection ("What it took": pick the top ~2K).  For every (b, i, h):
  * the k_eff far entries with the largest scores[b][i][h][0 .. n_far), the
  * lower index first among equal scores, written in ascending order to
  * idx[b][i][h][0 .. k_eff) and padded with -1 up to topk.
  * n_sel: [B][R][Hkv] int32 receives k_eff (may be NULL).
- * ws: at least sks_workspace_bytes(). */
+ * flags: 0, or SKS_TOPK_HIST_READY when sks_sketch_score produced these
+ *        scores with this workspace (its histogram is then reused).
+ * ws: at least sks_workspace_bytes(); its zero-at-rest region is returned to
+ *     zero. */
+#define SKS_TOPK_HIST_READY 1
 int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p,
-                    int32_t *idx, int32_t *n_sel, void *ws, size_t ws_bytes,
+                    int32_t flags, int32_t *idx, int32_t *n_sel, void *ws, size_t ws_bytes,
                     sks_stream_t stream);
 
 /* Gather/pack ("What it took": pack the picked tokens for the attention

@@ -21,9 +21,11 @@ KV_BF16, KV_I8 = 0, 1
 APPEND = -1
 HEAD_DIM, RANK = 128, 64
 
-EXPORTS = ("sks_last_error", "sks_runtime_version", "sks_workspace_bytes", "sks_sketch_build",
-           "sks_sketch_build_query", "sks_sketch_score", "sks_topk_select", "sks_gather_pack",
-           "sks_sparse_decode_attn")
+TOPK_HIST_READY = 1
+
+EXPORTS = ("sks_last_error", "sks_runtime_version", "sks_workspace_bytes", "sks_workspace_init",
+           "sks_sketch_build", "sks_sketch_build_query", "sks_sketch_score", "sks_topk_select",
+           "sks_gather_pack", "sks_sparse_decode_attn")
 
 
 class SksError(RuntimeError):
@@ -65,14 +67,16 @@ def lib():
         L.sks_runtime_version.argtypes = []
         L.sks_workspace_bytes.restype = sz
         L.sks_workspace_bytes.argtypes = [kvp, pp, i32]
+        L.sks_workspace_init.restype = ctypes.c_int
+        L.sks_workspace_init.argtypes = [vp, sz, vp]
         L.sks_sketch_build.restype = ctypes.c_int
         L.sks_sketch_build.argtypes = [kvp, pp, vp, i32, vp, i32, i32, vp, vp, vp, vp]
         L.sks_sketch_build_query.restype = ctypes.c_int
         L.sks_sketch_build_query.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp]
         L.sks_sketch_score.restype = ctypes.c_int
-        L.sks_sketch_score.argtypes = [vp, vp, kvp, pp, vp, vp]
+        L.sks_sketch_score.argtypes = [vp, vp, kvp, pp, vp, vp, sz, vp]
         L.sks_topk_select.restype = ctypes.c_int
-        L.sks_topk_select.argtypes = [vp, kvp, pp, vp, vp, vp, sz, vp]
+        L.sks_topk_select.argtypes = [vp, kvp, pp, i32, vp, vp, vp, sz, vp]
         L.sks_gather_pack.restype = ctypes.c_int
         L.sks_gather_pack.argtypes = [kvp, pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.sks_sparse_decode_attn.restype = ctypes.c_int
@@ -116,8 +120,16 @@ class Cache:
         return ctypes.byref(self.desc)
 
 
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def workspace_bytes(cache: Cache, p: Params, Hq: int) -> int:
     return lib().sks_workspace_bytes(cache.ref, ctypes.byref(p), Hq)
+
+
+def workspace_init(ws, stream=None):
+    _check(lib().sks_workspace_init(ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def sketch_build(cache: Cache, p: Params, basis, key_scale, S, t_begin=0, t_end=None, Kp=None,
@@ -135,15 +147,15 @@ def sketch_build_query(q, Hkv: int, basis, qsk, qscale=None, basis_per_head=Fals
                                         ptr(qsk), ptr(qscale), _stream(stream)))
 
 
-def sketch_score(qsk, S, cache: Cache, p: Params, scores, stream=None):
+def sketch_score(qsk, S, cache: Cache, p: Params, scores, ws=None, stream=None):
     _check(lib().sks_sketch_score(ptr(qsk), ptr(S), cache.ref, ctypes.byref(p), ptr(scores),
-                                  _stream(stream)))
+                                  ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def topk_select(scores, cache: Cache, p: Params, idx, n_sel, ws, stream=None):
-    _check(lib().sks_topk_select(ptr(scores), cache.ref, ctypes.byref(p), ptr(idx), ptr(n_sel),
-                                 ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                                 _stream(stream)))
+def topk_select(scores, cache: Cache, p: Params, idx, n_sel, ws, hist_ready=False, stream=None):
+    _check(lib().sks_topk_select(ptr(scores), cache.ref, ctypes.byref(p),
+                                 TOPK_HIST_READY if hist_ready else 0, ptr(idx), ptr(n_sel),
+                                 ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def gather_pack(cache: Cache, p: Params, idx, K_out, V_out, n_out, Kp=None, Vp=None,
@@ -159,6 +171,4 @@ def sparse_decode_attn(q, cache: Cache, p: Params, idx, out, ws, lse=None, Kp=No
     sm = 1.0 / math.sqrt(q.shape[3]) if sm_scale is None else sm_scale
     _check(lib().sks_sparse_decode_attn(ptr(q), Hq, cache.ref, ctypes.byref(p), ptr(idx),
                                         ptr(Kp), ptr(Vp), ctypes.c_float(sm), ptr(out), ptr(lse),
-                                        ptr(ws),
-                                        0 if ws is None else ws.numel() * ws.element_size(),
-                                        _stream(stream)))
+                                        ptr(ws), _nbytes(ws), _stream(stream)))

@@ -65,6 +65,26 @@ __global__ __launch_bounds__(AT_THREADS) void attn_split_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = lane >> 4, p = lane & 15;
   const int Hq = Hkv * G;
+  const int e_wave = split * ATTN_SPLIT + wave * AT_WAVE_ENTRIES;
+
+  // Descriptor of entry e_wave + lane: the row to gather (an index into the
+  // token rows, or the pooled rows when bit 1 of the flag is set) and whether
+  // it takes part.  Invalid entries point at row 0, which always exists, so
+  // the gathers below need no branches.
+  int my_row = 0, my_flag = 0;
+  {
+    const int e = e_wave + lane;
+    if (e < rg.k_eff) {
+      const int sel = idx[(size_t)seg * topk + e];
+      if ((unsigned)sel < (unsigned)rg.n_far) {
+        my_row = sel;
+        my_flag = POOLED ? 3 : 1;
+      }
+    } else if (e < rg.n_ent) {
+      my_row = rg.ws + (e - rg.k_eff);
+      my_flag = 1;
+    }
+  }
 
   // queries: dims [8p, 8p+8) of the G heads of this KV head
   uint4 qv[G];
@@ -89,49 +109,39 @@ __global__ __launch_bounds__(AT_THREADS) void attn_split_kernel(
     for (int d = 0; d < 8; ++d) acc[j][d] = 0.f;
   }
 
-  const int32_t *idx_row = idx + (size_t)seg * topk;
-  const size_t tok_base = ((size_t)b * Hkv + h) * T_max;
-  const size_t blk_base = ((size_t)b * Hkv + h) * NB;
-  const int e_wave = split * ATTN_SPLIT + wave * AT_WAVE_ENTRIES;
+  constexpr int EB = DT == SKS_KV_BF16 ? 2 : 1;           // bytes per element
+  const char *Kt = static_cast<const char *>(K) + ((size_t)b * Hkv + h) * T_max * D * EB;
+  const char *Vt = static_cast<const char *>(V) + ((size_t)b * Hkv + h) * T_max * D * EB;
+  const char *Kpb = reinterpret_cast<const char *>(Kp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
+  const char *Vpb = reinterpret_cast<const char *>(Vp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
+  const uint16_t *Kst = DT == SKS_KV_I8 ? Ks + ((size_t)b * Hkv + h) * T_max : nullptr;
+  const uint16_t *Vst = DT == SKS_KV_I8 ? Vs + ((size_t)b * Hkv + h) * T_max : nullptr;
 
+#pragma unroll
   for (int step = 0; step < AT_STEPS; ++step) {
-    const int e_step = e_wave + step * (4 * AT_U);
-    if (e_step >= rg.n_ent) break;                      // uniform across the wave
+    if (e_wave + step * (4 * AT_U) >= rg.n_ent) break;      // uniform across the wave
     uint4 kr[AT_U], vr[AT_U];
     float ksc[AT_U], vsc[AT_U];
     bool ok[AT_U];
 #pragma unroll
     for (int u = 0; u < AT_U; ++u) {
-      const int e = e_step + u * 4 + slot;
-      ok[u] = false;
-      size_t row = 0;
-      bool from_pool = false;
-      if (e < rg.k_eff) {
-        const int sel = idx_row[e];
-        ok[u] = (unsigned)sel < (unsigned)rg.n_far;
-        row = POOLED ? blk_base + (size_t)sel : tok_base + (size_t)sel;
-        from_pool = POOLED;
-      } else if (e < rg.n_ent) {
-        ok[u] = true;
-        row = tok_base + (size_t)(rg.ws + (e - rg.k_eff));
-      }
-      kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
-      ksc[u] = vsc[u] = 0.f;
-      if (ok[u]) {
-        if constexpr (DT == SKS_KV_BF16) {
-          const uint16_t *Kb = from_pool ? Kp : static_cast<const uint16_t *>(K);
-          const uint16_t *Vb = from_pool ? Vp : static_cast<const uint16_t *>(V);
-          kr[u] = *reinterpret_cast<const uint4 *>(Kb + row * D + 8 * p);
-          vr[u] = *reinterpret_cast<const uint4 *>(Vb + row * D + 8 * p);
-        } else {
-          const uint2 k8 = *reinterpret_cast<const uint2 *>(static_cast<const int8_t *>(K) + row * D + 8 * p);
-          const uint2 v8 = *reinterpret_cast<const uint2 *>(static_cast<const int8_t *>(V) + row * D + 8 * p);
-          kr[u] = make_uint4(k8.x, k8.y, 0, 0);
-          vr[u] = make_uint4(v8.x, v8.y, 0, 0);
-          ksc[u] = f16_bits_to_float(Ks[row]);
-          vsc[u] = f16_bits_to_float(Vs[row]);
-        }
+      const int src = step * (4 * AT_U) + u * 4 + slot;
+      const int r = __shfl(my_row, src);
+      const int f = __shfl(my_flag, src);
+      ok[u] = f & 1;
+      const bool pooled = POOLED && (f & 2);
+      const size_t off = (size_t)r * D * EB + 8 * p * EB;
+      if constexpr (DT == SKS_KV_BF16) {
+        kr[u] = *reinterpret_cast<const uint4 *>((pooled ? Kpb : Kt) + off);
+        vr[u] = *reinterpret_cast<const uint4 *>((pooled ? Vpb : Vt) + off);
+        ksc[u] = vsc[u] = 1.f;
+      } else {
+        const uint2 k8 = *reinterpret_cast<const uint2 *>(Kt + off);
+        const uint2 v8 = *reinterpret_cast<const uint2 *>(Vt + off);
+        kr[u] = make_uint4(k8.x, k8.y, 0, 0);
+        vr[u] = make_uint4(v8.x, v8.y, 0, 0);
+        ksc[u] = f16_bits_to_float(Kst[r]);
+        vsc[u] = f16_bits_to_float(Vst[r]);
       }
     }
 
@@ -149,20 +159,20 @@ __global__ __launch_bounds__(AT_THREADS) void attn_split_kernel(
       }
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        float s;
+        float sdot;
         if constexpr (DT == SKS_KV_BF16) {
-          s = dot2_bf16(qv[j].x, kr[u].x, 0.f);
-          s = dot2_bf16(qv[j].y, kr[u].y, s);
-          s = dot2_bf16(qv[j].z, kr[u].z, s);
-          s = dot2_bf16(qv[j].w, kr[u].w, s);
+          sdot = dot2_bf16(qv[j].x, kr[u].x, 0.f);
+          sdot = dot2_bf16(qv[j].y, kr[u].y, sdot);
+          sdot = dot2_bf16(qv[j].z, kr[u].z, sdot);
+          sdot = dot2_bf16(qv[j].w, kr[u].w, sdot);
         } else {
-          s = 0.f;
+          sdot = 0.f;
 #pragma unroll
-          for (int d = 0; d < 8; ++d) s = __builtin_fmaf(qf[j][d], kf[d], s);
+          for (int d = 0; d < 8; ++d) sdot = __builtin_fmaf(qf[j][d], kf[d], sdot);
         }
-        s = row16_sum_f(s);
-        if constexpr (DT == SKS_KV_I8) s *= ksc[u];
-        z[u][j] = ok[u] ? s * sm_log2 : NEG_INF;
+        sdot = row16_sum_f(sdot);
+        if constexpr (DT == SKS_KV_I8) sdot *= ksc[u];
+        z[u][j] = ok[u] ? sdot * sm_log2 : NEG_INF;
       }
     }
 
@@ -257,7 +267,10 @@ __global__ __launch_bounds__(AT_THREADS) void attn_split_kernel(
   }
 }
 
-// One workgroup of 128 threads per (segment, query head of the group).
+// One workgroup of 128 threads per (segment, query head of the group).  The
+// splits are merged in split order, MB at a time so that their loads are in
+// flight together; the order of operations is fixed by the shape.
+constexpr int MB = 8;
 __global__ __launch_bounds__(D) void attn_merge_kernel(const float2 *__restrict__ part_ml,
                                                        const float *__restrict__ part_acc,
                                                        int nsplit, int G, int Hkv,
@@ -267,19 +280,35 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float2 *__restrict_
   const int h = seg % Hkv, bi = seg / Hkv;
   const size_t orow = (size_t)bi * Hkv * G + (size_t)h * G + j;
   const size_t base = (size_t)seg * nsplit;
-  float M = NEG_INF;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(base + s) * G + j].x);
+  float M = NEG_INF, Lsum = 0.f, A = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += MB) {
+    float2 ml[MB];
+    float a[MB];
+#pragma unroll
+    for (int k = 0; k < MB; ++k) {
+      const int s = s0 + k;
+      ml[k] = s < nsplit ? part_ml[(base + s) * G + j] : make_float2(NEG_INF, 0.f);
+      a[k] = s < nsplit ? part_acc[((base + s) * G + j) * D + d] : 0.f;
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < MB; ++k) Mn = fmaxf(Mn, ml[k].x);
+    if (Mn == NEG_INF) continue;
+    const float wa = M == NEG_INF ? 0.f : exp2_fast(M - Mn);
+    Lsum *= wa;
+    A *= wa;
+#pragma unroll
+    for (int k = 0; k < MB; ++k) {
+      const float wt = ml[k].x == NEG_INF ? 0.f : exp2_fast(ml[k].x - Mn);
+      Lsum += ml[k].y * wt;
+      A += a[k] * wt;
+    }
+    M = Mn;
+  }
   if (M == NEG_INF) {
     out[orow * D + d] = 0.f;
     if (d == 0 && lse) lse[orow] = NEG_INF;
     return;
-  }
-  float Lsum = 0.f, A = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 ml = part_ml[(base + s) * G + j];
-    const float wt = ml.x == NEG_INF ? 0.f : exp2_fast(ml.x - M);
-    Lsum += ml.y * wt;
-    A += part_acc[((base + s) * G + j) * D + d] * wt;
   }
   out[orow * D + d] = A / Lsum;
   if (d == 0 && lse) lse[orow] = (M + __log2f(Lsum)) * 0.69314718055994530942f;
@@ -312,7 +341,7 @@ int attn_nsplit(const Shape &s) {
 
 }  // namespace
 
-size_t attn_ws_bytes(const Shape &s, int G) {
+size_t attn_scratch_bytes(const Shape &s, int G) {
   const size_t nseg = (size_t)s.B * s.R * s.Hkv;
   const size_t n = nseg * attn_nsplit(s) * G;
   return align_up(n * sizeof(float2), 256) + align_up(n * D * sizeof(float), 256);
@@ -320,13 +349,13 @@ size_t attn_ws_bytes(const Shape &s, int G) {
 
 hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
                        const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp,
-                       float sm_scale, float *out, float *lse, void *ws, hipStream_t st) {
+                       float sm_scale, float *out, float *lse, const TopkWs &w, hipStream_t st) {
   const int G = Hq / s.Hkv;
   const int nseg = s.B * s.R * s.Hkv;
   const int nsplit = attn_nsplit(s);
   const size_t n = (size_t)nseg * nsplit * G;
-  float2 *pml = static_cast<float2 *>(ws);
-  float *pacc = reinterpret_cast<float *>(static_cast<char *>(ws) + align_up(n * sizeof(float2), 256));
+  float2 *pml = reinterpret_cast<float2 *>(w.scratch);
+  float *pacc = reinterpret_cast<float *>(w.scratch + align_up(n * sizeof(float2), 256));
   const float sm_log2 = sm_scale * 1.4426950408889634f;
   dim3 grid(nsplit, nseg);
   switch (G) {

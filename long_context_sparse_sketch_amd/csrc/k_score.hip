@@ -9,6 +9,12 @@
 // loads in flight, does v_dot4 on its 16 bytes for every query row, and the
 // quad sums by DPP.  Lane p of a quad then writes the scores of unroll slots
 // p and p+4, so every store instruction writes 64 consecutive int32.
+//
+// Optionally (HIST) the kernel also builds the level-1 selection histogram
+// of each row (top 11 bits of the biased score, see k_topk.hip) in LDS while
+// the scores are in registers, and adds its non-zero bins to the workspace
+// histogram with integer atomics: the top-k pass then needs no extra read of
+// the scores to find its threshold bin.
 #include "sks_internal.h"
 
 namespace sks {
@@ -19,11 +25,12 @@ constexpr int SC_UNROLL = 8;                        // rows per lane-quad per st
 constexpr int SC_WAVE_STEP = 16 * SC_UNROLL;        // 128 rows per wave step
 constexpr int SC_BLOCK_STEP = SC_WAVE_STEP * (SC_THREADS / 64);   // 512
 
-template <int R>
+template <int R, bool HIST>
 __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     const int8_t *__restrict__ qsk, const int8_t *__restrict__ S,
-    const int32_t *__restrict__ seq_len, int32_t *__restrict__ scores, int Hkv, int T_max,
-    int NB, int window, int pool) {
+    const int32_t *__restrict__ seq_len, int32_t *__restrict__ scores,
+    int32_t *__restrict__ hist1, int Hkv, int T_max, int NB, int window, int pool, int topk) {
+  __shared__ int lh[HIST ? R * HIST1_BINS : 1];
   const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
   const int L0 = clamp_len(seq_len[b], T_max, R);
   const int Lmax = L0 + R - 1;
@@ -34,6 +41,20 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int quad = lane >> 2, part = lane & 3;
+  // per-row far counts (rows differ by one token each); a row whose top-k
+  // takes everything needs no histogram
+  int nf[R];
+  bool need_hist[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const RowGeom rg = row_geom(L0, i, window, pool, topk);
+    nf[i] = rg.n_far;
+    need_hist[i] = HIST && rg.k_eff < rg.n_far;
+  }
+  if (HIST) {
+    for (int k = threadIdx.x; k < R * HIST1_BINS; k += SC_THREADS) lh[k] = 0;
+    __syncthreads();
+  }
 
   int4 qv[R];
 #pragma unroll
@@ -74,6 +95,18 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
       const int t_hi = t_lo + 64;
       if (t_lo < c1) out[i][t_lo] = lo;
       if (t_hi < c1) out[i][t_hi] = hi;
+      if (HIST && need_hist[i]) {
+        if (t_lo < nf[i]) atomicAdd(&lh[i * HIST1_BINS + (biased_key(lo) >> HIST2_BITS)], 1);
+        if (t_hi < nf[i]) atomicAdd(&lh[i * HIST1_BINS + (biased_key(hi) >> HIST2_BITS)], 1);
+      }
+    }
+  }
+  if (HIST) {
+    __syncthreads();
+    for (int k = threadIdx.x; k < R * HIST1_BINS; k += SC_THREADS) {
+      const int v = lh[k];
+      const int i = k / HIST1_BINS;
+      if (v) atomicAdd(&hist1[((size_t)(b * R + i) * Hkv + h) * HIST1_BINS + (k % HIST1_BINS)], v);
     }
   }
 }
@@ -81,7 +114,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 }  // namespace
 
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
-                        const Shape &s, int32_t *scores, hipStream_t st) {
+                        const Shape &s, int32_t *scores, int32_t *hist1, hipStream_t st) {
   // the largest far count any row can have is (T_max - window) / pool <= NB
   long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   if (max_far <= 0) return hipSuccess;
@@ -89,8 +122,14 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
   switch (s.R) {
 #define SKS_SCORE_CASE(RR)                                                                     \
   case RR:                                                                                     \
-    score_kernel<RR><<<grid, SC_THREADS, 0, st>>>(qsk, S, seq_len, scores, s.Hkv, s.T_max,     \
-                                                  s.NB, s.window, s.pool);                     \
+    if (hist1)                                                                                 \
+      score_kernel<RR, true><<<grid, SC_THREADS, 0, st>>>(qsk, S, seq_len, scores, hist1,      \
+                                                          s.Hkv, s.T_max, s.NB, s.window,      \
+                                                          s.pool, s.topk);                     \
+    else                                                                                       \
+      score_kernel<RR, false><<<grid, SC_THREADS, 0, st>>>(qsk, S, seq_len, scores, nullptr,   \
+                                                           s.Hkv, s.T_max, s.NB, s.window,     \
+                                                           s.pool, s.topk);                    \
     break;
     SKS_SCORE_CASE(1)
     SKS_SCORE_CASE(2)

@@ -16,6 +16,7 @@ namespace sks {
 namespace {
 
 constexpr int KS_THREADS = 256;
+constexpr int SMALL_ROWS = 64;   // up to this many rows per (b, h): wave-per-row kernel
 
 // Project x (128 fp32 in registers) on the 64 basis rows and quantize.
 // Codes are written into the LDS row `dst` (64 bytes, 16 dwords).
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(KS_THREADS) void sketch_pool_kernel(
   if (threadIdx.x < n) {
     const size_t tok0 = (size_t)bh * T_max + (size_t)j * pool;
     const size_t out_row = (size_t)bh * NB + j;
-    const double inv = 1.0 / (double)pool;
+    const double dpool = (double)pool;
     float x[D];
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(KS_THREADS) void sketch_pool_kernel(
         uint16_t o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          o[e] = f64_to_bf16_rne(s[e] * inv);
+          o[e] = f64_to_bf16_rne(s[e] / dpool);   // exact sum, one rounding, then bf16
           if (which == 0) x[v * 8 + e] = __uint_as_float((uint32_t)o[e] << 16);
         }
         uint4 packed;
@@ -170,6 +171,70 @@ __global__ __launch_bounds__(KS_THREADS) void sketch_pool_kernel(
   }
   __syncthreads();
   flush_codes(codes, n, S, (size_t)bh * NB + j0);
+}
+
+// Few rows per (b, h) -- the per-step append of the rows' own tokens: one
+// wave per sketch row.  The 128-element key (or pooled block) is staged in
+// LDS, lane c dots basis row c with it, so the latency is that of one row
+// instead of one lane walking all 64 x 128 products.
+template <int DT>
+__global__ __launch_bounds__(64) void sketch_rows_small_kernel(
+    const void *__restrict__ K, const void *__restrict__ V, const uint16_t *__restrict__ Ks,
+    const int32_t *__restrict__ seq_len, const float *__restrict__ basis, int basis_per_head,
+    const float *__restrict__ key_scale, int Hkv, int T_max, int R, int NB, int pool, int append,
+    int t_begin, int t_end, int8_t *__restrict__ S, uint16_t *__restrict__ Kp,
+    uint16_t *__restrict__ Vp) {
+  __shared__ float x[D];
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
+  int j_lo, j_hi;
+  sketch_range(append, seq_len, b, T_max, R, pool, NB, t_begin, t_end, j_lo, j_hi);
+  const int j = j_lo + blockIdx.x;
+  if (j >= j_hi) return;
+  const int lane = threadIdx.x;
+  if (pool == 1) {
+    const size_t row = (size_t)bh * T_max + j;
+    float x0, x1;
+    if (DT == SKS_KV_BF16) {
+      const uint32_t w = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(K) + row * D)[lane];
+      x0 = bf16_lo(w);
+      x1 = bf16_hi(w);
+    } else {
+      const uint16_t w = reinterpret_cast<const uint16_t *>(static_cast<const int8_t *>(K) + row * D)[lane];
+      const float sc = f16_bits_to_float(Ks[row]);
+      x0 = (float)(int8_t)(w & 0xff) * sc;
+      x1 = (float)(int8_t)(w >> 8) * sc;
+    }
+    x[2 * lane] = x0;
+    x[2 * lane + 1] = x1;
+  } else {
+    // pooled block: fp64 mean of `pool` rows (exact for bf16), rounded once to bf16
+    const size_t tok0 = (size_t)bh * T_max + (size_t)j * pool;
+    const size_t out_row = (size_t)bh * NB + j;
+    const double dpool = (double)pool;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const uint16_t *src = static_cast<const uint16_t *>(which == 0 ? K : V);
+      double s0 = 0.0, s1 = 0.0;
+      for (int k = 0; k < pool; ++k) {
+        const uint32_t w = reinterpret_cast<const uint32_t *>(src + (tok0 + k) * D)[lane];
+        s0 += bf16_lo(w);
+        s1 += bf16_hi(w);
+      }
+      const uint16_t o0 = f64_to_bf16_rne(s0 / dpool), o1 = f64_to_bf16_rne(s1 / dpool);
+      reinterpret_cast<uint32_t *>((which == 0 ? Kp : Vp) + out_row * D)[lane] =
+          (uint32_t)o0 | ((uint32_t)o1 << 16);
+      if (which == 0) {
+        x[2 * lane] = __uint_as_float((uint32_t)o0 << 16);
+        x[2 * lane + 1] = __uint_as_float((uint32_t)o1 << 16);
+      }
+    }
+  }
+  __syncthreads();
+  const float *Prow = basis + (basis_per_head ? (size_t)h * RANK * D : 0) + (size_t)lane * D;
+  float y = 0.f;
+#pragma unroll 8
+  for (int d = 0; d < D; ++d) y = __builtin_fmaf(Prow[d], x[d], y);
+  S[((size_t)bh * NB + j) * RANK + lane] = quant_code(y, key_scale[h]);
 }
 
 // Query sketch: one wave per (b, i, h).  qbar = mean of the group's queries
@@ -215,6 +280,19 @@ hipError_t launch_sketch_keys(const sks_kv &kv, const Shape &s, const float *bas
   if (span <= 0) return hipSuccess;
   long nrows = s.pool == 1 ? span : span / s.pool + 1;
   if (nrows > s.NB) nrows = s.NB;
+  if (nrows <= SMALL_ROWS) {
+    // few rows per (b, h): one wave per row
+    dim3 g2((unsigned)nrows, s.B * s.Hkv);
+    if (s.dtype == SKS_KV_BF16)
+      sketch_rows_small_kernel<SKS_KV_BF16><<<g2, 64, 0, st>>>(
+          kv.K, kv.V, nullptr, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max, s.R,
+          s.NB, s.pool, append, t_begin, t_end, S, Kp, Vp);
+    else
+      sketch_rows_small_kernel<SKS_KV_I8><<<g2, 64, 0, st>>>(
+          kv.K, kv.V, kv.K_scale, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max,
+          s.R, s.NB, s.pool, append, t_begin, t_end, S, Kp, Vp);
+    return hipGetLastError();
+  }
   dim3 grid(ceil_div(nrows, KS_THREADS), s.B * s.Hkv);
   if (s.pool == 1) {
     if (s.dtype == SKS_KV_BF16)

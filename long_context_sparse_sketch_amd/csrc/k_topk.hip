@@ -4,19 +4,21 @@
 // the largest score, lower index first among equal scores, in ascending index
 // order, padded with -1.
 //
-// Scores fit in 21 bits once biased by 2^20 (|score| <= 64*127^2).  Radix
-// select on that key:
-//   1. hist:   2048-bin histogram of the top 11 bits (LDS, then integer
-//              atomics into global memory: order-independent, deterministic).
-//   2. filter: every workgroup finds the threshold bin b1 from the histogram
-//              and each wave compacts the candidates (bin >= b1) of its own
-//              1024-token sub-chunk IN ORDER (ballot + popcount), so the
-//              candidate list is index-ordered sub-chunk by sub-chunk.
-//   3. final:  one workgroup per segment: exact threshold T from a second
-//              1024-bin histogram over the low 10 bits of the boundary bin,
-//              then one ordered pass emitting score > T, plus the first
-//              (lowest-index) ties at T up to k.  Ordered block scans make the
-//              output ascending without any sort.
+// Scores fit in 21 bits once biased by 2^20 (|score| <= 64*127^2).
+//   level-1 histogram: 2048 bins of the top 11 bits, accumulated with integer
+//     atomics (order-independent, so deterministic) into a workspace region
+//     that is zero at rest.  Either the score kernel accumulates it while it
+//     streams the sketches, or topk_hist_kernel does it here.
+//   filter: every workgroup derives the threshold bin b1 from the histogram;
+//     each wave compacts the candidates (bin >= b1) of its 1024-token
+//     sub-chunk IN ORDER (ballot + popcount).
+//   final (one workgroup per segment): caches the candidates in LDS and runs
+//     an exact two-level radix select on them -- it never trusts the
+//     histogram beyond the filter's pruning: if fewer than k candidates came
+//     through (a histogram that was not zero at rest), it selects from the
+//     raw scores instead.  One ordered pass then emits score > T plus the
+//     lowest-index ties at T, ascending, without a sort.  It returns the
+//     segment's histogram to zero.
 #include "sks_internal.h"
 
 namespace sks {
@@ -24,6 +26,8 @@ namespace {
 
 constexpr int TK_THREADS = 256;
 constexpr int TF_THREADS = 1024;
+constexpr int TF_CACHE = 8192;                     // candidates cached in LDS
+constexpr int FILTER_ITERS = TK_SUB / 64;          // 16 loads in flight per lane
 static_assert(TK_CHUNK == TK_SUB * (TK_THREADS / 64), "one sub-chunk per wave");
 
 struct SegGeom {
@@ -41,11 +45,6 @@ __device__ __forceinline__ SegGeom seg_geom(int seg, const int32_t *seq_len, int
   g.n_far = rg.n_far;
   g.k_eff = rg.k_eff;
   return g;
-}
-
-__device__ __forceinline__ int biased_key(int s) {
-  int v = s + SCORE_BIAS;
-  return v < 0 ? 0 : (v > (1 << 21) - 1 ? (1 << 21) - 1 : v);
 }
 
 // Inclusive block-wide prefix sum; `tot` receives the block total.
@@ -75,12 +74,12 @@ __device__ int block_incl_scan(int v, int *scratch, int &tot) {
   return v + prefix;
 }
 
-// Largest bin b with sum_{b' >= b} hist[b'] >= need (requires total >= need).
-// Writes b to res[0] and sum_{b' > b} hist[b'] to res[1].
+// Largest bin b with sum_{b' >= b} hist[b'] >= need.  Writes b to res[0] and
+// sum_{b' > b} hist[b'] to res[1]; (0, 0) if the total is below need.
 __device__ void threshold_bin(const int *hist, int nbins, int need, int *scratch, int *res) {
   const int slice = nbins / blockDim.x;
   const int lo = threadIdx.x * slice;
-  if (threadIdx.x == 0) {                        // defined result even if total < need
+  if (threadIdx.x == 0) {
     res[0] = 0;
     res[1] = 0;
   }
@@ -88,7 +87,7 @@ __device__ void threshold_bin(const int *hist, int nbins, int need, int *scratch
   for (int k = 0; k < slice; ++k) v += hist[lo + k];
   int tot;
   const int incl = block_incl_scan(v, scratch, tot);
-  int above = tot - incl;                        // bins of higher-numbered slices
+  int above = tot - incl;
   if (above < need && above + v >= need) {
     for (int bb = lo + slice - 1; bb >= lo; --bb) {
       if (above + hist[bb] >= need) {
@@ -115,7 +114,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(
   __shared__ int lh[HIST1_BINS];
   const int seg = blockIdx.y;
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
-  if (g.k_eff >= g.n_far) return;               // everything selected: no histogram
+  if (g.k_eff >= g.n_far) return;               // everything selected: no histogram needed
   const int c0 = blockIdx.x * TK_CHUNK;
   if (c0 >= g.n_far) return;
   const int c1 = min(g.n_far, c0 + TK_CHUNK);
@@ -142,64 +141,57 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
   if (g.k_eff >= g.n_far) return;
   const int c0 = blockIdx.x * TK_CHUNK;
   if (c0 >= g.n_far) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = blockIdx.x * (TK_CHUNK / TK_SUB) + wave;
+  const int s0 = sub * TK_SUB;
+  const int s1 = min(g.n_far, s0 + TK_SUB);
+  const int32_t *row = scores + (size_t)seg * NB;
+  // issue this wave's score loads before waiting for the histogram
+  int keys[FILTER_ITERS];
+#pragma unroll
+  for (int r = 0; r < FILTER_ITERS; ++r) {
+    const int t = s0 + r * 64 + lane;
+    keys[r] = t < s1 ? biased_key(row[t]) : -1;
+  }
   const int32_t *gh = hist1 + (size_t)seg * HIST1_BINS;
   for (int k = threadIdx.x; k < HIST1_BINS; k += TK_THREADS) sh[k] = gh[k];
   __syncthreads();
   threshold_bin(sh, HIST1_BINS, g.k_eff, scratch, res);
   const int b1 = res[0];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = blockIdx.x * (TK_CHUNK / TK_SUB) + wave;
-  const int s0 = sub * TK_SUB;
   if (s0 >= g.n_far) return;
-  const int s1 = min(g.n_far, s0 + TK_SUB);
-  const int32_t *row = scores + (size_t)seg * NB;
   int2 *dst = cand + ((size_t)seg * n_sub_max + sub) * TK_SUB;
   int n = 0;
-  for (int t0 = s0; t0 < s1; t0 += 64) {
-    const int t = t0 + lane;
-    int key = 0;
-    bool f = false;
-    if (t < s1) {
-      key = biased_key(row[t]);
-      f = (key >> HIST2_BITS) >= b1;
-    }
+#pragma unroll
+  for (int r = 0; r < FILTER_ITERS; ++r) {
+    const bool f = keys[r] >= 0 && (keys[r] >> HIST2_BITS) >= b1;
     const unsigned long long m = __ballot(f);
-    if (f) {
-      const int pos = n + __popcll(m & ((1ull << lane) - 1ull));
-      dst[pos] = make_int2(t, key);
-    }
+    if (f) dst[n + __popcll(m & ((1ull << lane) - 1ull))] = make_int2(s0 + r * 64 + lane, keys[r]);
     n += __popcll(m);
   }
   if (lane == 0) cnt[(size_t)seg * n_sub_max + sub] = n;
 }
 
 __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
-    const int32_t *__restrict__ seq_len, const int32_t *__restrict__ hist1,
-    const int32_t *__restrict__ cnt, const int2 *__restrict__ cand, int n_sub_max, int R, int Hkv,
-    int T_max, int window, int pool, int topk, int32_t *__restrict__ idx,
-    int32_t *__restrict__ n_sel) {
+    const int32_t *__restrict__ scores, const int32_t *__restrict__ seq_len,
+    int32_t *__restrict__ hist1, const int32_t *__restrict__ cnt, const int2 *__restrict__ cand,
+    int n_sub_max, int R, int Hkv, int T_max, int NB, int window, int pool, int topk,
+    int32_t *__restrict__ idx, int32_t *__restrict__ n_sel) {
   __shared__ int h[HIST1_BINS];
   __shared__ int pre[TK_MAX_SUBS + 1];
+  __shared__ int2 cache[TF_CACHE];
   __shared__ int scratch[TF_THREADS / 64];
   __shared__ int res[2];
   const int seg = blockIdx.x;
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   int32_t *out = idx + (size_t)seg * topk;
+  // the filter has run: the histogram has done its job and returns to zero
+  int32_t *gh = hist1 + (size_t)seg * HIST1_BINS;
+  for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh[k] = 0;
   if (threadIdx.x == 0 && n_sel) n_sel[seg] = g.k_eff;
   if (g.k_eff >= g.n_far) {                      // every far entry is selected
     for (int j = threadIdx.x; j < topk; j += TF_THREADS) out[j] = j < g.n_far ? j : -1;
     return;
   }
-  // level 1: threshold bin and how many must come from it
-  const int32_t *gh = hist1 + (size_t)seg * HIST1_BINS;
-  for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) h[k] = gh[k];
-  __syncthreads();
-  threshold_bin(h, HIST1_BINS, g.k_eff, scratch, res);
-  const int b1 = res[0];
-  const int need1 = g.k_eff - res[1];
-  const int cnt_b1 = h[b1];
-  __syncthreads();
 
   // candidate list: exclusive prefix over the sub-chunk counts
   const int n_sub = (g.n_far + TK_SUB - 1) / TK_SUB;
@@ -215,93 +207,121 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
   }
   if (threadIdx.x == 0) pre[n_sub] = carry;
   __syncthreads();
-  const int m = carry;
+  // Fewer candidates than k means the histogram was not one of these scores
+  // (the workspace was not zero at rest): select from the raw scores instead.
+  const bool raw = carry < g.k_eff;
+  const int m = raw ? g.n_far : carry;
   const int2 *cseg = cand + (size_t)seg * n_sub_max * TK_SUB;
-  // ordinal -> candidate: last sub-chunk s with pre[s] <= o
-  auto locate = [&](int o) -> int2 {
-    int lo = 0, hi = n_sub;                      // pre[lo] <= o < pre[hi]
+  const int32_t *srow = scores + (size_t)seg * NB;
+  auto get = [&](int o) -> int2 {
+    if (raw) return make_int2(o, biased_key(srow[o]));
+    int lo = 0, hi = n_sub;                      // last sub-chunk s with pre[s] <= o
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (pre[mid] <= o) lo = mid; else hi = mid;
     }
     return cseg[(size_t)lo * TK_SUB + (o - pre[lo])];
   };
+  const bool cached = m <= TF_CACHE;
+  if (cached)
+    for (int o = threadIdx.x; o < m; o += TF_THREADS) cache[o] = get(o);
+  __syncthreads();
+  auto fetch = [&](int o) -> int2 { return cached ? cache[o] : get(o); };
 
-  // level 2: exact threshold key T and the number of ties at T to take
-  int T = b1 << HIST2_BITS;
-  int need2 = 0x7fffffff;
-  if (need1 < cnt_b1) {
-    for (int k = threadIdx.x; k < HIST2_BINS; k += TF_THREADS) h[k] = 0;
-    __syncthreads();
-    for (int o = threadIdx.x; o < m; o += TF_THREADS) {
-      const int2 c = locate(o);
-      if ((c.y >> HIST2_BITS) == b1) atomicAdd(&h[c.y & (HIST2_BINS - 1)], 1);
-    }
-    __syncthreads();
-    threshold_bin(h, HIST2_BINS, need1, scratch, res);
-    T |= res[0];
-    need2 = need1 - res[1];
+  // level 1 over the candidates
+  for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) h[k] = 0;
+  __syncthreads();
+  for (int o = threadIdx.x; o < m; o += TF_THREADS) atomicAdd(&h[fetch(o).y >> HIST2_BITS], 1);
+  __syncthreads();
+  threshold_bin(h, HIST1_BINS, g.k_eff, scratch, res);
+  const int b1 = res[0];
+  const int need1 = g.k_eff - res[1];
+  __syncthreads();
+  // level 2: low 10 bits inside bin b1
+  for (int k = threadIdx.x; k < HIST2_BINS; k += TF_THREADS) h[k] = 0;
+  __syncthreads();
+  for (int o = threadIdx.x; o < m; o += TF_THREADS) {
+    const int2 c = fetch(o);
+    if ((c.y >> HIST2_BITS) == b1) atomicAdd(&h[c.y & (HIST2_BINS - 1)], 1);
   }
+  __syncthreads();
+  threshold_bin(h, HIST2_BINS, need1, scratch, res);
+  const int T = (b1 << HIST2_BITS) | res[0];
+  const int need2 = need1 - res[1];              // ties at T to take, lowest index first
 
-  // ordered emission
-  int run_sel = 0, run_tie = 0;
+  // ordered emission: one scan of packed (greater-than, tie) counts per round
+  int run_gt = 0, run_tie = 0;
   for (int base = 0; base < m; base += TF_THREADS) {
     const int o = base + threadIdx.x;
     int2 c = make_int2(0, -1);
-    if (o < m) c = locate(o);
+    if (o < m) c = fetch(o);
+    const int gt = (o < m && c.y > T) ? 1 : 0;
     const int tie = (o < m && c.y == T) ? 1 : 0;
-    int tie_tot;
-    const int tie_rank = run_tie + block_incl_scan(tie, scratch, tie_tot) - tie;
-    const int sel = (o < m) && (c.y > T || (tie && tie_rank < need2)) ? 1 : 0;
-    int sel_tot;
-    const int pos = run_sel + block_incl_scan(sel, scratch, sel_tot) - sel;
+    const int packed = gt | (tie << 16);
+    int tot;
+    const int ex = block_incl_scan(packed, scratch, tot) - packed;
+    const int gt_before = run_gt + (ex & 0xffff), tie_before = run_tie + (ex >> 16);
+    const int sel = gt | ((tie && tie_before < need2) ? 1 : 0);
+    const int pos = gt_before + min(tie_before, need2);
     if (sel && pos < topk) out[pos] = c.x;
-    run_tie += tie_tot;
-    run_sel += sel_tot;
+    run_gt += tot & 0xffff;
+    run_tie += tot >> 16;
   }
   for (int j = g.k_eff + threadIdx.x; j < topk; j += TF_THREADS) out[j] = -1;
 }
 
 }  // namespace
 
-size_t topk_ws_bytes(const Shape &s) {
+size_t hist_region_bytes(const Shape &s) {
+  const size_t nseg = (size_t)s.B * s.R * s.Hkv;
+  return align_up(nseg * HIST1_BINS * 4, 256) + align_up(nseg * 4, 256);
+}
+
+size_t topk_scratch_bytes(const Shape &s) {
   const size_t nseg = (size_t)s.B * s.R * s.Hkv;
   const size_t n_sub = (size_t)ceil_div(s.NB, TK_SUB);
-  return align_up(nseg * HIST1_BINS * 4, 256) + align_up(nseg * n_sub * 4, 256) +
-         align_up(nseg * n_sub * TK_SUB * sizeof(int2), 256);
+  return align_up(nseg * n_sub * 4, 256) + align_up(nseg * n_sub * TK_SUB * sizeof(int2), 256);
 }
 
 TopkWs topk_ws_carve(const Shape &s, void *ws) {
   const size_t nseg = (size_t)s.B * s.R * s.Hkv;
   const size_t n_sub = (size_t)ceil_div(s.NB, TK_SUB);
-  char *p = static_cast<char *>(ws);
+  char *base = static_cast<char *>(ws);
   TopkWs w;
-  w.hist1 = reinterpret_cast<int32_t *>(p);
-  p += align_up(nseg * HIST1_BINS * 4, 256);
+  w.hist1 = reinterpret_cast<int32_t *>(base);
+  w.counters = reinterpret_cast<int32_t *>(base + align_up(nseg * HIST1_BINS * 4, 256));
+  char *p = base + hist_region_bytes(s);
+  w.scratch = p;
   w.cnt = reinterpret_cast<int32_t *>(p);
   p += align_up(nseg * n_sub * 4, 256);
   w.cand = reinterpret_cast<int2 *>(p);
-  w.nchunk = (int)n_sub;                        // sub-chunks per segment
+  w.nchunk = (int)n_sub;
   return w;
 }
 
+hipError_t launch_fill(int32_t *p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  fill_kernel<<<(int)std::min<size_t>(2048, (n + 255) / 256), 256, 0, st>>>(p, n, 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shape &s,
-                       int32_t *idx, int32_t *n_sel, const TopkWs &w, hipStream_t st) {
+                       bool hist_ready, int32_t *idx, int32_t *n_sel, const TopkWs &w,
+                       hipStream_t st) {
   const int nseg = s.B * s.R * s.Hkv;
-  const size_t nh = (size_t)nseg * HIST1_BINS;
-  fill_kernel<<<(int)std::min<size_t>(1024, (nh + 255) / 256), 256, 0, st>>>(w.hist1, nh, 0);
   long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   if (max_far > 0) {
     dim3 grid(ceil_div(max_far, TK_CHUNK), nseg);
-    topk_hist_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, s.R, s.Hkv, s.T_max,
-                                                  s.NB, s.window, s.pool, s.topk);
+    if (!hist_ready)
+      topk_hist_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, s.R, s.Hkv,
+                                                    s.T_max, s.NB, s.window, s.pool, s.topk);
     topk_filter_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.cnt, w.cand,
                                                     w.nchunk, s.R, s.Hkv, s.T_max, s.NB,
                                                     s.window, s.pool, s.topk);
   }
-  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(seq_len, w.hist1, w.cnt, w.cand, w.nchunk, s.R,
-                                                 s.Hkv, s.T_max, s.window, s.pool, s.topk, idx,
-                                                 n_sel);
+  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.cnt, w.cand,
+                                                 w.nchunk, s.R, s.Hkv, s.T_max, s.NB, s.window,
+                                                 s.pool, s.topk, idx, n_sel);
   return hipGetLastError();
 }
 

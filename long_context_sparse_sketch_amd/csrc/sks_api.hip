@@ -59,9 +59,10 @@ int check_shape(const sks_kv *kv, const sks_params *p, sks::Shape &s) {
   REQUIRE(p->pool >= 1 && p->pool <= SKS_MAX_POOL, "pool must be in [1, %d] (got %d)",
           SKS_MAX_POOL, p->pool);
   REQUIRE(kv->T_max / p->pool >= 1, "T_max / pool must be >= 1");
-  REQUIRE(p->window >= 0 && p->window <= kv->T_max, "window must be in [0, T_max] (got %d)",
-          p->window);
-  REQUIRE(p->topk >= 1 && p->topk <= kv->T_max, "topk must be in [1, T_max] (got %d)", p->topk);
+  REQUIRE(p->window >= 0 && p->window <= SKS_MAX_EXTENT, "window must be in [0, %d] (got %d)",
+          SKS_MAX_EXTENT, p->window);
+  REQUIRE(p->topk >= 1 && p->topk <= SKS_MAX_EXTENT, "topk must be in [1, %d] (got %d)",
+          SKS_MAX_EXTENT, p->topk);
   REQUIRE(kv->seq_len != nullptr, "kv->seq_len must not be NULL");
   REQUIRE(aligned(kv->seq_len, 4), "kv->seq_len must be 4-byte aligned");
   const long nseg = (long)kv->B * p->rows * kv->Hkv;
@@ -104,7 +105,20 @@ int check_heads(int Hq, int Hkv) {
   } while (0)
 
 size_t ws_bytes(const sks::Shape &s, int G) {
-  return std::max(sks::topk_ws_bytes(s), sks::attn_ws_bytes(s, G));
+  return sks::hist_region_bytes(s) +
+         std::max(sks::topk_scratch_bytes(s), sks::attn_scratch_bytes(s, G));
+}
+
+size_t topk_need(const sks::Shape &s) {
+  return sks::hist_region_bytes(s) + sks::topk_scratch_bytes(s);
+}
+
+int check_ws(const void *ws, size_t given, size_t need) {
+  if (!ws || given < need)
+    return fail(SKS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                ws ? given : (size_t)0);
+  if (!aligned(ws, 256)) return fail(SKS_ERR_ARG, "ws must be 256-byte aligned");
+  return SKS_OK;
 }
 
 }  // namespace
@@ -171,19 +185,33 @@ int sks_sketch_build_query(const uint16_t *q, int32_t B, int32_t R, int32_t Hq, 
                     "sks_sketch_build_query");
 }
 
+int sks_workspace_init(void *ws, size_t ws_bytes_given, sks_stream_t stream) {
+  REQUIRE(ws != nullptr, "ws must not be NULL");
+  REQUIRE(aligned(ws, 256), "ws must be 256-byte aligned");
+  return hip_status(sks::launch_fill(static_cast<int32_t *>(ws), ws_bytes_given / 4,
+                                     (hipStream_t)stream),
+                    "sks_workspace_init");
+}
+
 int sks_sketch_score(const int8_t *qsk, const int8_t *S, const sks_kv *kv, const sks_params *p,
-                     int32_t *scores, sks_stream_t stream) {
+                     int32_t *scores, void *ws, size_t ws_bytes_given, sks_stream_t stream) {
   sks::Shape s;
   TRY(check_shape(kv, p, s));
   REQUIRE_PTR(qsk, 16);
   REQUIRE_PTR(S, 16);
   REQUIRE_PTR(scores, 4);
-  return hip_status(sks::launch_score(qsk, S, kv->seq_len, s, scores, (hipStream_t)stream),
+  int32_t *hist = nullptr;
+  if (ws) {
+    TRY(check_ws(ws, ws_bytes_given, topk_need(s)));
+    hist = sks::topk_ws_carve(s, ws).hist1;
+  }
+  return hip_status(sks::launch_score(qsk, S, kv->seq_len, s, scores, hist, (hipStream_t)stream),
                     "sks_sketch_score");
 }
 
-int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p, int32_t *idx,
-                    int32_t *n_sel, void *ws, size_t ws_bytes_given, sks_stream_t stream) {
+int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p, int32_t flags,
+                    int32_t *idx, int32_t *n_sel, void *ws, size_t ws_bytes_given,
+                    sks_stream_t stream) {
   sks::Shape s;
   TRY(check_shape(kv, p, s));
   REQUIRE_PTR(scores, 4);
@@ -192,13 +220,11 @@ int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p
   if (sks::ceil_div(s.NB, sks::TK_SUB) > sks::TK_MAX_SUBS)
     return fail(SKS_ERR_UNSUPPORTED, "T_max / pool above %d is not supported by the selection",
                 sks::TK_MAX_SUBS * sks::TK_SUB);
-  const size_t need = sks::topk_ws_bytes(s);
-  if (!ws || ws_bytes_given < need)
-    return fail(SKS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
-                ws ? ws_bytes_given : (size_t)0);
-  if (!aligned(ws, 256)) return fail(SKS_ERR_ARG, "ws must be 256-byte aligned");
+  REQUIRE((flags & ~SKS_TOPK_HIST_READY) == 0, "unknown flags 0x%x", flags);
+  TRY(check_ws(ws, ws_bytes_given, topk_need(s)));
   const sks::TopkWs w = sks::topk_ws_carve(s, ws);
-  return hip_status(sks::launch_topk(scores, kv->seq_len, s, idx, n_sel, w, (hipStream_t)stream),
+  return hip_status(sks::launch_topk(scores, kv->seq_len, s, (flags & SKS_TOPK_HIST_READY) != 0,
+                                     idx, n_sel, w, (hipStream_t)stream),
                     "sks_topk_select");
 }
 
@@ -244,13 +270,10 @@ int sks_sparse_decode_attn(const uint16_t *q, int32_t Hq, const sks_kv *kv, cons
     REQUIRE_PTR(Vp, 16);
   }
   REQUIRE(sm_scale > 0.f && sm_scale < 1e30f, "sm_scale must be positive and finite");
-  const size_t need = sks::attn_ws_bytes(s, Hq / kv->Hkv);
-  if (!ws || ws_bytes_given < need)
-    return fail(SKS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
-                ws ? ws_bytes_given : (size_t)0);
-  if (!aligned(ws, 256)) return fail(SKS_ERR_ARG, "ws must be 256-byte aligned");
-  return hip_status(sks::launch_attn(q, Hq, *kv, s, idx, Kp, Vp, sm_scale, out, lse, ws,
-                                     (hipStream_t)stream),
+  TRY(check_ws(ws, ws_bytes_given,
+               sks::hist_region_bytes(s) + sks::attn_scratch_bytes(s, Hq / kv->Hkv)));
+  return hip_status(sks::launch_attn(q, Hq, *kv, s, idx, Kp, Vp, sm_scale, out, lse,
+                                     sks::topk_ws_carve(s, ws), (hipStream_t)stream),
                     "sks_sparse_decode_attn");
 }
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "sks.h"
 
 namespace sks {
@@ -75,6 +77,12 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
   return (uint16_t)(__float_as_uint(f) >> 16);
 }
 
+// Score -> unsigned 21-bit selection key (bias 2^20), clamped for safety.
+__device__ __forceinline__ int biased_key(int s) {
+  int v = s + SCORE_BIAS;
+  return v < 0 ? 0 : (v > (1 << 21) - 1 ? (1 << 21) - 1 : v);
+}
+
 __device__ __forceinline__ int8_t quant_code(float y, float scale) {
   float v = __builtin_rintf(y / scale);
   v = fminf(fmaxf(v, -127.0f), 127.0f);
@@ -126,24 +134,34 @@ hipError_t launch_sketch_keys(const sks_kv &kv, const Shape &s, const float *bas
 hipError_t launch_sketch_query(const uint16_t *q, int B, int R, int Hq, int Hkv,
                                const float *basis, int basis_per_head, int8_t *qsk,
                                float *qscale, hipStream_t st);
+// Workspace layout: [hist region | scratch].  The hist region (level-1
+// selection histograms [nseg][2048] and one merge counter per segment) is
+// zero at rest: the calls that use it return it to zero.  The scratch holds
+// the selection candidates or, later in the step, the attention partials.
+size_t hist_region_bytes(const Shape &s);
+size_t topk_scratch_bytes(const Shape &s);
+size_t attn_scratch_bytes(const Shape &s, int G);
+
+hipError_t launch_fill(int32_t *p, size_t n, hipStream_t st);
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
-                        const Shape &s, int32_t *scores, hipStream_t st);
+                        const Shape &s, int32_t *scores, int32_t *hist1, hipStream_t st);
 
 struct TopkWs {
-  int32_t *hist1;   // [nseg][HIST1_BINS]
-  int32_t *cnt;     // [nseg][nchunk]
-  int2 *cand;       // [nseg][nchunk * TK_CHUNK]
-  int nchunk;
+  int32_t *hist1;     // [nseg][HIST1_BINS], zero at rest
+  int32_t *counters;  // [nseg], zero at rest
+  char *scratch;      // start of the scratch area
+  int32_t *cnt;       // [nseg][nchunk]
+  int2 *cand;         // [nseg][nchunk * TK_SUB]
+  int nchunk;         // sub-lists per segment
 };
-size_t topk_ws_bytes(const Shape &s);
 TopkWs topk_ws_carve(const Shape &s, void *ws);
 hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shape &s,
-                       int32_t *idx, int32_t *n_sel, const TopkWs &w, hipStream_t st);
+                       bool hist_ready, int32_t *idx, int32_t *n_sel, const TopkWs &w,
+                       hipStream_t st);
 
-size_t attn_ws_bytes(const Shape &s, int G);
 hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
                        const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp,
-                       float sm_scale, float *out, float *lse, void *ws, hipStream_t st);
+                       float sm_scale, float *out, float *lse, const TopkWs &w, hipStream_t st);
 
 hipError_t launch_gather(const sks_kv &kv, const Shape &s, const int32_t *idx,
                          const uint16_t *Kp, const uint16_t *Vp, void *K_out, void *V_out,

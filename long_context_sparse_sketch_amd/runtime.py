@@ -6,7 +6,8 @@ the C-ABI calls of a step on the current stream:
 
     sks_sketch_build(APPEND)      sketch of the rows' own (just appended) tokens
     sks_sketch_build_query        rank-64 int8 query sketch per KV head
-    sks_sketch_score              int32 score of every far token / block
+    sks_sketch_score              int32 score of every far token / block, plus the
+                                  selection's level-1 histogram in the workspace
     sks_topk_select               top-k indices, ascending, -1 padded
     sks_sparse_decode_attn        gather + one merged softmax over far + window
 
@@ -68,6 +69,7 @@ class SparseDecodeLayer:
         if nbytes == 0:
             raise sks.SksError(sks.SKS_ERR_ARG, sks.last_error())
         self.ws = torch.empty((nbytes,), dtype=torch.uint8, device=cache.K.device)
+        sks.workspace_init(self.ws)          # the histogram region is zero at rest
         return self
 
     # ---- individual calls
@@ -79,13 +81,18 @@ class SparseDecodeLayer:
         sks.sketch_build_query(q, self.Hkv, self.basis, self.qsk, self.qscale,
                                self.basis_per_head, stream)
 
-    def score(self, stream=None, qsk=None, S=None):
+    def score(self, stream=None, qsk=None, S=None, fuse_hist=True):
+        """Scores; with fuse_hist the selection histogram is built in the same pass."""
         sks.sketch_score(self.qsk if qsk is None else qsk, self.S if S is None else S,
-                         self.cache, self.p, self.scores, stream)
+                         self.cache, self.p, self.scores, self.ws if fuse_hist else None, stream)
 
-    def select(self, stream=None, scores=None):
+    def select(self, stream=None, scores=None, hist_ready=None):
+        """Top-k; hist_ready defaults to True for the layer's own scores, which
+        `score()` produced with the fused histogram."""
+        if hist_ready is None:
+            hist_ready = scores is None
         sks.topk_select(self.scores if scores is None else scores, self.cache, self.p, self.idx,
-                        self.n_sel, self.ws, stream)
+                        self.n_sel, self.ws, hist_ready, stream)
 
     def attend(self, q, stream=None, idx=None, sm_scale=None):
         sks.sparse_decode_attn(q, self.cache, self.p, self.idx if idx is None else idx, self.out,

@@ -72,8 +72,9 @@ def test_cache_description_errors(L, mut, code, word):
 @pytest.mark.parametrize("p,Hq,word", [
     (sks.params(64, 32, rank=32), 8, "rank"),
     (sks.params(64, 0), 8, "topk"),
-    (sks.params(64, 5000), 8, "topk"),
+    (sks.params(64, (1 << 24) + 1), 8, "topk"),
     (sks.params(-1, 32), 8, "window"),
+    (sks.params((1 << 24) + 1, 32), 8, "window"),
     (sks.params(64, 32, pool=0), 8, "pool"),
     (sks.params(64, 32, pool=65), 8, "pool"),
     (sks.params(64, 32, rows=9), 8, "rows"),
@@ -115,10 +116,17 @@ def test_sketch_build_argument_errors(L):
 
 def test_score_topk_query_gather_argument_errors(L):
     k, p = kv(), sks.params(64, 32)
-    assert L.sks_sketch_score(None, FAKE, ctypes.byref(k), ctypes.byref(p), FAKE, None) == 1
+    assert L.sks_sketch_score(None, FAKE, ctypes.byref(k), ctypes.byref(p), FAKE, None, 0,
+                              None) == 1
     assert "qsk" in sks.last_error()
-    assert L.sks_topk_select(FAKE, ctypes.byref(k), ctypes.byref(p), FAKE, None, FAKE, 8,
+    assert L.sks_sketch_score(FAKE, FAKE, ctypes.byref(k), ctypes.byref(p), FAKE, FAKE, 8,
+                              None) == sks.SKS_ERR_WORKSPACE
+    assert L.sks_topk_select(FAKE, ctypes.byref(k), ctypes.byref(p), 0, FAKE, None, FAKE, 8,
                              None) == sks.SKS_ERR_WORKSPACE
+    assert L.sks_topk_select(FAKE, ctypes.byref(k), ctypes.byref(p), 6, FAKE, None, FAKE,
+                             1 << 30, None) == sks.SKS_ERR_ARG
+    assert "flags" in sks.last_error()
+    assert L.sks_workspace_init(None, 64, None) == sks.SKS_ERR_ARG
     assert L.sks_sketch_build_query(FAKE, 1, 1, 6, 4, FAKE, 0, FAKE, None, None) == 1
     assert "multiple" in sks.last_error()
     assert L.sks_gather_pack(ctypes.byref(k), ctypes.byref(p), FAKE, None, None, FAKE, FAKE,
@@ -136,8 +144,8 @@ def test_workspace_sizes_cover_selection_and_attention(L, cfg):
     nb = L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), cfg.Hq)
     nseg = cfg.B * cfg.R * cfg.Hkv
     NB = cfg.T_max // cfg.pool
-    # candidates (8 B per sketch row) dominate the selection workspace
-    assert nb >= nseg * NB * 8
+    # histograms (zero at rest) + candidates (8 B per sketch row)
+    assert nb >= nseg * 2048 * 4 + nseg * NB * 8
     nsplit = -(-(cfg.topk + cfg.window + cfg.pool - 1) // 256)
     assert nb >= nseg * nsplit * cfg.g * (128 + 2) * 4
     assert L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 0) == 0

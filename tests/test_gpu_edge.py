@@ -107,6 +107,7 @@ def test_topk_dense_ties_and_all_equal():
     idx = torch.empty((B, R, Hkv, k), dtype=torch.int32, device="cuda")
     n_sel = torch.empty((B, R, Hkv), dtype=torch.int32, device="cuda")
     ws = torch.empty((sks.workspace_bytes(cache, p, Hkv),), dtype=torch.uint8, device="cuda")
+    sks.workspace_init(ws)
     sks.topk_select(scores, cache, p, idx, n_sel, ws)
     got = idx.cpu().numpy()
     for b in range(B):

@@ -71,7 +71,7 @@ def test_scores_given_oracle_sketches(ctx):
     S = torch.from_numpy(arr["kcodes"]).cuda()
     qsk = torch.from_numpy(arr["qcode"]).cuda()
     g.layer.scores.fill_(0x7ABCDEF)
-    g.layer.score(qsk=qsk, S=S)
+    g.layer.score(qsk=qsk, S=S, fuse_hist=False)
     got = g.layer.scores.cpu().numpy()
     for (b, h), r in ref.items():
         for i in range(cfg.R):
@@ -90,6 +90,27 @@ def test_topk_given_oracle_scores(ctx):
     g.layer.select(scores=sc)
     assert np.array_equal(g.layer.idx.cpu().numpy(), arr["idx"])
     assert np.array_equal(g.layer.n_sel.cpu().numpy(), arr["n_sel"])
+    # the same scores through the fused-histogram path of the score kernel
+    g.layer.score(qsk=torch.from_numpy(arr["qcode"]).cuda(),
+                  S=torch.from_numpy(arr["kcodes"]).cuda())
+    g.layer.idx.fill_(-7)
+    g.layer.select()
+    assert np.array_equal(g.layer.idx.cpu().numpy(), arr["idx"])
+
+
+def test_topk_with_dirty_workspace(ctx):
+    """A workspace whose histogram region is not zero at rest costs time, never
+    correctness: the selection falls back to the raw scores."""
+    cfg, case, g, ref, arr = ctx
+    sc = torch.from_numpy(arr["scores"].astype(np.int32)).cuda()
+    for garbage in (0x01010101, -1, 0x7fffffff):
+        g.layer.ws.view(torch.int32)[: g.layer.ws.numel() // 4].fill_(garbage)
+        g.layer.idx.fill_(-7)
+        g.layer.select(scores=sc)
+        assert np.array_equal(g.layer.idx.cpu().numpy(), arr["idx"]), garbage
+    g.layer.idx.fill_(-7)
+    g.layer.select(scores=sc)                 # and the region is back to zero
+    assert np.array_equal(g.layer.idx.cpu().numpy(), arr["idx"])
 
 
 def test_attention_given_oracle_idx(ctx):
