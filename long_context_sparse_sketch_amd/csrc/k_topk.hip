@@ -9,9 +9,10 @@
 //     atomics (order-independent, so deterministic) into a workspace region
 //     that is zero at rest.  Either the score kernel accumulates it while it
 //     streams the sketches, or topk_hist_kernel does it here.
-//   filter: every workgroup derives the threshold bin b1 from the histogram;
-//     each wave compacts the candidates (bin >= b1) of its 1024-token
-//     sub-chunk IN ORDER (ballot + popcount).
+//   filter: every wave derives the threshold bin b1 from the histogram (after
+//     validating it: an invalid one makes every element a candidate) and
+//     compacts the candidates (bin >= b1) of its 1024-token sub-chunk IN ORDER
+//     (ballot + popcount).
 //   final (one workgroup per segment): caches the candidates in LDS and runs
 //     an exact two-level radix select on them -- it never trusts the
 //     histogram beyond the filter's pruning: if fewer than k candidates came
@@ -74,31 +75,57 @@ __device__ int block_incl_scan(int v, int *scratch, int &tot) {
   return v + prefix;
 }
 
-// Largest bin b with sum_{b' >= b} hist[b'] >= need.  Writes b to res[0] and
-// sum_{b' > b} hist[b'] to res[1]; (0, 0) if the total is below need.
-__device__ void threshold_bin(const int *hist, int nbins, int need, int *scratch, int *res) {
-  const int slice = nbins / blockDim.x;
-  const int lo = threadIdx.x * slice;
-  if (threadIdx.x == 0) {
-    res[0] = 0;
-    res[1] = 0;
+// Wave-level version over an LDS histogram of NBINS bins, no barriers: lane
+// l owns bins [l * NBINS/64, (l+1) * NBINS/64).  The histogram is first validated (every
+// bin in [0, n] and the total exactly n); an invalid one (a workspace that
+// was not zero at rest) yields bin 0, i.e. every element is a candidate, so
+// that all waves of all workgroups of a segment agree on the same threshold.
+// Returns the threshold bin; `above` receives sum_{b' > b} hist[b'].
+template <int NBINS = HIST1_BINS>
+__device__ int wave_threshold_bin(const int *hist, int need, int n, int &above) {
+  const int lane = threadIdx.x & 63;
+  constexpr int PER = NBINS / 64;
+  int v[PER];
+  long long sum = 0;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    v[k] = hist[lane * PER + k];
+    bad |= v[k] < 0 || v[k] > n;
+    sum += v[k];
   }
-  int v = 0;
-  for (int k = 0; k < slice; ++k) v += hist[lo + k];
-  int tot;
-  const int incl = block_incl_scan(v, scratch, tot);
-  int above = tot - incl;
-  if (above < need && above + v >= need) {
-    for (int bb = lo + slice - 1; bb >= lo; --bb) {
-      if (above + hist[bb] >= need) {
-        res[0] = bb;
-        res[1] = above;
-        break;
+  long long tot = sum;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+  const bool valid = !__any(bad) && tot == (long long)n;
+  above = 0;
+  if (!valid) return 0;
+  int incl = (int)sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  int ab = n - incl;                         // bins of higher lanes
+  int b = -1, ab_b = 0;
+  if (ab < need && ab + (int)sum >= need) {
+#pragma unroll
+    for (int k = PER - 1; k >= 0; --k) {
+      if (b < 0) {
+        if (ab + v[k] >= need) {
+          b = lane * PER + k;
+          ab_b = ab;
+        } else {
+          ab += v[k];
+        }
       }
-      above += hist[bb];
     }
   }
-  __syncthreads();
+  const unsigned long long who = __ballot(b >= 0);
+  if (who == 0) return 0;
+  const int src = __ffsll((long long)who) - 1;
+  above = __shfl(ab_b, src);
+  return __shfl(b, src);
 }
 
 __global__ void fill_kernel(int32_t *p, size_t n, int32_t v) {
@@ -134,38 +161,36 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
     const int32_t *__restrict__ hist1, int32_t *__restrict__ cnt, int2 *__restrict__ cand,
     int n_sub_max, int R, int Hkv, int T_max, int NB, int window, int pool, int topk) {
   __shared__ int sh[HIST1_BINS];
-  __shared__ int scratch[TK_THREADS / 64];
-  __shared__ int res[2];
   const int seg = blockIdx.y;
-  const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
-  if (g.k_eff >= g.n_far) return;
-  const int c0 = blockIdx.x * TK_CHUNK;
-  if (c0 >= g.n_far) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = blockIdx.x * (TK_CHUNK / TK_SUB) + wave;
   const int s0 = sub * TK_SUB;
-  const int s1 = min(g.n_far, s0 + TK_SUB);
   const int32_t *row = scores + (size_t)seg * NB;
-  // issue this wave's score loads before waiting for the histogram
-  int keys[FILTER_ITERS];
+  // Issue this wave's score loads and the histogram loads before the length
+  // is known: rows below NB are always in bounds.
+  int raw[FILTER_ITERS];
 #pragma unroll
   for (int r = 0; r < FILTER_ITERS; ++r) {
     const int t = s0 + r * 64 + lane;
-    keys[r] = t < s1 ? biased_key(row[t]) : -1;
+    raw[r] = t < NB ? row[t] : 0;
   }
   const int32_t *gh = hist1 + (size_t)seg * HIST1_BINS;
   for (int k = threadIdx.x; k < HIST1_BINS; k += TK_THREADS) sh[k] = gh[k];
+  const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   __syncthreads();
-  threshold_bin(sh, HIST1_BINS, g.k_eff, scratch, res);
-  const int b1 = res[0];
-  if (s0 >= g.n_far) return;
+  if (g.k_eff >= g.n_far || s0 >= g.n_far) return;
+  int above;
+  const int b1 = wave_threshold_bin(sh, g.k_eff, g.n_far, above);
+  const int s1 = min(g.n_far, s0 + TK_SUB);
   int2 *dst = cand + ((size_t)seg * n_sub_max + sub) * TK_SUB;
   int n = 0;
 #pragma unroll
   for (int r = 0; r < FILTER_ITERS; ++r) {
-    const bool f = keys[r] >= 0 && (keys[r] >> HIST2_BITS) >= b1;
+    const int t = s0 + r * 64 + lane;
+    const int key = biased_key(raw[r]);
+    const bool f = t < s1 && (key >> HIST2_BITS) >= b1;
     const unsigned long long m = __ballot(f);
-    if (f) dst[n + __popcll(m & ((1ull << lane) - 1ull))] = make_int2(s0 + r * 64 + lane, keys[r]);
+    if (f) dst[n + __popcll(m & ((1ull << lane) - 1ull))] = make_int2(t, key);
     n += __popcll(m);
   }
   if (lane == 0) cnt[(size_t)seg * n_sub_max + sub] = n;
@@ -176,15 +201,21 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
     int32_t *__restrict__ hist1, const int32_t *__restrict__ cnt, const int2 *__restrict__ cand,
     int n_sub_max, int R, int Hkv, int T_max, int NB, int window, int pool, int topk,
     int32_t *__restrict__ idx, int32_t *__restrict__ n_sel) {
-  __shared__ int h[HIST1_BINS];
+  __shared__ int h1[HIST1_BINS];
+  __shared__ int h2[HIST2_BINS];
   __shared__ int pre[TK_MAX_SUBS + 1];
   __shared__ int2 cache[TF_CACHE];
   __shared__ int scratch[TF_THREADS / 64];
-  __shared__ int res[2];
+  __shared__ int res[4];
   const int seg = blockIdx.x;
+  const int32_t *gc = cnt + (size_t)seg * n_sub_max;
+  // the first round of sub-list counts, loaded before the length is known
+  int cv0 = threadIdx.x < n_sub_max ? gc[threadIdx.x] : 0;
+  for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) h1[k] = 0;
+  for (int k = threadIdx.x; k < HIST2_BINS; k += TF_THREADS) h2[k] = 0;
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   int32_t *out = idx + (size_t)seg * topk;
-  // the filter has run: the histogram has done its job and returns to zero
+  // the filter has run: the segment's histogram returns to zero
   int32_t *gh = hist1 + (size_t)seg * HIST1_BINS;
   for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh[k] = 0;
   if (threadIdx.x == 0 && n_sel) n_sel[seg] = g.k_eff;
@@ -193,29 +224,28 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
     return;
   }
 
-  // candidate list: exclusive prefix over the sub-chunk counts
+  // candidate list: exclusive prefix over the sub-list counts
   const int n_sub = (g.n_far + TK_SUB - 1) / TK_SUB;
-  const int32_t *gc = cnt + (size_t)seg * n_sub_max;
   int carry = 0;
   for (int base = 0; base < n_sub; base += TF_THREADS) {
-    const int s = base + threadIdx.x;
-    const int v = s < n_sub ? gc[s] : 0;
+    const int sidx = base + threadIdx.x;
+    const int v = sidx < n_sub ? (base == 0 ? cv0 : gc[sidx]) : 0;
     int tot;
     const int incl = block_incl_scan(v, scratch, tot);
-    if (s < n_sub) pre[s] = carry + incl - v;
+    if (sidx < n_sub) pre[sidx] = carry + incl - v;
     carry += tot;
   }
   if (threadIdx.x == 0) pre[n_sub] = carry;
   __syncthreads();
-  // Fewer candidates than k means the histogram was not one of these scores
-  // (the workspace was not zero at rest): select from the raw scores instead.
+  // Fewer candidates than k means the filter's histogram was not one of these
+  // scores: select from the raw scores instead.
   const bool raw = carry < g.k_eff;
   const int m = raw ? g.n_far : carry;
   const int2 *cseg = cand + (size_t)seg * n_sub_max * TK_SUB;
   const int32_t *srow = scores + (size_t)seg * NB;
   auto get = [&](int o) -> int2 {
     if (raw) return make_int2(o, biased_key(srow[o]));
-    int lo = 0, hi = n_sub;                      // last sub-chunk s with pre[s] <= o
+    int lo = 0, hi = n_sub;                      // last sub-list s with pre[s] <= o
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (pre[mid] <= o) lo = mid; else hi = mid;
@@ -228,42 +258,61 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
   __syncthreads();
   auto fetch = [&](int o) -> int2 { return cached ? cache[o] : get(o); };
 
-  // level 1 over the candidates
-  for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) h[k] = 0;
+  // exact threshold key T: level 1 (top 11 bits), level 2 (low 10 bits)
+  for (int o = threadIdx.x; o < m; o += TF_THREADS) atomicAdd(&h1[fetch(o).y >> HIST2_BITS], 1);
   __syncthreads();
-  for (int o = threadIdx.x; o < m; o += TF_THREADS) atomicAdd(&h[fetch(o).y >> HIST2_BITS], 1);
-  __syncthreads();
-  threshold_bin(h, HIST1_BINS, g.k_eff, scratch, res);
-  const int b1 = res[0];
-  const int need1 = g.k_eff - res[1];
-  __syncthreads();
-  // level 2: low 10 bits inside bin b1
-  for (int k = threadIdx.x; k < HIST2_BINS; k += TF_THREADS) h[k] = 0;
-  __syncthreads();
-  for (int o = threadIdx.x; o < m; o += TF_THREADS) {
-    const int2 c = fetch(o);
-    if ((c.y >> HIST2_BITS) == b1) atomicAdd(&h[c.y & (HIST2_BINS - 1)], 1);
+  if (threadIdx.x < 64) {
+    int above;
+    const int b1 = wave_threshold_bin<HIST1_BINS>(h1, g.k_eff, m, above);
+    if (threadIdx.x == 0) {
+      res[0] = b1;
+      res[1] = g.k_eff - above;                  // still needed from bin b1
+    }
   }
   __syncthreads();
-  threshold_bin(h, HIST2_BINS, need1, scratch, res);
-  const int T = (b1 << HIST2_BITS) | res[0];
-  const int need2 = need1 - res[1];              // ties at T to take, lowest index first
+  const int b1 = res[0], need1 = res[1];
+  for (int o = threadIdx.x; o < m; o += TF_THREADS) {
+    const int2 c = fetch(o);
+    if ((c.y >> HIST2_BITS) == b1) atomicAdd(&h2[c.y & (HIST2_BINS - 1)], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    int above;
+    const int b2 = wave_threshold_bin<HIST2_BINS>(h2, need1, h1[b1], above);
+    if (threadIdx.x == 0) {
+      res[2] = (b1 << HIST2_BITS) | b2;
+      res[3] = need1 - above;                    // ties at T to take, lowest index first
+    }
+  }
+  __syncthreads();
+  const int T = res[2], need2 = res[3];
 
-  // ordered emission: one scan of packed (greater-than, tie) counts per round
+  // ordered emission: each thread owns 4 consecutive candidates per round,
+  // one block scan of packed (greater-than, tie) counts per round
   int run_gt = 0, run_tie = 0;
-  for (int base = 0; base < m; base += TF_THREADS) {
-    const int o = base + threadIdx.x;
-    int2 c = make_int2(0, -1);
-    if (o < m) c = fetch(o);
-    const int gt = (o < m && c.y > T) ? 1 : 0;
-    const int tie = (o < m && c.y == T) ? 1 : 0;
+  for (int base = 0; base < m; base += 4 * TF_THREADS) {
+    const int o0 = base + 4 * threadIdx.x;
+    int2 c[4];
+    int gt = 0, tie = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = o0 + q < m ? fetch(o0 + q) : make_int2(0, -1);
+      gt += c[q].y > T;
+      tie += c[q].y == T;
+    }
     const int packed = gt | (tie << 16);
     int tot;
     const int ex = block_incl_scan(packed, scratch, tot) - packed;
-    const int gt_before = run_gt + (ex & 0xffff), tie_before = run_tie + (ex >> 16);
-    const int sel = gt | ((tie && tie_before < need2) ? 1 : 0);
-    const int pos = gt_before + min(tie_before, need2);
-    if (sel && pos < topk) out[pos] = c.x;
+    int gt_before = run_gt + (ex & 0xffff), tie_before = run_tie + (ex >> 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool is_gt = c[q].y > T, is_tie = c[q].y == T;
+      const bool sel = is_gt || (is_tie && tie_before < need2);
+      const int pos = gt_before + min(tie_before, need2);
+      if (sel && pos < topk) out[pos] = c[q].x;
+      gt_before += is_gt;
+      tie_before += is_tie;
+    }
     run_gt += tot & 0xffff;
     run_tie += tot >> 16;
   }
