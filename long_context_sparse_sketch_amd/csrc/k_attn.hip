@@ -267,6 +267,295 @@ __global__ __launch_bounds__(AT_THREADS) void attn_split_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core version.  Per wave, tiles of 32 entries:
+//   QK:  S[16 heads][16 entries] = Q x K^T with v_mfma_f32_16x16x32_bf16, two
+//        sub-tiles of 16 entries (query heads padded to the 16 MFMA rows).
+//        A = Q: lane (n = lane%16, g = lane/16) holds head n, dims 32i+8g..+8;
+//        B = K^T: lane holds entry n, the same dims (16-byte gathers).
+//        C: lane holds S[4g + j][n], j = 0..3.
+//   softmax on that layout: each lane owns 4 heads x 1 entry; row max and
+//        sums over the 16 lanes of its DPP row.  The running max is only
+//        moved when a tile exceeds it by more than 2^RESCALE_SLACK (exact in
+//        real arithmetic; the ratio stays far inside fp32 range).
+//   PV:  O[16 heads][128] += P x V with the same MFMA, K = the 32 entries.
+//        P is split into bf16 hi + lo parts (two MFMAs) so its weights keep
+//        ~16 significant bits; V rows are staged row-major in wave-private
+//        LDS and read back per MFMA as 8 entries x 1 dim per lane.
+// All heads of the KV group share every gathered row; the 16-row MFMA shape
+// leaves 16 - G rows idle, which costs nothing here: the pass is bound by
+// the gathers.
+constexpr int AM_TILE = 32;
+constexpr int AM_WAVE_ENTRIES = ATTN_SPLIT / (AT_THREADS / 64);   // 64: two tiles
+constexpr int AM_TILES = AM_WAVE_ENTRIES / AM_TILE;
+constexpr int VROW = 132;                 // LDS V row stride in bf16 (264 B: conflict-free reads)
+constexpr float RESCALE_SLACK = 8.0f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// LDS written by some lanes of this wave and read by others: order the
+// accesses (in-order LDS queue per wave, no workgroup barrier needed).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// int8 codes -> bf16 (exact: |code| <= 127 needs 7 significant bits)
+__device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int sh) {
+  const float a = (float)(int8_t)(w >> sh), b = (float)(int8_t)(w >> (sh + 8));
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
+__device__ __forceinline__ float row16_max_f(float x) {
+  x = fmaxf(x, dpp_f<DPP_ROW_MIRROR>(x));
+  x = fmaxf(x, dpp_f<DPP_ROW_HMIRROR>(x));
+  x = fmaxf(x, dpp_f<DPP_QUAD_XOR1>(x));
+  x = fmaxf(x, dpp_f<DPP_QUAD_XOR2>(x));
+  return x;
+}
+
+template <int G, int DT, bool POOLED>
+__global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
+    const uint16_t *__restrict__ q, const void *__restrict__ K, const void *__restrict__ V,
+    const uint16_t *__restrict__ Ks, const uint16_t *__restrict__ Vs,
+    const int32_t *__restrict__ seq_len, const int32_t *__restrict__ idx,
+    const uint16_t *__restrict__ Kp, const uint16_t *__restrict__ Vp, float sm_log2, int R,
+    int Hkv, int T_max, int NB, int window, int pool, int topk, int nsplit,
+    float2 *__restrict__ part_ml, float *__restrict__ part_acc) {
+  static_assert(G >= 1 && G <= 16, "query heads per KV head");
+  __shared__ __align__(16) uint16_t s_v[4][AM_TILE * VROW];     // V tile per wave
+  __shared__ __align__(16) uint16_t s_p[4][2][16 * AM_TILE];    // P hi / lo [head][entry]
+  __shared__ float s_ml[4][16][2];
+  float *s_o = reinterpret_cast<float *>(&s_v[0][0]);          // reused after the loop
+
+  const int seg = blockIdx.y, split = blockIdx.x;
+  const int h = seg % Hkv, bi = seg / Hkv, i = bi % R, b = bi / R;
+  const int L0 = clamp_len(seq_len[b], T_max, R);
+  const RowGeom rg = row_geom(L0, i, window, pool, topk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int Hq = Hkv * G;
+  const int e_wave = split * ATTN_SPLIT + wave * AM_WAVE_ENTRIES;
+
+  // entry descriptors (see attn_split_kernel)
+  int my_row = 0, my_flag = 0;
+  {
+    const int e = e_wave + lane;
+    if (e < rg.k_eff) {
+      const int sel = idx[(size_t)seg * topk + e];
+      if ((unsigned)sel < (unsigned)rg.n_far) {
+        my_row = sel;
+        my_flag = POOLED ? 3 : 1;
+      }
+    } else if (e < rg.n_ent) {
+      my_row = rg.ws + (e - rg.k_eff);
+      my_flag = 1;
+    }
+  }
+
+  // Q as the A operand: head n, dims 32i + 8g .. +8 (zero rows past G)
+  u32x4_t qa[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    qa[c] = u32x4_t{0, 0, 0, 0};
+    if (n < G) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(
+          q + ((size_t)bi * Hq + (size_t)h * G + n) * D + 32 * c + 8 * g);
+      qa[c] = u32x4_t{w.x, w.y, w.z, w.w};
+    }
+  }
+
+  f32x4_t o[8];
+#pragma unroll
+  for (int blk = 0; blk < 8; ++blk) o[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m4[4], l4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m4[j] = NEG_INF;
+    l4[j] = 0.f;
+  }
+
+  constexpr int EB = DT == SKS_KV_BF16 ? 2 : 1;
+  const char *Kt = static_cast<const char *>(K) + ((size_t)b * Hkv + h) * T_max * D * EB;
+  const char *Vt = static_cast<const char *>(V) + ((size_t)b * Hkv + h) * T_max * D * EB;
+  const char *Kpb = reinterpret_cast<const char *>(Kp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
+  const char *Vpb = reinterpret_cast<const char *>(Vp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
+  const uint16_t *Kst = DT == SKS_KV_I8 ? Ks + ((size_t)b * Hkv + h) * T_max : nullptr;
+  const uint16_t *Vst = DT == SKS_KV_I8 ? Vs + ((size_t)b * Hkv + h) * T_max : nullptr;
+  uint16_t *sv = s_v[wave];
+
+#pragma unroll
+  for (int tile = 0; tile < AM_TILES; ++tile) {
+    const int e_tile = e_wave + tile * AM_TILE;
+    if (e_tile >= rg.n_ent) break;                         // uniform across the wave
+
+    // ---- gathers: K for the two QK sub-tiles, V rows of the tile
+    u32x4_t kb[2][4];
+    bool ok[2];
+    float ksc[2], vsc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int src = tile * AM_TILE + 16 * t + n;
+      const int r = __shfl(my_row, src), f = __shfl(my_flag, src);
+      ok[t] = f & 1;
+      const char *kbase = (POOLED && (f & 2)) ? Kpb : Kt;
+      const size_t off = (size_t)r * D * EB;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (DT == SKS_KV_BF16) {
+          const uint4 w = *reinterpret_cast<const uint4 *>(kbase + off + (32 * c + 8 * g) * 2);
+          kb[t][c] = u32x4_t{w.x, w.y, w.z, w.w};
+        } else {
+          const uint2 w = *reinterpret_cast<const uint2 *>(kbase + off + 32 * c + 8 * g);
+          kb[t][c] = u32x4_t{i8pair_to_bf16x2(w.x, 0), i8pair_to_bf16x2(w.x, 16),
+                             i8pair_to_bf16x2(w.y, 0), i8pair_to_bf16x2(w.y, 16)};
+        }
+      }
+      if constexpr (DT == SKS_KV_I8) {
+        ksc[t] = f16_bits_to_float(Kst[r]);
+        vsc[t] = f16_bits_to_float(Vst[r]);
+      } else {
+        ksc[t] = vsc[t] = 1.f;
+      }
+    }
+    // V: 32 rows x 16 chunks of 8 dims; lane takes chunk (x & 15) of row (x >> 4)
+    uint4 vv[8];
+#pragma unroll
+    for (int qq = 0; qq < 8; ++qq) {
+      const int x = qq * 64 + lane, ev = x >> 4, c = x & 15;
+      const int src = tile * AM_TILE + ev;
+      const int r = __shfl(my_row, src), f = __shfl(my_flag, src);
+      const char *vbase = (POOLED && (f & 2)) ? Vpb : Vt;
+      if constexpr (DT == SKS_KV_BF16) {
+        vv[qq] = *reinterpret_cast<const uint4 *>(vbase + (size_t)r * D * 2 + c * 16);
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2 *>(vbase + (size_t)r * D + c * 8);
+        vv[qq] = make_uint4(i8pair_to_bf16x2(w.x, 0), i8pair_to_bf16x2(w.x, 16),
+                            i8pair_to_bf16x2(w.y, 0), i8pair_to_bf16x2(w.y, 16));
+      }
+    }
+
+    // ---- QK on the matrix cores
+    f32x4_t sacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sacc[t] = mfma_bf16(qa[c], kb[t][c], sacc[t]);
+    }
+
+    // stage V (row-major, 8-byte stores: the padded stride is 8-byte aligned)
+#pragma unroll
+    for (int qq = 0; qq < 8; ++qq) {
+      const int x = qq * 64 + lane, ev = x >> 4, c = x & 15;
+      uint2 *dst = reinterpret_cast<uint2 *>(sv + ev * VROW + c * 8);
+      dst[0] = make_uint2(vv[qq].x, vv[qq].y);
+      dst[1] = make_uint2(vv[qq].z, vv[qq].w);
+    }
+
+    // ---- online softmax on the C layout (lane: heads 4g + j, entry n of each sub-tile)
+    float z[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z[t][j] = ok[t] ? sacc[t][j] * ksc[t] * sm_log2 : NEG_INF;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float mx = row16_max_f(fmaxf(z[0][j], z[1][j]));
+      if (mx > m4[j] + RESCALE_SLACK || (m4[j] == NEG_INF && mx != NEG_INF)) {
+        const float alpha = m4[j] == NEG_INF ? 0.f : exp2_fast(m4[j] - mx);
+        l4[j] *= alpha;
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) o[blk][j] *= alpha;
+        m4[j] = mx;
+      }
+    }
+    uint16_t *sp_hi = s_p[wave][0], *sp_lo = s_p[wave][1];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pv = (z[t][j] == NEG_INF) ? 0.f : exp2_fast(z[t][j] - m4[j]);
+        l4[j] += pv;
+        const float pw = pv * vsc[t];                       // value scale folded in
+        const uint32_t hi = f32_to_bf16_rne(pw);
+        const uint32_t lo = f32_to_bf16_rne(pw - __uint_as_float(hi << 16));
+        const int at = (4 * g + j) * AM_TILE + 16 * t + n;
+        sp_hi[at] = (uint16_t)hi;
+        sp_lo[at] = (uint16_t)lo;
+      }
+    }
+    wave_lds_sync();
+
+    // ---- PV on the matrix cores: A = P (head n, entries 8g..8g+8), B = V
+    const uint4 ph = *reinterpret_cast<const uint4 *>(sp_hi + n * AM_TILE + 8 * g);
+    const uint4 pl = *reinterpret_cast<const uint4 *>(sp_lo + n * AM_TILE + 8 * g);
+    const u32x4_t pa_hi = u32x4_t{ph.x, ph.y, ph.z, ph.w};
+    const u32x4_t pa_lo = u32x4_t{pl.x, pl.y, pl.z, pl.w};
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      const uint16_t *col = sv + (8 * g) * VROW + 16 * blk + n;
+      u32x4_t vb;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        vb[k] = (uint32_t)col[(2 * k) * VROW] | ((uint32_t)col[(2 * k + 1) * VROW] << 16);
+      o[blk] = mfma_bf16(pa_hi, vb, o[blk]);
+      o[blk] = mfma_bf16(pa_lo, vb, o[blk]);
+    }
+    wave_lds_sync();                                        // before the next tile reuses LDS
+  }
+
+  // denominators: sum the lane-partials over the 16 lanes of each DPP row
+#pragma unroll
+  for (int j = 0; j < 4; ++j) l4[j] = row16_sum_f(l4[j]);
+  __syncthreads();                                          // s_v is reused as s_o below
+  // wave partials to LDS: O rows 4g + j < G
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int hh = 4 * g + j;
+    if (hh < G) {
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) s_o[(wave * G + hh) * D + 16 * blk + n] = o[blk][j];
+      if (n == 0) {
+        s_ml[wave][hh][0] = m4[j];
+        s_ml[wave][hh][1] = l4[j];
+      }
+    }
+  }
+  __syncthreads();
+  // merge the 4 waves and write this split's partial
+  const size_t pbase = (size_t)seg * nsplit + split;
+  for (int x = threadIdx.x; x < G * D; x += AT_THREADS) {
+    const int j = x / D, d = x % D;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][j][0]);
+    float Lsum = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = s_ml[w][j][0];
+      const float wt = mw == NEG_INF ? 0.f : exp2_fast(mw - M);
+      Lsum += s_ml[w][j][1] * wt;
+      A += s_o[(w * G + j) * D + d] * wt;
+    }
+    part_acc[(pbase * G + j) * D + d] = A;
+    if (d == 0) part_ml[pbase * G + j] = make_float2(M, Lsum);
+  }
+}
+
 // One workgroup of 128 threads per (segment, query head of the group).  The
 // splits are merged in split order, MB at a time so that their loads are in
 // flight together; the order of operations is fixed by the shape.
@@ -318,7 +607,7 @@ template <int G, int DT, bool POOLED>
 void launch_split(dim3 grid, hipStream_t st, const uint16_t *q, const sks_kv &kv, const Shape &s,
                   const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp, float sm_log2,
                   int nsplit, float2 *pml, float *pacc) {
-  attn_split_kernel<G, DT, POOLED><<<grid, AT_THREADS, 0, st>>>(
+  attn_mfma_kernel<G, DT, POOLED><<<grid, AT_THREADS, 0, st>>>(
       q, kv.K, kv.V, kv.K_scale, kv.V_scale, kv.seq_len, idx, Kp, Vp, sm_log2, s.R, s.Hkv,
       s.T_max, s.NB, s.window, s.pool, s.topk, nsplit, pml, pacc);
 }

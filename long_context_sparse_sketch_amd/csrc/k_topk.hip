@@ -9,10 +9,10 @@
 //     atomics (order-independent, so deterministic) into a workspace region
 //     that is zero at rest.  Either the score kernel accumulates it while it
 //     streams the sketches, or topk_hist_kernel does it here.
-//   filter: every wave derives the threshold bin b1 from the histogram (after
-//     validating it: an invalid one makes every element a candidate) and
-//     compacts the candidates (bin >= b1) of its 1024-token sub-chunk IN ORDER
-//     (ballot + popcount).
+//   threshold (one wave per segment): validates the histogram and derives the
+//     threshold bin b1 (an invalid histogram makes every element a candidate).
+//   filter: each wave compacts the candidates (bin >= b1) of its 1024-token
+//     sub-chunk IN ORDER (ballot + popcount).
 //   final (one workgroup per segment): caches the candidates in LDS and runs
 //     an exact two-level radix select on them -- it never trusts the
 //     histogram beyond the filter's pruning: if fewer than k candidates came
@@ -81,25 +81,31 @@ __device__ int block_incl_scan(int v, int *scratch, int &tot) {
 // was not zero at rest) yields bin 0, i.e. every element is a candidate, so
 // that all waves of all workgroups of a segment agree on the same threshold.
 // Returns the threshold bin; `above` receives sum_{b' > b} hist[b'].
-template <int NBINS = HIST1_BINS>
-__device__ int wave_threshold_bin(const int *hist, int need, int n, int &above) {
+// LDS histograms are stored padded (see hpad) so that 64 lanes reading their
+// contiguous bins hit distinct banks.
+template <int NBINS>
+__device__ __forceinline__ int hpad(int b) { return b + b / (NBINS / 64); }
+template <int NBINS>
+constexpr int hpad_size() { return NBINS + 64; }
+
+// Threshold search over a histogram held in registers, lane l holding bins
+// [l*PER, (l+1)*PER) in v[].  No barriers.  Returns the bin b with
+// sum_{b' >= b} >= need > sum_{b' > b}; `above` receives sum_{b' > b}.
+template <int PER>
+__device__ int wave_threshold_regs(const int (&v)[PER], int need, int n, int &above) {
   const int lane = threadIdx.x & 63;
-  constexpr int PER = NBINS / 64;
-  int v[PER];
   long long sum = 0;
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    v[k] = hist[lane * PER + k];
     bad |= v[k] < 0 || v[k] > n;
     sum += v[k];
   }
   long long tot = sum;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
-  const bool valid = !__any(bad) && tot == (long long)n;
   above = 0;
-  if (!valid) return 0;
+  if (__any(bad) || tot != (long long)n) return 0;
   int incl = (int)sum;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -126,6 +132,20 @@ __device__ int wave_threshold_bin(const int *hist, int need, int n, int &above) 
   const int src = __ffsll((long long)who) - 1;
   above = __shfl(ab_b, src);
   return __shfl(b, src);
+}
+
+// Same search over a padded LDS histogram of NBINS bins.  The histogram is
+// validated first (every bin in [0, n], total exactly n); an invalid one (a
+// workspace that was not zero at rest) yields bin 0, i.e. every element is a
+// candidate, the same answer for every reader of the same histogram.
+template <int NBINS>
+__device__ int wave_threshold_bin(const int *hist, int need, int n, int &above) {
+  constexpr int PER = NBINS / 64;
+  const int lane = threadIdx.x & 63;
+  int v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) v[k] = hist[hpad<NBINS>(lane * PER + k)];
+  return wave_threshold_regs<PER>(v, need, n, above);
 }
 
 __global__ void fill_kernel(int32_t *p, size_t n, int32_t v) {
@@ -156,31 +176,50 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(
     if (lh[k]) atomicAdd(&gh[k], lh[k]);
 }
 
+// One wave per segment: validate the level-1 histogram and store the
+// threshold bin b1 once (0 when every element must be a candidate).  Lane l
+// loads its 32 contiguous bins as 8 independent 16-byte loads.
+__global__ __launch_bounds__(64) void topk_threshold_kernel(
+    const int32_t *__restrict__ seq_len, const int32_t *__restrict__ hist1,
+    int32_t *__restrict__ thr, int R, int Hkv, int T_max, int window, int pool, int topk) {
+  constexpr int PER = HIST1_BINS / 64;
+  const int seg = blockIdx.x, lane = threadIdx.x;
+  const int4 *gh = reinterpret_cast<const int4 *>(hist1 + (size_t)seg * HIST1_BINS + lane * PER);
+  int v[PER];
+#pragma unroll
+  for (int k = 0; k < PER / 4; ++k) {
+    const int4 w = gh[k];
+    v[4 * k] = w.x;
+    v[4 * k + 1] = w.y;
+    v[4 * k + 2] = w.z;
+    v[4 * k + 3] = w.w;
+  }
+  const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
+  int b1 = 0, above;
+  if (g.k_eff < g.n_far) b1 = wave_threshold_regs<PER>(v, g.k_eff, g.n_far, above);
+  if (lane == 0) thr[seg] = b1;
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
     const int32_t *__restrict__ scores, const int32_t *__restrict__ seq_len,
-    const int32_t *__restrict__ hist1, int32_t *__restrict__ cnt, int2 *__restrict__ cand,
+    const int32_t *__restrict__ thr, int32_t *__restrict__ cnt, int2 *__restrict__ cand,
     int n_sub_max, int R, int Hkv, int T_max, int NB, int window, int pool, int topk) {
-  __shared__ int sh[HIST1_BINS];
   const int seg = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = blockIdx.x * (TK_CHUNK / TK_SUB) + wave;
   const int s0 = sub * TK_SUB;
   const int32_t *row = scores + (size_t)seg * NB;
-  // Issue this wave's score loads and the histogram loads before the length
-  // is known: rows below NB are always in bounds.
+  // Issue this wave's score loads before the length is known: rows below NB
+  // are always in bounds.
   int raw[FILTER_ITERS];
 #pragma unroll
   for (int r = 0; r < FILTER_ITERS; ++r) {
     const int t = s0 + r * 64 + lane;
     raw[r] = t < NB ? row[t] : 0;
   }
-  const int32_t *gh = hist1 + (size_t)seg * HIST1_BINS;
-  for (int k = threadIdx.x; k < HIST1_BINS; k += TK_THREADS) sh[k] = gh[k];
+  const int b1 = thr[seg];
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
-  __syncthreads();
-  if (g.k_eff >= g.n_far || s0 >= g.n_far) return;
-  int above;
-  const int b1 = wave_threshold_bin(sh, g.k_eff, g.n_far, above);
+  if (g.k_eff >= g.n_far || s0 >= g.n_far) return;   // uniform per wave
   const int s1 = min(g.n_far, s0 + TK_SUB);
   int2 *dst = cand + ((size_t)seg * n_sub_max + sub) * TK_SUB;
   int n = 0;
@@ -201,8 +240,8 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
     int32_t *__restrict__ hist1, const int32_t *__restrict__ cnt, const int2 *__restrict__ cand,
     int n_sub_max, int R, int Hkv, int T_max, int NB, int window, int pool, int topk,
     int32_t *__restrict__ idx, int32_t *__restrict__ n_sel) {
-  __shared__ int h1[HIST1_BINS];
-  __shared__ int h2[HIST2_BINS];
+  __shared__ int h1[hpad_size<HIST1_BINS>()];
+  __shared__ int h2[hpad_size<HIST2_BINS>()];
   __shared__ int pre[TK_MAX_SUBS + 1];
   __shared__ int2 cache[TF_CACHE];
   __shared__ int scratch[TF_THREADS / 64];
@@ -211,8 +250,8 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
   const int32_t *gc = cnt + (size_t)seg * n_sub_max;
   // the first round of sub-list counts, loaded before the length is known
   int cv0 = threadIdx.x < n_sub_max ? gc[threadIdx.x] : 0;
-  for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) h1[k] = 0;
-  for (int k = threadIdx.x; k < HIST2_BINS; k += TF_THREADS) h2[k] = 0;
+  for (int k = threadIdx.x; k < hpad_size<HIST1_BINS>(); k += TF_THREADS) h1[k] = 0;
+  for (int k = threadIdx.x; k < hpad_size<HIST2_BINS>(); k += TF_THREADS) h2[k] = 0;
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   int32_t *out = idx + (size_t)seg * topk;
   // the filter has run: the segment's histogram returns to zero
@@ -253,13 +292,27 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
     return cseg[(size_t)lo * TK_SUB + (o - pre[lo])];
   };
   const bool cached = m <= TF_CACHE;
-  if (cached)
-    for (int o = threadIdx.x; o < m; o += TF_THREADS) cache[o] = get(o);
+  if (cached) {
+    // all lookups first, then all loads in flight together, then the stores
+    constexpr int PERT = TF_CACHE / TF_THREADS;
+    int2 tmp[PERT];
+#pragma unroll
+    for (int k = 0; k < PERT; ++k) {
+      const int o = threadIdx.x + k * TF_THREADS;
+      if (o < m) tmp[k] = get(o);
+    }
+#pragma unroll
+    for (int k = 0; k < PERT; ++k) {
+      const int o = threadIdx.x + k * TF_THREADS;
+      if (o < m) cache[o] = tmp[k];
+    }
+  }
   __syncthreads();
   auto fetch = [&](int o) -> int2 { return cached ? cache[o] : get(o); };
 
   // exact threshold key T: level 1 (top 11 bits), level 2 (low 10 bits)
-  for (int o = threadIdx.x; o < m; o += TF_THREADS) atomicAdd(&h1[fetch(o).y >> HIST2_BITS], 1);
+  for (int o = threadIdx.x; o < m; o += TF_THREADS)
+    atomicAdd(&h1[hpad<HIST1_BINS>(fetch(o).y >> HIST2_BITS)], 1);
   __syncthreads();
   if (threadIdx.x < 64) {
     int above;
@@ -273,12 +326,12 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
   const int b1 = res[0], need1 = res[1];
   for (int o = threadIdx.x; o < m; o += TF_THREADS) {
     const int2 c = fetch(o);
-    if ((c.y >> HIST2_BITS) == b1) atomicAdd(&h2[c.y & (HIST2_BINS - 1)], 1);
+    if ((c.y >> HIST2_BITS) == b1) atomicAdd(&h2[hpad<HIST2_BINS>(c.y & (HIST2_BINS - 1))], 1);
   }
   __syncthreads();
   if (threadIdx.x < 64) {
     int above;
-    const int b2 = wave_threshold_bin<HIST2_BINS>(h2, need1, h1[b1], above);
+    const int b2 = wave_threshold_bin<HIST2_BINS>(h2, need1, h1[hpad<HIST1_BINS>(b1)], above);
     if (threadIdx.x == 0) {
       res[2] = (b1 << HIST2_BITS) | b2;
       res[3] = need1 - above;                    // ties at T to take, lowest index first
@@ -364,7 +417,9 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
     if (!hist_ready)
       topk_hist_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, s.R, s.Hkv,
                                                     s.T_max, s.NB, s.window, s.pool, s.topk);
-    topk_filter_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.cnt, w.cand,
+    topk_threshold_kernel<<<nseg, 64, 0, st>>>(seq_len, w.hist1, w.counters, s.R, s.Hkv,
+                                               s.T_max, s.window, s.pool, s.topk);
+    topk_filter_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.counters, w.cnt, w.cand,
                                                     w.nchunk, s.R, s.Hkv, s.T_max, s.NB,
                                                     s.window, s.pool, s.topk);
   }

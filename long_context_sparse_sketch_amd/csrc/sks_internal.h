@@ -20,7 +20,7 @@ constexpr int HIST1_BITS = 11;           // top bits of the 21-bit biased score
 constexpr int HIST1_BINS = 1 << HIST1_BITS;
 constexpr int HIST2_BITS = 10;           // low bits
 constexpr int HIST2_BINS = 1 << HIST2_BITS;
-constexpr int SCORE_CHUNK = 2048;        // tokens per score workgroup
+constexpr int SCORE_CHUNK = 1024;        // tokens per score workgroup
 constexpr int TK_CHUNK = 4096;           // tokens per top-k filter workgroup
 constexpr int TK_SUB = 1024;             // tokens per filter wave (one candidate sub-list)
 constexpr int TK_MAX_SUBS = 8192;        // sub-lists per segment the final pass can index
@@ -134,9 +134,9 @@ hipError_t launch_sketch_keys(const sks_kv &kv, const Shape &s, const float *bas
 hipError_t launch_sketch_query(const uint16_t *q, int B, int R, int Hq, int Hkv,
                                const float *basis, int basis_per_head, int8_t *qsk,
                                float *qscale, hipStream_t st);
-// Workspace layout: [hist region | scratch].  The hist region (level-1
-// selection histograms [nseg][2048] and one merge counter per segment) is
-// zero at rest: the calls that use it return it to zero.  The scratch holds
+// Workspace layout: [hist region | scratch].  The hist region holds the
+// level-1 selection histograms [nseg][2048], zero at rest (the calls that use
+// them return them to zero), and one threshold bin per segment.  The scratch holds
 // the selection candidates or, later in the step, the attention partials.
 size_t hist_region_bytes(const Shape &s);
 size_t topk_scratch_bytes(const Shape &s);
@@ -148,7 +148,7 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
 
 struct TopkWs {
   int32_t *hist1;     // [nseg][HIST1_BINS], zero at rest
-  int32_t *counters;  // [nseg], zero at rest
+  int32_t *counters;  // [nseg]: per-segment threshold bin of the selection
   char *scratch;      // start of the scratch area
   int32_t *cnt;       // [nseg][nchunk]
   int2 *cand;         // [nseg][nchunk * TK_SUB]
