@@ -38,6 +38,11 @@ def parse():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--parts", type=int, default=2,
+                    help="sub-batches per step (scheduled on --streams streams)")
+    ap.add_argument("--streams", type=int, default=2)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying "
+                    "a captured HIP graph of the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -112,7 +117,7 @@ def main():
 
     from long_context_sparse_sketch_amd import binding as sks
     from long_context_sparse_sketch_amd import configs as C
-    from long_context_sparse_sketch_amd.runtime import SparseDecodeLayer, to_device
+    from long_context_sparse_sketch_amd.runtime import SparseDecodeLayer, StepRunner, to_device
     from long_context_sparse_sketch_amd.synth import make_case
 
     cfg = C.BY_NAME[args.config]
@@ -157,8 +162,20 @@ def main():
         del a, b
 
     stream = torch.cuda.current_stream()
+    runners = [StepRunner(lay, parts=args.parts, streams=args.streams) for lay in layers]
+    if not args.no_graph:
+        for r in runners:
+            r.capture(q)
+
+    def run_step(k):
+        r = runners[k % len(runners)]
+        if args.no_graph:
+            r.step(q)
+        else:
+            r.replay()
+
     for k in range(args.warmup):
-        layers[k % len(layers)].step(q)
+        run_step(k)
     torch.cuda.synchronize()
 
     def ev():
@@ -169,7 +186,7 @@ def main():
     torch.cuda.synchronize()
     start.record(stream)
     for k in range(args.steps):
-        layers[k % len(layers)].step(q)
+        run_step(k)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -234,7 +251,9 @@ def main():
         "data": "synthetic (seeded N(0,1) caches with planted needles)",
         "config": {"workload": cfg.name, "batch": cfg.B, "context": cfg.L, "rows": cfg.R,
                    "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "window": cfg.window,
-                   "topk": cfg.topk, "pool": cfg.pool, "replicas": args.replicas},
+                   "topk": cfg.topk, "pool": cfg.pool, "replicas": args.replicas,
+                   "schedule": f"{args.parts} sub-batches on {args.streams} streams, "
+                               + ("eager launches" if args.no_graph else "HIP graph replay")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": "sketch_score", "algorithmic_bytes": sketch_b,

@@ -209,14 +209,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
   const int sub = blockIdx.x * (TK_CHUNK / TK_SUB) + wave;
   const int s0 = sub * TK_SUB;
   const int32_t *row = scores + (size_t)seg * NB;
-  // Issue this wave's score loads before the length is known: rows below NB
-  // are always in bounds.
+  // Issue this wave's score loads before the length is known, all at once:
+  // the index is clamped below NB (always in bounds) instead of branching
+  // around the load, and entries past the far region are masked later.
   int raw[FILTER_ITERS];
 #pragma unroll
-  for (int r = 0; r < FILTER_ITERS; ++r) {
-    const int t = s0 + r * 64 + lane;
-    raw[r] = t < NB ? row[t] : 0;
-  }
+  for (int r = 0; r < FILTER_ITERS; ++r) raw[r] = row[min(s0 + r * 64 + lane, NB - 1)];
   const int b1 = thr[seg];
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   if (g.k_eff >= g.n_far || s0 >= g.n_far) return;   // uniform per wave
@@ -297,10 +295,7 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
     constexpr int PERT = TF_CACHE / TF_THREADS;
     int2 tmp[PERT];
 #pragma unroll
-    for (int k = 0; k < PERT; ++k) {
-      const int o = threadIdx.x + k * TF_THREADS;
-      if (o < m) tmp[k] = get(o);
-    }
+    for (int k = 0; k < PERT; ++k) tmp[k] = get(min(threadIdx.x + k * TF_THREADS, m - 1));
 #pragma unroll
     for (int k = 0; k < PERT; ++k) {
       const int o = threadIdx.x + k * TF_THREADS;

@@ -11,7 +11,14 @@ the C-ABI calls of a step on the current stream:
     sks_topk_select               top-k indices, ascending, -1 padded
     sks_sparse_decode_attn        gather + one merged softmax over far + window
 
-torch is used only to allocate device memory; no step calls back into it.
+torch is used only to allocate device memory and streams; no step calls back
+into it.
+
+`StepRunner` schedules one step of a layer as several sub-batches (views of
+the same buffers) on a few streams, so that the latency-bound selection and
+attention of one part overlap the bandwidth-bound score pass of another
+(segments never interact), and can capture the whole step into a HIP graph:
+every call only enqueues kernels and reads lengths on the device.
 """
 from __future__ import annotations
 
@@ -61,6 +68,23 @@ class SparseDecodeLayer:
         self.cache = None
         self.ws = None
 
+    def view(self, b0: int, b1: int) -> "SparseDecodeLayer":
+        """A layer over sequences [b0, b1) sharing this layer's buffers (own workspace)."""
+        v = SparseDecodeLayer.__new__(SparseDecodeLayer)
+        v.B, v.R, v.Hq, v.Hkv, v.T_max = b1 - b0, self.R, self.Hq, self.Hkv, self.T_max
+        v.window, v.topk, v.pool, v.kv_dtype = self.window, self.topk, self.pool, self.kv_dtype
+        v.NB, v.p = self.NB, self.p
+        for name in ("S", "Kp", "Vp", "qsk", "qscale", "scores", "idx", "n_sel", "out", "lse"):
+            t = getattr(self, name)
+            setattr(v, name, None if t is None else t[b0:b1])
+        c = self.cache
+        cache = sks.Cache(c.K[b0:b1], c.V[b0:b1], c.seq_len[b0:b1],
+                          None if c.K_scale is None else c.K_scale[b0:b1],
+                          None if c.V_scale is None else c.V_scale[b0:b1])
+        v.cache, v.ws = None, None
+        v.bind(cache, self.basis, self.key_scale, self.basis_per_head)
+        return v
+
     def bind(self, cache: sks.Cache, basis: torch.Tensor, key_scale: torch.Tensor,
              basis_per_head=False):
         self.cache, self.basis, self.key_scale = cache, basis, key_scale
@@ -107,3 +131,46 @@ class SparseDecodeLayer:
         self.select(stream)
         self.attend(q, stream)
         return self.out, self.lse
+
+
+class StepRunner:
+    """One decode step of a layer, split into `parts` sub-batches on `streams`
+    streams (fork/join on the caller's current stream), optionally captured
+    into a HIP graph and replayed."""
+
+    def __init__(self, layer: SparseDecodeLayer, parts: int = 2, streams: int = 2):
+        parts = max(1, min(parts, layer.B))
+        bounds = [layer.B * k // parts for k in range(parts + 1)]
+        self.layer = layer
+        self.views = [layer.view(bounds[k], bounds[k + 1]) for k in range(parts)]
+        self.bounds = bounds
+        dev = layer.S.device
+        self.streams = [torch.cuda.Stream(device=dev) for _ in range(max(1, streams))]
+        self.graph = None
+
+    def step(self, q):
+        main = torch.cuda.current_stream()
+        for st in self.streams:
+            st.wait_stream(main)
+        for k, v in enumerate(self.views):
+            st = self.streams[k % len(self.streams)]
+            with torch.cuda.stream(st):
+                v.step(q[self.bounds[k]:self.bounds[k + 1]])
+        for st in self.streams:
+            main.wait_stream(st)
+        return self.layer.out, self.layer.lse
+
+    def capture(self, q):
+        """Capture step(q) (q: a static input tensor) into a graph."""
+        self.step(q)                                   # warm up outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(q)
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
+        return self.layer.out, self.layer.lse
