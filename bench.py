@@ -38,11 +38,14 @@ def parse():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--parts", type=int, default=2,
+    ap.add_argument("--parts", type=int, default=1,
                     help="sub-batches per step (scheduled on --streams streams)")
-    ap.add_argument("--streams", type=int, default=2)
+    ap.add_argument("--streams", type=int, default=1)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying "
-                    "a captured HIP graph of the step")
+                    "a captured HIP graph")
+    ap.add_argument("--steps-per-graph", type=int, default=0,
+                    help="consecutive steps (one per cache replica) captured in one graph; "
+                         "0 = all replicas")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -117,7 +120,8 @@ def main():
 
     from long_context_sparse_sketch_amd import binding as sks
     from long_context_sparse_sketch_amd import configs as C
-    from long_context_sparse_sketch_amd.runtime import SparseDecodeLayer, StepRunner, to_device
+    from long_context_sparse_sketch_amd.runtime import (SparseDecodeLayer, StepRunner,
+                                                        capture_steps, to_device)
     from long_context_sparse_sketch_amd.synth import make_case
 
     cfg = C.BY_NAME[args.config]
@@ -163,19 +167,31 @@ def main():
 
     stream = torch.cuda.current_stream()
     runners = [StepRunner(lay, parts=args.parts, streams=args.streams) for lay in layers]
-    if not args.no_graph:
-        for r in runners:
-            r.capture(q)
+    R_ = len(runners)
+    spg = args.steps_per_graph or R_
+    if R_ % spg:
+        raise SystemExit("--replicas must be a multiple of --steps-per-graph")
+    # graphs of spg consecutive layers, plus one single-step graph per layer for
+    # step counts that do not fill a whole multi-step graph
+    multi = [] if args.no_graph else [capture_steps(runners[i:i + spg], q)
+                                      for i in range(0, R_, spg)]
+    single = [] if args.no_graph or spg == 1 else [capture_steps([r], q) for r in runners]
 
-    def run_step(k):
-        r = runners[k % len(runners)]
-        if args.no_graph:
-            r.step(q)
-        else:
-            r.replay()
+    def run_steps(k0, n):
+        """Steps k0 .. k0+n-1 (layer k % replicas), as eager launches or graph replays."""
+        k = k0
+        while k < k0 + n:
+            if args.no_graph:
+                runners[k % R_].step(q)
+                k += 1
+            elif (k % R_) % spg == 0 and k + spg <= k0 + n:
+                multi[(k % R_) // spg].replay()
+                k += spg
+            else:
+                (single[k % R_] if single else multi[k % R_]).replay()
+                k += 1
 
-    for k in range(args.warmup):
-        run_step(k)
+    run_steps(0, args.warmup)
     torch.cuda.synchronize()
 
     def ev():
@@ -185,8 +201,7 @@ def main():
     start, stop = ev(), ev()
     torch.cuda.synchronize()
     start.record(stream)
-    for k in range(args.steps):
-        run_step(k)
+    run_steps(args.warmup, args.steps)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -253,7 +268,8 @@ def main():
                    "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "window": cfg.window,
                    "topk": cfg.topk, "pool": cfg.pool, "replicas": args.replicas,
                    "schedule": f"{args.parts} sub-batches on {args.streams} streams, "
-                               + ("eager launches" if args.no_graph else "HIP graph replay")},
+                               + ("eager launches" if args.no_graph else
+                                  f"HIP graph replay ({spg} steps per graph)")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": "sketch_score", "algorithmic_bytes": sketch_b,

@@ -6,14 +6,11 @@
 //
 // Split-K flash decoding.  A workgroup takes ATTN_SPLIT consecutive entries
 // of one (sequence, row, KV head) attention set and all G query heads of
-// that KV head.  Inside a wave a row of 16 lanes owns one entry at a time:
-// lane p of the row gathers dims [8p, 8p+8) of the entry's K and V rows
-// (16-byte loads, a full 256-byte bf16 row per 16 lanes), dots them with the
-// G queries (v_dot2 bf16 -> fp32), and the row sums by DPP.  Each row keeps
-// its own online-softmax state (m, l, acc) in the log2 domain; the 4 rows of
-// a wave, then the 4 waves, are merged at the end, and the workgroup writes
-// one partial (m, l, acc[G][128]).  A second kernel merges the partials of
-// every split in split order, so results are deterministic.
+// that KV head; each of its 4 waves takes 64 of them as two tiles of 32
+// (see the matrix-core kernel below).  Online softmax in the log2 domain;
+// the waves' states are merged through LDS and the workgroup writes one
+// partial (m, l, acc[G][128]).  A second kernel merges the partials of every
+// split in split order, so results are deterministic.
 #include "sks_internal.h"
 
 namespace sks {
@@ -45,226 +42,6 @@ __device__ __forceinline__ void merge_state(float &m, float &l, float (&a)[N], f
 #pragma unroll
   for (int d = 0; d < N; ++d) a[d] = a[d] * wa + ao[d] * wb;
   m = M;
-}
-
-template <int G, int DT, bool POOLED>
-__global__ __launch_bounds__(AT_THREADS) void attn_split_kernel(
-    const uint16_t *__restrict__ q, const void *__restrict__ K, const void *__restrict__ V,
-    const uint16_t *__restrict__ Ks, const uint16_t *__restrict__ Vs,
-    const int32_t *__restrict__ seq_len, const int32_t *__restrict__ idx,
-    const uint16_t *__restrict__ Kp, const uint16_t *__restrict__ Vp, float sm_log2, int R,
-    int Hkv, int T_max, int NB, int window, int pool, int topk, int nsplit,
-    float2 *__restrict__ part_ml, float *__restrict__ part_acc) {
-  __shared__ float s_ml[4][G][2];
-  __shared__ float s_acc[4][G][D];
-
-  const int seg = blockIdx.y, split = blockIdx.x;
-  const int h = seg % Hkv, bi = seg / Hkv, i = bi % R, b = bi / R;
-  const int L0 = clamp_len(seq_len[b], T_max, R);
-  const RowGeom rg = row_geom(L0, i, window, pool, topk);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = lane >> 4, p = lane & 15;
-  const int Hq = Hkv * G;
-  const int e_wave = split * ATTN_SPLIT + wave * AT_WAVE_ENTRIES;
-
-  // Descriptor of entry e_wave + lane: the row to gather (an index into the
-  // token rows, or the pooled rows when bit 1 of the flag is set) and whether
-  // it takes part.  Invalid entries point at row 0, which always exists, so
-  // the gathers below need no branches.
-  int my_row = 0, my_flag = 0;
-  {
-    const int e = e_wave + lane;
-    if (e < rg.k_eff) {
-      const int sel = idx[(size_t)seg * topk + e];
-      if ((unsigned)sel < (unsigned)rg.n_far) {
-        my_row = sel;
-        my_flag = POOLED ? 3 : 1;
-      }
-    } else if (e < rg.n_ent) {
-      my_row = rg.ws + (e - rg.k_eff);
-      my_flag = 1;
-    }
-  }
-
-  // queries: dims [8p, 8p+8) of the G heads of this KV head
-  uint4 qv[G];
-  float qf[DT == SKS_KV_I8 ? G : 1][DT == SKS_KV_I8 ? 8 : 1];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    qv[j] = *reinterpret_cast<const uint4 *>(q + ((size_t)bi * Hq + (size_t)h * G + j) * D + 8 * p);
-    if constexpr (DT == SKS_KV_I8) {
-      qf[j][0] = bf16_lo(qv[j].x); qf[j][1] = bf16_hi(qv[j].x);
-      qf[j][2] = bf16_lo(qv[j].y); qf[j][3] = bf16_hi(qv[j].y);
-      qf[j][4] = bf16_lo(qv[j].z); qf[j][5] = bf16_hi(qv[j].z);
-      qf[j][6] = bf16_lo(qv[j].w); qf[j][7] = bf16_hi(qv[j].w);
-    }
-  }
-
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m[j] = NEG_INF;
-    l[j] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[j][d] = 0.f;
-  }
-
-  constexpr int EB = DT == SKS_KV_BF16 ? 2 : 1;           // bytes per element
-  const char *Kt = static_cast<const char *>(K) + ((size_t)b * Hkv + h) * T_max * D * EB;
-  const char *Vt = static_cast<const char *>(V) + ((size_t)b * Hkv + h) * T_max * D * EB;
-  const char *Kpb = reinterpret_cast<const char *>(Kp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
-  const char *Vpb = reinterpret_cast<const char *>(Vp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
-  const uint16_t *Kst = DT == SKS_KV_I8 ? Ks + ((size_t)b * Hkv + h) * T_max : nullptr;
-  const uint16_t *Vst = DT == SKS_KV_I8 ? Vs + ((size_t)b * Hkv + h) * T_max : nullptr;
-
-#pragma unroll
-  for (int step = 0; step < AT_STEPS; ++step) {
-    if (e_wave + step * (4 * AT_U) >= rg.n_ent) break;      // uniform across the wave
-    uint4 kr[AT_U], vr[AT_U];
-    float ksc[AT_U], vsc[AT_U];
-    bool ok[AT_U];
-#pragma unroll
-    for (int u = 0; u < AT_U; ++u) {
-      const int src = step * (4 * AT_U) + u * 4 + slot;
-      const int r = __shfl(my_row, src);
-      const int f = __shfl(my_flag, src);
-      ok[u] = f & 1;
-      const bool pooled = POOLED && (f & 2);
-      const size_t off = (size_t)r * D * EB + 8 * p * EB;
-      if constexpr (DT == SKS_KV_BF16) {
-        kr[u] = *reinterpret_cast<const uint4 *>((pooled ? Kpb : Kt) + off);
-        vr[u] = *reinterpret_cast<const uint4 *>((pooled ? Vpb : Vt) + off);
-        ksc[u] = vsc[u] = 1.f;
-      } else {
-        const uint2 k8 = *reinterpret_cast<const uint2 *>(Kt + off);
-        const uint2 v8 = *reinterpret_cast<const uint2 *>(Vt + off);
-        kr[u] = make_uint4(k8.x, k8.y, 0, 0);
-        vr[u] = make_uint4(v8.x, v8.y, 0, 0);
-        ksc[u] = f16_bits_to_float(Kst[r]);
-        vsc[u] = f16_bits_to_float(Vst[r]);
-      }
-    }
-
-    // logits z[u][j] in the log2 domain
-    float z[AT_U][G];
-#pragma unroll
-    for (int u = 0; u < AT_U; ++u) {
-      float kf[DT == SKS_KV_I8 ? 8 : 1];
-      if constexpr (DT == SKS_KV_I8) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          kf[k] = (float)(int8_t)(kr[u].x >> (8 * k));
-          kf[4 + k] = (float)(int8_t)(kr[u].y >> (8 * k));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float sdot;
-        if constexpr (DT == SKS_KV_BF16) {
-          sdot = dot2_bf16(qv[j].x, kr[u].x, 0.f);
-          sdot = dot2_bf16(qv[j].y, kr[u].y, sdot);
-          sdot = dot2_bf16(qv[j].z, kr[u].z, sdot);
-          sdot = dot2_bf16(qv[j].w, kr[u].w, sdot);
-        } else {
-          sdot = 0.f;
-#pragma unroll
-          for (int d = 0; d < 8; ++d) sdot = __builtin_fmaf(qf[j][d], kf[d], sdot);
-        }
-        sdot = row16_sum_f(sdot);
-        if constexpr (DT == SKS_KV_I8) sdot *= ksc[u];
-        z[u][j] = ok[u] ? sdot * sm_log2 : NEG_INF;
-      }
-    }
-
-    // values as fp32 (int8: the row scale is folded into the weight)
-    float vf[AT_U][8];
-#pragma unroll
-    for (int u = 0; u < AT_U; ++u) {
-      if constexpr (DT == SKS_KV_BF16) {
-        vf[u][0] = bf16_lo(vr[u].x); vf[u][1] = bf16_hi(vr[u].x);
-        vf[u][2] = bf16_lo(vr[u].y); vf[u][3] = bf16_hi(vr[u].y);
-        vf[u][4] = bf16_lo(vr[u].z); vf[u][5] = bf16_hi(vr[u].z);
-        vf[u][6] = bf16_lo(vr[u].w); vf[u][7] = bf16_hi(vr[u].w);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          vf[u][k] = (float)(int8_t)(vr[u].x >> (8 * k));
-          vf[u][4 + k] = (float)(int8_t)(vr[u].y >> (8 * k));
-        }
-      }
-    }
-
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float zmax = z[0][j];
-#pragma unroll
-      for (int u = 1; u < AT_U; ++u) zmax = fmaxf(zmax, z[u][j]);
-      const float m_new = fmaxf(m[j], zmax);
-      const float alpha = m[j] == NEG_INF ? 0.f : exp2_fast(m[j] - m_new);
-      float pu[AT_U];
-      float psum = 0.f;
-#pragma unroll
-      for (int u = 0; u < AT_U; ++u) {
-        pu[u] = z[u][j] == NEG_INF ? 0.f : exp2_fast(z[u][j] - m_new);
-        psum += pu[u];
-        if constexpr (DT == SKS_KV_I8) pu[u] *= vsc[u];
-      }
-      l[j] = l[j] * alpha + psum;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        float a = acc[j][d] * alpha;
-#pragma unroll
-        for (int u = 0; u < AT_U; ++u) a = __builtin_fmaf(pu[u], vf[u][d], a);
-        acc[j][d] = a;
-      }
-      m[j] = m_new;
-    }
-  }
-
-  // merge the 4 row-slots of the wave (lanes p, p+16, p+32, p+48)
-#pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float mo = __shfl_xor(m[j], off);
-      const float lo = __shfl_xor(l[j], off);
-      float ao[8];
-#pragma unroll
-      for (int d = 0; d < 8; ++d) ao[d] = __shfl_xor(acc[j][d], off);
-      merge_state<8>(m[j], l[j], acc[j], mo, lo, ao);
-    }
-  }
-  if (slot == 0) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-#pragma unroll
-      for (int d = 0; d < 8; ++d) s_acc[wave][j][8 * p + d] = acc[j][d];
-      if (p == 0) {
-        s_ml[wave][j][0] = m[j];
-        s_ml[wave][j][1] = l[j];
-      }
-    }
-  }
-  __syncthreads();
-
-  // merge the 4 waves and write this split's partial
-  const size_t pbase = (size_t)seg * nsplit + split;
-  for (int x = threadIdx.x; x < G * D; x += AT_THREADS) {
-    const int j = x / D, d = x % D;
-    float M = NEG_INF;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][j][0]);
-    float Lsum = 0.f, A = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = s_ml[w][j][0];
-      const float wt = mw == NEG_INF ? 0.f : exp2_fast(mw - M);
-      Lsum += s_ml[w][j][1] * wt;
-      A += s_acc[w][j][d] * wt;
-    }
-    part_acc[(pbase * G + j) * D + d] = A;
-    if (d == 0) part_ml[pbase * G + j] = make_float2(M, Lsum);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -327,6 +104,51 @@ __device__ __forceinline__ float row16_max_f(float x) {
   return x;
 }
 
+// Merge of the partials of one (segment, query head j, dim d) over all splits,
+// in split order, MB splits at a time so that their loads are in flight
+// together; the order of operations is fixed by the shape.
+constexpr int MB = 8;
+__device__ void merge_splits(const float2 *part_ml, const float *part_acc, int seg, int j, int d,
+                             int nsplit, int G, int Hkv, float *out, float *lse) {
+  const int h = seg % Hkv, bi = seg / Hkv;
+  const size_t orow = (size_t)bi * Hkv * G + (size_t)h * G + j;
+  const size_t base = (size_t)seg * nsplit;
+  const float *ml = reinterpret_cast<const float *>(part_ml);
+  float M = NEG_INF, Lsum = 0.f, A = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += MB) {
+    float mm[MB], ll[MB], a[MB];
+#pragma unroll
+    for (int k = 0; k < MB; ++k) {
+      const int sp = min(s0 + k, nsplit - 1);
+      const size_t e = (base + sp) * G + j;
+      mm[k] = s0 + k < nsplit ? ml[2 * e] : NEG_INF;
+      ll[k] = ml[2 * e + 1];
+      a[k] = part_acc[e * D + d];
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < MB; ++k) Mn = fmaxf(Mn, mm[k]);
+    if (Mn == NEG_INF) continue;
+    const float wa = M == NEG_INF ? 0.f : exp2_fast(M - Mn);
+    Lsum *= wa;
+    A *= wa;
+#pragma unroll
+    for (int k = 0; k < MB; ++k) {
+      const float wt = mm[k] == NEG_INF ? 0.f : exp2_fast(mm[k] - Mn);
+      Lsum += ll[k] * wt;
+      A += a[k] * wt;
+    }
+    M = Mn;
+  }
+  if (M == NEG_INF) {
+    out[orow * D + d] = 0.f;
+    if (d == 0 && lse) lse[orow] = NEG_INF;
+    return;
+  }
+  out[orow * D + d] = A / Lsum;
+  if (d == 0 && lse) lse[orow] = (M + __log2f(Lsum)) * 0.69314718055994530942f;
+}
+
 template <int G, int DT, bool POOLED>
 __global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
     const uint16_t *__restrict__ q, const void *__restrict__ K, const void *__restrict__ V,
@@ -350,7 +172,10 @@ __global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
   const int Hq = Hkv * G;
   const int e_wave = split * ATTN_SPLIT + wave * AM_WAVE_ENTRIES;
 
-  // entry descriptors (see attn_split_kernel)
+  // Descriptor of entry e_wave + lane: the row to gather (an index into the
+  // token rows, or the pooled rows when bit 1 of the flag is set) and whether
+  // it takes part.  Invalid entries point at row 0, which always exists, so
+  // the gathers below need no branches.
   int my_row = 0, my_flag = 0;
   {
     const int e = e_wave + lane;
@@ -554,74 +379,43 @@ __global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
     part_acc[(pbase * G + j) * D + d] = A;
     if (d == 0) part_ml[pbase * G + j] = make_float2(M, Lsum);
   }
+
 }
 
-// One workgroup of 128 threads per (segment, query head of the group).  The
-// splits are merged in split order, MB at a time so that their loads are in
-// flight together; the order of operations is fixed by the shape.
-constexpr int MB = 8;
+// One workgroup of 128 threads per (segment, query head of the group).
 __global__ __launch_bounds__(D) void attn_merge_kernel(const float2 *__restrict__ part_ml,
                                                        const float *__restrict__ part_acc,
                                                        int nsplit, int G, int Hkv,
                                                        float *__restrict__ out,
                                                        float *__restrict__ lse) {
-  const int seg = blockIdx.x, j = blockIdx.y, d = threadIdx.x;
-  const int h = seg % Hkv, bi = seg / Hkv;
-  const size_t orow = (size_t)bi * Hkv * G + (size_t)h * G + j;
-  const size_t base = (size_t)seg * nsplit;
-  float M = NEG_INF, Lsum = 0.f, A = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += MB) {
-    float2 ml[MB];
-    float a[MB];
-#pragma unroll
-    for (int k = 0; k < MB; ++k) {
-      const int s = s0 + k;
-      ml[k] = s < nsplit ? part_ml[(base + s) * G + j] : make_float2(NEG_INF, 0.f);
-      a[k] = s < nsplit ? part_acc[((base + s) * G + j) * D + d] : 0.f;
-    }
-    float Mn = M;
-#pragma unroll
-    for (int k = 0; k < MB; ++k) Mn = fmaxf(Mn, ml[k].x);
-    if (Mn == NEG_INF) continue;
-    const float wa = M == NEG_INF ? 0.f : exp2_fast(M - Mn);
-    Lsum *= wa;
-    A *= wa;
-#pragma unroll
-    for (int k = 0; k < MB; ++k) {
-      const float wt = ml[k].x == NEG_INF ? 0.f : exp2_fast(ml[k].x - Mn);
-      Lsum += ml[k].y * wt;
-      A += a[k] * wt;
-    }
-    M = Mn;
-  }
-  if (M == NEG_INF) {
-    out[orow * D + d] = 0.f;
-    if (d == 0 && lse) lse[orow] = NEG_INF;
-    return;
-  }
-  out[orow * D + d] = A / Lsum;
-  if (d == 0 && lse) lse[orow] = (M + __log2f(Lsum)) * 0.69314718055994530942f;
+  merge_splits(part_ml, part_acc, blockIdx.x, blockIdx.y, threadIdx.x, nsplit, G, Hkv, out, lse);
 }
+
+struct AttnOut {
+  float2 *pml;
+  float *pacc;
+  float *out, *lse;
+};
 
 template <int G, int DT, bool POOLED>
 void launch_split(dim3 grid, hipStream_t st, const uint16_t *q, const sks_kv &kv, const Shape &s,
                   const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp, float sm_log2,
-                  int nsplit, float2 *pml, float *pacc) {
+                  int nsplit, const AttnOut &o) {
   attn_mfma_kernel<G, DT, POOLED><<<grid, AT_THREADS, 0, st>>>(
       q, kv.K, kv.V, kv.K_scale, kv.V_scale, kv.seq_len, idx, Kp, Vp, sm_log2, s.R, s.Hkv,
-      s.T_max, s.NB, s.window, s.pool, s.topk, nsplit, pml, pacc);
+      s.T_max, s.NB, s.window, s.pool, s.topk, nsplit, o.pml, o.pacc);
 }
 
 template <int G>
 void dispatch_g(dim3 grid, hipStream_t st, const uint16_t *q, const sks_kv &kv, const Shape &s,
                 const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp, float sm_log2,
-                int nsplit, float2 *pml, float *pacc) {
+                int nsplit, const AttnOut &o) {
   if (s.dtype == SKS_KV_I8)
-    launch_split<G, SKS_KV_I8, false>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, pml, pacc);
+    launch_split<G, SKS_KV_I8, false>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o);
   else if (s.pool > 1)
-    launch_split<G, SKS_KV_BF16, true>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, pml, pacc);
+    launch_split<G, SKS_KV_BF16, true>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o);
   else
-    launch_split<G, SKS_KV_BF16, false>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, pml, pacc);
+    launch_split<G, SKS_KV_BF16, false>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o);
 }
 
 int attn_nsplit(const Shape &s) {
@@ -647,15 +441,16 @@ hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape 
   float *pacc = reinterpret_cast<float *>(w.scratch + align_up(n * sizeof(float2), 256));
   const float sm_log2 = sm_scale * 1.4426950408889634f;
   dim3 grid(nsplit, nseg);
+  const AttnOut o{pml, pacc, out, lse};
   switch (G) {
-    case 1: dispatch_g<1>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, pml, pacc); break;
-    case 2: dispatch_g<2>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, pml, pacc); break;
-    case 3: dispatch_g<3>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, pml, pacc); break;
-    case 4: dispatch_g<4>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, pml, pacc); break;
-    case 5: dispatch_g<5>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, pml, pacc); break;
-    case 6: dispatch_g<6>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, pml, pacc); break;
-    case 7: dispatch_g<7>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, pml, pacc); break;
-    case 8: dispatch_g<8>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, pml, pacc); break;
+    case 1: dispatch_g<1>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
+    case 2: dispatch_g<2>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
+    case 3: dispatch_g<3>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
+    case 4: dispatch_g<4>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
+    case 5: dispatch_g<5>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
+    case 6: dispatch_g<6>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
+    case 7: dispatch_g<7>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
+    case 8: dispatch_g<8>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

@@ -88,52 +88,6 @@ __device__ __forceinline__ int hpad(int b) { return b + b / (NBINS / 64); }
 template <int NBINS>
 constexpr int hpad_size() { return NBINS + 64; }
 
-// Threshold search over a histogram held in registers, lane l holding bins
-// [l*PER, (l+1)*PER) in v[].  No barriers.  Returns the bin b with
-// sum_{b' >= b} >= need > sum_{b' > b}; `above` receives sum_{b' > b}.
-template <int PER>
-__device__ int wave_threshold_regs(const int (&v)[PER], int need, int n, int &above) {
-  const int lane = threadIdx.x & 63;
-  long long sum = 0;
-  bool bad = false;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    bad |= v[k] < 0 || v[k] > n;
-    sum += v[k];
-  }
-  long long tot = sum;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
-  above = 0;
-  if (__any(bad) || tot != (long long)n) return 0;
-  int incl = (int)sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
-  int ab = n - incl;                         // bins of higher lanes
-  int b = -1, ab_b = 0;
-  if (ab < need && ab + (int)sum >= need) {
-#pragma unroll
-    for (int k = PER - 1; k >= 0; --k) {
-      if (b < 0) {
-        if (ab + v[k] >= need) {
-          b = lane * PER + k;
-          ab_b = ab;
-        } else {
-          ab += v[k];
-        }
-      }
-    }
-  }
-  const unsigned long long who = __ballot(b >= 0);
-  if (who == 0) return 0;
-  const int src = __ffsll((long long)who) - 1;
-  above = __shfl(ab_b, src);
-  return __shfl(b, src);
-}
-
 // Same search over a padded LDS histogram of NBINS bins.  The histogram is
 // validated first (every bin in [0, n], total exactly n); an invalid one (a
 // workspace that was not zero at rest) yields bin 0, i.e. every element is a
@@ -145,7 +99,8 @@ __device__ int wave_threshold_bin(const int *hist, int need, int n, int &above) 
   int v[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) v[k] = hist[hpad<NBINS>(lane * PER + k)];
-  return wave_threshold_regs<PER>(v, need, n, above);
+  bool valid;
+  return wave_threshold_regs<PER>(v, need, n, above, valid);
 }
 
 __global__ void fill_kernel(int32_t *p, size_t n, int32_t v) {
@@ -195,9 +150,10 @@ __global__ __launch_bounds__(64) void topk_threshold_kernel(
     v[4 * k + 3] = w.w;
   }
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
-  int b1 = 0, above;
-  if (g.k_eff < g.n_far) b1 = wave_threshold_regs<PER>(v, g.k_eff, g.n_far, above);
-  if (lane == 0) thr[seg] = b1;
+  int b1 = 0, above = 0;
+  bool valid = false;
+  if (g.k_eff < g.n_far) b1 = wave_threshold_regs<PER>(v, g.k_eff, g.n_far, above, valid);
+  if (lane == 0) reinterpret_cast<int4 *>(thr)[seg] = make_int4(b1, above, valid, 0);
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
@@ -215,7 +171,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
   int raw[FILTER_ITERS];
 #pragma unroll
   for (int r = 0; r < FILTER_ITERS; ++r) raw[r] = row[min(s0 + r * 64 + lane, NB - 1)];
-  const int b1 = thr[seg];
+  const int b1 = thr[4 * seg];
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   if (g.k_eff >= g.n_far || s0 >= g.n_far) return;   // uniform per wave
   const int s1 = min(g.n_far, s0 + TK_SUB);
@@ -235,9 +191,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
 
 __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
     const int32_t *__restrict__ scores, const int32_t *__restrict__ seq_len,
-    int32_t *__restrict__ hist1, const int32_t *__restrict__ cnt, const int2 *__restrict__ cand,
-    int n_sub_max, int R, int Hkv, int T_max, int NB, int window, int pool, int topk,
-    int32_t *__restrict__ idx, int32_t *__restrict__ n_sel) {
+    int32_t *__restrict__ hist1, const int32_t *__restrict__ thr, const int32_t *__restrict__ cnt,
+    const int2 *__restrict__ cand, int n_sub_max, int R, int Hkv, int T_max, int NB, int window,
+    int pool, int topk, int32_t *__restrict__ idx, int32_t *__restrict__ n_sel) {
   __shared__ int h1[hpad_size<HIST1_BINS>()];
   __shared__ int h2[hpad_size<HIST2_BINS>()];
   __shared__ int pre[TK_MAX_SUBS + 1];
@@ -248,6 +204,7 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
   const int32_t *gc = cnt + (size_t)seg * n_sub_max;
   // the first round of sub-list counts, loaded before the length is known
   int cv0 = threadIdx.x < n_sub_max ? gc[threadIdx.x] : 0;
+  const int4 th = reinterpret_cast<const int4 *>(thr)[seg];   // (b1, above1, valid, -)
   for (int k = threadIdx.x; k < hpad_size<HIST1_BINS>(); k += TF_THREADS) h1[k] = 0;
   for (int k = threadIdx.x; k < hpad_size<HIST2_BINS>(); k += TF_THREADS) h2[k] = 0;
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
@@ -305,16 +262,39 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
   __syncthreads();
   auto fetch = [&](int o) -> int2 { return cached ? cache[o] : get(o); };
 
-  // exact threshold key T: level 1 (top 11 bits), level 2 (low 10 bits)
-  for (int o = threadIdx.x; o < m; o += TF_THREADS)
-    atomicAdd(&h1[hpad<HIST1_BINS>(fetch(o).y >> HIST2_BITS)], 1);
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    int above;
-    const int b1 = wave_threshold_bin<HIST1_BINS>(h1, g.k_eff, m, above);
+  // exact threshold key T: level 1 (top 11 bits), level 2 (low 10 bits).
+  // With a valid histogram the candidates are exactly the elements of bins
+  // >= b1 and level 1 is already known; otherwise derive it from the
+  // candidates themselves.
+  // Candidates are exactly the elements of bins >= thr.x (the filter used the
+  // same value).  If that bin is a legal threshold -- the candidates above it
+  // number fewer than k, counted from the data, never from the histogram --
+  // level 1 is known; otherwise derive it from the candidates.
+  bool fast = th.z && !raw && th.x >= 0 && th.x < HIST1_BINS;
+  int above_data = 0;
+  if (fast) {
+    int part = 0;
+    for (int o = threadIdx.x; o < m; o += TF_THREADS) part += (fetch(o).y >> HIST2_BITS) > th.x;
+    block_incl_scan(part, scratch, above_data);
+    fast = above_data < g.k_eff;                 // uniform: block total
+  }
+  if (fast) {
     if (threadIdx.x == 0) {
-      res[0] = b1;
-      res[1] = g.k_eff - above;                  // still needed from bin b1
+      res[0] = th.x;
+      res[1] = g.k_eff - above_data;
+      h1[hpad<HIST1_BINS>(th.x)] = m - above_data;   // candidates in bin b1
+    }
+  } else {
+    for (int o = threadIdx.x; o < m; o += TF_THREADS)
+      atomicAdd(&h1[hpad<HIST1_BINS>(fetch(o).y >> HIST2_BITS)], 1);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      int above;
+      const int bb = wave_threshold_bin<HIST1_BINS>(h1, g.k_eff, m, above);
+      if (threadIdx.x == 0) {
+        res[0] = bb;
+        res[1] = g.k_eff - above;                // still needed from bin b1
+      }
     }
   }
   __syncthreads();
@@ -371,7 +351,8 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
 
 size_t hist_region_bytes(const Shape &s) {
   const size_t nseg = (size_t)s.B * s.R * s.Hkv;
-  return align_up(nseg * HIST1_BINS * 4, 256) + align_up(nseg * 4, 256);
+  return align_up(nseg * HIST1_BINS * 4, 256) + align_up(nseg * 16, 256) +
+         align_up((size_t)s.B * s.Hkv * 4, 256);
 }
 
 size_t topk_scratch_bytes(const Shape &s) {
@@ -385,8 +366,12 @@ TopkWs topk_ws_carve(const Shape &s, void *ws) {
   const size_t n_sub = (size_t)ceil_div(s.NB, TK_SUB);
   char *base = static_cast<char *>(ws);
   TopkWs w;
-  w.hist1 = reinterpret_cast<int32_t *>(base);
-  w.counters = reinterpret_cast<int32_t *>(base + align_up(nseg * HIST1_BINS * 4, 256));
+  char *q = base;
+  w.hist1 = reinterpret_cast<int32_t *>(q);
+  q += align_up(nseg * HIST1_BINS * 4, 256);
+  w.counters = reinterpret_cast<int32_t *>(q);
+  q += align_up(nseg * 16, 256);
+  w.score_ticket = reinterpret_cast<int32_t *>(q);
   char *p = base + hist_region_bytes(s);
   w.scratch = p;
   w.cnt = reinterpret_cast<int32_t *>(p);
@@ -409,18 +394,20 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
   long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   if (max_far > 0) {
     dim3 grid(ceil_div(max_far, TK_CHUNK), nseg);
-    if (!hist_ready)
+    if (!hist_ready) {
+      // (with a ready histogram the score pass has already stored the thresholds)
       topk_hist_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, s.R, s.Hkv,
                                                     s.T_max, s.NB, s.window, s.pool, s.topk);
-    topk_threshold_kernel<<<nseg, 64, 0, st>>>(seq_len, w.hist1, w.counters, s.R, s.Hkv,
-                                               s.T_max, s.window, s.pool, s.topk);
+      topk_threshold_kernel<<<nseg, 64, 0, st>>>(seq_len, w.hist1, w.counters, s.R, s.Hkv,
+                                                 s.T_max, s.window, s.pool, s.topk);
+    }
     topk_filter_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.counters, w.cnt, w.cand,
                                                     w.nchunk, s.R, s.Hkv, s.T_max, s.NB,
                                                     s.window, s.pool, s.topk);
   }
-  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.cnt, w.cand,
-                                                 w.nchunk, s.R, s.Hkv, s.T_max, s.NB, s.window,
-                                                 s.pool, s.topk, idx, n_sel);
+  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.counters, w.cnt,
+                                                 w.cand, w.nchunk, s.R, s.Hkv, s.T_max, s.NB,
+                                                 s.window, s.pool, s.topk, idx, n_sel);
   return hipGetLastError();
 }
 

@@ -200,12 +200,13 @@ int sks_sketch_score(const int8_t *qsk, const int8_t *S, const sks_kv *kv, const
   REQUIRE_PTR(qsk, 16);
   REQUIRE_PTR(S, 16);
   REQUIRE_PTR(scores, 4);
-  int32_t *hist = nullptr;
+  sks::TopkWs w;
   if (ws) {
     TRY(check_ws(ws, ws_bytes_given, topk_need(s)));
-    hist = sks::topk_ws_carve(s, ws).hist1;
+    w = sks::topk_ws_carve(s, ws);
   }
-  return hip_status(sks::launch_score(qsk, S, kv->seq_len, s, scores, hist, (hipStream_t)stream),
+  return hip_status(sks::launch_score(qsk, S, kv->seq_len, s, scores, ws ? &w : nullptr,
+                                      (hipStream_t)stream),
                     "sks_sketch_score");
 }
 

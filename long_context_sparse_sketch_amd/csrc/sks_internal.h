@@ -122,6 +122,56 @@ __device__ __forceinline__ float row16_sum_f(float x) {
   return x;
 }
 
+// ---------------------------------------------------------------- selection threshold
+// Threshold search over a histogram held in registers, lane l holding bins
+// [l*PER, (l+1)*PER) in v[].  No barriers.  Returns the bin b with
+// sum_{b' >= b} >= need > sum_{b' > b}; `above` receives sum_{b' > b}.
+template <int PER>
+__device__ __forceinline__ int wave_threshold_regs(const int (&v)[PER], int need, int n, int &above,
+                                   bool &valid) {
+  const int lane = threadIdx.x & 63;
+  long long sum = 0;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    bad |= v[k] < 0 || v[k] > n;
+    sum += v[k];
+  }
+  long long tot = sum;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+  above = 0;
+  valid = !__any(bad) && tot == (long long)n;
+  if (!valid) return 0;
+  int incl = (int)sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  int ab = n - incl;                         // bins of higher lanes
+  int b = -1, ab_b = 0;
+  if (ab < need && ab + (int)sum >= need) {
+#pragma unroll
+    for (int k = PER - 1; k >= 0; --k) {
+      if (b < 0) {
+        if (ab + v[k] >= need) {
+          b = lane * PER + k;
+          ab_b = ab;
+        } else {
+          ab += v[k];
+        }
+      }
+    }
+  }
+  const unsigned long long who = __ballot(b >= 0);
+  if (who == 0) return 0;
+  const int src = __ffsll((long long)who) - 1;
+  above = __shfl(ab_b, src);
+  return __shfl(b, src);
+}
+
+
 // ---------------------------------------------------------------- launchers
 struct Shape {
   int B, R, Hkv, T_max, NB, window, topk, pool, dtype;
@@ -135,20 +185,25 @@ hipError_t launch_sketch_query(const uint16_t *q, int B, int R, int Hq, int Hkv,
                                const float *basis, int basis_per_head, int8_t *qsk,
                                float *qscale, hipStream_t st);
 // Workspace layout: [hist region | scratch].  The hist region holds the
-// level-1 selection histograms [nseg][2048], zero at rest (the calls that use
-// them return them to zero), and one threshold bin per segment.  The scratch holds
+// level-1 selection histograms [nseg][2048] and one ticket counter per
+// (sequence, KV head), zero at rest (the calls that use them return them to
+// zero), plus the per-segment threshold bins.  The scratch holds
 // the selection candidates or, later in the step, the attention partials.
 size_t hist_region_bytes(const Shape &s);
 size_t topk_scratch_bytes(const Shape &s);
 size_t attn_scratch_bytes(const Shape &s, int G);
 
 hipError_t launch_fill(int32_t *p, size_t n, hipStream_t st);
+// With `w` (non-null) the score pass also builds the selection histogram and
+// its last workgroup per (sequence, KV head) stores the threshold bins.
+struct TopkWs;
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
-                        const Shape &s, int32_t *scores, int32_t *hist1, hipStream_t st);
+                        const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st);
 
 struct TopkWs {
   int32_t *hist1;     // [nseg][HIST1_BINS], zero at rest
-  int32_t *counters;  // [nseg]: per-segment threshold bin of the selection
+  int32_t *counters;  // [nseg][4]: threshold bin, count above it, histogram valid
+  int32_t *score_ticket;  // [B * Hkv], zero at rest
   char *scratch;      // start of the scratch area
   int32_t *cnt;       // [nseg][nchunk]
   int2 *cand;         // [nseg][nchunk * TK_SUB]

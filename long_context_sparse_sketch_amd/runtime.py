@@ -138,7 +138,8 @@ class StepRunner:
     streams (fork/join on the caller's current stream), optionally captured
     into a HIP graph and replayed."""
 
-    def __init__(self, layer: SparseDecodeLayer, parts: int = 2, streams: int = 2):
+    def __init__(self, layer: SparseDecodeLayer, parts: int = 1, streams: int = 1,
+                 overlap_append: bool = False):
         parts = max(1, min(parts, layer.B))
         bounds = [layer.B * k // parts for k in range(parts + 1)]
         self.layer = layer
@@ -146,31 +147,55 @@ class StepRunner:
         self.bounds = bounds
         dev = layer.S.device
         self.streams = [torch.cuda.Stream(device=dev) for _ in range(max(1, streams))]
+        self.append_stream = torch.cuda.Stream(device=dev) if overlap_append else None
         self.graph = None
 
     def step(self, q):
         main = torch.cuda.current_stream()
         for st in self.streams:
             st.wait_stream(main)
+        # The rows' own tokens lie inside every row's exact window when
+        # window >= rows, so this step's scoring never reads the sketches the
+        # append writes: the append then runs beside the query/score chain.
+        side = self.append_stream if self.layer.window >= self.layer.R else None
+        if side is None and len(self.streams) == 1 and len(self.views) == 1:
+            # plain single-stream step on the caller's stream
+            self.views[0].step(q)
+            return self.layer.out, self.layer.lse
+        if side is not None:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                for v in self.views:
+                    v.build_sketch(sks.APPEND, 0)
         for k, v in enumerate(self.views):
             st = self.streams[k % len(self.streams)]
             with torch.cuda.stream(st):
-                v.step(q[self.bounds[k]:self.bounds[k + 1]])
+                v.step(q[self.bounds[k]:self.bounds[k + 1]], append=side is None)
         for st in self.streams:
             main.wait_stream(st)
+        if side is not None:
+            main.wait_stream(side)
         return self.layer.out, self.layer.lse
 
     def capture(self, q):
         """Capture step(q) (q: a static input tensor) into a graph."""
-        self.step(q)                                   # warm up outside the capture
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            self.step(q)
-        torch.cuda.synchronize()
-        self.graph = g
-        return g
+        self.graph = capture_steps([self], q)
+        return self.graph
 
     def replay(self):
         self.graph.replay()
         return self.layer.out, self.layer.lse
+
+
+def capture_steps(runners, q):
+    """Capture one step of each runner, in order, into ONE HIP graph (e.g. the
+    layers of a decode iteration), so that a single launch replays them all."""
+    for r in runners:                                  # warm up outside the capture
+        r.step(q)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in runners:
+            r.step(q)
+    torch.cuda.synchronize()
+    return g
