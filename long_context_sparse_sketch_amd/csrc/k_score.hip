@@ -39,10 +39,8 @@ template <int R, bool HIST>
 __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     const int8_t *__restrict__ qsk, const int8_t *__restrict__ S,
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ scores,
-    int32_t *__restrict__ hist1, int32_t *__restrict__ thr, int32_t *__restrict__ ticket,
-    int Hkv, int T_max, int NB, int window, int pool, int topk) {
+    int32_t *__restrict__ hist1, int Hkv, int T_max, int NB, int window, int pool, int topk) {
   __shared__ int lh[HIST ? R * HIST1_BINS : 1];
-  __shared__ int s_last;
   const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
   const int L0 = clamp_len(seq_len[b], T_max, R);
   const int Lmax = L0 + R - 1;
@@ -55,13 +53,12 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   const int quad = lane >> 2, part = lane & 3;
   // per-row far counts (rows differ by one token each); a row whose top-k
   // takes everything needs no histogram
-  int nf[R], ke[R];
+  int nf[R];
   bool need_hist[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const RowGeom rg = row_geom(L0, i, window, pool, topk);
     nf[i] = rg.n_far;
-    ke[i] = rg.k_eff;
     need_hist[i] = HIST && rg.k_eff < rg.n_far;
   }
   if (HIST) {
@@ -121,35 +118,6 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
       const int i = k / HIST1_BINS;
       if (v) atomicAdd(&hist1[((size_t)(b * R + i) * Hkv + h) * HIST1_BINS + (k % HIST1_BINS)], v);
     }
-    // The last workgroup of this (b, h) to finish derives every row's
-    // threshold bin from the complete histogram (ticket counter, zero at
-    // rest; no workgroup ever waits for another).
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int nwg = (n_far + SCORE_CHUNK - 1) / SCORE_CHUNK;
-      s_last = atomicAdd(&ticket[bh], 1) == nwg - 1;
-    }
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      for (int i = wave; i < R; i += SC_THREADS / 64) {
-        const size_t seg = (size_t)(b * R + i) * Hkv + h;
-        int b1 = 0, above = 0;
-        bool valid = false;
-        if (need_hist[i]) {
-          constexpr int PER = HIST1_BINS / 64;
-          int v[PER];
-          const int32_t *gh = hist1 + seg * HIST1_BINS + lane * PER;
-#pragma unroll
-          for (int k = 0; k < PER; ++k)
-            v[k] = __hip_atomic_load(gh + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          b1 = wave_threshold_regs<PER>(v, ke[i], nf[i], above, valid);
-        }
-        if (lane == 0) reinterpret_cast<int4 *>(thr)[seg] = make_int4(b1, above, valid, 0);
-      }
-      if (threadIdx.x == 0) ticket[bh] = 0;
-    }
   }
 }
 
@@ -157,6 +125,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
                         const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st) {
+  int32_t *hist1 = w ? w->hist1 : nullptr;
   // the largest far count any row can have is (T_max - window) / pool <= NB
   long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   if (max_far <= 0) return hipSuccess;
@@ -164,15 +133,14 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
   switch (s.R) {
 #define SKS_SCORE_CASE(RR)                                                                     \
   case RR:                                                                                     \
-    if (w)                                                                                     \
-      score_kernel<RR, true><<<grid, SC_THREADS, 0, st>>>(qsk, S, seq_len, scores, w->hist1,   \
-                                                          w->counters, w->score_ticket, s.Hkv, \
-                                                          s.T_max, s.NB, s.window, s.pool,     \
-                                                          s.topk);                             \
+    if (hist1)                                                                                 \
+      score_kernel<RR, true><<<grid, SC_THREADS, 0, st>>>(qsk, S, seq_len, scores, hist1,      \
+                                                          s.Hkv, s.T_max, s.NB, s.window,      \
+                                                          s.pool, s.topk);                     \
     else                                                                                       \
       score_kernel<RR, false><<<grid, SC_THREADS, 0, st>>>(qsk, S, seq_len, scores, nullptr,   \
-                                                           nullptr, nullptr, s.Hkv, s.T_max,   \
-                                                           s.NB, s.window, s.pool, s.topk);    \
+                                                           s.Hkv, s.T_max, s.NB, s.window,     \
+                                                           s.pool, s.topk);                    \
     break;
     SKS_SCORE_CASE(1)
     SKS_SCORE_CASE(2)

@@ -351,8 +351,7 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
 
 size_t hist_region_bytes(const Shape &s) {
   const size_t nseg = (size_t)s.B * s.R * s.Hkv;
-  return align_up(nseg * HIST1_BINS * 4, 256) + align_up(nseg * 16, 256) +
-         align_up((size_t)s.B * s.Hkv * 4, 256);
+  return align_up(nseg * HIST1_BINS * 4, 256) + align_up(nseg * 16, 256);
 }
 
 size_t topk_scratch_bytes(const Shape &s) {
@@ -370,8 +369,6 @@ TopkWs topk_ws_carve(const Shape &s, void *ws) {
   w.hist1 = reinterpret_cast<int32_t *>(q);
   q += align_up(nseg * HIST1_BINS * 4, 256);
   w.counters = reinterpret_cast<int32_t *>(q);
-  q += align_up(nseg * 16, 256);
-  w.score_ticket = reinterpret_cast<int32_t *>(q);
   char *p = base + hist_region_bytes(s);
   w.scratch = p;
   w.cnt = reinterpret_cast<int32_t *>(p);
@@ -394,13 +391,11 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
   long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   if (max_far > 0) {
     dim3 grid(ceil_div(max_far, TK_CHUNK), nseg);
-    if (!hist_ready) {
-      // (with a ready histogram the score pass has already stored the thresholds)
+    if (!hist_ready)
       topk_hist_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, s.R, s.Hkv,
                                                     s.T_max, s.NB, s.window, s.pool, s.topk);
-      topk_threshold_kernel<<<nseg, 64, 0, st>>>(seq_len, w.hist1, w.counters, s.R, s.Hkv,
-                                                 s.T_max, s.window, s.pool, s.topk);
-    }
+    topk_threshold_kernel<<<nseg, 64, 0, st>>>(seq_len, w.hist1, w.counters, s.R, s.Hkv,
+                                               s.T_max, s.window, s.pool, s.topk);
     topk_filter_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.counters, w.cnt, w.cand,
                                                     w.nchunk, s.R, s.Hkv, s.T_max, s.NB,
                                                     s.window, s.pool, s.topk);

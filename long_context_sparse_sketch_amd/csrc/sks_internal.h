@@ -185,17 +185,18 @@ hipError_t launch_sketch_query(const uint16_t *q, int B, int R, int Hq, int Hkv,
                                const float *basis, int basis_per_head, int8_t *qsk,
                                float *qscale, hipStream_t st);
 // Workspace layout: [hist region | scratch].  The hist region holds the
-// level-1 selection histograms [nseg][2048] and one ticket counter per
-// (sequence, KV head), zero at rest (the calls that use them return them to
-// zero), plus the per-segment threshold bins.  The scratch holds
+// level-1 selection histograms [nseg][2048], zero at rest (the calls that use
+// them return them to zero), and the per-segment threshold bins.
+// (Kernels here never communicate between workgroups inside one launch: a
+// device-scope fence per workgroup costs far more on this GPU than a kernel
+// boundary.)  The scratch holds
 // the selection candidates or, later in the step, the attention partials.
 size_t hist_region_bytes(const Shape &s);
 size_t topk_scratch_bytes(const Shape &s);
 size_t attn_scratch_bytes(const Shape &s, int G);
 
 hipError_t launch_fill(int32_t *p, size_t n, hipStream_t st);
-// With `w` (non-null) the score pass also builds the selection histogram and
-// its last workgroup per (sequence, KV head) stores the threshold bins.
+// With `w` (non-null) the score pass also builds the selection histogram.
 struct TopkWs;
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
                         const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st);
@@ -203,7 +204,6 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
 struct TopkWs {
   int32_t *hist1;     // [nseg][HIST1_BINS], zero at rest
   int32_t *counters;  // [nseg][4]: threshold bin, count above it, histogram valid
-  int32_t *score_ticket;  // [B * Hkv], zero at rest
   char *scratch;      // start of the scratch area
   int32_t *cnt;       // [nseg][nchunk]
   int2 *cand;         // [nseg][nchunk * TK_SUB]
