@@ -27,6 +27,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "score_kernel_{workload}_hbm_counters.txt")
+SCORE_SOURCES = ("k_score.hip", "sks_internal.h")
 
 
 def parse():
@@ -65,6 +67,29 @@ def algorithmic_bytes(cfg):
     gathered = sum(B * Hkv * cfg.n_attended(i) * 2 * row_bytes for i in range(R))
     small = B * R * Hq * 128 * 2 + B * R * Hq * 128 * 4 + B * R * Hkv * cfg.topk * 4
     return sketch, gathered, small
+
+
+def counted_traffic(workload):
+    """HBM bytes per score launch from the committed FETCH_SIZE / WRITE_SIZE
+    counter summary (scaled by the copy-kernel calibration it records), or None
+    when there is none for this workload or the score kernel's sources have
+    changed since the counters were taken."""
+    import hashlib
+    path = COUNTERS.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for ln in open(path):
+        k, sep, v = ln.partition(":")
+        if sep:
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        with open(os.path.join(ROOT, "long_context_sparse_sketch_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("workload") != workload or fields.get("score_sources_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(cfg, case, seconds):
@@ -271,7 +296,8 @@ def main():
                                + ("eager launches" if args.no_graph else
                                   f"HIP graph replay ({spg} steps per graph)")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": counted_traffic(cfg.name),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                      "kernel": "sketch_score", "algorithmic_bytes": sketch_b,
                      "avg_ms": score_avg_ms},
         "detail": {

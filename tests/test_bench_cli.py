@@ -24,3 +24,18 @@ def test_algorithmic_bytes_of_the_250k_workload():
     s5, g5, _ = bench.algorithmic_bytes(C.C5)
     assert s5 == 4 * 8 * (65539 - 4096) * 64                  # one pass for the 3 rows
     assert g5 == sum(4 * 8 * 6144 * 2 * 130 for _ in range(3))
+
+
+def test_counted_traffic_follows_the_score_sources(tmp_path, monkeypatch):
+    """The committed counter summary is used only for its workload and only
+    while the score kernel's sources hash to the recorded value."""
+    sys.path.insert(0, ROOT)
+    import bench
+    src = open(bench.COUNTERS.format(workload="multi_agent_250k")).read()
+    t = bench.counted_traffic("multi_agent_250k")
+    assert t is not None and 5.0e8 < t < 6.0e8                # ~1.07 x the 503.6 MB of sketch
+    assert bench.counted_traffic("tiny") is None
+    fake = tmp_path / "score_kernel_multi_agent_250k_hbm_counters.txt"
+    fake.write_text(src.replace("score_sources_sha256: ", "score_sources_sha256: 00"))
+    monkeypatch.setattr(bench, "COUNTERS", str(tmp_path / "score_kernel_{workload}_hbm_counters.txt"))
+    assert bench.counted_traffic("multi_agent_250k") is None
