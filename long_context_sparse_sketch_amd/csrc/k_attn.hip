@@ -165,12 +165,16 @@ __global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
 
   const int seg = blockIdx.y, split = blockIdx.x;
   const int h = seg % Hkv, bi = seg / Hkv, i = bi % R, b = bi / R;
-  const int L0 = clamp_len(seq_len[b], T_max, R);
-  const RowGeom rg = row_geom(L0, i, window, pool, topk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int Hq = Hkv * G;
   const int e_wave = split * ATTN_SPLIT + wave * AM_WAVE_ENTRIES;
+  // The selected index of entry e_wave + lane is loaded together with the
+  // length, before it is known whether the entry is a selected one (the
+  // address is clamped into the segment's idx row, so always in bounds).
+  const int sel = idx[(size_t)seg * topk + min(e_wave + lane, topk - 1)];
+  const int L0 = clamp_len(seq_len[b], T_max, R);
+  const RowGeom rg = row_geom(L0, i, window, pool, topk);
 
   // Descriptor of entry e_wave + lane: the row to gather (an index into the
   // token rows, or the pooled rows when bit 1 of the flag is set) and whether
@@ -180,7 +184,6 @@ __global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
   {
     const int e = e_wave + lane;
     if (e < rg.k_eff) {
-      const int sel = idx[(size_t)seg * topk + e];
       if ((unsigned)sel < (unsigned)rg.n_far) {
         my_row = sel;
         my_flag = POOLED ? 3 : 1;

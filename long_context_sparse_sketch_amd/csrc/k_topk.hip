@@ -9,17 +9,22 @@
 //     atomics (order-independent, so deterministic) into a workspace region
 //     that is zero at rest.  Either the score kernel accumulates it while it
 //     streams the sketches, or topk_hist_kernel does it here.
-//   threshold (one wave per segment): validates the histogram and derives the
-//     threshold bin b1 (an invalid histogram makes every element a candidate).
-//   filter: each wave compacts the candidates (bin >= b1) of its 1024-token
-//     sub-chunk IN ORDER (ballot + popcount).
-//   final (one workgroup per segment): caches the candidates in LDS and runs
-//     an exact two-level radix select on them -- it never trusts the
-//     histogram beyond the filter's pruning: if fewer than k candidates came
-//     through (a histogram that was not zero at rest), it selects from the
-//     raw scores instead.  One ordered pass then emits score > T plus the
-//     lowest-index ties at T, ascending, without a sort.  It returns the
-//     segment's histogram to zero.
+//   filter: every workgroup first validates the segment's level-1 histogram
+//     and derives the threshold bin b1 from it (the same value in every
+//     workgroup; an invalid histogram makes every element a candidate), then
+//     each wave compacts the candidates (bin >= b1) of its 1024-token
+//     sub-chunk IN ORDER (ballot + popcount), and adds the low 10 bits of the
+//     candidates inside bin b1 to the level-2 histogram (also zero at rest).
+//   final (one workgroup per segment): guesses the threshold key T from the
+//     level-2 histogram, loads the candidates into registers in index order
+//     and counts, from the data, the candidates above T and equal to T.  When
+//     those counts show that T is the k-th largest key, it emits every
+//     candidate above T and the lowest-index ties at T, ascending, without a
+//     sort.  Otherwise (a workspace that was not zero at rest) it derives T
+//     from the candidates themselves with an exact two-level radix select in
+//     LDS -- or from the raw scores, if fewer than k candidates came through.
+//     The histograms are never trusted beyond what the data confirms.  It
+//     returns the segment's histograms to zero.
 #include "sks_internal.h"
 
 namespace sks {
@@ -27,9 +32,13 @@ namespace {
 
 constexpr int TK_THREADS = 256;
 constexpr int TF_THREADS = 1024;
-constexpr int TF_CACHE = 8192;                     // candidates cached in LDS
+constexpr int TF_WAVES = TF_THREADS / 64;
+constexpr int TF_CACHE = 8192;                     // candidates held by one final workgroup
+constexpr int TF_PERT = TF_CACHE / TF_THREADS;     // consecutive candidates per thread
 constexpr int FILTER_ITERS = TK_SUB / 64;          // 16 loads in flight per lane
+constexpr int HIST2_DIRECT_MAX = 4096;             // level-2 histogram built when bin b1 is this small
 static_assert(TK_CHUNK == TK_SUB * (TK_THREADS / 64), "one sub-chunk per wave");
+static_assert(TF_CACHE < 65536, "packed 16-bit counts in the emission scan");
 
 struct SegGeom {
   int b, i, h, n_far, k_eff;
@@ -48,50 +57,56 @@ __device__ __forceinline__ SegGeom seg_geom(int seg, const int32_t *seq_len, int
   return g;
 }
 
-// Inclusive block-wide prefix sum; `tot` receives the block total.
-// `scratch` must hold blockDim.x / 64 ints.  Contains __syncthreads().
+// Inclusive block-wide prefix sum of NW waves; `tot` receives the block
+// total.  `scratch` holds NW ints.  With REUSE a second barrier lets the
+// caller use the same scratch again right away.
+template <int NW, bool REUSE>
 __device__ int block_incl_scan(int v, int *scratch, int &tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_add(v);
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  tot = 0;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int n = __shfl_up(v, off);
-    if (lane >= off) v += n;
+  for (int w = 0; w < NW; ++w) {
+    const int t = scratch[w];
+    before += w < wave ? t : 0;
+    tot += t;
   }
-  if (lane == 63) scratch[wave] = v;
-  __syncthreads();
-  if (wave == 0) {
-    int w = lane < nw ? scratch[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      int n = __shfl_up(w, off);
-      if (lane >= off) w += n;
-    }
-    if (lane < nw) scratch[lane] = w;
-  }
-  __syncthreads();
-  const int prefix = wave > 0 ? scratch[wave - 1] : 0;
-  tot = scratch[nw - 1];
-  __syncthreads();
-  return v + prefix;
+  if (REUSE) __syncthreads();
+  return incl + before;
 }
 
-// Wave-level version over an LDS histogram of NBINS bins, no barriers: lane
-// l owns bins [l * NBINS/64, (l+1) * NBINS/64).  The histogram is first validated (every
-// bin in [0, n] and the total exactly n); an invalid one (a workspace that
-// was not zero at rest) yields bin 0, i.e. every element is a candidate, so
-// that all waves of all workgroups of a segment agree on the same threshold.
-// Returns the threshold bin; `above` receives sum_{b' > b} hist[b'].
-// LDS histograms are stored padded (see hpad) so that 64 lanes reading their
-// contiguous bins hit distinct banks.
+// Exclusive block-wide running maximum of non-negative values (0 before the
+// first thread); `scratch` holds NW ints and is not reused.
+template <int NW>
+__device__ int block_excl_max(int v, int *scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_max(v);
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) before = max(before, w < wave ? scratch[w] : 0);
+  const int prev = __builtin_amdgcn_update_dpp(0, incl, DPP_ROW_SHR + 1, 0xF, 0xF, false);
+  // the lane before the first of a row is the last lane of the previous row
+  const int r15 = __builtin_amdgcn_readlane(incl, 15), r31 = __builtin_amdgcn_readlane(incl, 31),
+            r47 = __builtin_amdgcn_readlane(incl, 47);
+  const int row = lane >> 4;
+  const int prev_row = row == 0 ? 0 : (row == 1 ? r15 : (row == 2 ? r31 : r47));
+  return max(before, (lane & 15) ? prev : prev_row);
+}
+
+// LDS histograms are stored padded so that 64 lanes reading their contiguous
+// bins hit distinct banks.
 template <int NBINS>
 __device__ __forceinline__ int hpad(int b) { return b + b / (NBINS / 64); }
 template <int NBINS>
 constexpr int hpad_size() { return NBINS + 64; }
 
-// Same search over a padded LDS histogram of NBINS bins.  The histogram is
-// validated first (every bin in [0, n], total exactly n); an invalid one (a
-// workspace that was not zero at rest) yields bin 0, i.e. every element is a
-// candidate, the same answer for every reader of the same histogram.
+// Threshold search by one wave over a padded LDS histogram of NBINS bins
+// (see wave_threshold_regs: an invalid histogram yields bin 0).
 template <int NBINS>
 __device__ int wave_threshold_bin(const int *hist, int need, int n, int &above) {
   constexpr int PER = NBINS / 64;
@@ -131,51 +146,95 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(
     if (lh[k]) atomicAdd(&gh[k], lh[k]);
 }
 
-// One wave per segment: validate the level-1 histogram and store the
-// threshold bin b1 once (0 when every element must be a candidate).  Lane l
-// loads its 32 contiguous bins as 8 independent 16-byte loads.
-__global__ __launch_bounds__(64) void topk_threshold_kernel(
-    const int32_t *__restrict__ seq_len, const int32_t *__restrict__ hist1,
-    int32_t *__restrict__ thr, int R, int Hkv, int T_max, int window, int pool, int topk) {
-  constexpr int PER = HIST1_BINS / 64;
-  const int seg = blockIdx.x, lane = threadIdx.x;
-  const int4 *gh = reinterpret_cast<const int4 *>(hist1 + (size_t)seg * HIST1_BINS + lane * PER);
-  int v[PER];
+// Level-1 threshold of one segment, computed by a whole filter workgroup
+// (every workgroup of the segment computes the same value from the same
+// histogram).  Thread t holds bins [8t, 8t+8).  The histogram is validated
+// first (every bin in [0, n], total exactly n); an invalid one (a workspace
+// that was not zero at rest) yields bin 0 -- every element a candidate.
+// Returns (b1, elements in bins above b1, valid, elements in bin b1).
+// Contains two __syncthreads().
+constexpr int TH_PER = HIST1_BINS / TK_THREADS;
+static_assert(TH_PER == 8, "two 16-byte loads of bins per thread");
+
+__device__ int4 block_threshold(const int (&v)[TH_PER], int need, int n, int *scratch, int *res) {
+  constexpr int NW = TK_THREADS / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cap = n + 1;
+  int sum = 0;
+  bool bad = false;
 #pragma unroll
-  for (int k = 0; k < PER / 4; ++k) {
-    const int4 w = gh[k];
-    v[4 * k] = w.x;
-    v[4 * k + 1] = w.y;
-    v[4 * k + 2] = w.z;
-    v[4 * k + 3] = w.w;
+  for (int k = 0; k < TH_PER; ++k) {
+    bad |= v[k] < 0 || v[k] > n;
+    sum = min(sum + min(max(v[k], 0), cap), cap);
   }
-  const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
-  int b1 = 0, above = 0;
-  bool valid = false;
-  if (g.k_eff < g.n_far) b1 = wave_threshold_regs<PER>(v, g.k_eff, g.n_far, above, valid);
-  if (lane == 0) reinterpret_cast<int4 *>(thr)[seg] = make_int4(b1, above, valid, 0);
+  const int incl = wave_incl_add_sat(sum, cap);
+  const bool wbad = __ballot(bad) != 0;
+  if (lane == 63) scratch[wave] = wbad ? -1 : incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  bool invalid = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = scratch[w];
+    invalid |= t < 0;
+    before += w < wave ? t : 0;
+    all = min(all + max(t, 0), cap);
+  }
+  if (invalid || all != n) return make_int4(0, 0, 0, 0);   // uniform
+  // valid: every partial sum is exact
+  int ab = n - (incl + before);                  // elements of higher threads' bins
+  if (ab < need && ab + sum >= need) {           // exactly one thread
+    int b = -1;
+#pragma unroll
+    for (int k = TH_PER - 1; k >= 0; --k) {
+      if (b < 0) {
+        if (ab + v[k] >= need) {
+          b = threadIdx.x * TH_PER + k;
+          res[0] = b;
+          res[1] = ab;
+          res[2] = v[k];
+        } else {
+          ab += v[k];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  return make_int4(res[0], res[1], 1, res[2]);
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
     const int32_t *__restrict__ scores, const int32_t *__restrict__ seq_len,
-    const int32_t *__restrict__ thr, int32_t *__restrict__ cnt, int2 *__restrict__ cand,
-    int n_sub_max, int R, int Hkv, int T_max, int NB, int window, int pool, int topk) {
+    const int32_t *__restrict__ hist1, int32_t *__restrict__ hist2, int32_t *__restrict__ thr,
+    int32_t *__restrict__ cnt, int2 *__restrict__ cand, int n_sub_max, int R, int Hkv, int T_max,
+    int NB, int window, int pool, int topk) {
+  __shared__ int scratch[TK_THREADS / 64];
+  __shared__ int res[3];
   const int seg = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = blockIdx.x * (TK_CHUNK / TK_SUB) + wave;
   const int s0 = sub * TK_SUB;
   const int32_t *row = scores + (size_t)seg * NB;
-  // Issue this wave's score loads before the length is known, all at once:
-  // the index is clamped below NB (always in bounds) instead of branching
-  // around the load, and entries past the far region are masked later.
+  // Issue this wave's score loads and the histogram loads before the length
+  // is known, all at once: the index is clamped below NB (always in bounds)
+  // instead of branching around the load, and entries past the far region
+  // are masked later.
   int raw[FILTER_ITERS];
 #pragma unroll
   for (int r = 0; r < FILTER_ITERS; ++r) raw[r] = row[min(s0 + r * 64 + lane, NB - 1)];
-  const int b1 = thr[4 * seg];
+  const int4 *gh = reinterpret_cast<const int4 *>(hist1 + (size_t)seg * HIST1_BINS) + 2 * threadIdx.x;
+  const int4 h0 = gh[0], h1v = gh[1];
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
-  if (g.k_eff >= g.n_far || s0 >= g.n_far) return;   // uniform per wave
+  if (g.k_eff >= g.n_far || blockIdx.x * TK_CHUNK >= g.n_far) return;   // uniform per workgroup
+  const int v[TH_PER] = {h0.x, h0.y, h0.z, h0.w, h1v.x, h1v.y, h1v.z, h1v.w};
+  const int4 th = block_threshold(v, g.k_eff, g.n_far, scratch, res);
+  if (blockIdx.x == 0 && threadIdx.x == 0) reinterpret_cast<int4 *>(thr)[seg] = th;
+  const int b1 = th.x;
+  const bool build_h2 = th.z && th.w <= HIST2_DIRECT_MAX;
+  if (s0 >= g.n_far) return;                     // uniform per wave
   const int s1 = min(g.n_far, s0 + TK_SUB);
   int2 *dst = cand + ((size_t)seg * n_sub_max + sub) * TK_SUB;
+  int32_t *h2 = hist2 + (size_t)seg * HIST2_BINS;
   int n = 0;
 #pragma unroll
   for (int r = 0; r < FILTER_ITERS; ++r) {
@@ -183,7 +242,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
     const int key = biased_key(raw[r]);
     const bool f = t < s1 && (key >> HIST2_BITS) >= b1;
     const unsigned long long m = __ballot(f);
-    if (f) dst[n + __popcll(m & ((1ull << lane) - 1ull))] = make_int2(t, key);
+    if (f) {
+      dst[n + __popcll(m & ((1ull << lane) - 1ull))] = make_int2(t, key);
+      if (build_h2 && (key >> HIST2_BITS) == b1) atomicAdd(&h2[key & (HIST2_BINS - 1)], 1);
+    }
     n += __popcll(m);
   }
   if (lane == 0) cnt[(size_t)seg * n_sub_max + sub] = n;
@@ -191,42 +253,80 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
 
 __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
     const int32_t *__restrict__ scores, const int32_t *__restrict__ seq_len,
-    int32_t *__restrict__ hist1, const int32_t *__restrict__ thr, const int32_t *__restrict__ cnt,
-    const int2 *__restrict__ cand, int n_sub_max, int R, int Hkv, int T_max, int NB, int window,
-    int pool, int topk, int32_t *__restrict__ idx, int32_t *__restrict__ n_sel) {
+    int32_t *__restrict__ hist1, int32_t *__restrict__ hist2, const int32_t *__restrict__ thr,
+    const int32_t *__restrict__ cnt, const int2 *__restrict__ cand, int n_sub_max, int R, int Hkv,
+    int T_max, int NB, int window, int pool, int topk, int32_t *__restrict__ idx,
+    int32_t *__restrict__ n_sel) {
   __shared__ int h1[hpad_size<HIST1_BINS>()];
   __shared__ int h2[hpad_size<HIST2_BINS>()];
   __shared__ int pre[TK_MAX_SUBS + 1];
-  __shared__ int2 cache[TF_CACHE];
-  __shared__ int scratch[TF_THREADS / 64];
-  __shared__ int res[4];
+  __shared__ int2 cache[TF_CACHE];               // .x doubles as the sub-list start marks
+  __shared__ int sc_pre[TF_WAVES], sc_own[TF_WAVES], sc_cnt[TF_WAVES];
+  __shared__ int res[6];
   const int seg = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int32_t *gc = cnt + (size_t)seg * n_sub_max;
-  // the first round of sub-list counts, loaded before the length is known
-  int cv0 = threadIdx.x < n_sub_max ? gc[threadIdx.x] : 0;
-  const int4 th = reinterpret_cast<const int4 *>(thr)[seg];   // (b1, above1, valid, -)
-  for (int k = threadIdx.x; k < hpad_size<HIST1_BINS>(); k += TF_THREADS) h1[k] = 0;
-  for (int k = threadIdx.x; k < hpad_size<HIST2_BINS>(); k += TF_THREADS) h2[k] = 0;
+  int32_t *gh2 = hist2 + (size_t)seg * HIST2_BINS;
+  // loads first: the first round of sub-list counts, the threshold record
+  // and (wave 0) the level-2 histogram, lane l holding bins [16l, 16l+16)
+  const int cv0 = threadIdx.x < n_sub_max ? gc[threadIdx.x] : 0;
+  const int4 th = reinterpret_cast<const int4 *>(thr)[seg];   // (b1, above b1, valid, in b1)
+  constexpr int H2_PER = HIST2_BINS / 64;
+  int hv[H2_PER];
+  if (wave == 0) {
+#pragma unroll
+    for (int k = 0; k < H2_PER / 4; ++k) {
+      const int4 w = reinterpret_cast<const int4 *>(gh2 + lane * H2_PER)[k];
+      hv[4 * k] = w.x;
+      hv[4 * k + 1] = w.y;
+      hv[4 * k + 2] = w.z;
+      hv[4 * k + 3] = w.w;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < TF_PERT; ++q) cache[threadIdx.x * TF_PERT + q].x = 0;   // no mark
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   int32_t *out = idx + (size_t)seg * topk;
-  // the filter has run: the segment's histogram returns to zero
-  int32_t *gh = hist1 + (size_t)seg * HIST1_BINS;
-  for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh[k] = 0;
+  // the filter has run: the segment's level-1 histogram returns to zero
+  int32_t *gh1 = hist1 + (size_t)seg * HIST1_BINS;
+  for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh1[k] = 0;
   if (threadIdx.x == 0 && n_sel) n_sel[seg] = g.k_eff;
+
+  // wave 0: the threshold guess T from the level-2 histogram (-1: none),
+  // then that histogram returns to zero (its values are consumed)
+  if (wave == 0) {
+    int T = -1;
+    if (g.k_eff < g.n_far && th.z && th.w >= 0 && th.w <= HIST2_DIRECT_MAX && th.x >= 0 &&
+        th.x < HIST1_BINS) {
+      int above;
+      bool valid;
+      const int b2 = wave_threshold_regs<H2_PER>(hv, g.k_eff - th.y, th.w, above, valid);
+      if (valid) T = (th.x << HIST2_BITS) | b2;
+    }
+    if (lane == 0) res[5] = T;
+#pragma unroll
+    for (int k = 0; k < H2_PER / 4; ++k)
+      reinterpret_cast<int4 *>(gh2 + lane * H2_PER)[k] = make_int4(0, 0, 0, 0);
+  }
   if (g.k_eff >= g.n_far) {                      // every far entry is selected
     for (int j = threadIdx.x; j < topk; j += TF_THREADS) out[j] = j < g.n_far ? j : -1;
     return;
   }
 
-  // candidate list: exclusive prefix over the sub-list counts
+  // candidate list: exclusive prefix over the sub-list counts; every
+  // non-empty sub-list also marks its first slot with its number + 1
   const int n_sub = (g.n_far + TK_SUB - 1) / TK_SUB;
   int carry = 0;
   for (int base = 0; base < n_sub; base += TF_THREADS) {
     const int sidx = base + threadIdx.x;
     const int v = sidx < n_sub ? (base == 0 ? cv0 : gc[sidx]) : 0;
     int tot;
-    const int incl = block_incl_scan(v, scratch, tot);
-    if (sidx < n_sub) pre[sidx] = carry + incl - v;
+    const int incl = block_incl_scan<TF_WAVES, true>(v, sc_pre, tot);
+    const int start = carry + incl - v;
+    if (sidx < n_sub) {
+      pre[sidx] = start;
+      if (v > 0 && start < TF_CACHE) cache[start].x = sidx + 1;
+    }
     carry += tot;
   }
   if (threadIdx.x == 0) pre[n_sub] = carry;
@@ -237,7 +337,69 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
   const int m = raw ? g.n_far : carry;
   const int2 *cseg = cand + (size_t)seg * n_sub_max * TK_SUB;
   const int32_t *srow = scores + (size_t)seg * NB;
-  auto get = [&](int o) -> int2 {
+  const bool cached = !raw && m <= TF_CACHE;
+  const int o0 = threadIdx.x * TF_PERT;          // this thread's slots [o0, o0 + TF_PERT)
+
+  if (cached) {
+    // The sub-list holding slot o is the last mark at or before o: a running
+    // maximum over the marks of this thread's slots, then across the block.
+    // Each thread reads and later overwrites only its own slots.
+    int mk[TF_PERT];
+    int run = 0;
+#pragma unroll
+    for (int q = 0; q < TF_PERT; ++q) {
+      run = max(run, cache[o0 + q].x);
+      mk[q] = run;
+    }
+    const int before = block_excl_max<TF_WAVES>(run, sc_own);
+    int2 c[TF_PERT];
+#pragma unroll
+    for (int q = 0; q < TF_PERT; ++q) {
+      const int o = min(o0 + q, m - 1);
+      const int s = max(max(before, mk[q]), 1) - 1;
+      c[q] = cseg[(size_t)s * TK_SUB + min(max(o - pre[s], 0), TK_SUB - 1)];
+    }
+    const int T = res[5];
+    if (T >= 0) {
+      // Count, from the data, the candidates above T and equal to T.  Every
+      // element with key >= T is a candidate (its bin is >= b1), so T is the
+      // k-th largest key exactly when above < k <= above + equal.
+      int gt = 0, tie = 0;
+#pragma unroll
+      for (int q = 0; q < TF_PERT; ++q) {
+        const bool in = o0 + q < m;
+        gt += in && c[q].y > T;
+        tie += in && c[q].y == T;
+      }
+      const int packed = gt | (tie << 16);
+      int tot;
+      const int ex = block_incl_scan<TF_WAVES, false>(packed, sc_cnt, tot) - packed;
+      const int gt_tot = tot & 0xffff, tie_tot = tot >> 16;
+      if (gt_tot < g.k_eff && gt_tot + tie_tot >= g.k_eff) {      // uniform
+        const int need = g.k_eff - gt_tot;     // ties at T to take, lowest index first
+        int gt_before = ex & 0xffff, tie_before = ex >> 16;
+#pragma unroll
+        for (int q = 0; q < TF_PERT; ++q) {
+          const bool in = o0 + q < m;
+          const bool is_gt = in && c[q].y > T, is_tie = in && c[q].y == T;
+          const bool sel = is_gt || (is_tie && tie_before < need);
+          const int pos = gt_before + min(tie_before, need);
+          if (sel) out[pos] = c[q].x;
+          gt_before += is_gt;
+          tie_before += is_tie;
+        }
+        for (int j = g.k_eff + threadIdx.x; j < topk; j += TF_THREADS) out[j] = -1;
+        return;
+      }
+    }
+    // the guess did not hold: keep the candidates in LDS for the exact path
+#pragma unroll
+    for (int q = 0; q < TF_PERT; ++q)
+      if (o0 + q < m) cache[o0 + q] = c[q];
+  }
+
+  // ---- exact path without the level-2 histogram
+  auto get = [&](int o) -> int2 {                // uncached access
     if (raw) return make_int2(o, biased_key(srow[o]));
     int lo = 0, hi = n_sub;                      // last sub-list s with pre[s] <= o
     while (hi - lo > 1) {
@@ -246,68 +408,56 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
     }
     return cseg[(size_t)lo * TK_SUB + (o - pre[lo])];
   };
-  const bool cached = m <= TF_CACHE;
-  if (cached) {
-    // all lookups first, then all loads in flight together, then the stores
-    constexpr int PERT = TF_CACHE / TF_THREADS;
-    int2 tmp[PERT];
-#pragma unroll
-    for (int k = 0; k < PERT; ++k) tmp[k] = get(min(threadIdx.x + k * TF_THREADS, m - 1));
-#pragma unroll
-    for (int k = 0; k < PERT; ++k) {
-      const int o = threadIdx.x + k * TF_THREADS;
-      if (o < m) cache[o] = tmp[k];
-    }
-  }
-  __syncthreads();
   auto fetch = [&](int o) -> int2 { return cached ? cache[o] : get(o); };
+  for (int k = threadIdx.x; k < hpad_size<HIST1_BINS>(); k += TF_THREADS) h1[k] = 0;
+  for (int k = threadIdx.x; k < hpad_size<HIST2_BINS>(); k += TF_THREADS) h2[k] = 0;
+  if (threadIdx.x == 0) res[4] = 0;
+  __syncthreads();
 
-  // exact threshold key T: level 1 (top 11 bits), level 2 (low 10 bits).
-  // With a valid histogram the candidates are exactly the elements of bins
-  // >= b1 and level 1 is already known; otherwise derive it from the
-  // candidates themselves.
-  // Candidates are exactly the elements of bins >= thr.x (the filter used the
-  // same value).  If that bin is a legal threshold -- the candidates above it
-  // number fewer than k, counted from the data, never from the histogram --
-  // level 1 is known; otherwise derive it from the candidates.
+  // Level 1 (top 11 bits): the candidates are exactly the elements of bins
+  // >= thr.x.  If that bin is a legal threshold -- fewer than k candidates
+  // above it, counted here from the data -- level 1 is known; otherwise it is
+  // derived from the candidates' own histogram.
   bool fast = th.z && !raw && th.x >= 0 && th.x < HIST1_BINS;
-  int above_data = 0;
   if (fast) {
     int part = 0;
     for (int o = threadIdx.x; o < m; o += TF_THREADS) part += (fetch(o).y >> HIST2_BITS) > th.x;
-    block_incl_scan(part, scratch, above_data);
-    fast = above_data < g.k_eff;                 // uniform: block total
-  }
-  if (fast) {
-    if (threadIdx.x == 0) {
+    part = __builtin_amdgcn_readlane(wave_incl_add(part), 63);
+    if (lane == 0 && part) atomicAdd(&res[4], part);
+    __syncthreads();
+    const int above_data = res[4];
+    fast = above_data < g.k_eff;                 // uniform
+    if (fast && threadIdx.x == 0) {
       res[0] = th.x;
-      res[1] = g.k_eff - above_data;
+      res[1] = g.k_eff - above_data;             // still needed from bin b1
       h1[hpad<HIST1_BINS>(th.x)] = m - above_data;   // candidates in bin b1
     }
-  } else {
+  }
+  if (!fast) {
     for (int o = threadIdx.x; o < m; o += TF_THREADS)
       atomicAdd(&h1[hpad<HIST1_BINS>(fetch(o).y >> HIST2_BITS)], 1);
     __syncthreads();
-    if (threadIdx.x < 64) {
+    if (wave == 0) {
       int above;
       const int bb = wave_threshold_bin<HIST1_BINS>(h1, g.k_eff, m, above);
-      if (threadIdx.x == 0) {
+      if (lane == 0) {
         res[0] = bb;
-        res[1] = g.k_eff - above;                // still needed from bin b1
+        res[1] = g.k_eff - above;
       }
     }
   }
   __syncthreads();
   const int b1 = res[0], need1 = res[1];
+  // level 2 (low 10 bits) over the candidates of bin b1
   for (int o = threadIdx.x; o < m; o += TF_THREADS) {
     const int2 c = fetch(o);
     if ((c.y >> HIST2_BITS) == b1) atomicAdd(&h2[hpad<HIST2_BINS>(c.y & (HIST2_BINS - 1))], 1);
   }
   __syncthreads();
-  if (threadIdx.x < 64) {
+  if (wave == 0) {
     int above;
     const int b2 = wave_threshold_bin<HIST2_BINS>(h2, need1, h1[hpad<HIST1_BINS>(b1)], above);
-    if (threadIdx.x == 0) {
+    if (lane == 0) {
       res[2] = (b1 << HIST2_BITS) | b2;
       res[3] = need1 - above;                    // ties at T to take, lowest index first
     }
@@ -319,18 +469,18 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
   // one block scan of packed (greater-than, tie) counts per round
   int run_gt = 0, run_tie = 0;
   for (int base = 0; base < m; base += 4 * TF_THREADS) {
-    const int o0 = base + 4 * threadIdx.x;
+    const int e0 = base + 4 * threadIdx.x;
     int2 c[4];
     int gt = 0, tie = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      c[q] = o0 + q < m ? fetch(o0 + q) : make_int2(0, -1);
+      c[q] = e0 + q < m ? fetch(e0 + q) : make_int2(0, -1);
       gt += c[q].y > T;
       tie += c[q].y == T;
     }
     const int packed = gt | (tie << 16);
     int tot;
-    const int ex = block_incl_scan(packed, scratch, tot) - packed;
+    const int ex = block_incl_scan<TF_WAVES, true>(packed, sc_pre, tot) - packed;
     int gt_before = run_gt + (ex & 0xffff), tie_before = run_tie + (ex >> 16);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -351,7 +501,8 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
 
 size_t hist_region_bytes(const Shape &s) {
   const size_t nseg = (size_t)s.B * s.R * s.Hkv;
-  return align_up(nseg * HIST1_BINS * 4, 256) + align_up(nseg * 16, 256);
+  return align_up(nseg * HIST1_BINS * 4, 256) + align_up(nseg * HIST2_BINS * 4, 256) +
+         align_up(nseg * 16, 256);
 }
 
 size_t topk_scratch_bytes(const Shape &s) {
@@ -368,6 +519,8 @@ TopkWs topk_ws_carve(const Shape &s, void *ws) {
   char *q = base;
   w.hist1 = reinterpret_cast<int32_t *>(q);
   q += align_up(nseg * HIST1_BINS * 4, 256);
+  w.hist2 = reinterpret_cast<int32_t *>(q);
+  q += align_up(nseg * HIST2_BINS * 4, 256);
   w.counters = reinterpret_cast<int32_t *>(q);
   char *p = base + hist_region_bytes(s);
   w.scratch = p;
@@ -394,15 +547,14 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
     if (!hist_ready)
       topk_hist_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, s.R, s.Hkv,
                                                     s.T_max, s.NB, s.window, s.pool, s.topk);
-    topk_threshold_kernel<<<nseg, 64, 0, st>>>(seq_len, w.hist1, w.counters, s.R, s.Hkv,
-                                               s.T_max, s.window, s.pool, s.topk);
-    topk_filter_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.counters, w.cnt, w.cand,
-                                                    w.nchunk, s.R, s.Hkv, s.T_max, s.NB,
-                                                    s.window, s.pool, s.topk);
+    topk_filter_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.hist2,
+                                                    w.counters, w.cnt, w.cand, w.nchunk, s.R,
+                                                    s.Hkv, s.T_max, s.NB, s.window, s.pool,
+                                                    s.topk);
   }
-  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.counters, w.cnt,
-                                                 w.cand, w.nchunk, s.R, s.Hkv, s.T_max, s.NB,
-                                                 s.window, s.pool, s.topk, idx, n_sel);
+  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.hist2, w.counters,
+                                                 w.cnt, w.cand, w.nchunk, s.R, s.Hkv, s.T_max,
+                                                 s.NB, s.window, s.pool, s.topk, idx, n_sel);
   return hipGetLastError();
 }
 

@@ -122,41 +122,84 @@ __device__ __forceinline__ float row16_sum_f(float x) {
   return x;
 }
 
+// ---------------------------------------------------------------- wave scans
+// Inclusive scans over the 64 lanes of a wave: DPP row shifts inside each row
+// of 16 lanes (a lane whose source lies outside its row adds 0), then the
+// totals of the lower rows, read from lanes 15, 31 and 47.
+constexpr int DPP_ROW_SHR = 0x110;     // row_shr:n = 0x110 + n
+
+template <int N>
+__device__ __forceinline__ int dpp_shr(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, DPP_ROW_SHR + N, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ int wave_incl_add(int x) {
+  x += dpp_shr<1>(x);
+  x += dpp_shr<2>(x);
+  x += dpp_shr<4>(x);
+  x += dpp_shr<8>(x);
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+// Saturating version for non-negative x <= cap < 2^29: every partial sum is
+// min(true sum, cap), so a total below cap is exact.
+__device__ __forceinline__ int wave_incl_add_sat(int x, int cap) {
+  x = min(x + dpp_shr<1>(x), cap);
+  x = min(x + dpp_shr<2>(x), cap);
+  x = min(x + dpp_shr<4>(x), cap);
+  x = min(x + dpp_shr<8>(x), cap);
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return min(x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0), cap);
+}
+
+// Running maximum of non-negative values.
+__device__ __forceinline__ int wave_incl_max(int x) {
+  x = max(x, dpp_shr<1>(x));
+  x = max(x, dpp_shr<2>(x));
+  x = max(x, dpp_shr<4>(x));
+  x = max(x, dpp_shr<8>(x));
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return max(x, max(row > 0 ? r0 : 0, max(row > 1 ? r1 : 0, row > 2 ? r2 : 0)));
+}
+
 // ---------------------------------------------------------------- selection threshold
 // Threshold search over a histogram held in registers, lane l holding bins
-// [l*PER, (l+1)*PER) in v[].  No barriers.  Returns the bin b with
-// sum_{b' >= b} >= need > sum_{b' > b}; `above` receives sum_{b' > b}.
+// [l*PER, (l+1)*PER) in v[].  No barriers.  The histogram is validated first
+// (every bin in [0, n], total exactly n, n < 2^28); an invalid one gives
+// valid = false and bin 0.  Otherwise returns the bin b with
+// sum_{b' >= b} >= need > sum_{b' > b} (0 if there is none); `above` receives
+// sum_{b' > b}.
 template <int PER>
 __device__ __forceinline__ int wave_threshold_regs(const int (&v)[PER], int need, int n, int &above,
-                                   bool &valid) {
-  const int lane = threadIdx.x & 63;
-  long long sum = 0;
+                                                   bool &valid) {
+  const int cap = n + 1;
+  int sum = 0;
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     bad |= v[k] < 0 || v[k] > n;
-    sum += v[k];
+    sum = min(sum + min(max(v[k], 0), cap), cap);
   }
-  long long tot = sum;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+  const int incl = wave_incl_add_sat(sum, cap);
+  const int tot = __builtin_amdgcn_readlane(incl, 63);
   above = 0;
-  valid = !__any(bad) && tot == (long long)n;
+  valid = __ballot(bad) == 0 && tot == n;
   if (!valid) return 0;
-  int incl = (int)sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
   int ab = n - incl;                         // bins of higher lanes
   int b = -1, ab_b = 0;
-  if (ab < need && ab + (int)sum >= need) {
+  if (ab < need && ab + sum >= need) {
 #pragma unroll
     for (int k = PER - 1; k >= 0; --k) {
       if (b < 0) {
         if (ab + v[k] >= need) {
-          b = lane * PER + k;
+          b = (int)(threadIdx.x & 63) * PER + k;
           ab_b = ab;
         } else {
           ab += v[k];
@@ -167,10 +210,9 @@ __device__ __forceinline__ int wave_threshold_regs(const int (&v)[PER], int need
   const unsigned long long who = __ballot(b >= 0);
   if (who == 0) return 0;
   const int src = __ffsll((long long)who) - 1;
-  above = __shfl(ab_b, src);
-  return __shfl(b, src);
+  above = __builtin_amdgcn_readlane(ab_b, src);
+  return __builtin_amdgcn_readlane(b, src);
 }
-
 
 // ---------------------------------------------------------------- launchers
 struct Shape {
@@ -185,8 +227,9 @@ hipError_t launch_sketch_query(const uint16_t *q, int B, int R, int Hq, int Hkv,
                                const float *basis, int basis_per_head, int8_t *qsk,
                                float *qscale, hipStream_t st);
 // Workspace layout: [hist region | scratch].  The hist region holds the
-// level-1 selection histograms [nseg][2048], zero at rest (the calls that use
-// them return them to zero), and the per-segment threshold bins.
+// level-1 and level-2 selection histograms [nseg][2048] and [nseg][1024],
+// zero at rest (the calls that use them return them to zero), and the
+// per-segment threshold bins.
 // (Kernels here never communicate between workgroups inside one launch: a
 // device-scope fence per workgroup costs far more on this GPU than a kernel
 // boundary.)  The scratch holds
@@ -203,7 +246,8 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
 
 struct TopkWs {
   int32_t *hist1;     // [nseg][HIST1_BINS], zero at rest
-  int32_t *counters;  // [nseg][4]: threshold bin, count above it, histogram valid
+  int32_t *hist2;     // [nseg][HIST2_BINS], zero at rest
+  int32_t *counters;  // [nseg][4]: threshold bin b1, count above it, valid, count in b1
   char *scratch;      // start of the scratch area
   int32_t *cnt;       // [nseg][nchunk]
   int2 *cand;         // [nseg][nchunk * TK_SUB]

@@ -27,15 +27,30 @@ def test_algorithmic_bytes_of_the_250k_workload():
 
 
 def test_counted_traffic_follows_the_score_sources(tmp_path, monkeypatch):
-    """The committed counter summary is used only for its workload and only
-    while the score kernel's sources hash to the recorded value."""
+    """A counter summary is used only for its workload and only while the
+    score kernel's sources hash to the value recorded with it."""
+    import hashlib
     sys.path.insert(0, ROOT)
     import bench
-    src = open(bench.COUNTERS.format(workload="multi_agent_250k")).read()
-    t = bench.counted_traffic("multi_agent_250k")
-    assert t is not None and 5.0e8 < t < 6.0e8                # ~1.07 x the 503.6 MB of sketch
-    assert bench.counted_traffic("tiny") is None
-    fake = tmp_path / "score_kernel_multi_agent_250k_hbm_counters.txt"
-    fake.write_text(src.replace("score_sources_sha256: ", "score_sources_sha256: 00"))
+    h = hashlib.sha256()
+    for f in bench.SCORE_SOURCES:
+        h.update(open(os.path.join(ROOT, "long_context_sparse_sketch_amd", "csrc", f), "rb").read())
+    body = ("workload: multi_agent_250k\nkernel: score_kernel\n"
+            f"score_sources_sha256: {h.hexdigest()}\ntraffic_bytes_per_launch: 537628512\n")
     monkeypatch.setattr(bench, "COUNTERS", str(tmp_path / "score_kernel_{workload}_hbm_counters.txt"))
+    (tmp_path / "score_kernel_multi_agent_250k_hbm_counters.txt").write_text(body)
+    assert bench.counted_traffic("multi_agent_250k") == 537628512
+    assert bench.counted_traffic("tiny") is None
+    (tmp_path / "score_kernel_multi_agent_250k_hbm_counters.txt").write_text(
+        body.replace("score_sources_sha256: ", "score_sources_sha256: 00"))
     assert bench.counted_traffic("multi_agent_250k") is None
+
+
+def test_committed_counter_summary_parses():
+    sys.path.insert(0, ROOT)
+    import bench
+    fields = dict(ln.split(":", 1) for ln in open(bench.COUNTERS.format(workload="multi_agent_250k"))
+                  if ln.startswith(("workload:", "traffic_bytes_per_launch:", "score_sources_sha256:")))
+    assert fields["workload"].strip() == "multi_agent_250k"
+    assert 5.0e8 < int(fields["traffic_bytes_per_launch"]) < 6.0e8   # ~1.07 x the 503.6 MB of sketch
+    assert len(fields["score_sources_sha256"].strip()) == 64
