@@ -14,7 +14,10 @@
 // of each row (top 11 bits of the biased score, see k_topk.hip) in LDS while
 // the scores are in registers, and adds its non-zero bins to the workspace
 // histogram with integer atomics: the top-k pass then needs no extra read of
-// the scores to find its threshold bin.
+// the scores to find its threshold bin.  It also records the largest biased
+// score of each row in its 1024-entry chunk (plus one; 0 for an empty
+// chunk), so that the top-k filter reads only the chunks that can hold a
+// candidate.
 #include "sks_internal.h"
 
 namespace sks {
@@ -39,8 +42,11 @@ template <int R, bool HIST>
 __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     const int8_t *__restrict__ qsk, const int8_t *__restrict__ S,
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ scores,
-    int32_t *__restrict__ hist1, int Hkv, int T_max, int NB, int window, int pool, int topk) {
+    int32_t *__restrict__ hist1, int32_t *__restrict__ cmax, int n_sub_max, int Hkv, int T_max,
+    int NB, int window, int pool, int topk) {
+  static_assert(SCORE_CHUNK == TK_SUB, "one chunk maximum per top-k sub-list");
   __shared__ int lh[HIST ? R * HIST1_BINS : 1];
+  __shared__ int lmax[HIST ? R * (SC_THREADS / 64) : 1];
   const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
   const int L0 = clamp_len(seq_len[b], T_max, R);
   const int Lmax = L0 + R - 1;
@@ -73,8 +79,12 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 
   const int4 *Sbh = reinterpret_cast<const int4 *>(S + (size_t)bh * NB * RANK) + part;
   int32_t *out[R];
+  int kmax[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) out[i] = scores + ((size_t)(b * R + i) * Hkv + h) * NB;
+  for (int i = 0; i < R; ++i) {
+    out[i] = scores + ((size_t)(b * R + i) * Hkv + h) * NB;
+    kmax[i] = 0;
+  }
 
   for (int base = c0 + wave * SC_WAVE_STEP; base < c1; base += SC_BLOCK_STEP) {
     int4 sv[SC_UNROLL];
@@ -106,13 +116,32 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
       if (t_lo < c1) __builtin_nontemporal_store(lo, &out[i][t_lo]);
       if (t_hi < c1) __builtin_nontemporal_store(hi, &out[i][t_hi]);
       if (HIST && need_hist[i]) {
-        if (t_lo < nf[i]) atomicAdd(&lh[i * HIST1_BINS + (biased_key(lo) >> HIST2_BITS)], 1);
-        if (t_hi < nf[i]) atomicAdd(&lh[i * HIST1_BINS + (biased_key(hi) >> HIST2_BITS)], 1);
+        const int klo = biased_key(lo), khi = biased_key(hi);
+        if (t_lo < nf[i]) {
+          atomicAdd(&lh[i * HIST1_BINS + (klo >> HIST2_BITS)], 1);
+          kmax[i] = max(kmax[i], klo + 1);
+        }
+        if (t_hi < nf[i]) {
+          atomicAdd(&lh[i * HIST1_BINS + (khi >> HIST2_BITS)], 1);
+          kmax[i] = max(kmax[i], khi + 1);
+        }
       }
     }
   }
   if (HIST) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int wm = __builtin_amdgcn_readlane(wave_incl_max(kmax[i]), 63);
+      if (lane == 0) lmax[i * (SC_THREADS / 64) + wave] = wm;
+    }
     __syncthreads();
+    if (threadIdx.x < R) {
+      const int i = threadIdx.x;
+      int m = 0;
+#pragma unroll
+      for (int w = 0; w < SC_THREADS / 64; ++w) m = max(m, lmax[i * (SC_THREADS / 64) + w]);
+      cmax[((size_t)(b * R + i) * Hkv + h) * n_sub_max + blockIdx.x] = m;
+    }
     for (int k = threadIdx.x; k < R * HIST1_BINS; k += SC_THREADS) {
       const int v = lh[k];
       const int i = k / HIST1_BINS;
@@ -126,6 +155,8 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
                         const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st) {
   int32_t *hist1 = w ? w->hist1 : nullptr;
+  int32_t *cmax = w ? w->cmax : nullptr;
+  const int n_sub_max = w ? w->nchunk : 0;
   // the largest far count any row can have is (T_max - window) / pool <= NB
   long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   if (max_far <= 0) return hipSuccess;
@@ -135,12 +166,12 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
   case RR:                                                                                     \
     if (hist1)                                                                                 \
       score_kernel<RR, true><<<grid, SC_THREADS, 0, st>>>(qsk, S, seq_len, scores, hist1,      \
-                                                          s.Hkv, s.T_max, s.NB, s.window,      \
-                                                          s.pool, s.topk);                     \
+                                                          cmax, n_sub_max, s.Hkv, s.T_max,     \
+                                                          s.NB, s.window, s.pool, s.topk);     \
     else                                                                                       \
       score_kernel<RR, false><<<grid, SC_THREADS, 0, st>>>(qsk, S, seq_len, scores, nullptr,   \
-                                                           s.Hkv, s.T_max, s.NB, s.window,     \
-                                                           s.pool, s.topk);                    \
+                                                           nullptr, 0, s.Hkv, s.T_max, s.NB,   \
+                                                           s.window, s.pool, s.topk);          \
     break;
     SKS_SCORE_CASE(1)
     SKS_SCORE_CASE(2)

@@ -9,10 +9,12 @@
 //     atomics (order-independent, so deterministic) into a workspace region
 //     that is zero at rest.  Either the score kernel accumulates it while it
 //     streams the sketches, or topk_hist_kernel does it here.
+//     The same pass records the largest key of every 1024-entry sub-list.
 //   filter: every workgroup first validates the segment's level-1 histogram
 //     and derives the threshold bin b1 from it (the same value in every
 //     workgroup; an invalid histogram makes every element a candidate), then
-//     each wave compacts the candidates (bin >= b1) of its 1024-token
+//     each wave skips a sub-list whose largest key lies below bin b1 and
+//     otherwise compacts the candidates (bin >= b1) of its 1024-token
 //     sub-chunk IN ORDER (ballot + popcount), and adds the low 10 bits of the
 //     candidates inside bin b1 to the level-2 histogram (also zero at rest).
 //   final (one workgroup per segment): guesses the threshold key T from the
@@ -126,10 +128,14 @@ __global__ void fill_kernel(int32_t *p, size_t n, int32_t v) {
 
 __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(
     const int32_t *__restrict__ scores, const int32_t *__restrict__ seq_len,
-    int32_t *__restrict__ hist1, int R, int Hkv, int T_max, int NB, int window, int pool,
-    int topk) {
+    int32_t *__restrict__ hist1, int32_t *__restrict__ cmax, int n_sub_max, int R, int Hkv,
+    int T_max, int NB, int window, int pool, int topk) {
+  constexpr int SUBS = TK_CHUNK / TK_SUB;          // sub-lists per workgroup
+  constexpr int PER_SUB = TK_SUB / TK_THREADS;     // elements per thread and sub-list
   __shared__ int lh[HIST1_BINS];
+  __shared__ int lmax[SUBS][TK_THREADS / 64];
   const int seg = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   if (g.k_eff >= g.n_far) return;               // everything selected: no histogram needed
   const int c0 = blockIdx.x * TK_CHUNK;
@@ -138,9 +144,29 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(
   for (int k = threadIdx.x; k < HIST1_BINS; k += TK_THREADS) lh[k] = 0;
   __syncthreads();
   const int32_t *row = scores + (size_t)seg * NB;
-  for (int t = c0 + threadIdx.x; t < c1; t += TK_THREADS)
-    atomicAdd(&lh[biased_key(row[t]) >> HIST2_BITS], 1);
+  int km[SUBS];
+#pragma unroll
+  for (int j = 0; j < SUBS; ++j) {
+    km[j] = 0;
+#pragma unroll
+    for (int k = 0; k < PER_SUB; ++k) {
+      const int t = c0 + j * TK_SUB + k * TK_THREADS + threadIdx.x;
+      if (t < c1) {
+        const int key = biased_key(row[t]);
+        atomicAdd(&lh[key >> HIST2_BITS], 1);
+        km[j] = max(km[j], key + 1);
+      }
+    }
+    const int wm = __builtin_amdgcn_readlane(wave_incl_max(km[j]), 63);
+    if (lane == 0) lmax[j][wave] = wm;
+  }
   __syncthreads();
+  if (threadIdx.x < SUBS && c0 + threadIdx.x * TK_SUB < c1) {
+    int m = 0;
+#pragma unroll
+    for (int w = 0; w < TK_THREADS / 64; ++w) m = max(m, lmax[threadIdx.x][w]);
+    cmax[(size_t)seg * n_sub_max + blockIdx.x * SUBS + threadIdx.x] = m;
+  }
   int32_t *gh = hist1 + (size_t)seg * HIST1_BINS;
   for (int k = threadIdx.x; k < HIST1_BINS; k += TK_THREADS)
     if (lh[k]) atomicAdd(&gh[k], lh[k]);
@@ -205,34 +231,45 @@ __device__ int4 block_threshold(const int (&v)[TH_PER], int need, int n, int *sc
 
 __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
     const int32_t *__restrict__ scores, const int32_t *__restrict__ seq_len,
-    const int32_t *__restrict__ hist1, int32_t *__restrict__ hist2, int32_t *__restrict__ thr,
-    int32_t *__restrict__ cnt, int2 *__restrict__ cand, int n_sub_max, int R, int Hkv, int T_max,
-    int NB, int window, int pool, int topk) {
+    const int32_t *__restrict__ hist1, const int32_t *__restrict__ cmax,
+    int32_t *__restrict__ hist2, int32_t *__restrict__ thr, int32_t *__restrict__ cnt,
+    int2 *__restrict__ cand, int n_sub_max, int R, int Hkv, int T_max, int NB, int window,
+    int pool, int topk) {
   __shared__ int scratch[TK_THREADS / 64];
   __shared__ int res[3];
   const int seg = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = blockIdx.x * (TK_CHUNK / TK_SUB) + wave;
   const int s0 = sub * TK_SUB;
-  const int32_t *row = scores + (size_t)seg * NB;
-  // Issue this wave's score loads and the histogram loads before the length
-  // is known, all at once: the index is clamped below NB (always in bounds)
-  // instead of branching around the load, and entries past the far region
-  // are masked later.
-  int raw[FILTER_ITERS];
-#pragma unroll
-  for (int r = 0; r < FILTER_ITERS; ++r) raw[r] = row[min(s0 + r * 64 + lane, NB - 1)];
+  // the histogram, this sub-list's largest key and the length, all at once
+  // (the sub-list index is clamped into the array; a sub-list past the far
+  // region returns below)
   const int4 *gh = reinterpret_cast<const int4 *>(hist1 + (size_t)seg * HIST1_BINS) + 2 * threadIdx.x;
   const int4 h0 = gh[0], h1v = gh[1];
+  const int cm = cmax[(size_t)seg * n_sub_max + min(sub, n_sub_max - 1)];
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   if (g.k_eff >= g.n_far || blockIdx.x * TK_CHUNK >= g.n_far) return;   // uniform per workgroup
   const int v[TH_PER] = {h0.x, h0.y, h0.z, h0.w, h1v.x, h1v.y, h1v.z, h1v.w};
   const int4 th = block_threshold(v, g.k_eff, g.n_far, scratch, res);
   if (blockIdx.x == 0 && threadIdx.x == 0) reinterpret_cast<int4 *>(thr)[seg] = th;
   const int b1 = th.x;
-  const bool build_h2 = th.z && th.w <= HIST2_DIRECT_MAX;
   if (s0 >= g.n_far) return;                     // uniform per wave
+  int32_t *cnt_out = cnt + (size_t)seg * n_sub_max + sub;
+  // The histogram and the maxima come from the same pass: with a valid
+  // histogram, a sub-list whose largest key lies below bin b1 holds no
+  // candidate and its scores are not read.
+  if (th.z && (cm == 0 || ((cm - 1) >> HIST2_BITS) < b1)) {
+    if (lane == 0) *cnt_out = 0;
+    return;
+  }
+  const bool build_h2 = th.z && th.w <= HIST2_DIRECT_MAX;
   const int s1 = min(g.n_far, s0 + TK_SUB);
+  const int32_t *row = scores + (size_t)seg * NB;
+  // all loads at once, the index clamped below NB (always in bounds)
+  // instead of branching around the load; entries past s1 are masked below
+  int raw[FILTER_ITERS];
+#pragma unroll
+  for (int r = 0; r < FILTER_ITERS; ++r) raw[r] = row[min(s0 + r * 64 + lane, NB - 1)];
   int2 *dst = cand + ((size_t)seg * n_sub_max + sub) * TK_SUB;
   int32_t *h2 = hist2 + (size_t)seg * HIST2_BINS;
   int n = 0;
@@ -248,7 +285,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
     }
     n += __popcll(m);
   }
-  if (lane == 0) cnt[(size_t)seg * n_sub_max + sub] = n;
+  if (lane == 0) *cnt_out = n;
 }
 
 __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
@@ -501,8 +538,9 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
 
 size_t hist_region_bytes(const Shape &s) {
   const size_t nseg = (size_t)s.B * s.R * s.Hkv;
+  const size_t n_sub = (size_t)ceil_div(s.NB, TK_SUB);
   return align_up(nseg * HIST1_BINS * 4, 256) + align_up(nseg * HIST2_BINS * 4, 256) +
-         align_up(nseg * 16, 256);
+         align_up(nseg * 16, 256) + align_up(nseg * n_sub * 4, 256);
 }
 
 size_t topk_scratch_bytes(const Shape &s) {
@@ -515,13 +553,15 @@ TopkWs topk_ws_carve(const Shape &s, void *ws) {
   const size_t nseg = (size_t)s.B * s.R * s.Hkv;
   const size_t n_sub = (size_t)ceil_div(s.NB, TK_SUB);
   char *base = static_cast<char *>(ws);
-  TopkWs w;
+  TopkWs w{};
   char *q = base;
   w.hist1 = reinterpret_cast<int32_t *>(q);
   q += align_up(nseg * HIST1_BINS * 4, 256);
   w.hist2 = reinterpret_cast<int32_t *>(q);
   q += align_up(nseg * HIST2_BINS * 4, 256);
   w.counters = reinterpret_cast<int32_t *>(q);
+  q += align_up(nseg * 16, 256);
+  w.cmax = reinterpret_cast<int32_t *>(q);
   char *p = base + hist_region_bytes(s);
   w.scratch = p;
   w.cnt = reinterpret_cast<int32_t *>(p);
@@ -545,9 +585,10 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
   if (max_far > 0) {
     dim3 grid(ceil_div(max_far, TK_CHUNK), nseg);
     if (!hist_ready)
-      topk_hist_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, s.R, s.Hkv,
-                                                    s.T_max, s.NB, s.window, s.pool, s.topk);
-    topk_filter_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.hist2,
+      topk_hist_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.cmax, w.nchunk,
+                                                    s.R, s.Hkv, s.T_max, s.NB, s.window, s.pool,
+                                                    s.topk);
+    topk_filter_kernel<<<grid, TK_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.cmax, w.hist2,
                                                     w.counters, w.cnt, w.cand, w.nchunk, s.R,
                                                     s.Hkv, s.T_max, s.NB, s.window, s.pool,
                                                     s.topk);

@@ -200,7 +200,7 @@ int sks_sketch_score(const int8_t *qsk, const int8_t *S, const sks_kv *kv, const
   REQUIRE_PTR(qsk, 16);
   REQUIRE_PTR(S, 16);
   REQUIRE_PTR(scores, 4);
-  sks::TopkWs w;
+  sks::TopkWs w{};
   if (ws) {
     TRY(check_ws(ws, ws_bytes_given, topk_need(s)));
     w = sks::topk_ws_carve(s, ws);

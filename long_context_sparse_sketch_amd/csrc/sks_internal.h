@@ -228,8 +228,9 @@ hipError_t launch_sketch_query(const uint16_t *q, int B, int R, int Hq, int Hkv,
                                float *qscale, hipStream_t st);
 // Workspace layout: [hist region | scratch].  The hist region holds the
 // level-1 and level-2 selection histograms [nseg][2048] and [nseg][1024],
-// zero at rest (the calls that use them return them to zero), and the
-// per-segment threshold bins.
+// zero at rest (the calls that use them return them to zero), the
+// per-segment threshold bins and the per-sub-list score maxima written with
+// the level-1 histogram.
 // (Kernels here never communicate between workgroups inside one launch: a
 // device-scope fence per workgroup costs far more on this GPU than a kernel
 // boundary.)  The scratch holds
@@ -247,6 +248,7 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
 struct TopkWs {
   int32_t *hist1;     // [nseg][HIST1_BINS], zero at rest
   int32_t *hist2;     // [nseg][HIST2_BINS], zero at rest
+  int32_t *cmax;      // [nseg][nchunk]: largest biased score of each sub-list + 1 (0: empty)
   int32_t *counters;  // [nseg][4]: threshold bin b1, count above it, valid, count in b1
   char *scratch;      // start of the scratch area
   int32_t *cnt;       // [nseg][nchunk]
