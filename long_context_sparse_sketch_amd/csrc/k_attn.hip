@@ -6,11 +6,14 @@
 //
 // Split-K flash decoding.  A workgroup takes ATTN_SPLIT consecutive entries
 // of one (sequence, row, KV head) attention set and all G query heads of
-// that KV head; each of its 4 waves takes 64 of them as two tiles of 32
-// (see the matrix-core kernel below).  Online softmax in the log2 domain;
+// that KV head; each of its 4 waves takes 96 of them as three tiles of 32
+// (see the matrix-core kernel below), gathering tile t + 1 while it
+// computes tile t.  Online softmax in the log2 domain;
 // the waves' states are merged through LDS and the workgroup writes one
 // partial (m, l, acc[G][128]).  A second kernel merges the partials of every
 // split in split order, so results are deterministic.
+#include <type_traits>
+
 #include "sks_internal.h"
 
 namespace sks {
@@ -63,8 +66,9 @@ __device__ __forceinline__ void merge_state(float &m, float &l, float (&a)[N], f
 // leaves 16 - G rows idle, which costs nothing here: the pass is bound by
 // the gathers.
 constexpr int AM_TILE = 32;
-constexpr int AM_WAVE_ENTRIES = ATTN_SPLIT / (AT_THREADS / 64);   // 64: two tiles
+constexpr int AM_WAVE_ENTRIES = ATTN_SPLIT / (AT_THREADS / 64);   // 96: three tiles
 constexpr int AM_TILES = AM_WAVE_ENTRIES / AM_TILE;
+static_assert(AM_WAVE_ENTRIES <= 128, "two entry descriptors per lane");
 constexpr int VROW = 132;                 // LDS V row stride in bf16 (264 B: conflict-free reads)
 constexpr float RESCALE_SLACK = 8.0f;
 
@@ -169,30 +173,47 @@ __global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
   const int n = lane & 15, g = lane >> 4;
   const int Hq = Hkv * G;
   const int e_wave = split * ATTN_SPLIT + wave * AM_WAVE_ENTRIES;
-  // The selected index of entry e_wave + lane is loaded together with the
-  // length, before it is known whether the entry is a selected one (the
-  // address is clamped into the segment's idx row, so always in bounds).
-  const int sel = idx[(size_t)seg * topk + min(e_wave + lane, topk - 1)];
+  // The selected indices of entries e_wave + lane and e_wave + 64 + lane are
+  // loaded together with the length, before it is known whether the entries
+  // are selected ones (the addresses are clamped into the segment's idx row,
+  // so always in bounds).
+  const int32_t *idx_row = idx + (size_t)seg * topk;
+  const int sel0 = idx_row[min(e_wave + lane, topk - 1)];
+  const int sel1 = idx_row[min(e_wave + 64 + lane, topk - 1)];
   const int L0 = clamp_len(seq_len[b], T_max, R);
   const RowGeom rg = row_geom(L0, i, window, pool, topk);
 
-  // Descriptor of entry e_wave + lane: the row to gather (an index into the
-  // token rows, or the pooled rows when bit 1 of the flag is set) and whether
-  // it takes part.  Invalid entries point at row 0, which always exists, so
-  // the gathers below need no branches.
-  int my_row = 0, my_flag = 0;
-  {
-    const int e = e_wave + lane;
+  // Descriptor of an entry: the row to gather (an index into the token rows,
+  // or the pooled rows when bit 1 of the flag is set) and whether it takes
+  // part.  Invalid entries point at row 0, which always exists, so the
+  // gathers below need no branches.  Lane l holds entries e_wave + l (row0,
+  // flag0) and e_wave + 64 + l (row1, flag1).
+  auto describe = [&](int e, int sel, int &row, int &flag) {
+    row = 0;
+    flag = 0;
     if (e < rg.k_eff) {
       if ((unsigned)sel < (unsigned)rg.n_far) {
-        my_row = sel;
-        my_flag = POOLED ? 3 : 1;
+        row = sel;
+        flag = POOLED ? 3 : 1;
       }
     } else if (e < rg.n_ent) {
-      my_row = rg.ws + (e - rg.k_eff);
-      my_flag = 1;
+      row = rg.ws + (e - rg.k_eff);
+      flag = 1;
     }
-  }
+  };
+  int row0, flag0, row1, flag1;
+  describe(e_wave + lane, sel0, row0, flag0);
+  describe(e_wave + 64 + lane, sel1, row1, flag1);
+  // descriptor of wave entry j (a compile-time tile offset plus a lane value)
+  auto desc = [&](int j, int &r, int &f) {
+    if (j < 64) {
+      r = __shfl(row0, j);
+      f = __shfl(flag0, j);
+    } else {
+      r = __shfl(row1, j - 64);
+      f = __shfl(flag1, j - 64);
+    }
+  };
 
   // Q as the A operand: head n, dims 32i + 8g .. +8 (zero rows past G)
   u32x4_t qa[4];
@@ -225,81 +246,96 @@ __global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
   const uint16_t *Vst = DT == SKS_KV_I8 ? Vs + ((size_t)b * Hkv + h) * T_max : nullptr;
   uint16_t *sv = s_v[wave];
 
-#pragma unroll
-  for (int tile = 0; tile < AM_TILES; ++tile) {
-    const int e_tile = e_wave + tile * AM_TILE;
-    if (e_tile >= rg.n_ent) break;                         // uniform across the wave
-
-    // ---- gathers: K for the two QK sub-tiles, V rows of the tile
-    u32x4_t kb[2][4];
-    bool ok[2];
-    float ksc[2], vsc[2];
+  // Raw gathered data of one tile, as loaded (converted to bf16 only when the
+  // tile is consumed, so that the next tile's loads stay in flight meanwhile).
+  using KRaw = typename std::conditional<DT == SKS_KV_BF16, uint4, uint2>::type;
+  struct Tile {
+    KRaw k[2][4];          // K: sub-tile t, lane (n, g): entry 16t + n, dims 32c + 8g .. +8
+    KRaw v[8];             // V: chunk (x & 15) of tile row (x >> 4), x = 64 qq + lane
+    int f[2];              // flags of the two K entries of this lane
+    uint16_t ks[2], vs[2]; // int8 row scales of the two K entries (fp16 bits)
+  };
+  // K/V rows are read once per step: nontemporal loads keep them from
+  // evicting lines that are reused.
+  auto ld = [](const char *p) -> KRaw {
+    if constexpr (DT == SKS_KV_BF16) {
+      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+      return make_uint4(v[0], v[1], v[2], v[3]);
+    } else {
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+      return make_uint2(v[0], v[1]);
+    }
+  };
+  auto gather = [&](int tile, Tile &d) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int src = tile * AM_TILE + 16 * t + n;
-      const int r = __shfl(my_row, src), f = __shfl(my_flag, src);
-      ok[t] = f & 1;
+      int r, f;
+      desc(tile * AM_TILE + 16 * t + n, r, f);
+      d.f[t] = f;
       const char *kbase = (POOLED && (f & 2)) ? Kpb : Kt;
       const size_t off = (size_t)r * D * EB;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if constexpr (DT == SKS_KV_BF16) {
-          const uint4 w = *reinterpret_cast<const uint4 *>(kbase + off + (32 * c + 8 * g) * 2);
-          kb[t][c] = u32x4_t{w.x, w.y, w.z, w.w};
-        } else {
-          const uint2 w = *reinterpret_cast<const uint2 *>(kbase + off + 32 * c + 8 * g);
-          kb[t][c] = u32x4_t{i8pair_to_bf16x2(w.x, 0), i8pair_to_bf16x2(w.x, 16),
-                             i8pair_to_bf16x2(w.y, 0), i8pair_to_bf16x2(w.y, 16)};
-        }
-      }
+      for (int c = 0; c < 4; ++c) d.k[t][c] = ld(kbase + off + (32 * c + 8 * g) * EB);
       if constexpr (DT == SKS_KV_I8) {
-        ksc[t] = f16_bits_to_float(Kst[r]);
-        vsc[t] = f16_bits_to_float(Vst[r]);
-      } else {
-        ksc[t] = vsc[t] = 1.f;
+        d.ks[t] = Kst[r];
+        d.vs[t] = Vst[r];
       }
     }
-    // V: 32 rows x 16 chunks of 8 dims; lane takes chunk (x & 15) of row (x >> 4)
-    uint4 vv[8];
 #pragma unroll
     for (int qq = 0; qq < 8; ++qq) {
       const int x = qq * 64 + lane, ev = x >> 4, c = x & 15;
-      const int src = tile * AM_TILE + ev;
-      const int r = __shfl(my_row, src), f = __shfl(my_flag, src);
+      int r, f;
+      desc(tile * AM_TILE + ev, r, f);
       const char *vbase = (POOLED && (f & 2)) ? Vpb : Vt;
-      if constexpr (DT == SKS_KV_BF16) {
-        vv[qq] = *reinterpret_cast<const uint4 *>(vbase + (size_t)r * D * 2 + c * 16);
-      } else {
-        const uint2 w = *reinterpret_cast<const uint2 *>(vbase + (size_t)r * D + c * 8);
-        vv[qq] = make_uint4(i8pair_to_bf16x2(w.x, 0), i8pair_to_bf16x2(w.x, 16),
-                            i8pair_to_bf16x2(w.y, 0), i8pair_to_bf16x2(w.y, 16));
-      }
+      d.v[qq] = ld(vbase + (size_t)r * D * EB + c * 8 * EB);
     }
+  };
+  auto to_bf16 = [&](const KRaw &w) -> u32x4_t {
+    if constexpr (DT == SKS_KV_BF16) {
+      return u32x4_t{w.x, w.y, w.z, w.w};
+    } else {
+      return u32x4_t{i8pair_to_bf16x2(w.x, 0), i8pair_to_bf16x2(w.x, 16),
+                     i8pair_to_bf16x2(w.y, 0), i8pair_to_bf16x2(w.y, 16)};
+    }
+  };
 
+  auto consume = [&](const Tile &d) {
     // ---- QK on the matrix cores
     f32x4_t sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sacc[t] = mfma_bf16(qa[c], kb[t][c], sacc[t]);
+      for (int c = 0; c < 4; ++c) sacc[t] = mfma_bf16(qa[c], to_bf16(d.k[t][c]), sacc[t]);
     }
 
     // stage V (row-major, 8-byte stores: the padded stride is 8-byte aligned)
 #pragma unroll
     for (int qq = 0; qq < 8; ++qq) {
       const int x = qq * 64 + lane, ev = x >> 4, c = x & 15;
+      const u32x4_t w = to_bf16(d.v[qq]);
       uint2 *dst = reinterpret_cast<uint2 *>(sv + ev * VROW + c * 8);
-      dst[0] = make_uint2(vv[qq].x, vv[qq].y);
-      dst[1] = make_uint2(vv[qq].z, vv[qq].w);
+      dst[0] = make_uint2(w[0], w[1]);
+      dst[1] = make_uint2(w[2], w[3]);
     }
 
     // ---- online softmax on the C layout (lane: heads 4g + j, entry n of each sub-tile)
+    float ksc[2], vsc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if constexpr (DT == SKS_KV_I8) {
+        ksc[t] = f16_bits_to_float(d.ks[t]);
+        vsc[t] = f16_bits_to_float(d.vs[t]);
+      } else {
+        ksc[t] = vsc[t] = 1.f;
+      }
+    }
     float z[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) z[t][j] = ok[t] ? sacc[t][j] * ksc[t] * sm_log2 : NEG_INF;
+      for (int j = 0; j < 4; ++j) z[t][j] = (d.f[t] & 1) ? sacc[t][j] * ksc[t] * sm_log2 : NEG_INF;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float mx = row16_max_f(fmaxf(z[0][j], z[1][j]));
@@ -344,6 +380,25 @@ __global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
       o[blk] = mfma_bf16(pa_lo, vb, o[blk]);
     }
     wave_lds_sync();                                        // before the next tile reuses LDS
+  };
+
+  // Software pipeline over the wave's tiles: the gathers of tile t + 1 are
+  // issued before tile t is consumed, so that the memory system always holds
+  // a tile's worth of requests per wave.
+  // Straight-line code: every tile is gathered and consumed (entries past the
+  // set read row 0 and are masked out), and the scheduling barriers keep each
+  // tile's loads in issue order.  The wait counter is in order, so a
+  // conditional or a reordered load of tile t + 1 would make tile t wait for
+  // it too.
+  Tile cur, nxt;
+  gather(0, cur);
+#pragma unroll
+  for (int tile = 0; tile < AM_TILES; ++tile) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (tile + 1 < AM_TILES) gather(tile + 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(cur);
+    cur = nxt;
   }
 
   // denominators: sum the lane-partials over the 16 lanes of each DPP row
