@@ -41,6 +41,7 @@ constexpr int FILTER_ITERS = TK_SUB / 64;          // 16 loads in flight per lan
 constexpr int HIST2_DIRECT_MAX = 4096;             // level-2 histogram built when bin b1 is this small
 static_assert(TK_CHUNK == TK_SUB * (TK_THREADS / 64), "one sub-chunk per wave");
 static_assert(TF_CACHE < 65536, "packed 16-bit counts in the emission scan");
+static_assert(TF_PERT == 8, "mark padding: one int every 8 slots");
 
 struct SegGeom {
   int b, i, h, n_far, k_eff;
@@ -297,7 +298,10 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
   __shared__ int h1[hpad_size<HIST1_BINS>()];
   __shared__ int h2[hpad_size<HIST2_BINS>()];
   __shared__ int pre[TK_MAX_SUBS + 1];
-  __shared__ int2 cache[TF_CACHE];               // .x doubles as the sub-list start marks
+  __shared__ int2 cache[TF_CACHE];
+  // sub-list start marks, one int per slot padded by one every 8 so that a
+  // thread's 8 consecutive slots fall in distinct banks across the wave
+  __shared__ int marks[TF_CACHE + TF_CACHE / 8];
   __shared__ int sc_pre[TF_WAVES], sc_own[TF_WAVES], sc_cnt[TF_WAVES];
   __shared__ int res[6];
   const int seg = blockIdx.x;
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
     }
   }
 #pragma unroll
-  for (int q = 0; q < TF_PERT; ++q) cache[threadIdx.x * TF_PERT + q].x = 0;   // no mark
+  for (int q = 0; q < TF_PERT; ++q) marks[threadIdx.x * (TF_PERT + 1) + q] = 0;   // no mark
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   int32_t *out = idx + (size_t)seg * topk;
   // the filter has run: the segment's level-1 histogram returns to zero
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
     const int start = carry + incl - v;
     if (sidx < n_sub) {
       pre[sidx] = start;
-      if (v > 0 && start < TF_CACHE) cache[start].x = sidx + 1;
+      if (v > 0 && start < TF_CACHE) marks[start + (start >> 3)] = sidx + 1;
     }
     carry += tot;
   }
@@ -380,12 +384,11 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
   if (cached) {
     // The sub-list holding slot o is the last mark at or before o: a running
     // maximum over the marks of this thread's slots, then across the block.
-    // Each thread reads and later overwrites only its own slots.
     int mk[TF_PERT];
     int run = 0;
 #pragma unroll
     for (int q = 0; q < TF_PERT; ++q) {
-      run = max(run, cache[o0 + q].x);
+      run = max(run, marks[threadIdx.x * (TF_PERT + 1) + q]);
       mk[q] = run;
     }
     const int before = block_excl_max<TF_WAVES>(run, sc_own);
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
 #pragma unroll
     for (int q = 0; q < TF_PERT; ++q) {
       const int o = min(o0 + q, m - 1);
-      const int s = max(max(before, mk[q]), 1) - 1;
+      const int s = min(max(max(before, mk[q]), 1) - 1, n_sub - 1);   // clamped: always in bounds
       c[q] = cseg[(size_t)s * TK_SUB + min(max(o - pre[s], 0), TK_SUB - 1)];
     }
     const int T = res[5];
