@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--steps-per-graph", type=int, default=0,
                     help="consecutive steps (one per cache replica) captured in one graph; "
                          "0 = all replicas")
+    ap.add_argument("--five-calls", action="store_true",
+                    help="issue each step as the five individual C-ABI calls instead of the one "
+                         "sks_decode_step call")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -191,7 +194,8 @@ def main():
         del a, b
 
     stream = torch.cuda.current_stream()
-    runners = [StepRunner(lay, parts=args.parts, streams=args.streams) for lay in layers]
+    runners = [StepRunner(lay, parts=args.parts, streams=args.streams, fused=not args.five_calls)
+               for lay in layers]
     R_ = len(runners)
     spg = args.steps_per_graph or R_
     if R_ % spg:
@@ -292,7 +296,8 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.B, "context": cfg.L, "rows": cfg.R,
                    "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "window": cfg.window,
                    "topk": cfg.topk, "pool": cfg.pool, "replicas": args.replicas,
-                   "schedule": f"{args.parts} sub-batches on {args.streams} streams, "
+                   "schedule": ("five C-ABI calls" if args.five_calls else "sks_decode_step")
+                               + f", {args.parts} sub-batches on {args.streams} streams, "
                                + ("eager launches" if args.no_graph else
                                   f"HIP graph replay ({spg} steps per graph)")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

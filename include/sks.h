@@ -215,6 +215,43 @@ int sks_sparse_decode_attn(const uint16_t *q, int32_t Hq, const sks_kv *kv,
                            const uint16_t *Vp, float sm_scale, float *out, float *lse,
                            void *ws, size_t ws_bytes, sks_stream_t stream);
 
+/* One whole decode step of one layer in a single call: the work of
+ *   sks_sketch_build(APPEND)      (with SKS_STEP_APPEND)
+ *   sks_sketch_build_query
+ *   sks_sketch_score(ws)
+ *   sks_topk_select(SKS_TOPK_HIST_READY)
+ *   sks_sparse_decode_attn
+ * in that order, with the same results bit for bit (the pages' statement of
+ * the work in "What it took": build the sketch, score every token, pick the
+ * top ~2K, attend, all graph-safe).  Grouping the calls lets launches share
+ * work that the order allows: the query sketch and the append run in one
+ * launch, and the final selection runs in the same launch as the exact-window
+ * part of the attention, which does not depend on it.
+ * Every buffer is caller-owned and keeps the layout of the individual call
+ * that writes or reads it; NULL is allowed where the individual call allows
+ * it (qscale, n_sel, lse; Kp/Vp when pool == 1).  The same validation as the
+ * individual calls happens before any launch. */
+typedef struct sks_step {
+  const uint16_t *q;        /* [B][R][Hq][128] bf16 queries of the rows         */
+  int32_t Hq;               /* query heads: a multiple of Hkv, Hq / Hkv <= 8    */
+  const float *basis;       /* [1 or Hkv][64][128] fp32 sketch basis            */
+  int32_t basis_per_head;   /* 0: one basis for all KV heads, 1: one per head   */
+  const float *key_scale;   /* [Hkv] frozen key-sketch scales                   */
+  int8_t *S;                /* [B][Hkv][NB][64] key sketch (APPEND rows written) */
+  uint16_t *Kp, *Vp;        /* [B][Hkv][NB][128] bf16 pooled rows (pool > 1)    */
+  float sm_scale;           /* logit scale, > 0 (1/sqrt(128) for the pages)     */
+  int8_t *qsk;              /* out: [B][R][Hkv][64] query sketch codes          */
+  float *qscale;            /* out: [B][R][Hkv] query sketch scales, or NULL    */
+  int32_t *scores;          /* out: [B][R][Hkv][NB] scores                      */
+  int32_t *idx;             /* out: [B][R][Hkv][topk] selected entries          */
+  int32_t *n_sel;           /* out: [B][R][Hkv] k_eff, or NULL                  */
+  float *out;               /* out: [B][R][Hq][128] fp32 attention output       */
+  float *lse;               /* out: [B][R][Hq] fp32 log-sum-exp, or NULL        */
+} sks_step;
+#define SKS_STEP_APPEND 1   /* sketch the rows' own tokens first */
+int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *step, int32_t flags,
+                    void *ws, size_t ws_bytes, sks_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,10 +22,11 @@ APPEND = -1
 HEAD_DIM, RANK = 128, 64
 
 TOPK_HIST_READY = 1
+STEP_APPEND = 1
 
 EXPORTS = ("sks_last_error", "sks_runtime_version", "sks_workspace_bytes", "sks_workspace_init",
            "sks_sketch_build", "sks_sketch_build_query", "sks_sketch_score", "sks_topk_select",
-           "sks_gather_pack", "sks_sparse_decode_attn")
+           "sks_gather_pack", "sks_sparse_decode_attn", "sks_decode_step")
 
 
 class SksError(RuntimeError):
@@ -45,6 +46,15 @@ class KVDesc(ctypes.Structure):
 class Params(ctypes.Structure):
     _fields_ = [("window", ctypes.c_int32), ("topk", ctypes.c_int32), ("pool", ctypes.c_int32),
                 ("rank", ctypes.c_int32), ("rows", ctypes.c_int32)]
+
+
+class StepDesc(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("Hq", ctypes.c_int32), ("basis", ctypes.c_void_p),
+                ("basis_per_head", ctypes.c_int32), ("key_scale", ctypes.c_void_p),
+                ("S", ctypes.c_void_p), ("Kp", ctypes.c_void_p), ("Vp", ctypes.c_void_p),
+                ("sm_scale", ctypes.c_float), ("qsk", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
+                ("scores", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("n_sel", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
 
 
 def params(window: int, topk: int, pool: int = 1, rows: int = 1, rank: int = RANK) -> Params:
@@ -82,6 +92,8 @@ def lib():
         L.sks_sparse_decode_attn.restype = ctypes.c_int
         L.sks_sparse_decode_attn.argtypes = [vp, i32, kvp, pp, vp, vp, vp, ctypes.c_float, vp,
                                              vp, vp, sz, vp]
+        L.sks_decode_step.restype = ctypes.c_int
+        L.sks_decode_step.argtypes = [kvp, pp, ctypes.POINTER(StepDesc), i32, vp, sz, vp]
         _LIB = L
     return _LIB
 
@@ -172,3 +184,16 @@ def sparse_decode_attn(q, cache: Cache, p: Params, idx, out, ws, lse=None, Kp=No
     _check(lib().sks_sparse_decode_attn(ptr(q), Hq, cache.ref, ctypes.byref(p), ptr(idx),
                                         ptr(Kp), ptr(Vp), ctypes.c_float(sm), ptr(out), ptr(lse),
                                         ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def decode_step(cache: Cache, p: Params, q, basis, key_scale, S, qsk, scores, idx, out, ws,
+                qscale=None, n_sel=None, lse=None, Kp=None, Vp=None, sm_scale=None,
+                basis_per_head=False, append=True, stream=None):
+    """The whole decode step (append, query sketch, score, select, attend) in one call."""
+    sm = 1.0 / math.sqrt(q.shape[3]) if sm_scale is None else sm_scale
+    st = StepDesc(ptr(q), q.shape[2], ptr(basis), int(basis_per_head), ptr(key_scale), ptr(S),
+                  ptr(Kp), ptr(Vp), sm, ptr(qsk), ptr(qscale), ptr(scores), ptr(idx), ptr(n_sel),
+                  ptr(out), ptr(lse))
+    _check(lib().sks_decode_step(cache.ref, ctypes.byref(p), ctypes.byref(st),
+                                 STEP_APPEND if append else 0, ptr(ws), _nbytes(ws),
+                                 _stream(stream)))

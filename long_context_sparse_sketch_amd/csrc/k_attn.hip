@@ -12,433 +12,10 @@
 // the waves' states are merged through LDS and the workgroup writes one
 // partial (m, l, acc[G][128]).  A second kernel merges the partials of every
 // split in split order, so results are deterministic.
-#include <type_traits>
-
-#include "sks_internal.h"
+#include "attn_body.h"
 
 namespace sks {
 namespace {
-
-constexpr int AT_THREADS = 256;
-constexpr int AT_U = 4;                            // entries per row-slot per step
-constexpr int AT_WAVE_ENTRIES = ATTN_SPLIT / (AT_THREADS / 64);     // 64
-constexpr int AT_STEPS = AT_WAVE_ENTRIES / (4 * AT_U);              // 4
-constexpr float NEG_INF = -__builtin_huge_valf();
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Merge another online-softmax state (mo, lo, ao) into (m, l, a).
-template <int N>
-__device__ __forceinline__ void merge_state(float &m, float &l, float (&a)[N], float mo, float lo,
-                                            const float (&ao)[N]) {
-  const float M = fmaxf(m, mo);
-  const float wa = m == NEG_INF ? 0.f : exp2_fast(m - M);
-  const float wb = mo == NEG_INF ? 0.f : exp2_fast(mo - M);
-  l = l * wa + lo * wb;
-#pragma unroll
-  for (int d = 0; d < N; ++d) a[d] = a[d] * wa + ao[d] * wb;
-  m = M;
-}
-
-// ---------------------------------------------------------------------------
-// Matrix-core version.  Per wave, tiles of 32 entries:
-//   QK:  S[16 heads][16 entries] = Q x K^T with v_mfma_f32_16x16x32_bf16, two
-//        sub-tiles of 16 entries (query heads padded to the 16 MFMA rows).
-//        A = Q: lane (n = lane%16, g = lane/16) holds head n, dims 32i+8g..+8;
-//        B = K^T: lane holds entry n, the same dims (16-byte gathers).
-//        C: lane holds S[4g + j][n], j = 0..3.
-//   softmax on that layout: each lane owns 4 heads x 1 entry; row max and
-//        sums over the 16 lanes of its DPP row.  The running max is only
-//        moved when a tile exceeds it by more than 2^RESCALE_SLACK (exact in
-//        real arithmetic; the ratio stays far inside fp32 range).
-//   PV:  O[16 heads][128] += P x V with the same MFMA, K = the 32 entries.
-//        P is split into bf16 hi + lo parts (two MFMAs) so its weights keep
-//        ~16 significant bits; V rows are staged row-major in wave-private
-//        LDS and read back per MFMA as 8 entries x 1 dim per lane.
-// All heads of the KV group share every gathered row; the 16-row MFMA shape
-// leaves 16 - G rows idle, which costs nothing here: the pass is bound by
-// the gathers.
-constexpr int AM_TILE = 32;
-constexpr int AM_WAVE_ENTRIES = ATTN_SPLIT / (AT_THREADS / 64);   // 96: three tiles
-constexpr int AM_TILES = AM_WAVE_ENTRIES / AM_TILE;
-static_assert(AM_WAVE_ENTRIES <= 128, "two entry descriptors per lane");
-constexpr int VROW = 132;                 // LDS V row stride in bf16 (264 B: conflict-free reads)
-constexpr float RESCALE_SLACK = 8.0f;
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-// LDS written by some lanes of this wave and read by others: order the
-// accesses (in-order LDS queue per wave, no workgroup barrier needed).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-// int8 codes -> bf16 (exact: |code| <= 127 needs 7 significant bits)
-__device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int sh) {
-  const float a = (float)(int8_t)(w >> sh), b = (float)(int8_t)(w >> (sh + 8));
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
-}
-
-__device__ __forceinline__ float row16_max_f(float x) {
-  x = fmaxf(x, dpp_f<DPP_ROW_MIRROR>(x));
-  x = fmaxf(x, dpp_f<DPP_ROW_HMIRROR>(x));
-  x = fmaxf(x, dpp_f<DPP_QUAD_XOR1>(x));
-  x = fmaxf(x, dpp_f<DPP_QUAD_XOR2>(x));
-  return x;
-}
-
-// Merge of the partials of one (segment, query head j, dim d) over all splits,
-// in split order, MB splits at a time so that their loads are in flight
-// together; the order of operations is fixed by the shape.
-constexpr int MB = 8;
-__device__ void merge_splits(const float2 *part_ml, const float *part_acc, int seg, int j, int d,
-                             int nsplit, int G, int Hkv, float *out, float *lse) {
-  const int h = seg % Hkv, bi = seg / Hkv;
-  const size_t orow = (size_t)bi * Hkv * G + (size_t)h * G + j;
-  const size_t base = (size_t)seg * nsplit;
-  const float *ml = reinterpret_cast<const float *>(part_ml);
-  float M = NEG_INF, Lsum = 0.f, A = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += MB) {
-    float mm[MB], ll[MB], a[MB];
-#pragma unroll
-    for (int k = 0; k < MB; ++k) {
-      const int sp = min(s0 + k, nsplit - 1);
-      const size_t e = (base + sp) * G + j;
-      mm[k] = s0 + k < nsplit ? ml[2 * e] : NEG_INF;
-      ll[k] = ml[2 * e + 1];
-      a[k] = part_acc[e * D + d];
-    }
-    float Mn = M;
-#pragma unroll
-    for (int k = 0; k < MB; ++k) Mn = fmaxf(Mn, mm[k]);
-    if (Mn == NEG_INF) continue;
-    const float wa = M == NEG_INF ? 0.f : exp2_fast(M - Mn);
-    Lsum *= wa;
-    A *= wa;
-#pragma unroll
-    for (int k = 0; k < MB; ++k) {
-      const float wt = mm[k] == NEG_INF ? 0.f : exp2_fast(mm[k] - Mn);
-      Lsum += ll[k] * wt;
-      A += a[k] * wt;
-    }
-    M = Mn;
-  }
-  if (M == NEG_INF) {
-    out[orow * D + d] = 0.f;
-    if (d == 0 && lse) lse[orow] = NEG_INF;
-    return;
-  }
-  out[orow * D + d] = A / Lsum;
-  if (d == 0 && lse) lse[orow] = (M + __log2f(Lsum)) * 0.69314718055994530942f;
-}
-
-template <int G, int DT, bool POOLED>
-__global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
-    const uint16_t *__restrict__ q, const void *__restrict__ K, const void *__restrict__ V,
-    const uint16_t *__restrict__ Ks, const uint16_t *__restrict__ Vs,
-    const int32_t *__restrict__ seq_len, const int32_t *__restrict__ idx,
-    const uint16_t *__restrict__ Kp, const uint16_t *__restrict__ Vp, float sm_log2, int R,
-    int Hkv, int T_max, int NB, int window, int pool, int topk, int nsplit,
-    float2 *__restrict__ part_ml, float *__restrict__ part_acc) {
-  static_assert(G >= 1 && G <= 16, "query heads per KV head");
-  __shared__ __align__(16) uint16_t s_v[4][AM_TILE * VROW];     // V tile per wave
-  __shared__ __align__(16) uint16_t s_p[4][2][16 * AM_TILE];    // P hi / lo [head][entry]
-  __shared__ float s_ml[4][16][2];
-  float *s_o = reinterpret_cast<float *>(&s_v[0][0]);          // reused after the loop
-
-  const int seg = blockIdx.y, split = blockIdx.x;
-  const int h = seg % Hkv, bi = seg / Hkv, i = bi % R, b = bi / R;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int Hq = Hkv * G;
-  const int e_wave = split * ATTN_SPLIT + wave * AM_WAVE_ENTRIES;
-  // The selected indices of entries e_wave + lane and e_wave + 64 + lane are
-  // loaded together with the length, before it is known whether the entries
-  // are selected ones (the addresses are clamped into the segment's idx row,
-  // so always in bounds).
-  const int32_t *idx_row = idx + (size_t)seg * topk;
-  const int sel0 = idx_row[min(e_wave + lane, topk - 1)];
-  const int sel1 = idx_row[min(e_wave + 64 + lane, topk - 1)];
-  const int L0 = clamp_len(seq_len[b], T_max, R);
-  const RowGeom rg = row_geom(L0, i, window, pool, topk);
-
-  // Descriptor of an entry: the row to gather (an index into the token rows,
-  // or the pooled rows when bit 1 of the flag is set) and whether it takes
-  // part.  Invalid entries point at row 0, which always exists, so the
-  // gathers below need no branches.  Lane l holds entries e_wave + l (row0,
-  // flag0) and e_wave + 64 + l (row1, flag1).
-  auto describe = [&](int e, int sel, int &row, int &flag) {
-    row = 0;
-    flag = 0;
-    if (e < rg.k_eff) {
-      if ((unsigned)sel < (unsigned)rg.n_far) {
-        row = sel;
-        flag = POOLED ? 3 : 1;
-      }
-    } else if (e < rg.n_ent) {
-      row = rg.ws + (e - rg.k_eff);
-      flag = 1;
-    }
-  };
-  int row0, flag0, row1, flag1;
-  describe(e_wave + lane, sel0, row0, flag0);
-  describe(e_wave + 64 + lane, sel1, row1, flag1);
-  // descriptor of wave entry j (a compile-time tile offset plus a lane value)
-  auto desc = [&](int j, int &r, int &f) {
-    if (j < 64) {
-      r = __shfl(row0, j);
-      f = __shfl(flag0, j);
-    } else {
-      r = __shfl(row1, j - 64);
-      f = __shfl(flag1, j - 64);
-    }
-  };
-
-  // Q as the A operand: head n, dims 32i + 8g .. +8 (zero rows past G)
-  u32x4_t qa[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    qa[c] = u32x4_t{0, 0, 0, 0};
-    if (n < G) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(
-          q + ((size_t)bi * Hq + (size_t)h * G + n) * D + 32 * c + 8 * g);
-      qa[c] = u32x4_t{w.x, w.y, w.z, w.w};
-    }
-  }
-
-  f32x4_t o[8];
-#pragma unroll
-  for (int blk = 0; blk < 8; ++blk) o[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m4[4], l4[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    m4[j] = NEG_INF;
-    l4[j] = 0.f;
-  }
-
-  constexpr int EB = DT == SKS_KV_BF16 ? 2 : 1;
-  const char *Kt = static_cast<const char *>(K) + ((size_t)b * Hkv + h) * T_max * D * EB;
-  const char *Vt = static_cast<const char *>(V) + ((size_t)b * Hkv + h) * T_max * D * EB;
-  const char *Kpb = reinterpret_cast<const char *>(Kp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
-  const char *Vpb = reinterpret_cast<const char *>(Vp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
-  const uint16_t *Kst = DT == SKS_KV_I8 ? Ks + ((size_t)b * Hkv + h) * T_max : nullptr;
-  const uint16_t *Vst = DT == SKS_KV_I8 ? Vs + ((size_t)b * Hkv + h) * T_max : nullptr;
-  uint16_t *sv = s_v[wave];
-
-  // Raw gathered data of one tile, as loaded (converted to bf16 only when the
-  // tile is consumed, so that the next tile's loads stay in flight meanwhile).
-  using KRaw = typename std::conditional<DT == SKS_KV_BF16, uint4, uint2>::type;
-  struct Tile {
-    KRaw k[2][4];          // K: sub-tile t, lane (n, g): entry 16t + n, dims 32c + 8g .. +8
-    KRaw v[8];             // V: chunk (x & 15) of tile row (x >> 4), x = 64 qq + lane
-    int f[2];              // flags of the two K entries of this lane
-    uint16_t ks[2], vs[2]; // int8 row scales of the two K entries (fp16 bits)
-  };
-  // K/V rows are read once per step: nontemporal loads keep them from
-  // evicting lines that are reused.
-  auto ld = [](const char *p) -> KRaw {
-    if constexpr (DT == SKS_KV_BF16) {
-      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-      return make_uint4(v[0], v[1], v[2], v[3]);
-    } else {
-      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-      const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
-      return make_uint2(v[0], v[1]);
-    }
-  };
-  auto gather = [&](int tile, Tile &d) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      int r, f;
-      desc(tile * AM_TILE + 16 * t + n, r, f);
-      d.f[t] = f;
-      const char *kbase = (POOLED && (f & 2)) ? Kpb : Kt;
-      const size_t off = (size_t)r * D * EB;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) d.k[t][c] = ld(kbase + off + (32 * c + 8 * g) * EB);
-      if constexpr (DT == SKS_KV_I8) {
-        d.ks[t] = Kst[r];
-        d.vs[t] = Vst[r];
-      }
-    }
-#pragma unroll
-    for (int qq = 0; qq < 8; ++qq) {
-      const int x = qq * 64 + lane, ev = x >> 4, c = x & 15;
-      int r, f;
-      desc(tile * AM_TILE + ev, r, f);
-      const char *vbase = (POOLED && (f & 2)) ? Vpb : Vt;
-      d.v[qq] = ld(vbase + (size_t)r * D * EB + c * 8 * EB);
-    }
-  };
-  auto to_bf16 = [&](const KRaw &w) -> u32x4_t {
-    if constexpr (DT == SKS_KV_BF16) {
-      return u32x4_t{w.x, w.y, w.z, w.w};
-    } else {
-      return u32x4_t{i8pair_to_bf16x2(w.x, 0), i8pair_to_bf16x2(w.x, 16),
-                     i8pair_to_bf16x2(w.y, 0), i8pair_to_bf16x2(w.y, 16)};
-    }
-  };
-
-  auto consume = [&](const Tile &d) {
-    // ---- QK on the matrix cores
-    f32x4_t sacc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) sacc[t] = mfma_bf16(qa[c], to_bf16(d.k[t][c]), sacc[t]);
-    }
-
-    // stage V (row-major, 8-byte stores: the padded stride is 8-byte aligned)
-#pragma unroll
-    for (int qq = 0; qq < 8; ++qq) {
-      const int x = qq * 64 + lane, ev = x >> 4, c = x & 15;
-      const u32x4_t w = to_bf16(d.v[qq]);
-      uint2 *dst = reinterpret_cast<uint2 *>(sv + ev * VROW + c * 8);
-      dst[0] = make_uint2(w[0], w[1]);
-      dst[1] = make_uint2(w[2], w[3]);
-    }
-
-    // ---- online softmax on the C layout (lane: heads 4g + j, entry n of each sub-tile)
-    float ksc[2], vsc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if constexpr (DT == SKS_KV_I8) {
-        ksc[t] = f16_bits_to_float(d.ks[t]);
-        vsc[t] = f16_bits_to_float(d.vs[t]);
-      } else {
-        ksc[t] = vsc[t] = 1.f;
-      }
-    }
-    float z[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) z[t][j] = (d.f[t] & 1) ? sacc[t][j] * ksc[t] * sm_log2 : NEG_INF;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float mx = row16_max_f(fmaxf(z[0][j], z[1][j]));
-      if (mx > m4[j] + RESCALE_SLACK || (m4[j] == NEG_INF && mx != NEG_INF)) {
-        const float alpha = m4[j] == NEG_INF ? 0.f : exp2_fast(m4[j] - mx);
-        l4[j] *= alpha;
-#pragma unroll
-        for (int blk = 0; blk < 8; ++blk) o[blk][j] *= alpha;
-        m4[j] = mx;
-      }
-    }
-    uint16_t *sp_hi = s_p[wave][0], *sp_lo = s_p[wave][1];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float pv = (z[t][j] == NEG_INF) ? 0.f : exp2_fast(z[t][j] - m4[j]);
-        l4[j] += pv;
-        const float pw = pv * vsc[t];                       // value scale folded in
-        const uint32_t hi = f32_to_bf16_rne(pw);
-        const uint32_t lo = f32_to_bf16_rne(pw - __uint_as_float(hi << 16));
-        const int at = (4 * g + j) * AM_TILE + 16 * t + n;
-        sp_hi[at] = (uint16_t)hi;
-        sp_lo[at] = (uint16_t)lo;
-      }
-    }
-    wave_lds_sync();
-
-    // ---- PV on the matrix cores: A = P (head n, entries 8g..8g+8), B = V
-    const uint4 ph = *reinterpret_cast<const uint4 *>(sp_hi + n * AM_TILE + 8 * g);
-    const uint4 pl = *reinterpret_cast<const uint4 *>(sp_lo + n * AM_TILE + 8 * g);
-    const u32x4_t pa_hi = u32x4_t{ph.x, ph.y, ph.z, ph.w};
-    const u32x4_t pa_lo = u32x4_t{pl.x, pl.y, pl.z, pl.w};
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
-      const uint16_t *col = sv + (8 * g) * VROW + 16 * blk + n;
-      u32x4_t vb;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        vb[k] = (uint32_t)col[(2 * k) * VROW] | ((uint32_t)col[(2 * k + 1) * VROW] << 16);
-      o[blk] = mfma_bf16(pa_hi, vb, o[blk]);
-      o[blk] = mfma_bf16(pa_lo, vb, o[blk]);
-    }
-    wave_lds_sync();                                        // before the next tile reuses LDS
-  };
-
-  // Software pipeline over the wave's tiles: the gathers of tile t + 1 are
-  // issued before tile t is consumed, so that the memory system always holds
-  // a tile's worth of requests per wave.
-  // Straight-line code: every tile is gathered and consumed (entries past the
-  // set read row 0 and are masked out), and the scheduling barriers keep each
-  // tile's loads in issue order.  The wait counter is in order, so a
-  // conditional or a reordered load of tile t + 1 would make tile t wait for
-  // it too.
-  Tile cur, nxt;
-  gather(0, cur);
-#pragma unroll
-  for (int tile = 0; tile < AM_TILES; ++tile) {
-    __builtin_amdgcn_sched_barrier(0);
-    if (tile + 1 < AM_TILES) gather(tile + 1, nxt);
-    __builtin_amdgcn_sched_barrier(0);
-    consume(cur);
-    cur = nxt;
-  }
-
-  // denominators: sum the lane-partials over the 16 lanes of each DPP row
-#pragma unroll
-  for (int j = 0; j < 4; ++j) l4[j] = row16_sum_f(l4[j]);
-  __syncthreads();                                          // s_v is reused as s_o below
-  // wave partials to LDS: O rows 4g + j < G
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int hh = 4 * g + j;
-    if (hh < G) {
-#pragma unroll
-      for (int blk = 0; blk < 8; ++blk) s_o[(wave * G + hh) * D + 16 * blk + n] = o[blk][j];
-      if (n == 0) {
-        s_ml[wave][hh][0] = m4[j];
-        s_ml[wave][hh][1] = l4[j];
-      }
-    }
-  }
-  __syncthreads();
-  // merge the 4 waves and write this split's partial
-  const size_t pbase = (size_t)seg * nsplit + split;
-  for (int x = threadIdx.x; x < G * D; x += AT_THREADS) {
-    const int j = x / D, d = x % D;
-    float M = NEG_INF;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][j][0]);
-    float Lsum = 0.f, A = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = s_ml[w][j][0];
-      const float wt = mw == NEG_INF ? 0.f : exp2_fast(mw - M);
-      Lsum += s_ml[w][j][1] * wt;
-      A += s_o[(w * G + j) * D + d] * wt;
-    }
-    part_acc[(pbase * G + j) * D + d] = A;
-    if (d == 0) part_ml[pbase * G + j] = make_float2(M, Lsum);
-  }
-
-}
 
 // One workgroup of 128 threads per (segment, query head of the group).
 __global__ __launch_bounds__(D) void attn_merge_kernel(const float2 *__restrict__ part_ml,
@@ -449,35 +26,20 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float2 *__restrict_
   merge_splits(part_ml, part_acc, blockIdx.x, blockIdx.y, threadIdx.x, nsplit, G, Hkv, out, lse);
 }
 
-struct AttnOut {
-  float2 *pml;
-  float *pacc;
-  float *out, *lse;
-};
-
 template <int G, int DT, bool POOLED>
-void launch_split(dim3 grid, hipStream_t st, const uint16_t *q, const sks_kv &kv, const Shape &s,
-                  const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp, float sm_log2,
-                  int nsplit, const AttnOut &o) {
-  attn_mfma_kernel<G, DT, POOLED><<<grid, AT_THREADS, 0, st>>>(
-      q, kv.K, kv.V, kv.K_scale, kv.V_scale, kv.seq_len, idx, Kp, Vp, sm_log2, s.R, s.Hkv,
-      s.T_max, s.NB, s.window, s.pool, s.topk, nsplit, o.pml, o.pacc);
+__global__ __launch_bounds__(AT_THREADS) void attn_kernel(AttnArgs a, int slot0) {
+  __shared__ AttnLds lds;
+  attn_body<G, DT, POOLED>(a, blockIdx.y, slot0 + blockIdx.x, lds);
 }
 
 template <int G>
-void dispatch_g(dim3 grid, hipStream_t st, const uint16_t *q, const sks_kv &kv, const Shape &s,
-                const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp, float sm_log2,
-                int nsplit, const AttnOut &o) {
-  if (s.dtype == SKS_KV_I8)
-    launch_split<G, SKS_KV_I8, false>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o);
-  else if (s.pool > 1)
-    launch_split<G, SKS_KV_BF16, true>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o);
+void dispatch_g(dim3 grid, hipStream_t st, const AttnArgs &a, int dtype, int pool, int slot0) {
+  if (dtype == SKS_KV_I8)
+    attn_kernel<G, SKS_KV_I8, false><<<grid, AT_THREADS, 0, st>>>(a, slot0);
+  else if (pool > 1)
+    attn_kernel<G, SKS_KV_BF16, true><<<grid, AT_THREADS, 0, st>>>(a, slot0);
   else
-    launch_split<G, SKS_KV_BF16, false>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o);
-}
-
-int attn_nsplit(const Shape &s) {
-  return ceil_div((long)s.topk + s.window + s.pool - 1, ATTN_SPLIT);
+    attn_kernel<G, SKS_KV_BF16, false><<<grid, AT_THREADS, 0, st>>>(a, slot0);
 }
 
 }  // namespace
@@ -488,33 +50,70 @@ size_t attn_scratch_bytes(const Shape &s, int G) {
   return align_up(n * sizeof(float2), 256) + align_up(n * D * sizeof(float), 256);
 }
 
+AttnArgs attn_args(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
+                   const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp, float sm_scale,
+                   const TopkWs &w) {
+  const int G = Hq / s.Hkv;
+  const int nseg = s.B * s.R * s.Hkv;
+  AttnArgs a;
+  a.q = q;
+  a.K = kv.K;
+  a.V = kv.V;
+  a.Ks = kv.K_scale;
+  a.Vs = kv.V_scale;
+  a.seq_len = kv.seq_len;
+  a.idx = idx;
+  a.Kp = Kp;
+  a.Vp = Vp;
+  a.sm_log2 = sm_scale * 1.4426950408889634f;
+  a.R = s.R;
+  a.Hkv = s.Hkv;
+  a.T_max = s.T_max;
+  a.NB = s.NB;
+  a.window = s.window;
+  a.pool = s.pool;
+  a.topk = s.topk;
+  a.nsplit = attn_nsplit(s);
+  const size_t n = (size_t)nseg * a.nsplit * G;
+  a.part_ml = reinterpret_cast<float2 *>(w.attn);
+  a.part_acc = reinterpret_cast<float *>(w.attn + align_up(n * sizeof(float2), 256));
+  return a;
+}
+
+hipError_t launch_attn_slots(const AttnArgs &a, int G, int dtype, int nseg, int slot0, int nslots,
+                             hipStream_t st) {
+  if (nslots <= 0) return hipSuccess;
+  dim3 grid(nslots, nseg);
+  switch (G) {
+    case 1: dispatch_g<1>(grid, st, a, dtype, a.pool, slot0); break;
+    case 2: dispatch_g<2>(grid, st, a, dtype, a.pool, slot0); break;
+    case 3: dispatch_g<3>(grid, st, a, dtype, a.pool, slot0); break;
+    case 4: dispatch_g<4>(grid, st, a, dtype, a.pool, slot0); break;
+    case 5: dispatch_g<5>(grid, st, a, dtype, a.pool, slot0); break;
+    case 6: dispatch_g<6>(grid, st, a, dtype, a.pool, slot0); break;
+    case 7: dispatch_g<7>(grid, st, a, dtype, a.pool, slot0); break;
+    case 8: dispatch_g<8>(grid, st, a, dtype, a.pool, slot0); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const AttnArgs &a, int G, int nseg, float *out, float *lse,
+                             hipStream_t st) {
+  attn_merge_kernel<<<dim3(nseg, G), D, 0, st>>>(a.part_ml, a.part_acc, a.nsplit, G, a.Hkv, out,
+                                                 lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
                        const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp,
                        float sm_scale, float *out, float *lse, const TopkWs &w, hipStream_t st) {
   const int G = Hq / s.Hkv;
   const int nseg = s.B * s.R * s.Hkv;
-  const int nsplit = attn_nsplit(s);
-  const size_t n = (size_t)nseg * nsplit * G;
-  float2 *pml = reinterpret_cast<float2 *>(w.scratch);
-  float *pacc = reinterpret_cast<float *>(w.scratch + align_up(n * sizeof(float2), 256));
-  const float sm_log2 = sm_scale * 1.4426950408889634f;
-  dim3 grid(nsplit, nseg);
-  const AttnOut o{pml, pacc, out, lse};
-  switch (G) {
-    case 1: dispatch_g<1>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
-    case 2: dispatch_g<2>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
-    case 3: dispatch_g<3>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
-    case 4: dispatch_g<4>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
-    case 5: dispatch_g<5>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
-    case 6: dispatch_g<6>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
-    case 7: dispatch_g<7>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
-    case 8: dispatch_g<8>(grid, st, q, kv, s, idx, Kp, Vp, sm_log2, nsplit, o); break;
-    default: return hipErrorInvalidValue;
-  }
-  hipError_t e = hipGetLastError();
+  const AttnArgs a = attn_args(q, Hq, kv, s, idx, Kp, Vp, sm_scale, w);
+  hipError_t e = launch_attn_slots(a, G, s.dtype, nseg, 0, a.nsplit, st);
   if (e != hipSuccess) return e;
-  attn_merge_kernel<<<dim3(nseg, G), D, 0, st>>>(pml, pacc, nsplit, G, s.Hkv, out, lse);
-  return hipGetLastError();
+  return launch_attn_merge(a, G, nseg, out, lse, st);
 }
 
 }  // namespace sks

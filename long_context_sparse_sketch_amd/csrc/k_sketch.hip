@@ -178,17 +178,19 @@ __global__ __launch_bounds__(KS_THREADS) void sketch_pool_kernel(
 // LDS, lane c dots basis row c with it, so the latency is that of one row
 // instead of one lane walking all 64 x 128 products.
 template <int DT>
-__global__ __launch_bounds__(64) void sketch_rows_small_kernel(
-    const void *__restrict__ K, const void *__restrict__ V, const uint16_t *__restrict__ Ks,
-    const int32_t *__restrict__ seq_len, const float *__restrict__ basis, int basis_per_head,
-    const float *__restrict__ key_scale, int Hkv, int T_max, int R, int NB, int pool, int append,
-    int t_begin, int t_end, int8_t *__restrict__ S, uint16_t *__restrict__ Kp,
-    uint16_t *__restrict__ Vp) {
+__device__ void sketch_row_wave(const void *__restrict__ K, const void *__restrict__ V,
+                                const uint16_t *__restrict__ Ks,
+                                const int32_t *__restrict__ seq_len,
+                                const float *__restrict__ basis, int basis_per_head,
+                                const float *__restrict__ key_scale, int Hkv, int T_max, int R,
+                                int NB, int pool, int append, int t_begin, int t_end,
+                                int8_t *__restrict__ S, uint16_t *__restrict__ Kp,
+                                uint16_t *__restrict__ Vp, int bh, int jx) {
   __shared__ float x[D];
-  const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
+  const int b = bh / Hkv, h = bh % Hkv;
   int j_lo, j_hi;
   sketch_range(append, seq_len, b, T_max, R, pool, NB, t_begin, t_end, j_lo, j_hi);
-  const int j = j_lo + blockIdx.x;
+  const int j = j_lo + jx;
   if (j >= j_hi) return;
   const int lane = threadIdx.x;
   if (pool == 1) {
@@ -237,13 +239,23 @@ __global__ __launch_bounds__(64) void sketch_rows_small_kernel(
   S[((size_t)bh * NB + j) * RANK + lane] = quant_code(y, key_scale[h]);
 }
 
+template <int DT>
+__global__ __launch_bounds__(64) void sketch_rows_small_kernel(
+    const void *__restrict__ K, const void *__restrict__ V, const uint16_t *__restrict__ Ks,
+    const int32_t *__restrict__ seq_len, const float *__restrict__ basis, int basis_per_head,
+    const float *__restrict__ key_scale, int Hkv, int T_max, int R, int NB, int pool, int append,
+    int t_begin, int t_end, int8_t *__restrict__ S, uint16_t *__restrict__ Kp,
+    uint16_t *__restrict__ Vp) {
+  sketch_row_wave<DT>(K, V, Ks, seq_len, basis, basis_per_head, key_scale, Hkv, T_max, R, NB, pool,
+                      append, t_begin, t_end, S, Kp, Vp, blockIdx.y, blockIdx.x);
+}
+
 // Query sketch: one wave per (b, i, h).  qbar = mean of the group's queries
 // (fp32), y = P qbar by lane c, absmax over the wave, codes by lane c.
-__global__ __launch_bounds__(64) void sketch_query_kernel(
-    const uint16_t *__restrict__ q, int R, int Hq, int Hkv, const float *__restrict__ basis,
-    int basis_per_head, int8_t *__restrict__ qsk, float *__restrict__ qscale) {
-  __shared__ float qbar[D];
-  const int seg = blockIdx.x;                  // (b * R + i) * Hkv + h
+__device__ void sketch_query_wave(const uint16_t *__restrict__ q, int R, int Hq, int Hkv,
+                                  const float *__restrict__ basis, int basis_per_head,
+                                  int8_t *__restrict__ qsk, float *__restrict__ qscale, int seg) {
+  __shared__ float qbar[D];                    // seg = (b * R + i) * Hkv + h
   const int h = seg % Hkv, bi = seg / Hkv;
   const int g = Hq / Hkv;
   const int lane = threadIdx.x;
@@ -266,6 +278,31 @@ __global__ __launch_bounds__(64) void sketch_query_kernel(
   int8_t code = amax > 0.f ? quant_code(y, scale) : (int8_t)0;
   qsk[(size_t)seg * RANK + lane] = code;
   if (lane == 0 && qscale) qscale[seg] = amax > 0.f ? scale : 0.f;
+}
+
+__global__ __launch_bounds__(64) void sketch_query_kernel(
+    const uint16_t *__restrict__ q, int R, int Hq, int Hkv, const float *__restrict__ basis,
+    int basis_per_head, int8_t *__restrict__ qsk, float *__restrict__ qscale) {
+  sketch_query_wave(q, R, Hq, Hkv, basis, basis_per_head, qsk, qscale, blockIdx.x);
+}
+
+// The step prologue in one launch: workgroups [0, nq) sketch the queries,
+// the rest the rows' own tokens (append), nrows per (b, h).
+template <int DT>
+__global__ __launch_bounds__(64) void step_prologue_kernel(
+    const uint16_t *__restrict__ q, int Hq, const void *__restrict__ K,
+    const void *__restrict__ V, const uint16_t *__restrict__ Ks,
+    const int32_t *__restrict__ seq_len, const float *__restrict__ basis, int basis_per_head,
+    const float *__restrict__ key_scale, int Hkv, int T_max, int R, int NB, int pool, int nq,
+    int nrows, int8_t *__restrict__ qsk, float *__restrict__ qscale, int8_t *__restrict__ S,
+    uint16_t *__restrict__ Kp, uint16_t *__restrict__ Vp) {
+  if ((int)blockIdx.x < nq) {
+    sketch_query_wave(q, R, Hq, Hkv, basis, basis_per_head, qsk, qscale, blockIdx.x);
+    return;
+  }
+  const int w = blockIdx.x - nq;
+  sketch_row_wave<DT>(K, V, Ks, seq_len, basis, basis_per_head, key_scale, Hkv, T_max, R, NB, pool,
+                      1, 0, 0, S, Kp, Vp, w / nrows, w % nrows);
 }
 
 }  // namespace
@@ -309,6 +346,27 @@ hipError_t launch_sketch_keys(const sks_kv &kv, const Shape &s, const float *bas
         basis, basis_per_head, key_scale, s.Hkv, s.T_max, s.R, s.NB, s.pool, append, t_begin,
         t_end, S, Kp, Vp);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_step_prologue(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
+                                const float *basis, int basis_per_head, const float *key_scale,
+                                int8_t *qsk, float *qscale, int8_t *S, uint16_t *Kp, uint16_t *Vp,
+                                hipStream_t st) {
+  // append rows per (b, h), as in launch_sketch_keys' append mode
+  long nrows = s.pool == 1 ? (long)s.R : ((long)s.R + s.pool) / s.pool + 1;
+  if (nrows > s.NB) nrows = s.NB;
+  if (nrows > SMALL_ROWS) return hipErrorInvalidValue;
+  const int nq = s.B * s.R * s.Hkv;
+  const unsigned grid = (unsigned)(nq + nrows * s.B * s.Hkv);
+  if (s.dtype == SKS_KV_BF16)
+    step_prologue_kernel<SKS_KV_BF16><<<grid, 64, 0, st>>>(
+        q, Hq, kv.K, kv.V, nullptr, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max,
+        s.R, s.NB, s.pool, nq, (int)nrows, qsk, qscale, S, Kp, Vp);
+  else
+    step_prologue_kernel<SKS_KV_I8><<<grid, 64, 0, st>>>(
+        q, Hq, kv.K, kv.V, kv.K_scale, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv,
+        s.T_max, s.R, s.NB, s.pool, nq, (int)nrows, qsk, qscale, S, Kp, Vp);
   return hipGetLastError();
 }
 

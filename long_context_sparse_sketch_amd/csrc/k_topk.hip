@@ -27,99 +27,10 @@
 //     LDS -- or from the raw scores, if fewer than k candidates came through.
 //     The histograms are never trusted beyond what the data confirms.  It
 //     returns the segment's histograms to zero.
-#include "sks_internal.h"
+#include "topk_body.h"
 
 namespace sks {
 namespace {
-
-constexpr int TK_THREADS = 256;
-constexpr int TF_THREADS = 1024;
-constexpr int TF_WAVES = TF_THREADS / 64;
-constexpr int TF_CACHE = 8192;                     // candidates held by one final workgroup
-constexpr int TF_PERT = TF_CACHE / TF_THREADS;     // consecutive candidates per thread
-constexpr int FILTER_ITERS = TK_SUB / 64;          // 16 loads in flight per lane
-constexpr int HIST2_DIRECT_MAX = 4096;             // level-2 histogram built when bin b1 is this small
-static_assert(TK_CHUNK == TK_SUB * (TK_THREADS / 64), "one sub-chunk per wave");
-static_assert(TF_CACHE < 65536, "packed 16-bit counts in the emission scan");
-static_assert(TF_PERT == 8, "mark padding: one int every 8 slots");
-
-struct SegGeom {
-  int b, i, h, n_far, k_eff;
-};
-
-__device__ __forceinline__ SegGeom seg_geom(int seg, const int32_t *seq_len, int R, int Hkv,
-                                            int T_max, int window, int pool, int topk) {
-  SegGeom g;
-  g.h = seg % Hkv;
-  g.i = (seg / Hkv) % R;
-  g.b = seg / (Hkv * R);
-  const int L0 = clamp_len(seq_len[g.b], T_max, R);
-  RowGeom rg = row_geom(L0, g.i, window, pool, topk);
-  g.n_far = rg.n_far;
-  g.k_eff = rg.k_eff;
-  return g;
-}
-
-// Inclusive block-wide prefix sum of NW waves; `tot` receives the block
-// total.  `scratch` holds NW ints.  With REUSE a second barrier lets the
-// caller use the same scratch again right away.
-template <int NW, bool REUSE>
-__device__ int block_incl_scan(int v, int *scratch, int &tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int incl = wave_incl_add(v);
-  if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  tot = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int t = scratch[w];
-    before += w < wave ? t : 0;
-    tot += t;
-  }
-  if (REUSE) __syncthreads();
-  return incl + before;
-}
-
-// Exclusive block-wide running maximum of non-negative values (0 before the
-// first thread); `scratch` holds NW ints and is not reused.
-template <int NW>
-__device__ int block_excl_max(int v, int *scratch) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int incl = wave_incl_max(v);
-  if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
-  int before = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) before = max(before, w < wave ? scratch[w] : 0);
-  const int prev = __builtin_amdgcn_update_dpp(0, incl, DPP_ROW_SHR + 1, 0xF, 0xF, false);
-  // the lane before the first of a row is the last lane of the previous row
-  const int r15 = __builtin_amdgcn_readlane(incl, 15), r31 = __builtin_amdgcn_readlane(incl, 31),
-            r47 = __builtin_amdgcn_readlane(incl, 47);
-  const int row = lane >> 4;
-  const int prev_row = row == 0 ? 0 : (row == 1 ? r15 : (row == 2 ? r31 : r47));
-  return max(before, (lane & 15) ? prev : prev_row);
-}
-
-// LDS histograms are stored padded so that 64 lanes reading their contiguous
-// bins hit distinct banks.
-template <int NBINS>
-__device__ __forceinline__ int hpad(int b) { return b + b / (NBINS / 64); }
-template <int NBINS>
-constexpr int hpad_size() { return NBINS + 64; }
-
-// Threshold search by one wave over a padded LDS histogram of NBINS bins
-// (see wave_threshold_regs: an invalid histogram yields bin 0).
-template <int NBINS>
-__device__ int wave_threshold_bin(const int *hist, int need, int n, int &above) {
-  constexpr int PER = NBINS / 64;
-  const int lane = threadIdx.x & 63;
-  int v[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) v[k] = hist[hpad<NBINS>(lane * PER + k)];
-  bool valid;
-  return wave_threshold_regs<PER>(v, need, n, above, valid);
-}
 
 __global__ void fill_kernel(int32_t *p, size_t n, int32_t v) {
   for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < n;
@@ -289,252 +200,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
   if (lane == 0) *cnt_out = n;
 }
 
-__global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
-    const int32_t *__restrict__ scores, const int32_t *__restrict__ seq_len,
-    int32_t *__restrict__ hist1, int32_t *__restrict__ hist2, const int32_t *__restrict__ thr,
-    const int32_t *__restrict__ cnt, const int2 *__restrict__ cand, int n_sub_max, int R, int Hkv,
-    int T_max, int NB, int window, int pool, int topk, int32_t *__restrict__ idx,
-    int32_t *__restrict__ n_sel) {
-  __shared__ int h1[hpad_size<HIST1_BINS>()];
-  __shared__ int h2[hpad_size<HIST2_BINS>()];
-  __shared__ int pre[TK_MAX_SUBS + 1];
-  __shared__ int2 cache[TF_CACHE];
-  // sub-list start marks, one int per slot padded by one every 8 so that a
-  // thread's 8 consecutive slots fall in distinct banks across the wave
-  __shared__ int marks[TF_CACHE + TF_CACHE / 8];
-  __shared__ int sc_pre[TF_WAVES], sc_own[TF_WAVES], sc_cnt[TF_WAVES];
-  __shared__ int res[6];
-  const int seg = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int32_t *gc = cnt + (size_t)seg * n_sub_max;
-  int32_t *gh2 = hist2 + (size_t)seg * HIST2_BINS;
-  // loads first: the first round of sub-list counts, the threshold record
-  // and (wave 0) the level-2 histogram, lane l holding bins [16l, 16l+16)
-  const int cv0 = threadIdx.x < n_sub_max ? gc[threadIdx.x] : 0;
-  const int4 th = reinterpret_cast<const int4 *>(thr)[seg];   // (b1, above b1, valid, in b1)
-  constexpr int H2_PER = HIST2_BINS / 64;
-  int hv[H2_PER];
-  if (wave == 0) {
-#pragma unroll
-    for (int k = 0; k < H2_PER / 4; ++k) {
-      const int4 w = reinterpret_cast<const int4 *>(gh2 + lane * H2_PER)[k];
-      hv[4 * k] = w.x;
-      hv[4 * k + 1] = w.y;
-      hv[4 * k + 2] = w.z;
-      hv[4 * k + 3] = w.w;
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < TF_PERT; ++q) marks[threadIdx.x * (TF_PERT + 1) + q] = 0;   // no mark
-  const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
-  int32_t *out = idx + (size_t)seg * topk;
-  // the filter has run: the segment's level-1 histogram returns to zero
-  int32_t *gh1 = hist1 + (size_t)seg * HIST1_BINS;
-  for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh1[k] = 0;
-  if (threadIdx.x == 0 && n_sel) n_sel[seg] = g.k_eff;
+constexpr int TF_THREADS = 1024;
 
-  // wave 0: the threshold guess T from the level-2 histogram (-1: none),
-  // then that histogram returns to zero (its values are consumed)
-  if (wave == 0) {
-    int T = -1;
-    if (g.k_eff < g.n_far && th.z && th.w >= 0 && th.w <= HIST2_DIRECT_MAX && th.x >= 0 &&
-        th.x < HIST1_BINS) {
-      int above;
-      bool valid;
-      const int b2 = wave_threshold_regs<H2_PER>(hv, g.k_eff - th.y, th.w, above, valid);
-      if (valid) T = (th.x << HIST2_BITS) | b2;
-    }
-    if (lane == 0) res[5] = T;
-#pragma unroll
-    for (int k = 0; k < H2_PER / 4; ++k)
-      reinterpret_cast<int4 *>(gh2 + lane * H2_PER)[k] = make_int4(0, 0, 0, 0);
-  }
-  if (g.k_eff >= g.n_far) {                      // every far entry is selected
-    for (int j = threadIdx.x; j < topk; j += TF_THREADS) out[j] = j < g.n_far ? j : -1;
-    return;
-  }
-
-  // candidate list: exclusive prefix over the sub-list counts; every
-  // non-empty sub-list also marks its first slot with its number + 1
-  const int n_sub = (g.n_far + TK_SUB - 1) / TK_SUB;
-  int carry = 0;
-  for (int base = 0; base < n_sub; base += TF_THREADS) {
-    const int sidx = base + threadIdx.x;
-    const int v = sidx < n_sub ? (base == 0 ? cv0 : gc[sidx]) : 0;
-    int tot;
-    const int incl = block_incl_scan<TF_WAVES, true>(v, sc_pre, tot);
-    const int start = carry + incl - v;
-    if (sidx < n_sub) {
-      pre[sidx] = start;
-      if (v > 0 && start < TF_CACHE) marks[start + (start >> 3)] = sidx + 1;
-    }
-    carry += tot;
-  }
-  if (threadIdx.x == 0) pre[n_sub] = carry;
-  __syncthreads();
-  // Fewer candidates than k means the filter's histogram was not one of these
-  // scores: select from the raw scores instead.
-  const bool raw = carry < g.k_eff;
-  const int m = raw ? g.n_far : carry;
-  const int2 *cseg = cand + (size_t)seg * n_sub_max * TK_SUB;
-  const int32_t *srow = scores + (size_t)seg * NB;
-  const bool cached = !raw && m <= TF_CACHE;
-  const int o0 = threadIdx.x * TF_PERT;          // this thread's slots [o0, o0 + TF_PERT)
-
-  if (cached) {
-    // The sub-list holding slot o is the last mark at or before o: a running
-    // maximum over the marks of this thread's slots, then across the block.
-    int mk[TF_PERT];
-    int run = 0;
-#pragma unroll
-    for (int q = 0; q < TF_PERT; ++q) {
-      run = max(run, marks[threadIdx.x * (TF_PERT + 1) + q]);
-      mk[q] = run;
-    }
-    const int before = block_excl_max<TF_WAVES>(run, sc_own);
-    int2 c[TF_PERT];
-#pragma unroll
-    for (int q = 0; q < TF_PERT; ++q) {
-      const int o = min(o0 + q, m - 1);
-      const int s = min(max(max(before, mk[q]), 1) - 1, n_sub - 1);   // clamped: always in bounds
-      c[q] = cseg[(size_t)s * TK_SUB + min(max(o - pre[s], 0), TK_SUB - 1)];
-    }
-    const int T = res[5];
-    if (T >= 0) {
-      // Count, from the data, the candidates above T and equal to T.  Every
-      // element with key >= T is a candidate (its bin is >= b1), so T is the
-      // k-th largest key exactly when above < k <= above + equal.
-      int gt = 0, tie = 0;
-#pragma unroll
-      for (int q = 0; q < TF_PERT; ++q) {
-        const bool in = o0 + q < m;
-        gt += in && c[q].y > T;
-        tie += in && c[q].y == T;
-      }
-      const int packed = gt | (tie << 16);
-      int tot;
-      const int ex = block_incl_scan<TF_WAVES, false>(packed, sc_cnt, tot) - packed;
-      const int gt_tot = tot & 0xffff, tie_tot = tot >> 16;
-      if (gt_tot < g.k_eff && gt_tot + tie_tot >= g.k_eff) {      // uniform
-        const int need = g.k_eff - gt_tot;     // ties at T to take, lowest index first
-        int gt_before = ex & 0xffff, tie_before = ex >> 16;
-#pragma unroll
-        for (int q = 0; q < TF_PERT; ++q) {
-          const bool in = o0 + q < m;
-          const bool is_gt = in && c[q].y > T, is_tie = in && c[q].y == T;
-          const bool sel = is_gt || (is_tie && tie_before < need);
-          const int pos = gt_before + min(tie_before, need);
-          if (sel) out[pos] = c[q].x;
-          gt_before += is_gt;
-          tie_before += is_tie;
-        }
-        for (int j = g.k_eff + threadIdx.x; j < topk; j += TF_THREADS) out[j] = -1;
-        return;
-      }
-    }
-    // the guess did not hold: keep the candidates in LDS for the exact path
-#pragma unroll
-    for (int q = 0; q < TF_PERT; ++q)
-      if (o0 + q < m) cache[o0 + q] = c[q];
-  }
-
-  // ---- exact path without the level-2 histogram
-  auto get = [&](int o) -> int2 {                // uncached access
-    if (raw) return make_int2(o, biased_key(srow[o]));
-    int lo = 0, hi = n_sub;                      // last sub-list s with pre[s] <= o
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pre[mid] <= o) lo = mid; else hi = mid;
-    }
-    return cseg[(size_t)lo * TK_SUB + (o - pre[lo])];
-  };
-  auto fetch = [&](int o) -> int2 { return cached ? cache[o] : get(o); };
-  for (int k = threadIdx.x; k < hpad_size<HIST1_BINS>(); k += TF_THREADS) h1[k] = 0;
-  for (int k = threadIdx.x; k < hpad_size<HIST2_BINS>(); k += TF_THREADS) h2[k] = 0;
-  if (threadIdx.x == 0) res[4] = 0;
-  __syncthreads();
-
-  // Level 1 (top 11 bits): the candidates are exactly the elements of bins
-  // >= thr.x.  If that bin is a legal threshold -- fewer than k candidates
-  // above it, counted here from the data -- level 1 is known; otherwise it is
-  // derived from the candidates' own histogram.
-  bool fast = th.z && !raw && th.x >= 0 && th.x < HIST1_BINS;
-  if (fast) {
-    int part = 0;
-    for (int o = threadIdx.x; o < m; o += TF_THREADS) part += (fetch(o).y >> HIST2_BITS) > th.x;
-    part = __builtin_amdgcn_readlane(wave_incl_add(part), 63);
-    if (lane == 0 && part) atomicAdd(&res[4], part);
-    __syncthreads();
-    const int above_data = res[4];
-    fast = above_data < g.k_eff;                 // uniform
-    if (fast && threadIdx.x == 0) {
-      res[0] = th.x;
-      res[1] = g.k_eff - above_data;             // still needed from bin b1
-      h1[hpad<HIST1_BINS>(th.x)] = m - above_data;   // candidates in bin b1
-    }
-  }
-  if (!fast) {
-    for (int o = threadIdx.x; o < m; o += TF_THREADS)
-      atomicAdd(&h1[hpad<HIST1_BINS>(fetch(o).y >> HIST2_BITS)], 1);
-    __syncthreads();
-    if (wave == 0) {
-      int above;
-      const int bb = wave_threshold_bin<HIST1_BINS>(h1, g.k_eff, m, above);
-      if (lane == 0) {
-        res[0] = bb;
-        res[1] = g.k_eff - above;
-      }
-    }
-  }
-  __syncthreads();
-  const int b1 = res[0], need1 = res[1];
-  // level 2 (low 10 bits) over the candidates of bin b1
-  for (int o = threadIdx.x; o < m; o += TF_THREADS) {
-    const int2 c = fetch(o);
-    if ((c.y >> HIST2_BITS) == b1) atomicAdd(&h2[hpad<HIST2_BINS>(c.y & (HIST2_BINS - 1))], 1);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int above;
-    const int b2 = wave_threshold_bin<HIST2_BINS>(h2, need1, h1[hpad<HIST1_BINS>(b1)], above);
-    if (lane == 0) {
-      res[2] = (b1 << HIST2_BITS) | b2;
-      res[3] = need1 - above;                    // ties at T to take, lowest index first
-    }
-  }
-  __syncthreads();
-  const int T = res[2], need2 = res[3];
-
-  // ordered emission: each thread owns 4 consecutive candidates per round,
-  // one block scan of packed (greater-than, tie) counts per round
-  int run_gt = 0, run_tie = 0;
-  for (int base = 0; base < m; base += 4 * TF_THREADS) {
-    const int e0 = base + 4 * threadIdx.x;
-    int2 c[4];
-    int gt = 0, tie = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      c[q] = e0 + q < m ? fetch(e0 + q) : make_int2(0, -1);
-      gt += c[q].y > T;
-      tie += c[q].y == T;
-    }
-    const int packed = gt | (tie << 16);
-    int tot;
-    const int ex = block_incl_scan<TF_WAVES, true>(packed, sc_pre, tot) - packed;
-    int gt_before = run_gt + (ex & 0xffff), tie_before = run_tie + (ex >> 16);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool is_gt = c[q].y > T, is_tie = c[q].y == T;
-      const bool sel = is_gt || (is_tie && tie_before < need2);
-      const int pos = gt_before + min(tie_before, need2);
-      if (sel && pos < topk) out[pos] = c[q].x;
-      gt_before += is_gt;
-      tie_before += is_tie;
-    }
-    run_gt += tot & 0xffff;
-    run_tie += tot >> 16;
-  }
-  for (int j = g.k_eff + threadIdx.x; j < topk; j += TF_THREADS) out[j] = -1;
+__global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(FinalArgs a) {
+  __shared__ FinalLds<TF_THREADS, TK_MAX_SUBS, true> lds;
+  final_body<TF_THREADS, TK_MAX_SUBS, true>(a, blockIdx.x, lds);
 }
 
 }  // namespace
@@ -571,6 +241,7 @@ TopkWs topk_ws_carve(const Shape &s, void *ws) {
   p += align_up(nseg * n_sub * 4, 256);
   w.cand = reinterpret_cast<int2 *>(p);
   w.nchunk = (int)n_sub;
+  w.attn = base + hist_region_bytes(s) + topk_scratch_bytes(s);
   return w;
 }
 
@@ -580,9 +251,8 @@ hipError_t launch_fill(int32_t *p, size_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shape &s,
-                       bool hist_ready, int32_t *idx, int32_t *n_sel, const TopkWs &w,
-                       hipStream_t st) {
+hipError_t launch_topk_filter(const int32_t *scores, const int32_t *seq_len, const Shape &s,
+                              bool hist_ready, const TopkWs &w, hipStream_t st) {
   const int nseg = s.B * s.R * s.Hkv;
   long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   if (max_far > 0) {
@@ -596,9 +266,16 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
                                                     s.Hkv, s.T_max, s.NB, s.window, s.pool,
                                                     s.topk);
   }
-  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(scores, seq_len, w.hist1, w.hist2, w.counters,
-                                                 w.cnt, w.cand, w.nchunk, s.R, s.Hkv, s.T_max,
-                                                 s.NB, s.window, s.pool, s.topk, idx, n_sel);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shape &s,
+                       bool hist_ready, int32_t *idx, int32_t *n_sel, const TopkWs &w,
+                       hipStream_t st) {
+  const int nseg = s.B * s.R * s.Hkv;
+  hipError_t e = launch_topk_filter(scores, seq_len, s, hist_ready, w, st);
+  if (e != hipSuccess) return e;
+  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(final_args(scores, seq_len, s, idx, n_sel, w));
   return hipGetLastError();
 }
 

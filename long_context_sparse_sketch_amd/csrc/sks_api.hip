@@ -105,8 +105,7 @@ int check_heads(int Hq, int Hkv) {
   } while (0)
 
 size_t ws_bytes(const sks::Shape &s, int G) {
-  return sks::hist_region_bytes(s) +
-         std::max(sks::topk_scratch_bytes(s), sks::attn_scratch_bytes(s, G));
+  return sks::hist_region_bytes(s) + sks::topk_scratch_bytes(s) + sks::attn_scratch_bytes(s, G);
 }
 
 size_t topk_need(const sks::Shape &s) {
@@ -272,10 +271,59 @@ int sks_sparse_decode_attn(const uint16_t *q, int32_t Hq, const sks_kv *kv, cons
   }
   REQUIRE(sm_scale > 0.f && sm_scale < 1e30f, "sm_scale must be positive and finite");
   TRY(check_ws(ws, ws_bytes_given,
-               sks::hist_region_bytes(s) + sks::attn_scratch_bytes(s, Hq / kv->Hkv)));
+               ws_bytes(s, Hq / kv->Hkv)));
   return hip_status(sks::launch_attn(q, Hq, *kv, s, idx, Kp, Vp, sm_scale, out, lse,
                                      sks::topk_ws_carve(s, ws), (hipStream_t)stream),
                     "sks_sparse_decode_attn");
+}
+
+int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *st, int32_t flags,
+                    void *ws, size_t ws_bytes_given, sks_stream_t stream) {
+  sks::Shape s;
+  TRY(check_shape(kv, p, s));
+  TRY(check_cache(kv, true));
+  REQUIRE(st != nullptr, "step must not be NULL");
+  REQUIRE((flags & ~SKS_STEP_APPEND) == 0, "unknown flags 0x%x", flags);
+  TRY(check_heads(st->Hq, kv->Hkv));
+  REQUIRE(st->basis_per_head == 0 || st->basis_per_head == 1, "basis_per_head must be 0 or 1");
+  REQUIRE_PTR(st->q, 16);
+  REQUIRE_PTR(st->basis, 4);
+  REQUIRE_PTR(st->key_scale, 4);
+  REQUIRE_PTR(st->S, 16);
+  REQUIRE_PTR(st->qsk, 16);
+  REQUIRE_PTR(st->scores, 4);
+  REQUIRE_PTR(st->idx, 4);
+  REQUIRE_PTR(st->out, 16);
+  if (st->qscale) REQUIRE(aligned(st->qscale, 4), "qscale must be 4-byte aligned");
+  if (st->n_sel) REQUIRE(aligned(st->n_sel, 4), "n_sel must be 4-byte aligned");
+  if (st->lse) REQUIRE(aligned(st->lse, 4), "lse must be 4-byte aligned");
+  if (s.pool > 1) {
+    REQUIRE_PTR(st->Kp, 16);
+    REQUIRE_PTR(st->Vp, 16);
+  } else {
+    REQUIRE(st->Kp == nullptr && st->Vp == nullptr, "Kp and Vp must be NULL when pool == 1");
+  }
+  REQUIRE(st->sm_scale > 0.f && st->sm_scale < 1e30f, "sm_scale must be positive and finite");
+  if (sks::ceil_div(s.NB, sks::TK_SUB) > sks::TK_MAX_SUBS)
+    return fail(SKS_ERR_UNSUPPORTED, "T_max / pool above %d is not supported by the selection",
+                sks::TK_MAX_SUBS * sks::TK_SUB);
+  TRY(check_ws(ws, ws_bytes_given, ws_bytes(s, st->Hq / kv->Hkv)));
+  const sks::TopkWs w = sks::topk_ws_carve(s, ws);
+  const hipStream_t hs = (hipStream_t)stream;
+  hipError_t e;
+  if (flags & SKS_STEP_APPEND)
+    e = sks::launch_step_prologue(st->q, st->Hq, *kv, s, st->basis, st->basis_per_head,
+                                  st->key_scale, st->qsk, st->qscale, st->S, st->Kp, st->Vp, hs);
+  else
+    e = sks::launch_sketch_query(st->q, s.B, s.R, st->Hq, s.Hkv, st->basis, st->basis_per_head,
+                                 st->qsk, st->qscale, hs);
+  if (e == hipSuccess) e = sks::launch_score(st->qsk, st->S, kv->seq_len, s, st->scores, &w, hs);
+  if (e == hipSuccess)
+    e = sks::launch_topk(st->scores, kv->seq_len, s, true, st->idx, st->n_sel, w, hs);
+  if (e == hipSuccess)
+    e = sks::launch_attn(st->q, st->Hq, *kv, s, st->idx, st->Kp, st->Vp, st->sm_scale, st->out,
+                         st->lse, w, hs);
+  return hip_status(e, "sks_decode_step");
 }
 
 }  // extern "C"

@@ -226,15 +226,15 @@ hipError_t launch_sketch_keys(const sks_kv &kv, const Shape &s, const float *bas
 hipError_t launch_sketch_query(const uint16_t *q, int B, int R, int Hq, int Hkv,
                                const float *basis, int basis_per_head, int8_t *qsk,
                                float *qscale, hipStream_t st);
-// Workspace layout: [hist region | scratch].  The hist region holds the
-// level-1 and level-2 selection histograms [nseg][2048] and [nseg][1024],
-// zero at rest (the calls that use them return them to zero), the
-// per-segment threshold bins and the per-sub-list score maxima written with
-// the level-1 histogram.
+// Workspace layout: [hist region | selection scratch | attention partials].
+// The hist region holds the level-1 and level-2 selection histograms
+// [nseg][2048] and [nseg][1024], zero at rest (the calls that use them return
+// them to zero), the per-segment threshold bins and the per-sub-list score
+// maxima written with the level-1 histogram.  The selection scratch holds the
+// candidate lists, the last region the attention partials.
 // (Kernels here never communicate between workgroups inside one launch: a
 // device-scope fence per workgroup costs far more on this GPU than a kernel
-// boundary.)  The scratch holds
-// the selection candidates or, later in the step, the attention partials.
+// boundary.)
 size_t hist_region_bytes(const Shape &s);
 size_t topk_scratch_bytes(const Shape &s);
 size_t attn_scratch_bytes(const Shape &s, int G);
@@ -250,16 +250,23 @@ struct TopkWs {
   int32_t *hist2;     // [nseg][HIST2_BINS], zero at rest
   int32_t *cmax;      // [nseg][nchunk]: largest biased score of each sub-list + 1 (0: empty)
   int32_t *counters;  // [nseg][4]: threshold bin b1, count above it, valid, count in b1
-  char *scratch;      // start of the scratch area
+  char *scratch;      // start of the selection scratch (cnt, cand)
+  char *attn;         // start of the attention partials (after the selection scratch)
   int32_t *cnt;       // [nseg][nchunk]
   int2 *cand;         // [nseg][nchunk * TK_SUB]
   int nchunk;         // sub-lists per segment
 };
 TopkWs topk_ws_carve(const Shape &s, void *ws);
+hipError_t launch_topk_filter(const int32_t *scores, const int32_t *seq_len, const Shape &s,
+                              bool hist_ready, const TopkWs &w, hipStream_t st);
 hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shape &s,
                        bool hist_ready, int32_t *idx, int32_t *n_sel, const TopkWs &w,
                        hipStream_t st);
 
+hipError_t launch_step_prologue(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
+                                const float *basis, int basis_per_head, const float *key_scale,
+                                int8_t *qsk, float *qscale, int8_t *S, uint16_t *Kp, uint16_t *Vp,
+                                hipStream_t st);
 hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
                        const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp,
                        float sm_scale, float *out, float *lse, const TopkWs &w, hipStream_t st);

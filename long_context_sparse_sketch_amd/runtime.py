@@ -11,6 +11,8 @@ the C-ABI calls of a step on the current stream:
     sks_topk_select               top-k indices, ascending, -1 padded
     sks_sparse_decode_attn        gather + one merged softmax over far + window
 
+or all of them as the one call sks_decode_step (the default of `step`).
+
 torch is used only to allocate device memory and streams; no step calls back
 into it.
 
@@ -123,7 +125,15 @@ class SparseDecodeLayer:
                                self.ws, self.lse, self.Kp, self.Vp, sm_scale, stream)
 
     # ---- one decode step
-    def step(self, q, stream=None, append=True):
+    def step(self, q, stream=None, append=True, fused=True):
+        """One step; `fused` issues it as the single sks_decode_step call,
+        otherwise as the individual calls (same results)."""
+        if fused:
+            sks.decode_step(self.cache, self.p, q, self.basis, self.key_scale, self.S, self.qsk,
+                            self.scores, self.idx, self.out, self.ws, qscale=self.qscale,
+                            n_sel=self.n_sel, lse=self.lse, Kp=self.Kp, Vp=self.Vp,
+                            basis_per_head=self.basis_per_head, append=append, stream=stream)
+            return self.out, self.lse
         if append:
             self.build_sketch(sks.APPEND, 0, stream)
         self.query_sketch(q, stream)
@@ -139,7 +149,7 @@ class StepRunner:
     into a HIP graph and replayed."""
 
     def __init__(self, layer: SparseDecodeLayer, parts: int = 1, streams: int = 1,
-                 overlap_append: bool = False):
+                 overlap_append: bool = False, fused: bool = True):
         parts = max(1, min(parts, layer.B))
         bounds = [layer.B * k // parts for k in range(parts + 1)]
         self.layer = layer
@@ -149,6 +159,7 @@ class StepRunner:
         self.streams = [torch.cuda.Stream(device=dev) for _ in range(max(1, streams))]
         self.append_stream = torch.cuda.Stream(device=dev) if overlap_append else None
         self.graph = None
+        self.fused = fused
 
     def step(self, q):
         main = torch.cuda.current_stream()
@@ -160,7 +171,7 @@ class StepRunner:
         side = self.append_stream if self.layer.window >= self.layer.R else None
         if side is None and len(self.streams) == 1 and len(self.views) == 1:
             # plain single-stream step on the caller's stream
-            self.views[0].step(q)
+            self.views[0].step(q, fused=self.fused)
             return self.layer.out, self.layer.lse
         if side is not None:
             side.wait_stream(main)
@@ -170,7 +181,7 @@ class StepRunner:
         for k, v in enumerate(self.views):
             st = self.streams[k % len(self.streams)]
             with torch.cuda.stream(st):
-                v.step(q[self.bounds[k]:self.bounds[k + 1]], append=side is None)
+                v.step(q[self.bounds[k]:self.bounds[k + 1]], append=side is None, fused=self.fused)
         for st in self.streams:
             main.wait_stream(st)
         if side is not None:

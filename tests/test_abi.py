@@ -150,3 +150,41 @@ def test_workspace_sizes_cover_selection_and_attention(L, cfg):
     assert nb >= nseg * nsplit * cfg.g * (128 + 2) * 4
     assert L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 0) == 0
     assert L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 9 * cfg.Hkv) == 0
+
+
+def step_desc(**kw):
+    d = dict(q=FAKE, Hq=8, basis=FAKE, basis_per_head=0, key_scale=FAKE, S=FAKE, Kp=None, Vp=None,
+             sm_scale=0.088, qsk=FAKE, qscale=None, scores=FAKE, idx=FAKE, n_sel=None, out=FAKE,
+             lse=None)
+    d.update(kw)
+    return sks.StepDesc(*[d[f] for f, _ in sks.StepDesc._fields_])
+
+
+def test_decode_step_argument_errors(L):
+    k, p = kv(), sks.params(64, 32)
+    call = lambda st, flags=1, ws=FAKE, nb=1 << 30: L.sks_decode_step(
+        ctypes.byref(k), ctypes.byref(p), st if st is None else ctypes.byref(st), flags, ws, nb,
+        None)
+    assert call(None) == sks.SKS_ERR_ARG and "step" in sks.last_error()
+    assert call(step_desc(), flags=2) == sks.SKS_ERR_ARG and "flags" in sks.last_error()
+    assert call(step_desc(Hq=6)) == sks.SKS_ERR_ARG and "multiple" in sks.last_error()
+    assert call(step_desc(scores=None)) == sks.SKS_ERR_ARG and "scores" in sks.last_error()
+    assert call(step_desc(out=FAKE + 4)) == sks.SKS_ERR_ARG and "aligned" in sks.last_error()
+    assert call(step_desc(Kp=FAKE, Vp=FAKE)) == sks.SKS_ERR_ARG
+    assert call(step_desc(sm_scale=0.0)) == sks.SKS_ERR_ARG and "sm_scale" in sks.last_error()
+    assert call(step_desc(), nb=64) == sks.SKS_ERR_WORKSPACE
+    p4 = sks.params(64, 32, pool=4)
+    assert L.sks_decode_step(ctypes.byref(k), ctypes.byref(p4), ctypes.byref(step_desc()), 1,
+                             FAKE, 1 << 30, None) == sks.SKS_ERR_ARG
+    assert "Kp" in sks.last_error()
+
+
+def test_workspace_holds_selection_and_attention_scratch_apart(L):
+    """The combined step runs the final selection and window attention in one
+    launch, so their scratch areas must not overlap: the workspace is the sum."""
+    k, p = kv(B=8, Hkv=4, T=250000), sks.params(4096, 2048)
+    small = L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 24)
+    n_sub = -(-250000 // 1024)
+    cand = 32 * n_sub * 1024 * 8
+    part = 32 * (-(-2048 // 384) + -(-4096 // 384)) * 6 * (8 + 512)
+    assert small >= cand + part

@@ -197,3 +197,24 @@ def test_determinism_bits(ctx):
     g.run_full()
     assert torch.equal(o1, g.layer.out) and torch.equal(l1, g.layer.lse)
     assert torch.equal(i1, g.layer.idx)
+
+
+def test_fused_step_equals_individual_calls(ctx):
+    """sks_decode_step (one call, grouped launches) gives the results of the
+    individual calls bit for bit, every output buffer included."""
+    cfg, case, g, ref, arr = ctx
+    lay = g.layer
+    names = ["S", "qsk", "qscale", "scores", "idx", "n_sel", "out", "lse"]
+    if cfg.pool > 1:
+        names += ["Kp", "Vp"]
+    got = {}
+    for fused in (False, True):
+        for n in ("qsk", "qscale", "scores", "idx", "n_sel", "out", "lse"):
+            t = getattr(lay, n)
+            t.view(torch.uint8).fill_(0x5A)                       # same poison for both runs
+        lay.build_sketch(0, g.T)
+        lay.step(g.q, fused=fused)
+        torch.cuda.synchronize()
+        got[fused] = {n: getattr(lay, n).clone() for n in names}
+    for n in names:
+        assert torch.equal(got[False][n].view(torch.uint8), got[True][n].view(torch.uint8)), n
