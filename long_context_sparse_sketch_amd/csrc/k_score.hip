@@ -47,6 +47,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   static_assert(SCORE_CHUNK == TK_SUB, "one chunk maximum per top-k sub-list");
   __shared__ int lh[HIST ? R * HIST1_BINS : 1];
   __shared__ int lmax[HIST ? R * (SC_THREADS / 64) : 1];
+  __shared__ __align__(16) int lsc[R * SCORE_CHUNK];     // this chunk's scores, written at the end
   const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
   const int L0 = clamp_len(seq_len[b], T_max, R);
   const int Lmax = L0 + R - 1;
@@ -113,8 +114,8 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
       }
       const int t_lo = base + part * 16 + quad;
       const int t_hi = t_lo + 64;
-      if (t_lo < c1) __builtin_nontemporal_store(lo, &out[i][t_lo]);
-      if (t_hi < c1) __builtin_nontemporal_store(hi, &out[i][t_hi]);
+      lsc[i * SCORE_CHUNK + (t_lo - c0)] = lo;
+      lsc[i * SCORE_CHUNK + (t_hi - c0)] = hi;
       if (HIST && need_hist[i]) {
         const int klo = biased_key(lo), khi = biased_key(hi);
         if (t_lo < nf[i]) {
@@ -134,7 +135,29 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
       const int wm = __builtin_amdgcn_readlane(wave_incl_max(kmax[i]), 63);
       if (lane == 0) lmax[i * (SC_THREADS / 64) + wave] = wm;
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  // The chunk's scores leave in one burst per row: 16-byte stores when the
+  // row is 16-byte aligned here, else 4-byte stores.
+  const int n_chunk = c1 - c0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    int32_t *dst = out[i] + c0;
+    if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      for (int v = threadIdx.x; 4 * v < n_chunk; v += SC_THREADS) {
+        const v4i_t w = *reinterpret_cast<const v4i_t *>(&lsc[i * SCORE_CHUNK + 4 * v]);
+        if (4 * v + 4 <= n_chunk) {
+          __builtin_nontemporal_store(w, reinterpret_cast<v4i_t *>(dst) + v);
+        } else {
+          for (int k = 0; 4 * v + k < n_chunk; ++k) dst[4 * v + k] = w[k];
+        }
+      }
+    } else {
+      for (int t = threadIdx.x; t < n_chunk; t += SC_THREADS)
+        __builtin_nontemporal_store(lsc[i * SCORE_CHUNK + t], dst + t);
+    }
+  }
+  if (HIST) {
     if (threadIdx.x < R) {
       const int i = threadIdx.x;
       int m = 0;
