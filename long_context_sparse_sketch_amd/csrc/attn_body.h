@@ -239,16 +239,33 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
     }
   };
 
-  // Q as the A operand: head n, dims 32i + 8g .. +8 (zero rows past G)
+  // Q as the A operand: head n, the 8 dims of MFMA step c that lane group g
+  // holds (zero rows past G).  The dot product does not depend on how the
+  // 128 dims are spread over the steps, as long as Q and K use the same
+  // spread: bf16 takes dims 32c + 8g .. +8; int8 takes 16 consecutive dims
+  // per pair of steps, (c / 2) * 64 + 16g + (c % 2) * 8 .. +8, so that a lane
+  // reads 16 bytes of an int8 row at once.
+  auto qdim = [&](int c) {
+    return DT == SKS_KV_I8 ? (c >> 1) * 64 + 16 * g + (c & 1) * 8 : 32 * c + 8 * g;
+  };
   u32x4_t qa[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     qa[c] = u32x4_t{0, 0, 0, 0};
     if (n < G) {
       const uint4 w = *reinterpret_cast<const uint4 *>(
-          q + ((size_t)bi * Hq + (size_t)h * G + n) * D + 32 * c + 8 * g);
+          q + ((size_t)bi * Hq + (size_t)h * G + n) * D + qdim(c));
       qa[c] = u32x4_t{w.x, w.y, w.z, w.w};
     }
+  }
+  // int8 caches: each lane's entries' row scales, with the descriptors
+  float ksd0 = 1.f, vsd0 = 1.f, ksd1 = 1.f, vsd1 = 1.f;
+  if constexpr (DT == SKS_KV_I8) {
+    const size_t sbase = ((size_t)b * Hkv + h) * T_max;
+    ksd0 = f16_bits_to_float(Ks[sbase + row0]);
+    vsd0 = f16_bits_to_float(Vs[sbase + row0]);
+    ksd1 = f16_bits_to_float(Ks[sbase + row1]);
+    vsd1 = f16_bits_to_float(Vs[sbase + row1]);
   }
 
   f32x4_t o[8];
@@ -266,61 +283,69 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   const char *Vt = static_cast<const char *>(V) + ((size_t)b * Hkv + h) * T_max * D * EB;
   const char *Kpb = reinterpret_cast<const char *>(Kp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
   const char *Vpb = reinterpret_cast<const char *>(Vp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
-  const uint16_t *Kst = DT == SKS_KV_I8 ? Ks + ((size_t)b * Hkv + h) * T_max : nullptr;
-  const uint16_t *Vst = DT == SKS_KV_I8 ? Vs + ((size_t)b * Hkv + h) * T_max : nullptr;
   uint16_t *sv = s_v[wave];
 
   // Raw gathered data of one tile, as loaded (converted to bf16 only when the
   // tile is consumed, so that the next tile's loads stay in flight meanwhile).
-  using KRaw = typename std::conditional<DT == SKS_KV_BF16, uint4, uint2>::type;
+  // bf16: K sub-tile t, lane (n, g): entry 16t + n, 16 bytes per MFMA step;
+  //       V: 16 bytes (8 dims) of chunk (x & 15) of tile row (x >> 4),
+  //       x = 64 qq + lane.
+  // int8: K: 16 bytes for steps 0-1 and 16 bytes for steps 2-3 (see qdim);
+  //       V: 16 bytes (16 dims) of chunk (x & 7) of tile row (x >> 3).
+  constexpr bool I8 = DT == SKS_KV_I8;
+  constexpr int KLD = I8 ? 2 : 4;                    // K loads per sub-tile
+  constexpr int VLD = I8 ? 4 : 8;                    // V loads per tile
   struct Tile {
-    KRaw k[2][4];          // K: sub-tile t, lane (n, g): entry 16t + n, dims 32c + 8g .. +8
-    KRaw v[8];             // V: chunk (x & 15) of tile row (x >> 4), x = 64 qq + lane
+    uint4 k[2][KLD];
+    uint4 v[VLD];
     int f[2];              // flags of the two K entries of this lane
-    uint16_t ks[2], vs[2]; // int8 row scales of the two K entries (fp16 bits)
+    float ks[2], vs[2];    // int8 row scales of the two K entries
   };
   // K/V rows are read once per step: nontemporal loads keep them from
   // evicting lines that are reused.
-  auto ld = [](const char *p) -> KRaw {
-    if constexpr (DT == SKS_KV_BF16) {
-      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-      return make_uint4(v[0], v[1], v[2], v[3]);
-    } else {
-      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-      const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
-      return make_uint2(v[0], v[1]);
-    }
+  auto ld = [](const char *p) -> uint4 {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
   };
   auto gather = [&](int tile, Tile &d) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      const int j = tile * AM_TILE + 16 * t + n;
       int r, f;
-      desc(tile * AM_TILE + 16 * t + n, r, f);
+      desc(j, r, f);
       d.f[t] = f;
       const char *kbase = (POOLED && (f & 2)) ? Kpb : Kt;
       const size_t off = (size_t)r * D * EB;
+      if constexpr (I8) {
+        d.k[t][0] = ld(kbase + off + 16 * g);
+        d.k[t][1] = ld(kbase + off + 64 + 16 * g);
+        d.ks[t] = j < 64 ? __shfl(ksd0, j) : __shfl(ksd1, j - 64);
+        d.vs[t] = j < 64 ? __shfl(vsd0, j) : __shfl(vsd1, j - 64);
+      } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) d.k[t][c] = ld(kbase + off + (32 * c + 8 * g) * EB);
-      if constexpr (DT == SKS_KV_I8) {
-        d.ks[t] = Kst[r];
-        d.vs[t] = Vst[r];
+        for (int c = 0; c < 4; ++c) d.k[t][c] = ld(kbase + off + (32 * c + 8 * g) * 2);
       }
     }
 #pragma unroll
-    for (int qq = 0; qq < 8; ++qq) {
-      const int x = qq * 64 + lane, ev = x >> 4, c = x & 15;
+    for (int qq = 0; qq < VLD; ++qq) {
+      const int x = qq * 64 + lane;
+      const int ev = I8 ? x >> 3 : x >> 4, c = I8 ? x & 7 : x & 15;
       int r, f;
       desc(tile * AM_TILE + ev, r, f);
       const char *vbase = (POOLED && (f & 2)) ? Vpb : Vt;
-      d.v[qq] = ld(vbase + (size_t)r * D * EB + c * 8 * EB);
+      d.v[qq] = ld(vbase + (size_t)r * D * EB + c * 16);
     }
   };
-  auto to_bf16 = [&](const KRaw &w) -> u32x4_t {
-    if constexpr (DT == SKS_KV_BF16) {
-      return u32x4_t{w.x, w.y, w.z, w.w};
+  // K operand of MFMA step c as 8 bf16 (int8 codes convert exactly)
+  auto kop = [&](const Tile &d, int t, int c) -> u32x4_t {
+    if constexpr (I8) {
+      const uint4 &w = d.k[t][c >> 1];
+      const uint32_t a = (c & 1) ? w.z : w.x, bb = (c & 1) ? w.w : w.y;
+      return u32x4_t{i8pair_to_bf16x2(a, 0), i8pair_to_bf16x2(a, 16), i8pair_to_bf16x2(bb, 0),
+                     i8pair_to_bf16x2(bb, 16)};
     } else {
-      return u32x4_t{i8pair_to_bf16x2(w.x, 0), i8pair_to_bf16x2(w.x, 16),
-                     i8pair_to_bf16x2(w.y, 0), i8pair_to_bf16x2(w.y, 16)};
+      const uint4 &w = d.k[t][c];
+      return u32x4_t{w.x, w.y, w.z, w.w};
     }
   };
 
@@ -331,29 +356,35 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
     for (int t = 0; t < 2; ++t) {
       sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sacc[t] = mfma_bf16(qa[c], to_bf16(d.k[t][c]), sacc[t]);
+      for (int c = 0; c < 4; ++c) sacc[t] = mfma_bf16(qa[c], kop(d, t, c), sacc[t]);
     }
 
     // stage V (row-major, 8-byte stores: the padded stride is 8-byte aligned)
 #pragma unroll
-    for (int qq = 0; qq < 8; ++qq) {
-      const int x = qq * 64 + lane, ev = x >> 4, c = x & 15;
-      const u32x4_t w = to_bf16(d.v[qq]);
-      uint2 *dst = reinterpret_cast<uint2 *>(sv + ev * VROW + c * 8);
-      dst[0] = make_uint2(w[0], w[1]);
-      dst[1] = make_uint2(w[2], w[3]);
+    for (int qq = 0; qq < VLD; ++qq) {
+      const int x = qq * 64 + lane;
+      const uint4 &w = d.v[qq];
+      if constexpr (I8) {
+        const int ev = x >> 3, c = x & 7;
+        uint2 *dst = reinterpret_cast<uint2 *>(sv + ev * VROW + c * 16);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          dst[k] = make_uint2(i8pair_to_bf16x2(ws[k], 0), i8pair_to_bf16x2(ws[k], 16));
+      } else {
+        const int ev = x >> 4, c = x & 15;
+        uint2 *dst = reinterpret_cast<uint2 *>(sv + ev * VROW + c * 8);
+        dst[0] = make_uint2(w.x, w.y);
+        dst[1] = make_uint2(w.z, w.w);
+      }
     }
 
     // ---- online softmax on the C layout (lane: heads 4g + j, entry n of each sub-tile)
     float ksc[2], vsc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      if constexpr (DT == SKS_KV_I8) {
-        ksc[t] = f16_bits_to_float(d.ks[t]);
-        vsc[t] = f16_bits_to_float(d.vs[t]);
-      } else {
-        ksc[t] = vsc[t] = 1.f;
-      }
+      ksc[t] = I8 ? d.ks[t] : 1.f;
+      vsc[t] = I8 ? d.vs[t] : 1.f;
     }
     float z[2][4];
 #pragma unroll

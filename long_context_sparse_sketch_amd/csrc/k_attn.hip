@@ -27,7 +27,7 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float2 *__restrict_
 }
 
 template <int G, int DT, bool POOLED>
-__global__ __launch_bounds__(AT_THREADS) void attn_kernel(AttnArgs a, int slot0) {
+__global__ __launch_bounds__(AT_THREADS, 2) void attn_kernel(AttnArgs a, int slot0) {
   __shared__ AttnLds lds;
   attn_body<G, DT, POOLED>(a, blockIdx.y, slot0 + blockIdx.x, lds);
 }
