@@ -235,6 +235,20 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
 
+    # spread: each multi-step graph replay timed on its own (per-step time =
+    # replay time / steps per graph)
+    spread = None
+    if not args.no_graph:
+        per = []
+        for k in range(max(8, args.steps // spg)):
+            a, b = ev(), ev()
+            a.record(stream)
+            multi[k % len(multi)].replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) / spg)
+        spread = {f"p{p}": float(np.percentile(per, p)) for p in (10, 50, 90)}
+
     # dominant kernel: K back-to-back launches (rotating replicas) between two
     # events on the launch stream -> average launch duration
     e0, e1 = ev(), ev()
@@ -254,6 +268,24 @@ def main():
     e3.record(stream)
     torch.cuda.synchronize()
     attn_avg_ms = e2.elapsed_time(e3) / args.steps
+
+    # standalone gather/pack of the same rows into packed buffers
+    Cn = cfg.topk + cfg.window + cfg.pool - 1
+    kdt = torch.int8 if i8 else torch.bfloat16
+    Ko = torch.empty((cfg.B, cfg.R, cfg.Hkv, Cn, 128), dtype=kdt, device=dev)
+    Vo = torch.empty_like(Ko)
+    Kso = torch.empty((cfg.B, cfg.R, cfg.Hkv, Cn), dtype=torch.int16, device=dev) if i8 else None
+    Vso = torch.empty_like(Kso) if i8 else None
+    n_out = torch.empty((cfg.B, cfg.R, cfg.Hkv), dtype=torch.int32, device=dev)
+    e4, e5 = ev(), ev()
+    e4.record(stream)
+    for k in range(args.steps):
+        lay = layers[k % len(layers)]
+        sks.gather_pack(lay.cache, lay.p, lay.idx, Ko, Vo, n_out, lay.Kp, lay.Vp, Kso, Vso)
+    e5.record(stream)
+    torch.cuda.synchronize()
+    gather_avg_ms = e4.elapsed_time(e5) / args.steps
+    del Ko, Vo, Kso, Vso
 
     # per-phase breakdown (events between the calls of each step; includes
     # the events' own small overhead)
@@ -310,6 +342,9 @@ def main():
             "gathered_kv_bytes": gather_b,
             "attn_avg_ms": attn_avg_ms,
             "attn_GBps": gather_b / (attn_avg_ms * 1e-3) / 1e9,
+            "gather_pack_avg_ms": gather_avg_ms,
+            "gather_pack_GBps": 2 * gather_b / (gather_avg_ms * 1e-3) / 1e9,
+            "step_ms_spread": spread,
             "score_plus_attn_GBps": (sketch_b + gather_b) / ((score_avg_ms + attn_avg_ms) * 1e-3) / 1e9,
             "step_GBps": (sketch_b + gather_b + small_b) / (ms_per_step * 1e-3) / 1e9,
             "phase_ms_median": phase_ms,

@@ -6,72 +6,19 @@
 // (one file)" of the same list.  Pooled mode: the 4:1 mean-pooled far field
 // of "What it adds" on the "Agens SGLang" README.
 //
-// Layout: one lane per token (or pooled block).  The lane holds its key in
-// 128 fp32 registers and walks the 64 basis rows; basis addresses are uniform
-// across the wave, so they come through scalar loads.  The 64 int8 codes of
-// a lane are staged in LDS and leave as one contiguous, coalesced block.
+// Bulk builds run on the matrix cores (sketch_mfma_kernel, below); the few
+// rows of a step's append take one wave per row (sketch_rows_small_kernel).
 #include "sks_internal.h"
 
 namespace sks {
 namespace {
 
-constexpr int KS_THREADS = 256;
 constexpr int SMALL_ROWS = 64;   // up to this many rows per (b, h): wave-per-row kernel
 
-// Project x (128 fp32 in registers) on the 64 basis rows and quantize.
-// Codes are written into the LDS row `dst` (64 bytes, 16 dwords).
-__device__ __forceinline__ void project_quantize(const float (&x)[D], const float *__restrict__ P,
-                                                 float scale, uint32_t *dst) {
-#pragma unroll 1
-  for (int c4 = 0; c4 < RANK / 4; ++c4) {
-    uint32_t packed = 0;
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const float *row = P + (c4 * 4 + cc) * D;
-      float acc = 0.0f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) acc = __builtin_fmaf(row[d], x[d], acc);
-      packed |= (uint32_t)(uint8_t)quant_code(acc, scale) << (8 * cc);
-    }
-    dst[c4] = packed;
-  }
-}
-
-// Load the key row of token t into fp32 registers (bf16 or int8 * fp16 scale).
-template <int DT>
-__device__ __forceinline__ void load_key(const void *K, const uint16_t *Ks, size_t row,
-                                         float (&x)[D]) {
-  if (DT == SKS_KV_BF16) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(K) + row * D);
-#pragma unroll
-    for (int v = 0; v < D / 8; ++v) {
-      uint4 w = src[v];
-      x[v * 8 + 0] = bf16_lo(w.x); x[v * 8 + 1] = bf16_hi(w.x);
-      x[v * 8 + 2] = bf16_lo(w.y); x[v * 8 + 3] = bf16_hi(w.y);
-      x[v * 8 + 4] = bf16_lo(w.z); x[v * 8 + 5] = bf16_hi(w.z);
-      x[v * 8 + 6] = bf16_lo(w.w); x[v * 8 + 7] = bf16_hi(w.w);
-    }
-  } else {
-    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const int8_t *>(K) + row * D);
-    float sc = f16_bits_to_float(Ks[row]);
-#pragma unroll
-    for (int v = 0; v < D / 16; ++v) {
-      uint4 w = src[v];
-      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb)
-          x[v * 16 + k * 4 + bb] = (float)(int8_t)(ws[k] >> (8 * bb)) * sc;   // exact
-    }
-  }
-}
-
-// Copy the staged code rows [0, n) of this workgroup to S rows [j0, j0 + n).
-__device__ __forceinline__ void flush_codes(const uint32_t *lds, int n, int8_t *S, size_t row0) {
-  uint4 *dst = reinterpret_cast<uint4 *>(S + row0 * RANK);
-  const uint4 *src = reinterpret_cast<const uint4 *>(lds);
-  for (int v = threadIdx.x; v < n * (RANK / 16); v += blockDim.x) dst[v] = src[v];
+// int8 code pair (bits sh .. sh+15 of w) -> two bf16 (exact: |code| <= 127)
+__device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int sh) {
+  const float a = (float)(int8_t)(w >> sh), b = (float)(int8_t)(w >> (sh + 8));
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
 // First sketch row of the range handled by this (b, h): host range or append.
@@ -92,85 +39,179 @@ __device__ __forceinline__ void sketch_range(int append, const int32_t *seq_len,
   if (j_hi > NB) j_hi = NB;
 }
 
-template <int DT>
-__global__ __launch_bounds__(KS_THREADS) void sketch_keys_kernel(
-    const void *__restrict__ K, const uint16_t *__restrict__ Ks, const int32_t *__restrict__ seq_len,
-    const float *__restrict__ basis, int basis_per_head, const float *__restrict__ key_scale,
-    int Hkv, int T_max, int R, int NB, int append, int t_begin, int t_end,
-    int8_t *__restrict__ S) {
-  __shared__ uint32_t codes[KS_THREADS * (RANK / 4)];
-  const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
-  int j_lo, j_hi;
-  sketch_range(append, seq_len, b, T_max, R, 1, NB, t_begin, t_end, j_lo, j_hi);
-  const int j0 = j_lo + blockIdx.x * KS_THREADS;
-  if (j0 >= j_hi) return;
-  const int n = min(KS_THREADS, j_hi - j0);
-  const int t = j0 + threadIdx.x;
-  const float *P = basis + (basis_per_head ? (size_t)h * RANK * D : 0);
-  const float scale = key_scale[h];
-  if (threadIdx.x < n) {
-    float x[D];
-    load_key<DT>(K, Ks, (size_t)bh * T_max + t, x);
-    project_quantize(x, P, scale, &codes[threadIdx.x * (RANK / 4)]);
-  }
-  __syncthreads();
-  flush_codes(codes, n, S, (size_t)bh * NB + j0);
+// ---------------------------------------------------------------------------
+// Bulk sketch on the matrix cores.  Per (b, h), Y[rows][64] = X[rows][128] P^T:
+// v_mfma_f32_16x16x32_bf16 with A = 16 rows x 32 dims of X (lane (n, g): row
+// n, dims 32c + 8g .. +8) and B = 32 dims x 16 basis rows (lane: basis row n,
+// the same dims).  X is exact in bf16 (bf16 rows; int8 codes, whose fp16 row
+// scale multiplies Y afterwards).  The fp32 basis is split exactly into three
+// bf16 parts, P = hi + mid + lo (8 + 8 + 8 significant bits), so every
+// product is exact and only the fp32 accumulation rounds -- the same
+// accuracy as an fp32 dot product.  The split basis sits in LDS in operand
+// order; codes are staged per wave and leave as 16-byte stores.
+constexpr int SM_THREADS = 256;
+constexpr int SM_TILE = 64;                              // rows per wave and iteration
+constexpr int SM_ITERS = 4;
+constexpr int SM_ROWS = SM_TILE * (SM_THREADS / 64) * SM_ITERS;   // 1024 rows per workgroup
+
+typedef __bf16 sk_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float sk_f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t sk_u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ sk_f32x4_t sk_mfma(sk_u32x4_t a, sk_u32x4_t b, sk_f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sk_bf16x8_t, a),
+                                                 __builtin_bit_cast(sk_bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Pooled blocks (bf16 caches): mean of `pool` consecutive K and V rows in
-// fp64 (exact for bf16 inputs), rounded once to bf16; the sketch is taken of
-// the stored bf16 pooled key.
-__global__ __launch_bounds__(KS_THREADS) void sketch_pool_kernel(
-    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t sk_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// component `part` (0 hi, 1 mid, 2 lo) of the exact three-way bf16 split
+__device__ __forceinline__ uint32_t sk_split(float p, int part) {
+  const uint32_t hi = sk_bf16(p);
+  if (part == 0) return hi;
+  const float r1 = p - __uint_as_float(hi << 16);           // exact
+  const uint32_t mid = sk_bf16(r1);
+  if (part == 1) return mid;
+  return sk_bf16(r1 - __uint_as_float(mid << 16));          // exact remainder, <= 8 bits
+}
+
+template <int DT>
+__global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
+    const void *__restrict__ X, const uint16_t *__restrict__ Xs, long x_rows_per_bh,
     const int32_t *__restrict__ seq_len, const float *__restrict__ basis, int basis_per_head,
-    const float *__restrict__ key_scale, int Hkv, int T_max, int R, int NB, int pool, int append,
-    int t_begin, int t_end, int8_t *__restrict__ S, uint16_t *__restrict__ Kp,
-    uint16_t *__restrict__ Vp) {
-  __shared__ uint32_t codes[KS_THREADS * (RANK / 4)];
+    const float *__restrict__ key_scale, int Hkv, int T_max, int R, int NB, int pool,
+    int append, int t_begin, int t_end, int8_t *__restrict__ S) {
+  __shared__ sk_u32x4_t bop[3][4][4][64];                   // [part][basis block][step][lane]
+  __shared__ __align__(16) uint8_t stage[SM_THREADS / 64][SM_TILE * RANK];
   const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
   int j_lo, j_hi;
   sketch_range(append, seq_len, b, T_max, R, pool, NB, t_begin, t_end, j_lo, j_hi);
-  const int j0 = j_lo + blockIdx.x * KS_THREADS;
+  const int j0 = j_lo + blockIdx.x * SM_ROWS;
   if (j0 >= j_hi) return;
-  const int n = min(KS_THREADS, j_hi - j0);
-  const int j = j0 + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+
+  // the split basis, in B-operand order
   const float *P = basis + (basis_per_head ? (size_t)h * RANK * D : 0);
-  const float scale = key_scale[h];
-  if (threadIdx.x < n) {
-    const size_t tok0 = (size_t)bh * T_max + (size_t)j * pool;
-    const size_t out_row = (size_t)bh * NB + j;
-    const double dpool = (double)pool;
-    float x[D];
+  for (int e = threadIdx.x; e < 3 * 4 * 4 * 64; e += SM_THREADS) {
+    const int part = e >> 10, nb = (e >> 8) & 3, c = (e >> 6) & 3, l = e & 63;
+    const float *src = P + (size_t)(16 * nb + (l & 15)) * D + 32 * c + 8 * (l >> 4);
+    sk_u32x4_t w;
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      const uint16_t *src = which == 0 ? K : V;
-      uint16_t *dst = which == 0 ? Kp : Vp;
-#pragma unroll
-      for (int v = 0; v < D / 8; ++v) {
-        double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int k = 0; k < pool; ++k) {
-          uint4 w = *reinterpret_cast<const uint4 *>(src + (tok0 + k) * D + v * 8);
-          s[0] += bf16_lo(w.x); s[1] += bf16_hi(w.x); s[2] += bf16_lo(w.y); s[3] += bf16_hi(w.y);
-          s[4] += bf16_lo(w.z); s[5] += bf16_hi(w.z); s[6] += bf16_lo(w.w); s[7] += bf16_hi(w.w);
-        }
-        uint16_t o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          o[e] = f64_to_bf16_rne(s[e] / dpool);   // exact sum, one rounding, then bf16
-          if (which == 0) x[v * 8 + e] = __uint_as_float((uint32_t)o[e] << 16);
-        }
-        uint4 packed;
-        packed.x = o[0] | ((uint32_t)o[1] << 16);
-        packed.y = o[2] | ((uint32_t)o[3] << 16);
-        packed.z = o[4] | ((uint32_t)o[5] << 16);
-        packed.w = o[6] | ((uint32_t)o[7] << 16);
-        *reinterpret_cast<uint4 *>(dst + out_row * D + v * 8) = packed;
-      }
-    }
-    project_quantize(x, P, scale, &codes[threadIdx.x * (RANK / 4)]);
+    for (int k = 0; k < 4; ++k)
+      w[k] = sk_split(src[2 * k], part) | (sk_split(src[2 * k + 1], part) << 16);
+    bop[part][nb][c][l] = w;
   }
   __syncthreads();
-  flush_codes(codes, n, S, (size_t)bh * NB + j0);
+
+  const float kscale = key_scale[h];
+  constexpr int EB = DT == SKS_KV_BF16 ? 2 : 1;
+  const char *Xbh = static_cast<const char *>(X) + (size_t)bh * x_rows_per_bh * D * EB;
+  const uint16_t *Xsbh = DT == SKS_KV_I8 ? Xs + (size_t)bh * x_rows_per_bh : nullptr;
+  uint8_t *st = stage[wave];
+
+  for (int it = 0; it < SM_ITERS; ++it) {
+    const int row0 = j0 + it * (SM_TILE * SM_THREADS / 64) + wave * SM_TILE;
+    if (row0 >= j_hi) break;                                // uniform per wave
+    // A operands: rows row0 + 16m + n (clamped into the range), 8 dims per step
+    sk_u32x4_t a[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const size_t r = (size_t)min(row0 + 16 * m + n, j_hi - 1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (DT == SKS_KV_BF16) {
+          const uint4 w = *reinterpret_cast<const uint4 *>(Xbh + (r * D + 32 * c + 8 * g) * 2);
+          a[m][c] = sk_u32x4_t{w.x, w.y, w.z, w.w};
+        } else {
+          const uint2 w = *reinterpret_cast<const uint2 *>(Xbh + r * D + 32 * c + 8 * g);
+          a[m][c] = sk_u32x4_t{i8pair_bf16(w.x, 0), i8pair_bf16(w.x, 16), i8pair_bf16(w.y, 0),
+                               i8pair_bf16(w.y, 16)};
+        }
+      }
+    }
+    float xs = 1.f;                                          // int8: scale of row row0 + lane
+    if constexpr (DT == SKS_KV_I8) xs = f16_bits_to_float(Xsbh[min(row0 + lane, j_hi - 1)]);
+
+    sk_f32x4_t acc[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[m][nb] = sk_f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int part = 0; part < 3; ++part) {
+          const sk_u32x4_t bv = bop[part][nb][c][lane];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[m][nb] = sk_mfma(a[m][c], bv, acc[m][nb]);
+        }
+
+    // codes: lane holds Y[row 16m + 4g + j][basis 16nb + n]
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 16 * m + 4 * g + j;
+        const float sc = DT == SKS_KV_I8 ? __shfl(xs, rr) : 1.f;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          st[rr * RANK + 16 * nb + n] = (uint8_t)quant_code(acc[m][nb][j] * sc, kscale);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 64 rows x 64 B, contiguous in S: 16-byte pieces, rows past the range skipped
+    uint4 *dst = reinterpret_cast<uint4 *>(S + ((size_t)bh * NB + row0) * RANK);
+#pragma unroll
+    for (int k = 0; k < SM_TILE * RANK / 16 / 64; ++k) {
+      const int piece = k * 64 + lane;
+      if (row0 + piece / (RANK / 16) < j_hi) dst[piece] = reinterpret_cast<const uint4 *>(st)[piece];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// Pooled blocks (bf16 caches): mean of `pool` consecutive K and V rows in
+// fp64 (exact sums of bf16 values), rounded once to bf16 and stored in Kp/Vp;
+// the sketch of the stored pooled keys follows in sketch_mfma_kernel.
+// Thread: one 16-byte piece (8 dims) of one block's K or V row; the 16
+// threads of a row are adjacent, so every load and store is coalesced.
+constexpr int PM_THREADS = 256;
+constexpr int PM_BLOCKS = PM_THREADS / 32;                  // blocks per workgroup (K and V)
+
+__global__ __launch_bounds__(PM_THREADS) void pool_mean_kernel(
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const int32_t *__restrict__ seq_len, int Hkv, int T_max, int R, int NB, int pool, int append,
+    int t_begin, int t_end, uint16_t *__restrict__ Kp, uint16_t *__restrict__ Vp) {
+  const int bh = blockIdx.y, b = bh / Hkv;
+  int j_lo, j_hi;
+  sketch_range(append, seq_len, b, T_max, R, pool, NB, t_begin, t_end, j_lo, j_hi);
+  const int j = j_lo + blockIdx.x * PM_BLOCKS + (threadIdx.x >> 5);
+  if (j >= j_hi) return;
+  const int which = (threadIdx.x >> 4) & 1, piece = threadIdx.x & 15;
+  const uint16_t *src = (which == 0 ? K : V) + ((size_t)bh * T_max + (size_t)j * pool) * D + piece * 8;
+  double sm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int k = 0; k < pool; ++k) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(src + (size_t)k * D);
+    sm[0] += bf16_lo(w.x); sm[1] += bf16_hi(w.x); sm[2] += bf16_lo(w.y); sm[3] += bf16_hi(w.y);
+    sm[4] += bf16_lo(w.z); sm[5] += bf16_hi(w.z); sm[6] += bf16_lo(w.w); sm[7] += bf16_hi(w.w);
+  }
+  const double dpool = (double)pool;
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = f64_to_bf16_rne(sm[2 * e] / dpool) | ((uint32_t)f64_to_bf16_rne(sm[2 * e + 1] / dpool) << 16);
+  *reinterpret_cast<uint4 *>((which == 0 ? Kp : Vp) + ((size_t)bh * NB + j) * D + piece * 8) =
+      make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // Few rows per (b, h) -- the per-step append of the rows' own tokens: one
@@ -330,21 +371,25 @@ hipError_t launch_sketch_keys(const sks_kv &kv, const Shape &s, const float *bas
           s.R, s.NB, s.pool, append, t_begin, t_end, S, Kp, Vp);
     return hipGetLastError();
   }
-  dim3 grid(ceil_div(nrows, KS_THREADS), s.B * s.Hkv);
+  dim3 grid(ceil_div(nrows, SM_ROWS), s.B * s.Hkv);
   if (s.pool == 1) {
     if (s.dtype == SKS_KV_BF16)
-      sketch_keys_kernel<SKS_KV_BF16><<<grid, KS_THREADS, 0, st>>>(
-          kv.K, nullptr, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max, s.R,
-          s.NB, append, t_begin, t_end, S);
+      sketch_mfma_kernel<SKS_KV_BF16><<<grid, SM_THREADS, 0, st>>>(
+          kv.K, nullptr, s.T_max, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max,
+          s.R, s.NB, 1, append, t_begin, t_end, S);
     else
-      sketch_keys_kernel<SKS_KV_I8><<<grid, KS_THREADS, 0, st>>>(
-          kv.K, kv.K_scale, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max, s.R,
-          s.NB, append, t_begin, t_end, S);
+      sketch_mfma_kernel<SKS_KV_I8><<<grid, SM_THREADS, 0, st>>>(
+          kv.K, kv.K_scale, s.T_max, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv,
+          s.T_max, s.R, s.NB, 1, append, t_begin, t_end, S);
   } else {
-    sketch_pool_kernel<<<grid, KS_THREADS, 0, st>>>(
+    dim3 gp(ceil_div(nrows, PM_BLOCKS), s.B * s.Hkv);
+    pool_mean_kernel<<<gp, PM_THREADS, 0, st>>>(
         static_cast<const uint16_t *>(kv.K), static_cast<const uint16_t *>(kv.V), kv.seq_len,
-        basis, basis_per_head, key_scale, s.Hkv, s.T_max, s.R, s.NB, s.pool, append, t_begin,
-        t_end, S, Kp, Vp);
+        s.Hkv, s.T_max, s.R, s.NB, s.pool, append, t_begin, t_end, Kp, Vp);
+    // then the sketch of the stored pooled keys (rows of Kp, NB per (b, h))
+    sketch_mfma_kernel<SKS_KV_BF16><<<grid, SM_THREADS, 0, st>>>(
+        Kp, nullptr, s.NB, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max, s.R,
+        s.NB, s.pool, append, t_begin, t_end, S);
   }
   return hipGetLastError();
 }
