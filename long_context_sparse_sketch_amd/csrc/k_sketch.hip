@@ -51,8 +51,8 @@ __device__ __forceinline__ void sketch_range(int append, const int32_t *seq_len,
 // order; codes are staged per wave and leave as 16-byte stores.
 constexpr int SM_THREADS = 256;
 constexpr int SM_TILE = 64;                              // rows per wave and iteration
-constexpr int SM_ITERS = 4;
-constexpr int SM_ROWS = SM_TILE * (SM_THREADS / 64) * SM_ITERS;   // 1024 rows per workgroup
+constexpr int SM_ITERS = 16;
+constexpr int SM_ROWS = SM_TILE * (SM_THREADS / 64) * SM_ITERS;   // 4096 rows per workgroup
 
 typedef __bf16 sk_bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float sk_f32x4_t __attribute__((ext_vector_type(4)));
@@ -114,11 +114,9 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
   const uint16_t *Xsbh = DT == SKS_KV_I8 ? Xs + (size_t)bh * x_rows_per_bh : nullptr;
   uint8_t *st = stage[wave];
 
-  for (int it = 0; it < SM_ITERS; ++it) {
-    const int row0 = j0 + it * (SM_TILE * SM_THREADS / 64) + wave * SM_TILE;
-    if (row0 >= j_hi) break;                                // uniform per wave
-    // A operands: rows row0 + 16m + n (clamped into the range), 8 dims per step
-    sk_u32x4_t a[4][4];
+  // A operands of a tile: rows row0 + 16m + n (clamped into the range), 8
+  // dims per step, loaded one tile ahead of their use
+  auto load_tile = [&](int row0, sk_u32x4_t (&a)[4][4], float &xs) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const size_t r = (size_t)min(row0 + 16 * m + n, j_hi - 1);
@@ -129,13 +127,39 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
           a[m][c] = sk_u32x4_t{w.x, w.y, w.z, w.w};
         } else {
           const uint2 w = *reinterpret_cast<const uint2 *>(Xbh + r * D + 32 * c + 8 * g);
-          a[m][c] = sk_u32x4_t{i8pair_bf16(w.x, 0), i8pair_bf16(w.x, 16), i8pair_bf16(w.y, 0),
-                               i8pair_bf16(w.y, 16)};
+          a[m][c] = sk_u32x4_t{w.x, w.y, 0u, 0u};             // converted when used
         }
       }
     }
-    float xs = 1.f;                                          // int8: scale of row row0 + lane
+    xs = 1.f;                                               // int8: scale of row row0 + lane
     if constexpr (DT == SKS_KV_I8) xs = f16_bits_to_float(Xsbh[min(row0 + lane, j_hi - 1)]);
+  };
+  auto tile_row = [&](int it) { return j0 + it * (SM_TILE * SM_THREADS / 64) + wave * SM_TILE; };
+  sk_u32x4_t cur[4][4], nxt[4][4];
+  float xs_cur, xs_nxt;
+  load_tile(min(tile_row(0), j_hi - 1), cur, xs_cur);
+  for (int it = 0; it < SM_ITERS; ++it) {
+    const int row0 = tile_row(it);
+    if (row0 >= j_hi) break;                                // uniform per wave
+    // the next tile's loads go out before this tile's products (a tile past
+    // the range reloads the last row: in bounds, unused)
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(min(tile_row(it + 1), j_hi - 1), nxt, xs_nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    sk_u32x4_t a[4][4];
+    const float xs = xs_cur;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (DT == SKS_KV_BF16) {
+          a[m][c] = cur[m][c];
+        } else {
+          const uint32_t x0 = cur[m][c][0], x1 = cur[m][c][1];
+          a[m][c] = sk_u32x4_t{i8pair_bf16(x0, 0), i8pair_bf16(x0, 16), i8pair_bf16(x1, 0),
+                               i8pair_bf16(x1, 16)};
+        }
+      }
 
     sk_f32x4_t acc[4][4];
 #pragma unroll
@@ -177,6 +201,11 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cur[m][c] = nxt[m][c];
+    xs_cur = xs_nxt;
   }
 }
 
