@@ -108,7 +108,7 @@ def cpu_baseline(cfg, case, seconds):
         prep = []
         for h in range(cfg.Hkv):             # bulk key sketch: outside the timed region
             Kf, Vf = orc.cache_rows(case.K, case.V, case.K_scale, case.V_scale, 0, h,
-                                    cfg.kv_dtype == 1)
+                                    cfg.kv_dtype)
             Kp, Vp = orc.pool_mean(Kf, cfg.pool), orc.pool_mean(Vf, cfg.pool)
             _, kc = orc.key_sketch(Kp, case.basis, float(case.key_scale[h]))
             prep.append((Kf, Vf, Kp, Vp, kc))

@@ -23,6 +23,8 @@ RANK = 64
 
 KV_BF16 = 0
 KV_I8 = 1
+KV_I4 = 2
+KV_NAMES = {KV_BF16: "bf16", KV_I8: "int8", KV_I4: "int4"}
 
 
 @dataclass(frozen=True)
@@ -37,7 +39,7 @@ class Config:
     window: int
     topk: int
     pool: int           # far-field pooling ratio r (1 = unpooled)
-    kv_dtype: int       # KV_BF16 or KV_I8 (int8 + fp16 per-token scale)
+    kv_dtype: int       # KV_BF16, KV_I8 or KV_I4 (int8 / packed int4 + fp16 per-token scale)
     needle_kind: str    # how needles are planted (see synth.py)
     needle_count: int   # per sequence (clusters) or per KV head
     needle_amp: float
@@ -54,6 +56,11 @@ class Config:
     @property
     def g(self) -> int:
         return self.Hq // self.Hkv
+
+    @property
+    def kv_row_bytes(self) -> int:
+        """Bytes of one cached K (or V) row, its scale excluded."""
+        return {KV_BF16: 2 * HEAD_DIM, KV_I8: HEAD_DIM, KV_I4: HEAD_DIM // 2}[self.kv_dtype]
 
     @property
     def T_max(self) -> int:
@@ -118,3 +125,16 @@ def small(cfg: Config) -> Config:
                       window=min(cfg.window, 1000 + cfg.cid),
                       topk=min(cfg.topk, 700 if cfg.pool == 1 else 300),
                       needle_count=min(cfg.needle_count, 40 if cfg.cid != 3 else 150))
+
+
+def with_kv(cfg: Config, kv_dtype: int) -> Config:
+    """`cfg` with another KV storage type (name suffixed with it unless it is
+    the config's own).  The int4 cache is the one the claims list of "8
+    agents x 250K context ..." keeps in host RAM; here it is a storage option
+    of every shape.  Pooling needs a bf16 cache."""
+    if kv_dtype == cfg.kv_dtype:
+        return cfg
+    if cfg.pool > 1 and kv_dtype != KV_BF16:
+        raise ValueError(f"{cfg.name}: pooling needs a bf16 cache")
+    base = cfg.name.replace("_" + KV_NAMES[cfg.kv_dtype], "")
+    return cfg.scaled(name=f"{base}_{KV_NAMES[kv_dtype]}", kv_dtype=kv_dtype)

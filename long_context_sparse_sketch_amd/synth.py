@@ -13,7 +13,9 @@ retrieval evals that are not available):
   "What it took" list of "8 agents x 250K context ... on two 3090s" suggests).
 * q, K, V: float32 N(0,1) rounded to bfloat16 (round to nearest even).  For the
   int8 cache, each (token, KV head) row of K and of V gets
-  ``scale = fp16(absmax / 127)`` and ``code = clip(rint(x / scale), -127, 127)``.
+  ``scale = fp16(absmax / 127)`` and ``code = clip(rint(x / scale), -127, 127)``;
+  the int4 cache likewise with 7 in place of 127, two codes per byte (dimension
+  2j in the low nibble of byte j, 2j+1 in the high nibble, two's complement).
 * needles: keys planted as ``amp * qbar_h + N(0, noise^2)`` where ``qbar_h`` is
   the mean of KV head h's group of (bf16) query vectors of row 0.  Kinds:
   ``random`` (count per KV head, uniform positions without replacement in the
@@ -32,7 +34,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .configs import Config, KV_BF16, KV_I8
+from .configs import Config, KV_BF16, KV_I4, KV_I8
 
 _TAG_BASIS, _TAG_Q, _TAG_K, _TAG_V, _TAG_POS, _TAG_NOISE = range(6)
 
@@ -52,15 +54,35 @@ def _bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-def quantize_rows_i8(x: np.ndarray):
-    """Per-row symmetric int8 with an fp16 scale (the int8 cache encoding)."""
+def _quantize_rows(x: np.ndarray, cmax: int):
     amax = np.abs(x).max(axis=-1)
-    scale16 = (amax / np.float32(127.0)).astype(np.float16)
+    scale16 = (amax / np.float32(cmax)).astype(np.float16)
     s = scale16.astype(np.float32)
     safe = np.where(s > 0, s, np.float32(1.0))
-    codes = np.clip(np.rint(x / safe[..., None]), -127, 127)
+    codes = np.clip(np.rint(x / safe[..., None]), -cmax, cmax)
     codes = np.where(s[..., None] > 0, codes, 0).astype(np.int8)
     return codes, scale16.view(np.uint16)
+
+
+def quantize_rows_i8(x: np.ndarray):
+    """Per-row symmetric int8 with an fp16 scale (the int8 cache encoding)."""
+    return _quantize_rows(x, 127)
+
+
+def pack_i4(codes: np.ndarray) -> np.ndarray:
+    """int4 codes [..][128] in [-8, 7] -> bytes [..][64]: dimension 2j in the
+    low nibble of byte j, dimension 2j+1 in the high nibble."""
+    c = np.asarray(codes, dtype=np.int64)
+    if c.size and (c.min() < -8 or c.max() > 7):
+        raise ValueError("int4 codes must lie in [-8, 7]")
+    u = (c & 0xF).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def quantize_rows_i4(x: np.ndarray):
+    """Per-row symmetric int4 (codes in [-7, 7]) with an fp16 scale, packed."""
+    codes, scale = _quantize_rows(x, 7)
+    return pack_i4(codes), scale
 
 
 @dataclass
@@ -70,9 +92,9 @@ class Case:
     basis: np.ndarray           # [64][128] float32
     key_scale: np.ndarray       # [Hkv] float32
     q: np.ndarray               # [B][R][Hq][128] uint16 (bf16 bits)
-    K: np.ndarray               # [B][Hkv][T][128] uint16 (bf16) or int8
+    K: np.ndarray               # [B][Hkv][T][128] uint16 (bf16) or int8; [..][64] uint8 (int4)
     V: np.ndarray
-    K_scale: np.ndarray | None  # [B][Hkv][T] uint16 (fp16 bits) for int8
+    K_scale: np.ndarray | None  # [B][Hkv][T] uint16 (fp16 bits) for int8 / int4
     V_scale: np.ndarray | None
     seq_len: np.ndarray         # [B] int32, length of row 0
     needles: dict = field(default_factory=dict)   # (b, h) -> sorted token positions
@@ -138,8 +160,9 @@ def _kv_block(cfg: Config, b: int, h: int, qbar: np.ndarray):
         k[pos] = np.float32(cfg.needle_amp) * qbar[None, :] + noise
     if cfg.kv_dtype == KV_BF16:
         return f32_to_bf16_bits(k), f32_to_bf16_bits(v), None, None, pos
-    kc, ks = quantize_rows_i8(k)
-    vc, vs = quantize_rows_i8(v)
+    quant = quantize_rows_i8 if cfg.kv_dtype == KV_I8 else quantize_rows_i4
+    kc, ks = quant(k)
+    vc, vs = quant(v)
     return kc, vc, ks, vs, pos
 
 
@@ -150,11 +173,12 @@ def make_case(cfg: Config, seqs=None, threads: int | None = None) -> Case:
     basis = make_basis(cfg)
     key_scale = np.full((cfg.Hkv,), 1.0 / 16.0, dtype=np.float32)
     q = np.stack([_query(cfg, b) for b in seqs]) if B else np.zeros((0, cfg.R, cfg.Hq, cfg.D), np.uint16)
-    kv_np = np.uint16 if cfg.kv_dtype == KV_BF16 else np.int8
-    K = np.empty((B, cfg.Hkv, T, cfg.D), dtype=kv_np)
+    kv_np = {KV_BF16: np.uint16, KV_I8: np.int8, KV_I4: np.uint8}[cfg.kv_dtype]
+    row = cfg.D // 2 if cfg.kv_dtype == KV_I4 else cfg.D
+    K = np.empty((B, cfg.Hkv, T, row), dtype=kv_np)
     V = np.empty_like(K)
     Ks = Vs = None
-    if cfg.kv_dtype == KV_I8:
+    if cfg.kv_dtype != KV_BF16:
         Ks = np.empty((B, cfg.Hkv, T), dtype=np.uint16)
         Vs = np.empty_like(Ks)
     qf = _bf16_bits_to_f32(q) if B else None

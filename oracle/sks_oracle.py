@@ -68,6 +68,25 @@ def i8_rows_to_f64(codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
     return np.asarray(codes, dtype=np.int8).astype(np.float64) * f16_to_f64(scale_bits)[..., None]
 
 
+def i4_unpack(packed: np.ndarray) -> np.ndarray:
+    """int4 rows [..][64] uint8 -> codes [..][128] int64.
+
+    Byte j of a row holds dimension 2j in its low nibble and dimension 2j+1
+    in its high nibble; each nibble is a two's-complement code in [-8, 7].
+    (The int4 cache of the claims list of "8 agents x 250K context ...": the
+    pages give no bit layout, so this plain one is the reading.)"""
+    p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    lo, hi = p & 0xF, p >> 4
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    return np.stack([lo, hi], axis=-1).reshape(*p.shape[:-1], 2 * p.shape[-1])
+
+
+def i4_rows_to_f64(packed: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """int4 row codes times the row's fp16 scale, exactly."""
+    return i4_unpack(packed).astype(np.float64) * f16_to_f64(scale_bits)[..., None]
+
+
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float64 values to the nearest bfloat16 value, ties to even.
 
@@ -197,12 +216,24 @@ def attend(q_heads: np.ndarray, Krows: np.ndarray, Vrows: np.ndarray, sm_scale: 
 # --------------------------------------------------------------------------
 # one decode step
 # --------------------------------------------------------------------------
-def cache_rows(K, V, Ks, Vs, b: int, h: int, kv_i8: bool, T: int | None = None):
-    """Float64 K, V rows [T][128] of (sequence b, KV head h)."""
+KV_BF16, KV_I8, KV_I4 = 0, 1, 2      # cache storage: bf16 rows, int8 codes, packed int4 codes
+
+
+def cache_rows(K, V, Ks, Vs, b: int, h: int, kv_dtype: int, T: int | None = None):
+    """Float64 K, V rows [T][128] of (sequence b, KV head h).
+
+    kv_dtype: KV_BF16 (bf16 bits), KV_I8 (int8 codes, fp16-bit row scales
+    Ks, Vs) or KV_I4 (packed int4 codes [..][64] uint8, fp16-bit row scales)."""
     T = K.shape[2] if T is None else T
-    if kv_i8:
+    kv_dtype = int(kv_dtype)
+    if kv_dtype == KV_I8:
         return (i8_rows_to_f64(K[b, h, :T], Ks[b, h, :T]),
                 i8_rows_to_f64(V[b, h, :T], Vs[b, h, :T]))
+    if kv_dtype == KV_I4:
+        return (i4_rows_to_f64(K[b, h, :T], Ks[b, h, :T]),
+                i4_rows_to_f64(V[b, h, :T], Vs[b, h, :T]))
+    if kv_dtype != KV_BF16:
+        raise ValueError(f"unknown KV storage {kv_dtype}")
     return bf16_to_f64(K[b, h, :T]), bf16_to_f64(V[b, h, :T])
 
 
@@ -243,11 +274,12 @@ def decode_head(qrows: np.ndarray, Kf: np.ndarray, Vf: np.ndarray, basis: np.nda
 
 
 def decode_step(q, K, V, Ks, Vs, seq_len, basis, key_scale, window: int, topk: int,
-                r: int, kv_i8: bool, heads=None, sm_scale: float | None = None):
+                r: int, kv_dtype: int, heads=None, sm_scale: float | None = None):
     """Oracle decode step over a batch.
 
-    q: [B][R][Hq][128] bf16 bits; K, V: [B][Hkv][T][128] bf16 bits or int8 with
-    fp16-bit scales Ks, Vs [B][Hkv][T]; seq_len [B] (row-0 lengths); basis
+    q: [B][R][Hq][128] bf16 bits; K, V: [B][Hkv][T][128] bf16 bits or int8, or
+    [B][Hkv][T][64] packed int4 (see cache_rows), the codes with fp16-bit row
+    scales Ks, Vs [B][Hkv][T]; seq_len [B] (row-0 lengths); basis
     [64][128] (shared) or [Hkv][64][128]; key_scale [Hkv].
     heads: optional iterable of (b, h) pairs to compute (default: all).
     Returns {(b, h): decode_head result}.
@@ -261,7 +293,7 @@ def decode_step(q, K, V, Ks, Vs, seq_len, basis, key_scale, window: int, topk: i
     pairs = [(b, h) for b in range(B) for h in range(Hkv)] if heads is None else list(heads)
     out = {}
     for b, h in pairs:
-        Kf, Vf = cache_rows(K, V, Ks, Vs, b, h, kv_i8)
+        Kf, Vf = cache_rows(K, V, Ks, Vs, b, h, kv_dtype)
         P = basis if basis.ndim == 2 else basis[h]
         out[(b, h)] = decode_head(qf[b, :, h * g:(h + 1) * g], Kf, Vf, P,
                                   float(key_scale[h]), int(seq_len[b]), window, topk, r, sm)

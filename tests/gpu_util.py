@@ -65,7 +65,7 @@ class GpuCase:
         c, cfg = self.case, self.cfg
         return orc.decode_step(c.q, c.K, c.V, c.K_scale, c.V_scale, self.seq_len_np, c.basis,
                                c.key_scale, self.window, self.topk, self.pool,
-                               cfg.kv_dtype == C.KV_I8, heads=heads)
+                               cfg.kv_dtype, heads=heads)
 
 
 def sketch_ok(code_gpu: np.ndarray, y: np.ndarray, s: float):
@@ -80,7 +80,7 @@ def oracle_key_projection(case, b, h, pool):
     """Float64 projection y of every sketch row of (b, h), from the oracle."""
     cfg = case.cfg
     Kf, Vf = orc.cache_rows(case.K, case.V, case.K_scale, case.V_scale, b, h,
-                            cfg.kv_dtype == C.KV_I8)
+                            cfg.kv_dtype)
     Kp = orc.pool_mean(Kf, pool)
     return orc.project(Kp, case.basis), Kp, orc.pool_mean(Vf, pool)
 

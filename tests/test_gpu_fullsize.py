@@ -47,7 +47,7 @@ def test_full_size_sampled_parity(cfg):
     S = g.layer.S
     for (b, h), r in ref.items():
         Kf, _ = orc.cache_rows(case.K, case.V, case.K_scale, case.V_scale, b, h,
-                               cfg.kv_dtype == C.KV_I8)
+                               cfg.kv_dtype)
         y = orc.project(orc.pool_mean(Kf, cfg.pool), case.basis)[: g.layer.NB]
         got = S[b, h].cpu().numpy()
         assert sketch_ok(got, y, float(case.key_scale[h])).all(), (b, h)

@@ -123,3 +123,21 @@ def test_caught_bf16_decode_wrong_shift(monkeypatch):
         u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 15
         return u32.view(np.float32).astype(np.float64)
     expect_caught(monkeypatch, "bf16_to_f64", bad, pins.test_bf16_decode_closed_form)
+
+
+def test_caught_i4_nibbles_swapped(monkeypatch):
+    real = orc.i4_unpack
+
+    def bad(packed):
+        p = np.asarray(packed, np.uint8)
+        return real(((p << 4) | (p >> 4)).astype(np.uint8))
+    expect_caught(monkeypatch, "i4_unpack", bad, pins.test_i4_dequant_hand_decoded)
+
+
+def test_caught_i4_without_sign_extension(monkeypatch):
+    def bad(packed):
+        p = np.asarray(packed, np.uint8).astype(np.int64)
+        return np.stack([p & 15, p >> 4], axis=-1).reshape(*p.shape[:-1], 2 * p.shape[-1])
+    expect_caught(monkeypatch, "i4_unpack", bad, pins.test_i4_dequant_hand_decoded,
+                  pins.test_i4_cache_reduces_to_i8_cache_with_the_same_codes)
+

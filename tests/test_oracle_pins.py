@@ -42,6 +42,48 @@ def test_i8_dequant_exact():
     assert orc.i8_rows_to_f64(codes, scale).tolist() == [[63.5, -63.5, 0.0, 0.5]]
 
 
+def test_i4_dequant_hand_decoded():
+    # bytes 0x21 0xF8 0x07 0x90: low nibble first, two's complement
+    #   0x21 -> 1, 2;  0xF8 -> -8, -1;  0x07 -> 7, 0;  0x90 -> 0, -7
+    packed = np.array([[0x21, 0xF8, 0x07, 0x90]], np.uint8)
+    assert orc.i4_unpack(packed).tolist() == [[1, 2, -8, -1, 7, 0, 0, -7]]
+    scale = np.array([0x3800], np.uint16)     # fp16 0.5
+    assert orc.i4_rows_to_f64(packed, scale).tolist() == [[0.5, 1.0, -4.0, -0.5, 3.5, 0.0, 0.0,
+                                                            -3.5]]
+    # every byte value: the two nibbles are (b & 15) and (b >> 4), values >= 8 wrap by 16
+    allb = np.arange(256, dtype=np.uint8)[None, :]
+    got = orc.i4_unpack(allb)[0]
+    for b in range(256):
+        lo, hi = b % 16, b // 16
+        assert got[2 * b] == (lo if lo < 8 else lo - 16)
+        assert got[2 * b + 1] == (hi if hi < 8 else hi - 16)
+
+
+def test_i4_cache_reduces_to_i8_cache_with_the_same_codes():
+    """An int4 cache is an int8 cache whose codes happen to lie in [-8, 7]:
+    the whole step must agree exactly with the (separately pinned) int8 path."""
+    from long_context_sparse_sketch_amd.synth import pack_i4
+    rng = np.random.default_rng(41)
+    T, L, Hq, Hkv = 700, 698, 6, 2
+    kc = rng.integers(-8, 8, (1, Hkv, T, 128)).astype(np.int8)
+    vc = rng.integers(-8, 8, (1, Hkv, T, 128)).astype(np.int8)
+    ks = (rng.uniform(0.05, 0.5, (1, Hkv, T))).astype(np.float16).view(np.uint16)
+    vs = (rng.uniform(0.05, 0.5, (1, Hkv, T))).astype(np.float16).view(np.uint16)
+    q = f32_to_bf16_bits(rng.standard_normal((1, 2, Hq, 128)).astype(np.float32))
+    basis = np.linalg.qr(rng.standard_normal((128, 64)))[0].T.astype(np.float32)
+    kscale = np.full(Hkv, 1 / 16, np.float32)
+    sl = np.array([L], np.int32)
+    a = orc.decode_step(q, kc, vc, ks, vs, sl, basis, kscale, 100, 50, 1, orc.KV_I8)
+    b = orc.decode_step(q, pack_i4(kc), pack_i4(vc), ks, vs, sl, basis, kscale, 100, 50, 1,
+                        orc.KV_I4)
+    for key in a:
+        for field in ("kcodes",):
+            assert np.array_equal(a[key][field], b[key][field])
+        for i in range(2):
+            for field in ("qcode", "scores", "idx", "out", "lse"):
+                assert np.array_equal(a[key][field][i], b[key][field][i]), (key, field, i)
+
+
 def test_round_to_bf16_ties_and_nearest():
     one = 1.0
     assert orc.round_to_bf16(np.array([one + 2.0 ** -8]))[0] == 1.0                # tie -> even
@@ -295,7 +337,7 @@ def _run_case(case, heads=None):
     cfg = case.cfg
     return orc.decode_step(case.q, case.K, case.V, case.K_scale, case.V_scale, case.seq_len,
                            case.basis, case.key_scale, cfg.window, cfg.topk, cfg.pool,
-                           cfg.kv_dtype == C.KV_I8, heads=heads)
+                           cfg.kv_dtype, heads=heads)
 
 
 def test_batch_invariance_of_inputs_and_oracle():
@@ -325,7 +367,9 @@ def _check_needles(case, res, row=0):
             assert np.isin(sel, units).all(), (b, h)
 
 
-@pytest.mark.parametrize("cfg", [C.C1, C.small(C.C2), C.small(C.C3), C.small(C.C4), C.small(C.C5)],
+@pytest.mark.parametrize("cfg", [C.C1, C.small(C.C2), C.small(C.C3), C.small(C.C4), C.small(C.C5),
+                                 C.with_kv(C.small(C.C3), C.KV_I4),
+                                 C.with_kv(C.small(C.C5), C.KV_I4)],
                          ids=lambda c: c.name)
 def test_needle_recall(cfg):
     case = make_case(cfg)
@@ -338,3 +382,19 @@ def test_synth_int8_quantization_bound():
     Kf = orc.i8_rows_to_f64(case.K[0, 0], case.K_scale[0, 0])
     assert np.abs(case.K[0, 0]).max() <= 127
     assert (np.abs(case.K[0, 0]).max(axis=1) >= 126).all()
+
+
+def test_synth_int4_quantization_bound():
+    cfg = C.with_kv(C.small(C.C5), C.KV_I4)
+    case = make_case(cfg, seqs=[0])
+    assert case.K.shape[-1] == 64 and case.K.dtype == np.uint8
+    codes = orc.i4_unpack(case.K[0, 0])
+    assert np.abs(codes).max() <= 7 and (np.abs(codes).max(axis=1) == 7).all()
+    Kf = orc.i4_rows_to_f64(case.K[0, 0], case.K_scale[0, 0])
+    # the int4 rows sit within half a step (plus the fp16 scale's rounding) of the
+    # same draw stored as int8, which is itself within half of its own step
+    ref = make_case(C.small(C.C5), seqs=[0])
+    K8 = orc.i8_rows_to_f64(ref.K[0, 0], ref.K_scale[0, 0])
+    s4 = orc.f16_to_f64(case.K_scale[0, 0])[:, None]
+    s8 = orc.f16_to_f64(ref.K_scale[0, 0])[:, None]
+    assert (np.abs(Kf - K8) <= 0.5 * s4 * 1.01 + 0.5 * s8 + 1e-12).all()
