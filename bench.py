@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="multi_agent_250k")
+    ap.add_argument("--kv", choices=("bf16", "int8", "int4"), default=None,
+                    help="store the workload's KV cache in another format (default: its own)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -64,7 +66,7 @@ def algorithmic_bytes(cfg):
     plus q in, out and idx out.
     """
     B, R, Hkv, Hq = cfg.B, cfg.R, cfg.Hkv, cfg.Hq
-    row_bytes = 128 * (2 if cfg.kv_dtype == 0 else 1) + (0 if cfg.kv_dtype == 0 else 2)
+    row_bytes = cfg.kv_row_bytes + (0 if cfg.kv_dtype == 0 else 2)     # codes carry an fp16 scale
     n_far_max = cfg.n_far(R - 1)
     sketch = B * Hkv * n_far_max * 64
     gathered = sum(B * Hkv * cfg.n_attended(i) * 2 * row_bytes for i in range(R))
@@ -153,6 +155,8 @@ def main():
     from long_context_sparse_sketch_amd.synth import make_case
 
     cfg = C.BY_NAME[args.config]
+    if args.kv is not None:
+        cfg = C.with_kv(cfg, {v: k for k, v in C.KV_NAMES.items()}[args.kv])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sks.lib()
@@ -161,7 +165,7 @@ def main():
     print(f"[bench] generated {cfg.name} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
           flush=True)
 
-    i8 = cfg.kv_dtype == C.KV_I8
+    i8 = cfg.kv_dtype != C.KV_BF16          # int8 codes or packed int4 bytes, with row scales
     K0 = torch.from_numpy(case.K).to(dev) if i8 else to_device(case.K, dev, bf16=True)
     V0 = torch.from_numpy(case.V).to(dev) if i8 else to_device(case.V, dev, bf16=True)
     Ks0 = to_device(case.K_scale, dev) if i8 else None
@@ -271,8 +275,8 @@ def main():
 
     # standalone gather/pack of the same rows into packed buffers
     Cn = cfg.topk + cfg.window + cfg.pool - 1
-    kdt = torch.int8 if i8 else torch.bfloat16
-    Ko = torch.empty((cfg.B, cfg.R, cfg.Hkv, Cn, 128), dtype=kdt, device=dev)
+    kdt = {C.KV_BF16: torch.bfloat16, C.KV_I8: torch.int8, C.KV_I4: torch.uint8}[cfg.kv_dtype]
+    Ko = torch.empty((cfg.B, cfg.R, cfg.Hkv, Cn, case.K.shape[-1]), dtype=kdt, device=dev)
     Vo = torch.empty_like(Ko)
     Kso = torch.empty((cfg.B, cfg.R, cfg.Hkv, Cn), dtype=torch.int16, device=dev) if i8 else None
     Vso = torch.empty_like(Kso) if i8 else None
@@ -323,7 +327,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8 sketch / bf16 KV / f32 accumulate" if not i8 else "i8 sketch / i8 KV / f32 accumulate",
+        "dtype": f"i8 sketch / {C.KV_NAMES[cfg.kv_dtype]} KV / f32 accumulate",
         "data": "synthetic (seeded N(0,1) caches with planted needles)",
         "config": {"workload": cfg.name, "batch": cfg.B, "context": cfg.L, "rows": cfg.R,
                    "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "window": cfg.window,

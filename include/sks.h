@@ -61,14 +61,19 @@ typedef struct ihipStream_t *sks_stream_t; /* a hipStream_t */
 enum sks_status {
   SKS_OK = 0,
   SKS_ERR_ARG = 1,          /* invalid argument; nothing was launched          */
-  SKS_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. int8 + pooling)  */
+  SKS_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. int8/int4 + pooling) */
   SKS_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required       */
   SKS_ERR_HIP = 4           /* a HIP launch failed                              */
 };
 
 enum sks_kv_dtype {
   SKS_KV_BF16 = 0,          /* K, V hold bfloat16                               */
-  SKS_KV_I8 = 1             /* K, V hold int8 codes; x = code * fp16 row scale  */
+  SKS_KV_I8 = 1,            /* K, V hold int8 codes; x = code * fp16 row scale  */
+  SKS_KV_I4 = 2             /* K, V hold int4 codes, 64 bytes per row: byte j
+                               has dim 2j in its low and dim 2j+1 in its high
+                               nibble, two's complement in [-8, 7];
+                               x = code * fp16 row scale (the int4 KV of the
+                               claims list of "8 agents x 250K context ...")  */
 };
 
 #define SKS_HEAD_DIM 128
@@ -85,10 +90,10 @@ typedef struct sks_kv {
   int32_t D;                /* head dim, must be 128                            */
   int32_t T_max;            /* cache capacity in tokens                         */
   int32_t dtype;            /* enum sks_kv_dtype                                */
-  const void *K;            /* [B][Hkv][T_max][D] bf16 or int8                  */
+  const void *K;            /* [B][Hkv][T_max][D] bf16 or int8, [..][D/2] int4   */
   const void *V;            /* [B][Hkv][T_max][D]                               */
-  const uint16_t *K_scale;  /* [B][Hkv][T_max] fp16 bits, int8 only, else NULL  */
-  const uint16_t *V_scale;  /* [B][Hkv][T_max] fp16 bits, int8 only, else NULL  */
+  const uint16_t *K_scale;  /* [B][Hkv][T_max] fp16 bits, int8/int4, else NULL  */
+  const uint16_t *V_scale;  /* [B][Hkv][T_max] fp16 bits, int8/int4, else NULL  */
   const int32_t *seq_len;   /* [B] device: L of query row 0 (own token included) */
 } sks_kv;
 
@@ -191,9 +196,10 @@ int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p
  * kernel).  For every (b, i, h) writes the row's attention set, selected far
  * entries first (ascending, rows of Kp/Vp when pool > 1, else of K/V), then
  * the window tokens [ws, L_i) ascending, into
- *   K_out, V_out: [B][R][Hkv][C][128] with C = topk + window + pool - 1,
- * same element type as the cache (int8 caches also write the fp16 row scales
- * to Ks_out, Vs_out [B][R][Hkv][C]; NULL for bf16), and the entry count to
+ *   K_out, V_out: [B][R][Hkv][C][row] with C = topk + window + pool - 1,
+ * rows in the cache's own format (int8 and int4 caches also write the fp16
+ * row scales to Ks_out, Vs_out [B][R][Hkv][C]; NULL for bf16), and the entry
+ * count to
  * n_out [B][R][Hkv].  Slots past n_out are not written. */
 int sks_gather_pack(const sks_kv *kv, const sks_params *p, const int32_t *idx,
                     const uint16_t *Kp, const uint16_t *Vp, void *K_out, void *V_out,
@@ -202,7 +208,7 @@ int sks_gather_pack(const sks_kv *kv, const sks_params *p, const int32_t *idx,
 
 /* Sparse decode attention, one merged softmax over the selected far entries
  * and the exact window ("What it adds" of "Agens SGLang"; "int8 attention"
- * of "What it took" for int8 caches, dequantised in registers).  For query
+ * of "What it took" for int8 and int4 caches, dequantised in registers).  For query
  * head hq of row i of sequence b, with U its row's attention set:
  *   z_j = sm_scale * (q . K_j),  out = sum_j softmax(z)_j V_j,
  *   lse = log sum_j exp(z_j)     (U empty: out = 0, lse = -inf).

@@ -17,7 +17,7 @@ _LIB = None
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsks.so")
 
 SKS_OK, SKS_ERR_ARG, SKS_ERR_UNSUPPORTED, SKS_ERR_WORKSPACE, SKS_ERR_HIP = range(5)
-KV_BF16, KV_I8 = 0, 1
+KV_BF16, KV_I8, KV_I4 = 0, 1, 2
 APPEND = -1
 HEAD_DIM, RANK = 128, 64
 
@@ -123,7 +123,10 @@ class Cache:
     def __init__(self, K, V, seq_len, K_scale=None, V_scale=None):
         self.K, self.V, self.seq_len, self.K_scale, self.V_scale = K, V, seq_len, K_scale, V_scale
         B, Hkv, T, D = K.shape
-        dtype = KV_I8 if K.dtype == torch.int8 else KV_BF16
+        # int8 codes as torch.int8; packed int4 rows (64 bytes) as torch.uint8
+        dtype = {torch.int8: KV_I8, torch.uint8: KV_I4}.get(K.dtype, KV_BF16)
+        if dtype == KV_I4:
+            D *= 2
         self.desc = KVDesc(B, Hkv, D, T, dtype, ptr(K), ptr(V), ptr(K_scale), ptr(V_scale),
                            ptr(seq_len))
 

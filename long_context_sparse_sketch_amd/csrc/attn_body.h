@@ -92,6 +92,25 @@ __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int sh) {
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
+// int4 codes (eight two's-complement nibbles of w, low nibble first: dims
+// 0..7 of a group of 8) -> code + I4_BIAS as bf16, exactly: with u = nibble
+// ^ 8 = code + 8 in [0, 15], the bf16 pattern 0x4300 | u is 128 + u.  The
+// eight values come out in the slot order I4_ORDER = dims 0, 2, 4, 6, 1, 3,
+// 5, 7, so that each bf16 pair is one byte permute of the masked low (or
+// high) nibbles with the constant 0x43 bytes: about one VALU op per value.
+// The bias is taken out of the products afterwards (see attn_body).
+constexpr float I4_BIAS = 136.f;
+__device__ __forceinline__ u32x4_t i4_biased_bf16x8(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;   // dims 0,2,4,6 / 1,3,5,7
+  const uint32_t k43 = 0x43434343u;
+  // perm(S0, S1, sel): selector bytes 0-3 pick bytes of S1, 4-7 bytes of S0
+  return u32x4_t{__builtin_amdgcn_perm(k43, lo, 0x04010400u), __builtin_amdgcn_perm(k43, lo, 0x04030402u),
+                 __builtin_amdgcn_perm(k43, hi, 0x04010400u), __builtin_amdgcn_perm(k43, hi, 0x04030402u)};
+}
+// dim held by slot s (0..7) of a group of 8 in I4_ORDER
+__device__ __forceinline__ int i4_slot_dim(int s) { return s < 4 ? 2 * s : 2 * (s - 4) + 1; }
+
 __device__ __forceinline__ float row16_max_f(float x) {
   x = fmaxf(x, dpp_f<DPP_ROW_MIRROR>(x));
   x = fmaxf(x, dpp_f<DPP_ROW_HMIRROR>(x));
@@ -244,9 +263,12 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   // 128 dims are spread over the steps, as long as Q and K use the same
   // spread: bf16 takes dims 32c + 8g .. +8; int8 takes 16 consecutive dims
   // per pair of steps, (c / 2) * 64 + 16g + (c % 2) * 8 .. +8, so that a lane
-  // reads 16 bytes of an int8 row at once.
+  // reads 16 bytes of an int8 row at once; int4 takes dims 32g + 8c .. +8, so
+  // that the 16 bytes of a lane's int4 K load cover its four steps.
   auto qdim = [&](int c) {
-    return DT == SKS_KV_I8 ? (c >> 1) * 64 + 16 * g + (c & 1) * 8 : 32 * c + 8 * g;
+    return DT == SKS_KV_I8   ? (c >> 1) * 64 + 16 * g + (c & 1) * 8
+           : DT == SKS_KV_I4 ? 32 * g + 8 * c
+                             : 32 * c + 8 * g;
   };
   u32x4_t qa[4];
 #pragma unroll
@@ -255,18 +277,36 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
     if (n < G) {
       const uint4 w = *reinterpret_cast<const uint4 *>(
           q + ((size_t)bi * Hq + (size_t)h * G + n) * D + qdim(c));
-      qa[c] = u32x4_t{w.x, w.y, w.z, w.w};
+      if constexpr (DT == SKS_KV_I4)      // the slot order of the int4 K operand
+        qa[c] = u32x4_t{(w.x & 0xffffu) | (w.y << 16), (w.z & 0xffffu) | (w.w << 16),
+                        (w.x >> 16) | (w.y & 0xffff0000u), (w.z >> 16) | (w.w & 0xffff0000u)};
+      else
+        qa[c] = u32x4_t{w.x, w.y, w.z, w.w};
     }
   }
-  // int8 caches: each lane's entries' row scales, with the descriptors
+  // int8 / int4 caches: each lane's entries' row scales, with the descriptors
   float ksd0 = 1.f, vsd0 = 1.f, ksd1 = 1.f, vsd1 = 1.f;
-  if constexpr (DT == SKS_KV_I8) {
+  if constexpr (DT != SKS_KV_BF16) {
     const size_t sbase = ((size_t)b * Hkv + h) * T_max;
     ksd0 = f16_bits_to_float(Ks[sbase + row0]);
     vsd0 = f16_bits_to_float(Vs[sbase + row0]);
     ksd1 = f16_bits_to_float(Ks[sbase + row1]);
     vsd1 = f16_bits_to_float(Vs[sbase + row1]);
   }
+
+  // int4: the K operand is code + I4_BIAS, so each logit carries
+  // I4_BIAS * sum_d q_d of its head; kb4[j] is that term for head 4g + j
+  // (Q times a B operand of ones: the same matrix-core arithmetic)
+  float kb4[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (DT == SKS_KV_I4) {
+    f32x4_t qs = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qs = mfma_bf16(qa[c], ones, qs);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kb4[j] = I4_BIAS * qs[j];
+  }
+  float c4[4] = {0.f, 0.f, 0.f, 0.f};        // int4: sum of the PV weights per head (see below)
 
   f32x4_t o[8];
 #pragma unroll
@@ -278,9 +318,9 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
     l4[j] = 0.f;
   }
 
-  constexpr int EB = DT == SKS_KV_BF16 ? 2 : 1;
-  const char *Kt = static_cast<const char *>(K) + ((size_t)b * Hkv + h) * T_max * D * EB;
-  const char *Vt = static_cast<const char *>(V) + ((size_t)b * Hkv + h) * T_max * D * EB;
+  constexpr int RB = DT == SKS_KV_BF16 ? 2 * D : DT == SKS_KV_I8 ? D : D / 2;   // row bytes
+  const char *Kt = static_cast<const char *>(K) + ((size_t)b * Hkv + h) * T_max * RB;
+  const char *Vt = static_cast<const char *>(V) + ((size_t)b * Hkv + h) * T_max * RB;
   const char *Kpb = reinterpret_cast<const char *>(Kp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
   const char *Vpb = reinterpret_cast<const char *>(Vp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
   uint16_t *sv = s_v[wave];
@@ -292,14 +332,17 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   //       x = 64 qq + lane.
   // int8: K: 16 bytes for steps 0-1 and 16 bytes for steps 2-3 (see qdim);
   //       V: 16 bytes (16 dims) of chunk (x & 7) of tile row (x >> 3).
-  constexpr bool I8 = DT == SKS_KV_I8;
-  constexpr int KLD = I8 ? 2 : 4;                    // K loads per sub-tile
-  constexpr int VLD = I8 ? 4 : 8;                    // V loads per tile
+  // int4: K: 16 bytes (dims 32g .. +32) for all four steps;
+  //       V: 16 bytes (32 dims) of chunk (x & 3) of tile row (x >> 2).
+  constexpr bool I8 = DT == SKS_KV_I8, I4 = DT == SKS_KV_I4, Q = I8 || I4;
+  constexpr int KLD = I4 ? 1 : I8 ? 2 : 4;           // K loads per sub-tile
+  constexpr int VLD = I4 ? 2 : I8 ? 4 : 8;           // V loads per tile
+  constexpr int VSH = I4 ? 2 : I8 ? 3 : 4;           // log2(V loads per row)
   struct Tile {
     uint4 k[2][KLD];
     uint4 v[VLD];
     int f[2];              // flags of the two K entries of this lane
-    float ks[2], vs[2];    // int8 row scales of the two K entries
+    float ks[2], vs[2];    // int8 / int4 row scales of the two K entries
   };
   // K/V rows are read once per step: nontemporal loads keep them from
   // evicting lines that are reused.
@@ -315,10 +358,10 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
       desc(j, r, f);
       d.f[t] = f;
       const char *kbase = (POOLED && (f & 2)) ? Kpb : Kt;
-      const size_t off = (size_t)r * D * EB;
-      if constexpr (I8) {
+      const size_t off = (size_t)r * RB;
+      if constexpr (Q) {
         d.k[t][0] = ld(kbase + off + 16 * g);
-        d.k[t][1] = ld(kbase + off + 64 + 16 * g);
+        if constexpr (I8) d.k[t][1] = ld(kbase + off + 64 + 16 * g);
         d.ks[t] = j < 64 ? __shfl(ksd0, j) : __shfl(ksd1, j - 64);
         d.vs[t] = j < 64 ? __shfl(vsd0, j) : __shfl(vsd1, j - 64);
       } else {
@@ -329,16 +372,20 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
 #pragma unroll
     for (int qq = 0; qq < VLD; ++qq) {
       const int x = qq * 64 + lane;
-      const int ev = I8 ? x >> 3 : x >> 4, c = I8 ? x & 7 : x & 15;
+      const int ev = x >> VSH, c = x & ((1 << VSH) - 1);
       int r, f;
       desc(tile * AM_TILE + ev, r, f);
       const char *vbase = (POOLED && (f & 2)) ? Vpb : Vt;
-      d.v[qq] = ld(vbase + (size_t)r * D * EB + c * 16);
+      d.v[qq] = ld(vbase + (size_t)r * RB + c * 16);
     }
   };
-  // K operand of MFMA step c as 8 bf16 (int8 codes convert exactly)
+  // K operand of MFMA step c as 8 bf16 (int8 codes convert exactly; int4
+  // codes as code + I4_BIAS, also exact)
   auto kop = [&](const Tile &d, int t, int c) -> u32x4_t {
-    if constexpr (I8) {
+    if constexpr (I4) {
+      const uint4 &w = d.k[t][0];
+      return i4_biased_bf16x8(c == 0 ? w.x : c == 1 ? w.y : c == 2 ? w.z : w.w);
+    } else if constexpr (I8) {
       const uint4 &w = d.k[t][c >> 1];
       const uint32_t a = (c & 1) ? w.z : w.x, bb = (c & 1) ? w.w : w.y;
       return u32x4_t{i8pair_to_bf16x2(a, 0), i8pair_to_bf16x2(a, 16), i8pair_to_bf16x2(bb, 0),
@@ -364,7 +411,19 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
     for (int qq = 0; qq < VLD; ++qq) {
       const int x = qq * 64 + lane;
       const uint4 &w = d.v[qq];
-      if constexpr (I8) {
+      if constexpr (I4) {
+        // 32 dims as code + I4_BIAS (the bias is removed from O at the end),
+        // each group of 8 columns in I4_ORDER (undone when O is written)
+        const int ev = x >> 2, c = x & 3;
+        uint2 *dst = reinterpret_cast<uint2 *>(sv + ev * VROW + c * 32);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x4_t bv = i4_biased_bf16x8(ws[k]);
+          dst[2 * k] = make_uint2(bv[0], bv[1]);
+          dst[2 * k + 1] = make_uint2(bv[2], bv[3]);
+        }
+      } else if constexpr (I8) {
         const int ev = x >> 3, c = x & 7;
         uint2 *dst = reinterpret_cast<uint2 *>(sv + ev * VROW + c * 16);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -383,20 +442,22 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
     float ksc[2], vsc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      ksc[t] = I8 ? d.ks[t] : 1.f;
-      vsc[t] = I8 ? d.vs[t] : 1.f;
+      ksc[t] = Q ? d.ks[t] : 1.f;
+      vsc[t] = Q ? d.vs[t] : 1.f;
     }
     float z[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) z[t][j] = (d.f[t] & 1) ? sacc[t][j] * ksc[t] * sm_log2 : NEG_INF;
+      for (int j = 0; j < 4; ++j)
+        z[t][j] = (d.f[t] & 1) ? (sacc[t][j] - kb4[j]) * ksc[t] * sm_log2 : NEG_INF;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float mx = row16_max_f(fmaxf(z[0][j], z[1][j]));
       if (mx > m4[j] + RESCALE_SLACK || (m4[j] == NEG_INF && mx != NEG_INF)) {
         const float alpha = m4[j] == NEG_INF ? 0.f : exp2_fast(m4[j] - mx);
         l4[j] *= alpha;
+        if constexpr (I4) c4[j] *= alpha;
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) o[blk][j] *= alpha;
         m4[j] = mx;
@@ -412,6 +473,7 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
         const float pw = pv * vsc[t];                       // value scale folded in
         const uint32_t hi = f32_to_bf16_rne(pw);
         const uint32_t lo = f32_to_bf16_rne(pw - __uint_as_float(hi << 16));
+        if constexpr (I4) c4[j] += __uint_as_float(hi << 16) + __uint_as_float(lo << 16);
         const int at = (4 * g + j) * AM_TILE + 16 * t + n;
         sp_hi[at] = (uint16_t)hi;
         sp_lo[at] = (uint16_t)lo;
@@ -459,6 +521,16 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   // denominators: sum the lane-partials over the 16 lanes of each DPP row
 #pragma unroll
   for (int j = 0; j < 4; ++j) l4[j] = row16_sum_f(l4[j]);
+  // int4: O holds sum_j w_j (v_j + I4_BIAS) with w_j the bf16 weights fed to
+  // the matrix cores; take out I4_BIAS * sum_j w_j
+  if constexpr (I4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float cb = I4_BIAS * row16_sum_f(c4[j]);
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) o[blk][j] -= cb;
+    }
+  }
   __syncthreads();                                          // s_v is reused as s_o below
   // wave partials to LDS: O rows 4g + j < G
 #pragma unroll
@@ -466,7 +538,12 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
     const int hh = 4 * g + j;
     if (hh < G) {
 #pragma unroll
-      for (int blk = 0; blk < 8; ++blk) s_o[(wave * G + hh) * D + 16 * blk + n] = o[blk][j];
+      for (int blk = 0; blk < 8; ++blk) {
+        // int4: V columns are in I4_ORDER within each group of 8
+        const int col = 16 * blk + n;
+        const int dim = I4 ? (col & ~7) + i4_slot_dim(col & 7) : col;
+        s_o[(wave * G + hh) * D + dim] = o[blk][j];
+      }
       if (n == 0) {
         s_ml[wave][hh][0] = m4[j];
         s_ml[wave][hh][1] = l4[j];

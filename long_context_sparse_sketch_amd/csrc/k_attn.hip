@@ -36,6 +36,8 @@ template <int G>
 void dispatch_g(dim3 grid, hipStream_t st, const AttnArgs &a, int dtype, int pool, int slot0) {
   if (dtype == SKS_KV_I8)
     attn_kernel<G, SKS_KV_I8, false><<<grid, AT_THREADS, 0, st>>>(a, slot0);
+  else if (dtype == SKS_KV_I4)
+    attn_kernel<G, SKS_KV_I4, false><<<grid, AT_THREADS, 0, st>>>(a, slot0);
   else if (pool > 1)
     attn_kernel<G, SKS_KV_BF16, true><<<grid, AT_THREADS, 0, st>>>(a, slot0);
   else

@@ -3,7 +3,7 @@
 // for the attention kernel).  Selected far entries first (ascending; pooled
 // rows when pool > 1), then the exact window, into a dense per-(b, i, h)
 // buffer of C = topk + window + pool - 1 row slots.  Rows move as 16-byte
-// vectors, a bf16 row being 16 lanes and an int8 row 8 lanes.
+// vectors, a bf16 row being 16 lanes, an int8 row 8 and an int4 row 4.
 #include "sks_internal.h"
 
 namespace sks {
@@ -20,7 +20,7 @@ __global__ __launch_bounds__(GP_THREADS) void gather_kernel(
     const uint16_t *__restrict__ Vp, int R, int Hkv, int T_max, int NB, int window, int pool,
     int topk, int C, void *__restrict__ K_out, void *__restrict__ V_out,
     uint16_t *__restrict__ Ks_out, uint16_t *__restrict__ Vs_out, int32_t *__restrict__ n_out) {
-  constexpr int ROW_BYTES = DT == SKS_KV_BF16 ? D * 2 : D;
+  constexpr int ROW_BYTES = DT == SKS_KV_BF16 ? D * 2 : DT == SKS_KV_I8 ? D : D / 2;
   constexpr int VECS = ROW_BYTES / 16;
   const int seg = blockIdx.y;
   const int h = seg % Hkv, bi = seg / Hkv, i = bi % R, b = bi / R;
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(GP_THREADS) void gather_kernel(
     reinterpret_cast<uint4 *>(static_cast<char *>(K_out) + (out_base + e) * ROW_BYTES)[v] = kv4;
     reinterpret_cast<uint4 *>(static_cast<char *>(V_out) + (out_base + e) * ROW_BYTES)[v] = vv4;
   }
-  if constexpr (DT == SKS_KV_I8) {
+  if constexpr (DT != SKS_KV_BF16) {
     const int e = e0 + threadIdx.x;
     if (threadIdx.x < GP_ROWS && e < rg.n_ent) {
       bool ok = true;
@@ -88,6 +88,8 @@ hipError_t launch_gather(const sks_kv &kv, const Shape &s, const int32_t *idx,
                                                      K_out, V_out, Ks_out, Vs_out, n_out)
   if (s.dtype == SKS_KV_I8)
     SKS_GATHER(SKS_KV_I8, false);
+  else if (s.dtype == SKS_KV_I4)
+    SKS_GATHER(SKS_KV_I4, false);
   else if (s.pool > 1)
     SKS_GATHER(SKS_KV_BF16, true);
   else

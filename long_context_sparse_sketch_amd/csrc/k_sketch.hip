@@ -21,6 +21,26 @@ __device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int sh) {
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
+// int4 codes (eight two's-complement nibbles of w, low nibble first) -> four
+// bf16 pairs, exactly; out[p] holds dims 2p, 2p + 1
+typedef uint32_t sk_u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ sk_u32x4_t i4x8_bf16(uint32_t w) {
+  sk_u32x4_t o;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float a = (float)((int32_t)(w << (28 - 8 * p)) >> 28);
+    const float b = (float)((int32_t)(w << (24 - 8 * p)) >> 28);
+    o[p] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+  }
+  return o;
+}
+
+// Bytes of one cached K row.
+template <int DT>
+constexpr int row_bytes() {
+  return DT == SKS_KV_BF16 ? 2 * D : DT == SKS_KV_I8 ? D : D / 2;
+}
+
 // First sketch row of the range handled by this (b, h): host range or append.
 __device__ __forceinline__ void sketch_range(int append, const int32_t *seq_len, int b, int T_max,
                                              int R, int pool, int NB, int t_begin, int t_end,
@@ -42,9 +62,10 @@ __device__ __forceinline__ void sketch_range(int append, const int32_t *seq_len,
 // ---------------------------------------------------------------------------
 // Bulk sketch on the matrix cores.  Per (b, h), Y[rows][64] = X[rows][128] P^T:
 // v_mfma_f32_16x16x32_bf16 with A = 16 rows x 32 dims of X (lane (n, g): row
-// n, dims 32c + 8g .. +8) and B = 32 dims x 16 basis rows (lane: basis row n,
-// the same dims).  X is exact in bf16 (bf16 rows; int8 codes, whose fp16 row
-// scale multiplies Y afterwards).  The fp32 basis is split exactly into three
+// n, dims 32c + 8g .. +8 of step c; int4 rows take dims 32g + 8c .. +8, so
+// that one 16-byte load holds a lane's four steps) and B = 32 dims x 16
+// basis rows (lane: basis row n, the same dims).  X is exact in bf16 (bf16
+// rows; int8 and int4 codes, whose fp16 row scale multiplies Y afterwards).  The fp32 basis is split exactly into three
 // bf16 parts, P = hi + mid + lo (8 + 8 + 8 significant bits), so every
 // product is exact and only the fp32 accumulation rounds -- the same
 // accuracy as an fp32 dot product.  The split basis sits in LDS in operand
@@ -56,7 +77,12 @@ constexpr int SM_ROWS = SM_TILE * (SM_THREADS / 64) * SM_ITERS;   // 4096 rows p
 
 typedef __bf16 sk_bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float sk_f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t sk_u32x4_t __attribute__((ext_vector_type(4)));
+
+// first of the 8 dims of MFMA step c held by lane group g
+template <int DT>
+__device__ __forceinline__ int sm_dim(int c, int g) {
+  return DT == SKS_KV_I4 ? 32 * g + 8 * c : 32 * c + 8 * g;
+}
 
 __device__ __forceinline__ sk_f32x4_t sk_mfma(sk_u32x4_t a, sk_u32x4_t b, sk_f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sk_bf16x8_t, a),
@@ -99,7 +125,7 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
   const float *P = basis + (basis_per_head ? (size_t)h * RANK * D : 0);
   for (int e = threadIdx.x; e < 3 * 4 * 4 * 64; e += SM_THREADS) {
     const int part = e >> 10, nb = (e >> 8) & 3, c = (e >> 6) & 3, l = e & 63;
-    const float *src = P + (size_t)(16 * nb + (l & 15)) * D + 32 * c + 8 * (l >> 4);
+    const float *src = P + (size_t)(16 * nb + (l & 15)) * D + sm_dim<DT>(c, l >> 4);
     sk_u32x4_t w;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -109,9 +135,9 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
   __syncthreads();
 
   const float kscale = key_scale[h];
-  constexpr int EB = DT == SKS_KV_BF16 ? 2 : 1;
-  const char *Xbh = static_cast<const char *>(X) + (size_t)bh * x_rows_per_bh * D * EB;
-  const uint16_t *Xsbh = DT == SKS_KV_I8 ? Xs + (size_t)bh * x_rows_per_bh : nullptr;
+  constexpr int RB = row_bytes<DT>();
+  const char *Xbh = static_cast<const char *>(X) + (size_t)bh * x_rows_per_bh * RB;
+  const uint16_t *Xsbh = DT != SKS_KV_BF16 ? Xs + (size_t)bh * x_rows_per_bh : nullptr;
   uint8_t *st = stage[wave];
 
   // A operands of a tile: rows row0 + 16m + n (clamped into the range), 8
@@ -122,7 +148,12 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
       const size_t r = (size_t)min(row0 + 16 * m + n, j_hi - 1);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        if constexpr (DT == SKS_KV_BF16) {
+        if constexpr (DT == SKS_KV_I4) {
+          if (c == 0) {                                       // all four steps: 16 bytes
+            const uint4 w = *reinterpret_cast<const uint4 *>(Xbh + r * RB + 16 * g);
+            a[m][0] = sk_u32x4_t{w.x, w.y, w.z, w.w};
+          }
+        } else if constexpr (DT == SKS_KV_BF16) {
           const uint4 w = *reinterpret_cast<const uint4 *>(Xbh + (r * D + 32 * c + 8 * g) * 2);
           a[m][c] = sk_u32x4_t{w.x, w.y, w.z, w.w};
         } else {
@@ -131,8 +162,8 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
         }
       }
     }
-    xs = 1.f;                                               // int8: scale of row row0 + lane
-    if constexpr (DT == SKS_KV_I8) xs = f16_bits_to_float(Xsbh[min(row0 + lane, j_hi - 1)]);
+    xs = 1.f;                                               // codes: scale of row row0 + lane
+    if constexpr (DT != SKS_KV_BF16) xs = f16_bits_to_float(Xsbh[min(row0 + lane, j_hi - 1)]);
   };
   auto tile_row = [&](int it) { return j0 + it * (SM_TILE * SM_THREADS / 64) + wave * SM_TILE; };
   sk_u32x4_t cur[4][4], nxt[4][4];
@@ -154,6 +185,8 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
       for (int c = 0; c < 4; ++c) {
         if constexpr (DT == SKS_KV_BF16) {
           a[m][c] = cur[m][c];
+        } else if constexpr (DT == SKS_KV_I4) {
+          a[m][c] = i4x8_bf16(cur[m][0][c]);
         } else {
           const uint32_t x0 = cur[m][c][0], x1 = cur[m][c][1];
           a[m][c] = sk_u32x4_t{i8pair_bf16(x0, 0), i8pair_bf16(x0, 16), i8pair_bf16(x1, 0),
@@ -183,7 +216,7 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = 16 * m + 4 * g + j;
-        const float sc = DT == SKS_KV_I8 ? __shfl(xs, rr) : 1.f;
+        const float sc = DT != SKS_KV_BF16 ? __shfl(xs, rr) : 1.f;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
           st[rr * RANK + 16 * nb + n] = (uint8_t)quant_code(acc[m][nb][j] * sc, kscale);
@@ -270,6 +303,11 @@ __device__ void sketch_row_wave(const void *__restrict__ K, const void *__restri
       const uint32_t w = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(K) + row * D)[lane];
       x0 = bf16_lo(w);
       x1 = bf16_hi(w);
+    } else if (DT == SKS_KV_I4) {
+      const uint32_t w = (static_cast<const uint8_t *>(K) + row * (D / 2))[lane];
+      const float sc = f16_bits_to_float(Ks[row]);
+      x0 = (float)((int32_t)(w << 28) >> 28) * sc;
+      x1 = (float)((int32_t)(w << 24) >> 28) * sc;
     } else {
       const uint16_t w = reinterpret_cast<const uint16_t *>(static_cast<const int8_t *>(K) + row * D)[lane];
       const float sc = f16_bits_to_float(Ks[row]);
@@ -390,26 +428,33 @@ hipError_t launch_sketch_keys(const sks_kv &kv, const Shape &s, const float *bas
   if (nrows <= SMALL_ROWS) {
     // few rows per (b, h): one wave per row
     dim3 g2((unsigned)nrows, s.B * s.Hkv);
+#define SKS_ROWS_SMALL(DT)                                                                         \
+  sketch_rows_small_kernel<DT><<<g2, 64, 0, st>>>(kv.K, kv.V, kv.K_scale, kv.seq_len, basis,      \
+                                                  basis_per_head, key_scale, s.Hkv, s.T_max, s.R, \
+                                                  s.NB, s.pool, append, t_begin, t_end, S, Kp, Vp)
     if (s.dtype == SKS_KV_BF16)
-      sketch_rows_small_kernel<SKS_KV_BF16><<<g2, 64, 0, st>>>(
-          kv.K, kv.V, nullptr, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max, s.R,
-          s.NB, s.pool, append, t_begin, t_end, S, Kp, Vp);
+      SKS_ROWS_SMALL(SKS_KV_BF16);
+    else if (s.dtype == SKS_KV_I8)
+      SKS_ROWS_SMALL(SKS_KV_I8);
     else
-      sketch_rows_small_kernel<SKS_KV_I8><<<g2, 64, 0, st>>>(
-          kv.K, kv.V, kv.K_scale, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max,
-          s.R, s.NB, s.pool, append, t_begin, t_end, S, Kp, Vp);
+      SKS_ROWS_SMALL(SKS_KV_I4);
+#undef SKS_ROWS_SMALL
     return hipGetLastError();
   }
   dim3 grid(ceil_div(nrows, SM_ROWS), s.B * s.Hkv);
   if (s.pool == 1) {
+#define SKS_MFMA(DT)                                                                              \
+  sketch_mfma_kernel<DT><<<grid, SM_THREADS, 0, st>>>(kv.K, kv.K_scale, s.T_max, kv.seq_len,     \
+                                                      basis, basis_per_head, key_scale, s.Hkv,   \
+                                                      s.T_max, s.R, s.NB, 1, append, t_begin,    \
+                                                      t_end, S)
     if (s.dtype == SKS_KV_BF16)
-      sketch_mfma_kernel<SKS_KV_BF16><<<grid, SM_THREADS, 0, st>>>(
-          kv.K, nullptr, s.T_max, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max,
-          s.R, s.NB, 1, append, t_begin, t_end, S);
+      SKS_MFMA(SKS_KV_BF16);
+    else if (s.dtype == SKS_KV_I8)
+      SKS_MFMA(SKS_KV_I8);
     else
-      sketch_mfma_kernel<SKS_KV_I8><<<grid, SM_THREADS, 0, st>>>(
-          kv.K, kv.K_scale, s.T_max, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv,
-          s.T_max, s.R, s.NB, 1, append, t_begin, t_end, S);
+      SKS_MFMA(SKS_KV_I4);
+#undef SKS_MFMA
   } else {
     dim3 gp(ceil_div(nrows, PM_BLOCKS), s.B * s.Hkv);
     pool_mean_kernel<<<gp, PM_THREADS, 0, st>>>(
@@ -433,14 +478,18 @@ hipError_t launch_step_prologue(const uint16_t *q, int Hq, const sks_kv &kv, con
   if (nrows > SMALL_ROWS) return hipErrorInvalidValue;
   const int nq = s.B * s.R * s.Hkv;
   const unsigned grid = (unsigned)(nq + nrows * s.B * s.Hkv);
+#define SKS_PROLOGUE(DT)                                                                          \
+  step_prologue_kernel<DT><<<grid, 64, 0, st>>>(q, Hq, kv.K, kv.V, kv.K_scale, kv.seq_len, basis, \
+                                                basis_per_head, key_scale, s.Hkv, s.T_max, s.R,   \
+                                                s.NB, s.pool, nq, (int)nrows, qsk, qscale, S, Kp, \
+                                                Vp)
   if (s.dtype == SKS_KV_BF16)
-    step_prologue_kernel<SKS_KV_BF16><<<grid, 64, 0, st>>>(
-        q, Hq, kv.K, kv.V, nullptr, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max,
-        s.R, s.NB, s.pool, nq, (int)nrows, qsk, qscale, S, Kp, Vp);
+    SKS_PROLOGUE(SKS_KV_BF16);
+  else if (s.dtype == SKS_KV_I8)
+    SKS_PROLOGUE(SKS_KV_I8);
   else
-    step_prologue_kernel<SKS_KV_I8><<<grid, 64, 0, st>>>(
-        q, Hq, kv.K, kv.V, kv.K_scale, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv,
-        s.T_max, s.R, s.NB, s.pool, nq, (int)nrows, qsk, qscale, S, Kp, Vp);
+    SKS_PROLOGUE(SKS_KV_I4);
+#undef SKS_PROLOGUE
   return hipGetLastError();
 }
 

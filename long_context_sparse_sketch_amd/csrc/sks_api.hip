@@ -52,7 +52,8 @@ int check_shape(const sks_kv *kv, const sks_params *p, sks::Shape &s) {
   REQUIRE(kv->D == SKS_HEAD_DIM, "D must be %d (got %d)", SKS_HEAD_DIM, kv->D);
   REQUIRE(p->rank == SKS_RANK, "rank must be %d (got %d)", SKS_RANK, p->rank);
   REQUIRE(kv->B >= 1 && kv->Hkv >= 1, "B and Hkv must be >= 1 (got %d, %d)", kv->B, kv->Hkv);
-  REQUIRE(kv->dtype == SKS_KV_BF16 || kv->dtype == SKS_KV_I8, "unknown KV dtype %d", kv->dtype);
+  REQUIRE(kv->dtype == SKS_KV_BF16 || kv->dtype == SKS_KV_I8 || kv->dtype == SKS_KV_I4,
+          "unknown KV dtype %d", kv->dtype);
   REQUIRE(p->rows >= 1 && p->rows <= SKS_MAX_ROWS, "rows must be in [1, %d] (got %d)",
           SKS_MAX_ROWS, p->rows);
   REQUIRE(kv->T_max >= p->rows, "T_max (%d) must be >= rows (%d)", kv->T_max, p->rows);
@@ -84,7 +85,7 @@ int check_shape(const sks_kv *kv, const sks_params *p, sks::Shape &s) {
 int check_cache(const sks_kv *kv, bool need_v) {
   REQUIRE_PTR(kv->K, 16);
   if (need_v) REQUIRE_PTR(kv->V, 16);
-  if (kv->dtype == SKS_KV_I8) {
+  if (kv->dtype != SKS_KV_BF16) {
     REQUIRE_PTR(kv->K_scale, 2);
     if (need_v) REQUIRE_PTR(kv->V_scale, 2);
   }
@@ -242,7 +243,7 @@ int sks_gather_pack(const sks_kv *kv, const sks_params *p, const int32_t *idx, c
     REQUIRE_PTR(Kp, 16);
     REQUIRE_PTR(Vp, 16);
   }
-  if (s.dtype == SKS_KV_I8) {
+  if (s.dtype != SKS_KV_BF16) {
     REQUIRE_PTR(Ks_out, 2);
     REQUIRE_PTR(Vs_out, 2);
   } else {

@@ -39,11 +39,11 @@ class GpuCase:
         B = case.B
         T = case.K.shape[2]
         self.T = T
-        i8 = cfg.kv_dtype == C.KV_I8
-        self.K = to_device(case.K, bf16=True) if not i8 else torch.from_numpy(case.K).cuda()
-        self.V = to_device(case.V, bf16=True) if not i8 else torch.from_numpy(case.V).cuda()
-        self.Ks = to_device(case.K_scale) if i8 else None
-        self.Vs = to_device(case.V_scale) if i8 else None
+        codes = cfg.kv_dtype != C.KV_BF16      # int8 codes, or packed int4 bytes
+        self.K = to_device(case.K, bf16=True) if not codes else torch.from_numpy(case.K).cuda()
+        self.V = to_device(case.V, bf16=True) if not codes else torch.from_numpy(case.V).cuda()
+        self.Ks = to_device(case.K_scale) if codes else None
+        self.Vs = to_device(case.V_scale) if codes else None
         sl = case.seq_len if seq_len is None else np.asarray(seq_len, np.int32)
         self.seq_len_np = sl
         self.seq_len = torch.from_numpy(sl.copy()).cuda()

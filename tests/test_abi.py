@@ -61,6 +61,8 @@ def call_attn(L, k, p, Hq=8, ws_bytes=1 << 30, q=FAKE, out=FAKE, idx=FAKE, ws=FA
     (dict(sl=0), sks.SKS_ERR_ARG, "seq_len"),
     (dict(dtype=7), sks.SKS_ERR_ARG, "dtype"),
     (dict(dtype=sks.KV_I8), sks.SKS_ERR_ARG, "K_scale"),
+    (dict(dtype=sks.KV_I4), sks.SKS_ERR_ARG, "K_scale"),
+    (dict(dtype=sks.KV_I4, Ks=FAKE), sks.SKS_ERR_ARG, "V_scale"),
 ])
 def test_cache_description_errors(L, mut, code, word):
     k = kv(**mut)
@@ -93,8 +95,9 @@ def test_workspace_errors(L):
     assert rc == sks.SKS_ERR_WORKSPACE
 
 
-def test_unsupported_int8_pooling(L):
-    k = kv(dtype=sks.KV_I8, Ks=FAKE, Vs=FAKE)
+@pytest.mark.parametrize("dtype", [sks.KV_I8, sks.KV_I4])
+def test_unsupported_code_cache_pooling(L, dtype):
+    k = kv(dtype=dtype, Ks=FAKE, Vs=FAKE)
     rc = call_attn(L, k, sks.params(64, 32, pool=4))
     assert rc == sks.SKS_ERR_UNSUPPORTED
 

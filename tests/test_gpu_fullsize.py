@@ -29,7 +29,8 @@ def sample_pairs(cfg):
     return sorted({(0, 0), (B - 1, H - 1), (B // 2, H // 2)})
 
 
-@pytest.mark.parametrize("cfg", [C.C2, C.C3, C.C4, C.C5], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C.C2, C.C3, C.C4, C.C5, C.with_kv(C.C3, C.KV_I4)],
+                         ids=lambda c: c.name)
 def test_full_size_sampled_parity(cfg):
     flush(f"[full] {cfg.name}: generating {cfg.B} x {cfg.L}")
     case = make_case(cfg)

@@ -16,7 +16,9 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("cfg,parts,streams", [(C.small(C.C3), 2, 2), (C.small(C.C5), 2, 1),
-                                               (C.small(C.C4), 2, 2)], ids=lambda x: str(x))
+                                               (C.small(C.C4), 2, 2),
+                                               (C.with_kv(C.small(C.C5), C.KV_I4), 2, 1)],
+                         ids=lambda x: str(x))
 def test_streams_and_graph_replays_match_eager(cfg, parts, streams):
     flush(f"[graph] {cfg.name} parts={parts} streams={streams}")
     case = make_case(cfg)

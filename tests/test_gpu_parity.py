@@ -15,7 +15,9 @@ from tests.gpu_util import (GpuCase, assert_attn_close, flush, lse_close, oracle
 
 pytestmark = pytest.mark.gpu
 
-CFGS = [C.C1, C.small(C.C2), C.small(C.C3), C.small(C.C4), C.small(C.C5)]
+CFGS = [C.C1, C.small(C.C2), C.small(C.C3), C.small(C.C4), C.small(C.C5),
+        C.with_kv(C.C1, C.KV_I4), C.with_kv(C.small(C.C3), C.KV_I4),
+        C.with_kv(C.small(C.C5), C.KV_I4)]
 
 
 @pytest.fixture(scope="module", params=CFGS, ids=lambda c: c.name)
@@ -126,9 +128,9 @@ def test_gather_pack_given_oracle_idx(ctx):
     cfg, case, g, ref, arr = ctx
     B, R, Hkv = case.B, cfg.R, cfg.Hkv
     Cn = g.topk + g.window + g.pool - 1
-    i8 = cfg.kv_dtype == C.KV_I8
-    dt = torch.int8 if i8 else torch.bfloat16
-    Ko = torch.zeros((B, R, Hkv, Cn, 128), dtype=dt, device="cuda")
+    i8 = cfg.kv_dtype != C.KV_BF16              # int8 codes or packed int4 bytes
+    dt = {C.KV_BF16: torch.bfloat16, C.KV_I8: torch.int8, C.KV_I4: torch.uint8}[cfg.kv_dtype]
+    Ko = torch.zeros((B, R, Hkv, Cn, case.K.shape[-1]), dtype=dt, device="cuda")
     Vo = torch.zeros_like(Ko)
     Kso = torch.zeros((B, R, Hkv, Cn), dtype=torch.int16, device="cuda") if i8 else None
     Vso = torch.zeros_like(Kso) if i8 else None
