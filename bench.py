@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--config", default="multi_agent_250k")
     ap.add_argument("--kv", choices=("bf16", "int8", "int4"), default=None,
                     help="store the workload's KV cache in another format (default: its own)")
+    ap.add_argument("--host-kv", action="store_true",
+                    help="keep the full K/V in pinned host memory (read over PCIe for the "
+                         "selected rows) with the window in a device ring")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -175,13 +178,36 @@ def main():
     basis = torch.from_numpy(case.basis).to(dev)
     kscale = torch.from_numpy(case.key_scale).to(dev)
 
+    W_hot = cfg.window + cfg.R
+    if args.host_kv:
+        # full cache in pinned host memory; the window (and the rows' own
+        # tokens) in a device ring of W_hot slots, position p in slot p % W_hot
+        if cfg.pool > 1:
+            raise SystemExit("--host-kv needs an unpooled workload")
+        def ring_of(t):
+            if t is None:
+                return None
+            end = int(case.seq_len[0]) + cfg.R - 1       # equal lengths in the workloads
+            pos = torch.arange(max(0, end - W_hot), end, device=dev)
+            r = torch.zeros((t.shape[0], t.shape[1], W_hot) + tuple(t.shape[3:]), dtype=t.dtype,
+                            device=dev)
+            r[:, :, pos % W_hot] = t[:, :, pos]
+            return r
+        hot0 = tuple(ring_of(t) for t in (K0, V0, Ks0, Vs0))
+        K0, V0, Ks0, Vs0 = (None if t is None else t.cpu().pin_memory() for t in (K0, V0, Ks0, Vs0))
+        torch.cuda.synchronize()
+    copy = (lambda t: t.clone().pin_memory()) if args.host_kv else (lambda t: t.clone())
+
     layers = []
     for r in range(args.replicas):
-        K = K0 if r == 0 else K0.clone()
-        V = V0 if r == 0 else V0.clone()
-        Ks = Ks0 if (r == 0 or Ks0 is None) else Ks0.clone()
-        Vs = Vs0 if (r == 0 or Vs0 is None) else Vs0.clone()
-        cache = sks.Cache(K, V, sl, Ks, Vs)
+        K = K0 if r == 0 else copy(K0)
+        V = V0 if r == 0 else copy(V0)
+        Ks = Ks0 if (r == 0 or Ks0 is None) else copy(Ks0)
+        Vs = Vs0 if (r == 0 or Vs0 is None) else copy(Vs0)
+        hot = None
+        if args.host_kv:
+            hot = tuple(None if t is None else (t if r == 0 else t.clone()) for t in hot0)
+        cache = sks.Cache(K, V, sl, Ks, Vs, hot=hot)
         lay = SparseDecodeLayer(cfg.B, cfg.R, cfg.Hq, cfg.Hkv, cfg.T_max, cfg.window, cfg.topk,
                                 cfg.pool, cfg.kv_dtype, dev).bind(cache, basis, kscale)
         lay.build_sketch(0, cfg.T_max)
@@ -315,6 +341,10 @@ def main():
 
     ms_per_step = total_ms / args.steps
     sketch_b, gather_b, small_b = algorithmic_bytes(cfg)
+    # bytes of the selected far rows (K and V, with their scales): what crosses
+    # PCIe with a host tier
+    row_b = cfg.kv_row_bytes + (0 if cfg.kv_dtype == C.KV_BF16 else 2)
+    selected_b = sum(cfg.B * cfg.Hkv * min(cfg.topk, cfg.n_far(i)) * 2 * row_b for i in range(cfg.R))
     achieved = sketch_b / (score_avg_ms * 1e-3) / 1e9
     line = {
         "metric": "decode-attn steps/s and achieved HBM GB/s (% peak) at 250K ctx, top-k 2048",
@@ -329,7 +359,8 @@ def main():
         "vs_baseline": None,
         "dtype": f"i8 sketch / {C.KV_NAMES[cfg.kv_dtype]} KV / f32 accumulate",
         "data": "synthetic (seeded N(0,1) caches with planted needles)",
-        "config": {"workload": cfg.name, "batch": cfg.B, "context": cfg.L, "rows": cfg.R,
+        "config": {"workload": cfg.name + ("+host_kv" if args.host_kv else ""), "batch": cfg.B,
+                   "context": cfg.L, "rows": cfg.R,
                    "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "window": cfg.window,
                    "topk": cfg.topk, "pool": cfg.pool, "replicas": args.replicas,
                    "schedule": ("five C-ABI calls" if args.five_calls else "sks_decode_step")
@@ -347,6 +378,10 @@ def main():
             "attn_avg_ms": attn_avg_ms,
             "attn_GBps": gather_b / (attn_avg_ms * 1e-3) / 1e9,
             "gather_pack_avg_ms": gather_avg_ms,
+            "kv_tier": (f"host (pinned host K/V, device ring of {W_hot} slots)" if args.host_kv
+                        else "device"),
+            "host_selected_bytes": selected_b if args.host_kv else None,
+            "attn_host_GBps": (selected_b / (attn_avg_ms * 1e-3) / 1e9 if args.host_kv else None),
             "gather_pack_GBps": 2 * gather_b / (gather_avg_ms * 1e-3) / 1e9,
             "step_ms_spread": spread,
             "score_plus_attn_GBps": (sketch_b + gather_b) / ((score_avg_ms + attn_avg_ms) * 1e-3) / 1e9,

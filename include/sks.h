@@ -95,6 +95,22 @@ typedef struct sks_kv {
   const uint16_t *K_scale;  /* [B][Hkv][T_max] fp16 bits, int8/int4, else NULL  */
   const uint16_t *V_scale;  /* [B][Hkv][T_max] fp16 bits, int8/int4, else NULL  */
   const int32_t *seq_len;   /* [B] device: L of query row 0 (own token included) */
+  /* Hot tier (optional, all NULL / 0 without one).  "8 agents x 250K
+   * context ...", claims list: the full KV cache lives in host RAM, the GPU
+   * keeps the sketch and a small hot set, and only the picked tokens cross
+   * PCIe.  With a hot tier, K, V (and their scales) may be pinned host memory
+   * mapped into the device's address space (pass the device address, e.g.
+   * from hipHostGetDevicePointer); they are then read only for the selected
+   * far rows and for host-range key sketch builds.  The exact window and the
+   * rows' own tokens (APPEND) are read from the ring below, in which
+   * position p sits in slot p % W_hot.  The caller keeps the ring current:
+   * it must hold every position in [L_0 + rows - 1 - W_hot, L_0 + rows - 1).
+   * Needs pool == 1 (SKS_ERR_UNSUPPORTED otherwise). */
+  const void *K_hot;        /* [B][Hkv][W_hot][row] same format as K, or NULL   */
+  const void *V_hot;        /* [B][Hkv][W_hot][row]                             */
+  const uint16_t *K_hot_scale; /* [B][Hkv][W_hot] fp16 bits, int8/int4, else NULL */
+  const uint16_t *V_hot_scale; /* [B][Hkv][W_hot]                               */
+  int32_t W_hot;            /* ring slots, window + rows <= W_hot <= T_max      */
 } sks_kv;
 
 /* Selection parameters of the step. */

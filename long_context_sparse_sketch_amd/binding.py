@@ -40,7 +40,10 @@ class KVDesc(ctypes.Structure):
                 ("T_max", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("K", ctypes.c_void_p), ("V", ctypes.c_void_p),
                 ("K_scale", ctypes.c_void_p), ("V_scale", ctypes.c_void_p),
-                ("seq_len", ctypes.c_void_p)]
+                ("seq_len", ctypes.c_void_p),
+                ("K_hot", ctypes.c_void_p), ("V_hot", ctypes.c_void_p),
+                ("K_hot_scale", ctypes.c_void_p), ("V_hot_scale", ctypes.c_void_p),
+                ("W_hot", ctypes.c_int32)]
 
 
 class Params(ctypes.Structure):
@@ -94,6 +97,9 @@ def lib():
                                              vp, vp, sz, vp]
         L.sks_decode_step.restype = ctypes.c_int
         L.sks_decode_step.argtypes = [kvp, pp, ctypes.POINTER(StepDesc), i32, vp, sz, vp]
+        # the HIP runtime the library runs on (one of its dependencies)
+        L.hipHostGetDevicePointer.restype = ctypes.c_int
+        L.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(vp), vp, ctypes.c_uint]
         _LIB = L
     return _LIB
 
@@ -111,6 +117,24 @@ def ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def device_address(t) -> int | None:
+    """Address under which the GPU reaches tensor `t`: its data pointer for a
+    device tensor; for a pinned host tensor the device address of its pinned
+    allocation (hipHostGetDevicePointer) plus the tensor's offset in it."""
+    if t is None:
+        return None
+    if t.is_cuda:
+        return t.data_ptr()
+    if not t.is_pinned():
+        raise ValueError("a host tensor handed to the GPU must be pinned (pin_memory=True)")
+    base = t.untyped_storage().data_ptr()
+    dev = ctypes.c_void_p()
+    rc = lib().hipHostGetDevicePointer(ctypes.byref(dev), ctypes.c_void_p(base), 0)
+    if rc != 0 or not dev.value:
+        raise SksError(SKS_ERR_HIP, f"hipHostGetDevicePointer failed ({rc})")
+    return dev.value + (t.data_ptr() - base)
+
+
 def _stream(stream):
     if stream is not None:
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
@@ -118,17 +142,30 @@ def _stream(stream):
 
 
 class Cache:
-    """Descriptor of one layer's KV cache; keeps the tensors alive."""
+    """Descriptor of one layer's KV cache; keeps the tensors alive.
 
-    def __init__(self, K, V, seq_len, K_scale=None, V_scale=None):
+    K, V (and scales) may be device tensors or, with a hot tier, pinned host
+    tensors.  hot = (K_hot, V_hot, K_hot_scale, V_hot_scale): the ring of the
+    last W_hot positions in device memory, [B][Hkv][W_hot][row], position p
+    in slot p % W_hot (scales None for bf16)."""
+
+    def __init__(self, K, V, seq_len, K_scale=None, V_scale=None, hot=None):
         self.K, self.V, self.seq_len, self.K_scale, self.V_scale = K, V, seq_len, K_scale, V_scale
+        self.hot = hot
         B, Hkv, T, D = K.shape
         # int8 codes as torch.int8; packed int4 rows (64 bytes) as torch.uint8
         dtype = {torch.int8: KV_I8, torch.uint8: KV_I4}.get(K.dtype, KV_BF16)
         if dtype == KV_I4:
             D *= 2
-        self.desc = KVDesc(B, Hkv, D, T, dtype, ptr(K), ptr(V), ptr(K_scale), ptr(V_scale),
-                           ptr(seq_len))
+        if hot is None:
+            hk = hv = hks = hvs = None
+            W_hot = 0
+        else:
+            hk, hv, hks, hvs = hot
+            W_hot = hk.shape[2]
+        da = device_address
+        self.desc = KVDesc(B, Hkv, D, T, dtype, da(K), da(V), da(K_scale), da(V_scale),
+                           ptr(seq_len), ptr(hk), ptr(hv), ptr(hks), ptr(hvs), W_hot)
 
     @property
     def ref(self):

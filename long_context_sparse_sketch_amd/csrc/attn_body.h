@@ -7,6 +7,7 @@
 #include <type_traits>
 
 #include "sks_internal.h"
+#include "tier.h"
 
 namespace sks {
 namespace {
@@ -170,8 +171,11 @@ __device__ void merge_splits(const float2 *part_ml, const float *part_acc, int s
 // combines the slots in this order.
 struct AttnArgs {
   const uint16_t *q;
-  const void *K, *V;
+  const void *K, *V;                  // full cache (selected far rows)
   const uint16_t *Ks, *Vs;
+  const void *Kh, *Vh;                // window rows: hot ring of W_hot slots (or the full cache)
+  const uint16_t *Ksh, *Vsh;
+  int W_hot;
   const int32_t *seq_len, *idx;
   const uint16_t *Kp, *Vp;
   float sm_log2;
@@ -224,14 +228,16 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   const RowGeom rg = row_geom(L0, i, window, pool, topk);
   const int e_hi = min((slot + 1) * ATTN_SPLIT, rg.n_ent);   // end of this slot's entries
 
-  // Descriptor of an entry: the row to gather (an index into the token rows,
-  // or the pooled rows when bit 1 of the flag is set) and whether it takes
-  // part.  Invalid entries point at row 0, which always exists, so the
-  // gathers below need no branches.  Lane l holds entries e_wave + l (row0,
-  // flag0) and e_wave + 64 + l (row1, flag1).
+  // Descriptor of an entry: the row to gather and whether it takes part
+  // (bit 0).  The row indexes the token rows of the full cache, the pooled
+  // rows when bit 1 is set, or the slots of the hot ring when bit 2 is set
+  // (window rows).  Invalid entries point at ring slot 0, which always
+  // exists, so the gathers below need no branches.  Lane l holds entries
+  // e_wave + l (row0, flag0) and e_wave + 64 + l (row1, flag1).
+  const int W_hot = a.W_hot;
   auto describe = [&](int e, int sel, int &row, int &flag) {
     row = 0;
-    flag = 0;
+    flag = 4;
     if (e >= e_hi) {
       // past this slot: masked
     } else if (e < rg.k_eff) {
@@ -240,8 +246,9 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
         flag = POOLED ? 3 : 1;
       }
     } else if (e < rg.n_ent) {
-      row = rg.ws + (e - rg.k_eff);
-      flag = 1;
+      // (pooled caches have no hot tier: the ring is the full cache)
+      row = POOLED ? rg.ws + (e - rg.k_eff) : hot_slot(rg.ws + (e - rg.k_eff), W_hot);
+      flag = 5;
     }
   };
   int row0, flag0, row1, flag1;
@@ -287,11 +294,14 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   // int8 / int4 caches: each lane's entries' row scales, with the descriptors
   float ksd0 = 1.f, vsd0 = 1.f, ksd1 = 1.f, vsd1 = 1.f;
   if constexpr (DT != SKS_KV_BF16) {
-    const size_t sbase = ((size_t)b * Hkv + h) * T_max;
-    ksd0 = f16_bits_to_float(Ks[sbase + row0]);
-    vsd0 = f16_bits_to_float(Vs[sbase + row0]);
-    ksd1 = f16_bits_to_float(Ks[sbase + row1]);
-    vsd1 = f16_bits_to_float(Vs[sbase + row1]);
+    const uint16_t *Kst = Ks + ((size_t)b * Hkv + h) * T_max;
+    const uint16_t *Vst = Vs + ((size_t)b * Hkv + h) * T_max;
+    const uint16_t *Ksht = a.Ksh + ((size_t)b * Hkv + h) * W_hot;
+    const uint16_t *Vsht = a.Vsh + ((size_t)b * Hkv + h) * W_hot;
+    ksd0 = f16_bits_to_float(((flag0 & 4) ? Ksht : Kst)[row0]);
+    vsd0 = f16_bits_to_float(((flag0 & 4) ? Vsht : Vst)[row0]);
+    ksd1 = f16_bits_to_float(((flag1 & 4) ? Ksht : Kst)[row1]);
+    vsd1 = f16_bits_to_float(((flag1 & 4) ? Vsht : Vst)[row1]);
   }
 
   // int4: the K operand is code + I4_BIAS, so each logit carries
@@ -321,6 +331,8 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   constexpr int RB = DT == SKS_KV_BF16 ? 2 * D : DT == SKS_KV_I8 ? D : D / 2;   // row bytes
   const char *Kt = static_cast<const char *>(K) + ((size_t)b * Hkv + h) * T_max * RB;
   const char *Vt = static_cast<const char *>(V) + ((size_t)b * Hkv + h) * T_max * RB;
+  const char *Kht = static_cast<const char *>(a.Kh) + ((size_t)b * Hkv + h) * W_hot * RB;
+  const char *Vht = static_cast<const char *>(a.Vh) + ((size_t)b * Hkv + h) * W_hot * RB;
   const char *Kpb = reinterpret_cast<const char *>(Kp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
   const char *Vpb = reinterpret_cast<const char *>(Vp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
   uint16_t *sv = s_v[wave];
@@ -357,7 +369,7 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
       int r, f;
       desc(j, r, f);
       d.f[t] = f;
-      const char *kbase = (POOLED && (f & 2)) ? Kpb : Kt;
+      const char *kbase = (POOLED && (f & 2)) ? Kpb : (!POOLED && (f & 4)) ? Kht : Kt;
       const size_t off = (size_t)r * RB;
       if constexpr (Q) {
         d.k[t][0] = ld(kbase + off + 16 * g);
@@ -375,7 +387,7 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
       const int ev = x >> VSH, c = x & ((1 << VSH) - 1);
       int r, f;
       desc(tile * AM_TILE + ev, r, f);
-      const char *vbase = (POOLED && (f & 2)) ? Vpb : Vt;
+      const char *vbase = (POOLED && (f & 2)) ? Vpb : (!POOLED && (f & 4)) ? Vht : Vt;
       d.v[qq] = ld(vbase + (size_t)r * RB + c * 16);
     }
   };

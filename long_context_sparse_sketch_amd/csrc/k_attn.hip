@@ -63,6 +63,12 @@ AttnArgs attn_args(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
   a.V = kv.V;
   a.Ks = kv.K_scale;
   a.Vs = kv.V_scale;
+  const HotRows hr = hot_rows(kv);
+  a.Kh = hr.K;
+  a.Vh = hr.V;
+  a.Ksh = hr.Ks;
+  a.Vsh = hr.Vs;
+  a.W_hot = hr.W;
   a.seq_len = kv.seq_len;
   a.idx = idx;
   a.Kp = Kp;

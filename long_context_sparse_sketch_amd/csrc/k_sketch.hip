@@ -9,6 +9,7 @@
 // Bulk builds run on the matrix cores (sketch_mfma_kernel, below); the few
 // rows of a step's append take one wave per row (sketch_rows_small_kernel).
 #include "sks_internal.h"
+#include "tier.h"
 
 namespace sks {
 namespace {
@@ -279,10 +280,13 @@ __global__ __launch_bounds__(PM_THREADS) void pool_mean_kernel(
 // Few rows per (b, h) -- the per-step append of the rows' own tokens: one
 // wave per sketch row.  The 128-element key (or pooled block) is staged in
 // LDS, lane c dots basis row c with it, so the latency is that of one row
-// instead of one lane walking all 64 x 128 products.
+// instead of one lane walking all 64 x 128 products.  Appended tokens
+// (pool == 1) are read from the hot ring Kh (slot = position % W_hot; the
+// full cache itself when there is no hot tier).
 template <int DT>
 __device__ void sketch_row_wave(const void *__restrict__ K, const void *__restrict__ V,
-                                const uint16_t *__restrict__ Ks,
+                                const uint16_t *__restrict__ Ks, const void *__restrict__ Kh,
+                                const uint16_t *__restrict__ Ksh, int W_hot,
                                 const int32_t *__restrict__ seq_len,
                                 const float *__restrict__ basis, int basis_per_head,
                                 const float *__restrict__ key_scale, int Hkv, int T_max, int R,
@@ -297,7 +301,11 @@ __device__ void sketch_row_wave(const void *__restrict__ K, const void *__restri
   if (j >= j_hi) return;
   const int lane = threadIdx.x;
   if (pool == 1) {
-    const size_t row = (size_t)bh * T_max + j;
+    if (append) {
+      K = Kh;
+      Ks = Ksh;
+    }
+    const size_t row = append ? (size_t)bh * W_hot + hot_slot(j, W_hot) : (size_t)bh * T_max + j;
     float x0, x1;
     if (DT == SKS_KV_BF16) {
       const uint32_t w = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(K) + row * D)[lane];
@@ -350,12 +358,14 @@ __device__ void sketch_row_wave(const void *__restrict__ K, const void *__restri
 template <int DT>
 __global__ __launch_bounds__(64) void sketch_rows_small_kernel(
     const void *__restrict__ K, const void *__restrict__ V, const uint16_t *__restrict__ Ks,
+    const void *__restrict__ Kh, const uint16_t *__restrict__ Ksh, int W_hot,
     const int32_t *__restrict__ seq_len, const float *__restrict__ basis, int basis_per_head,
     const float *__restrict__ key_scale, int Hkv, int T_max, int R, int NB, int pool, int append,
     int t_begin, int t_end, int8_t *__restrict__ S, uint16_t *__restrict__ Kp,
     uint16_t *__restrict__ Vp) {
-  sketch_row_wave<DT>(K, V, Ks, seq_len, basis, basis_per_head, key_scale, Hkv, T_max, R, NB, pool,
-                      append, t_begin, t_end, S, Kp, Vp, blockIdx.y, blockIdx.x);
+  sketch_row_wave<DT>(K, V, Ks, Kh, Ksh, W_hot, seq_len, basis, basis_per_head, key_scale, Hkv,
+                      T_max, R, NB, pool, append, t_begin, t_end, S, Kp, Vp, blockIdx.y,
+                      blockIdx.x);
 }
 
 // Query sketch: one wave per (b, i, h).  qbar = mean of the group's queries
@@ -399,8 +409,8 @@ __global__ __launch_bounds__(64) void sketch_query_kernel(
 template <int DT>
 __global__ __launch_bounds__(64) void step_prologue_kernel(
     const uint16_t *__restrict__ q, int Hq, const void *__restrict__ K,
-    const void *__restrict__ V, const uint16_t *__restrict__ Ks,
-    const int32_t *__restrict__ seq_len, const float *__restrict__ basis, int basis_per_head,
+    const void *__restrict__ V, const uint16_t *__restrict__ Ks, const void *__restrict__ Kh,
+    const uint16_t *__restrict__ Ksh, int W_hot, const int32_t *__restrict__ seq_len, const float *__restrict__ basis, int basis_per_head,
     const float *__restrict__ key_scale, int Hkv, int T_max, int R, int NB, int pool, int nq,
     int nrows, int8_t *__restrict__ qsk, float *__restrict__ qscale, int8_t *__restrict__ S,
     uint16_t *__restrict__ Kp, uint16_t *__restrict__ Vp) {
@@ -409,8 +419,8 @@ __global__ __launch_bounds__(64) void step_prologue_kernel(
     return;
   }
   const int w = blockIdx.x - nq;
-  sketch_row_wave<DT>(K, V, Ks, seq_len, basis, basis_per_head, key_scale, Hkv, T_max, R, NB, pool,
-                      1, 0, 0, S, Kp, Vp, w / nrows, w % nrows);
+  sketch_row_wave<DT>(K, V, Ks, Kh, Ksh, W_hot, seq_len, basis, basis_per_head, key_scale, Hkv,
+                      T_max, R, NB, pool, 1, 0, 0, S, Kp, Vp, w / nrows, w % nrows);
 }
 
 }  // namespace
@@ -425,13 +435,15 @@ hipError_t launch_sketch_keys(const sks_kv &kv, const Shape &s, const float *bas
   if (span <= 0) return hipSuccess;
   long nrows = s.pool == 1 ? span : span / s.pool + 1;
   if (nrows > s.NB) nrows = s.NB;
-  if (nrows <= SMALL_ROWS) {
-    // few rows per (b, h): one wave per row
+  if (nrows <= SMALL_ROWS || append) {
+    // few rows per (b, h): one wave per row (an append is at most R + 1 rows)
     dim3 g2((unsigned)nrows, s.B * s.Hkv);
+    const HotRows hr = hot_rows(kv);
 #define SKS_ROWS_SMALL(DT)                                                                         \
-  sketch_rows_small_kernel<DT><<<g2, 64, 0, st>>>(kv.K, kv.V, kv.K_scale, kv.seq_len, basis,      \
-                                                  basis_per_head, key_scale, s.Hkv, s.T_max, s.R, \
-                                                  s.NB, s.pool, append, t_begin, t_end, S, Kp, Vp)
+  sketch_rows_small_kernel<DT><<<g2, 64, 0, st>>>(kv.K, kv.V, kv.K_scale, hr.K, hr.Ks, hr.W,     \
+                                                  kv.seq_len, basis, basis_per_head, key_scale,   \
+                                                  s.Hkv, s.T_max, s.R, s.NB, s.pool, append,      \
+                                                  t_begin, t_end, S, Kp, Vp)
     if (s.dtype == SKS_KV_BF16)
       SKS_ROWS_SMALL(SKS_KV_BF16);
     else if (s.dtype == SKS_KV_I8)
@@ -478,11 +490,12 @@ hipError_t launch_step_prologue(const uint16_t *q, int Hq, const sks_kv &kv, con
   if (nrows > SMALL_ROWS) return hipErrorInvalidValue;
   const int nq = s.B * s.R * s.Hkv;
   const unsigned grid = (unsigned)(nq + nrows * s.B * s.Hkv);
+  const HotRows hr = hot_rows(kv);
 #define SKS_PROLOGUE(DT)                                                                          \
-  step_prologue_kernel<DT><<<grid, 64, 0, st>>>(q, Hq, kv.K, kv.V, kv.K_scale, kv.seq_len, basis, \
-                                                basis_per_head, key_scale, s.Hkv, s.T_max, s.R,   \
-                                                s.NB, s.pool, nq, (int)nrows, qsk, qscale, S, Kp, \
-                                                Vp)
+  step_prologue_kernel<DT><<<grid, 64, 0, st>>>(q, Hq, kv.K, kv.V, kv.K_scale, hr.K, hr.Ks,     \
+                                                hr.W, kv.seq_len, basis, basis_per_head,          \
+                                                key_scale, s.Hkv, s.T_max, s.R, s.NB, s.pool, nq, \
+                                                (int)nrows, qsk, qscale, S, Kp, Vp)
   if (s.dtype == SKS_KV_BF16)
     SKS_PROLOGUE(SKS_KV_BF16);
   else if (s.dtype == SKS_KV_I8)

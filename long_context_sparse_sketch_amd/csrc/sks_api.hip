@@ -70,6 +70,13 @@ int check_shape(const sks_kv *kv, const sks_params *p, sks::Shape &s) {
   REQUIRE(nseg <= 65535, "B * rows * Hkv must be <= 65535 (got %ld)", nseg);
   if (p->pool > 1 && kv->dtype != SKS_KV_BF16)
     return fail(SKS_ERR_UNSUPPORTED, "pooling (pool > 1) needs a bf16 cache");
+  if (kv->K_hot || kv->V_hot || kv->K_hot_scale || kv->V_hot_scale || kv->W_hot) {
+    REQUIRE(kv->K_hot && kv->V_hot, "kv->K_hot and kv->V_hot must both be set or both NULL");
+    if (p->pool > 1) return fail(SKS_ERR_UNSUPPORTED, "a hot tier needs pool == 1");
+    REQUIRE(kv->W_hot >= p->window + p->rows && kv->W_hot <= kv->T_max,
+            "W_hot (%d) must be in [window + rows, T_max] = [%d, %d]", kv->W_hot,
+            p->window + p->rows, kv->T_max);
+  }
   s.B = kv->B;
   s.R = p->rows;
   s.Hkv = kv->Hkv;
@@ -88,6 +95,14 @@ int check_cache(const sks_kv *kv, bool need_v) {
   if (kv->dtype != SKS_KV_BF16) {
     REQUIRE_PTR(kv->K_scale, 2);
     if (need_v) REQUIRE_PTR(kv->V_scale, 2);
+  }
+  if (kv->K_hot) {
+    REQUIRE_PTR(kv->K_hot, 16);
+    if (need_v) REQUIRE_PTR(kv->V_hot, 16);
+    if (kv->dtype != SKS_KV_BF16) {
+      REQUIRE_PTR(kv->K_hot_scale, 2);
+      if (need_v) REQUIRE_PTR(kv->V_hot_scale, 2);
+    }
   }
   return SKS_OK;
 }

@@ -80,9 +80,9 @@ class SparseDecodeLayer:
             t = getattr(self, name)
             setattr(v, name, None if t is None else t[b0:b1])
         c = self.cache
-        cache = sks.Cache(c.K[b0:b1], c.V[b0:b1], c.seq_len[b0:b1],
-                          None if c.K_scale is None else c.K_scale[b0:b1],
-                          None if c.V_scale is None else c.V_scale[b0:b1])
+        sl = lambda t: None if t is None else t[b0:b1]
+        cache = sks.Cache(c.K[b0:b1], c.V[b0:b1], c.seq_len[b0:b1], sl(c.K_scale), sl(c.V_scale),
+                          None if c.hot is None else tuple(sl(t) for t in c.hot))
         v.cache, v.ws = None, None
         v.bind(cache, self.basis, self.key_scale, self.basis_per_head)
         return v
@@ -94,7 +94,7 @@ class SparseDecodeLayer:
         nbytes = sks.workspace_bytes(cache, self.p, self.Hq)
         if nbytes == 0:
             raise sks.SksError(sks.SKS_ERR_ARG, sks.last_error())
-        self.ws = torch.empty((nbytes,), dtype=torch.uint8, device=cache.K.device)
+        self.ws = torch.empty((nbytes,), dtype=torch.uint8, device=cache.seq_len.device)
         sks.workspace_init(self.ws)          # the histogram region is zero at rest
         return self
 

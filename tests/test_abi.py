@@ -95,6 +95,37 @@ def test_workspace_errors(L):
     assert rc == sks.SKS_ERR_WORKSPACE
 
 
+def hot(k, K_hot=FAKE, V_hot=FAKE, Ks=0, Vs=0, W=200):
+    k.K_hot, k.V_hot = K_hot or None, V_hot or None
+    k.K_hot_scale, k.V_hot_scale = Ks or None, Vs or None
+    k.W_hot = W
+    return k
+
+
+@pytest.mark.parametrize("mut,p,code,word", [
+    (dict(V_hot=0), sks.params(64, 32), sks.SKS_ERR_ARG, "both"),
+    (dict(K_hot=0), sks.params(64, 32), sks.SKS_ERR_ARG, "both"),
+    (dict(W=64), sks.params(64, 32), sks.SKS_ERR_ARG, "W_hot"),
+    (dict(W=64), sks.params(63, 32, rows=2), sks.SKS_ERR_ARG, "W_hot"),   # window + rows > W_hot
+    (dict(W=1001), sks.params(64, 32), sks.SKS_ERR_ARG, "W_hot"),    # > T_max
+    (dict(K_hot=FAKE + 8), sks.params(64, 32), sks.SKS_ERR_ARG, "aligned"),
+    (dict(), sks.params(64, 32, pool=4), sks.SKS_ERR_UNSUPPORTED, "pool"),
+])
+def test_hot_tier_errors(L, mut, p, code, word):
+    k = hot(kv(), **mut)
+    assert call_attn(L, k, p) == code
+    assert word in sks.last_error()
+
+
+def test_hot_tier_scales_required_for_codes(L):
+    k = hot(kv(dtype=sks.KV_I4, Ks=FAKE, Vs=FAKE))
+    assert call_attn(L, k, sks.params(64, 32)) == sks.SKS_ERR_ARG
+    assert "K_hot_scale" in sks.last_error()
+    k = hot(kv(dtype=sks.KV_I8, Ks=FAKE, Vs=FAKE), Ks=FAKE)
+    assert call_attn(L, k, sks.params(64, 32)) == sks.SKS_ERR_ARG
+    assert "V_hot_scale" in sks.last_error()
+
+
 @pytest.mark.parametrize("dtype", [sks.KV_I8, sks.KV_I4])
 def test_unsupported_code_cache_pooling(L, dtype):
     k = kv(dtype=dtype, Ks=FAKE, Vs=FAKE)
