@@ -205,3 +205,26 @@ def make_case(cfg: Config, seqs=None, threads: int | None = None) -> Case:
             work(it)
     seq_len = np.full((B,), cfg.L, dtype=np.int32)
     return Case(cfg, seqs, basis, key_scale, q, K, V, Ks, Vs, seq_len, needles)
+
+
+_TAG_REFIT = 100
+
+
+def make_refit_keys(B: int, Hkv: int, T: int, seed: int, tau: float = 24.0, gap: float = 0.5):
+    """bf16 keys [B][Hkv][T][128] with a planted spectrum, standing in for keys
+    captured from a model (a basis refit needs keys with structure; N(0,1)
+    keys are isotropic).  Per KV head: x = U (sigma * z), z ~ N(0, I), U a
+    seeded random orthogonal matrix, sigma_i = exp(-i / tau) for i < 64 and
+    gap * exp(-i / tau) beyond.  Returns (K bits, U [Hkv][128][128], sigma)."""
+    D = 128
+    i = np.arange(D)
+    sigma = np.exp(-i / tau) * np.where(i < 64, 1.0, gap)
+    U = np.stack([np.linalg.qr(_rng(seed, _TAG_REFIT, h).standard_normal((D, D)))[0]
+                  for h in range(Hkv)])
+    K = np.empty((B, Hkv, T, D), np.uint16)
+    for b in range(B):
+        for h in range(Hkv):
+            z = _rng(seed, _TAG_REFIT + 1, b, h).standard_normal((T, D))
+            K[b, h] = f32_to_bf16_bits(((z * sigma) @ U[h].T).astype(np.float32))
+    return K, U, sigma
+

@@ -29,6 +29,13 @@ Plain NumPy, float64 for real arithmetic and int64 for integers, loops over
   0 are averaged (K and V), stored as bfloat16, and sketched from the stored
   pooled key; a tail shorter than r joins the exact window; pooled logits get
   no count bias.
+* Basis refit -- "8 agents x 250K context ...", "What it took": a frozen
+  sketch basis in one file plus a script that refits it.  Read as principal
+  directions of captured keys: the Gram matrix G = sum_t x_t x_t^T of the
+  keys, its 64 leading eigenvectors (largest eigenvalues first, each signed so
+  that its largest-magnitude component is positive) as the basis rows, and a
+  key scale max_t max_c |(P x_t)_c| / 127, so that no captured key's code
+  clips.
 * Verify rows -- "Agens SGLang", "Quick start": the verify step of speculative
   decoding is served as a chain.  Row i of a sequence sits at position L-1+i,
   sees [0, L+i) and has its own window and its own selection, so verifying is
@@ -298,3 +305,67 @@ def decode_step(q, K, V, Ks, Vs, seq_len, basis, key_scale, window: int, topk: i
         out[(b, h)] = decode_head(qf[b, :, h * g:(h + 1) * g], Kf, Vf, P,
                                   float(key_scale[h]), int(seq_len[b]), window, topk, r, sm)
     return out
+
+
+# --------------------------------------------------------------------------
+# sketch-basis refit
+# --------------------------------------------------------------------------
+def refit_keys(K, seq_len, h: int, t_begin: int, t_end: int) -> np.ndarray:
+    """Captured keys of KV head h: positions [t_begin, min(t_end, L_b)) of
+    every sequence b, bf16 bits -> float64 rows, sequences in order."""
+    rows = []
+    for b in range(K.shape[0]):
+        hi = min(int(t_end), int(seq_len[b]), K.shape[2])
+        lo = max(0, int(t_begin))
+        if hi > lo:
+            rows.append(bf16_to_f64(K[b, h, lo:hi]))
+    return np.concatenate(rows, axis=0) if rows else np.zeros((0, K.shape[3]))
+
+
+def key_gram(keys: np.ndarray) -> np.ndarray:
+    """G = sum over keys x of the outer product x x^T ([n][128] -> [128][128])."""
+    x = np.asarray(keys, np.float64)
+    return x.T @ x
+
+
+def basis_from_gram(G: np.ndarray, rank: int = 64):
+    """The `rank` leading eigenvectors of the symmetric matrix G as rows
+    (largest eigenvalue first; equal eigenvalues keep the solver's order),
+    each signed so that its largest-magnitude component (the first one on
+    ties) is positive.  Returns (basis [rank][128], eigenvalues [128]
+    descending)."""
+    w, U = np.linalg.eigh(np.asarray(G, np.float64))
+    order = np.argsort(-w, kind="stable")
+    w, U = w[order], U[:, order]
+    P = U[:, :rank].T.copy()
+    for r in range(rank):
+        k = int(np.argmax(np.abs(P[r])))
+        if P[r, k] < 0:
+            P[r] = -P[r]
+    return P, w
+
+
+def refit_key_scale(keys: np.ndarray, basis: np.ndarray) -> float:
+    """max over keys and sketch coordinates of |P x| / 127 (1.0 when every
+    projection is zero, where any scale gives all-zero codes)."""
+    if len(keys) == 0:
+        return 1.0
+    m = float(np.abs(project(keys, basis)).max())
+    return m / CODE_MAX if m > 0 else 1.0
+
+
+def refit(K, seq_len, t_begin: int, t_end: int, per_head: bool = True, rank: int = 64):
+    """Refit from a bf16 cache: per KV head (or one basis from the keys of
+    every head).  Returns (gram [n][128][128], basis [n][rank][128] float64,
+    eigenvalues [n][128], key_scale [Hkv]) with n = Hkv or 1."""
+    Hkv = K.shape[1]
+    keys = [refit_keys(K, seq_len, h, t_begin, t_end) for h in range(Hkv)]
+    grams = [key_gram(k) for k in keys]
+    if not per_head:
+        grams = [np.sum(grams, axis=0)]
+    fits = [basis_from_gram(G, rank) for G in grams]
+    basis = np.stack([f[0] for f in fits])
+    eig = np.stack([f[1] for f in fits])
+    scale = np.array([refit_key_scale(keys[h], basis[h if per_head else 0]) for h in range(Hkv)])
+    return np.stack(grams), basis, eig, scale
+

@@ -141,3 +141,27 @@ def test_caught_i4_without_sign_extension(monkeypatch):
     expect_caught(monkeypatch, "i4_unpack", bad, pins.test_i4_dequant_hand_decoded,
                   pins.test_i4_cache_reduces_to_i8_cache_with_the_same_codes)
 
+
+def test_caught_refit_ascending_order(monkeypatch):
+    def bad(G, rank=64):
+        w, U = np.linalg.eigh(np.asarray(G, np.float64))
+        return U[:, :rank].T.copy(), w
+    expect_caught(monkeypatch, "basis_from_gram", bad, pins.test_basis_from_diagonal_gram_closed_form,
+                  pins.test_basis_from_planted_gram_and_sign_convention)
+
+
+def test_caught_refit_without_sign_convention(monkeypatch):
+    def bad(G, rank=64):
+        w, U = np.linalg.eigh(np.asarray(G, np.float64))
+        order = np.argsort(-w, kind="stable")
+        return U[:, order][:, :rank].T.copy() * -1.0, w[order]
+    expect_caught(monkeypatch, "basis_from_gram", bad, pins.test_basis_from_diagonal_gram_closed_form,
+                  pins.test_basis_from_planted_gram_and_sign_convention)
+
+
+def test_caught_refit_scale_off_by_one(monkeypatch):
+    real = orc.project
+    expect_caught(monkeypatch, "refit_key_scale",
+                  lambda keys, basis: float(np.abs(real(keys, basis)).max()) / 128,
+                  pins.test_refit_key_scale_closed_form)
+
