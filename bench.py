@@ -317,6 +317,35 @@ def main():
     gather_avg_ms = e4.elapsed_time(e5) / args.steps
     del Ko, Vo, Kso, Vso
 
+    # basis refit over every cached key (off the per-step path; bf16 caches):
+    # Gram matrix, eigenvectors, key scale, each timed on its own (median of 3)
+    refit = None
+    if cfg.kv_dtype == C.KV_BF16:
+        lay = layers[0]
+        rws = torch.empty(sks.refit_workspace_bytes(lay.cache, 0, cfg.T_max), dtype=torch.uint8,
+                          device=dev)
+        G = torch.empty((cfg.Hkv, 128, 128), dtype=torch.float64, device=dev)
+        Pn = torch.empty((cfg.Hkv, 64, 128), dtype=torch.float32, device=dev)
+        ksn = torch.empty(cfg.Hkv, dtype=torch.float32, device=dev)
+        calls = {"gram": lambda: sks.refit_gram(lay.cache, 0, cfg.T_max, G, rws),
+                 "basis": lambda: sks.refit_basis(G, Pn, rws),
+                 "key_scale": lambda: sks.refit_key_scale(lay.cache, 0, cfg.T_max, Pn, ksn, rws)}
+        refit = {}
+        for name, fn in calls.items():
+            ts = []
+            for _ in range(3):
+                a, b = ev(), ev()
+                a.record(stream)
+                fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            refit[name + "_ms"] = float(np.median(ts))
+        key_bytes = cfg.B * cfg.Hkv * cfg.L * cfg.kv_row_bytes
+        refit["gram_GBps"] = key_bytes / (refit["gram_ms"] * 1e-3) / 1e9
+        refit["key_scale_GBps"] = key_bytes / (refit["key_scale_ms"] * 1e-3) / 1e9
+        del rws, G, Pn, ksn
+
     # per-phase breakdown (events between the calls of each step; includes
     # the events' own small overhead)
     names = ("append_sketch", "query_sketch", "score", "topk", "attention")
@@ -384,6 +413,7 @@ def main():
             "attn_host_GBps": (selected_b / (attn_avg_ms * 1e-3) / 1e9 if args.host_kv else None),
             "gather_pack_GBps": 2 * gather_b / (gather_avg_ms * 1e-3) / 1e9,
             "step_ms_spread": spread,
+            "refit": refit,
             "score_plus_attn_GBps": (sketch_b + gather_b) / ((score_avg_ms + attn_avg_ms) * 1e-3) / 1e9,
             "step_GBps": (sketch_b + gather_b + small_b) / (ms_per_step * 1e-3) / 1e9,
             "phase_ms_median": phase_ms,

@@ -274,6 +274,45 @@ typedef struct sks_step {
 int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *step, int32_t flags,
                     void *ws, size_t ws_bytes, sks_stream_t stream);
 
+/* ---------------------------------------------------------------- basis refit
+ * "What it took" of "8 agents x 250K context ...": a frozen sketch basis in
+ * one file plus the script that refits it.  A refit reads the captured keys
+ * of every sequence b and KV head h at positions [t_begin, min(t_end,
+ * seq_len[b])) of a bf16 cache (int8/int4 caches: SKS_ERR_UNSUPPORTED) and
+ * computes, in three calls on one stream:
+ *   G = sum of x x^T over the keys (fp64 [128][128], per KV head or over all),
+ *   basis = the 64 eigenvectors of G with the largest eigenvalues, as rows in
+ *           descending eigenvalue order, each signed so that its
+ *           largest-magnitude component (the first one on ties) is positive,
+ *   key_scale[h] = max over the keys of (b, h) of max_c |(P x)_c| / 127, so
+ *           that no captured key's code clips (1 if every projection is 0).
+ * The outputs can be handed to every other call as basis / key_scale.  Same
+ * conventions as above: device pointers, nothing allocated, errors before any
+ * launch.  The Gram matrix accumulates exact bf16 products in fp32 per
+ * 8,192-key chunk and the chunks in fp64; the eigen-decomposition is cyclic
+ * Jacobi in fp64.  Equal eigenvalues leave the order among them, and hence
+ * the basis, to the solver. */
+
+/* Workspace bytes for sks_refit_gram and sks_refit_key_scale on this key
+ * range; it also covers sks_refit_basis for up to Hkv matrices.  0 on
+ * invalid arguments. */
+size_t sks_refit_workspace_bytes(const sks_kv *kv, int32_t t_begin, int32_t t_end);
+
+/* gram: [per_head ? Hkv : 1][128][128] fp64, symmetric, 8-byte aligned. */
+int sks_refit_gram(const sks_kv *kv, int32_t t_begin, int32_t t_end, int32_t per_head,
+                   double *gram, void *ws, size_t ws_bytes, sks_stream_t stream);
+
+/* From n Gram matrices [n][128][128] fp64: basis [n][64][128] fp32 and, if
+ * eigval is not NULL, all eigenvalues [n][128] fp64 in descending order.
+ * ws: at least n * 128 * 128 * 8 bytes (scratch). */
+int sks_refit_basis(const double *gram, int32_t n, float *basis, double *eigval, void *ws,
+                    size_t ws_bytes, sks_stream_t stream);
+
+/* key_scale: [Hkv] fp32, from basis [1 or Hkv][64][128] (basis_per_head). */
+int sks_refit_key_scale(const sks_kv *kv, int32_t t_begin, int32_t t_end, const float *basis,
+                        int32_t basis_per_head, float *key_scale, void *ws, size_t ws_bytes,
+                        sks_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,9 @@ STEP_APPEND = 1
 
 EXPORTS = ("sks_last_error", "sks_runtime_version", "sks_workspace_bytes", "sks_workspace_init",
            "sks_sketch_build", "sks_sketch_build_query", "sks_sketch_score", "sks_topk_select",
-           "sks_gather_pack", "sks_sparse_decode_attn", "sks_decode_step")
+           "sks_gather_pack", "sks_sparse_decode_attn", "sks_decode_step",
+           "sks_refit_workspace_bytes", "sks_refit_gram", "sks_refit_basis",
+           "sks_refit_key_scale")
 
 
 class SksError(RuntimeError):
@@ -97,6 +99,14 @@ def lib():
                                              vp, vp, sz, vp]
         L.sks_decode_step.restype = ctypes.c_int
         L.sks_decode_step.argtypes = [kvp, pp, ctypes.POINTER(StepDesc), i32, vp, sz, vp]
+        L.sks_refit_workspace_bytes.restype = sz
+        L.sks_refit_workspace_bytes.argtypes = [kvp, i32, i32]
+        L.sks_refit_gram.restype = ctypes.c_int
+        L.sks_refit_gram.argtypes = [kvp, i32, i32, i32, vp, vp, sz, vp]
+        L.sks_refit_basis.restype = ctypes.c_int
+        L.sks_refit_basis.argtypes = [vp, i32, vp, vp, vp, sz, vp]
+        L.sks_refit_key_scale.restype = ctypes.c_int
+        L.sks_refit_key_scale.argtypes = [kvp, i32, i32, vp, i32, vp, vp, sz, vp]
         # the HIP runtime the library runs on (one of its dependencies)
         L.hipHostGetDevicePointer.restype = ctypes.c_int
         L.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(vp), vp, ctypes.c_uint]
@@ -237,3 +247,24 @@ def decode_step(cache: Cache, p: Params, q, basis, key_scale, S, qsk, scores, id
     _check(lib().sks_decode_step(cache.ref, ctypes.byref(p), ctypes.byref(st),
                                  STEP_APPEND if append else 0, ptr(ws), _nbytes(ws),
                                  _stream(stream)))
+
+
+def refit_workspace_bytes(cache: Cache, t_begin: int, t_end: int) -> int:
+    return lib().sks_refit_workspace_bytes(cache.ref, t_begin, t_end)
+
+
+def refit_gram(cache: Cache, t_begin: int, t_end: int, gram, ws, per_head=True, stream=None):
+    _check(lib().sks_refit_gram(cache.ref, t_begin, t_end, int(per_head), ptr(gram), ptr(ws),
+                                _nbytes(ws), _stream(stream)))
+
+
+def refit_basis(gram, basis, ws, eigval=None, stream=None):
+    _check(lib().sks_refit_basis(ptr(gram), gram.shape[0], ptr(basis), ptr(eigval), ptr(ws),
+                                 _nbytes(ws), _stream(stream)))
+
+
+def refit_key_scale(cache: Cache, t_begin: int, t_end: int, basis, key_scale, ws,
+                    basis_per_head=True, stream=None):
+    _check(lib().sks_refit_key_scale(cache.ref, t_begin, t_end, ptr(basis), int(basis_per_head),
+                                     ptr(key_scale), ptr(ws), _nbytes(ws), _stream(stream)))
+

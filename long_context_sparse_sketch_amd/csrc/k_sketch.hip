@@ -9,6 +9,7 @@
 // Bulk builds run on the matrix cores (sketch_mfma_kernel, below); the few
 // rows of a step's append take one wave per row (sketch_rows_small_kernel).
 #include "sks_internal.h"
+#include "refit.h"
 #include "tier.h"
 
 namespace sks {
@@ -106,19 +107,29 @@ __device__ __forceinline__ uint32_t sk_split(float p, int part) {
   return sk_bf16(r1 - __uint_as_float(mid << 16));          // exact remainder, <= 8 bits
 }
 
-template <int DT>
+// AMAX: instead of codes, the largest |y| over the rows [t_begin, min(t_end,
+// seq_len[b])) (the key-scale pass of a basis refit); each workgroup writes
+// its maximum to amax[blockIdx.y * gridDim.x + blockIdx.x] (0 if it has no
+// rows).  Rows past the range are clamped copies of its last row, which
+// leave the maximum unchanged.
+template <int DT, bool AMAX = false>
 __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
     const void *__restrict__ X, const uint16_t *__restrict__ Xs, long x_rows_per_bh,
     const int32_t *__restrict__ seq_len, const float *__restrict__ basis, int basis_per_head,
     const float *__restrict__ key_scale, int Hkv, int T_max, int R, int NB, int pool,
-    int append, int t_begin, int t_end, int8_t *__restrict__ S) {
+    int append, int t_begin, int t_end, int8_t *__restrict__ S, float *__restrict__ amax = nullptr) {
   __shared__ sk_u32x4_t bop[3][4][4][64];                   // [part][basis block][step][lane]
   __shared__ __align__(16) uint8_t stage[SM_THREADS / 64][SM_TILE * RANK];
   const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
   int j_lo, j_hi;
   sketch_range(append, seq_len, b, T_max, R, pool, NB, t_begin, t_end, j_lo, j_hi);
+  if constexpr (AMAX) j_hi = min(j_hi, clamp_len(seq_len[b], T_max, 1));
   const int j0 = j_lo + blockIdx.x * SM_ROWS;
-  if (j0 >= j_hi) return;
+  if (j0 >= j_hi) {
+    if constexpr (AMAX)
+      if (threadIdx.x == 0) amax[(size_t)blockIdx.y * gridDim.x + blockIdx.x] = 0.f;
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
 
@@ -135,7 +146,8 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
   }
   __syncthreads();
 
-  const float kscale = key_scale[h];
+  const float kscale = AMAX ? 1.f : key_scale[h];
+  float am = 0.f;                                           // AMAX: this lane's largest |y|
   constexpr int RB = row_bytes<DT>();
   const char *Xbh = static_cast<const char *>(X) + (size_t)bh * x_rows_per_bh * RB;
   const uint16_t *Xsbh = DT != SKS_KV_BF16 ? Xs + (size_t)bh * x_rows_per_bh : nullptr;
@@ -211,6 +223,22 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
           for (int m = 0; m < 4; ++m) acc[m][nb] = sk_mfma(a[m][c], bv, acc[m][nb]);
         }
 
+    if constexpr (AMAX) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float sc = DT != SKS_KV_BF16 ? __shfl(xs, 16 * m + 4 * g + j) : 1.f;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) am = fmaxf(am, fabsf(acc[m][nb][j] * sc));
+        }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cur[m][c] = nxt[m][c];
+      xs_cur = xs_nxt;
+      continue;
+    }
     // codes: lane holds Y[row 16m + 4g + j][basis 16nb + n]
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -240,6 +268,18 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) cur[m][c] = nxt[m][c];
     xs_cur = xs_nxt;
+  }
+  if constexpr (AMAX) {
+    // max is exact in any order: the result does not depend on the schedule
+    for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+    __shared__ float wmax[SM_THREADS / 64];
+    if (lane == 0) wmax[wave] = am;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float m = wmax[0];
+      for (int w = 1; w < SM_THREADS / 64; ++w) m = fmaxf(m, wmax[w]);
+      amax[(size_t)blockIdx.y * gridDim.x + blockIdx.x] = m;
+    }
   }
 }
 
@@ -477,6 +517,21 @@ hipError_t launch_sketch_keys(const sks_kv &kv, const Shape &s, const float *bas
         Kp, nullptr, s.NB, kv.seq_len, basis, basis_per_head, key_scale, s.Hkv, s.T_max, s.R,
         s.NB, s.pool, append, t_begin, t_end, S);
   }
+  return hipGetLastError();
+}
+
+// Largest |P x| per workgroup over the keys [t_begin, min(t_end, L_b)) of
+// every (b, h) (bf16 caches); amax gets grid.x * B * Hkv maxima, grid.x =
+// refit_amax_chunks(...).
+int refit_amax_chunks(long span) { return span <= 0 ? 1 : ceil_div(span, SM_ROWS); }
+
+hipError_t launch_refit_amax(const sks_kv &kv, int t_begin, int t_end, const float *basis,
+                             int basis_per_head, float *amax, hipStream_t st) {
+  const long span = (long)t_end - (long)t_begin;
+  dim3 grid(refit_amax_chunks(span), kv.B * kv.Hkv);
+  sketch_mfma_kernel<SKS_KV_BF16, true><<<grid, SM_THREADS, 0, st>>>(
+      kv.K, nullptr, kv.T_max, kv.seq_len, basis, basis_per_head, nullptr, kv.Hkv, kv.T_max, 1,
+      kv.T_max, 1, 0, t_begin, t_end, nullptr, amax);
   return hipGetLastError();
 }
 

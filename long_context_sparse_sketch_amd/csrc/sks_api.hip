@@ -7,6 +7,7 @@
 
 #include <algorithm>
 
+#include "refit.h"
 #include "sks_internal.h"
 
 namespace {
@@ -340,6 +341,85 @@ int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *st, i
     e = sks::launch_attn(st->q, st->Hq, *kv, s, st->idx, st->Kp, st->Vp, st->sm_scale, st->out,
                          st->lse, w, hs);
   return hip_status(e, "sks_decode_step");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ basis refit
+namespace {
+
+int check_refit_kv(const sks_kv *kv, int32_t t_begin, int32_t t_end) {
+  REQUIRE(kv != nullptr, "kv must not be NULL");
+  REQUIRE(kv->D == SKS_HEAD_DIM, "D must be %d (got %d)", SKS_HEAD_DIM, kv->D);
+  REQUIRE(kv->B >= 1 && kv->Hkv >= 1, "B and Hkv must be >= 1 (got %d, %d)", kv->B, kv->Hkv);
+  REQUIRE(kv->T_max >= 1, "T_max must be >= 1");
+  REQUIRE((long)kv->B * kv->Hkv <= 65535, "B * Hkv must be <= 65535");
+  REQUIRE(kv->dtype == SKS_KV_BF16 || kv->dtype == SKS_KV_I8 || kv->dtype == SKS_KV_I4,
+          "unknown KV dtype %d", kv->dtype);
+  if (kv->dtype != SKS_KV_BF16)
+    return fail(SKS_ERR_UNSUPPORTED, "the basis refit takes bf16 keys");
+  REQUIRE(t_begin >= 0 && t_begin <= t_end && t_end <= kv->T_max,
+          "key range [%d, %d) must lie in [0, T_max = %d]", t_begin, t_end, kv->T_max);
+  REQUIRE_PTR(kv->K, 16);
+  REQUIRE(kv->seq_len != nullptr, "kv->seq_len must not be NULL");
+  REQUIRE(aligned(kv->seq_len, 4), "kv->seq_len must be 4-byte aligned");
+  return SKS_OK;
+}
+
+size_t refit_ws(const sks_kv *kv, int32_t t_begin, int32_t t_end) {
+  const long span = (long)t_end - (long)t_begin;
+  const size_t gram = sks::refit_gram_scratch_bytes(kv->B, kv->Hkv, span);
+  const size_t vecs = (size_t)kv->Hkv * SKS_HEAD_DIM * SKS_HEAD_DIM * sizeof(double);
+  const size_t amax = (size_t)kv->B * kv->Hkv * sks::refit_amax_chunks(span) * sizeof(float);
+  return sks::align_up(std::max(gram, std::max(vecs, amax)), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sks_refit_workspace_bytes(const sks_kv *kv, int32_t t_begin, int32_t t_end) {
+  if (check_refit_kv(kv, t_begin, t_end) != SKS_OK) return 0;
+  ok();
+  return refit_ws(kv, t_begin, t_end);
+}
+
+int sks_refit_gram(const sks_kv *kv, int32_t t_begin, int32_t t_end, int32_t per_head,
+                   double *gram, void *ws, size_t ws_bytes_given, sks_stream_t stream) {
+  TRY(check_refit_kv(kv, t_begin, t_end));
+  REQUIRE_PTR(gram, 8);
+  TRY(check_ws(ws, ws_bytes_given, refit_ws(kv, t_begin, t_end)));
+  return hip_status(sks::launch_refit_gram(*kv, t_begin, t_end, per_head ? 1 : 0, gram, ws,
+                                           (hipStream_t)stream),
+                    "sks_refit_gram");
+}
+
+int sks_refit_basis(const double *gram, int32_t n, float *basis, double *eigval, void *ws,
+                    size_t ws_bytes_given, sks_stream_t stream) {
+  REQUIRE(n >= 1 && n <= 65535, "n must be in [1, 65535] (got %d)", n);
+  REQUIRE_PTR(gram, 8);
+  REQUIRE_PTR(basis, 4);
+  if (eigval) REQUIRE(aligned(eigval, 8), "eigval must be 8-byte aligned");
+  TRY(check_ws(ws, ws_bytes_given, (size_t)n * SKS_HEAD_DIM * SKS_HEAD_DIM * sizeof(double)));
+  return hip_status(sks::launch_refit_basis(gram, n, basis, eigval, ws, (hipStream_t)stream),
+                    "sks_refit_basis");
+}
+
+int sks_refit_key_scale(const sks_kv *kv, int32_t t_begin, int32_t t_end, const float *basis,
+                        int32_t basis_per_head, float *key_scale, void *ws, size_t ws_bytes_given,
+                        sks_stream_t stream) {
+  TRY(check_refit_kv(kv, t_begin, t_end));
+  REQUIRE_PTR(basis, 4);
+  REQUIRE_PTR(key_scale, 4);
+  TRY(check_ws(ws, ws_bytes_given, refit_ws(kv, t_begin, t_end)));
+  const long span = (long)t_end - (long)t_begin;
+  float *amax = static_cast<float *>(ws);
+  const hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = sks::launch_refit_amax(*kv, t_begin, t_end, basis, basis_per_head, amax, hs);
+  if (e == hipSuccess)
+    e = sks::launch_refit_scale_reduce(amax, kv->B, kv->Hkv, sks::refit_amax_chunks(span),
+                                       key_scale, hs);
+  return hip_status(e, "sks_refit_key_scale");
 }
 
 }  // extern "C"

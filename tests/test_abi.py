@@ -222,3 +222,23 @@ def test_workspace_holds_selection_and_attention_scratch_apart(L):
     cand = 32 * n_sub * 1024 * 8
     part = 32 * (-(-2048 // 384) + -(-4096 // 384)) * 6 * (8 + 512)
     assert small >= cand + part
+
+
+def test_refit_argument_errors(L):
+    k = kv(T=1000)
+    assert L.sks_refit_workspace_bytes(ctypes.byref(k), 0, 1000) > 0
+    assert L.sks_refit_workspace_bytes(ctypes.byref(k), 0, 1001) == 0
+    assert "key range" in sks.last_error()
+    assert L.sks_refit_workspace_bytes(ctypes.byref(k), 5, 4) == 0
+    assert L.sks_refit_gram(ctypes.byref(k), 0, 1000, 1, FAKE, FAKE, 16, None) == \
+        sks.SKS_ERR_WORKSPACE
+    assert L.sks_refit_gram(ctypes.byref(k), 0, 1000, 1, FAKE + 4, FAKE, 1 << 30, None) == \
+        sks.SKS_ERR_ARG and "aligned" in sks.last_error()
+    k8 = kv(T=1000, dtype=sks.KV_I8, Ks=FAKE, Vs=FAKE)
+    assert L.sks_refit_gram(ctypes.byref(k8), 0, 10, 1, FAKE, FAKE, 1 << 30, None) == \
+        sks.SKS_ERR_UNSUPPORTED and "bf16" in sks.last_error()
+    assert L.sks_refit_basis(FAKE, 0, FAKE, None, FAKE, 1 << 30, None) == sks.SKS_ERR_ARG
+    assert L.sks_refit_basis(FAKE, 2, FAKE, None, FAKE, 128 * 128 * 8, None) == \
+        sks.SKS_ERR_WORKSPACE
+    assert L.sks_refit_key_scale(ctypes.byref(k), 0, 1000, None, 1, FAKE, FAKE, 1 << 30,
+                                 None) == sks.SKS_ERR_ARG and "basis" in sks.last_error()
