@@ -24,10 +24,9 @@ pytestmark = pytest.mark.gpu
 OUTS = ("S", "qsk", "qscale", "scores", "idx", "n_sel", "out", "lse")
 
 
-def poison_value(t):
-    """A byte pattern that wrecks any result it enters: bf16 / fp16 0x7B7B
-    (about 1.3e36 / 6.5e4), int8 codes 0x7B = 123, int4 codes 7 and -5."""
-    return 0x7B
+# A byte pattern that wrecks any result it enters: bf16 / fp16 0x7B7B (about
+# 1.3e36 / 6.1e4), int8 codes 0x7B = 123, int4 codes 7 and -5.
+POISON = 0x7B
 
 
 def build_tier(g: GpuCase, W_hot: int):
@@ -42,7 +41,7 @@ def build_tier(g: GpuCase, W_hot: int):
             continue
         r = torch.empty((t.shape[0], t.shape[1], W_hot) + tuple(t.shape[3:]), dtype=t.dtype,
                         device="cuda")
-        r.view(torch.uint8).fill_(poison_value(t))             # slots with no valid position
+        r.view(torch.uint8).fill_(POISON)             # slots with no valid position
         for b in range(t.shape[0]):
             end = int(g.seq_len_np[b]) + R - 1                  # one past the last row's token
             pos = torch.arange(max(0, end - W_hot), end, device="cuda")
@@ -61,7 +60,7 @@ def poison_host(g: GpuCase, host):
             continue
         for b in range(t.shape[0]):
             start = max(0, int(g.seq_len_np[b]) + R - 1 - W)
-            t[b][:, start:].view(torch.uint8).fill_(poison_value(t))
+            t[b][:, start:].view(torch.uint8).fill_(POISON)
 
 
 def run(layer, q):
@@ -159,3 +158,29 @@ def test_host_tier_gather_pack_and_graph_replay():
         outs.append((Ko, Vo, Kso, Vso, n_out))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_host_tier_full_size_int4():
+    """The benchmark's shape (8 x 250K, int4, graph-replayed step as bench.py
+    --kv int4 --host-kv times it): bit-equal to the all-device step."""
+    cfg = C.with_kv(C.C3, C.KV_I4)
+    flush(f"[tier] full size {cfg.name}")
+    case = make_case(cfg)
+    g = GpuCase(case)
+    g.layer.build_sketch(0, g.T)
+    runner = StepRunner(g.layer)
+    runner.capture(g.q)
+    runner.replay()
+    torch.cuda.synchronize()
+    want = {n: getattr(g.layer, n).clone() for n in OUTS}
+    cache, host, ring = build_tier(g, g.window + cfg.R)
+    lay = SparseDecodeLayer(case.B, cfg.R, cfg.Hq, cfg.Hkv, g.T, g.window, g.topk, g.pool,
+                            cfg.kv_dtype).bind(cache, g.basis, g.key_scale)
+    lay.S.copy_(g.layer.S)
+    poison_host(g, host)
+    runner = StepRunner(lay)
+    runner.capture(g.q)
+    runner.replay()
+    torch.cuda.synchronize()
+    for n in OUTS:
+        assert torch.equal(want[n].view(torch.uint8), getattr(lay, n).view(torch.uint8)), n
