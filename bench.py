@@ -39,6 +39,11 @@ def parse():
     ap.add_argument("--config", default="multi_agent_250k")
     ap.add_argument("--kv", choices=("bf16", "int8", "int4"), default=None,
                     help="store the workload's KV cache in another format (default: its own)")
+    ap.add_argument("--context", type=int, default=None,
+                    help="override the workload's context length (e.g. a short chat)")
+    ap.add_argument("--dense", action="store_true",
+                    help="time the dense step (no scoring or selection: each row attends its "
+                         "last window + topk tokens), the switch's choice for short rows")
     ap.add_argument("--host-kv", action="store_true",
                     help="keep the full K/V in pinned host memory (read over PCIe for the "
                          "selected rows) with the window in a device ring")
@@ -160,6 +165,8 @@ def main():
     cfg = C.BY_NAME[args.config]
     if args.kv is not None:
         cfg = C.with_kv(cfg, {v: k for k, v in C.KV_NAMES.items()}[args.kv])
+    if args.context is not None:
+        cfg = cfg.scaled(name=f"{cfg.name}_ctx{args.context}", L=args.context)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sks.lib()
@@ -224,7 +231,8 @@ def main():
         del a, b
 
     stream = torch.cuda.current_stream()
-    runners = [StepRunner(lay, parts=args.parts, streams=args.streams, fused=not args.five_calls)
+    runners = [StepRunner(lay, parts=args.parts, streams=args.streams, fused=not args.five_calls,
+                          dense=args.dense)
                for lay in layers]
     R_ = len(runners)
     spg = args.steps_per_graph or R_
@@ -388,11 +396,13 @@ def main():
         "vs_baseline": None,
         "dtype": f"i8 sketch / {C.KV_NAMES[cfg.kv_dtype]} KV / f32 accumulate",
         "data": "synthetic (seeded N(0,1) caches with planted needles)",
-        "config": {"workload": cfg.name + ("+host_kv" if args.host_kv else ""), "batch": cfg.B,
+        "config": {"workload": cfg.name + ("+host_kv" if args.host_kv else "")
+                               + ("+dense" if args.dense else ""), "batch": cfg.B,
                    "context": cfg.L, "rows": cfg.R,
                    "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "window": cfg.window,
                    "topk": cfg.topk, "pool": cfg.pool, "replicas": args.replicas,
-                   "schedule": ("five C-ABI calls" if args.five_calls else "sks_decode_step")
+                   "schedule": ("five C-ABI calls" if args.five_calls else
+                                "sks_decode_step" + (" (dense)" if args.dense else ""))
                                + f", {args.parts} sub-batches on {args.streams} streams, "
                                + ("eager launches" if args.no_graph else
                                   f"HIP graph replay ({spg} steps per graph)")},

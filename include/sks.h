@@ -247,8 +247,18 @@ int sks_sparse_decode_attn(const uint16_t *q, int32_t Hq, const sks_kv *kv,
  * the work in "What it took": build the sketch, score every token, pick the
  * top ~2K, attend, all graph-safe).  Grouping the calls lets launches share
  * work that the order allows: the query sketch and the append run in one
- * launch, and the final selection runs in the same launch as the exact-window
- * part of the attention, which does not depend on it.
+ * launch.
+ * With SKS_STEP_DENSE the step skips scoring and selection (the dense half of
+ * the per-step dense/sparse switch of "What it took", so that short chats
+ * stay at full speed): every row attends, under one softmax, to its last
+ * window + topk tokens -- all of [0, L_i) when L_i <= window + topk, which is
+ * exactly the set the sparse step attends for such rows when pool == 1.  The
+ * attention entries are then in position order, so out and lse equal the
+ * sparse step's up to rounding, not bit for bit.  scores, idx and n_sel are
+ * left as they are (idx must still point at a buffer of its size); the
+ * APPEND sketch rows are written as usual, so that later sparse steps find
+ * the sketch current.  Which mode a step takes is the caller's choice (it
+ * knows its lengths); the workspace of the sparse step serves both.
  * Every buffer is caller-owned and keeps the layout of the individual call
  * that writes or reads it; NULL is allowed where the individual call allows
  * it (qscale, n_sel, lse; Kp/Vp when pool == 1).  The same validation as the
@@ -271,6 +281,7 @@ typedef struct sks_step {
   float *lse;               /* out: [B][R][Hq] fp32 log-sum-exp, or NULL        */
 } sks_step;
 #define SKS_STEP_APPEND 1   /* sketch the rows' own tokens first */
+#define SKS_STEP_DENSE 2    /* no selection: attend the last window + topk tokens */
 int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *step, int32_t flags,
                     void *ws, size_t ws_bytes, sks_stream_t stream);
 

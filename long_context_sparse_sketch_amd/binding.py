@@ -23,6 +23,7 @@ HEAD_DIM, RANK = 128, 64
 
 TOPK_HIST_READY = 1
 STEP_APPEND = 1
+STEP_DENSE = 2
 
 EXPORTS = ("sks_last_error", "sks_runtime_version", "sks_workspace_bytes", "sks_workspace_init",
            "sks_sketch_build", "sks_sketch_build_query", "sks_sketch_score", "sks_topk_select",
@@ -238,14 +239,16 @@ def sparse_decode_attn(q, cache: Cache, p: Params, idx, out, ws, lse=None, Kp=No
 
 def decode_step(cache: Cache, p: Params, q, basis, key_scale, S, qsk, scores, idx, out, ws,
                 qscale=None, n_sel=None, lse=None, Kp=None, Vp=None, sm_scale=None,
-                basis_per_head=False, append=True, stream=None):
-    """The whole decode step (append, query sketch, score, select, attend) in one call."""
+                basis_per_head=False, append=True, dense=False, stream=None):
+    """The whole decode step (append, query sketch, score, select, attend) in one call;
+    dense: no scoring or selection, attend the last window + topk tokens."""
     sm = 1.0 / math.sqrt(q.shape[3]) if sm_scale is None else sm_scale
     st = StepDesc(ptr(q), q.shape[2], ptr(basis), int(basis_per_head), ptr(key_scale), ptr(S),
                   ptr(Kp), ptr(Vp), sm, ptr(qsk), ptr(qscale), ptr(scores), ptr(idx), ptr(n_sel),
                   ptr(out), ptr(lse))
     _check(lib().sks_decode_step(cache.ref, ctypes.byref(p), ctypes.byref(st),
-                                 STEP_APPEND if append else 0, ptr(ws), _nbytes(ws),
+                                 (STEP_APPEND if append else 0) | (STEP_DENSE if dense else 0),
+                                 ptr(ws), _nbytes(ws),
                                  _stream(stream)))
 
 

@@ -180,6 +180,7 @@ struct AttnArgs {
   const uint16_t *Kp, *Vp;
   float sm_log2;
   int R, Hkv, T_max, NB, window, pool, topk, nsplit;
+  int kmax;                           // selected entries per row at most: topk, or 0 (dense step)
   float2 *part_ml;
   float *part_acc;
 };
@@ -225,7 +226,7 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   const int sel0 = idx_row[min(e_wave + lane, topk - 1)];
   const int sel1 = idx_row[min(e_wave + 64 + lane, topk - 1)];
   const int L0 = clamp_len(seq_len[b], T_max, R);
-  const RowGeom rg = row_geom(L0, i, window, pool, topk);
+  const RowGeom rg = row_geom(L0, i, window, pool, a.kmax);
   const int e_hi = min((slot + 1) * ATTN_SPLIT, rg.n_ent);   // end of this slot's entries
 
   // Descriptor of an entry: the row to gather and whether it takes part

@@ -81,6 +81,7 @@ AttnArgs attn_args(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
   a.window = s.window;
   a.pool = s.pool;
   a.topk = s.topk;
+  a.kmax = s.topk;
   a.nsplit = attn_nsplit(s);
   const size_t n = (size_t)nseg * a.nsplit * G;
   a.part_ml = reinterpret_cast<float2 *>(w.attn);
@@ -115,10 +116,19 @@ hipError_t launch_attn_merge(const AttnArgs &a, int G, int nseg, float *out, flo
 
 hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
                        const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp,
-                       float sm_scale, float *out, float *lse, const TopkWs &w, hipStream_t st) {
+                       float sm_scale, float *out, float *lse, const TopkWs &w, hipStream_t st,
+                       bool dense) {
   const int G = Hq / s.Hkv;
   const int nseg = s.B * s.R * s.Hkv;
-  const AttnArgs a = attn_args(q, Hq, kv, s, idx, Kp, Vp, sm_scale, w);
+  AttnArgs a = attn_args(q, Hq, kv, s, idx, Kp, Vp, sm_scale, w);
+  if (dense) {
+    // no selection: one softmax over the last window + topk tokens of each
+    // row (all of them when L_i <= window + topk); the attention set is then
+    // at most window + topk + pool - 1 entries, the sparse step's bound, so
+    // the split count and the workspace stay those of the sparse step
+    a.window = s.window + s.topk;
+    a.kmax = 0;
+  }
   hipError_t e = launch_attn_slots(a, G, s.dtype, nseg, 0, a.nsplit, st);
   if (e != hipSuccess) return e;
   return launch_attn_merge(a, G, nseg, out, lse, st);

@@ -300,7 +300,7 @@ int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *st, i
   TRY(check_shape(kv, p, s));
   TRY(check_cache(kv, true));
   REQUIRE(st != nullptr, "step must not be NULL");
-  REQUIRE((flags & ~SKS_STEP_APPEND) == 0, "unknown flags 0x%x", flags);
+  REQUIRE((flags & ~(SKS_STEP_APPEND | SKS_STEP_DENSE)) == 0, "unknown flags 0x%x", flags);
   TRY(check_heads(st->Hq, kv->Hkv));
   REQUIRE(st->basis_per_head == 0 || st->basis_per_head == 1, "basis_per_head must be 0 or 1");
   REQUIRE_PTR(st->q, 16);
@@ -334,12 +334,15 @@ int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *st, i
   else
     e = sks::launch_sketch_query(st->q, s.B, s.R, st->Hq, s.Hkv, st->basis, st->basis_per_head,
                                  st->qsk, st->qscale, hs);
-  if (e == hipSuccess) e = sks::launch_score(st->qsk, st->S, kv->seq_len, s, st->scores, &w, hs);
-  if (e == hipSuccess)
-    e = sks::launch_topk(st->scores, kv->seq_len, s, true, st->idx, st->n_sel, w, hs);
+  const bool dense = (flags & SKS_STEP_DENSE) != 0;
+  if (!dense) {
+    if (e == hipSuccess) e = sks::launch_score(st->qsk, st->S, kv->seq_len, s, st->scores, &w, hs);
+    if (e == hipSuccess)
+      e = sks::launch_topk(st->scores, kv->seq_len, s, true, st->idx, st->n_sel, w, hs);
+  }
   if (e == hipSuccess)
     e = sks::launch_attn(st->q, st->Hq, *kv, s, st->idx, st->Kp, st->Vp, st->sm_scale, st->out,
-                         st->lse, w, hs);
+                         st->lse, w, hs, dense);
   return hip_status(e, "sks_decode_step");
 }
 

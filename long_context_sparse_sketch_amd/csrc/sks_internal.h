@@ -269,7 +269,8 @@ hipError_t launch_step_prologue(const uint16_t *q, int Hq, const sks_kv &kv, con
                                 hipStream_t st);
 hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
                        const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp,
-                       float sm_scale, float *out, float *lse, const TopkWs &w, hipStream_t st);
+                       float sm_scale, float *out, float *lse, const TopkWs &w, hipStream_t st,
+                       bool dense = false);
 
 hipError_t launch_gather(const sks_kv &kv, const Shape &s, const int32_t *idx,
                          const uint16_t *Kp, const uint16_t *Vp, void *K_out, void *V_out,

@@ -125,14 +125,21 @@ class SparseDecodeLayer:
                                self.ws, self.lse, self.Kp, self.Vp, sm_scale, stream)
 
     # ---- one decode step
-    def step(self, q, stream=None, append=True, fused=True):
+    def dense_covers(self, max_len: int) -> bool:
+        """True when a dense step attends exactly the sparse step's set for
+        rows up to max_len tokens (the switch: dense for short rows)."""
+        return self.pool == 1 and max_len + self.R - 1 <= self.window + self.topk
+
+    def step(self, q, stream=None, append=True, fused=True, dense=False):
         """One step; `fused` issues it as the single sks_decode_step call,
-        otherwise as the individual calls (same results)."""
-        if fused:
+        otherwise as the individual calls (same results).  `dense` skips
+        scoring and selection (one call only)."""
+        if fused or dense:
             sks.decode_step(self.cache, self.p, q, self.basis, self.key_scale, self.S, self.qsk,
                             self.scores, self.idx, self.out, self.ws, qscale=self.qscale,
                             n_sel=self.n_sel, lse=self.lse, Kp=self.Kp, Vp=self.Vp,
-                            basis_per_head=self.basis_per_head, append=append, stream=stream)
+                            basis_per_head=self.basis_per_head, append=append, dense=dense,
+                            stream=stream)
             return self.out, self.lse
         if append:
             self.build_sketch(sks.APPEND, 0, stream)
@@ -146,10 +153,11 @@ class SparseDecodeLayer:
 class StepRunner:
     """One decode step of a layer, split into `parts` sub-batches on `streams`
     streams (fork/join on the caller's current stream), optionally captured
-    into a HIP graph and replayed."""
+    into a HIP graph and replayed.  `dense`: the step without selection (the
+    caller's switch for short rows, see SparseDecodeLayer.dense_covers)."""
 
     def __init__(self, layer: SparseDecodeLayer, parts: int = 1, streams: int = 1,
-                 overlap_append: bool = False, fused: bool = True):
+                 overlap_append: bool = False, fused: bool = True, dense: bool = False):
         parts = max(1, min(parts, layer.B))
         bounds = [layer.B * k // parts for k in range(parts + 1)]
         self.layer = layer
@@ -160,6 +168,7 @@ class StepRunner:
         self.append_stream = torch.cuda.Stream(device=dev) if overlap_append else None
         self.graph = None
         self.fused = fused
+        self.dense = dense
 
     def step(self, q):
         main = torch.cuda.current_stream()
@@ -171,7 +180,7 @@ class StepRunner:
         side = self.append_stream if self.layer.window >= self.layer.R else None
         if side is None and len(self.streams) == 1 and len(self.views) == 1:
             # plain single-stream step on the caller's stream
-            self.views[0].step(q, fused=self.fused)
+            self.views[0].step(q, fused=self.fused, dense=self.dense)
             return self.layer.out, self.layer.lse
         if side is not None:
             side.wait_stream(main)
@@ -181,7 +190,8 @@ class StepRunner:
         for k, v in enumerate(self.views):
             st = self.streams[k % len(self.streams)]
             with torch.cuda.stream(st):
-                v.step(q[self.bounds[k]:self.bounds[k + 1]], append=side is None, fused=self.fused)
+                v.step(q[self.bounds[k]:self.bounds[k + 1]], append=side is None, fused=self.fused,
+                       dense=self.dense)
         for st in self.streams:
             main.wait_stream(st)
         if side is not None:

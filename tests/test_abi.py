@@ -200,7 +200,8 @@ def test_decode_step_argument_errors(L):
         ctypes.byref(k), ctypes.byref(p), st if st is None else ctypes.byref(st), flags, ws, nb,
         None)
     assert call(None) == sks.SKS_ERR_ARG and "step" in sks.last_error()
-    assert call(step_desc(), flags=2) == sks.SKS_ERR_ARG and "flags" in sks.last_error()
+    assert call(step_desc(), flags=4) == sks.SKS_ERR_ARG and "flags" in sks.last_error()
+    assert call(step_desc(), flags=8 | 3) == sks.SKS_ERR_ARG and "flags" in sks.last_error()
     assert call(step_desc(Hq=6)) == sks.SKS_ERR_ARG and "multiple" in sks.last_error()
     assert call(step_desc(scores=None)) == sks.SKS_ERR_ARG and "scores" in sks.last_error()
     assert call(step_desc(out=FAKE + 4)) == sks.SKS_ERR_ARG and "aligned" in sks.last_error()
