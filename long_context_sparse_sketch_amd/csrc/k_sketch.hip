@@ -37,6 +37,17 @@ __device__ __forceinline__ sk_u32x4_t i4x8_bf16(uint32_t w) {
   return o;
 }
 
+// Key code from y and the reciprocal of the frozen key scale, computed once:
+// a multiply instead of an IEEE division per code (equal to rne(y / scale)
+// whenever 1/scale is exact, e.g. for a power-of-two scale; otherwise a code
+// can differ only where y / scale lies within an ulp of a rounding boundary).
+// The bulk build and the per-step append use the same form.
+__device__ __forceinline__ int8_t key_code(float y, float inv_scale) {
+  float v = __builtin_rintf(y * inv_scale);
+  v = fminf(fmaxf(v, -127.0f), 127.0f);
+  return (int8_t)(int)v;
+}
+
 // Bytes of one cached K row.
 template <int DT>
 constexpr int row_bytes() {
@@ -66,12 +77,13 @@ __device__ __forceinline__ void sketch_range(int append, const int32_t *seq_len,
 // v_mfma_f32_16x16x32_bf16 with A = 16 rows x 32 dims of X (lane (n, g): row
 // n, dims 32c + 8g .. +8 of step c; int4 rows take dims 32g + 8c .. +8, so
 // that one 16-byte load holds a lane's four steps) and B = 32 dims x 16
-// basis rows (lane: basis row n, the same dims).  X is exact in bf16 (bf16
-// rows; int8 and int4 codes, whose fp16 row scale multiplies Y afterwards).  The fp32 basis is split exactly into three
-// bf16 parts, P = hi + mid + lo (8 + 8 + 8 significant bits), so every
-// product is exact and only the fp32 accumulation rounds -- the same
-// accuracy as an fp32 dot product.  The split basis sits in LDS in operand
-// order; codes are staged per wave and leave as 16-byte stores.
+// basis rows (block nb, lane: basis row 4n + nb, the same dims).  X is exact
+// in bf16 (bf16 rows; int8 and int4 codes, whose fp16 row scale multiplies Y
+// afterwards).  The fp32 basis is split exactly into three bf16 parts, P =
+// hi + mid + lo (8 + 8 + 8 significant bits), so every product is exact and
+// only the fp32 accumulation rounds -- the same accuracy as an fp32 dot
+// product.  The split basis sits in LDS in operand order; a lane's four
+// codes of a row are staged as one word per wave and leave as 16-byte stores.
 constexpr int SM_THREADS = 256;
 constexpr int SM_TILE = 64;                              // rows per wave and iteration
 constexpr int SM_ITERS = 16;
@@ -137,7 +149,9 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
   const float *P = basis + (basis_per_head ? (size_t)h * RANK * D : 0);
   for (int e = threadIdx.x; e < 3 * 4 * 4 * 64; e += SM_THREADS) {
     const int part = e >> 10, nb = (e >> 8) & 3, c = (e >> 6) & 3, l = e & 63;
-    const float *src = P + (size_t)(16 * nb + (l & 15)) * D + sm_dim<DT>(c, l >> 4);
+    // column n of basis block nb is basis row 4n + nb: a lane's four blocks
+    // then hold four consecutive codes of a row
+    const float *src = P + (size_t)(4 * (l & 15) + nb) * D + sm_dim<DT>(c, l >> 4);
     sk_u32x4_t w;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -146,7 +160,7 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
   }
   __syncthreads();
 
-  const float kscale = AMAX ? 1.f : key_scale[h];
+  const float kinv = AMAX ? 1.f : 1.0f / key_scale[h];
   float am = 0.f;                                           // AMAX: this lane's largest |y|
   constexpr int RB = row_bytes<DT>();
   const char *Xbh = static_cast<const char *>(X) + (size_t)bh * x_rows_per_bh * RB;
@@ -239,16 +253,19 @@ __global__ __launch_bounds__(SM_THREADS, 2) void sketch_mfma_kernel(
       xs_cur = xs_nxt;
       continue;
     }
-    // codes: lane holds Y[row 16m + 4g + j][basis 16nb + n]
+    // codes: lane holds Y[row 16m + 4g + j][basis 4n + nb], i.e. bytes
+    // 4n .. 4n + 3 of the row's code, stored as one 32-bit word
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = 16 * m + 4 * g + j;
         const float sc = DT != SKS_KV_BF16 ? __shfl(xs, rr) : 1.f;
+        uint32_t word = 0;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          st[rr * RANK + 16 * nb + n] = (uint8_t)quant_code(acc[m][nb][j] * sc, kscale);
+          word |= (uint32_t)(uint8_t)key_code(acc[m][nb][j] * sc, kinv) << (8 * nb);
+        *reinterpret_cast<uint32_t *>(st + rr * RANK + 4 * n) = word;
       }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -392,7 +409,7 @@ __device__ void sketch_row_wave(const void *__restrict__ K, const void *__restri
   float y = 0.f;
 #pragma unroll 8
   for (int d = 0; d < D; ++d) y = __builtin_fmaf(Prow[d], x[d], y);
-  S[((size_t)bh * NB + j) * RANK + lane] = quant_code(y, key_scale[h]);
+  S[((size_t)bh * NB + j) * RANK + lane] = key_code(y, 1.0f / key_scale[h]);
 }
 
 template <int DT>
