@@ -182,12 +182,27 @@ __global__ __launch_bounds__(JB_THREADS) void jacobi_kernel(const double *__rest
   __shared__ double sgn[RANK];
   __shared__ int done;
   const int mat = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const double *Gm = G + (size_t)mat * D * D;
   double *V = Vws + (size_t)mat * D * D;
-  for (int x = tid; x < D * D; x += JB_THREADS) {
-    const int i = x / D, j = x % D;
-    A[i * JB_LDA + j] = Gm[x];
-    V[x] = i == j ? 1.0 : 0.0;
+  for (int x = tid; x < D * D; x += JB_THREADS) A[(x / D) * JB_LDA + x % D] = Gm[x];
+  // V in registers: lane k holds, for rows i = 8 wave .. 8 wave + 7, the
+  // entries of the two columns of pair k of the current round (vt: the first
+  // index p, vb: the second index q).  Round r pairs (127, r) and
+  // ((r + k) % 127, (r - k) % 127): from one round to the next, the first index
+  // of pair k + 1 becomes that of pair k, the second of pair k - 1 that of pair
+  // k (pair 0 keeps 127 and takes the first index of pair 1; pair 63 takes
+  // its own second index as the first), so the columns move one lane per
+  // round and V never leaves the registers until the end.
+  constexpr int VR = D / (JB_THREADS / 64);      // rows per wave
+  auto top_idx = [&](int r) { return lane == 0 ? D - 1 : (r + lane) % (D - 1); };
+  auto bot_idx = [&](int r) { return lane == 0 ? r : (r - lane + (D - 1)) % (D - 1); };
+  double vt[VR], vb[VR];
+#pragma unroll
+  for (int u = 0; u < VR; ++u) {
+    const int i = wave * VR + u;
+    vt[u] = i == top_idx(0) ? 1.0 : 0.0;
+    vb[u] = i == bot_idx(0) ? 1.0 : 0.0;
   }
   __syncthreads();
 
@@ -248,27 +263,29 @@ __global__ __launch_bounds__(JB_THREADS) void jacobi_kernel(const double *__rest
         *aq = s * a + c * bq;
       }
       __syncthreads();
-      // columns p, q of A <- A J, and of V <- V J; every V element of the
-      // round is loaded before any is stored, so the global round trips overlap
+      // columns p, q of A <- A J
+      for (int x = tid; x < (D / 2) * D; x += JB_THREADS) {
+        const int k = x / D, i = x % D;
+        const double c = rc[k], s = rs[k];
+        double *ap = A + i * JB_LDA + rp[k], *aq = A + i * JB_LDA + rq[k];
+        const double a = *ap, bq = *aq;
+        *ap = c * a - s * bq;
+        *aq = s * a + c * bq;
+      }
+      // V <- V J on this lane's pair, then the columns move to the next
+      // round's lanes (see above)
       {
-        constexpr int PER = (D / 2) * D / JB_THREADS;
-        double va[PER], vb[PER];
+        const double c = rc[lane], s = rs[lane];
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          const int x = tid + u * JB_THREADS, k = x / D, i = x % D;
-          va[u] = V[(size_t)i * D + rp[k]];
-          vb[u] = V[(size_t)i * D + rq[k]];
-        }
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          const int x = tid + u * JB_THREADS, k = x / D, i = x % D;
-          const double c = rc[k], s = rs[k];
-          double *ap = A + i * JB_LDA + rp[k], *aq = A + i * JB_LDA + rq[k];
-          const double a = *ap, bq = *aq;
-          *ap = c * a - s * bq;
-          *aq = s * a + c * bq;
-          V[(size_t)i * D + rp[k]] = c * va[u] - s * vb[u];
-          V[(size_t)i * D + rq[k]] = s * va[u] + c * vb[u];
+        for (int u = 0; u < VR; ++u) {
+          const double a = vt[u], b = vb[u];
+          vt[u] = c * a - s * b;
+          vb[u] = s * a + c * b;
+          const double from_next_top = __shfl_down(vt[u], 1);    // lane k + 1's first column
+          const double from_prev_bot = __shfl_up(vb[u], 1);      // lane k - 1's second column
+          const double t = lane == 0 ? vt[u] : (lane == 63 ? vb[u] : from_next_top);
+          vb[u] = lane == 0 ? from_next_top : from_prev_bot;
+          vt[u] = t;
         }
       }
       __syncthreads();
@@ -280,6 +297,14 @@ __global__ __launch_bounds__(JB_THREADS) void jacobi_kernel(const double *__rest
     }
   }
 
+  // V to the workspace: after whole sweeps the lanes hold round 0's columns
+#pragma unroll
+  for (int u = 0; u < VR; ++u) {
+    const int i = wave * VR + u;
+    V[(size_t)i * D + top_idx(0)] = vt[u];
+    V[(size_t)i * D + bot_idx(0)] = vb[u];
+  }
+  __syncthreads();
   // eigenvalues in descending order (equal values: lower index first)
   if (tid < D) {
     const double d = A[tid * JB_LDA + tid];
