@@ -84,3 +84,27 @@ def test_dense_step_graph_replays():
         runner.replay()
         torch.cuda.synchronize()
         assert torch.equal(g.layer.out, want[0]) and torch.equal(g.layer.lse, want[1]), rep
+
+
+def test_dense_step_full_size_graph():
+    """The 8 x 250K benchmark cache through a graph-replayed dense step (as
+    bench.py --dense times it): sampled (sequence, KV head) pairs against the
+    oracle over each row's last window + topk tokens."""
+    cfg = C.C3
+    flush(f"[dense] full size {cfg.name}")
+    case = make_case(cfg)
+    g = GpuCase(case)
+    g.layer.build_sketch(0, g.T)
+    runner = StepRunner(g.layer, dense=True)
+    runner.capture(g.q)
+    runner.replay()
+    torch.cuda.synchronize()
+    pairs = sorted({(0, 0), (cfg.B - 1, cfg.Hkv - 1), (cfg.B // 2, cfg.Hkv // 2)})
+    c = case
+    ref = orc.decode_step(c.q, c.K, c.V, None, None, c.seq_len, c.basis, c.key_scale,
+                          g.window + g.topk, 0, 1, cfg.kv_dtype, heads=pairs)
+    out, lse = g.layer.out.cpu().numpy(), g.layer.lse.cpu().numpy()
+    for (b, h), r in ref.items():
+        sl = slice(h * cfg.g, (h + 1) * cfg.g)
+        assert_attn_close(out[b, 0, sl], r["out"][0], f"{(b, h)}")
+        lse_close(lse[b, 0, sl], r["lse"][0], f"{(b, h)}")
