@@ -1,0 +1,93 @@
+"""GPU parity on seeded random shapes: batch, verify rows (up to 8), query
+group size (up to 8), pooling (up to 64), KV storage, window (0 included),
+top-k (1 included) and ragged lengths (empty rows included), each drawn per
+case.  The named workloads never reach most of these combinations.
+
+Per case, through the C ABI against the oracle:
+* the GPU's key and query sketches within the sketch bound;
+* scores bit-exact given the oracle's codes;
+* selection bit-exact given the oracle's scores (fused-histogram path too);
+* attention within the output bound given the oracle's indices.
+"""
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_sketch_amd import configs as C
+from long_context_sparse_sketch_amd.synth import make_case
+from oracle import sks_oracle as orc
+from tests.gpu_util import (GpuCase, assert_attn_close, flush, lse_close, oracle_key_projection,
+                            ref_arrays, sketch_ok)
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = list(range(48))
+
+
+def draw(seed):
+    rng = np.random.default_rng(7000 + seed)
+    R = int(rng.choice([1, 1, 2, 3, 8]))
+    Hkv = int(rng.integers(1, 4))
+    G = int(rng.integers(1, 9))
+    pool = int(rng.choice([1, 1, 1, 1, 2, 4, 7, 64]))
+    kv = C.KV_BF16 if pool > 1 else int(rng.choice([C.KV_BF16, C.KV_I8, C.KV_I4]))
+    window = int(rng.choice([0, 1, 17, int(rng.integers(0, 1500))]))
+    topk = int(rng.choice([1, 3, int(rng.integers(1, 2000))]))
+    B = int(rng.integers(1, 4))
+    L = max(int(rng.integers(2, 6000)), pool + 2)
+    cfg = C.Config(f"rand{seed}", 100 + seed, B=B, R=R, Hq=Hkv * G, Hkv=Hkv, L=L, window=window,
+                   topk=topk, pool=pool, kv_dtype=kv, needle_kind="random",
+                   needle_count=min(16, L - 1), needle_amp=3.0, needle_noise=0.5)
+    lengths = rng.integers(0, L + 1, B).astype(np.int32)
+    lengths[0] = L                                  # one full-length sequence
+    if B > 1 and rng.random() < 0.5:
+        lengths[1] = 0                              # an empty one
+    return cfg, lengths
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_shape(seed):
+    cfg, sl = draw(seed)
+    flush(f"[random] seed {seed}: B={cfg.B} R={cfg.R} Hq/Hkv={cfg.Hq}/{cfg.Hkv} L={sl.tolist()} "
+          f"W={cfg.window} k={cfg.topk} r={cfg.pool} kv={C.KV_NAMES[cfg.kv_dtype]}")
+    case = make_case(cfg)
+    g = GpuCase(case, seq_len=sl)
+    ref = g.oracle()
+    arr = ref_arrays(ref, cfg, case.B, g.topk, g.layer.NB)
+    g.run_full()
+
+    # sketches (the GPU's own)
+    S = g.layer.S.cpu().numpy()
+    s = float(case.key_scale[0])
+    for b in range(case.B):
+        for h in range(cfg.Hkv):
+            y, _, _ = oracle_key_projection(case, b, h, cfg.pool)
+            n = min(g.layer.NB, y.shape[0])
+            assert sketch_ok(S[b, h, :n], y[:n], s).all(), (b, h)
+    qsk = g.layer.qsk.cpu().numpy()
+    qf = orc.bf16_to_f64(case.q)
+    for b in range(case.B):
+        for i in range(cfg.R):
+            for h in range(cfg.Hkv):
+                _, qs, y = orc.query_sketch(qf[b, i, h * cfg.g:(h + 1) * cfg.g], case.basis)
+                assert sketch_ok(qsk[b, i, h], y, qs).all(), (b, i, h)
+
+    # scores on the oracle's codes (with the fused histogram), then selection
+    g.layer.score(qsk=torch.from_numpy(arr["qcode"]).cuda(),
+                  S=torch.from_numpy(arr["kcodes"]).cuda())
+    g.layer.idx.fill_(-7)
+    g.layer.select()
+    torch.cuda.synchronize()
+    got = g.layer.scores.cpu().numpy()
+    for (b, h), r in ref.items():
+        for i in range(cfg.R):
+            n = len(r["scores"][i])
+            assert np.array_equal(got[b, i, h, :n], r["scores"][i]), (b, i, h)
+    assert np.array_equal(g.layer.idx.cpu().numpy(), arr["idx"])
+    assert np.array_equal(g.layer.n_sel.cpu().numpy(), arr["n_sel"])
+
+    # attention on the oracle's indices
+    g.layer.attend(g.q, idx=torch.from_numpy(arr["idx"]).cuda())
+    torch.cuda.synchronize()
+    assert_attn_close(g.layer.out.cpu().numpy(), arr["out"], cfg.name)
+    lse_close(g.layer.lse.cpu().numpy(), arr["lse"], cfg.name)
