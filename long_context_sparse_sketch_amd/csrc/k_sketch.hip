@@ -334,6 +334,26 @@ __global__ __launch_bounds__(PM_THREADS) void pool_mean_kernel(
       make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Lane c's basis row (128 fp32) into registers.  The row wave and the query
+// wave issue these loads first, so that they overlap the key / query loads,
+// and then dot the row with the staged vector in the order d = 0 .. 127.
+__device__ __forceinline__ void load_basis_row(const float *__restrict__ Prow, float4 (&pr)[D / 4]) {
+#pragma unroll
+  for (int k = 0; k < D / 4; ++k) pr[k] = reinterpret_cast<const float4 *>(Prow)[k];
+}
+__device__ __forceinline__ float dot_basis_row(const float4 (&pr)[D / 4], const float *x) {
+  float y = 0.f;
+#pragma unroll
+  for (int k = 0; k < D / 4; ++k) {
+    const float4 xv = reinterpret_cast<const float4 *>(x)[k];
+    y = __builtin_fmaf(pr[k].x, xv.x, y);
+    y = __builtin_fmaf(pr[k].y, xv.y, y);
+    y = __builtin_fmaf(pr[k].z, xv.z, y);
+    y = __builtin_fmaf(pr[k].w, xv.w, y);
+  }
+  return y;
+}
+
 // Few rows per (b, h) -- the per-step append of the rows' own tokens: one
 // wave per sketch row.  The 128-element key (or pooled block) is staged in
 // LDS, lane c dots basis row c with it, so the latency is that of one row
@@ -350,13 +370,15 @@ __device__ void sketch_row_wave(const void *__restrict__ K, const void *__restri
                                 int NB, int pool, int append, int t_begin, int t_end,
                                 int8_t *__restrict__ S, uint16_t *__restrict__ Kp,
                                 uint16_t *__restrict__ Vp, int bh, int jx) {
-  __shared__ float x[D];
+  __shared__ __align__(16) float x[D];
   const int b = bh / Hkv, h = bh % Hkv;
   int j_lo, j_hi;
   sketch_range(append, seq_len, b, T_max, R, pool, NB, t_begin, t_end, j_lo, j_hi);
   const int j = j_lo + jx;
   if (j >= j_hi) return;
   const int lane = threadIdx.x;
+  float4 pr[D / 4];
+  load_basis_row(basis + (basis_per_head ? (size_t)h * RANK * D : 0) + (size_t)lane * D, pr);
   if (pool == 1) {
     if (append) {
       K = Kh;
@@ -405,10 +427,7 @@ __device__ void sketch_row_wave(const void *__restrict__ K, const void *__restri
     }
   }
   __syncthreads();
-  const float *Prow = basis + (basis_per_head ? (size_t)h * RANK * D : 0) + (size_t)lane * D;
-  float y = 0.f;
-#pragma unroll 8
-  for (int d = 0; d < D; ++d) y = __builtin_fmaf(Prow[d], x[d], y);
+  const float y = dot_basis_row(pr, x);
   S[((size_t)bh * NB + j) * RANK + lane] = key_code(y, 1.0f / key_scale[h]);
 }
 
@@ -430,23 +449,31 @@ __global__ __launch_bounds__(64) void sketch_rows_small_kernel(
 __device__ void sketch_query_wave(const uint16_t *__restrict__ q, int R, int Hq, int Hkv,
                                   const float *__restrict__ basis, int basis_per_head,
                                   int8_t *__restrict__ qsk, float *__restrict__ qscale, int seg) {
-  __shared__ float qbar[D];                    // seg = (b * R + i) * Hkv + h
+  __shared__ __align__(16) float qbar[D];     // seg = (b * R + i) * Hkv + h
   const int h = seg % Hkv, bi = seg / Hkv;
   const int g = Hq / Hkv;
   const int lane = threadIdx.x;
+  float4 pr[D / 4];
+  load_basis_row(basis + (basis_per_head ? (size_t)h * RANK * D : 0) + (size_t)lane * D, pr);
+  // the group's queries, up to 8 loads in flight, summed in head order
   const uint16_t *qg = q + ((size_t)bi * Hq + (size_t)h * g) * D;
   float s0 = 0.f, s1 = 0.f;
-  for (int j = 0; j < g; ++j) {
-    uint32_t w = *reinterpret_cast<const uint32_t *>(qg + (size_t)j * D + 2 * lane);
-    s0 += bf16_lo(w);
-    s1 += bf16_hi(w);
+  for (int j0 = 0; j0 < g; j0 += 8) {
+    uint32_t w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      w[u] = j0 + u < g ? *reinterpret_cast<const uint32_t *>(qg + (size_t)(j0 + u) * D + 2 * lane) : 0u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < g) {
+        s0 += bf16_lo(w[u]);
+        s1 += bf16_hi(w[u]);
+      }
   }
   qbar[2 * lane] = s0 / (float)g;
   qbar[2 * lane + 1] = s1 / (float)g;
   __syncthreads();
-  const float *Prow = basis + (basis_per_head ? (size_t)h * RANK * D : 0) + (size_t)lane * D;
-  float y = 0.f;
-  for (int d = 0; d < D; ++d) y = __builtin_fmaf(Prow[d], qbar[d], y);
+  const float y = dot_basis_row(pr, qbar);
   float amax = fabsf(y);
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   float scale = amax / 127.0f;
