@@ -101,9 +101,10 @@ typedef struct sks_kv {
    * PCIe.  With a hot tier, K, V (and their scales) may be pinned host memory
    * mapped into the device's address space (pass the device address, e.g.
    * from hipHostGetDevicePointer); they are then read only for the selected
-   * far rows and for host-range key sketch builds.  The exact window and the
-   * rows' own tokens (APPEND) are read from the ring below, in which
-   * position p sits in slot p % W_hot.  The caller keeps the ring current:
+   * far rows, for host-range key sketch builds and, in a dense step, for the
+   * window positions older than the ring.  The exact window and the rows' own
+   * tokens (APPEND) are read from the ring below, in which position p sits
+   * in slot p % W_hot.  The caller keeps the ring current:
    * it must hold every position in [L_0 + rows - 1 - W_hot, L_0 + rows - 1).
    * Needs pool == 1 (SKS_ERR_UNSUPPORTED otherwise). */
   const void *K_hot;        /* [B][Hkv][W_hot][row] same format as K, or NULL   */

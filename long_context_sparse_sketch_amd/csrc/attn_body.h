@@ -232,10 +232,13 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   // Descriptor of an entry: the row to gather and whether it takes part
   // (bit 0).  The row indexes the token rows of the full cache, the pooled
   // rows when bit 1 is set, or the slots of the hot ring when bit 2 is set
-  // (window rows).  Invalid entries point at ring slot 0, which always
-  // exists, so the gathers below need no branches.  Lane l holds entries
-  // e_wave + l (row0, flag0) and e_wave + 64 + l (row1, flag1).
+  // (window rows).  A window row older than the ring holds (positions below
+  // ring_lo; only the dense step's longer window reaches them) comes from the
+  // full cache.  Invalid entries point at ring slot 0, which always exists,
+  // so the gathers below need no branches.  Lane l holds entries e_wave + l
+  // (row0, flag0) and e_wave + 64 + l (row1, flag1).
   const int W_hot = a.W_hot;
+  const int ring_lo = L0 + R - 1 - W_hot;
   auto describe = [&](int e, int sel, int &row, int &flag) {
     row = 0;
     flag = 4;
@@ -248,8 +251,14 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
       }
     } else if (e < rg.n_ent) {
       // (pooled caches have no hot tier: the ring is the full cache)
-      row = POOLED ? rg.ws + (e - rg.k_eff) : hot_slot(rg.ws + (e - rg.k_eff), W_hot);
-      flag = 5;
+      const int pos = rg.ws + (e - rg.k_eff);
+      if (!POOLED && pos < ring_lo) {
+        row = pos;
+        flag = 1;
+      } else {
+        row = POOLED ? pos : hot_slot(pos, W_hot);
+        flag = 5;
+      }
     }
   };
   int row0, flag0, row1, flag1;

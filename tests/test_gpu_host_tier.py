@@ -190,3 +190,37 @@ def test_host_tier_full_size_int4():
     torch.cuda.synchronize()
     for n in OUTS:
         assert torch.equal(want[n].view(torch.uint8), getattr(lay, n).view(torch.uint8)), n
+
+
+@pytest.mark.parametrize("short", [True, False], ids=["within_window_plus_topk", "long"])
+def test_host_tier_dense_step(short):
+    """A dense step attends the last window + topk tokens, more than the ring
+    holds: the positions older than the ring come from host memory, the rest
+    from the ring (the host copy of the latter is poisoned)."""
+    cfg = C.small(C.C3)
+    case = make_case(cfg)
+    B = case.B
+    if short:     # longer than the ring, within window + topk
+        sl = np.array([cfg.window + cfg.topk - 3 - 211 * b for b in range(B)], np.int32)
+    else:
+        sl = np.array([cfg.L - 5 * b for b in range(B)], np.int32)
+    g = GpuCase(case, seq_len=sl)
+    g.layer.build_sketch(0, g.T)
+    for n in OUTS[1:]:
+        getattr(g.layer, n).view(torch.uint8).fill_(0x5A)
+    g.layer.step(g.q, dense=True)
+    torch.cuda.synchronize()
+    want = {n: getattr(g.layer, n).clone() for n in OUTS}
+    W_hot = g.window + cfg.R + 37
+    assert int(sl.min()) > W_hot
+    cache, host, ring = build_tier(g, W_hot)
+    lay = SparseDecodeLayer(B, cfg.R, cfg.Hq, cfg.Hkv, g.T, g.window, g.topk, g.pool,
+                            cfg.kv_dtype).bind(cache, g.basis, g.key_scale)
+    lay.S.copy_(g.layer.S)
+    poison_host(g, host)
+    for n in OUTS[1:]:
+        getattr(lay, n).view(torch.uint8).fill_(0x5A)
+    lay.step(g.q, dense=True)
+    torch.cuda.synchronize()
+    for n in OUTS:
+        assert torch.equal(want[n].view(torch.uint8), getattr(lay, n).view(torch.uint8)), n
