@@ -127,6 +127,21 @@ def small(cfg: Config) -> Config:
                       needle_count=min(cfg.needle_count, 40 if cfg.cid != 3 else 150))
 
 
+def full_set(cfg: Config) -> Config:
+    """A reduced context with the workload's full attention set: the same
+    window, top-k, pooling, rows, heads and dtype, a far region a little over
+    twice top-k, and enough sequences that the attention pass runs in its
+    deeper splits (384 entries for bf16, 256 for int8 / int4), which the
+    `small` shapes never reach: at least 512 workgroups of 384-entry splits
+    (segments x splits)."""
+    set_max = cfg.topk + cfg.window + cfg.pool - 1
+    per_seq = cfg.R * cfg.Hkv * -(-set_max // 384)
+    B = max(1, -(-512 // per_seq))
+    L = cfg.window + 2 * cfg.topk * cfg.pool + 1234
+    return cfg.scaled(name=cfg.name + "_full_set", B=B, L=L,
+                      needle_count=min(cfg.needle_count, 40 if cfg.cid != 3 else 150))
+
+
 def with_kv(cfg: Config, kv_dtype: int) -> Config:
     """`cfg` with another KV storage type (name suffixed with it unless it is
     the config's own).  The int4 cache is the one the claims list of "8

@@ -1,7 +1,6 @@
-// Device code of the sparse decode attention shared by its kernels: one
-// attention slot of one segment as a template, so that it runs both in its
-// own kernel and as one role of a combined launch.  (Algorithm: see
-// k_attn.hip.)
+// Device code of the sparse decode attention: one attention slot of one
+// segment as a template over the group size, the KV storage, pooling and the
+// tiles per wave.  (Algorithm: see k_attn.hip.)
 #pragma once
 
 #include <type_traits>
@@ -13,9 +12,6 @@ namespace sks {
 namespace {
 
 constexpr int AT_THREADS = 256;
-constexpr int AT_U = 4;                            // entries per row-slot per step
-constexpr int AT_WAVE_ENTRIES = ATTN_SPLIT / (AT_THREADS / 64);     // 64
-constexpr int AT_STEPS = AT_WAVE_ENTRIES / (4 * AT_U);              // 4
 constexpr float NEG_INF = -__builtin_huge_valf();
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -59,9 +55,13 @@ __device__ __forceinline__ void merge_state(float &m, float &l, float (&a)[N], f
 // leaves 16 - G rows idle, which costs nothing here: the pass is bound by
 // the gathers.
 constexpr int AM_TILE = 32;
-constexpr int AM_WAVE_ENTRIES = ATTN_SPLIT / (AT_THREADS / 64);   // 96: three tiles
-constexpr int AM_TILES = AM_WAVE_ENTRIES / AM_TILE;
-static_assert(AM_WAVE_ENTRIES <= 128, "two entry descriptors per lane");
+// Entries per workgroup (the attention split): 4 waves of TILES tiles each.
+// More tiles per wave keep a tile's gathers in flight while the previous one
+// is consumed; fewer make more workgroups and shorter chains (see
+// attn_split).
+template <int TILES>
+constexpr int attn_split_entries() { return (AT_THREADS / 64) * TILES * AM_TILE; }
+static_assert(attn_split_entries<3>() == ATTN_SPLIT, "the largest split");
 constexpr int VROW = 132;                 // LDS V row stride in bf16 (264 B: conflict-free reads)
 constexpr float RESCALE_SLACK = 8.0f;
 
@@ -120,24 +120,30 @@ __device__ __forceinline__ float row16_max_f(float x) {
   return x;
 }
 
-// Merge of the partials of one (segment, query head j, dim d) over all splits,
-// in split order, MB splits at a time so that their loads are in flight
-// together; the order of operations is fixed by the shape.
-constexpr int MB = 8;
-__device__ void merge_splits(const float2 *part_ml, const float *part_acc, int seg, int j, int d,
-                             int nsplit, int G, int Hkv, float *out, float *lse) {
-  const int h = seg % Hkv, bi = seg / Hkv;
-  const size_t orow = (size_t)bi * Hkv * G + (size_t)h * G + j;
-  const size_t base = (size_t)seg * nsplit;
-  const float *ml = reinterpret_cast<const float *>(part_ml);
-  float M = NEG_INF, Lsum = 0.f, A = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += MB) {
+// Merge of the partials of one (segment, query head j, dim d) over all
+// splits.  The splits are cut into merge_parts(nsplit) <= MP contiguous
+// parts, merged in parallel (one group of D threads per part, MB splits'
+// loads in flight at a time), and the parts' states are then combined in
+// part order through LDS: the order of operations is fixed by the shape.
+constexpr int MP = 4;
+constexpr int MB = 16;
+// one part per MB splits (one round of loads each), at most MP
+inline int merge_parts(int nsplit) { return std::min(MP, std::max(1, (nsplit + MB - 1) / MB)); }
+
+// (M, Lsum, A) over splits [s0, s1) of the segment's partials at `base`
+__device__ __forceinline__ void merge_range(const float *ml, const float *part_acc, size_t base,
+                                            int j, int d, int s0, int s1, int G, float &M,
+                                            float &Lsum, float &A) {
+  M = NEG_INF;
+  Lsum = 0.f;
+  A = 0.f;
+  for (int c0 = s0; c0 < s1; c0 += MB) {
     float mm[MB], ll[MB], a[MB];
 #pragma unroll
     for (int k = 0; k < MB; ++k) {
-      const int sp = min(s0 + k, nsplit - 1);
+      const int sp = min(c0 + k, s1 - 1);
       const size_t e = (base + sp) * G + j;
-      mm[k] = s0 + k < nsplit ? ml[2 * e] : NEG_INF;
+      mm[k] = c0 + k < s1 ? ml[2 * e] : NEG_INF;
       ll[k] = ml[2 * e + 1];
       a[k] = part_acc[e * D + d];
     }
@@ -156,19 +162,51 @@ __device__ void merge_splits(const float2 *part_ml, const float *part_acc, int s
     }
     M = Mn;
   }
-  if (M == NEG_INF) {
+}
+
+// One workgroup of D x merge_parts(nsplit) threads per (segment, query head
+// j): thread (d, p) merges dim d over part p of the splits.
+__device__ void merge_splits(const float2 *part_ml, const float *part_acc, int seg, int j,
+                             int nsplit, int G, int Hkv, float *out, float *lse) {
+  __shared__ float s_a[MP][D];
+  __shared__ float s_m[MP][2];
+  const int d = threadIdx.x, p = threadIdx.y, np = blockDim.y;
+  const int per = (nsplit + np - 1) / np;
+  const int s0 = min(p * per, nsplit), s1 = min(s0 + per, nsplit);
+  float M, Lsum, A;
+  merge_range(reinterpret_cast<const float *>(part_ml), part_acc, (size_t)seg * nsplit, j, d, s0,
+              s1, G, M, Lsum, A);
+  s_a[p][d] = A;
+  if (d == 0) {
+    s_m[p][0] = M;
+    s_m[p][1] = Lsum;
+  }
+  __syncthreads();
+  if (p != 0) return;
+  float Mt = NEG_INF;
+  for (int q = 0; q < np; ++q) Mt = fmaxf(Mt, s_m[q][0]);
+  const int h = seg % Hkv, bi = seg / Hkv;
+  const size_t orow = (size_t)bi * Hkv * G + (size_t)h * G + j;
+  if (Mt == NEG_INF) {
     out[orow * D + d] = 0.f;
     if (d == 0 && lse) lse[orow] = NEG_INF;
     return;
   }
-  out[orow * D + d] = A / Lsum;
-  if (d == 0 && lse) lse[orow] = (M + __log2f(Lsum)) * 0.69314718055994530942f;
+  float Lt = 0.f, At = 0.f;
+  for (int q = 0; q < np; ++q) {
+    const float mq = s_m[q][0];
+    const float wt = mq == NEG_INF ? 0.f : exp2_fast(mq - Mt);
+    Lt += s_m[q][1] * wt;
+    At += s_a[q][d] * wt;
+  }
+  out[orow * D + d] = At / Lt;
+  if (d == 0 && lse) lse[orow] = (Mt + __log2f(Lt)) * 0.69314718055994530942f;
 }
 
 // Arguments of the attention pass.  The partials of a segment occupy nsplit
-// slots: slot s covers entries [s * ATTN_SPLIT, (s + 1) * ATTN_SPLIT) of the
-// attention set (selected entries first, then the window); the merge
-// combines the slots in this order.
+// slots: slot s covers entries [s * split, (s + 1) * split) of the attention
+// set (selected entries first, then the window), split being 128, 256 or
+// 384 as chosen by attn_split(); the merge combines the slots in this order.
 struct AttnArgs {
   const uint16_t *q;
   const void *K, *V;                  // full cache (selected far rows)
@@ -180,6 +218,7 @@ struct AttnArgs {
   const uint16_t *Kp, *Vp;
   float sm_log2;
   int R, Hkv, T_max, NB, window, pool, topk, nsplit;
+  int split;                          // entries per slot: attn_split() of the shape
   int kmax;                           // selected entries per row at most: topk, or 0 (dense step)
   float2 *part_ml;
   float *part_acc;
@@ -192,10 +231,14 @@ struct AttnLds {
 };
 
 // One attention slot (see AttnArgs) of one segment, by a workgroup of
-// AT_THREADS threads.
-template <int G, int DT, bool POOLED>
+// AT_THREADS threads, TILES tiles of AM_TILE entries per wave.
+template <int G, int DT, bool POOLED, int TILES>
 __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head");
+  constexpr int WAVE_ENTRIES = TILES * AM_TILE;
+  constexpr int SPLIT = attn_split_entries<TILES>();
+  static_assert(WAVE_ENTRIES <= 128, "two entry descriptors per lane");
+  constexpr bool TWO = WAVE_ENTRIES > 64;            // the second descriptor is used
   const uint16_t *__restrict__ q = a.q;
   const void *__restrict__ K = a.K;
   const void *__restrict__ V = a.V;
@@ -221,13 +264,13 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   // loaded together with the length, before it is known whether the entries
   // are selected ones (the addresses are clamped into the segment's idx row,
   // so always in bounds).
-  const int e_wave = slot * ATTN_SPLIT + wave * AM_WAVE_ENTRIES;
+  const int e_wave = slot * SPLIT + wave * WAVE_ENTRIES;
   const int32_t *idx_row = idx + (size_t)seg * topk;
   const int sel0 = idx_row[min(e_wave + lane, topk - 1)];
-  const int sel1 = idx_row[min(e_wave + 64 + lane, topk - 1)];
+  const int sel1 = TWO ? idx_row[min(e_wave + 64 + lane, topk - 1)] : -1;
   const int L0 = clamp_len(seq_len[b], T_max, R);
   const RowGeom rg = row_geom(L0, i, window, pool, a.kmax);
-  const int e_hi = min((slot + 1) * ATTN_SPLIT, rg.n_ent);   // end of this slot's entries
+  const int e_hi = min((slot + 1) * SPLIT, rg.n_ent);   // end of this slot's entries
 
   // Descriptor of an entry: the row to gather and whether it takes part
   // (bit 0).  The row indexes the token rows of the full cache, the pooled
@@ -261,12 +304,12 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
       }
     }
   };
-  int row0, flag0, row1, flag1;
+  int row0, flag0, row1 = 0, flag1 = 4;
   describe(e_wave + lane, sel0, row0, flag0);
-  describe(e_wave + 64 + lane, sel1, row1, flag1);
+  if constexpr (TWO) describe(e_wave + 64 + lane, sel1, row1, flag1);
   // descriptor of wave entry j (a compile-time tile offset plus a lane value)
   auto desc = [&](int j, int &r, int &f) {
-    if (j < 64) {
+    if (!TWO || j < 64) {
       r = __shfl(row0, j);
       f = __shfl(flag0, j);
     } else {
@@ -310,8 +353,10 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
     const uint16_t *Vsht = a.Vsh + ((size_t)b * Hkv + h) * W_hot;
     ksd0 = f16_bits_to_float(((flag0 & 4) ? Ksht : Kst)[row0]);
     vsd0 = f16_bits_to_float(((flag0 & 4) ? Vsht : Vst)[row0]);
-    ksd1 = f16_bits_to_float(((flag1 & 4) ? Ksht : Kst)[row1]);
-    vsd1 = f16_bits_to_float(((flag1 & 4) ? Vsht : Vst)[row1]);
+    if constexpr (TWO) {
+      ksd1 = f16_bits_to_float(((flag1 & 4) ? Ksht : Kst)[row1]);
+      vsd1 = f16_bits_to_float(((flag1 & 4) ? Vsht : Vst)[row1]);
+    }
   }
 
   // int4: the K operand is code + I4_BIAS, so each logit carries
@@ -384,8 +429,8 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
       if constexpr (Q) {
         d.k[t][0] = ld(kbase + off + 16 * g);
         if constexpr (I8) d.k[t][1] = ld(kbase + off + 64 + 16 * g);
-        d.ks[t] = j < 64 ? __shfl(ksd0, j) : __shfl(ksd1, j - 64);
-        d.vs[t] = j < 64 ? __shfl(vsd0, j) : __shfl(vsd1, j - 64);
+        d.ks[t] = (!TWO || j < 64) ? __shfl(ksd0, j) : __shfl(ksd1, j - 64);
+        d.vs[t] = (!TWO || j < 64) ? __shfl(vsd0, j) : __shfl(vsd1, j - 64);
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c) d.k[t][c] = ld(kbase + off + (32 * c + 8 * g) * 2);
@@ -532,9 +577,9 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   Tile cur, nxt;
   gather(0, cur);
 #pragma unroll
-  for (int tile = 0; tile < AM_TILES; ++tile) {
+  for (int tile = 0; tile < TILES; ++tile) {
     __builtin_amdgcn_sched_barrier(0);
-    if (tile + 1 < AM_TILES) gather(tile + 1, nxt);
+    if (tile + 1 < TILES) gather(tile + 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
     consume(cur);
     cur = nxt;
@@ -596,10 +641,24 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
 
 }
 
+// Entries per attention slot for a shape: 128 (one tile per wave) when
+// 384-entry slots would give fewer than ATTN_SMALL_BELOW workgroups
+// (segments x slots); else 384 (three tiles) for bf16 rows, whose gathers
+// need the deeper pipeline, and 256 (two tiles) for int8 / int4 rows, whose
+// smaller gathers leave each wave's chain of dependent steps the longer part.
+// A function of the shape alone, so the split count, the workspace and the
+// merge order are fixed by the shape.
+inline int attn_split(const Shape &s) {
+  const long set = (long)s.topk + s.window + s.pool - 1;   // the largest attention set
+  const long nseg = (long)s.B * s.R * s.Hkv;
+  if (nseg * ceil_div(set, ATTN_SPLIT) < ATTN_SMALL_BELOW) return attn_split_entries<1>();
+  return s.dtype == SKS_KV_BF16 ? attn_split_entries<3>() : attn_split_entries<2>();
+}
+
 // attention slots of a segment (the largest attention set: topk selected
 // entries and a window of up to window + pool - 1 tokens)
 inline int attn_nsplit(const Shape &s) {
-  return ceil_div((long)s.topk + s.window + s.pool - 1, ATTN_SPLIT);
+  return ceil_div((long)s.topk + s.window + s.pool - 1, attn_split(s));
 }
 
 }  // namespace

@@ -4,11 +4,13 @@
 // attention" over the picked rows in "What it took" on the page "8 agents x
 // 250K context, concurrently, on two 3090s").
 //
-// Split-K flash decoding.  A workgroup takes ATTN_SPLIT consecutive entries
-// of one (sequence, row, KV head) attention set and all G query heads of
-// that KV head; each of its 4 waves takes 96 of them as three tiles of 32
-// (see the matrix-core kernel below), gathering tile t + 1 while it
-// computes tile t.  Online softmax in the log2 domain;
+// Split-K flash decoding.  A workgroup takes ATTN_SPLIT (384) consecutive
+// entries of one (sequence, row, KV head) attention set and all G query heads
+// of that KV head; each of its 4 waves takes 96 of them as three tiles of 32
+// (see attn_body.h), gathering tile t + 1 while it computes tile t.  Shapes
+// whose 384-entry splits would not fill the chip take 128 entries per
+// workgroup (one tile per wave), and int8 / int4 caches 256 (two tiles).
+// Online softmax in the log2 domain;
 // the waves' states are merged through LDS and the workgroup writes one
 // partial (m, l, acc[G][128]).  A second kernel merges the partials of every
 // split in split order, so results are deterministic.
@@ -17,31 +19,42 @@
 namespace sks {
 namespace {
 
-// One workgroup of 128 threads per (segment, query head of the group).
-__global__ __launch_bounds__(D) void attn_merge_kernel(const float2 *__restrict__ part_ml,
-                                                       const float *__restrict__ part_acc,
-                                                       int nsplit, int G, int Hkv,
-                                                       float *__restrict__ out,
-                                                       float *__restrict__ lse) {
-  merge_splits(part_ml, part_acc, blockIdx.x, blockIdx.y, threadIdx.x, nsplit, G, Hkv, out, lse);
+// One workgroup of D x merge_parts(nsplit) threads per (segment, query head
+// of the group).
+__global__ __launch_bounds__(D * MP) void attn_merge_kernel(const float2 *__restrict__ part_ml,
+                                                            const float *__restrict__ part_acc,
+                                                            int nsplit, int G, int Hkv,
+                                                            float *__restrict__ out,
+                                                            float *__restrict__ lse) {
+  merge_splits(part_ml, part_acc, blockIdx.x, blockIdx.y, nsplit, G, Hkv, out, lse);
 }
 
-template <int G, int DT, bool POOLED>
+template <int G, int DT, bool POOLED, int TILES>
 __global__ __launch_bounds__(AT_THREADS, 2) void attn_kernel(AttnArgs a, int slot0) {
   __shared__ AttnLds lds;
-  attn_body<G, DT, POOLED>(a, blockIdx.y, slot0 + blockIdx.x, lds);
+  attn_body<G, DT, POOLED, TILES>(a, blockIdx.y, slot0 + blockIdx.x, lds);
+}
+
+template <int G, int TILES>
+void dispatch_t(dim3 grid, hipStream_t st, const AttnArgs &a, int dtype, int pool, int slot0) {
+  if (dtype == SKS_KV_I8)
+    attn_kernel<G, SKS_KV_I8, false, TILES><<<grid, AT_THREADS, 0, st>>>(a, slot0);
+  else if (dtype == SKS_KV_I4)
+    attn_kernel<G, SKS_KV_I4, false, TILES><<<grid, AT_THREADS, 0, st>>>(a, slot0);
+  else if (pool > 1)
+    attn_kernel<G, SKS_KV_BF16, true, TILES><<<grid, AT_THREADS, 0, st>>>(a, slot0);
+  else
+    attn_kernel<G, SKS_KV_BF16, false, TILES><<<grid, AT_THREADS, 0, st>>>(a, slot0);
 }
 
 template <int G>
 void dispatch_g(dim3 grid, hipStream_t st, const AttnArgs &a, int dtype, int pool, int slot0) {
-  if (dtype == SKS_KV_I8)
-    attn_kernel<G, SKS_KV_I8, false><<<grid, AT_THREADS, 0, st>>>(a, slot0);
-  else if (dtype == SKS_KV_I4)
-    attn_kernel<G, SKS_KV_I4, false><<<grid, AT_THREADS, 0, st>>>(a, slot0);
-  else if (pool > 1)
-    attn_kernel<G, SKS_KV_BF16, true><<<grid, AT_THREADS, 0, st>>>(a, slot0);
+  if (a.split == attn_split_entries<1>())
+    dispatch_t<G, 1>(grid, st, a, dtype, pool, slot0);
+  else if (a.split == attn_split_entries<2>())
+    dispatch_t<G, 2>(grid, st, a, dtype, pool, slot0);
   else
-    attn_kernel<G, SKS_KV_BF16, false><<<grid, AT_THREADS, 0, st>>>(a, slot0);
+    dispatch_t<G, 3>(grid, st, a, dtype, pool, slot0);
 }
 
 }  // namespace
@@ -82,6 +95,7 @@ AttnArgs attn_args(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
   a.pool = s.pool;
   a.topk = s.topk;
   a.kmax = s.topk;
+  a.split = attn_split(s);
   a.nsplit = attn_nsplit(s);
   const size_t n = (size_t)nseg * a.nsplit * G;
   a.part_ml = reinterpret_cast<float2 *>(w.attn);
@@ -109,8 +123,8 @@ hipError_t launch_attn_slots(const AttnArgs &a, int G, int dtype, int nseg, int 
 
 hipError_t launch_attn_merge(const AttnArgs &a, int G, int nseg, float *out, float *lse,
                              hipStream_t st) {
-  attn_merge_kernel<<<dim3(nseg, G), D, 0, st>>>(a.part_ml, a.part_acc, a.nsplit, G, a.Hkv, out,
-                                                 lse);
+  attn_merge_kernel<<<dim3(nseg, G), dim3(D, merge_parts(a.nsplit)), 0, st>>>(a.part_ml, a.part_acc, a.nsplit, G,
+                                                            a.Hkv, out, lse);
   return hipGetLastError();
 }
 

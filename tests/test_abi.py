@@ -180,10 +180,36 @@ def test_workspace_sizes_cover_selection_and_attention(L, cfg):
     NB = cfg.T_max // cfg.pool
     # histograms (zero at rest) + candidates (8 B per sketch row)
     assert nb >= nseg * 2048 * 4 + nseg * NB * 8
-    nsplit = -(-(cfg.topk + cfg.window + cfg.pool - 1) // 256)
+    # attention partials: at least one per 384 entries (the largest split)
+    nsplit = -(-(cfg.topk + cfg.window + cfg.pool - 1) // 384)
     assert nb >= nseg * nsplit * cfg.g * (128 + 2) * 4
     assert L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 0) == 0
     assert L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 9 * cfg.Hkv) == 0
+
+
+SPLIT_CASES = ([(C.small(c), 128) for c in C.ALL]
+               + [(C.full_set(c), 256 if c.kv_dtype else 384) for c in C.ALL[1:]]
+               + [(C.C1, 128), (C.C2, 128), (C.C3, 384), (C.C4, 384), (C.C5, 256),
+                  (C.with_kv(C.C3, C.KV_I4), 256), (C.with_kv(C.C3, C.KV_I8), 256),
+                  (C.with_kv(C.C2, C.KV_I4), 128)])
+
+
+@pytest.mark.parametrize("cfg,split", SPLIT_CASES, ids=[c.name for c, _ in SPLIT_CASES])
+def test_attention_split_follows_the_shape(L, cfg, split):
+    """The attention pass takes 128-entry splits when 384-entry ones would
+    give fewer than 512 workgroups (segments x splits); else 384-entry ones
+    for bf16 rows and 256-entry ones for int8 / int4 rows.  Read off the
+    workspace: only the partials, (m, l, acc[128]) fp32 per query head and
+    split, grow with the group size."""
+    quant = cfg.kv_dtype != C.KV_BF16
+    k = kv(B=cfg.B, Hkv=cfg.Hkv, T=cfg.T_max, dtype=cfg.kv_dtype,
+           Ks=FAKE if quant else None, Vs=FAKE if quant else None)
+    p = sks.params(cfg.window, cfg.topk, cfg.pool, cfg.R)
+    w1 = L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), cfg.Hkv)
+    w2 = L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 2 * cfg.Hkv)
+    nseg = cfg.B * cfg.R * cfg.Hkv
+    nsplit = round((w2 - w1) / (nseg * (8 + 128 * 4)))
+    assert nsplit == -(-(cfg.topk + cfg.window + cfg.pool - 1) // split)
 
 
 def step_desc(**kw):
@@ -215,8 +241,8 @@ def test_decode_step_argument_errors(L):
 
 
 def test_workspace_holds_selection_and_attention_scratch_apart(L):
-    """The combined step runs the final selection and window attention in one
-    launch, so their scratch areas must not overlap: the workspace is the sum."""
+    """The selection scratch and the attention partials are separate regions:
+    the workspace holds their sum (partials: at least one per 384 entries)."""
     k, p = kv(B=8, Hkv=4, T=250000), sks.params(4096, 2048)
     small = L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 24)
     n_sub = -(-250000 // 1024)

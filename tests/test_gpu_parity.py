@@ -1,6 +1,8 @@
 """GPU parity of every step of the HIP path against the CPU oracle, through
 the C ABI, on the five workload shapes reduced to sizes the oracle finishes in
-seconds (several tiles and a ragged tail each)."""
+seconds (several tiles and a ragged tail each).  The reduced shapes run the
+attention pass in its small splits; the full-set shapes (a short context with
+the workloads' own window and top-k, and more sequences) in its large ones."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +19,9 @@ pytestmark = pytest.mark.gpu
 
 CFGS = [C.C1, C.small(C.C2), C.small(C.C3), C.small(C.C4), C.small(C.C5),
         C.with_kv(C.C1, C.KV_I4), C.with_kv(C.small(C.C3), C.KV_I4),
-        C.with_kv(C.small(C.C5), C.KV_I4)]
+        C.with_kv(C.small(C.C5), C.KV_I4),
+        C.full_set(C.C3), C.full_set(C.C4), C.full_set(C.C5),
+        C.with_kv(C.full_set(C.C3), C.KV_I4)]
 
 
 @pytest.fixture(scope="module", params=CFGS, ids=lambda c: c.name)
