@@ -448,6 +448,9 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, case, args.cpu_seconds)
+        # the oracle's rate over the step's algorithmic bytes, as for the GPU
+        line["cpu_baseline"]["GBps"] = (line["cpu_baseline"]["value"]
+                                        * line["detail"]["algorithmic_bytes_per_step"] / 1e9)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
