@@ -200,6 +200,8 @@ int sks_sketch_score(const int8_t *qsk, const int8_t *S, const sks_kv *kv,
  * lower index first among equal scores, written in ascending order to
  * idx[b][i][h][0 .. k_eff) and padded with -1 up to topk.
  * n_sel: [B][R][Hkv] int32 receives k_eff (may be NULL).
+ * Caches of up to 8,388,608 sketch rows (T_max / pool): above that the call
+ * returns SKS_ERR_UNSUPPORTED (so does sks_decode_step).
  * flags: 0, or SKS_TOPK_HIST_READY when sks_sketch_score produced these
  *        scores with this workspace (its histogram is then reused).
  * ws: at least sks_workspace_bytes(); its zero-at-rest region is returned to

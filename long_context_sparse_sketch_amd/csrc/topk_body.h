@@ -1,7 +1,6 @@
-// Device code of the exact top-k selection shared by its kernels: the
-// helpers, and the final pass as a template on the workgroup size, so that it
-// runs both as its own kernel and as one role of a combined launch.
-// (Selection algorithm: see k_topk.hip.)
+// Device code of the exact top-k selection: the helpers shared by its
+// kernels, and the final pass as a template on the workgroup size and the
+// candidate capacity.  (Selection algorithm: see k_topk.hip.)
 #pragma once
 
 #include "sks_internal.h"

@@ -207,6 +207,52 @@ def make_case(cfg: Config, seqs=None, threads: int | None = None) -> Case:
     return Case(cfg, seqs, basis, key_scale, q, K, V, Ks, Vs, seq_len, needles)
 
 
+_TAG_DEVICE = 101
+
+
+def make_case_on_device(cfg: Config, device) -> Case:
+    """The inputs of a bf16-cache `cfg` with K and V drawn on `device`, for
+    caches too large to draw on the host in reasonable time (millions of
+    tokens per sequence): K, V are N(0,1) from torch's generator on the
+    device, seeded from (seed, tag), rounded to bf16 by torch (nearest even);
+    q, basis, key scale, needle positions and needle rows as in `make_case`.
+    Returns a Case whose K and V are device tensors [B][Hkv][T][128] bf16."""
+    import torch
+
+    if cfg.kv_dtype != KV_BF16:
+        raise ValueError("make_case_on_device draws bf16 caches only")
+    B, T, D = cfg.B, cfg.T_max, cfg.D
+    basis = make_basis(cfg)
+    key_scale = np.full((cfg.Hkv,), 1.0 / 16.0, dtype=np.float32)
+    q = np.stack([_query(cfg, b) for b in range(B)])
+    qf = _bf16_bits_to_f32(q)
+    seed = int(np.random.SeedSequence(cfg.seed, spawn_key=(_TAG_DEVICE,)).generate_state(1)[0])
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    K = torch.empty((B, cfg.Hkv, T, D), dtype=torch.bfloat16, device=device)
+    V = torch.empty_like(K)
+    chunk = 1 << 22
+    needles = {}
+    for b in range(B):
+        for h in range(cfg.Hkv):
+            for dst in (K, V):
+                for t0 in range(0, T, chunk):
+                    t1 = min(T, t0 + chunk)
+                    dst[b, h, t0:t1] = torch.randn((t1 - t0, D), generator=gen, device=device,
+                                                   dtype=torch.float32).to(torch.bfloat16)
+            qbar = qf[b, 0, h * cfg.g:(h + 1) * cfg.g].astype(np.float64).mean(axis=0).astype(np.float32)
+            pos = _needle_positions(cfg, b, h, cfg.L - 1)
+            if pos.size:
+                gn = _rng(cfg.seed, _TAG_NOISE, b, h)
+                noise = gn.standard_normal((pos.size, D), dtype=np.float32) * np.float32(cfg.needle_noise)
+                rows = f32_to_bf16_bits(np.float32(cfg.needle_amp) * qbar[None, :] + noise)
+                K[b, h, torch.from_numpy(pos).to(device)] = \
+                    torch.from_numpy(rows.view(np.int16)).to(device).view(torch.bfloat16)
+            needles[(b, h)] = pos
+    seq_len = np.full((B,), cfg.L, dtype=np.int32)
+    return Case(cfg, tuple(range(B)), basis, key_scale, q, K, V, None, None, seq_len, needles)
+
+
 _TAG_REFIT = 100
 
 

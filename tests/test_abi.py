@@ -212,6 +212,28 @@ def test_attention_split_follows_the_shape(L, cfg, split):
     assert nsplit == -(-(cfg.topk + cfg.window + cfg.pool - 1) // split)
 
 
+MAX_ROWS = 8192 * 1024     # sketch rows (T_max / pool) the selection supports
+
+
+@pytest.mark.parametrize("pool", [1, 4])
+def test_cache_size_limit(L, pool):
+    """T_max / pool above 8,388,608 is refused before any launch; at the limit
+    the call gets as far as the workspace check."""
+    p = sks.params(4096, 2048, pool)
+    for T, code in ((MAX_ROWS * pool + pool, sks.SKS_ERR_UNSUPPORTED),
+                    (MAX_ROWS * pool, sks.SKS_ERR_WORKSPACE)):
+        k = kv(B=1, Hkv=1, T=T)
+        rc = L.sks_topk_select(FAKE, ctypes.byref(k), ctypes.byref(p), 0, FAKE, None, FAKE, 8,
+                               None)
+        assert rc == code, (T, sks.last_error())
+        if code == sks.SKS_ERR_UNSUPPORTED:
+            assert "8388608" in sks.last_error()
+        kw = dict(Kp=FAKE, Vp=FAKE) if pool > 1 else {}
+        rc = L.sks_decode_step(ctypes.byref(k), ctypes.byref(p), ctypes.byref(step_desc(**kw)), 1,
+                               FAKE, 8, None)
+        assert rc == code, (T, sks.last_error())
+
+
 def step_desc(**kw):
     d = dict(q=FAKE, Hq=8, basis=FAKE, basis_per_head=0, key_scale=FAKE, S=FAKE, Kp=None, Vp=None,
              sm_scale=0.088, qsk=FAKE, qscale=None, scores=FAKE, idx=FAKE, n_sel=None, out=FAKE,
