@@ -207,6 +207,34 @@ def make_case(cfg: Config, seqs=None, threads: int | None = None) -> Case:
     return Case(cfg, seqs, basis, key_scale, q, K, V, Ks, Vs, seq_len, needles)
 
 
+def random_arrays(B: int, R: int, Hq: int, Hkv: int, T: int, seed: int, i8: bool = False):
+    """Plain random inputs for edge-case tests, from one seeded stream:
+    q [B][R][Hq][128] bf16 bits, K, V [B][Hkv][T][128] (bf16 bits, or int8
+    codes with fp16 row scales Ks, Vs), a QR basis [64][128] and key scales
+    of 1/16.  Returns (q, K, V, Ks, Vs, basis, key_scale)."""
+    rng = np.random.default_rng(seed)
+    q = f32_to_bf16_bits(rng.standard_normal((B, R, Hq, 128)).astype(np.float32))
+    basis = np.linalg.qr(rng.standard_normal((128, 64)))[0].T.astype(np.float32)
+    ks = np.full(Hkv, 1 / 16, np.float32)
+    if not i8:
+        K = f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, 128)).astype(np.float32))
+        V = f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, 128)).astype(np.float32))
+        return q, K, V, None, None, basis, ks
+    K, Ks = quantize_rows_i8(rng.standard_normal((B, Hkv, T, 128)).astype(np.float32))
+    V, Vs = quantize_rows_i8(rng.standard_normal((B, Hkv, T, 128)).astype(np.float32))
+    return q, K, V, Ks, Vs, basis, ks
+
+
+def random_scores(shape, lo: int, hi: int, seed: int) -> np.ndarray:
+    """int32 scores drawn uniformly from [lo, hi] (narrow ranges: dense ties)."""
+    return np.random.default_rng(seed).integers(lo, hi + 1, shape).astype(np.int32)
+
+
+def distinct_diagonal(n: int, seed: int) -> np.ndarray:
+    """The values 1..n in a seeded random order (a diagonal with distinct entries)."""
+    return np.random.default_rng(seed).permutation(n).astype(np.float64) + 1.0
+
+
 _TAG_DEVICE = 101
 
 

@@ -8,7 +8,7 @@ import torch
 
 from long_context_sparse_sketch_amd import binding as sks
 from long_context_sparse_sketch_amd import configs as C
-from long_context_sparse_sketch_amd.synth import f32_to_bf16_bits, make_case
+from long_context_sparse_sketch_amd.synth import make_case, random_arrays, random_scores
 from oracle import sks_oracle as orc
 from tests.gpu_util import assert_attn_close, flush, lse_close, run_arrays
 from tests.golden_util import build_inputs, load_examples, parse_value
@@ -35,21 +35,6 @@ def test_golden_worked_examples_on_gpu(ex):
             assert r["lse"][0, i, 0] == pytest.approx(parse_value(case["lse"][i]), rel=1e-6)
 
 
-def rand_inputs(B, R, Hq, Hkv, T, seed, i8=False):
-    rng = np.random.default_rng(seed)
-    q = f32_to_bf16_bits(rng.standard_normal((B, R, Hq, 128)).astype(np.float32))
-    basis = np.linalg.qr(rng.standard_normal((128, 64)))[0].T.astype(np.float32)
-    ks = np.full(Hkv, 1 / 16, np.float32)
-    if not i8:
-        K = f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, 128)).astype(np.float32))
-        V = f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, 128)).astype(np.float32))
-        return q, K, V, None, None, basis, ks
-    from long_context_sparse_sketch_amd.synth import quantize_rows_i8
-    K, Ks = quantize_rows_i8(rng.standard_normal((B, Hkv, T, 128)).astype(np.float32))
-    V, Vs = quantize_rows_i8(rng.standard_normal((B, Hkv, T, 128)).astype(np.float32))
-    return q, K, V, Ks, Vs, basis, ks
-
-
 def oracle_of(q, K, V, Ks, Vs, seq_len, basis, ks, window, topk, pool):
     return orc.decode_step(q, K, V, Ks, Vs, np.asarray(seq_len), basis, ks, window, topk, pool,
                            K.dtype == np.int8)
@@ -70,10 +55,24 @@ def test_dense_and_extreme_selection(window, topk):
     """k >= n_far (dense), window covering all, no window, k = 1."""
     flush(f"[edge] dense/extreme window={window} topk={topk}")
     B, R, Hq, Hkv, T = 2, 1, 8, 2, 2100
-    q, K, V, Ks, Vs, basis, ks = rand_inputs(B, R, Hq, Hkv, T, seed=window + topk)
+    q, K, V, Ks, Vs, basis, ks = random_arrays(B, R, Hq, Hkv, T, seed=window + topk)
     sl = [2048, 1999]
     ref = oracle_of(q, K, V, Ks, Vs, sl, basis, ks, window, topk, 1)
     r = run_arrays(q, K, V, sl, basis, ks, window, topk, ref=ref)
+    compare_all(r, ref, Hq // Hkv, R)
+
+
+@pytest.mark.parametrize("topk", [8192, 8193, 20000])
+def test_large_k_beyond_register_cache(topk):
+    """k at and past the final pass's register cache of 8,192 candidates
+    (more candidates than it holds: the exact path over the candidate lists),
+    with far regions a few times k; two verify rows, ragged lengths."""
+    flush(f"[edge] large k={topk}")
+    B, R, Hq, Hkv, T = 2, 2, 8, 2, 45001
+    q, K, V, Ks, Vs, basis, ks = random_arrays(B, R, Hq, Hkv, T, seed=topk)
+    sl = [T - R + 1, 30123]
+    ref = oracle_of(q, K, V, Ks, Vs, sl, basis, ks, 1000, topk, 1)
+    r = run_arrays(q, K, V, sl, basis, ks, 1000, topk, ref=ref)
     compare_all(r, ref, Hq // Hkv, R)
 
 
@@ -81,7 +80,7 @@ def test_empty_and_short_rows():
     """seq_len 0 (nothing to attend), 1, and shorter than the window."""
     flush("[edge] empty and short rows")
     B, R, Hq, Hkv, T = 4, 1, 4, 1, 600
-    q, K, V, Ks, Vs, basis, ks = rand_inputs(B, R, Hq, Hkv, T, seed=3)
+    q, K, V, Ks, Vs, basis, ks = random_arrays(B, R, Hq, Hkv, T, seed=3)
     sl = [0, 1, 37, 600]
     ref = oracle_of(q, K, V, Ks, Vs, sl, basis, ks, 64, 16, 1)
     r = run_arrays(q, K, V, sl, basis, ks, 64, 16, ref=ref)
@@ -94,13 +93,12 @@ def test_topk_dense_ties_and_all_equal():
     """Scores from a narrow range (dense ties) and all-equal scores, fed directly."""
     flush("[edge] top-k ties")
     B, R, Hkv, T = 3, 1, 2, 70001
-    rng = np.random.default_rng(17)
     K = torch.zeros((B, Hkv, T, 128), dtype=torch.bfloat16, device="cuda")
     sl = torch.tensor([T, T, 50000], dtype=torch.int32, device="cuda")
     cache = sks.Cache(K, K, sl)
     W, k = 1000, 2048
     p = sks.params(W, k)
-    sc = rng.integers(-3, 4, (B, R, Hkv, T)).astype(np.int32)
+    sc = random_scores((B, R, Hkv, T), -3, 3, seed=17)
     sc[1, 0, 1] = 5                                   # all equal
     sc[2, 0, 0, :20000] = 1000000                     # many maxima
     scores = torch.from_numpy(sc).cuda()

@@ -21,7 +21,7 @@ import torch
 from long_context_sparse_sketch_amd import binding as sks
 from long_context_sparse_sketch_amd import configs as C
 from long_context_sparse_sketch_amd.runtime import to_device
-from long_context_sparse_sketch_amd.synth import make_case, make_refit_keys
+from long_context_sparse_sketch_amd.synth import distinct_diagonal, make_case, make_refit_keys
 from oracle import sks_oracle as orc
 from tests.gpu_util import flush
 
@@ -108,7 +108,7 @@ def test_refit_planted_keys(per_head):
 
 def test_refit_diagonal_gram_and_degenerate_ranges():
     # a diagonal Gram matrix: the basis is the coordinate axes of its 64 largest entries
-    d = np.random.default_rng(3).permutation(128).astype(np.float64) + 1.0
+    d = distinct_diagonal(128, seed=3)
     G_in = np.diag(d)[None]
     K = np.zeros((1, 1, 64, 128), np.uint16)
     _, basis, eig, _ = gpu_refit(K, [64], 0, 64, gram_in=G_in)
