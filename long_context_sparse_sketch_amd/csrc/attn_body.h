@@ -12,6 +12,8 @@ namespace sks {
 namespace {
 
 constexpr int AT_THREADS = 256;
+constexpr int ATTN_SPLIT = 384;          // attention entries per workgroup, at most
+constexpr long ATTN_SMALL_SET = 1536;    // smaller attention sets: 128-entry slots
 constexpr float NEG_INF = -__builtin_huge_valf();
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -641,17 +643,18 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
 
 }
 
-// Entries per attention slot for a shape: 128 (one tile per wave) when
-// 384-entry slots would give fewer than ATTN_SMALL_BELOW workgroups
-// (segments x slots); else 384 (three tiles) for bf16 rows, whose gathers
-// need the deeper pipeline, and 256 (two tiles) for int8 / int4 rows, whose
-// smaller gathers leave each wave's chain of dependent steps the longer part.
-// A function of the shape alone, so the split count, the workspace and the
-// merge order are fixed by the shape.
+// Entries per attention slot: 128 (one tile per wave) for attention sets of
+// fewer than ATTN_SMALL_SET entries, which would otherwise make too few
+// workgroups to fill the chip; else 384 (three tiles) for bf16 rows, whose
+// gathers need the deeper pipeline, and 256 (two tiles) for int8 / int4
+// rows, whose smaller gathers leave each wave's chain of dependent steps the
+// longer part.  The split fixes each row's order of operations, so it is a
+// function of the per-row parameters only (window, top-k, pooling, KV
+// storage): never of the batch size, the rows per sequence or the heads, so
+// that a row's results do not depend on what it is decoded with.
 inline int attn_split(const Shape &s) {
   const long set = (long)s.topk + s.window + s.pool - 1;   // the largest attention set
-  const long nseg = (long)s.B * s.R * s.Hkv;
-  if (nseg * ceil_div(set, ATTN_SPLIT) < ATTN_SMALL_BELOW) return attn_split_entries<1>();
+  if (set < ATTN_SMALL_SET) return attn_split_entries<1>();
   return s.dtype == SKS_KV_BF16 ? attn_split_entries<3>() : attn_split_entries<2>();
 }
 

@@ -7,9 +7,9 @@
 // Split-K flash decoding.  A workgroup takes ATTN_SPLIT (384) consecutive
 // entries of one (sequence, row, KV head) attention set and all G query heads
 // of that KV head; each of its 4 waves takes 96 of them as three tiles of 32
-// (see attn_body.h), gathering tile t + 1 while it computes tile t.  Shapes
-// whose 384-entry splits would not fill the chip take 128 entries per
-// workgroup (one tile per wave), and int8 / int4 caches 256 (two tiles).
+// (see attn_body.h), gathering tile t + 1 while it computes tile t.
+// Attention sets under 1,536 entries take 128 entries per workgroup (one
+// tile per wave), and int8 / int4 caches 256 (two tiles).
 // Online softmax in the log2 domain;
 // the waves' states are merged through LDS and the workgroup writes one
 // partial (m, l, acc[G][128]).  A second kernel merges the partials of every

@@ -24,8 +24,6 @@ constexpr int SCORE_CHUNK = 1024;        // tokens per score workgroup
 constexpr int TK_CHUNK = 4096;           // tokens per top-k filter workgroup
 constexpr int TK_SUB = 1024;             // tokens per filter wave (one candidate sub-list)
 constexpr int TK_MAX_SUBS = 8192;        // sub-lists per segment the final pass can index
-constexpr int ATTN_SPLIT = 384;          // attention entries per workgroup, at most
-constexpr long ATTN_SMALL_BELOW = 512;   // fewer 384-entry workgroups: 128-entry ones
 constexpr int ATTN_MAX_G = 8;            // query heads per KV head supported
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

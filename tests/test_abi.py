@@ -187,29 +187,38 @@ def test_workspace_sizes_cover_selection_and_attention(L, cfg):
     assert L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 9 * cfg.Hkv) == 0
 
 
-SPLIT_CASES = ([(C.small(c), 128) for c in C.ALL]
-               + [(C.full_set(c), 256 if c.kv_dtype else 384) for c in C.ALL[1:]]
-               + [(C.C1, 128), (C.C2, 128), (C.C3, 384), (C.C4, 384), (C.C5, 256),
-                  (C.with_kv(C.C3, C.KV_I4), 256), (C.with_kv(C.C3, C.KV_I8), 256),
-                  (C.with_kv(C.C2, C.KV_I4), 128)])
+def expected_split(cfg):
+    """128 entries for attention sets under 1,536, else 384 (bf16) or 256 (int8, int4)."""
+    if cfg.topk + cfg.window + cfg.pool - 1 < 1536:
+        return 128
+    return 384 if cfg.kv_dtype == C.KV_BF16 else 256
 
 
-@pytest.mark.parametrize("cfg,split", SPLIT_CASES, ids=[c.name for c, _ in SPLIT_CASES])
-def test_attention_split_follows_the_shape(L, cfg, split):
-    """The attention pass takes 128-entry splits when 384-entry ones would
-    give fewer than 512 workgroups (segments x splits); else 384-entry ones
-    for bf16 rows and 256-entry ones for int8 / int4 rows.  Read off the
-    workspace: only the partials, (m, l, acc[128]) fp32 per query head and
-    split, grow with the group size."""
+SPLIT_CFGS = ([C.small(c) for c in C.ALL] + [C.full_set(c) for c in C.ALL[1:]] + list(C.ALL)
+              + [C.with_kv(C.C3, C.KV_I4), C.with_kv(C.C3, C.KV_I8), C.with_kv(C.C1, C.KV_I4)])
+
+
+def partial_splits(L, cfg, B, R):
+    """Attention splits per segment, read off the workspace: only the partials,
+    (m, l, acc[128]) fp32 per query head and split, grow with the group size."""
     quant = cfg.kv_dtype != C.KV_BF16
-    k = kv(B=cfg.B, Hkv=cfg.Hkv, T=cfg.T_max, dtype=cfg.kv_dtype,
+    k = kv(B=B, Hkv=cfg.Hkv, T=cfg.T_max, dtype=cfg.kv_dtype,
            Ks=FAKE if quant else None, Vs=FAKE if quant else None)
-    p = sks.params(cfg.window, cfg.topk, cfg.pool, cfg.R)
+    p = sks.params(cfg.window, cfg.topk, cfg.pool, R)
     w1 = L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), cfg.Hkv)
     w2 = L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), 2 * cfg.Hkv)
-    nseg = cfg.B * cfg.R * cfg.Hkv
-    nsplit = round((w2 - w1) / (nseg * (8 + 128 * 4)))
-    assert nsplit == -(-(cfg.topk + cfg.window + cfg.pool - 1) // split)
+    return round((w2 - w1) / (B * R * cfg.Hkv * (8 + 128 * 4)))
+
+
+@pytest.mark.parametrize("cfg", SPLIT_CFGS, ids=lambda c: c.name)
+def test_attention_split_follows_the_row_parameters(L, cfg):
+    """The split is 128 entries for attention sets under 1,536, else 384 for
+    bf16 rows and 256 for int8 / int4 rows; the same for any batch size and
+    any number of verify rows (it fixes a row's order of operations)."""
+    want = -(-(cfg.topk + cfg.window + cfg.pool - 1) // expected_split(cfg))
+    assert partial_splits(L, cfg, cfg.B, cfg.R) == want
+    for B, R in ((1, 1), (1, 8), (64, 1), (64, 3)):
+        assert partial_splits(L, cfg, B, R) == want, (B, R)
 
 
 MAX_ROWS = 8192 * 1024     # sketch rows (T_max / pool) the selection supports

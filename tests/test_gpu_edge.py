@@ -135,6 +135,27 @@ def test_verify_rows_equal_sequential_on_gpu():
         assert np.array_equal(full["lse"][:, i], one["lse"][:, 0])
 
 
+@pytest.mark.parametrize("kv", [C.KV_I8, C.KV_BF16], ids=["int8", "bf16"])
+def test_verify_rows_in_a_batch_equal_lone_decodes(kv):
+    """The workload's own window and top-k, two sequences of three verify
+    rows: every row gives the bits of an R = 1 decode of its sequence alone
+    at that length, although the batched step has 6x the segments (its
+    order of operations may not depend on the batch or the rows)."""
+    cfg = C.with_kv(C.full_set(C.C5), kv)
+    flush(f"[edge] verify rows in a batch {cfg.name}")
+    case = make_case(cfg)
+    full = run_arrays(case.q, case.K, case.V, case.seq_len, case.basis, case.key_scale,
+                      cfg.window, cfg.topk, 1, case.K_scale, case.V_scale)
+    for b in range(cfg.B):
+        one = make_case(cfg, seqs=[b])
+        for i in range(cfg.R):
+            r = run_arrays(np.ascontiguousarray(one.q[:, i:i + 1]), one.K, one.V,
+                           one.seq_len + i, one.basis, one.key_scale, cfg.window, cfg.topk, 1,
+                           one.K_scale, one.V_scale)
+            for key in ("idx", "out", "lse"):
+                assert np.array_equal(full[key][b, i], r[key][0, 0]), (b, i, key)
+
+
 @pytest.mark.parametrize("cfg", [C.small(C.C3), C.small(C.C4)], ids=lambda c: c.name)
 def test_batch_invariance_bits(cfg):
     """A sequence gives the same bits alone and inside its batch."""
