@@ -130,10 +130,9 @@ def small(cfg: Config) -> Config:
 def full_set(cfg: Config) -> Config:
     """A reduced context with the workload's full attention set: the same
     window, top-k, pooling, rows, heads and dtype, a far region a little over
-    twice top-k, and enough sequences that the attention pass runs in its
-    deeper splits (384 entries for bf16, 256 for int8 / int4), which the
-    `small` shapes never reach: at least 512 workgroups of 384-entry splits
-    (segments x splits)."""
+    twice top-k, and enough sequences for at least 512 attention workgroups
+    of 384 entries (segments x splits): the workload's whole attention sets
+    at a size the oracle finishes in seconds."""
     set_max = cfg.topk + cfg.window + cfg.pool - 1
     per_seq = cfg.R * cfg.Hkv * -(-set_max // 384)
     B = max(1, -(-512 // per_seq))

@@ -1,8 +1,9 @@
 """GPU parity of every step of the HIP path against the CPU oracle, through
 the C ABI, on the five workload shapes reduced to sizes the oracle finishes in
-seconds (several tiles and a ragged tail each).  The reduced shapes run the
-attention pass in its small splits; the full-set shapes (a short context with
-the workloads' own window and top-k, and more sequences) in its large ones."""
+seconds (several tiles and a ragged tail each), and on the full-set shapes
+(a short context with the workloads' own window and top-k, and more
+sequences).  Between them the attention pass runs in all three of its split
+sizes (128, 256 and 384 entries)."""
 import numpy as np
 import pytest
 import torch
