@@ -33,8 +33,10 @@
  * - Device lengths are clamped to [0, T_max - rows + 1] inside the kernels,
  *   so a bad length gives unspecified but memory-safe results.
  * - Results are bit-deterministic for identical inputs, whatever the batch
- *   composition: no floating-point atomics, split counts fixed by the shape,
- *   fixed merge order.
+ *   composition and the number of verify rows: no floating-point atomics,
+ *   attention split counts fixed by the per-row parameters (window, topk,
+ *   pool, KV storage), fixed merge order.  A verify row gives the bits of a
+ *   one-row step at its length.
  *
  * Geometry of query row i (0 <= i < rows) of sequence b, with r = pool:
  *   L_i   = seq_len[b] + i        tokens visible to the row (its own included;
