@@ -4,6 +4,13 @@ Every function here forwards torch tensors' device pointers and the current
 HIP stream to the C ABI of the same name; all computation happens in the HIP
 kernels.  The library is loaded after torch so that both share one HIP
 runtime.  There is no fallback: a missing library raises.
+
+The C ABI checks what a pointer can tell (NULL, alignment) but not how much
+memory lies behind it, so every tensor is checked here first, before the
+call: contiguous, on the GPU (or pinned host memory where a host tier
+allows it) and exactly the byte size its layout in sks.h needs for this
+cache and these parameters.  A mismatch raises ValueError and launches
+nothing.
 """
 from __future__ import annotations
 
@@ -128,6 +135,54 @@ def ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+class _T:
+    """One tensor argument: its name, the bytes its layout needs, whether it
+    may be None and whether pinned host memory is allowed."""
+    __slots__ = ("t", "name", "nbytes", "optional", "host_ok")
+
+    def __init__(self, t, name: str, nbytes: int, optional: bool = False, host_ok: bool = False):
+        self.t, self.name, self.nbytes, self.optional, self.host_ok = t, name, nbytes, optional, host_ok
+
+
+def _ptrs(*args: _T):
+    """Device pointers of the arguments, after checking every one of them:
+    first that each is present (unless optional), contiguous and exactly
+    its layout's byte size, then that each is on the GPU (or pinned host
+    memory where allowed).  Raises ValueError naming the first argument that
+    fails; nothing is launched."""
+    for a in args:
+        t = a.t
+        if t is None:
+            if not a.optional:
+                raise ValueError(f"{a.name} is required")
+            continue
+        if not t.is_contiguous():
+            raise ValueError(f"{a.name} must be contiguous")
+        if _nbytes(t) != a.nbytes:
+            raise ValueError(f"{a.name}: {a.nbytes} bytes expected, got {_nbytes(t)} "
+                             f"(shape {tuple(t.shape)}, {t.dtype})")
+    out = []
+    for a in args:
+        t = a.t
+        if t is None:
+            out.append(None)
+        elif t.is_cuda:
+            out.append(t.data_ptr())
+        elif a.host_ok:
+            out.append(device_address(t))
+        else:
+            raise ValueError(f"{a.name} must be a GPU tensor")
+    return out
+
+
+def _row_bytes(dtype: int) -> int:
+    return {KV_BF16: 2 * HEAD_DIM, KV_I8: HEAD_DIM, KV_I4: HEAD_DIM // 2}[dtype]
+
+
 def device_address(t) -> int | None:
     """Address under which the GPU reaches tensor `t`: its data pointer for a
     device tensor; for a pinned host tensor the device address of its pinned
@@ -163,28 +218,89 @@ class Cache:
     def __init__(self, K, V, seq_len, K_scale=None, V_scale=None, hot=None):
         self.K, self.V, self.seq_len, self.K_scale, self.V_scale = K, V, seq_len, K_scale, V_scale
         self.hot = hot
+        if K.dim() != 4:
+            raise ValueError(f"K must be [B][Hkv][T][row], got shape {tuple(K.shape)}")
         B, Hkv, T, D = K.shape
-        # int8 codes as torch.int8; packed int4 rows (64 bytes) as torch.uint8
-        dtype = {torch.int8: KV_I8, torch.uint8: KV_I4}.get(K.dtype, KV_BF16)
+        # bf16 rows as torch.bfloat16; int8 codes as torch.int8; packed int4
+        # rows (64 bytes) as torch.uint8
+        dtype = {torch.bfloat16: KV_BF16, torch.int8: KV_I8, torch.uint8: KV_I4}.get(K.dtype)
+        if dtype is None:
+            raise ValueError(f"K must be bfloat16, int8 or uint8 (packed int4), got {K.dtype}")
         if dtype == KV_I4:
             D *= 2
-        if hot is None:
-            hk = hv = hks = hvs = None
-            W_hot = 0
-        else:
+        if V.dtype != K.dtype:
+            raise ValueError(f"V ({V.dtype}) must have K's dtype ({K.dtype})")
+        rb, quant = K.shape[3] * K.element_size(), dtype != KV_BF16
+        kv_b, sc_b = B * Hkv * T * rb, B * Hkv * T * 2
+        if quant == (K_scale is None) or quant == (V_scale is None):
+            raise ValueError("int8 / int4 caches need K_scale and V_scale, bf16 caches none")
+        # K, V and their scales may be pinned host memory (read through its
+        # device address: a host tier keeps the window in the device ring)
+        args = [_T(K, "K", kv_b, host_ok=True), _T(V, "V", kv_b, host_ok=True),
+                _T(K_scale, "K_scale", sc_b, optional=True, host_ok=True),
+                _T(V_scale, "V_scale", sc_b, optional=True, host_ok=True),
+                _T(seq_len, "seq_len", 4 * B)]
+        W_hot = 0
+        if hot is not None:
             hk, hv, hks, hvs = hot
+            if hk is None or hk.dim() != 4:
+                raise ValueError("K_hot must be [B][Hkv][W_hot][row]")
+            if quant == (hks is None) or quant == (hvs is None):
+                raise ValueError("a hot tier of an int8 / int4 cache needs its scales, bf16 none")
             W_hot = hk.shape[2]
-        da = device_address
-        self.desc = KVDesc(B, Hkv, D, T, dtype, da(K), da(V), da(K_scale), da(V_scale),
-                           ptr(seq_len), ptr(hk), ptr(hv), ptr(hks), ptr(hvs), W_hot)
+            args += [_T(hk, "K_hot", B * Hkv * W_hot * rb), _T(hv, "V_hot", B * Hkv * W_hot * rb),
+                     _T(hks, "K_hot_scale", B * Hkv * W_hot * 2, optional=True),
+                     _T(hvs, "V_hot_scale", B * Hkv * W_hot * 2, optional=True)]
+        ptrs = _ptrs(*args) + [None] * (4 if hot is None else 0)
+        self.desc = KVDesc(B, Hkv, D, T, dtype, *ptrs[:5], *ptrs[5:9], W_hot)
 
     @property
     def ref(self):
         return ctypes.byref(self.desc)
 
 
-def _nbytes(t) -> int:
-    return 0 if t is None else t.numel() * t.element_size()
+class _Dims:
+    """The byte sizes of a call's tensors, from the cache descriptor and parameters."""
+
+    def __init__(self, cache: Cache, p: Params | None = None):
+        d = cache.desc
+        self.B, self.Hkv, self.T = d.B, d.Hkv, d.T_max
+        self.rb = _row_bytes(d.dtype) if d.D == HEAD_DIM else 0
+        if p is not None:
+            self.R, self.k, self.pool = p.rows, p.topk, max(1, p.pool)
+            self.NB = self.T // self.pool
+            self.C = p.topk + p.window + self.pool - 1
+
+    def seg(self, per=1):            # [B][R][Hkv] x `per` bytes
+        return self.B * self.R * self.Hkv * per
+
+    def basis(self, basis, per_head):
+        return _T(basis, "basis", (self.Hkv if per_head else 1) * RANK * HEAD_DIM * 4)
+
+    def key_scale(self, ks):
+        return _T(ks, "key_scale", 4 * self.Hkv)
+
+    def S(self, S):                  # [B][Hkv][NB][64] int8
+        return _T(S, "S", self.B * self.Hkv * self.NB * RANK)
+
+    def pooled(self, t, name):       # Kp, Vp: [B][Hkv][NB][128] bf16, None when pool == 1
+        return _T(t, name, self.B * self.Hkv * self.NB * HEAD_DIM * 2, optional=True)
+
+    def scores(self, t):
+        return _T(t, "scores", self.seg(4 * self.NB))
+
+    def idx(self, t):
+        return _T(t, "idx", self.seg(4 * self.k))
+
+    def q(self, q):                  # [B][R][Hq][128] bf16; returns (arg, Hq)
+        if q is None or q.dim() != 4 or q.shape[3] != HEAD_DIM:
+            raise ValueError(f"q must be [B][R][Hq][{HEAD_DIM}] bf16")
+        return _T(q, "q", self.B * self.R * q.shape[2] * HEAD_DIM * 2), q.shape[2]
+
+
+def _ws(ws, optional=False):
+    """A workspace: any contiguous GPU byte buffer (the library checks its size)."""
+    return _T(ws, "ws", _nbytes(ws), optional=optional)
 
 
 def workspace_bytes(cache: Cache, p: Params, Hq: int) -> int:
@@ -192,49 +308,73 @@ def workspace_bytes(cache: Cache, p: Params, Hq: int) -> int:
 
 
 def workspace_init(ws, stream=None):
-    _check(lib().sks_workspace_init(ptr(ws), _nbytes(ws), _stream(stream)))
+    (wa,) = _ptrs(_ws(ws))
+    _check(lib().sks_workspace_init(wa, _nbytes(ws), _stream(stream)))
 
 
 def sketch_build(cache: Cache, p: Params, basis, key_scale, S, t_begin=0, t_end=None, Kp=None,
                  Vp=None, basis_per_head=False, stream=None):
     if t_end is None:
         t_end = cache.desc.T_max
-    _check(lib().sks_sketch_build(cache.ref, ctypes.byref(p), ptr(basis), int(basis_per_head),
-                                  ptr(key_scale), t_begin, t_end, ptr(S), ptr(Kp), ptr(Vp),
-                                  _stream(stream)))
+    d = _Dims(cache, p)
+    ba, ka, sa, kpa, vpa = _ptrs(d.basis(basis, basis_per_head), d.key_scale(key_scale), d.S(S),
+                                 d.pooled(Kp, "Kp"), d.pooled(Vp, "Vp"))
+    _check(lib().sks_sketch_build(cache.ref, ctypes.byref(p), ba, int(basis_per_head), ka,
+                                  t_begin, t_end, sa, kpa, vpa, _stream(stream)))
 
 
 def sketch_build_query(q, Hkv: int, basis, qsk, qscale=None, basis_per_head=False, stream=None):
+    if q is None or q.dim() != 4 or q.shape[3] != HEAD_DIM:
+        raise ValueError(f"q must be [B][R][Hq][{HEAD_DIM}] bf16")
     B, R, Hq, _ = q.shape
-    _check(lib().sks_sketch_build_query(ptr(q), B, R, Hq, Hkv, ptr(basis), int(basis_per_head),
-                                        ptr(qsk), ptr(qscale), _stream(stream)))
+    qa, ba, qsa, qca = _ptrs(_T(q, "q", B * R * Hq * HEAD_DIM * 2),
+                             _T(basis, "basis", (Hkv if basis_per_head else 1) * RANK * HEAD_DIM * 4),
+                             _T(qsk, "qsk", B * R * Hkv * RANK),
+                             _T(qscale, "qscale", 4 * B * R * Hkv, optional=True))
+    _check(lib().sks_sketch_build_query(qa, B, R, Hq, Hkv, ba, int(basis_per_head), qsa, qca,
+                                        _stream(stream)))
 
 
 def sketch_score(qsk, S, cache: Cache, p: Params, scores, ws=None, stream=None):
-    _check(lib().sks_sketch_score(ptr(qsk), ptr(S), cache.ref, ctypes.byref(p), ptr(scores),
-                                  ptr(ws), _nbytes(ws), _stream(stream)))
+    d = _Dims(cache, p)
+    qa, sa, ca, wa = _ptrs(_T(qsk, "qsk", d.seg(RANK)), d.S(S), d.scores(scores),
+                           _ws(ws, optional=True))
+    _check(lib().sks_sketch_score(qa, sa, cache.ref, ctypes.byref(p), ca, wa, _nbytes(ws),
+                                  _stream(stream)))
 
 
 def topk_select(scores, cache: Cache, p: Params, idx, n_sel, ws, hist_ready=False, stream=None):
-    _check(lib().sks_topk_select(ptr(scores), cache.ref, ctypes.byref(p),
-                                 TOPK_HIST_READY if hist_ready else 0, ptr(idx), ptr(n_sel),
-                                 ptr(ws), _nbytes(ws), _stream(stream)))
+    d = _Dims(cache, p)
+    ca, ia, na, wa = _ptrs(d.scores(scores), d.idx(idx),
+                           _T(n_sel, "n_sel", d.seg(4), optional=True), _ws(ws))
+    _check(lib().sks_topk_select(ca, cache.ref, ctypes.byref(p),
+                                 TOPK_HIST_READY if hist_ready else 0, ia, na, wa, _nbytes(ws),
+                                 _stream(stream)))
 
 
 def gather_pack(cache: Cache, p: Params, idx, K_out, V_out, n_out, Kp=None, Vp=None,
                 Ks_out=None, Vs_out=None, stream=None):
-    _check(lib().sks_gather_pack(cache.ref, ctypes.byref(p), ptr(idx), ptr(Kp), ptr(Vp),
-                                 ptr(K_out), ptr(V_out), ptr(Ks_out), ptr(Vs_out), ptr(n_out),
-                                 _stream(stream)))
+    d = _Dims(cache, p)
+    rows = d.seg(d.C * d.rb)
+    ptrs = _ptrs(d.idx(idx), d.pooled(Kp, "Kp"), d.pooled(Vp, "Vp"), _T(K_out, "K_out", rows),
+                 _T(V_out, "V_out", rows), _T(Ks_out, "Ks_out", d.seg(2 * d.C), optional=True),
+                 _T(Vs_out, "Vs_out", d.seg(2 * d.C), optional=True),
+                 _T(n_out, "n_out", d.seg(4)))
+    _check(lib().sks_gather_pack(cache.ref, ctypes.byref(p), *ptrs, _stream(stream)))
 
 
 def sparse_decode_attn(q, cache: Cache, p: Params, idx, out, ws, lse=None, Kp=None, Vp=None,
                        sm_scale=None, stream=None):
-    Hq = q.shape[2]
-    sm = 1.0 / math.sqrt(q.shape[3]) if sm_scale is None else sm_scale
-    _check(lib().sks_sparse_decode_attn(ptr(q), Hq, cache.ref, ctypes.byref(p), ptr(idx),
-                                        ptr(Kp), ptr(Vp), ctypes.c_float(sm), ptr(out), ptr(lse),
-                                        ptr(ws), _nbytes(ws), _stream(stream)))
+    d = _Dims(cache, p)
+    qt, Hq = d.q(q)
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else sm_scale
+    qa, ia, kpa, vpa, oa, la, wa = _ptrs(
+        qt, d.idx(idx), d.pooled(Kp, "Kp"), d.pooled(Vp, "Vp"),
+        _T(out, "out", d.B * d.R * Hq * HEAD_DIM * 4),
+        _T(lse, "lse", d.B * d.R * Hq * 4, optional=True), _ws(ws))
+    _check(lib().sks_sparse_decode_attn(qa, Hq, cache.ref, ctypes.byref(p), ia, kpa, vpa,
+                                        ctypes.c_float(sm), oa, la, wa, _nbytes(ws),
+                                        _stream(stream)))
 
 
 def decode_step(cache: Cache, p: Params, q, basis, key_scale, S, qsk, scores, idx, out, ws,
@@ -242,14 +382,21 @@ def decode_step(cache: Cache, p: Params, q, basis, key_scale, S, qsk, scores, id
                 basis_per_head=False, append=True, dense=False, stream=None):
     """The whole decode step (append, query sketch, score, select, attend) in one call;
     dense: no scoring or selection, attend the last window + topk tokens."""
-    sm = 1.0 / math.sqrt(q.shape[3]) if sm_scale is None else sm_scale
-    st = StepDesc(ptr(q), q.shape[2], ptr(basis), int(basis_per_head), ptr(key_scale), ptr(S),
-                  ptr(Kp), ptr(Vp), sm, ptr(qsk), ptr(qscale), ptr(scores), ptr(idx), ptr(n_sel),
-                  ptr(out), ptr(lse))
+    d = _Dims(cache, p)
+    qt, Hq = d.q(q)
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else sm_scale
+    (qa, ba, ka, sa, kpa, vpa, qsa, qca, ca, ia, na, oa, la, wa) = _ptrs(
+        qt, d.basis(basis, basis_per_head), d.key_scale(key_scale), d.S(S),
+        d.pooled(Kp, "Kp"), d.pooled(Vp, "Vp"), _T(qsk, "qsk", d.seg(RANK)),
+        _T(qscale, "qscale", d.seg(4), optional=True), d.scores(scores), d.idx(idx),
+        _T(n_sel, "n_sel", d.seg(4), optional=True),
+        _T(out, "out", d.B * d.R * Hq * HEAD_DIM * 4),
+        _T(lse, "lse", d.B * d.R * Hq * 4, optional=True), _ws(ws))
+    st = StepDesc(qa, Hq, ba, int(basis_per_head), ka, sa, kpa, vpa, sm, qsa, qca, ca, ia, na,
+                  oa, la)
     _check(lib().sks_decode_step(cache.ref, ctypes.byref(p), ctypes.byref(st),
                                  (STEP_APPEND if append else 0) | (STEP_DENSE if dense else 0),
-                                 ptr(ws), _nbytes(ws),
-                                 _stream(stream)))
+                                 wa, _nbytes(ws), _stream(stream)))
 
 
 def refit_workspace_bytes(cache: Cache, t_begin: int, t_end: int) -> int:
@@ -257,17 +404,25 @@ def refit_workspace_bytes(cache: Cache, t_begin: int, t_end: int) -> int:
 
 
 def refit_gram(cache: Cache, t_begin: int, t_end: int, gram, ws, per_head=True, stream=None):
-    _check(lib().sks_refit_gram(cache.ref, t_begin, t_end, int(per_head), ptr(gram), ptr(ws),
-                                _nbytes(ws), _stream(stream)))
+    n = cache.desc.Hkv if per_head else 1
+    ga, wa = _ptrs(_T(gram, "gram", n * HEAD_DIM * HEAD_DIM * 8), _ws(ws))
+    _check(lib().sks_refit_gram(cache.ref, t_begin, t_end, int(per_head), ga, wa, _nbytes(ws),
+                                _stream(stream)))
 
 
 def refit_basis(gram, basis, ws, eigval=None, stream=None):
-    _check(lib().sks_refit_basis(ptr(gram), gram.shape[0], ptr(basis), ptr(eigval), ptr(ws),
-                                 _nbytes(ws), _stream(stream)))
+    if gram is None or gram.dim() != 3:
+        raise ValueError(f"gram must be [n][{HEAD_DIM}][{HEAD_DIM}] float64")
+    n = gram.shape[0]
+    ga, ba, ea, wa = _ptrs(_T(gram, "gram", n * HEAD_DIM * HEAD_DIM * 8),
+                           _T(basis, "basis", n * RANK * HEAD_DIM * 4),
+                           _T(eigval, "eigval", n * HEAD_DIM * 8, optional=True), _ws(ws))
+    _check(lib().sks_refit_basis(ga, n, ba, ea, wa, _nbytes(ws), _stream(stream)))
 
 
 def refit_key_scale(cache: Cache, t_begin: int, t_end: int, basis, key_scale, ws,
                     basis_per_head=True, stream=None):
-    _check(lib().sks_refit_key_scale(cache.ref, t_begin, t_end, ptr(basis), int(basis_per_head),
-                                     ptr(key_scale), ptr(ws), _nbytes(ws), _stream(stream)))
-
+    d = _Dims(cache)
+    ba, ka, wa = _ptrs(d.basis(basis, basis_per_head), d.key_scale(key_scale), _ws(ws))
+    _check(lib().sks_refit_key_scale(cache.ref, t_begin, t_end, ba, int(basis_per_head), ka, wa,
+                                     _nbytes(ws), _stream(stream)))

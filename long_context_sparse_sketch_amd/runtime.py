@@ -16,11 +16,12 @@ or all of them as the one call sks_decode_step (the default of `step`).
 torch is used only to allocate device memory and streams; no step calls back
 into it.
 
-`StepRunner` schedules one step of a layer as several sub-batches (views of
-the same buffers) on a few streams, so that the latency-bound selection and
-attention of one part overlap the bandwidth-bound score pass of another
-(segments never interact), and can capture the whole step into a HIP graph:
-every call only enqueues kernels and reads lengths on the device.
+`StepRunner` captures whole steps into HIP graphs (every call only enqueues
+kernels and reads lengths on the device) and can schedule one step as
+several sub-batches (views of the same buffers; segments never interact) on
+a few streams, so that one part's latency-bound selection and attention
+overlap another's score pass.  On the workloads measured here one stream is
+the faster schedule: splitting pays every latency-bound kernel once per part.
 """
 from __future__ import annotations
 
