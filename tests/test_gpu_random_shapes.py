@@ -7,7 +7,9 @@ Per case, through the C ABI against the oracle:
 * the GPU's key and query sketches within the sketch bound;
 * scores bit-exact given the oracle's codes;
 * selection bit-exact given the oracle's scores (fused-histogram path too);
-* attention within the output bound given the oracle's indices.
+* attention within the output bound given the oracle's indices;
+and, on a subset, the dense step (no selection; each row attends its last
+window + topk tokens) against the oracle with that window.
 """
 import numpy as np
 import pytest
@@ -21,7 +23,7 @@ from tests.gpu_util import (GpuCase, assert_attn_close, flush, lse_close, oracle
 
 pytestmark = pytest.mark.gpu
 
-SEEDS = list(range(48))
+SEEDS = list(range(200))
 
 
 def draw(seed):
@@ -89,5 +91,23 @@ def test_random_shape(seed):
     # attention on the oracle's indices
     g.layer.attend(g.q, idx=torch.from_numpy(arr["idx"]).cuda())
     torch.cuda.synchronize()
+    assert_attn_close(g.layer.out.cpu().numpy(), arr["out"], cfg.name)
+    lse_close(g.layer.lse.cpu().numpy(), arr["lse"], cfg.name)
+
+
+@pytest.mark.parametrize("seed", SEEDS[:40])
+def test_random_shape_dense_step(seed):
+    cfg, sl = draw(seed)
+    flush(f"[random dense] seed {seed}: B={cfg.B} R={cfg.R} Hq/Hkv={cfg.Hq}/{cfg.Hkv} "
+          f"L={sl.tolist()} W={cfg.window} k={cfg.topk} r={cfg.pool} kv={C.KV_NAMES[cfg.kv_dtype]}")
+    case = make_case(cfg)
+    g = GpuCase(case, seq_len=sl)
+    g.layer.build_sketch(0, g.T)
+    g.layer.step(g.q, dense=True)
+    torch.cuda.synchronize()
+    c = case
+    ref = orc.decode_step(c.q, c.K, c.V, c.K_scale, c.V_scale, sl, c.basis, c.key_scale,
+                          g.window + g.topk, 0, g.pool, cfg.kv_dtype)
+    arr = ref_arrays(ref, cfg, case.B, 0, g.layer.NB)
     assert_attn_close(g.layer.out.cpu().numpy(), arr["out"], cfg.name)
     lse_close(g.layer.lse.cpu().numpy(), arr["lse"], cfg.name)
