@@ -224,3 +224,35 @@ def test_host_tier_dense_step(short):
     torch.cuda.synchronize()
     for n in OUTS:
         assert torch.equal(want[n].view(torch.uint8), getattr(lay, n).view(torch.uint8)), n
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_shape_host_tier(seed):
+    """Seeded random shapes (unpooled: a hot tier needs pool == 1) with a ring
+    of window + rows + 0..63 slots: every output bit-equal to the all-device
+    run, the host copy of every position the rows may not read from host
+    poisoned."""
+    from tests.test_gpu_random_shapes import draw
+    cfg, sl = draw(seed)
+    if cfg.pool > 1:
+        cfg = cfg.scaled(pool=1)
+    if cfg.window + cfg.R > cfg.T_max:        # the ring may not exceed the cache
+        cfg = cfg.scaled(window=cfg.T_max - cfg.R)
+    extra = int(np.random.default_rng(900 + seed).integers(0, 64))
+    flush(f"[tier random] seed {seed}: B={cfg.B} R={cfg.R} Hq/Hkv={cfg.Hq}/{cfg.Hkv} "
+          f"L={sl.tolist()} W={cfg.window} k={cfg.topk} kv={C.KV_NAMES[cfg.kv_dtype]} "
+          f"ring +{extra}")
+    case = make_case(cfg)
+    g = GpuCase(case, seq_len=sl)
+    g.layer.build_sketch(0, g.T)
+    S0 = g.layer.S.clone()
+    want = run(g.layer, g.q)
+    W_hot = min(g.window + cfg.R + extra, g.T)
+    cache, host, ring = build_tier(g, W_hot)
+    lay = SparseDecodeLayer(case.B, cfg.R, cfg.Hq, cfg.Hkv, g.T, g.window, g.topk, 1,
+                            cfg.kv_dtype).bind(cache, g.basis, g.key_scale)
+    lay.S.copy_(S0)
+    poison_host(g, host)
+    got = run(lay, g.q)
+    for n in OUTS:
+        assert torch.equal(want[n].view(torch.uint8), got[n].view(torch.uint8)), n
