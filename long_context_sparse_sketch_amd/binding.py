@@ -145,15 +145,17 @@ class _T:
     __slots__ = ("t", "name", "nbytes", "optional", "host_ok")
 
     def __init__(self, t, name: str, nbytes: int, optional: bool = False, host_ok: bool = False):
-        self.t, self.name, self.nbytes, self.optional, self.host_ok = t, name, nbytes, optional, host_ok
+        self.t, self.name, self.nbytes = t, name, nbytes
+        self.optional, self.host_ok = optional, host_ok
 
 
-def _ptrs(*args: _T):
+def _ptrs(*args: _T, stream=None, launch: bool = True, cache=None):
     """Device pointers of the arguments, after checking every one of them:
     first that each is present (unless optional), contiguous and exactly
     its layout's byte size, then that each is on the GPU (or pinned host
-    memory where allowed).  Raises ValueError naming the first argument that
-    fails; nothing is launched."""
+    memory where allowed), all on one device with `cache`'s lengths -- for
+    a launch, the device of `stream` (the current device when it is None).  Raises ValueError naming
+    the first argument that fails; nothing is launched."""
     for a in args:
         t = a.t
         if t is None:
@@ -176,6 +178,21 @@ def _ptrs(*args: _T):
             out.append(device_address(t))
         else:
             raise ValueError(f"{a.name} must be a GPU tensor")
+    devs = {(a.name, a.t.device.index) for a in args if a.t is not None and a.t.is_cuda}
+    sl = getattr(cache, "seq_len", None)
+    if sl is not None and sl.is_cuda:
+        devs.add(("the cache", sl.device.index))
+    idxs = {i for _, i in devs}
+    if len(idxs) > 1:
+        raise ValueError("tensors on several devices: "
+                         + ", ".join(f"{n} on cuda:{i}" for n, i in sorted(devs)))
+    if launch and idxs:
+        dev = next(iter(idxs))
+        want = getattr(stream, "device", None)
+        want = torch.cuda.current_device() if stream is None else getattr(want, "index", dev)
+        if want != dev:
+            raise ValueError(f"tensors are on cuda:{dev} but the launch goes to cuda:{want} "
+                             f"(use torch.cuda.device({dev}) or a stream of that device)")
     return out
 
 
@@ -251,7 +268,7 @@ class Cache:
             args += [_T(hk, "K_hot", B * Hkv * W_hot * rb), _T(hv, "V_hot", B * Hkv * W_hot * rb),
                      _T(hks, "K_hot_scale", B * Hkv * W_hot * 2, optional=True),
                      _T(hvs, "V_hot_scale", B * Hkv * W_hot * 2, optional=True)]
-        ptrs = _ptrs(*args) + [None] * (4 if hot is None else 0)
+        ptrs = _ptrs(*args, launch=False) + [None] * (4 if hot is None else 0)
         self.desc = KVDesc(B, Hkv, D, T, dtype, *ptrs[:5], *ptrs[5:9], W_hot)
 
     @property
@@ -308,7 +325,7 @@ def workspace_bytes(cache: Cache, p: Params, Hq: int) -> int:
 
 
 def workspace_init(ws, stream=None):
-    (wa,) = _ptrs(_ws(ws))
+    (wa,) = _ptrs(_ws(ws), stream=stream)
     _check(lib().sks_workspace_init(wa, _nbytes(ws), _stream(stream)))
 
 
@@ -318,7 +335,7 @@ def sketch_build(cache: Cache, p: Params, basis, key_scale, S, t_begin=0, t_end=
         t_end = cache.desc.T_max
     d = _Dims(cache, p)
     ba, ka, sa, kpa, vpa = _ptrs(d.basis(basis, basis_per_head), d.key_scale(key_scale), d.S(S),
-                                 d.pooled(Kp, "Kp"), d.pooled(Vp, "Vp"))
+                                 d.pooled(Kp, "Kp"), d.pooled(Vp, "Vp"), stream=stream, cache=cache)
     _check(lib().sks_sketch_build(cache.ref, ctypes.byref(p), ba, int(basis_per_head), ka,
                                   t_begin, t_end, sa, kpa, vpa, _stream(stream)))
 
@@ -328,9 +345,10 @@ def sketch_build_query(q, Hkv: int, basis, qsk, qscale=None, basis_per_head=Fals
         raise ValueError(f"q must be [B][R][Hq][{HEAD_DIM}] bf16")
     B, R, Hq, _ = q.shape
     qa, ba, qsa, qca = _ptrs(_T(q, "q", B * R * Hq * HEAD_DIM * 2),
-                             _T(basis, "basis", (Hkv if basis_per_head else 1) * RANK * HEAD_DIM * 4),
+                             _T(basis, "basis",
+                                (Hkv if basis_per_head else 1) * RANK * HEAD_DIM * 4),
                              _T(qsk, "qsk", B * R * Hkv * RANK),
-                             _T(qscale, "qscale", 4 * B * R * Hkv, optional=True))
+                             _T(qscale, "qscale", 4 * B * R * Hkv, optional=True), stream=stream)
     _check(lib().sks_sketch_build_query(qa, B, R, Hq, Hkv, ba, int(basis_per_head), qsa, qca,
                                         _stream(stream)))
 
@@ -338,7 +356,7 @@ def sketch_build_query(q, Hkv: int, basis, qsk, qscale=None, basis_per_head=Fals
 def sketch_score(qsk, S, cache: Cache, p: Params, scores, ws=None, stream=None):
     d = _Dims(cache, p)
     qa, sa, ca, wa = _ptrs(_T(qsk, "qsk", d.seg(RANK)), d.S(S), d.scores(scores),
-                           _ws(ws, optional=True))
+                           _ws(ws, optional=True), stream=stream, cache=cache)
     _check(lib().sks_sketch_score(qa, sa, cache.ref, ctypes.byref(p), ca, wa, _nbytes(ws),
                                   _stream(stream)))
 
@@ -346,7 +364,8 @@ def sketch_score(qsk, S, cache: Cache, p: Params, scores, ws=None, stream=None):
 def topk_select(scores, cache: Cache, p: Params, idx, n_sel, ws, hist_ready=False, stream=None):
     d = _Dims(cache, p)
     ca, ia, na, wa = _ptrs(d.scores(scores), d.idx(idx),
-                           _T(n_sel, "n_sel", d.seg(4), optional=True), _ws(ws))
+                           _T(n_sel, "n_sel", d.seg(4), optional=True), _ws(ws), stream=stream,
+                           cache=cache)
     _check(lib().sks_topk_select(ca, cache.ref, ctypes.byref(p),
                                  TOPK_HIST_READY if hist_ready else 0, ia, na, wa, _nbytes(ws),
                                  _stream(stream)))
@@ -359,7 +378,7 @@ def gather_pack(cache: Cache, p: Params, idx, K_out, V_out, n_out, Kp=None, Vp=N
     ptrs = _ptrs(d.idx(idx), d.pooled(Kp, "Kp"), d.pooled(Vp, "Vp"), _T(K_out, "K_out", rows),
                  _T(V_out, "V_out", rows), _T(Ks_out, "Ks_out", d.seg(2 * d.C), optional=True),
                  _T(Vs_out, "Vs_out", d.seg(2 * d.C), optional=True),
-                 _T(n_out, "n_out", d.seg(4)))
+                 _T(n_out, "n_out", d.seg(4)), stream=stream, cache=cache)
     _check(lib().sks_gather_pack(cache.ref, ctypes.byref(p), *ptrs, _stream(stream)))
 
 
@@ -371,7 +390,7 @@ def sparse_decode_attn(q, cache: Cache, p: Params, idx, out, ws, lse=None, Kp=No
     qa, ia, kpa, vpa, oa, la, wa = _ptrs(
         qt, d.idx(idx), d.pooled(Kp, "Kp"), d.pooled(Vp, "Vp"),
         _T(out, "out", d.B * d.R * Hq * HEAD_DIM * 4),
-        _T(lse, "lse", d.B * d.R * Hq * 4, optional=True), _ws(ws))
+        _T(lse, "lse", d.B * d.R * Hq * 4, optional=True), _ws(ws), stream=stream, cache=cache)
     _check(lib().sks_sparse_decode_attn(qa, Hq, cache.ref, ctypes.byref(p), ia, kpa, vpa,
                                         ctypes.c_float(sm), oa, la, wa, _nbytes(ws),
                                         _stream(stream)))
@@ -391,7 +410,7 @@ def decode_step(cache: Cache, p: Params, q, basis, key_scale, S, qsk, scores, id
         _T(qscale, "qscale", d.seg(4), optional=True), d.scores(scores), d.idx(idx),
         _T(n_sel, "n_sel", d.seg(4), optional=True),
         _T(out, "out", d.B * d.R * Hq * HEAD_DIM * 4),
-        _T(lse, "lse", d.B * d.R * Hq * 4, optional=True), _ws(ws))
+        _T(lse, "lse", d.B * d.R * Hq * 4, optional=True), _ws(ws), stream=stream, cache=cache)
     st = StepDesc(qa, Hq, ba, int(basis_per_head), ka, sa, kpa, vpa, sm, qsa, qca, ca, ia, na,
                   oa, la)
     _check(lib().sks_decode_step(cache.ref, ctypes.byref(p), ctypes.byref(st),
@@ -405,7 +424,8 @@ def refit_workspace_bytes(cache: Cache, t_begin: int, t_end: int) -> int:
 
 def refit_gram(cache: Cache, t_begin: int, t_end: int, gram, ws, per_head=True, stream=None):
     n = cache.desc.Hkv if per_head else 1
-    ga, wa = _ptrs(_T(gram, "gram", n * HEAD_DIM * HEAD_DIM * 8), _ws(ws))
+    ga, wa = _ptrs(_T(gram, "gram", n * HEAD_DIM * HEAD_DIM * 8), _ws(ws), stream=stream,
+                   cache=cache)
     _check(lib().sks_refit_gram(cache.ref, t_begin, t_end, int(per_head), ga, wa, _nbytes(ws),
                                 _stream(stream)))
 
@@ -416,13 +436,15 @@ def refit_basis(gram, basis, ws, eigval=None, stream=None):
     n = gram.shape[0]
     ga, ba, ea, wa = _ptrs(_T(gram, "gram", n * HEAD_DIM * HEAD_DIM * 8),
                            _T(basis, "basis", n * RANK * HEAD_DIM * 4),
-                           _T(eigval, "eigval", n * HEAD_DIM * 8, optional=True), _ws(ws))
+                           _T(eigval, "eigval", n * HEAD_DIM * 8, optional=True), _ws(ws),
+                           stream=stream)
     _check(lib().sks_refit_basis(ga, n, ba, ea, wa, _nbytes(ws), _stream(stream)))
 
 
 def refit_key_scale(cache: Cache, t_begin: int, t_end: int, basis, key_scale, ws,
                     basis_per_head=True, stream=None):
     d = _Dims(cache)
-    ba, ka, wa = _ptrs(d.basis(basis, basis_per_head), d.key_scale(key_scale), _ws(ws))
+    ba, ka, wa = _ptrs(d.basis(basis, basis_per_head), d.key_scale(key_scale), _ws(ws),
+                       stream=stream, cache=cache)
     _check(lib().sks_refit_key_scale(cache.ref, t_begin, t_end, ba, int(basis_per_head), ka, wa,
                                      _nbytes(ws), _stream(stream)))
