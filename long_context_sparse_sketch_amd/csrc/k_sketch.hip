@@ -404,27 +404,38 @@ __device__ void sketch_row_wave(const void *__restrict__ K, const void *__restri
     x[2 * lane] = x0;
     x[2 * lane + 1] = x1;
   } else {
-    // pooled block: fp64 mean of `pool` rows (exact for bf16), rounded once to bf16
+    // pooled block: fp64 mean of `pool` rows (exact for bf16), rounded once to
+    // bf16.  The K and V rows are loaded 8 at a time, all in flight together,
+    // and summed in row order.
     const size_t tok0 = (size_t)bh * T_max + (size_t)j * pool;
     const size_t out_row = (size_t)bh * NB + j;
     const double dpool = (double)pool;
+    const uint32_t *Kw = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(K) + tok0 * D) + lane;
+    const uint32_t *Vw = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(V) + tok0 * D) + lane;
+    double k0s = 0.0, k1s = 0.0, v0s = 0.0, v1s = 0.0;
+    for (int k0 = 0; k0 < pool; k0 += 8) {
+      uint32_t wk[8], wv[8];
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      const uint16_t *src = static_cast<const uint16_t *>(which == 0 ? K : V);
-      double s0 = 0.0, s1 = 0.0;
-      for (int k = 0; k < pool; ++k) {
-        const uint32_t w = reinterpret_cast<const uint32_t *>(src + (tok0 + k) * D)[lane];
-        s0 += bf16_lo(w);
-        s1 += bf16_hi(w);
+      for (int u = 0; u < 8; ++u) {
+        const bool in = k0 + u < pool;
+        wk[u] = in ? Kw[(size_t)(k0 + u) * (D / 2)] : 0u;
+        wv[u] = in ? Vw[(size_t)(k0 + u) * (D / 2)] : 0u;
       }
-      const uint16_t o0 = f64_to_bf16_rne(s0 / dpool), o1 = f64_to_bf16_rne(s1 / dpool);
-      reinterpret_cast<uint32_t *>((which == 0 ? Kp : Vp) + out_row * D)[lane] =
-          (uint32_t)o0 | ((uint32_t)o1 << 16);
-      if (which == 0) {
-        x[2 * lane] = __uint_as_float((uint32_t)o0 << 16);
-        x[2 * lane + 1] = __uint_as_float((uint32_t)o1 << 16);
-      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < pool) {
+          k0s += bf16_lo(wk[u]);
+          k1s += bf16_hi(wk[u]);
+          v0s += bf16_lo(wv[u]);
+          v1s += bf16_hi(wv[u]);
+        }
     }
+    const uint16_t o0 = f64_to_bf16_rne(k0s / dpool), o1 = f64_to_bf16_rne(k1s / dpool);
+    const uint16_t p0 = f64_to_bf16_rne(v0s / dpool), p1 = f64_to_bf16_rne(v1s / dpool);
+    reinterpret_cast<uint32_t *>(Kp + out_row * D)[lane] = (uint32_t)o0 | ((uint32_t)o1 << 16);
+    reinterpret_cast<uint32_t *>(Vp + out_row * D)[lane] = (uint32_t)p0 | ((uint32_t)p1 << 16);
+    x[2 * lane] = __uint_as_float((uint32_t)o0 << 16);
+    x[2 * lane + 1] = __uint_as_float((uint32_t)o1 << 16);
   }
   __syncthreads();
   const float y = dot_basis_row(pr, x);
