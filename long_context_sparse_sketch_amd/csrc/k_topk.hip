@@ -22,9 +22,10 @@
 //     and counts, from the data, the candidates above T and equal to T.  When
 //     those counts show that T is the k-th largest key, it emits every
 //     candidate above T and the lowest-index ties at T, ascending, without a
-//     sort.  Otherwise (a workspace that was not zero at rest) it derives T
-//     from the candidates themselves with an exact two-level radix select in
-//     LDS -- or from the raw scores, if fewer than k candidates came through.
+//     sort.  Otherwise (a workspace that was not zero at rest, or more
+//     candidates than the 8,192 its registers hold) it derives T from the
+//     candidates themselves with an exact two-level radix select in LDS --
+//     or from the raw scores, if fewer than k candidates came through.
 //     The histograms are never trusted beyond what the data confirms.  It
 //     returns the segment's histograms to zero.
 #include "topk_body.h"
