@@ -63,6 +63,7 @@ def call_attn(L, k, p, Hq=8, ws_bytes=1 << 30, q=FAKE, out=FAKE, idx=FAKE, ws=FA
     (dict(dtype=sks.KV_I8), sks.SKS_ERR_ARG, "K_scale"),
     (dict(dtype=sks.KV_I4), sks.SKS_ERR_ARG, "K_scale"),
     (dict(dtype=sks.KV_I4, Ks=FAKE), sks.SKS_ERR_ARG, "V_scale"),
+    (dict(B=8192, Hkv=8), sks.SKS_ERR_ARG, "65535"),     # segments: a grid dimension
 ])
 def test_cache_description_errors(L, mut, code, word):
     k = kv(**mut)
