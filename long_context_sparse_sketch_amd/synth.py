@@ -259,24 +259,29 @@ def make_case_on_device(cfg: Config, device) -> Case:
     gen.manual_seed(seed)
     K = torch.empty((B, cfg.Hkv, T, D), dtype=torch.bfloat16, device=device)
     V = torch.empty_like(K)
+    # K, then V, over the flattened cache in chunks of 4M rows
     chunk = 1 << 22
-    needles = {}
+    n = B * cfg.Hkv * T
+    for dst in (K.view(n, D), V.view(n, D)):
+        for r0 in range(0, n, chunk):
+            r1 = min(n, r0 + chunk)
+            dst[r0:r1] = torch.randn((r1 - r0, D), generator=gen, device=device,
+                                     dtype=torch.float32).to(torch.bfloat16)
+    # needles: every (sequence, KV head)'s rows planted with one indexed write
+    needles, at, rows = {}, [], []
     for b in range(B):
         for h in range(cfg.Hkv):
-            for dst in (K, V):
-                for t0 in range(0, T, chunk):
-                    t1 = min(T, t0 + chunk)
-                    dst[b, h, t0:t1] = torch.randn((t1 - t0, D), generator=gen, device=device,
-                                                   dtype=torch.float32).to(torch.bfloat16)
-            qbar = qf[b, 0, h * cfg.g:(h + 1) * cfg.g].astype(np.float64).mean(axis=0).astype(np.float32)
             pos = _needle_positions(cfg, b, h, cfg.L - 1)
+            needles[(b, h)] = pos
             if pos.size:
+                qbar = qf[b, 0, h * cfg.g:(h + 1) * cfg.g].astype(np.float64).mean(axis=0).astype(np.float32)
                 gn = _rng(cfg.seed, _TAG_NOISE, b, h)
                 noise = gn.standard_normal((pos.size, D), dtype=np.float32) * np.float32(cfg.needle_noise)
-                rows = f32_to_bf16_bits(np.float32(cfg.needle_amp) * qbar[None, :] + noise)
-                K[b, h, torch.from_numpy(pos).to(device)] = \
-                    torch.from_numpy(rows.view(np.int16)).to(device).view(torch.bfloat16)
-            needles[(b, h)] = pos
+                rows.append(f32_to_bf16_bits(np.float32(cfg.needle_amp) * qbar[None, :] + noise))
+                at.append(pos + (b * cfg.Hkv + h) * T)
+    if at:
+        K.view(n, D)[torch.from_numpy(np.concatenate(at)).to(device)] = \
+            torch.from_numpy(np.concatenate(rows).view(np.int16)).to(device).view(torch.bfloat16)
     seq_len = np.full((B,), cfg.L, dtype=np.int32)
     return Case(cfg, tuple(range(B)), basis, key_scale, q, K, V, None, None, seq_len, needles)
 

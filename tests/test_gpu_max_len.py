@@ -1,4 +1,6 @@
-"""The largest cache the selection supports: one sequence of 8,388,608
+"""The largest sizes the library supports.
+
+test_largest_cache -- the largest cache the selection supports: one sequence of 8,388,608
 tokens per KV head (T_max / pool at the limit: 8,192 sub-lists of 1,024
 sketch rows in the final pass), two KV heads, through the whole step (bulk
 key sketch, then sks_decode_step), against the oracle, for each head:
@@ -94,3 +96,47 @@ def test_largest_cache():
         hs = slice(h * G, (h + 1) * G)
         assert_attn_close(layer.out[0, 0, hs].cpu().numpy(), out, f"{cfg.name} head {h}")
         lse_close(layer.lse[0, 0, hs].cpu().numpy(), lse, f"{cfg.name} head {h}")
+
+
+def test_most_segments():
+    """8,191 sequences x 8 KV heads = 65,528 (sequence, KV head) segments, the
+    most a grid dimension holds (65,535), on short rows: sampled segments
+    (the first, the last and some between) against the oracle: sketches within
+    the bound, scores and indices bit-exact given the GPU's codes, outputs
+    within the output bound."""
+    B, HKV_, G_ = 8191, 8, 1
+    cfg = C.Config("max_segments", 92, B=B, R=1, Hq=HKV_ * G_, Hkv=HKV_, L=64, window=16,
+                   topk=8, pool=1, kv_dtype=C.KV_BF16, needle_kind="random", needle_count=2,
+                   needle_amp=3.0, needle_noise=0.5)
+    flush(f"[max] {B} x {HKV_} segments")
+    case = make_case_on_device(cfg, "cuda")
+    K, V = case.K, case.V
+    sl = torch.from_numpy(case.seq_len.copy()).cuda()
+    layer = SparseDecodeLayer(B, 1, HKV_ * G_, HKV_, cfg.T_max, 16, 8, 1, sks.KV_BF16)
+    layer.bind(sks.Cache(K, V, sl), torch.from_numpy(case.basis).cuda(),
+               torch.from_numpy(case.key_scale).cuda())
+    q = torch.from_numpy(case.q.view(np.int16)).cuda().view(torch.bfloat16)
+    layer.build_sketch(0, cfg.T_max)
+    layer.step(q)
+    torch.cuda.synchronize()
+    n_far = cfg.L - 16
+    qf = orc.bf16_to_f64(case.q)
+    for b, h in [(0, 0), (B - 1, HKV_ - 1), (B // 2, 3), (1234, 5), (B - 2, 0)]:
+        Kf = rows_f64(K[b, h], np.arange(cfg.L))
+        Vf = rows_f64(V[b, h], np.arange(cfg.L))
+        y = orc.project(Kf, case.basis)
+        codes = layer.S[b, h].cpu().numpy()
+        assert sketch_ok(codes[:cfg.L], y, float(case.key_scale[h])).all(), (b, h)
+        qg = qf[b, 0, h * G_:(h + 1) * G_]
+        _, qs, yq = orc.query_sketch(qg, case.basis)
+        qc = layer.qsk[b, 0, h].cpu().numpy()
+        assert sketch_ok(qc, yq, qs).all(), (b, h)
+        sc = orc.scores(qc, codes[:n_far])
+        assert np.array_equal(layer.scores[b, 0, h, :n_far].cpu().numpy().astype(np.int64), sc)
+        sel = orc.select_topk(sc, 8)
+        assert np.array_equal(layer.idx[b, 0, h].cpu().numpy(), sel.astype(np.int32)), (b, h)
+        rows = np.concatenate([sel, np.arange(n_far, cfg.L)])
+        out, lse = orc.attend(qg, Kf[rows], Vf[rows], 1.0 / math.sqrt(128.0))
+        hs = slice(h * G_, (h + 1) * G_)
+        assert_attn_close(layer.out[b, 0, hs].cpu().numpy(), out, f"{(b, h)}")
+        lse_close(layer.lse[b, 0, hs].cpu().numpy(), lse, f"{(b, h)}")
