@@ -50,9 +50,12 @@ def compare_all(r, ref, g, R):
             lse_close(r["lse"][b, i, sl], o["lse"][i], f"{(b, i, h)}")
 
 
-@pytest.mark.parametrize("window,topk", [(100, 3000), (3000, 5), (0, 2500), (2047, 1)])
+@pytest.mark.parametrize("window,topk", [(100, 3000), (3000, 5), (0, 2500), (2047, 1),
+                                         (100, 1 << 24)])
 def test_dense_and_extreme_selection(window, topk):
-    """k >= n_far (dense), window covering all, no window, k = 1."""
+    """k >= n_far (dense), window covering all, no window, k = 1, and k at its
+    largest (2^24: tens of thousands of attention slots per segment, all but
+    the first masked; idx rows padded to 2^24)."""
     flush(f"[edge] dense/extreme window={window} topk={topk}")
     B, R, Hq, Hkv, T = 2, 1, 8, 2, 2100
     q, K, V, Ks, Vs, basis, ks = random_arrays(B, R, Hq, Hkv, T, seed=window + topk)
