@@ -51,11 +51,11 @@ def compare_all(r, ref, g, R):
 
 
 @pytest.mark.parametrize("window,topk", [(100, 3000), (3000, 5), (0, 2500), (2047, 1),
-                                         (100, 1 << 24)])
+                                         (100, 1 << 24), (1 << 24, 5)])
 def test_dense_and_extreme_selection(window, topk):
     """k >= n_far (dense), window covering all, no window, k = 1, and k at its
     largest (2^24: tens of thousands of attention slots per segment, all but
-    the first masked; idx rows padded to 2^24)."""
+    the first masked; idx rows padded to 2^24) and the window at its largest."""
     flush(f"[edge] dense/extreme window={window} topk={topk}")
     B, R, Hq, Hkv, T = 2, 1, 8, 2, 2100
     q, K, V, Ks, Vs, basis, ks = random_arrays(B, R, Hq, Hkv, T, seed=window + topk)
