@@ -274,9 +274,18 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
                        bool hist_ready, int32_t *idx, int32_t *n_sel, const TopkWs &w,
                        hipStream_t st) {
   const int nseg = s.B * s.R * s.Hkv;
-  hipError_t e = launch_topk_filter(scores, seq_len, s, hist_ready, w, st);
-  if (e != hipSuccess) return e;
-  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(final_args(scores, seq_len, s, idx, n_sel, w));
+  // Far regions that fit the final pass's registers need no filter: every
+  // far entry is a candidate there, and the exact select runs in LDS.
+  const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
+  FinalArgs a = final_args(scores, seq_len, s, idx, n_sel, w);
+  if (max_far <= TF_CACHE) {
+    a.skip = 1;
+    a.h1_ready = hist_ready;
+  } else {
+    hipError_t e = launch_topk_filter(scores, seq_len, s, hist_ready, w, st);
+    if (e != hipSuccess) return e;
+  }
+  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -93,6 +93,17 @@ __device__ int wave_threshold_bin(const int *hist, int need, int n, int &above) 
   return wave_threshold_regs<PER>(v, need, n, above, valid);
 }
 
+// As wave_threshold_bin, also reporting whether the histogram's total was n.
+template <int NBINS>
+__device__ int wave_threshold_bin_valid(const int *hist, int need, int n, int &above, bool &valid) {
+  constexpr int PER = NBINS / 64;
+  const int lane = threadIdx.x & 63;
+  int v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) v[k] = hist[hpad<NBINS>(lane * PER + k)];
+  return wave_threshold_regs<PER>(v, need, n, above, valid);
+}
+
 // Arguments of the final select pass.
 struct FinalArgs {
   const int32_t *scores, *seq_len;
@@ -101,6 +112,8 @@ struct FinalArgs {
   const int2 *cand;
   int n_sub_max, R, Hkv, T_max, NB, window, pool, topk;
   int32_t *idx, *n_sel;
+  int skip;      // no filter ran: every far entry is a candidate (n_far <= TF_CACHE)
+  int h1_ready;  // (with skip) the score pass built this step's level-1 histogram
 };
 
 // LDS of the final pass for NT threads, segments of up to MAXSUB sub-lists,
@@ -148,8 +161,25 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   const int cv0 = threadIdx.x < n_sub_max ? gc[threadIdx.x] : 0;
   const int4 th = reinterpret_cast<const int4 *>(thr)[seg];   // (b1, above b1, valid, in b1)
   constexpr int H2_PER = HIST2_BINS / 64;
+  constexpr int H1_PER = HIST1_BINS / 64;
+  const bool skip = a.skip, h1_ready = a.skip && a.h1_ready;   // uniform
+  int32_t *gh1 = hist1 + (size_t)seg * HIST1_BINS;
   int hv[H2_PER];
-  if (wave == 0) {
+  int h1v[H1_PER];
+  if (wave == 0 && h1_ready) {
+    // the score pass's level-1 histogram of this segment, lane l holding bins
+    // [32l, 32l+32); the same lanes return those bins to zero afterwards
+#pragma unroll
+    for (int k = 0; k < H1_PER / 4; ++k) {
+      const int4 w = reinterpret_cast<const int4 *>(gh1 + lane * H1_PER)[k];
+      h1v[4 * k] = w.x;
+      h1v[4 * k + 1] = w.y;
+      h1v[4 * k + 2] = w.z;
+      h1v[4 * k + 3] = w.w;
+    }
+#pragma unroll
+    for (int k = 0; k < H2_PER; ++k) hv[k] = 0;
+  } else if (wave == 0) {
 #pragma unroll
     for (int k = 0; k < H2_PER / 4; ++k) {
       const int4 w = reinterpret_cast<const int4 *>(gh2 + lane * H2_PER)[k];
@@ -163,17 +193,25 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   for (int q = 0; q < TF_PERT; ++q) marks[threadIdx.x * (TF_PERT + 1) + q] = 0;   // no mark
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   int32_t *out = idx + (size_t)seg * topk;
-  // the filter has run: the segment's level-1 histogram returns to zero
-  int32_t *gh1 = hist1 + (size_t)seg * HIST1_BINS;
-  for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh1[k] = 0;
+  // the segment's level-1 histogram returns to zero (when wave 0 has read
+  // it, by the lanes that read it)
+  if (h1_ready) {
+    if (wave == 0) {
+#pragma unroll
+      for (int k = 0; k < H1_PER / 4; ++k)
+        reinterpret_cast<int4 *>(gh1 + lane * H1_PER)[k] = make_int4(0, 0, 0, 0);
+    }
+  } else {
+    for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh1[k] = 0;
+  }
   if (threadIdx.x == 0 && n_sel) n_sel[seg] = g.k_eff;
 
   // wave 0: the threshold guess T from the level-2 histogram (-1: none),
   // then that histogram returns to zero (its values are consumed)
   if (wave == 0) {
     int T = -1;
-    if (g.k_eff < g.n_far && th.z && th.w >= 0 && th.w <= HIST2_DIRECT_MAX && th.x >= 0 &&
-        th.x < HIST1_BINS) {
+    if (!skip && g.k_eff < g.n_far && th.z && th.w >= 0 && th.w <= HIST2_DIRECT_MAX &&
+        th.x >= 0 && th.x < HIST1_BINS) {
       int above;
       bool valid;
       const int b2 = wave_threshold_regs<H2_PER>(hv, g.k_eff - th.y, th.w, above, valid);
@@ -191,9 +229,10 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
 
   // candidate list: exclusive prefix over the sub-list counts; every
   // non-empty sub-list also marks its first slot with its number + 1
+  // (without a filter pass the candidates are the far entries themselves)
   const int n_sub = (g.n_far + TK_SUB - 1) / TK_SUB;
   int carry = 0;
-  for (int base = 0; base < n_sub; base += TF_THREADS) {
+  for (int base = 0; base < (skip ? 0 : n_sub); base += TF_THREADS) {
     const int sidx = base + threadIdx.x;
     const int v = sidx < n_sub ? (base == 0 ? cv0 : gc[sidx]) : 0;
     int tot;
@@ -209,8 +248,8 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   __syncthreads();
   // Fewer candidates than k means the filter's histogram was not one of these
   // scores: select from the raw scores instead.
-  const bool raw = carry < g.k_eff;
-  const int m = raw ? g.n_far : carry;
+  const bool raw = !skip && carry < g.k_eff;
+  const int m = raw || skip ? g.n_far : carry;
   const int2 *cseg = cand + (size_t)seg * n_sub_max * TK_SUB;
   const int32_t *srow = scores + (size_t)seg * NB;
   const bool in_regs = !raw && m <= TF_CACHE;   // the candidates fit this thread's registers
@@ -218,22 +257,72 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   const int o0 = threadIdx.x * TF_PERT;          // this thread's slots [o0, o0 + TF_PERT)
 
   if (in_regs) {
-    // The sub-list holding slot o is the last mark at or before o: a running
-    // maximum over the marks of this thread's slots, then across the block.
-    int mk[TF_PERT];
-    int run = 0;
-#pragma unroll
-    for (int q = 0; q < TF_PERT; ++q) {
-      run = max(run, marks[threadIdx.x * (TF_PERT + 1) + q]);
-      mk[q] = run;
-    }
-    const int before = block_excl_max<TF_WAVES>(run, sc_own);
     int2 c[TF_PERT];
+    if (skip) {
+      // the far entries themselves, in index order
 #pragma unroll
-    for (int q = 0; q < TF_PERT; ++q) {
-      const int o = min(o0 + q, m - 1);
-      const int s = min(max(max(before, mk[q]), 1) - 1, n_sub - 1);   // clamped: always in bounds
-      c[q] = cseg[(size_t)s * TK_SUB + min(max(o - pre[s], 0), TK_SUB - 1)];
+      for (int q = 0; q < TF_PERT; ++q) {
+        const int o = min(o0 + q, m - 1);
+        c[q] = make_int2(o, biased_key(srow[o]));
+      }
+    } else {
+      // The sub-list holding slot o is the last mark at or before o: a running
+      // maximum over the marks of this thread's slots, then across the block.
+      int mk[TF_PERT];
+      int run = 0;
+#pragma unroll
+      for (int q = 0; q < TF_PERT; ++q) {
+        run = max(run, marks[threadIdx.x * (TF_PERT + 1) + q]);
+        mk[q] = run;
+      }
+      const int before = block_excl_max<TF_WAVES>(run, sc_own);
+#pragma unroll
+      for (int q = 0; q < TF_PERT; ++q) {
+        const int o = min(o0 + q, m - 1);
+        const int s = min(max(max(before, mk[q]), 1) - 1, n_sub - 1);   // clamped: always in bounds
+        c[q] = cseg[(size_t)s * TK_SUB + min(max(o - pre[s], 0), TK_SUB - 1)];
+      }
+    }
+    if (h1_ready) {
+      // Guess T without a filter pass: bin b1 from the score pass's level-1
+      // histogram, then a level-2 histogram of the low bits of the keys in
+      // bin b1, which sit in registers.  The counts below check the guess
+      // against the data before it is used.
+      for (int k = threadIdx.x; k < hpad_size<HIST2_BINS>(); k += TF_THREADS) h2[k] = 0;
+      if (wave == 0) {
+        int above;
+        bool valid;
+        const int b1 = wave_threshold_regs<H1_PER>(h1v, g.k_eff, g.n_far, above, valid);
+        int mine = 0;
+#pragma unroll
+        for (int k = 0; k < H1_PER; ++k) mine = (k == (b1 & (H1_PER - 1))) ? h1v[k] : mine;
+        const int inb1 = __shfl(mine, b1 / H1_PER);
+        if (lane == 0) {
+          res[0] = valid ? b1 : -1;
+          res[1] = g.k_eff - above;
+          res[2] = inb1;
+        }
+      }
+      __syncthreads();
+      const int b1 = res[0];
+      if (b1 >= 0) {
+#pragma unroll
+        for (int q = 0; q < TF_PERT; ++q)
+          if (o0 + q < m && (c[q].y >> HIST2_BITS) == b1)
+            atomicAdd(&h2[hpad<HIST2_BINS>(c[q].y & (HIST2_BINS - 1))], 1);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        int T = -1;
+        if (b1 >= 0) {
+          int above;
+          bool valid;
+          const int b2 = wave_threshold_bin_valid<HIST2_BINS>(h2, res[1], res[2], above, valid);
+          if (valid) T = (b1 << HIST2_BITS) | b2;
+        }
+        if (lane == 0) res[5] = T;
+      }
+      __syncthreads();
     }
     const int T = res[5];
     if (T >= 0) {
@@ -278,7 +367,7 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
 
   // ---- exact path without the level-2 histogram
   auto get = [&](int o) -> int2 {                // uncached access
-    if (raw) return make_int2(o, biased_key(srow[o]));
+    if (raw || skip) return make_int2(o, biased_key(srow[o]));
     int lo = 0, hi = n_sub;                      // last sub-list s with pre[s] <= o
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -296,7 +385,7 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   // >= thr.x.  If that bin is a legal threshold -- fewer than k candidates
   // above it, counted here from the data -- level 1 is known; otherwise it is
   // derived from the candidates' own histogram.
-  bool fast = th.z && !raw && th.x >= 0 && th.x < HIST1_BINS;
+  bool fast = !skip && th.z && !raw && th.x >= 0 && th.x < HIST1_BINS;
   if (fast) {
     int part = 0;
     for (int o = threadIdx.x; o < m; o += TF_THREADS) part += (fetch(o).y >> HIST2_BITS) > th.x;
@@ -396,6 +485,8 @@ inline FinalArgs final_args(const int32_t *scores, const int32_t *seq_len, const
   a.topk = s.topk;
   a.idx = idx;
   a.n_sel = n_sel;
+  a.skip = 0;
+  a.h1_ready = 0;
   return a;
 }
 

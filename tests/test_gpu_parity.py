@@ -118,6 +118,19 @@ def test_topk_with_dirty_workspace(ctx):
     g.layer.idx.fill_(-7)
     g.layer.select(scores=sc)                 # and the region is back to zero
     assert np.array_equal(g.layer.idx.cpu().numpy(), arr["idx"])
+    # the score pass adds its histogram onto the dirty region: the selection's
+    # threshold guess from it is wrong and the check against the data catches it
+    qc, kc = torch.from_numpy(arr["qcode"]).cuda(), torch.from_numpy(arr["kcodes"]).cuda()
+    for garbage in (0x01010101, -1, 0x7fffffff, 0x00100000):
+        g.layer.ws.view(torch.int32)[: g.layer.ws.numel() // 4].fill_(garbage)
+        g.layer.score(qsk=qc, S=kc)
+        g.layer.idx.fill_(-7)
+        g.layer.select()
+        assert np.array_equal(g.layer.idx.cpu().numpy(), arr["idx"]), ("fused", garbage)
+    g.layer.score(qsk=qc, S=kc)
+    g.layer.idx.fill_(-7)
+    g.layer.select()
+    assert np.array_equal(g.layer.idx.cpu().numpy(), arr["idx"])
 
 
 def test_attention_given_oracle_idx(ctx):
