@@ -10,9 +10,13 @@ before timing starts.  `--replicas` distinct copies of the cache (standing in
 for consecutive layers) are visited round-robin so that no step finds the
 previous step's data in the last-level cache.
 
-Prints ONE JSON line with steps/s, the roofline of the dominant kernel
-(sketch_score, HBM-bound) measured with HIP events on the launch stream, and
-the CPU oracle timed on a bounded sample.
+The steps run with SKS_STEP_NO_SCORES (the scores buffer is scratch), so
+that long far regions take the candidate mode, which stores no scores;
+--keep-scores stores them.
+
+Prints ONE JSON line with steps/s, the roofline of the dominant kernel (the
+score pass, HBM-bound) measured with HIP events on the launch stream, and the
+CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -61,6 +65,8 @@ def parse():
     ap.add_argument("--five-calls", action="store_true",
                     help="issue each step as the five individual C-ABI calls instead of the one "
                          "sks_decode_step call")
+    ap.add_argument("--keep-scores", action="store_true",
+                    help="store the int32 scores in every step (no candidate mode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -82,11 +88,12 @@ def algorithmic_bytes(cfg):
     return sketch, gathered, small
 
 
-def counted_traffic(workload):
-    """HBM bytes per score launch from the committed FETCH_SIZE / WRITE_SIZE
-    counter summary (scaled by the copy-kernel calibration it records), or None
-    when there is none for this workload or the score kernel's sources have
-    changed since the counters were taken."""
+def counted_traffic(workload, mode):
+    """HBM bytes per score launch (mode "candidates" or "stores") from the
+    committed FETCH_SIZE / WRITE_SIZE counter summary (scaled by the
+    copy-kernel calibration it records), or None when there is none for this
+    workload and mode or the score kernel's sources have changed since the
+    counters were taken."""
     import hashlib
     path = COUNTERS.format(workload=workload)
     if not os.path.exists(path):
@@ -100,7 +107,8 @@ def counted_traffic(workload):
     for f in SCORE_SOURCES:
         with open(os.path.join(ROOT, "long_context_sparse_sketch_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    if fields.get("workload") != workload or fields.get("score_sources_sha256") != h.hexdigest():
+    if (fields.get("workload") != workload or fields.get("mode", "stores") != mode
+            or fields.get("score_sources_sha256") != h.hexdigest()):
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -232,8 +240,14 @@ def main():
 
     stream = torch.cuda.current_stream()
     runners = [StepRunner(lay, parts=args.parts, streams=args.streams, fused=not args.five_calls,
-                          dense=args.dense)
+                          dense=args.dense, keep_scores=args.keep_scores)
                for lay in layers]
+    # the step's own rule (sks.h, SKS_STEP_NO_SCORES): candidate mode for one
+    # row per sequence, rows of more than 8,192 far entries and at least 2^20
+    # far entries in all
+    max_far = max(0, cfg.T_max - cfg.window) // cfg.pool
+    cand = (not args.keep_scores and not args.dense and not args.five_calls and cfg.R == 1
+            and max_far > 8192 and cfg.B * cfg.Hkv * max_far >= 1 << 20)
     R_ = len(runners)
     spg = args.steps_per_graph or R_
     if R_ % spg:
@@ -318,8 +332,17 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (reps * n)
 
-    # dominant kernel: its average launch duration
-    score_avg_ms = launch_avg_ms(lambda lay: lay.score())
+    # dominant kernel: its average launch duration -- in candidate mode the
+    # score pass alone, on the estimates the steps left in each workspace
+    stores_avg_ms = launch_avg_ms(lambda lay: lay.score())
+    if cand:
+        # the sample pass's estimates in the workspace timed here (the steps
+        # ran through a view with a workspace of its own)
+        for lay in layers:
+            lay.score_candidates()
+        score_avg_ms = launch_avg_ms(lambda lay: lay.score_candidates(flags=sks.CAND_KEEP_ESTIMATE))
+    else:
+        score_avg_ms = stores_avg_ms
     for lay in layers:                       # the extra histograms: back to zero at rest
         sks.workspace_init(lay.ws)
     # attention (gather + merged softmax) the same way, on each layer's last selection
@@ -378,9 +401,15 @@ def main():
         e[1].record(stream)
         lay.query_sketch(q)
         e[2].record(stream)
-        lay.score()
+        if cand:
+            lay.score_candidates()
+        else:
+            lay.score()
         e[3].record(stream)
-        lay.select()
+        if cand:
+            lay.select_candidates()
+        else:
+            lay.select()
         e[4].record(stream)
         lay.attend(q)
         e[5].record(stream)
@@ -414,14 +443,18 @@ def main():
                    "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "window": cfg.window,
                    "topk": cfg.topk, "pool": cfg.pool, "replicas": args.replicas,
                    "schedule": ("five C-ABI calls" if args.five_calls else
-                                "sks_decode_step" + (" (dense)" if args.dense else ""))
+                                "sks_decode_step" + (" (dense)" if args.dense else "")
+                                + (" (candidate mode: scores not stored)" if cand else ""))
                                + f", {args.parts} sub-batches on {args.streams} streams, "
                                + ("eager launches" if args.no_graph else
                                   f"HIP graph replay ({spg} steps per graph)")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": counted_traffic(cfg.name),
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": counted_traffic(cfg.name, "candidates" if cand else "stores"),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
-                     "kernel": "sketch_score", "algorithmic_bytes": sketch_b,
+                     "kernel": ("score pass in candidate mode (sks_score_candidates, "
+                                "SKS_CAND_KEEP_ESTIMATE)" if cand else "sketch_score"),
+                     "algorithmic_bytes": sketch_b,
                      "avg_ms": score_avg_ms,
                      "avg_ms_timing": ("HIP events around back-to-back launches, "
                                        + ("eager" if args.no_graph else
@@ -429,6 +462,7 @@ def main():
         "detail": {
             "algorithmic_bytes_per_step": sketch_b + gather_b + small_b,
             "gathered_kv_bytes": gather_b,
+            "score_with_stores_avg_ms": stores_avg_ms,
             "attn_avg_ms": attn_avg_ms,
             "attn_GBps": gather_b / (attn_avg_ms * 1e-3) / 1e9,
             "gather_pack_avg_ms": gather_avg_ms,

@@ -213,6 +213,41 @@ int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p
                     int32_t flags, int32_t *idx, int32_t *n_sel, void *ws, size_t ws_bytes,
                     sks_stream_t stream);
 
+/* Candidate mode of the score pass and the selection: the same selection as
+ * sks_sketch_score(ws) + sks_topk_select(SKS_TOPK_HIST_READY), bit for bit,
+ * without storing the scores, so that the score pass streams only the
+ * sketches.  sks_score_candidates
+ *   1. (without SKS_CAND_KEEP_ESTIMATE) scores every 64th far entry of each
+ *      (b, i, h) and stores in ws an estimate E of its k-th largest biased
+ *      score (score + 2^20), set low enough that with high probability at
+ *      least k entries reach it;
+ *   2. scores every far token as sks_sketch_score does, accumulates the
+ *      level-1 histogram into ws as sks_sketch_score(ws) does, and keeps in
+ *      ws, instead of the scores, every far entry whose biased score is at
+ *      least E (index and biased score, ascending).
+ * sks_topk_select_candidates then selects as sks_topk_select, from those
+ * entries.  Where fewer than k entries reached E, it recomputes that
+ * segment's scores from qsk and S into `scores` ([B][R][Hkv][NB] int32,
+ * scratch: its contents afterwards are unspecified) and selects from them.
+ * E only decides the time taken, never the result.
+ * Flags of sks_score_candidates:
+ *   SKS_CAND_KEEP_ESTIMATE  reuse the estimates already in ws (step 2 only);
+ *   SKS_CAND_TEST_HIGH      (tests) E above every score: every segment with
+ *                           k_eff < n_far takes the recomputing path;
+ *   SKS_CAND_TEST_ZERO      (tests) E = 0: every far entry is kept.
+ * ws: at least sks_workspace_bytes(); the two calls use the same ws, in this
+ * order, with no other selection call on it in between. */
+#define SKS_CAND_KEEP_ESTIMATE 1
+#define SKS_CAND_TEST_HIGH 2
+#define SKS_CAND_TEST_ZERO 4
+int sks_score_candidates(const int8_t *qsk, const int8_t *S, const sks_kv *kv,
+                         const sks_params *p, int32_t flags, void *ws, size_t ws_bytes,
+                         sks_stream_t stream);
+int sks_topk_select_candidates(const int8_t *qsk, const int8_t *S, const sks_kv *kv,
+                               const sks_params *p, int32_t *scores, int32_t *idx,
+                               int32_t *n_sel, void *ws, size_t ws_bytes,
+                               sks_stream_t stream);
+
 /* Gather/pack ("What it took": pack the picked tokens for the attention
  * kernel).  For every (b, i, h) writes the row's attention set, selected far
  * entries first (ascending, rows of Kp/Vp when pool > 1, else of K/V), then
@@ -264,6 +299,13 @@ int sks_sparse_decode_attn(const uint16_t *q, int32_t Hq, const sks_kv *kv,
  * APPEND sketch rows are written as usual, so that later sparse steps find
  * the sketch current.  Which mode a step takes is the caller's choice (it
  * knows its lengths); the workspace of the sparse step serves both.
+ * With SKS_STEP_NO_SCORES the caller does not read `scores` after the step:
+ * where it pays (one row per sequence, rows of more than 8,192 far entries
+ * and at least 2^20 far entries over all (b, h)), the step scores and
+ * selects in candidate
+ * mode (sks_score_candidates + sks_topk_select_candidates), which stores no
+ * scores; idx, n_sel, out and lse are the same bit for bit, and `scores` is
+ * then scratch with unspecified contents.
  * Every buffer is caller-owned and keeps the layout of the individual call
  * that writes or reads it; NULL is allowed where the individual call allows
  * it (qscale, n_sel, lse; Kp/Vp when pool == 1).  The same validation as the
@@ -287,6 +329,7 @@ typedef struct sks_step {
 } sks_step;
 #define SKS_STEP_APPEND 1   /* sketch the rows' own tokens first */
 #define SKS_STEP_DENSE 2    /* no selection: attend the last window + topk tokens */
+#define SKS_STEP_NO_SCORES 4  /* scores are scratch: candidate mode where it pays */
 int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *step, int32_t flags,
                     void *ws, size_t ws_bytes, sks_stream_t stream);
 

@@ -31,10 +31,14 @@ HEAD_DIM, RANK = 128, 64
 TOPK_HIST_READY = 1
 STEP_APPEND = 1
 STEP_DENSE = 2
+STEP_NO_SCORES = 4
+CAND_KEEP_ESTIMATE = 1
+CAND_TEST_HIGH = 2
+CAND_TEST_ZERO = 4
 
 EXPORTS = ("sks_last_error", "sks_runtime_version", "sks_workspace_bytes", "sks_workspace_init",
            "sks_sketch_build", "sks_sketch_build_query", "sks_sketch_score", "sks_topk_select",
-           "sks_gather_pack", "sks_sparse_decode_attn", "sks_decode_step",
+           "sks_score_candidates", "sks_topk_select_candidates", "sks_gather_pack", "sks_sparse_decode_attn", "sks_decode_step",
            "sks_refit_workspace_bytes", "sks_refit_gram", "sks_refit_basis",
            "sks_refit_key_scale")
 
@@ -100,6 +104,10 @@ def lib():
         L.sks_sketch_score.argtypes = [vp, vp, kvp, pp, vp, vp, sz, vp]
         L.sks_topk_select.restype = ctypes.c_int
         L.sks_topk_select.argtypes = [vp, kvp, pp, i32, vp, vp, vp, sz, vp]
+        L.sks_score_candidates.restype = ctypes.c_int
+        L.sks_score_candidates.argtypes = [vp, vp, kvp, pp, i32, vp, sz, vp]
+        L.sks_topk_select_candidates.restype = ctypes.c_int
+        L.sks_topk_select_candidates.argtypes = [vp, vp, kvp, pp, vp, vp, vp, vp, sz, vp]
         L.sks_gather_pack.restype = ctypes.c_int
         L.sks_gather_pack.argtypes = [kvp, pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.sks_sparse_decode_attn.restype = ctypes.c_int
@@ -371,6 +379,25 @@ def topk_select(scores, cache: Cache, p: Params, idx, n_sel, ws, hist_ready=Fals
                                  _stream(stream)))
 
 
+def score_candidates(qsk, S, cache: Cache, p: Params, ws, flags=0, stream=None):
+    """Candidate mode's score pass (sample estimate unless CAND_KEEP_ESTIMATE)."""
+    d = _Dims(cache, p)
+    qa, sa, wa = _ptrs(_T(qsk, "qsk", d.seg(RANK)), d.S(S), _ws(ws), stream=stream, cache=cache)
+    _check(lib().sks_score_candidates(qa, sa, cache.ref, ctypes.byref(p), int(flags), wa,
+                                      _nbytes(ws), _stream(stream)))
+
+
+def topk_select_candidates(qsk, S, cache: Cache, p: Params, scores, idx, n_sel, ws,
+                           stream=None):
+    """Selection from score_candidates' lists; `scores` is scratch."""
+    d = _Dims(cache, p)
+    qa, sa, ca, ia, na, wa = _ptrs(_T(qsk, "qsk", d.seg(RANK)), d.S(S), d.scores(scores),
+                                   d.idx(idx), _T(n_sel, "n_sel", d.seg(4), optional=True),
+                                   _ws(ws), stream=stream, cache=cache)
+    _check(lib().sks_topk_select_candidates(qa, sa, cache.ref, ctypes.byref(p), ca, ia, na, wa,
+                                            _nbytes(ws), _stream(stream)))
+
+
 def gather_pack(cache: Cache, p: Params, idx, K_out, V_out, n_out, Kp=None, Vp=None,
                 Ks_out=None, Vs_out=None, stream=None):
     d = _Dims(cache, p)
@@ -398,9 +425,10 @@ def sparse_decode_attn(q, cache: Cache, p: Params, idx, out, ws, lse=None, Kp=No
 
 def decode_step(cache: Cache, p: Params, q, basis, key_scale, S, qsk, scores, idx, out, ws,
                 qscale=None, n_sel=None, lse=None, Kp=None, Vp=None, sm_scale=None,
-                basis_per_head=False, append=True, dense=False, stream=None):
+                basis_per_head=False, append=True, dense=False, keep_scores=True, stream=None):
     """The whole decode step (append, query sketch, score, select, attend) in one call;
-    dense: no scoring or selection, attend the last window + topk tokens."""
+    dense: no scoring or selection, attend the last window + topk tokens;
+    keep_scores=False: `scores` is scratch (candidate mode where it pays)."""
     d = _Dims(cache, p)
     qt, Hq = d.q(q)
     sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else sm_scale
@@ -414,7 +442,8 @@ def decode_step(cache: Cache, p: Params, q, basis, key_scale, S, qsk, scores, id
     st = StepDesc(qa, Hq, ba, int(basis_per_head), ka, sa, kpa, vpa, sm, qsa, qca, ca, ia, na,
                   oa, la)
     _check(lib().sks_decode_step(cache.ref, ctypes.byref(p), ctypes.byref(st),
-                                 (STEP_APPEND if append else 0) | (STEP_DENSE if dense else 0),
+                                 (STEP_APPEND if append else 0) | (STEP_DENSE if dense else 0)
+                                 | (0 if keep_scores else STEP_NO_SCORES),
                                  wa, _nbytes(ws), _stream(stream)))
 
 

@@ -18,6 +18,12 @@
 // score of each row in its 1024-entry chunk (plus one; 0 for an empty
 // chunk), so that the top-k filter reads only the chunks that can hold a
 // candidate.
+//
+// In candidate mode (CAND, with HIST) no score is stored: each row keeps,
+// in its chunk's candidate list of the selection workspace, the entries
+// whose biased score reaches the row's estimate E (written beforehand by the
+// selection's sample pass), as (index, biased score) in index order, and the
+// list's length.  The final selection pass then needs no filter pass.
 #include "sks_internal.h"
 
 namespace sks {
@@ -38,16 +44,20 @@ constexpr int SC_UNROLL = 8;                        // rows per lane-quad per st
 constexpr int SC_WAVE_STEP = 16 * SC_UNROLL;        // 128 rows per wave step
 constexpr int SC_BLOCK_STEP = SC_WAVE_STEP * (SC_THREADS / 64);   // 512
 
-template <int R, bool HIST>
+template <int R, bool HIST, bool CAND>
 __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     const int8_t *__restrict__ qsk, const int8_t *__restrict__ S,
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ scores,
     int32_t *__restrict__ hist1, int32_t *__restrict__ cmax, int n_sub_max, int Hkv, int T_max,
-    int NB, int window, int pool, int topk) {
+    int NB, int window, int pool, int topk, const int32_t *__restrict__ est,
+    int2 *__restrict__ cand, int32_t *__restrict__ cnt) {
   static_assert(SCORE_CHUNK == TK_SUB, "one chunk maximum per top-k sub-list");
+  static_assert(SCORE_CHUNK == 4 * SC_THREADS, "candidate compaction: 4 rounds of 64 per wave");
+  static_assert(!CAND || HIST, "candidate mode builds the histogram too");
   __shared__ int lh[HIST ? R * HIST1_BINS : 1];
   __shared__ int lmax[HIST ? R * (SC_THREADS / 64) : 1];
-  __shared__ __align__(16) int lsc[R * SCORE_CHUNK];     // this chunk's scores, written at the end
+  __shared__ int gcnt[CAND ? R * 16 : 1];                // candidates per 64-token group
+  __shared__ __align__(16) int lsc[CAND ? 1 : R * SCORE_CHUNK];   // the chunk's scores, stored at the end
   const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
   const int L0 = clamp_len(seq_len[b], T_max, R);
   const int Lmax = L0 + R - 1;
@@ -77,17 +87,33 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 #pragma unroll
   for (int i = 0; i < R; ++i)
     qv[i] = *reinterpret_cast<const int4 *>(qsk + ((size_t)(b * R + i) * Hkv + h) * RANK + part * 16);
+  int e_row[R];                                    // candidate mode: each row's estimate
+#pragma unroll
+  for (int i = 0; i < R; ++i) e_row[i] = CAND ? est[(size_t)(b * R + i) * Hkv + h] : 0;
 
   const int4 *Sbh = reinterpret_cast<const int4 *>(S + (size_t)bh * NB * RANK) + part;
   int32_t *out[R];
   int kmax[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    out[i] = scores + ((size_t)(b * R + i) * Hkv + h) * NB;
+    out[i] = CAND ? nullptr : scores + ((size_t)(b * R + i) * Hkv + h) * NB;
     kmax[i] = 0;
   }
 
-  for (int base = c0 + wave * SC_WAVE_STEP; base < c1; base += SC_BLOCK_STEP) {
+  // candidate mode keeps each lane's keys and the waves' candidate ballots of
+  // its (at most two) steps in registers: [step][lo, hi]
+  int ck[R][4];
+  unsigned long long cm[R][4];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ck[i][k] = 0;
+      cm[i][k] = 0ull;
+    }
+  static_assert(SCORE_CHUNK == 2 * SC_BLOCK_STEP, "two steps per wave and chunk");
+  int it = 0;
+  for (int base = c0 + wave * SC_WAVE_STEP; base < c1; base += SC_BLOCK_STEP, ++it) {
     int4 sv[SC_UNROLL];
 #pragma unroll
     for (int u = 0; u < SC_UNROLL; ++u) {
@@ -114,34 +140,90 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
       }
       const int t_lo = base + part * 16 + quad;
       const int t_hi = t_lo + 64;
-      lsc[i * SCORE_CHUNK + (t_lo - c0)] = lo;
-      lsc[i * SCORE_CHUNK + (t_hi - c0)] = hi;
+      if (CAND) {
+        const int klo = biased_key(lo), khi = biased_key(hi);
+        const unsigned long long blo = __ballot(need_hist[i] && t_lo < nf[i] && klo >= e_row[i]);
+        const unsigned long long bhi = __ballot(need_hist[i] && t_hi < nf[i] && khi >= e_row[i]);
+        if (it == 0) {
+          ck[i][0] = klo;
+          ck[i][1] = khi;
+          cm[i][0] = blo;
+          cm[i][1] = bhi;
+        } else {
+          ck[i][2] = klo;
+          ck[i][3] = khi;
+          cm[i][2] = blo;
+          cm[i][3] = bhi;
+        }
+      } else {
+        lsc[i * SCORE_CHUNK + (t_lo - c0)] = lo;
+        lsc[i * SCORE_CHUNK + (t_hi - c0)] = hi;
+      }
       if (HIST && need_hist[i]) {
         const int klo = biased_key(lo), khi = biased_key(hi);
         if (t_lo < nf[i]) {
           atomicAdd(&lh[i * HIST1_BINS + (klo >> HIST2_BITS)], 1);
-          kmax[i] = max(kmax[i], klo + 1);
+          if (!CAND) kmax[i] = max(kmax[i], klo + 1);
         }
         if (t_hi < nf[i]) {
           atomicAdd(&lh[i * HIST1_BINS + (khi >> HIST2_BITS)], 1);
-          kmax[i] = max(kmax[i], khi + 1);
+          if (!CAND) kmax[i] = max(kmax[i], khi + 1);
         }
       }
     }
   }
-  if (HIST) {
+  if (HIST && !CAND) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int wm = __builtin_amdgcn_readlane(wave_incl_max(kmax[i]), 63);
       if (lane == 0) lmax[i * (SC_THREADS / 64) + wave] = wm;
     }
   }
+  if (CAND && lane == 0) {
+    // 64-token groups in token order: g = step * 8 + wave * 2 + (lo, hi)
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) gcnt[i * 16 + (k >> 1) * 8 + wave * 2 + (k & 1)] = __popcll(cm[i][k]);
+  }
   __syncthreads();
+  if (CAND) {
+    // Lane 4q + p holds token 16p + q of each group: its rank among the
+    // group's candidates counts the set bits of parts p' < p, then those of
+    // part p below quad q.
+    constexpr unsigned long long PART0 = 0x1111111111111111ull;
+    const unsigned long long before_q = (1ull << (4 * quad)) - 1ull;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (!need_hist[i]) continue;                 // uniform: the row selects everything
+      const size_t seg = (size_t)(b * R + i) * Hkv + h;
+      int2 *dst = cand + (seg * n_sub_max + blockIdx.x) * TK_SUB;
+      int tot = 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) tot += gcnt[i * 16 + k];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int g = (k >> 1) * 8 + wave * 2 + (k & 1);
+        int off = 0;
+        for (int j = 0; j < g; ++j) off += gcnt[i * 16 + j];
+        const unsigned long long M = cm[i][k];
+        if ((M >> lane) & 1ull) {
+          int rank = __popcll(M & (PART0 << part) & before_q);
+#pragma unroll
+          for (int pp = 0; pp < 3; ++pp) rank += pp < part ? __popcll(M & (PART0 << pp)) : 0;
+          const int tok = c0 + (k >> 1) * SC_BLOCK_STEP + wave * SC_WAVE_STEP + (k & 1) * 64 +
+                          16 * part + quad;
+          dst[off + rank] = make_int2(tok, ck[i][k]);
+        }
+      }
+      if (threadIdx.x == 0) cnt[seg * n_sub_max + blockIdx.x] = tot;
+    }
+  }
   // The chunk's scores leave in one burst per row: 16-byte stores when the
   // row is 16-byte aligned here, else 4-byte stores.
   const int n_chunk = c1 - c0;
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
+  for (int i = 0; i < (CAND ? 0 : R); ++i) {
     int32_t *dst = out[i] + c0;
     if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
       for (int v = threadIdx.x; 4 * v < n_chunk; v += SC_THREADS) {
@@ -158,7 +240,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     }
   }
   if (HIST) {
-    if (threadIdx.x < R) {
+    if (!CAND && threadIdx.x < R) {
       const int i = threadIdx.x;
       int m = 0;
 #pragma unroll
@@ -176,7 +258,9 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 }  // namespace
 
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
-                        const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st) {
+                        const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st,
+                        bool cand) {
+  if (cand && !w) return hipErrorInvalidValue;
   int32_t *hist1 = w ? w->hist1 : nullptr;
   int32_t *cmax = w ? w->cmax : nullptr;
   const int n_sub_max = w ? w->nchunk : 0;
@@ -187,14 +271,18 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
   switch (s.R) {
 #define SKS_SCORE_CASE(RR)                                                                     \
   case RR:                                                                                     \
-    if (hist1)                                                                                 \
-      score_kernel<RR, true><<<grid, SC_THREADS, 0, st>>>(qsk, S, seq_len, scores, hist1,      \
-                                                          cmax, n_sub_max, s.Hkv, s.T_max,     \
-                                                          s.NB, s.window, s.pool, s.topk);     \
+    if (cand)                                                                                  \
+      score_kernel<RR, true, true><<<grid, SC_THREADS, 0, st>>>(                               \
+          qsk, S, seq_len, nullptr, hist1, nullptr, n_sub_max, s.Hkv, s.T_max, s.NB, s.window, \
+          s.pool, s.topk, w->est, w->cand, w->cnt);                                            \
+    else if (hist1)                                                                            \
+      score_kernel<RR, true, false><<<grid, SC_THREADS, 0, st>>>(                              \
+          qsk, S, seq_len, scores, hist1, cmax, n_sub_max, s.Hkv, s.T_max, s.NB, s.window,     \
+          s.pool, s.topk, nullptr, nullptr, nullptr);                                          \
     else                                                                                       \
-      score_kernel<RR, false><<<grid, SC_THREADS, 0, st>>>(qsk, S, seq_len, scores, nullptr,   \
-                                                           nullptr, 0, s.Hkv, s.T_max, s.NB,   \
-                                                           s.window, s.pool, s.topk);          \
+      score_kernel<RR, false, false><<<grid, SC_THREADS, 0, st>>>(                             \
+          qsk, S, seq_len, scores, nullptr, nullptr, 0, s.Hkv, s.T_max, s.NB, s.window,        \
+          s.pool, s.topk, nullptr, nullptr, nullptr);                                          \
     break;
     SKS_SCORE_CASE(1)
     SKS_SCORE_CASE(2)

@@ -245,6 +245,54 @@ int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p
                     "sks_topk_select");
 }
 
+int sks_score_candidates(const int8_t *qsk, const int8_t *S, const sks_kv *kv,
+                         const sks_params *p, int32_t flags, void *ws, size_t ws_bytes_given,
+                         sks_stream_t stream) {
+  sks::Shape s;
+  TRY(check_shape(kv, p, s));
+  REQUIRE_PTR(qsk, 16);
+  REQUIRE_PTR(S, 16);
+  if (sks::ceil_div(s.NB, sks::TK_SUB) > sks::TK_MAX_SUBS)
+    return fail(SKS_ERR_UNSUPPORTED, "T_max / pool above %d is not supported by the selection",
+                sks::TK_MAX_SUBS * sks::TK_SUB);
+  const int32_t known = SKS_CAND_KEEP_ESTIMATE | SKS_CAND_TEST_HIGH | SKS_CAND_TEST_ZERO;
+  REQUIRE((flags & ~known) == 0, "unknown flags 0x%x", flags);
+  REQUIRE((flags & (SKS_CAND_TEST_HIGH | SKS_CAND_TEST_ZERO)) !=
+              (SKS_CAND_TEST_HIGH | SKS_CAND_TEST_ZERO),
+          "SKS_CAND_TEST_HIGH and SKS_CAND_TEST_ZERO exclude each other");
+  TRY(check_ws(ws, ws_bytes_given, topk_need(s)));
+  const sks::TopkWs w = sks::topk_ws_carve(s, ws);
+  const hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (!(flags & SKS_CAND_KEEP_ESTIMATE))
+    e = sks::launch_topk_sample(qsk, S, kv->seq_len, s, w,
+                                (flags & SKS_CAND_TEST_HIGH) ? 1 : (flags & SKS_CAND_TEST_ZERO) ? 2 : 0,
+                                hs);
+  if (e == hipSuccess) e = sks::launch_score(qsk, S, kv->seq_len, s, nullptr, &w, hs, true);
+  return hip_status(e, "sks_score_candidates");
+}
+
+int sks_topk_select_candidates(const int8_t *qsk, const int8_t *S, const sks_kv *kv,
+                               const sks_params *p, int32_t *scores, int32_t *idx,
+                               int32_t *n_sel, void *ws, size_t ws_bytes_given,
+                               sks_stream_t stream) {
+  sks::Shape s;
+  TRY(check_shape(kv, p, s));
+  REQUIRE_PTR(qsk, 16);
+  REQUIRE_PTR(S, 16);
+  REQUIRE_PTR(scores, 4);
+  REQUIRE_PTR(idx, 4);
+  if (n_sel) REQUIRE(aligned(n_sel, 4), "n_sel must be 4-byte aligned");
+  if (sks::ceil_div(s.NB, sks::TK_SUB) > sks::TK_MAX_SUBS)
+    return fail(SKS_ERR_UNSUPPORTED, "T_max / pool above %d is not supported by the selection",
+                sks::TK_MAX_SUBS * sks::TK_SUB);
+  TRY(check_ws(ws, ws_bytes_given, topk_need(s)));
+  const sks::TopkWs w = sks::topk_ws_carve(s, ws);
+  return hip_status(sks::launch_topk_cand(qsk, S, scores, kv->seq_len, s, idx, n_sel, w,
+                                          (hipStream_t)stream),
+                    "sks_topk_select_candidates");
+}
+
 int sks_gather_pack(const sks_kv *kv, const sks_params *p, const int32_t *idx, const uint16_t *Kp,
                     const uint16_t *Vp, void *K_out, void *V_out, uint16_t *Ks_out,
                     uint16_t *Vs_out, int32_t *n_out, sks_stream_t stream) {
@@ -300,7 +348,8 @@ int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *st, i
   TRY(check_shape(kv, p, s));
   TRY(check_cache(kv, true));
   REQUIRE(st != nullptr, "step must not be NULL");
-  REQUIRE((flags & ~(SKS_STEP_APPEND | SKS_STEP_DENSE)) == 0, "unknown flags 0x%x", flags);
+  REQUIRE((flags & ~(SKS_STEP_APPEND | SKS_STEP_DENSE | SKS_STEP_NO_SCORES)) == 0,
+          "unknown flags 0x%x", flags);
   TRY(check_heads(st->Hq, kv->Hkv));
   REQUIRE(st->basis_per_head == 0 || st->basis_per_head == 1, "basis_per_head must be 0 or 1");
   REQUIRE_PTR(st->q, 16);
@@ -335,7 +384,16 @@ int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *st, i
     e = sks::launch_sketch_query(st->q, s.B, s.R, st->Hq, s.Hkv, st->basis, st->basis_per_head,
                                  st->qsk, st->qscale, hs);
   const bool dense = (flags & SKS_STEP_DENSE) != 0;
-  if (!dense) {
+  const bool cand = (flags & SKS_STEP_NO_SCORES) && sks::topk_cand_preferred(s);
+  if (!dense && cand) {
+    if (e == hipSuccess)
+      e = sks::launch_topk_sample(st->qsk, st->S, kv->seq_len, s, w, 0, hs);
+    if (e == hipSuccess)
+      e = sks::launch_score(st->qsk, st->S, kv->seq_len, s, nullptr, &w, hs, true);
+    if (e == hipSuccess)
+      e = sks::launch_topk_cand(st->qsk, st->S, st->scores, kv->seq_len, s, st->idx, st->n_sel,
+                                w, hs);
+  } else if (!dense) {
     if (e == hipSuccess) e = sks::launch_score(st->qsk, st->S, kv->seq_len, s, st->scores, &w, hs);
     if (e == hipSuccess)
       e = sks::launch_topk(st->scores, kv->seq_len, s, true, st->idx, st->n_sel, w, hs);

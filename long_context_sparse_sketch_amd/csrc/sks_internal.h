@@ -239,20 +239,25 @@ size_t topk_scratch_bytes(const Shape &s);
 size_t attn_scratch_bytes(const Shape &s, int G);
 
 hipError_t launch_fill(int32_t *p, size_t n, hipStream_t st);
-// With `w` (non-null) the score pass also builds the selection histogram.
+// With `w` (non-null) the score pass also builds the selection histogram;
+// with `cand` it stores no scores but the selection's candidates at or above
+// the sample pass's estimates (candidate mode).
 struct TopkWs;
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
-                        const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st);
+                        const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st,
+                        bool cand = false);
 
 struct TopkWs {
   int32_t *hist1;     // [nseg][HIST1_BINS], zero at rest
   int32_t *hist2;     // [nseg][HIST2_BINS], zero at rest
   int32_t *cmax;      // [nseg][nchunk]: largest biased score of each sub-list + 1 (0: empty)
+  int32_t *hsamp;     // [nseg][HIST1_BINS]: candidate mode's sample histogram, zero at rest
   int32_t *counters;  // [nseg][4]: threshold bin b1, count above it, valid, count in b1
   char *scratch;      // start of the selection scratch (cnt, cand)
   char *attn;         // start of the attention partials (after the selection scratch)
   int32_t *cnt;       // [nseg][nchunk]
   int2 *cand;         // [nseg][nchunk * TK_SUB]
+  int32_t *est;       // [nseg]: candidate mode's per-segment key estimate
   int nchunk;         // sub-lists per segment
 };
 TopkWs topk_ws_carve(const Shape &s, void *ws);
@@ -261,6 +266,15 @@ hipError_t launch_topk_filter(const int32_t *scores, const int32_t *seq_len, con
 hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shape &s,
                        bool hist_ready, int32_t *idx, int32_t *n_sel, const TopkWs &w,
                        hipStream_t st);
+// Candidate mode: the sample pass (per-segment estimates; force 1: above
+// every key, 2: zero), and the final pass over the score pass's candidates,
+// which rescores a segment into `scores` when its estimate was too high.
+bool topk_cand_preferred(const Shape &s);
+hipError_t launch_topk_sample(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
+                              const Shape &s, const TopkWs &w, int force, hipStream_t st);
+hipError_t launch_topk_cand(const int8_t *qsk, const int8_t *S, int32_t *scores,
+                            const int32_t *seq_len, const Shape &s, int32_t *idx,
+                            int32_t *n_sel, const TopkWs &w, hipStream_t st);
 
 hipError_t launch_step_prologue(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
                                 const float *basis, int basis_per_head, const float *key_scale,

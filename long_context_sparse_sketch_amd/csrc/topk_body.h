@@ -114,6 +114,13 @@ struct FinalArgs {
   int32_t *idx, *n_sel;
   int skip;      // no filter ran: every far entry is a candidate (n_far <= TF_CACHE)
   int h1_ready;  // (with skip) the score pass built this step's level-1 histogram
+  // Candidate mode: the score pass wrote the candidate lists (every far entry
+  // at or above the segment's estimate) and the level-1 histogram, and no
+  // scores.  A segment with fewer than k candidates is rescored from qsk and
+  // S into `rescore` (the scores buffer) and selected from there.
+  int cand_mode;
+  const int8_t *qsk, *S;
+  int32_t *rescore;
 };
 
 // LDS of the final pass for NT threads, segments of up to MAXSUB sub-lists,
@@ -139,7 +146,7 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   constexpr int TF_WAVES = NT / 64;
   constexpr int TF_PERT = TF_CACHE / NT;
   static_assert(TF_PERT * NT == TF_CACHE, "slots per thread");
-  const int32_t *__restrict__ scores = a.scores;
+  const int32_t *scores = a.scores;           // written by this pass when rescoring
   const int32_t *__restrict__ seq_len = a.seq_len;
   int32_t *__restrict__ hist1 = a.hist1;
   int32_t *__restrict__ hist2 = a.hist2;
@@ -162,7 +169,8 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   const int4 th = reinterpret_cast<const int4 *>(thr)[seg];   // (b1, above b1, valid, in b1)
   constexpr int H2_PER = HIST2_BINS / 64;
   constexpr int H1_PER = HIST1_BINS / 64;
-  const bool skip = a.skip, h1_ready = a.skip && a.h1_ready;   // uniform
+  const bool skip = a.skip, cmode = a.cand_mode;   // uniform
+  const bool h1_ready = (skip && a.h1_ready) || cmode;   // this step's level-1 histogram
   int32_t *gh1 = hist1 + (size_t)seg * HIST1_BINS;
   int hv[H2_PER];
   int h1v[H1_PER];
@@ -210,7 +218,7 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   // then that histogram returns to zero (its values are consumed)
   if (wave == 0) {
     int T = -1;
-    if (!skip && g.k_eff < g.n_far && th.z && th.w >= 0 && th.w <= HIST2_DIRECT_MAX &&
+    if (!skip && !cmode && g.k_eff < g.n_far && th.z && th.w >= 0 && th.w <= HIST2_DIRECT_MAX &&
         th.x >= 0 && th.x < HIST1_BINS) {
       int above;
       bool valid;
@@ -247,11 +255,43 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   if (threadIdx.x == 0) pre[n_sub] = carry;
   __syncthreads();
   // Fewer candidates than k means the filter's histogram was not one of these
-  // scores: select from the raw scores instead.
+  // scores (candidate mode: the estimate lay above the k-th largest key):
+  // select from the raw scores instead.
   const bool raw = !skip && carry < g.k_eff;
+  if (raw && cmode) {
+    // candidate mode stored no scores: recompute this segment's, exactly as
+    // the score pass does (int32 dot products of the int8 codes)
+    const int4 *qrow = reinterpret_cast<const int4 *>(a.qsk + (size_t)seg * RANK);
+    const int4 q0 = qrow[0], q1 = qrow[1], q2 = qrow[2], q3 = qrow[3];
+    const int4 *Sseg = reinterpret_cast<const int4 *>(a.S + ((size_t)g.b * Hkv + g.h) * NB * RANK);
+    int32_t *dst = a.rescore + (size_t)seg * NB;
+    for (int o = threadIdx.x; o < g.n_far; o += TF_THREADS) {
+      const int4 *r = Sseg + (size_t)o * 4;
+      const int4 s0 = r[0], s1 = r[1], s2 = r[2], s3 = r[3];
+      int acc = 0;
+      acc = __builtin_amdgcn_sdot4(s0.x, q0.x, acc, false);
+      acc = __builtin_amdgcn_sdot4(s0.y, q0.y, acc, false);
+      acc = __builtin_amdgcn_sdot4(s0.z, q0.z, acc, false);
+      acc = __builtin_amdgcn_sdot4(s0.w, q0.w, acc, false);
+      acc = __builtin_amdgcn_sdot4(s1.x, q1.x, acc, false);
+      acc = __builtin_amdgcn_sdot4(s1.y, q1.y, acc, false);
+      acc = __builtin_amdgcn_sdot4(s1.z, q1.z, acc, false);
+      acc = __builtin_amdgcn_sdot4(s1.w, q1.w, acc, false);
+      acc = __builtin_amdgcn_sdot4(s2.x, q2.x, acc, false);
+      acc = __builtin_amdgcn_sdot4(s2.y, q2.y, acc, false);
+      acc = __builtin_amdgcn_sdot4(s2.z, q2.z, acc, false);
+      acc = __builtin_amdgcn_sdot4(s2.w, q2.w, acc, false);
+      acc = __builtin_amdgcn_sdot4(s3.x, q3.x, acc, false);
+      acc = __builtin_amdgcn_sdot4(s3.y, q3.y, acc, false);
+      acc = __builtin_amdgcn_sdot4(s3.z, q3.z, acc, false);
+      acc = __builtin_amdgcn_sdot4(s3.w, q3.w, acc, false);
+      dst[o] = acc;
+    }
+    __syncthreads();                             // the workgroup's stores are visible to it
+  }
   const int m = raw || skip ? g.n_far : carry;
   const int2 *cseg = cand + (size_t)seg * n_sub_max * TK_SUB;
-  const int32_t *srow = scores + (size_t)seg * NB;
+  const int32_t *srow = (cmode ? a.rescore : scores) + (size_t)seg * NB;
   const bool in_regs = !raw && m <= TF_CACHE;   // the candidates fit this thread's registers
   const bool cached = LDS_CACHE && in_regs;     // ... and the LDS cache of the exact path
   const int o0 = threadIdx.x * TF_PERT;          // this thread's slots [o0, o0 + TF_PERT)
@@ -385,7 +425,7 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   // >= thr.x.  If that bin is a legal threshold -- fewer than k candidates
   // above it, counted here from the data -- level 1 is known; otherwise it is
   // derived from the candidates' own histogram.
-  bool fast = !skip && th.z && !raw && th.x >= 0 && th.x < HIST1_BINS;
+  bool fast = !skip && !cmode && th.z && !raw && th.x >= 0 && th.x < HIST1_BINS;
   if (fast) {
     int part = 0;
     for (int o = threadIdx.x; o < m; o += TF_THREADS) part += (fetch(o).y >> HIST2_BITS) > th.x;
@@ -487,6 +527,10 @@ inline FinalArgs final_args(const int32_t *scores, const int32_t *seq_len, const
   a.n_sel = n_sel;
   a.skip = 0;
   a.h1_ready = 0;
+  a.cand_mode = 0;
+  a.qsk = nullptr;
+  a.S = nullptr;
+  a.rescore = nullptr;
   return a;
 }
 

@@ -113,6 +113,17 @@ class SparseDecodeLayer:
         sks.sketch_score(self.qsk if qsk is None else qsk, self.S if S is None else S,
                          self.cache, self.p, self.scores, self.ws if fuse_hist else None, stream)
 
+    def score_candidates(self, stream=None, qsk=None, S=None, flags=0):
+        """Candidate mode's score pass: no scores stored (see select_candidates)."""
+        sks.score_candidates(self.qsk if qsk is None else qsk, self.S if S is None else S,
+                             self.cache, self.p, self.ws, flags, stream)
+
+    def select_candidates(self, stream=None, qsk=None, S=None):
+        """Selection from score_candidates' lists (self.scores is scratch)."""
+        sks.topk_select_candidates(self.qsk if qsk is None else qsk, self.S if S is None else S,
+                                   self.cache, self.p, self.scores, self.idx, self.n_sel,
+                                   self.ws, stream)
+
     def select(self, stream=None, scores=None, hist_ready=None):
         """Top-k; hist_ready defaults to True for the layer's own scores, which
         `score()` produced with the fused histogram."""
@@ -131,16 +142,18 @@ class SparseDecodeLayer:
         rows up to max_len tokens (the switch: dense for short rows)."""
         return self.pool == 1 and max_len + self.R - 1 <= self.window + self.topk
 
-    def step(self, q, stream=None, append=True, fused=True, dense=False):
+    def step(self, q, stream=None, append=True, fused=True, dense=False, keep_scores=True):
         """One step; `fused` issues it as the single sks_decode_step call,
         otherwise as the individual calls (same results).  `dense` skips
-        scoring and selection (one call only)."""
+        scoring and selection (one call only).  keep_scores=False lets the
+        fused step run the selection in candidate mode, which stores no
+        scores (same idx, out and lse)."""
         if fused or dense:
             sks.decode_step(self.cache, self.p, q, self.basis, self.key_scale, self.S, self.qsk,
                             self.scores, self.idx, self.out, self.ws, qscale=self.qscale,
                             n_sel=self.n_sel, lse=self.lse, Kp=self.Kp, Vp=self.Vp,
                             basis_per_head=self.basis_per_head, append=append, dense=dense,
-                            stream=stream)
+                            keep_scores=keep_scores, stream=stream)
             return self.out, self.lse
         if append:
             self.build_sketch(sks.APPEND, 0, stream)
@@ -155,10 +168,12 @@ class StepRunner:
     """One decode step of a layer, split into `parts` sub-batches on `streams`
     streams (fork/join on the caller's current stream), optionally captured
     into a HIP graph and replayed.  `dense`: the step without selection (the
-    caller's switch for short rows, see SparseDecodeLayer.dense_covers)."""
+    caller's switch for short rows, see SparseDecodeLayer.dense_covers).
+    `keep_scores=False`: the scores buffer is scratch (candidate mode)."""
 
     def __init__(self, layer: SparseDecodeLayer, parts: int = 1, streams: int = 1,
-                 overlap_append: bool = False, fused: bool = True, dense: bool = False):
+                 overlap_append: bool = False, fused: bool = True, dense: bool = False,
+                 keep_scores: bool = True):
         parts = max(1, min(parts, layer.B))
         bounds = [layer.B * k // parts for k in range(parts + 1)]
         self.layer = layer
@@ -170,6 +185,7 @@ class StepRunner:
         self.graph = None
         self.fused = fused
         self.dense = dense
+        self.keep_scores = keep_scores
 
     def step(self, q):
         main = torch.cuda.current_stream()
@@ -181,7 +197,8 @@ class StepRunner:
         side = self.append_stream if self.layer.window >= self.layer.R else None
         if side is None and len(self.streams) == 1 and len(self.views) == 1:
             # plain single-stream step on the caller's stream
-            self.views[0].step(q, fused=self.fused, dense=self.dense)
+            self.views[0].step(q, fused=self.fused, dense=self.dense,
+                               keep_scores=self.keep_scores)
             return self.layer.out, self.layer.lse
         if side is not None:
             side.wait_stream(main)
@@ -192,7 +209,7 @@ class StepRunner:
             st = self.streams[k % len(self.streams)]
             with torch.cuda.stream(st):
                 v.step(q[self.bounds[k]:self.bounds[k + 1]], append=side is None, fused=self.fused,
-                       dense=self.dense)
+                       dense=self.dense, keep_scores=self.keep_scores)
         for st in self.streams:
             main.wait_stream(st)
         if side is not None:

@@ -244,6 +244,25 @@ def test_cache_size_limit(L, pool):
         assert rc == code, (T, sks.last_error())
 
 
+def test_candidate_calls_argument_errors(L):
+    k, p = kv(), sks.params(64, 32)
+    sc = lambda flags=0, qsk=FAKE, S=FAKE, ws=FAKE, nb=1 << 30: L.sks_score_candidates(
+        qsk, S, ctypes.byref(k), ctypes.byref(p), flags, ws, nb, None)
+    assert sc(flags=8) == sks.SKS_ERR_ARG and "flags" in sks.last_error()
+    assert sc(flags=sks.CAND_TEST_HIGH | sks.CAND_TEST_ZERO) == sks.SKS_ERR_ARG
+    assert "exclude" in sks.last_error()
+    assert sc(qsk=None) == sks.SKS_ERR_ARG and "qsk" in sks.last_error()
+    assert sc(S=FAKE + 4) == sks.SKS_ERR_ARG and "aligned" in sks.last_error()
+    assert sc(ws=None) == sks.SKS_ERR_WORKSPACE
+    assert sc(nb=16) == sks.SKS_ERR_WORKSPACE
+    sel = lambda scores=FAKE, idx=FAKE, n_sel=None, nb=1 << 30: L.sks_topk_select_candidates(
+        FAKE, FAKE, ctypes.byref(k), ctypes.byref(p), scores, idx, n_sel, FAKE, nb, None)
+    assert sel(scores=None) == sks.SKS_ERR_ARG and "scores" in sks.last_error()
+    assert sel(idx=None) == sks.SKS_ERR_ARG and "idx" in sks.last_error()
+    assert sel(n_sel=FAKE + 2) == sks.SKS_ERR_ARG and "n_sel" in sks.last_error()
+    assert sel(nb=16) == sks.SKS_ERR_WORKSPACE
+
+
 def step_desc(**kw):
     d = dict(q=FAKE, Hq=8, basis=FAKE, basis_per_head=0, key_scale=FAKE, S=FAKE, Kp=None, Vp=None,
              sm_scale=0.088, qsk=FAKE, qscale=None, scores=FAKE, idx=FAKE, n_sel=None, out=FAKE,
@@ -258,7 +277,7 @@ def test_decode_step_argument_errors(L):
         ctypes.byref(k), ctypes.byref(p), st if st is None else ctypes.byref(st), flags, ws, nb,
         None)
     assert call(None) == sks.SKS_ERR_ARG and "step" in sks.last_error()
-    assert call(step_desc(), flags=4) == sks.SKS_ERR_ARG and "flags" in sks.last_error()
+    assert call(step_desc(), flags=16) == sks.SKS_ERR_ARG and "flags" in sks.last_error()
     assert call(step_desc(), flags=8 | 3) == sks.SKS_ERR_ARG and "flags" in sks.last_error()
     assert call(step_desc(Hq=6)) == sks.SKS_ERR_ARG and "multiple" in sks.last_error()
     assert call(step_desc(scores=None)) == sks.SKS_ERR_ARG and "scores" in sks.last_error()

@@ -27,8 +27,8 @@ def test_algorithmic_bytes_of_the_250k_workload():
 
 
 def test_counted_traffic_follows_the_score_sources(tmp_path, monkeypatch):
-    """A counter summary is used only for its workload and only while the
-    score kernel's sources hash to the value recorded with it."""
+    """A counter summary is used only for its workload and score-pass mode and
+    only while the score kernel's sources hash to the value recorded with it."""
     import hashlib
     sys.path.insert(0, ROOT)
     import bench
@@ -39,11 +39,16 @@ def test_counted_traffic_follows_the_score_sources(tmp_path, monkeypatch):
             f"score_sources_sha256: {h.hexdigest()}\ntraffic_bytes_per_launch: 537628512\n")
     monkeypatch.setattr(bench, "COUNTERS", str(tmp_path / "score_kernel_{workload}_hbm_counters.txt"))
     (tmp_path / "score_kernel_multi_agent_250k_hbm_counters.txt").write_text(body)
-    assert bench.counted_traffic("multi_agent_250k") == 537628512
-    assert bench.counted_traffic("tiny") is None
+    assert bench.counted_traffic("multi_agent_250k", "stores") == 537628512
+    assert bench.counted_traffic("multi_agent_250k", "candidates") is None
+    assert bench.counted_traffic("tiny", "stores") is None
+    (tmp_path / "score_kernel_multi_agent_250k_hbm_counters.txt").write_text(
+        body + "mode: candidates\n")
+    assert bench.counted_traffic("multi_agent_250k", "candidates") == 537628512
+    assert bench.counted_traffic("multi_agent_250k", "stores") is None
     (tmp_path / "score_kernel_multi_agent_250k_hbm_counters.txt").write_text(
         body.replace("score_sources_sha256: ", "score_sources_sha256: 00"))
-    assert bench.counted_traffic("multi_agent_250k") is None
+    assert bench.counted_traffic("multi_agent_250k", "stores") is None
 
 
 def test_committed_counter_summary_parses():

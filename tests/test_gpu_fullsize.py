@@ -8,13 +8,19 @@ For each configuration:
 * with the oracle's int8 key/query codes written into the sampled segments,
   the GPU scores and selected indices there are bit-exact and the attention
   outputs are within tolerance (same kernels and launch shapes as the graph);
+* the selection's candidate mode gives the same indices there, with the
+  sample pass's estimate and with every segment recomputing its scores;
 * the end-to-end step (GPU sketches) recalls the planted needles on every
-  segment of the batch.
+  segment of the batch;
+* the step without stored scores (candidate mode, as the benchmark runs it)
+  gives the stored-score step's indices, outputs and log-sum-exps bit for
+  bit on every segment.
 """
 import numpy as np
 import pytest
 import torch
 
+from long_context_sparse_sketch_amd import binding as sks
 from long_context_sparse_sketch_amd import configs as C
 from long_context_sparse_sketch_amd.runtime import StepRunner
 from long_context_sparse_sketch_amd.synth import make_case
@@ -78,6 +84,19 @@ def test_full_size_sampled_parity(cfg):
             assert_attn_close(out[b, i, sl], r["out"][i], f"{cfg.name} {(b, i, h)}")
             lse_close(lse[b, i, sl], r["lse"][i], f"{cfg.name} {(b, i, h)}")
 
+    # 2b. the selection's candidate mode on the same codes: the same indices,
+    #     with the sample pass's estimate and with every segment recomputing
+    qc, kc = g.layer.qsk.clone(), g.layer.S
+    for flags in (0, sks.CAND_TEST_HIGH):
+        g.layer.score_candidates(qsk=qc, S=kc, flags=flags)
+        g.layer.idx.fill_(-7)
+        g.layer.select_candidates(qsk=qc, S=kc)
+        torch.cuda.synchronize()
+        idx = g.layer.idx.cpu().numpy()
+        for (b, h), r in ref.items():
+            for i in range(cfg.R):
+                assert np.array_equal(idx[b, i, h], r["idx"][i]), (flags, b, i, h)
+
     # 3. end to end (GPU sketches, graph replay): needle recall on every segment
     g.layer.build_sketch(0, g.T)
     runner.replay()
@@ -93,4 +112,18 @@ def test_full_size_sampled_parity(cfg):
             assert np.isin(units, sel).all(), (b, h)
         else:
             assert np.isin(sel, units).all(), (b, h)
+
+    # 4. the benchmark's step (SKS_STEP_NO_SCORES: candidate mode at these
+    #    sizes) against the stored-score step, every segment, bit for bit
+    lay = g.layer
+    want = [t.clone() for t in (lay.idx, lay.n_sel, lay.out, lay.lse)]
+    runner_ns = StepRunner(lay, keep_scores=False)
+    runner_ns.capture(g.q)
+    for t in (lay.idx, lay.n_sel):
+        t.fill_(-7)
+    runner_ns.replay()
+    torch.cuda.synchronize()
+    for name, a, b in zip(("idx", "n_sel", "out", "lse"), want,
+                          (lay.idx, lay.n_sel, lay.out, lay.lse)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (cfg.name, name)
     flush(f"[full] {cfg.name}: ok")
