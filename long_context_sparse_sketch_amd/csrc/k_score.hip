@@ -21,9 +21,11 @@
 //
 // In candidate mode (CAND, with HIST) no score is stored: each row keeps,
 // in its chunk's candidate list of the selection workspace, the entries
-// whose biased score reaches the row's estimate E (written beforehand by the
-// selection's sample pass), as (index, biased score) in index order, and the
-// list's length.  The final selection pass then needs no filter pass.
+// whose biased score reaches the row's estimate E, as (index, biased score)
+// in index order, and the list's length.  Every workgroup derives E itself
+// from the segment's sample histogram (built beforehand by the selection's
+// sample pass; see k_topk.hip for the rule), so every workgroup of a segment
+// finds the same E.  The final selection pass then needs no filter pass.
 #include "sks_internal.h"
 
 namespace sks {
@@ -49,14 +51,16 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     const int8_t *__restrict__ qsk, const int8_t *__restrict__ S,
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ scores,
     int32_t *__restrict__ hist1, int32_t *__restrict__ cmax, int n_sub_max, int Hkv, int T_max,
-    int NB, int window, int pool, int topk, const int32_t *__restrict__ est,
-    int2 *__restrict__ cand, int32_t *__restrict__ cnt) {
+    int NB, int window, int pool, int topk, const int32_t *__restrict__ hsamp,
+    int2 *__restrict__ cand, int32_t *__restrict__ cnt, int force) {
   static_assert(SCORE_CHUNK == TK_SUB, "one chunk maximum per top-k sub-list");
   static_assert(SCORE_CHUNK == 4 * SC_THREADS, "candidate compaction: 4 rounds of 64 per wave");
   static_assert(!CAND || HIST, "candidate mode builds the histogram too");
   __shared__ int lh[HIST ? R * HIST1_BINS : 1];
   __shared__ int lmax[HIST ? R * (SC_THREADS / 64) : 1];
   __shared__ int gcnt[CAND ? R * 16 : 1];                // candidates per 64-token group
+  __shared__ int escan[CAND ? SC_THREADS / 64 : 1];      // estimate: the waves' bin counts
+  __shared__ int e_lds[CAND ? R : 1];
   __shared__ __align__(16) int lsc[CAND ? 1 : R * SCORE_CHUNK];   // the chunk's scores, stored at the end
   const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
   const int L0 = clamp_len(seq_len[b], T_max, R);
@@ -70,12 +74,13 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   const int quad = lane >> 2, part = lane & 3;
   // per-row far counts (rows differ by one token each); a row whose top-k
   // takes everything needs no histogram
-  int nf[R];
+  int nf[R], ke[R];
   bool need_hist[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const RowGeom rg = row_geom(L0, i, window, pool, topk);
     nf[i] = rg.n_far;
+    ke[i] = rg.k_eff;
     need_hist[i] = HIST && rg.k_eff < rg.n_far;
   }
   if (HIST) {
@@ -87,9 +92,26 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 #pragma unroll
   for (int i = 0; i < R; ++i)
     qv[i] = *reinterpret_cast<const int4 *>(qsk + ((size_t)(b * R + i) * Hkv + h) * RANK + part * 16);
-  int e_row[R];                                    // candidate mode: each row's estimate
+  // candidate mode: thread t's 8 bins of each row's sample histogram, from
+  // the top bin down (bins 2047 - 8t ... 2040 - 8t), loaded ahead of the stream
+  constexpr int EPER = HIST1_BINS / SC_THREADS;
+  int hsv[CAND ? R : 1][EPER];
+  if (CAND) {
 #pragma unroll
-  for (int i = 0; i < R; ++i) e_row[i] = CAND ? est[(size_t)(b * R + i) * Hkv + h] : 0;
+    for (int i = 0; i < R; ++i) {
+      const int4 *src = reinterpret_cast<const int4 *>(
+          hsamp + ((size_t)(b * R + i) * Hkv + h) * HIST1_BINS + HIST1_BINS - EPER * (threadIdx.x + 1));
+      const int4 lo4 = src[0], hi4 = src[1];     // ascending bins
+      hsv[i][0] = hi4.w; hsv[i][1] = hi4.z; hsv[i][2] = hi4.y; hsv[i][3] = hi4.x;
+      hsv[i][4] = lo4.w; hsv[i][5] = lo4.z; hsv[i][6] = lo4.y; hsv[i][7] = lo4.x;
+    }
+  }
+  // Every workgroup of a segment must derive the same E (the final pass
+  // relies on one E per segment): bins are clamped to [0, 2^18] -- a real
+  // sample never exceeds 2^17 per bin -- so that no sum below can overflow
+  // and the running counts stay monotone even for a workspace that held
+  // garbage.
+  constexpr int HS_MAX = 1 << 18;
 
   const int4 *Sbh = reinterpret_cast<const int4 *>(S + (size_t)bh * NB * RANK) + part;
   int32_t *out[R];
@@ -108,7 +130,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      ck[i][k] = 0;
+      ck[i][k] = -1;                             // no token: never a candidate
       cm[i][k] = 0ull;
     }
   static_assert(SCORE_CHUNK == 2 * SC_BLOCK_STEP, "two steps per wave and chunk");
@@ -141,19 +163,15 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
       const int t_lo = base + part * 16 + quad;
       const int t_hi = t_lo + 64;
       if (CAND) {
-        const int klo = biased_key(lo), khi = biased_key(hi);
-        const unsigned long long blo = __ballot(need_hist[i] && t_lo < nf[i] && klo >= e_row[i]);
-        const unsigned long long bhi = __ballot(need_hist[i] && t_hi < nf[i] && khi >= e_row[i]);
+        // keys of tokens past the row's far region never become candidates
+        const int klo = t_lo < nf[i] ? biased_key(lo) : -1;
+        const int khi = t_hi < nf[i] ? biased_key(hi) : -1;
         if (it == 0) {
           ck[i][0] = klo;
           ck[i][1] = khi;
-          cm[i][0] = blo;
-          cm[i][1] = bhi;
         } else {
           ck[i][2] = klo;
           ck[i][3] = khi;
-          cm[i][2] = blo;
-          cm[i][3] = bhi;
         }
       } else {
         lsc[i * SCORE_CHUNK + (t_lo - c0)] = lo;
@@ -179,12 +197,56 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
       if (lane == 0) lmax[i * (SC_THREADS / 64) + wave] = wm;
     }
   }
-  if (CAND && lane == 0) {
-    // 64-token groups in token order: g = step * 8 + wave * 2 + (lo, hi)
+  if (CAND) {
+    // Each row's estimate E: the lowest key of the sample histogram's bin
+    // holding the rho-th largest sampled key, rho = 2 k' + 8 with k' the
+    // expected number of sampled entries among the k largest; 0 when fewer
+    // than rho entries were sampled.  force 1: above every key; 2: 0.
 #pragma unroll
-    for (int i = 0; i < R; ++i)
+    for (int i = 0; i < R; ++i) {
+      int sum = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) gcnt[i * 16 + (k >> 1) * 8 + wave * 2 + (k & 1)] = __popcll(cm[i][k]);
+      for (int k = 0; k < EPER; ++k) sum += min(max(hsv[i][k], 0), HS_MAX);
+      const int incl = wave_incl_add(sum);
+      if (lane == 63) escan[wave] = incl;
+      __syncthreads();
+      int before = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < SC_THREADS / 64; ++w) {
+        before += w < wave ? escan[w] : 0;
+        tot += escan[w];
+      }
+      const int m = (nf[i] + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
+      const int kp = nf[i] > 0 ? (int)(((long)ke[i] * m + nf[i] - 1) / nf[i]) : 0;
+      const int rho = 2 * kp + 8;
+      int run = before + incl - sum;             // sampled keys in higher bins
+      const int top = HIST1_BINS - 1 - EPER * (int)threadIdx.x;
+      if (threadIdx.x == 0 && (tot < rho || force)) e_lds[i] = force == 1 ? (1 << 30) : 0;
+      if (!force && tot >= rho && run < rho && run + sum >= rho) {
+        int bin = top - (EPER - 1);
+#pragma unroll
+        for (int k = 0; k < EPER; ++k) {
+          const int c = min(max(hsv[i][k], 0), HS_MAX);
+          if (run < rho && run + c >= rho) bin = top - k;
+          run += c;
+        }
+        e_lds[i] = bin << HIST2_BITS;
+      }
+      __syncthreads();                           // escan is reused by the next row
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int E = e_lds[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cm[i][k] = __ballot(need_hist[i] && ck[i][k] >= E);
+    }
+    if (lane == 0) {
+      // 64-token groups in token order: g = step * 8 + wave * 2 + (lo, hi)
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) gcnt[i * 16 + (k >> 1) * 8 + wave * 2 + (k & 1)] = __popcll(cm[i][k]);
+    }
   }
   __syncthreads();
   if (CAND) {
@@ -259,7 +321,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
                         const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st,
-                        bool cand) {
+                        bool cand, int force) {
   if (cand && !w) return hipErrorInvalidValue;
   int32_t *hist1 = w ? w->hist1 : nullptr;
   int32_t *cmax = w ? w->cmax : nullptr;
@@ -274,15 +336,15 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
     if (cand)                                                                                  \
       score_kernel<RR, true, true><<<grid, SC_THREADS, 0, st>>>(                               \
           qsk, S, seq_len, nullptr, hist1, nullptr, n_sub_max, s.Hkv, s.T_max, s.NB, s.window, \
-          s.pool, s.topk, w->est, w->cand, w->cnt);                                            \
+          s.pool, s.topk, w->hsamp, w->cand, w->cnt, force);                                   \
     else if (hist1)                                                                            \
       score_kernel<RR, true, false><<<grid, SC_THREADS, 0, st>>>(                              \
           qsk, S, seq_len, scores, hist1, cmax, n_sub_max, s.Hkv, s.T_max, s.NB, s.window,     \
-          s.pool, s.topk, nullptr, nullptr, nullptr);                                          \
+          s.pool, s.topk, nullptr, nullptr, nullptr, 0);                                       \
     else                                                                                       \
       score_kernel<RR, false, false><<<grid, SC_THREADS, 0, st>>>(                             \
           qsk, S, seq_len, scores, nullptr, nullptr, 0, s.Hkv, s.T_max, s.NB, s.window,        \
-          s.pool, s.topk, nullptr, nullptr, nullptr);                                          \
+          s.pool, s.topk, nullptr, nullptr, nullptr, 0);                                       \
     break;
     SKS_SCORE_CASE(1)
     SKS_SCORE_CASE(2)

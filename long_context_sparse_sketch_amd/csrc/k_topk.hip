@@ -32,13 +32,13 @@
 // Candidate mode (the decode step when its caller does not read the scores)
 // replaces the stored scores and the filter pass:
 //   sample: scores every 64th far entry (512 sampled rows per workgroup)
-//     into a per-segment histogram of the level-1 bins; then one small
-//     workgroup per segment takes as its estimate E the lowest key of the bin
-//     holding the rho-th largest sampled key, rho = 2 k' + 8 where k' is the
-//     expected number of sampled entries among the k largest.  E is a
-//     heuristic: only the time depends on it.
-//   the score pass keeps every far entry with key >= E in the candidate
-//     lists (see k_score.hip) and builds the level-1 histogram as usual.
+//     into a per-segment histogram of the level-1 bins (zero at rest).
+//   the score pass: every workgroup takes as the segment's estimate E the
+//     lowest key of the sample bin holding the rho-th largest sampled key,
+//     rho = 2 k' + 8 where k' is the expected number of sampled entries among
+//     the k largest, keeps every far entry with key >= E in the candidate
+//     lists (see k_score.hip) and builds the level-1 histogram as usual.  E
+//     is a heuristic: only the time depends on it.
 //   final: as above, with the threshold guess taken from the level-1
 //     histogram and a level-2 histogram of the bin-b1 candidates.  If at
 //     least k entries reach E, the k largest are all candidates and the
@@ -219,15 +219,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
 
 constexpr int TF_THREADS = 1024;
 
-constexpr int SAMPLE_STRIDE = 64;       // one far entry in 64 is sampled
 constexpr int SAMPLE_THREADS = 256;
 constexpr int SAMPLE_UNROLL = 8;        // sketch loads in flight per lane
 constexpr int SAMPLE_WG_ROWS = SAMPLE_THREADS / 4 * SAMPLE_UNROLL;   // 512 sampled rows
-constexpr int EST_THREADS = 256;
 
 // Sample pass: workgroup x of segment y scores sampled rows j * 64,
 // j in [512x, 512x + 512), and adds their level-1 bins to the segment's
-// sample histogram (zero at rest; est_kernel returns it to zero).
+// sample histogram (zero at rest; the final pass returns it to zero).
 __global__ __launch_bounds__(SAMPLE_THREADS) void topk_sample_kernel(
     const int8_t *__restrict__ qsk, const int8_t *__restrict__ S,
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ hsamp, int R, int Hkv, int T_max,
@@ -268,51 +266,6 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void topk_sample_kernel(
     if (lh[k]) atomicAdd(&gh[k], lh[k]);
 }
 
-// The segment's estimate E from its sample histogram, which returns to zero:
-// the lowest key of the bin holding the rho-th largest sampled key,
-// rho = 2 k' + 8 with k' the expected number of sampled entries among the k
-// largest.  force 1: E above every key; 2: E = 0.
-__global__ __launch_bounds__(EST_THREADS) void topk_est_kernel(
-    const int32_t *__restrict__ seq_len, int32_t *__restrict__ hsamp, int32_t *__restrict__ est,
-    int R, int Hkv, int T_max, int window, int pool, int topk, int force) {
-  __shared__ int sc[EST_THREADS / 64];
-  constexpr int PER = HIST1_BINS / EST_THREADS;   // 8 bins per thread, from the top down
-  const int seg = blockIdx.x;
-  const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
-  if (g.k_eff >= g.n_far || force) {            // uniform
-    if (threadIdx.x == 0) est[seg] = force == 1 ? (1 << 30) : 0;
-    return;
-  }
-  int32_t *gh = hsamp + (size_t)seg * HIST1_BINS;
-  const int top = HIST1_BINS - 1 - PER * (int)threadIdx.x;   // bins top, top - 1, ...
-  int v[PER];
-  int sum = 0;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    v[k] = max(gh[top - k], 0);
-    sum += v[k];
-  }
-#pragma unroll
-  for (int k = 0; k < PER; ++k) gh[top - k] = 0;
-  const int m = (g.n_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
-  const int kp = (int)(((long)g.k_eff * m + g.n_far - 1) / g.n_far);
-  const int rho = 2 * kp + 8;
-  int tot;
-  const int incl = block_incl_scan<EST_THREADS / 64, false>(sum, sc, tot);
-  int run = incl - sum;                          // sampled keys in higher bins
-  if (tot < rho) {
-    if (threadIdx.x == 0) est[seg] = 0;          // too few samples: every entry is a candidate
-  } else if (run < rho && incl >= rho) {
-    int bin = top - (PER - 1);
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      if (run < rho && run + v[k] >= rho) bin = top - k;
-      run += v[k];
-    }
-    est[seg] = bin << HIST2_BITS;
-  }
-}
-
 __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(FinalArgs a) {
   __shared__ FinalLds<TF_THREADS, TK_MAX_SUBS, true> lds;
   final_body<TF_THREADS, TK_MAX_SUBS, true>(a, blockIdx.x, lds);
@@ -330,8 +283,7 @@ size_t hist_region_bytes(const Shape &s) {
 size_t topk_scratch_bytes(const Shape &s) {
   const size_t nseg = (size_t)s.B * s.R * s.Hkv;
   const size_t n_sub = (size_t)ceil_div(s.NB, TK_SUB);
-  return align_up(nseg * n_sub * 4, 256) + align_up(nseg * n_sub * TK_SUB * sizeof(int2), 256) +
-         align_up(nseg * 4, 256);
+  return align_up(nseg * n_sub * 4, 256) + align_up(nseg * n_sub * TK_SUB * sizeof(int2), 256);
 }
 
 TopkWs topk_ws_carve(const Shape &s, void *ws) {
@@ -354,8 +306,6 @@ TopkWs topk_ws_carve(const Shape &s, void *ws) {
   w.cnt = reinterpret_cast<int32_t *>(p);
   p += align_up(nseg * n_sub * 4, 256);
   w.cand = reinterpret_cast<int2 *>(p);
-  p += align_up(nseg * n_sub * TK_SUB * sizeof(int2), 256);
-  w.est = reinterpret_cast<int32_t *>(p);
   w.nchunk = (int)n_sub;
   w.attn = base + hist_region_bytes(s) + topk_scratch_bytes(s);
   return w;
@@ -416,15 +366,13 @@ bool topk_cand_preferred(const Shape &s) {
 }
 
 hipError_t launch_topk_sample(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
-                              const Shape &s, const TopkWs &w, int force, hipStream_t st) {
+                              const Shape &s, const TopkWs &w, hipStream_t st) {
   const int nseg = s.B * s.R * s.Hkv;
   const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   const long max_m = (max_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
-  if (!force && max_m > 0)
+  if (max_m > 0)
     topk_sample_kernel<<<dim3(ceil_div(max_m, SAMPLE_WG_ROWS), nseg), SAMPLE_THREADS, 0, st>>>(
         qsk, S, seq_len, w.hsamp, s.R, s.Hkv, s.T_max, s.NB, s.window, s.pool, s.topk);
-  topk_est_kernel<<<nseg, EST_THREADS, 0, st>>>(seq_len, w.hsamp, w.est, s.R, s.Hkv, s.T_max,
-                                                s.window, s.pool, s.topk, force);
   return hipGetLastError();
 }
 
@@ -434,6 +382,7 @@ hipError_t launch_topk_cand(const int8_t *qsk, const int8_t *S, int32_t *scores,
   const int nseg = s.B * s.R * s.Hkv;
   FinalArgs a = final_args(scores, seq_len, s, idx, n_sel, w);
   a.cand_mode = 1;
+  a.hsamp = w.hsamp;
   a.qsk = qsk;
   a.S = S;
   a.rescore = scores;

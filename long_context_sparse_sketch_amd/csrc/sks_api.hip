@@ -264,11 +264,10 @@ int sks_score_candidates(const int8_t *qsk, const int8_t *S, const sks_kv *kv,
   const sks::TopkWs w = sks::topk_ws_carve(s, ws);
   const hipStream_t hs = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (!(flags & SKS_CAND_KEEP_ESTIMATE))
-    e = sks::launch_topk_sample(qsk, S, kv->seq_len, s, w,
-                                (flags & SKS_CAND_TEST_HIGH) ? 1 : (flags & SKS_CAND_TEST_ZERO) ? 2 : 0,
-                                hs);
-  if (e == hipSuccess) e = sks::launch_score(qsk, S, kv->seq_len, s, nullptr, &w, hs, true);
+  const int force = (flags & SKS_CAND_TEST_HIGH) ? 1 : (flags & SKS_CAND_TEST_ZERO) ? 2 : 0;
+  if (!(flags & SKS_CAND_KEEP_ESTIMATE) && !force)
+    e = sks::launch_topk_sample(qsk, S, kv->seq_len, s, w, hs);
+  if (e == hipSuccess) e = sks::launch_score(qsk, S, kv->seq_len, s, nullptr, &w, hs, true, force);
   return hip_status(e, "sks_score_candidates");
 }
 
@@ -387,7 +386,7 @@ int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *st, i
   const bool cand = (flags & SKS_STEP_NO_SCORES) && sks::topk_cand_preferred(s);
   if (!dense && cand) {
     if (e == hipSuccess)
-      e = sks::launch_topk_sample(st->qsk, st->S, kv->seq_len, s, w, 0, hs);
+      e = sks::launch_topk_sample(st->qsk, st->S, kv->seq_len, s, w, hs);
     if (e == hipSuccess)
       e = sks::launch_score(st->qsk, st->S, kv->seq_len, s, nullptr, &w, hs, true);
     if (e == hipSuccess)

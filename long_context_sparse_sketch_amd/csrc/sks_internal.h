@@ -25,6 +25,7 @@ constexpr int TK_CHUNK = 4096;           // tokens per top-k filter workgroup
 constexpr int TK_SUB = 1024;             // tokens per filter wave (one candidate sub-list)
 constexpr int TK_MAX_SUBS = 8192;        // sub-lists per segment the final pass can index
 constexpr int ATTN_MAX_G = 8;            // query heads per KV head supported
+constexpr int SAMPLE_STRIDE = 64;        // candidate mode samples one far entry in 64
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
@@ -241,11 +242,12 @@ size_t attn_scratch_bytes(const Shape &s, int G);
 hipError_t launch_fill(int32_t *p, size_t n, hipStream_t st);
 // With `w` (non-null) the score pass also builds the selection histogram;
 // with `cand` it stores no scores but the selection's candidates at or above
-// the sample pass's estimates (candidate mode).
+// the estimates it derives from the sample pass's histograms (candidate
+// mode; force 1: estimate above every key, 2: zero).
 struct TopkWs;
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
                         const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st,
-                        bool cand = false);
+                        bool cand = false, int force = 0);
 
 struct TopkWs {
   int32_t *hist1;     // [nseg][HIST1_BINS], zero at rest
@@ -257,7 +259,6 @@ struct TopkWs {
   char *attn;         // start of the attention partials (after the selection scratch)
   int32_t *cnt;       // [nseg][nchunk]
   int2 *cand;         // [nseg][nchunk * TK_SUB]
-  int32_t *est;       // [nseg]: candidate mode's per-segment key estimate
   int nchunk;         // sub-lists per segment
 };
 TopkWs topk_ws_carve(const Shape &s, void *ws);
@@ -266,12 +267,12 @@ hipError_t launch_topk_filter(const int32_t *scores, const int32_t *seq_len, con
 hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shape &s,
                        bool hist_ready, int32_t *idx, int32_t *n_sel, const TopkWs &w,
                        hipStream_t st);
-// Candidate mode: the sample pass (per-segment estimates; force 1: above
-// every key, 2: zero), and the final pass over the score pass's candidates,
-// which rescores a segment into `scores` when its estimate was too high.
+// Candidate mode: the sample pass (per-segment sample histograms), and the
+// final pass over the score pass's candidates, which rescores a segment into
+// `scores` when its estimate was too high.
 bool topk_cand_preferred(const Shape &s);
 hipError_t launch_topk_sample(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
-                              const Shape &s, const TopkWs &w, int force, hipStream_t st);
+                              const Shape &s, const TopkWs &w, hipStream_t st);
 hipError_t launch_topk_cand(const int8_t *qsk, const int8_t *S, int32_t *scores,
                             const int32_t *seq_len, const Shape &s, int32_t *idx,
                             int32_t *n_sel, const TopkWs &w, hipStream_t st);

@@ -119,6 +119,7 @@ struct FinalArgs {
   // scores.  A segment with fewer than k candidates is rescored from qsk and
   // S into `rescore` (the scores buffer) and selected from there.
   int cand_mode;
+  int32_t *hsamp;   // candidate mode: the sample histograms, returned to zero here
   const int8_t *qsk, *S;
   int32_t *rescore;
 };
@@ -213,6 +214,8 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
     for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh1[k] = 0;
   }
   if (threadIdx.x == 0 && n_sel) n_sel[seg] = g.k_eff;
+  if (cmode)
+    for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) a.hsamp[(size_t)seg * HIST1_BINS + k] = 0;
 
   // wave 0: the threshold guess T from the level-2 histogram (-1: none),
   // then that histogram returns to zero (its values are consumed)
@@ -528,6 +531,7 @@ inline FinalArgs final_args(const int32_t *scores, const int32_t *seq_len, const
   a.skip = 0;
   a.h1_ready = 0;
   a.cand_mode = 0;
+  a.hsamp = nullptr;
   a.qsk = nullptr;
   a.S = nullptr;
   a.rescore = nullptr;
