@@ -218,20 +218,23 @@ int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p
  * without storing the scores, so that the score pass streams only the
  * sketches.  sks_score_candidates
  *   1. (without SKS_CAND_KEEP_ESTIMATE) scores every 64th far entry of each
- *      (b, i, h) and stores in ws an estimate E of its k-th largest biased
- *      score (score + 2^20), set low enough that with high probability at
- *      least k entries reach it;
- *   2. scores every far token as sks_sketch_score does, accumulates the
- *      level-1 histogram into ws as sks_sketch_score(ws) does, and keeps in
- *      ws, instead of the scores, every far entry whose biased score is at
- *      least E (index and biased score, ascending).
+ *      (b, i, h) into a sample histogram in ws;
+ *   2. derives from that histogram an estimate E of each (b, i, h)'s k-th
+ *      largest biased score (score + 2^20), set low enough that with high
+ *      probability at least k entries reach it; scores every far token as
+ *      sks_sketch_score does, accumulates the level-1 histogram into ws as
+ *      sks_sketch_score(ws) does, and keeps in ws, instead of the scores,
+ *      every far entry whose biased score is at least E (index and biased
+ *      score, ascending).
  * sks_topk_select_candidates then selects as sks_topk_select, from those
  * entries.  Where fewer than k entries reached E, it recomputes that
  * segment's scores from qsk and S into `scores` ([B][R][Hkv][NB] int32,
  * scratch: its contents afterwards are unspecified) and selects from them.
  * E only decides the time taken, never the result.
  * Flags of sks_score_candidates:
- *   SKS_CAND_KEEP_ESTIMATE  reuse the estimates already in ws (step 2 only);
+ *   SKS_CAND_KEEP_ESTIMATE  reuse the sample histograms already in ws (step
+ *                           2 only; sks_topk_select_candidates returns them
+ *                           to zero, after which E is 0);
  *   SKS_CAND_TEST_HIGH      (tests) E above every score: every segment with
  *                           k_eff < n_far takes the recomputing path;
  *   SKS_CAND_TEST_ZERO      (tests) E = 0: every far entry is kept.
