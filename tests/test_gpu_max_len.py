@@ -9,7 +9,10 @@ key sketch, then sks_decode_step), against the oracle, for each head:
   the sketch bound, the query sketch likewise;
 * every far token's score (8,384,512 of them) bit-exact given the GPU's codes;
 * the selected indices bit-exact (the oracle's full sort of all scores);
-* the attention output within the output bound, over the oracle's rows.
+* the attention output within the output bound, over the oracle's rows;
+* the selection's candidate mode (131,008 sampled rows per head, 256 sample
+  workgroups each) picks the same indices, with the sampled estimate and
+  with every head recomputing its scores.
 
 The second head's K and V rows lie 2 GiB and more past the start of the
 cache, so every byte offset into it needs 64-bit arithmetic."""
@@ -97,13 +100,24 @@ def test_largest_cache():
         assert_attn_close(layer.out[0, 0, hs].cpu().numpy(), out, f"{cfg.name} head {h}")
         lse_close(layer.lse[0, 0, hs].cpu().numpy(), lse, f"{cfg.name} head {h}")
 
+    # candidate mode on the same codes: the stored-score selection's indices
+    want = layer.idx.clone()
+    for flags in (0, sks.CAND_TEST_HIGH):
+        flush(f"[max] candidate mode, flags {flags}")
+        layer.score_candidates(flags=flags)
+        layer.idx.fill_(-7)
+        layer.select_candidates()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.idx, want), flags
+
 
 def test_most_segments():
     """8,191 sequences x 8 KV heads = 65,528 (sequence, KV head) segments, the
     most a grid dimension holds (65,535), on short rows: sampled segments
     (the first, the last and some between) against the oracle: sketches within
     the bound, scores and indices bit-exact given the GPU's codes, outputs
-    within the output bound."""
+    within the output bound; the candidate mode's selection equal to the
+    stored-score one on every segment."""
     B, HKV_, G_ = 8191, 8, 1
     cfg = C.Config("max_segments", 92, B=B, R=1, Hq=HKV_ * G_, Hkv=HKV_, L=64, window=16,
                    topk=8, pool=1, kv_dtype=C.KV_BF16, needle_kind="random", needle_count=2,
@@ -140,3 +154,11 @@ def test_most_segments():
         hs = slice(h * G_, (h + 1) * G_)
         assert_attn_close(layer.out[b, 0, hs].cpu().numpy(), out, f"{(b, h)}")
         lse_close(layer.lse[b, 0, hs].cpu().numpy(), lse, f"{(b, h)}")
+    # candidate mode over all 65,528 segments: the stored-score selection
+    want = layer.idx.clone()
+    for flags in (0, sks.CAND_TEST_HIGH, sks.CAND_TEST_ZERO):
+        layer.score_candidates(flags=flags)
+        layer.idx.fill_(-7)
+        layer.select_candidates()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.idx, want), flags
