@@ -56,3 +56,47 @@ def test_streams_and_graph_replays_match_eager(cfg, parts, streams):
     for a, b in zip(got, (g.layer.out, g.layer.lse, g.layer.idx)):
         assert torch.equal(a, b)
     g.seq_len.add_(5)
+
+
+@pytest.mark.parametrize("cfg", [C.small(C.C3), C.small(C.C4), C.with_kv(C.small(C.C5), C.KV_I4)],
+                         ids=lambda c: c.name)
+def test_candidate_selection_graph_replays(cfg):
+    """The candidate mode's passes (sample, score, final) captured in a graph:
+    every replay gives the stored-score selection's indices, with eager work
+    between replays (its histograms return to zero each time), and the
+    captured passes follow device-side lengths."""
+    flush(f"[graph candidates] {cfg.name}")
+    case = make_case(cfg)
+    g = GpuCase(case)
+    lay = g.layer
+    lay.build_sketch(0, g.T)
+    lay.step(g.q)
+    torch.cuda.synchronize()
+    want = lay.idx.clone()
+
+    def sel():
+        lay.score_candidates()
+        lay.select_candidates()
+
+    sel()                                                    # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sel()
+    for rep in range(3):
+        lay.idx.fill_(-5)
+        x = torch.randn(1000, device="cuda").sum()          # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lay.idx, want), rep
+        del x
+    g.seq_len.sub_(5)
+    graph.replay()
+    torch.cuda.synchronize()
+    got = lay.idx.clone()
+    lay.score()
+    lay.select()
+    torch.cuda.synchronize()
+    assert torch.equal(got, lay.idx)
+    g.seq_len.add_(5)
