@@ -246,23 +246,32 @@ def cache_rows(K, V, Ks, Vs, b: int, h: int, kv_dtype: int, T: int | None = None
 
 def decode_head(qrows: np.ndarray, Kf: np.ndarray, Vf: np.ndarray, basis: np.ndarray,
                 key_scale: float, L0: int, window: int, topk: int, r: int,
-                sm_scale: float):
+                sm_scale: float, codes=None):
     """Full step for one (sequence, KV head), every query row.
 
     qrows: [R][g][128] float64 query vectors of this KV head's group.
     Kf, Vf: [T][128] float64 cache rows (T >= L0 + R - 1).
+    codes: optional (key codes [T / r][64], [query code [64] per row]) used in
+    place of the sketches computed here (the scores, selection and attention
+    are then those of the given codes; qscale is reported as nan).
     Returns a dict of per-row lists plus the key sketch of the cache.
     """
     R = qrows.shape[0]
     T = Kf.shape[0]
     Kp, Vp = pool_mean(Kf, r), pool_mean(Vf, r)       # pooled rows (r == 1: the rows)
-    _, kcodes = key_sketch(Kp, basis, key_scale)      # one code row per block/token
+    if codes is None:
+        _, kcodes = key_sketch(Kp, basis, key_scale)  # one code row per block/token
+    else:
+        kcodes = np.asarray(codes[0], np.int8)
     res = {"kcodes": kcodes, "Kp": Kp, "Vp": Vp, "qcode": [], "qscale": [], "scores": [],
            "idx": [], "n_sel": [], "out": [], "lse": [], "n_far": [], "win_start": []}
     for i in range(R):
         Li = max(0, min(L0 + i, T))
         n_far, ws = row_geometry(Li, window, r)
-        qc, qs, _ = query_sketch(qrows[i], basis)
+        if codes is None:
+            qc, qs, _ = query_sketch(qrows[i], basis)
+        else:
+            qc, qs = np.asarray(codes[1][i], np.int8), float("nan")
         sc = scores(qc, kcodes[:n_far])
         sel = select_topk(sc, topk)
         Kset = np.concatenate([Kp[sel], Kf[ws:Li]], axis=0)
@@ -280,8 +289,20 @@ def decode_head(qrows: np.ndarray, Kf: np.ndarray, Vf: np.ndarray, basis: np.nda
     return res
 
 
+def head_basis(basis: np.ndarray, h: int) -> np.ndarray:
+    """The basis of KV head h: the one shared basis ([64][128]), or row h of a
+    per-head basis ([Hkv][64][128])."""
+    basis = np.asarray(basis, np.float64)
+    return basis if basis.ndim == 2 else basis[h]
+
+
+def head_key_scale(key_scale, h: int) -> float:
+    """The frozen key-sketch scale of KV head h (one scale per KV head)."""
+    return float(np.asarray(key_scale, np.float64)[h])
+
+
 def decode_step(q, K, V, Ks, Vs, seq_len, basis, key_scale, window: int, topk: int,
-                r: int, kv_dtype: int, heads=None, sm_scale: float | None = None):
+                r: int, kv_dtype: int, heads=None, sm_scale: float | None = None, codes=None):
     """Oracle decode step over a batch.
 
     q: [B][R][Hq][128] bf16 bits; K, V: [B][Hkv][T][128] bf16 bits or int8, or
@@ -289,6 +310,9 @@ def decode_step(q, K, V, Ks, Vs, seq_len, basis, key_scale, window: int, topk: i
     scales Ks, Vs [B][Hkv][T]; seq_len [B] (row-0 lengths); basis
     [64][128] (shared) or [Hkv][64][128]; key_scale [Hkv].
     heads: optional iterable of (b, h) pairs to compute (default: all).
+    codes: optional (key codes [B][Hkv][T / r][64], query codes [B][R][Hkv][64])
+    int8 arrays used instead of the sketches this step would compute (for
+    checking a selection made from another implementation's sketches).
     Returns {(b, h): decode_head result}.
     """
     B, R, Hq, D = q.shape
@@ -296,14 +320,14 @@ def decode_step(q, K, V, Ks, Vs, seq_len, basis, key_scale, window: int, topk: i
     g = Hq // Hkv
     sm = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
     qf = bf16_to_f64(q)
-    basis = np.asarray(basis, np.float64)
     pairs = [(b, h) for b in range(B) for h in range(Hkv)] if heads is None else list(heads)
     out = {}
     for b, h in pairs:
         Kf, Vf = cache_rows(K, V, Ks, Vs, b, h, kv_dtype)
-        P = basis if basis.ndim == 2 else basis[h]
-        out[(b, h)] = decode_head(qf[b, :, h * g:(h + 1) * g], Kf, Vf, P,
-                                  float(key_scale[h]), int(seq_len[b]), window, topk, r, sm)
+        given = None if codes is None else (codes[0][b, h], [codes[1][b, i, h] for i in range(R)])
+        out[(b, h)] = decode_head(qf[b, :, h * g:(h + 1) * g], Kf, Vf, head_basis(basis, h),
+                                  head_key_scale(key_scale, h), int(seq_len[b]), window, topk,
+                                  r, sm, codes=given)
     return out
 
 

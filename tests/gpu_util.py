@@ -61,11 +61,14 @@ class GpuCase:
         torch.cuda.synchronize()
         return out, lse
 
-    def oracle(self, heads=None):
+    def oracle(self, heads=None, codes=None):
+        """The oracle's step on this case; `codes` = (key codes [B][Hkv][NB][64],
+        query codes [B][R][Hkv][64]) makes it score, select and attend from
+        those int8 sketches (e.g. the GPU's own) instead of its own."""
         c, cfg = self.case, self.cfg
         return orc.decode_step(c.q, c.K, c.V, c.K_scale, c.V_scale, self.seq_len_np, c.basis,
                                c.key_scale, self.window, self.topk, self.pool,
-                               cfg.kv_dtype, heads=heads)
+                               cfg.kv_dtype, heads=heads, codes=codes)
 
 
 def sketch_ok(code_gpu: np.ndarray, y: np.ndarray, s: float):
@@ -129,7 +132,7 @@ __all__ = ["GpuCase", "sketch_ok", "oracle_key_projection", "assert_attn_close",
 
 
 def run_arrays(q, K, V, seq_len, basis, key_scale, window, topk, pool=1, Ks=None, Vs=None,
-               ref=None):
+               ref=None, basis_per_head=False):
     """Run one full GPU step (bulk sketch + step) on raw host arrays.
 
     q: [B][R][Hq][128] bf16 bits; K, V: [B][Hkv][T][128] bf16 bits or int8.
@@ -151,7 +154,8 @@ def run_arrays(q, K, V, seq_len, basis, key_scale, window, topk, pool=1, Ks=None
     layer = SparseDecodeLayer(B, R, Hq, Hkv, T, window, topk, pool,
                               sks.KV_I8 if i8 else sks.KV_BF16)
     layer.bind(cache, torch.from_numpy(np.ascontiguousarray(basis, np.float32)).cuda(),
-               torch.from_numpy(np.ascontiguousarray(key_scale, np.float32)).cuda())
+               torch.from_numpy(np.ascontiguousarray(key_scale, np.float32)).cuda(),
+               basis_per_head=basis_per_head)
     layer.build_sketch(0, T)
     qd = to_device(q, bf16=True)
     if ref is None:

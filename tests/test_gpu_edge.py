@@ -11,7 +11,8 @@ from long_context_sparse_sketch_amd import configs as C
 from long_context_sparse_sketch_amd.synth import make_case, random_arrays, random_scores
 from oracle import sks_oracle as orc
 from tests.gpu_util import assert_attn_close, flush, lse_close, run_arrays
-from tests.golden_util import build_inputs, load_examples, parse_value
+from tests.golden_util import (build_inputs, build_multi_head_inputs, load_examples,
+                               load_multi_head_examples, parse_value)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +34,31 @@ def test_golden_worked_examples_on_gpu(ex):
                 want[int(d)] = parse_value(v)
             np.testing.assert_allclose(r["out"][0, i, 0], want, rtol=1e-6, atol=1e-6)
             assert r["lse"][0, i, 0] == pytest.approx(parse_value(case["lse"][i]), rel=1e-6)
+
+
+@pytest.mark.parametrize("ex", load_multi_head_examples(), ids=lambda e: e["name"])
+def test_golden_per_head_examples_on_gpu(ex):
+    """One basis and one key scale per KV head (3/8 for head 1, not a power of
+    two): codes, scores, indices and outputs as worked out by hand."""
+    flush(f"[edge] golden {ex['name']}")
+    inp = build_multi_head_inputs(ex)
+    for case in ex["cases"]:
+        r = run_arrays(inp["q"], inp["K"], inp["V"], inp["seq_len"], inp["basis"],
+                       inp["key_scale"], inp["window"], case["topk"], inp["pool"],
+                       basis_per_head=True)
+        for h in range(ex["Hkv"]):
+            assert r["S"][0, h, :, 0].tolist() == ex["key_codes_dim0"][h], h
+            assert not r["S"][0, h, :, 1:].any()
+            assert r["qsk"][0, 0, h, 0] == ex["qcode_dim0"][h] and not r["qsk"][0, 0, h, 1:].any()
+            n = len(case["scores"][h])
+            assert r["scores"][0, 0, h, :n].tolist() == case["scores"][h], h
+            want_idx = case["idx"][h] + [-1] * (case["topk"] - len(case["idx"][h]))
+            assert r["idx"][0, 0, h].tolist() == want_idx, h
+            want = np.zeros(128)
+            for d, v in case["out"][h].items():
+                want[int(d)] = parse_value(v)
+            np.testing.assert_allclose(r["out"][0, 0, h], want, rtol=1e-6, atol=1e-6)
+            assert r["lse"][0, 0, h] == pytest.approx(parse_value(case["lse"][h]), rel=1e-6)
 
 
 def oracle_of(q, K, V, Ks, Vs, seq_len, basis, ks, window, topk, pool):

@@ -35,7 +35,8 @@ def sample_pairs(cfg):
     return sorted({(0, 0), (B - 1, H - 1), (B // 2, H // 2)})
 
 
-@pytest.mark.parametrize("cfg", [C.C2, C.C3, C.C4, C.C5, C.with_kv(C.C3, C.KV_I4)],
+@pytest.mark.parametrize("cfg", [C.C2, C.C3, C.C4, C.C5, C.with_kv(C.C3, C.KV_I4),
+                                 C.with_kv(C.C3, C.KV_I8)],
                          ids=lambda c: c.name)
 def test_full_size_sampled_parity(cfg):
     flush(f"[full] {cfg.name}: generating {cfg.B} x {cfg.L}")
@@ -97,12 +98,26 @@ def test_full_size_sampled_parity(cfg):
             for i in range(cfg.R):
                 assert np.array_equal(idx[b, i, h], r["idx"][i]), (flags, b, i, h)
 
-    # 3. end to end (GPU sketches, graph replay): needle recall on every segment
+    # 3. end to end (GPU sketches, graph replay): on the sampled pairs, the
+    #    oracle's scores, selection and attention on the GPU's own codes give
+    #    the same indices and outputs within tolerance; needle recall on every
+    #    segment
     g.layer.build_sketch(0, g.T)
     runner.replay()
     torch.cuda.synchronize()
     idx = g.layer.idx.cpu().numpy()
     n_sel = g.layer.n_sel.cpu().numpy()
+    out = g.layer.out.cpu().numpy()
+    lse = g.layer.lse.cpu().numpy()
+    Sg, qg = g.layer.S.cpu().numpy(), g.layer.qsk.cpu().numpy()
+    ref_own = g.oracle(heads=pairs, codes=(Sg, qg))
+    for (b, h), r in ref_own.items():
+        for i in range(cfg.R):
+            assert np.array_equal(idx[b, i, h], r["idx"][i]), ("own codes", b, i, h)
+            assert n_sel[b, i, h] == r["n_sel"][i]
+            sl = slice(h * gq, (h + 1) * gq)
+            assert_attn_close(out[b, i, sl], r["out"][i], f"{cfg.name} own codes {(b, i, h)}")
+            lse_close(lse[b, i, sl], r["lse"][i], f"{cfg.name} own codes {(b, i, h)}")
     for (b, h), pos in case.needles.items():
         Li = int(case.seq_len[b])
         n_far, ws = orc.row_geometry(Li, cfg.window, cfg.pool)

@@ -7,7 +7,7 @@ import pytest
 
 from oracle import sks_oracle as orc
 from tests import test_oracle_pins as pins
-from tests.golden_util import load_examples
+from tests.golden_util import load_examples, load_multi_head_examples
 
 EXAMPLES = load_examples()
 
@@ -165,3 +165,20 @@ def test_caught_refit_scale_off_by_one(monkeypatch):
                   lambda keys, basis: float(np.abs(real(keys, basis)).max()) / 128,
                   pins.test_refit_key_scale_closed_form)
 
+
+
+def per_head_goldens():
+    for ex in load_multi_head_examples():
+        pins.test_golden_per_head_examples(ex)
+
+
+def test_caught_shared_basis_for_every_head(monkeypatch):
+    def bad(basis, h):
+        basis = np.asarray(basis, np.float64)
+        return basis if basis.ndim == 2 else basis[0]
+    expect_caught(monkeypatch, "head_basis", bad, per_head_goldens)
+
+
+def test_caught_first_head_key_scale_for_every_head(monkeypatch):
+    expect_caught(monkeypatch, "head_key_scale",
+                  lambda ks, h: float(np.asarray(ks, np.float64)[0]), per_head_goldens)

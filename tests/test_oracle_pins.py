@@ -16,7 +16,8 @@ import torch
 from oracle import sks_oracle as orc
 from long_context_sparse_sketch_amd import configs as C
 from long_context_sparse_sketch_amd.synth import f32_to_bf16_bits, make_case
-from tests.golden_util import build_inputs, load_examples, parse_value
+from tests.golden_util import (build_inputs, build_multi_head_inputs, load_examples,
+                               load_multi_head_examples, parse_value)
 
 SM = 1.0 / math.sqrt(128.0)
 
@@ -233,6 +234,63 @@ def test_golden_worked_examples(ex):
                 want[int(d)] = parse_value(v)
             np.testing.assert_allclose(out, want, rtol=1e-13, atol=1e-13)
             assert res["lse"][i][0] == pytest.approx(parse_value(case["lse"][i]), rel=1e-13)
+
+
+@pytest.mark.parametrize("ex", load_multi_head_examples(), ids=lambda e: e["name"])
+def test_golden_per_head_examples(ex):
+    """One basis and one key scale per KV head (one of them not a power of
+    two): every code, score, index, output and lse of each head as worked out
+    by hand in the fixture."""
+    inp = build_multi_head_inputs(ex)
+    for case in ex["cases"]:
+        res = orc.decode_step(inp["q"], inp["K"], inp["V"], None, None, inp["seq_len"],
+                              inp["basis"], inp["key_scale"], inp["window"], case["topk"],
+                              inp["pool"], orc.KV_BF16)
+        for h in range(ex["Hkv"]):
+            r = res[(0, h)]
+            assert r["kcodes"][:, 0].tolist() == ex["key_codes_dim0"][h], h
+            assert not r["kcodes"][:, 1:].any()
+            assert r["qcode"][0][0] == ex["qcode_dim0"][h] and not r["qcode"][0][1:].any()
+            assert r["scores"][0].tolist() == case["scores"][h], h
+            want_idx = case["idx"][h] + [-1] * (case["topk"] - len(case["idx"][h]))
+            assert r["idx"][0].tolist() == want_idx, h
+            want = np.zeros(128)
+            for d, v in case["out"][h].items():
+                want[int(d)] = parse_value(v)
+            np.testing.assert_allclose(r["out"][0][0], want, rtol=1e-13, atol=1e-13)
+            assert r["lse"][0][0] == pytest.approx(parse_value(case["lse"][h]), rel=1e-13)
+
+
+def test_given_codes_reproduce_the_step_and_drive_the_selection():
+    """decode_step fed with codes: its own codes give its own results bit for
+    bit; codes made by hand select exactly what those codes rank highest."""
+    inp = random_inputs(900, 6, 2, 880, seed=17)
+    base = orc.decode_step(inp["q"], inp["K"], inp["V"], None, None, inp["seq_len"],
+                           inp["basis"], inp["key_scale"], 200, 50, 1, orc.KV_BF16)
+    kc = np.stack([base[(0, h)]["kcodes"] for h in range(2)])[None]
+    qc = np.stack([base[(0, h)]["qcode"][0] for h in range(2)])[None, None]
+    again = orc.decode_step(inp["q"], inp["K"], inp["V"], None, None, inp["seq_len"],
+                            inp["basis"], inp["key_scale"], 200, 50, 1, orc.KV_BF16,
+                            codes=(kc, qc))
+    for key in base:
+        for f in ("kcodes", "scores", "idx", "out", "lse"):
+            for x, y in zip(np.atleast_1d(base[key][f]), np.atleast_1d(again[key][f])):
+                assert np.array_equal(x, y), (key, f)
+    # hand-made codes: query e_0 * 1, key t has code t % 97 in dim 0 -> the 50
+    # far tokens with the largest t % 97 (ties: lower t) are selected
+    kc2 = np.zeros_like(kc)
+    kc2[..., 0] = (np.arange(kc.shape[2]) % 97)[None, None, :]
+    qc2 = np.zeros_like(qc)
+    qc2[..., 0] = 1
+    got = orc.decode_step(inp["q"], inp["K"], inp["V"], None, None, inp["seq_len"],
+                          inp["basis"], inp["key_scale"], 200, 50, 1, orc.KV_BF16,
+                          codes=(kc2, qc2))
+    n_far = 880 - 200
+    t = np.arange(n_far)
+    order = sorted(t, key=lambda x: (-(x % 97), x))[:50]
+    for h in range(2):
+        assert got[(0, h)]["idx"][0].tolist() == sorted(order)
+        assert got[(0, h)]["scores"][0].tolist() == (t % 97).tolist()
 
 
 # ----------------------------------------------------------------- attention
