@@ -336,6 +336,31 @@ typedef struct sks_step {
 int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *step, int32_t flags,
                     void *ws, size_t ws_bytes, sks_stream_t stream);
 
+/* sks_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static array of
+ * SKS_STATIC_WORKSPACE_BYTES that the library holds on every GPU it runs on
+ * until the process ends; the call itself allocates and frees nothing.
+ * Same arguments, flags, validation and results (bit for bit) as
+ * sks_decode_step; the caller still provides every input and output.
+ * - A shape whose workspace (sks_workspace_bytes) exceeds the static array
+ *   returns SKS_ERR_WORKSPACE before any launch (every workload shape of this
+ *   library fits: 8 x 250,000 tokens with 24/4 heads needs about 67 MB).
+ * - The array of a GPU is shared by every call on that GPU (the GPU of
+ *   `stream`; the current device for the null stream) and keeps the last
+ *   call's contents.  Calls that may overlap on one GPU -- on streams not
+ *   ordered with each other, or from several host threads -- race on it and
+ *   must not be issued.
+ * - The first call on a GPU looks up that GPU's copy of the array
+ *   (hipGetSymbolAddress; issue it once outside a graph capture if the
+ *   capture must contain only the step).  The first call and every call whose
+ *   shape differs from the previous call's on that GPU also clear the
+ *   selection histograms with a fill kernel (a dirty region would cost time,
+ *   never correctness). */
+#define SKS_STATIC_WORKSPACE_BYTES (96u << 20)
+int sks_decode_step_static(const sks_kv *kv, const sks_params *p, const sks_step *step,
+                           int32_t flags, sks_stream_t stream);
+
 /* ---------------------------------------------------------------- basis refit
  * "What it took" of "8 agents x 250K context ...": a frozen sketch basis in
  * one file plus the script that refits it.  A refit reads the captured keys

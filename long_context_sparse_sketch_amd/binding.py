@@ -38,7 +38,8 @@ CAND_TEST_ZERO = 4
 
 EXPORTS = ("sks_last_error", "sks_runtime_version", "sks_workspace_bytes", "sks_workspace_init",
            "sks_sketch_build", "sks_sketch_build_query", "sks_sketch_score", "sks_topk_select",
-           "sks_score_candidates", "sks_topk_select_candidates", "sks_gather_pack", "sks_sparse_decode_attn", "sks_decode_step",
+           "sks_score_candidates", "sks_topk_select_candidates", "sks_gather_pack",
+           "sks_sparse_decode_attn", "sks_decode_step", "sks_decode_step_static",
            "sks_refit_workspace_bytes", "sks_refit_gram", "sks_refit_basis",
            "sks_refit_key_scale")
 
@@ -115,6 +116,8 @@ def lib():
                                              vp, vp, sz, vp]
         L.sks_decode_step.restype = ctypes.c_int
         L.sks_decode_step.argtypes = [kvp, pp, ctypes.POINTER(StepDesc), i32, vp, sz, vp]
+        L.sks_decode_step_static.restype = ctypes.c_int
+        L.sks_decode_step_static.argtypes = [kvp, pp, ctypes.POINTER(StepDesc), i32, vp]
         L.sks_refit_workspace_bytes.restype = sz
         L.sks_refit_workspace_bytes.argtypes = [kvp, i32, i32]
         L.sks_refit_gram.restype = ctypes.c_int
@@ -445,6 +448,34 @@ def decode_step(cache: Cache, p: Params, q, basis, key_scale, S, qsk, scores, id
                                  (STEP_APPEND if append else 0) | (STEP_DENSE if dense else 0)
                                  | (0 if keep_scores else STEP_NO_SCORES),
                                  wa, _nbytes(ws), _stream(stream)))
+
+
+STATIC_WORKSPACE_BYTES = 96 << 20      # SKS_STATIC_WORKSPACE_BYTES of sks.h
+
+
+def decode_step_static(cache: Cache, p: Params, q, basis, key_scale, S, qsk, scores, idx, out,
+                       qscale=None, n_sel=None, lse=None, Kp=None, Vp=None, sm_scale=None,
+                       basis_per_head=False, append=True, dense=False, keep_scores=True,
+                       stream=None):
+    """decode_step with the library's static workspace (sks_decode_step_static):
+    no workspace argument, nothing allocated by the call."""
+    d = _Dims(cache, p)
+    qt, Hq = d.q(q)
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else sm_scale
+    (qa, ba, ka, sa, kpa, vpa, qsa, qca, ca, ia, na, oa, la) = _ptrs(
+        qt, d.basis(basis, basis_per_head), d.key_scale(key_scale), d.S(S),
+        d.pooled(Kp, "Kp"), d.pooled(Vp, "Vp"), _T(qsk, "qsk", d.seg(RANK)),
+        _T(qscale, "qscale", d.seg(4), optional=True), d.scores(scores), d.idx(idx),
+        _T(n_sel, "n_sel", d.seg(4), optional=True),
+        _T(out, "out", d.B * d.R * Hq * HEAD_DIM * 4),
+        _T(lse, "lse", d.B * d.R * Hq * 4, optional=True), stream=stream, cache=cache)
+    st = StepDesc(qa, Hq, ba, int(basis_per_head), ka, sa, kpa, vpa, sm, qsa, qca, ca, ia, na,
+                  oa, la)
+    _check(lib().sks_decode_step_static(cache.ref, ctypes.byref(p), ctypes.byref(st),
+                                        (STEP_APPEND if append else 0)
+                                        | (STEP_DENSE if dense else 0)
+                                        | (0 if keep_scores else STEP_NO_SCORES),
+                                        _stream(stream)))
 
 
 def refit_workspace_bytes(cache: Cache, t_begin: int, t_end: int) -> int:

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "refit.h"
 #include "sks_internal.h"
@@ -134,6 +135,122 @@ int check_ws(const void *ws, size_t given, size_t need) {
     return fail(SKS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                 ws ? given : (size_t)0);
   if (!aligned(ws, 256)) return fail(SKS_ERR_ARG, "ws must be 256-byte aligned");
+  return SKS_OK;
+}
+
+// Validation of sks_decode_step's arguments (all but the workspace).
+int check_step(const sks_kv *kv, const sks_params *p, const sks_step *st, int32_t flags,
+               sks::Shape &s) {
+  TRY(check_shape(kv, p, s));
+  TRY(check_cache(kv, true));
+  REQUIRE(st != nullptr, "step must not be NULL");
+  REQUIRE((flags & ~(SKS_STEP_APPEND | SKS_STEP_DENSE | SKS_STEP_NO_SCORES)) == 0,
+          "unknown flags 0x%x", flags);
+  TRY(check_heads(st->Hq, kv->Hkv));
+  REQUIRE(st->basis_per_head == 0 || st->basis_per_head == 1, "basis_per_head must be 0 or 1");
+  REQUIRE_PTR(st->q, 16);
+  REQUIRE_PTR(st->basis, 4);
+  REQUIRE_PTR(st->key_scale, 4);
+  REQUIRE_PTR(st->S, 16);
+  REQUIRE_PTR(st->qsk, 16);
+  REQUIRE_PTR(st->scores, 4);
+  REQUIRE_PTR(st->idx, 4);
+  REQUIRE_PTR(st->out, 16);
+  if (st->qscale) REQUIRE(aligned(st->qscale, 4), "qscale must be 4-byte aligned");
+  if (st->n_sel) REQUIRE(aligned(st->n_sel, 4), "n_sel must be 4-byte aligned");
+  if (st->lse) REQUIRE(aligned(st->lse, 4), "lse must be 4-byte aligned");
+  if (s.pool > 1) {
+    REQUIRE_PTR(st->Kp, 16);
+    REQUIRE_PTR(st->Vp, 16);
+  } else {
+    REQUIRE(st->Kp == nullptr && st->Vp == nullptr, "Kp and Vp must be NULL when pool == 1");
+  }
+  REQUIRE(st->sm_scale > 0.f && st->sm_scale < 1e30f, "sm_scale must be positive and finite");
+  if (sks::ceil_div(s.NB, sks::TK_SUB) > sks::TK_MAX_SUBS)
+    return fail(SKS_ERR_UNSUPPORTED, "T_max / pool above %d is not supported by the selection",
+                sks::TK_MAX_SUBS * sks::TK_SUB);
+  return SKS_OK;
+}
+
+// The launches of one decode step on a carved workspace.
+hipError_t enqueue_step(const sks_kv &kv, const sks::Shape &s, const sks_step &st, int32_t flags,
+                        const sks::TopkWs &w, hipStream_t hs) {
+  hipError_t e;
+  if (flags & SKS_STEP_APPEND)
+    e = sks::launch_step_prologue(st.q, st.Hq, kv, s, st.basis, st.basis_per_head, st.key_scale,
+                                  st.qsk, st.qscale, st.S, st.Kp, st.Vp, hs);
+  else
+    e = sks::launch_sketch_query(st.q, s.B, s.R, st.Hq, s.Hkv, st.basis, st.basis_per_head,
+                                 st.qsk, st.qscale, hs);
+  const bool dense = (flags & SKS_STEP_DENSE) != 0;
+  const bool cand = (flags & SKS_STEP_NO_SCORES) && sks::topk_cand_preferred(s);
+  if (!dense && cand) {
+    if (e == hipSuccess) e = sks::launch_topk_sample(st.qsk, st.S, kv.seq_len, s, w, hs);
+    if (e == hipSuccess) e = sks::launch_score(st.qsk, st.S, kv.seq_len, s, nullptr, &w, hs, true);
+    if (e == hipSuccess)
+      e = sks::launch_topk_cand(st.qsk, st.S, st.scores, kv.seq_len, s, st.idx, st.n_sel, w, hs);
+  } else if (!dense) {
+    if (e == hipSuccess) e = sks::launch_score(st.qsk, st.S, kv.seq_len, s, st.scores, &w, hs);
+    if (e == hipSuccess)
+      e = sks::launch_topk(st.scores, kv.seq_len, s, true, st.idx, st.n_sel, w, hs);
+  }
+  if (e == hipSuccess)
+    e = sks::launch_attn(st.q, st.Hq, kv, s, st.idx, st.Kp, st.Vp, st.sm_scale, st.out, st.lse,
+                         w, hs, dense);
+  return e;
+}
+
+// ---------------------------------------------------------------- static workspace
+// The workspace of sks_decode_step_static: one array per GPU, alive until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address of each
+// GPU's copy comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[SKS_STATIC_WORKSPACE_BYTES];
+
+constexpr int STATIC_MAX_DEVICES = 64;
+std::mutex g_static_mu;
+void *g_static_ptr[STATIC_MAX_DEVICES];
+bool g_static_used[STATIC_MAX_DEVICES];
+sks::Shape g_static_last[STATIC_MAX_DEVICES];   // shape of the device's previous call
+
+bool same_layout(const sks::Shape &a, const sks::Shape &b) {
+  return a.B == b.B && a.R == b.R && a.Hkv == b.Hkv && a.T_max == b.T_max && a.NB == b.NB &&
+         a.window == b.window && a.topk == b.topk && a.pool == b.pool && a.dtype == b.dtype;
+}
+
+// The static workspace of the device that runs `stream` (the current device
+// for the null stream); `clear` is set when its selection histograms must be
+// zeroed first (the device's first call, or a change of shape).
+int static_workspace(hipStream_t stream, const sks::Shape &s, void *&ws, bool &clear) {
+  int dev = -1;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess)
+      return fail(SKS_ERR_HIP, "hipStreamGetDevice failed for the given stream");
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return fail(SKS_ERR_HIP, "hipGetDevice failed");
+  }
+  if (dev < 0 || dev >= STATIC_MAX_DEVICES)
+    return fail(SKS_ERR_UNSUPPORTED, "device %d: the static workspace serves devices 0..%d", dev,
+                STATIC_MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(SKS_ERR_HIP, "hipGetDevice failed");
+    if (cur != dev && hipSetDevice(dev) != hipSuccess)
+      return fail(SKS_ERR_HIP, "hipSetDevice(%d) failed", dev);
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr)
+      return fail(SKS_ERR_HIP, "hipGetSymbolAddress of the static workspace on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_static_ptr[dev] = ptr;
+  }
+  ws = g_static_ptr[dev];
+  clear = !g_static_used[dev] || !same_layout(g_static_last[dev], s);
+  g_static_used[dev] = true;
+  g_static_last[dev] = s;
   return SKS_OK;
 }
 
@@ -344,63 +461,33 @@ int sks_sparse_decode_attn(const uint16_t *q, int32_t Hq, const sks_kv *kv, cons
 int sks_decode_step(const sks_kv *kv, const sks_params *p, const sks_step *st, int32_t flags,
                     void *ws, size_t ws_bytes_given, sks_stream_t stream) {
   sks::Shape s;
-  TRY(check_shape(kv, p, s));
-  TRY(check_cache(kv, true));
-  REQUIRE(st != nullptr, "step must not be NULL");
-  REQUIRE((flags & ~(SKS_STEP_APPEND | SKS_STEP_DENSE | SKS_STEP_NO_SCORES)) == 0,
-          "unknown flags 0x%x", flags);
-  TRY(check_heads(st->Hq, kv->Hkv));
-  REQUIRE(st->basis_per_head == 0 || st->basis_per_head == 1, "basis_per_head must be 0 or 1");
-  REQUIRE_PTR(st->q, 16);
-  REQUIRE_PTR(st->basis, 4);
-  REQUIRE_PTR(st->key_scale, 4);
-  REQUIRE_PTR(st->S, 16);
-  REQUIRE_PTR(st->qsk, 16);
-  REQUIRE_PTR(st->scores, 4);
-  REQUIRE_PTR(st->idx, 4);
-  REQUIRE_PTR(st->out, 16);
-  if (st->qscale) REQUIRE(aligned(st->qscale, 4), "qscale must be 4-byte aligned");
-  if (st->n_sel) REQUIRE(aligned(st->n_sel, 4), "n_sel must be 4-byte aligned");
-  if (st->lse) REQUIRE(aligned(st->lse, 4), "lse must be 4-byte aligned");
-  if (s.pool > 1) {
-    REQUIRE_PTR(st->Kp, 16);
-    REQUIRE_PTR(st->Vp, 16);
-  } else {
-    REQUIRE(st->Kp == nullptr && st->Vp == nullptr, "Kp and Vp must be NULL when pool == 1");
-  }
-  REQUIRE(st->sm_scale > 0.f && st->sm_scale < 1e30f, "sm_scale must be positive and finite");
-  if (sks::ceil_div(s.NB, sks::TK_SUB) > sks::TK_MAX_SUBS)
-    return fail(SKS_ERR_UNSUPPORTED, "T_max / pool above %d is not supported by the selection",
-                sks::TK_MAX_SUBS * sks::TK_SUB);
+  TRY(check_step(kv, p, st, flags, s));
   TRY(check_ws(ws, ws_bytes_given, ws_bytes(s, st->Hq / kv->Hkv)));
-  const sks::TopkWs w = sks::topk_ws_carve(s, ws);
+  return hip_status(enqueue_step(*kv, s, *st, flags, sks::topk_ws_carve(s, ws), (hipStream_t)stream),
+                    "sks_decode_step");
+}
+
+int sks_decode_step_static(const sks_kv *kv, const sks_params *p, const sks_step *st,
+                           int32_t flags, sks_stream_t stream) {
+  sks::Shape s;
+  TRY(check_step(kv, p, st, flags, s));
+  const size_t need = ws_bytes(s, st->Hq / kv->Hkv);
+  if (need > (size_t)SKS_STATIC_WORKSPACE_BYTES)
+    return fail(SKS_ERR_WORKSPACE,
+                "this shape needs a %zu-byte workspace, more than the %zu bytes of the static one "
+                "(use sks_decode_step with a caller-provided workspace)",
+                need, (size_t)SKS_STATIC_WORKSPACE_BYTES);
   const hipStream_t hs = (hipStream_t)stream;
-  hipError_t e;
-  if (flags & SKS_STEP_APPEND)
-    e = sks::launch_step_prologue(st->q, st->Hq, *kv, s, st->basis, st->basis_per_head,
-                                  st->key_scale, st->qsk, st->qscale, st->S, st->Kp, st->Vp, hs);
-  else
-    e = sks::launch_sketch_query(st->q, s.B, s.R, st->Hq, s.Hkv, st->basis, st->basis_per_head,
-                                 st->qsk, st->qscale, hs);
-  const bool dense = (flags & SKS_STEP_DENSE) != 0;
-  const bool cand = (flags & SKS_STEP_NO_SCORES) && sks::topk_cand_preferred(s);
-  if (!dense && cand) {
-    if (e == hipSuccess)
-      e = sks::launch_topk_sample(st->qsk, st->S, kv->seq_len, s, w, hs);
-    if (e == hipSuccess)
-      e = sks::launch_score(st->qsk, st->S, kv->seq_len, s, nullptr, &w, hs, true);
-    if (e == hipSuccess)
-      e = sks::launch_topk_cand(st->qsk, st->S, st->scores, kv->seq_len, s, st->idx, st->n_sel,
-                                w, hs);
-  } else if (!dense) {
-    if (e == hipSuccess) e = sks::launch_score(st->qsk, st->S, kv->seq_len, s, st->scores, &w, hs);
-    if (e == hipSuccess)
-      e = sks::launch_topk(st->scores, kv->seq_len, s, true, st->idx, st->n_sel, w, hs);
-  }
-  if (e == hipSuccess)
-    e = sks::launch_attn(st->q, st->Hq, *kv, s, st->idx, st->Kp, st->Vp, st->sm_scale, st->out,
-                         st->lse, w, hs, dense);
-  return hip_status(e, "sks_decode_step");
+  void *ws = nullptr;
+  bool clear = false;
+  TRY(static_workspace(hs, s, ws, clear));
+  hipError_t e = hipSuccess;
+  // the selection histograms must be zero at rest; a call of another shape
+  // lays its scratch over them, so they are cleared (a fill kernel, no memset
+  // node) at the device's first call and after a change of shape
+  if (clear) e = sks::launch_fill(static_cast<int32_t *>(ws), sks::hist_region_bytes(s) / 4, hs);
+  if (e == hipSuccess) e = enqueue_step(*kv, s, *st, flags, sks::topk_ws_carve(s, ws), hs);
+  return hip_status(e, "sks_decode_step_static");
 }
 
 }  // extern "C"

@@ -320,3 +320,33 @@ def test_refit_argument_errors(L):
         sks.SKS_ERR_WORKSPACE
     assert L.sks_refit_key_scale(ctypes.byref(k), 0, 1000, None, 1, FAKE, FAKE, 1 << 30,
                                  None) == sks.SKS_ERR_ARG and "basis" in sks.last_error()
+
+
+def test_static_step_argument_errors_and_size_limit(L):
+    """The allocation-free step validates like sks_decode_step, before any
+    launch, and refuses shapes whose workspace exceeds its static array."""
+    k, p = kv(), sks.params(64, 32)
+    call = lambda st, flags=1, kk=k, pp=p: L.sks_decode_step_static(
+        ctypes.byref(kk), ctypes.byref(pp), st if st is None else ctypes.byref(st), flags, None)
+    assert call(None) == sks.SKS_ERR_ARG and "step" in sks.last_error()
+    assert call(step_desc(), flags=16) == sks.SKS_ERR_ARG and "flags" in sks.last_error()
+    assert call(step_desc(Hq=6)) == sks.SKS_ERR_ARG and "multiple" in sks.last_error()
+    assert call(step_desc(idx=None)) == sks.SKS_ERR_ARG and "idx" in sks.last_error()
+    # a shape beyond the static workspace: refused with the sizes in the message
+    big = kv(B=64, Hkv=8, T=250000)
+    need = L.sks_workspace_bytes(ctypes.byref(big), ctypes.byref(p), 8)
+    assert need > sks.STATIC_WORKSPACE_BYTES
+    assert call(step_desc(), kk=big) == sks.SKS_ERR_WORKSPACE
+    assert str(need) in sks.last_error() and str(sks.STATIC_WORKSPACE_BYTES) in sks.last_error()
+
+
+def test_static_workspace_size_matches_header_and_fits_every_workload(L):
+    text = open(HEADER).read()
+    m = re.search(r"#define SKS_STATIC_WORKSPACE_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == sks.STATIC_WORKSPACE_BYTES
+    from long_context_sparse_sketch_amd import configs as C
+    for cfg in C.ALL:
+        k = kv(B=cfg.B, Hkv=cfg.Hkv, T=cfg.T_max, dtype=cfg.kv_dtype, Ks=FAKE, Vs=FAKE)
+        p = sks.params(cfg.window, cfg.topk, cfg.pool, cfg.R)
+        need = L.sks_workspace_bytes(ctypes.byref(k), ctypes.byref(p), cfg.Hq)
+        assert 0 < need <= sks.STATIC_WORKSPACE_BYTES, (cfg.name, need)
