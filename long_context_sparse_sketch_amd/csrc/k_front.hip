@@ -1,0 +1,164 @@
+// The decode step's first launch: the work that comes before the score pass,
+// in one grid of 256-thread workgroups ("What it took" on the page "8 agents
+// x 250K context, concurrently, on two 3090s": build the sketch, score every
+// token, pick the top ~2K -- graph-safe):
+//
+//   [0, nq)               the query sketch of every (sequence, row, KV head);
+//   [.., + n_app)         the append: the key sketch (and pooled block) of
+//                         the rows' own tokens (sketch_body.h);
+//   [.., + n_samp)        candidate mode's sample pass (topk_body.h), each
+//                         workgroup computing its segment's query sketch
+//                         itself (the same routine and bits as above), so
+//                         that it needs nothing from this launch.
+// The three are independent chains of a few dependent loads each, so one
+// launch pays their latency once instead of three times.  The append writes
+// sketch rows of the rows' own tokens, which the sample pass reads only when
+// the window is shorter than the rows (then a sampled row may be read while
+// it is written: the sample decides only how long the selection takes, never
+// its result).
+#include "sketch_body.h"
+#include "tier.h"
+#include "topk_body.h"
+
+namespace sks {
+namespace {
+
+struct FrontArgs {
+  int R, Hkv, T_max, NB, window, pool, topk;
+  int n_samp, samp_per_seg, nq, n_app, app_rows;
+  const int32_t *seq_len;
+  // the query sketch and the append
+  const uint16_t *q;
+  int Hq;
+  const float *basis;
+  int basis_per_head;
+  const float *key_scale;
+  int8_t *qsk;
+  float *qscale;
+  const void *K, *V;
+  const uint16_t *Ks;
+  const void *Kh;
+  const uint16_t *Ksh;
+  int W_hot;
+  int8_t *S;
+  uint16_t *Kp, *Vp;
+  // the sample pass
+  int32_t *hsamp;
+};
+
+struct SampleLds {
+  int lh[HIST1_BINS];
+  __align__(16) int8_t qcode[RANK];
+  SketchLds sk;
+};
+
+union FrontLds {
+  SampleLds samp;
+  SketchLds sk;
+};
+
+template <int DT, bool CAND>
+__global__ __launch_bounds__(SK_THREADS) void front_kernel(FrontArgs f) {
+  static_assert(SK_THREADS == SAMPLE_THREADS, "one workgroup size");
+  __shared__ FrontLds lds;
+  int blk = blockIdx.x;
+  if (blk < f.nq) {
+    block_query_sketch(f.q, f.R, f.Hq, f.Hkv, f.basis, f.basis_per_head, blk,
+                       f.qsk + (size_t)blk * RANK, f.qscale ? f.qscale + blk : nullptr, lds.sk);
+    return;
+  }
+  blk -= f.nq;
+  if (blk < f.n_app) {
+    block_key_row<DT>(f.K, f.V, f.Ks, f.Kh, f.Ksh, f.W_hot, f.seq_len, f.basis,
+                      f.basis_per_head, f.key_scale, f.Hkv, f.T_max, f.R, f.NB, f.pool, 1, 0, 0,
+                      f.S, f.Kp, f.Vp, blk / f.app_rows, blk % f.app_rows, lds.sk);
+    return;
+  }
+  blk -= f.n_app;
+  if (CAND && blk < f.n_samp) {
+    const int seg = blk / f.samp_per_seg;
+    const SegGeom g = seg_geom(seg, f.seq_len, f.R, f.Hkv, f.T_max, f.window, f.pool, f.topk);
+    if (g.k_eff >= g.n_far) return;             // uniform: no selection needed
+    const int m = (g.n_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
+    const int j0 = (blk % f.samp_per_seg) * SAMPLE_WG_ROWS;
+    if (j0 >= m) return;
+    int4 sv[SAMPLE_UNROLL];
+    sample_load(f.S, ((size_t)g.b * f.Hkv + g.h) * f.NB, j0, m, sv);
+    for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS) lds.samp.lh[k] = 0;
+    block_query_sketch(f.q, f.R, f.Hq, f.Hkv, f.basis, f.basis_per_head, seg, lds.samp.qcode,
+                       nullptr, lds.samp.sk);
+    __syncthreads();
+    const int4 qv = reinterpret_cast<const int4 *>(lds.samp.qcode)[threadIdx.x & 3];
+    sample_bins(sv, qv, j0, m, lds.samp.lh);
+    __syncthreads();
+    sample_flush(lds.samp.lh, f.hsamp + (size_t)seg * HIST1_BINS);
+  }
+}
+
+template <int DT>
+void launch_front_t(const FrontArgs &f, bool cand, int grid, hipStream_t st) {
+  if (cand)
+    front_kernel<DT, true><<<grid, SK_THREADS, 0, st>>>(f);
+  else
+    front_kernel<DT, false><<<grid, SK_THREADS, 0, st>>>(f);
+}
+
+}  // namespace
+
+hipError_t launch_step_front(const sks_kv &kv, const Shape &s, const uint16_t *q, int Hq,
+                             const float *basis, int basis_per_head, const float *key_scale,
+                             int8_t *qsk, float *qscale, int8_t *S, uint16_t *Kp, uint16_t *Vp,
+                             bool append, bool cand, const TopkWs &w, hipStream_t st) {
+  FrontArgs f;
+  f.R = s.R;
+  f.Hkv = s.Hkv;
+  f.T_max = s.T_max;
+  f.NB = s.NB;
+  f.window = s.window;
+  f.pool = s.pool;
+  f.topk = s.topk;
+  f.seq_len = kv.seq_len;
+  const int nseg = s.B * s.R * s.Hkv;
+  f.samp_per_seg = 1;
+  f.n_samp = 0;
+  if (cand) {
+    const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
+    const long max_m = (max_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
+    f.samp_per_seg = std::max(1, ceil_div(max_m, SAMPLE_WG_ROWS));
+    f.n_samp = f.samp_per_seg * nseg;
+  }
+  f.nq = nseg;
+  // append rows per (b, h), as in launch_sketch_keys' append mode
+  long app_rows = s.pool == 1 ? (long)s.R : ((long)s.R + s.pool) / s.pool + 1;
+  if (app_rows > s.NB) app_rows = s.NB;
+  f.app_rows = (int)app_rows;
+  f.n_app = append ? f.app_rows * s.B * s.Hkv : 0;
+  f.q = q;
+  f.Hq = Hq;
+  f.basis = basis;
+  f.basis_per_head = basis_per_head;
+  f.key_scale = key_scale;
+  f.qsk = qsk;
+  f.qscale = qscale;
+  f.K = kv.K;
+  f.V = kv.V;
+  f.Ks = kv.K_scale;
+  const HotRows hr = hot_rows(kv);
+  f.Kh = hr.K;
+  f.Ksh = hr.Ks;
+  f.W_hot = hr.W;
+  f.S = S;
+  f.Kp = Kp;
+  f.Vp = Vp;
+  f.hsamp = w.hsamp;
+  const long grid = (long)f.nq + f.n_app + f.n_samp;
+  if (s.dtype == SKS_KV_I8)
+    launch_front_t<SKS_KV_I8>(f, cand, (int)grid, st);
+  else if (s.dtype == SKS_KV_I4)
+    launch_front_t<SKS_KV_I4>(f, cand, (int)grid, st);
+  else
+    launch_front_t<SKS_KV_BF16>(f, cand, (int)grid, st);
+  return hipGetLastError();
+}
+
+}  // namespace sks

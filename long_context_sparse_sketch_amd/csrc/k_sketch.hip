@@ -7,15 +7,17 @@
 // of "What it adds" on the "Agens SGLang" README.
 //
 // Bulk builds run on the matrix cores (sketch_mfma_kernel, below); the few
-// rows of a step's append take one wave per row (sketch_rows_small_kernel).
+// rows of a step's append take one workgroup per row (sketch_rows_small_kernel,
+// sketch_body.h).
 #include "sks_internal.h"
 #include "refit.h"
+#include "sketch_body.h"
 #include "tier.h"
 
 namespace sks {
 namespace {
 
-constexpr int SMALL_ROWS = 64;   // up to this many rows per (b, h): wave-per-row kernel
+constexpr int SMALL_ROWS = 64;   // up to this many rows per (b, h): workgroup-per-row kernel
 
 // int8 code pair (bits sh .. sh+15 of w) -> two bf16 (exact: |code| <= 127)
 __device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int sh) {
@@ -37,39 +39,10 @@ __device__ __forceinline__ sk_u32x4_t i4x8_bf16(uint32_t w) {
   return o;
 }
 
-// Key code from y and the reciprocal of the frozen key scale, computed once:
-// a multiply instead of an IEEE division per code (equal to rne(y / scale)
-// whenever 1/scale is exact, e.g. for a power-of-two scale; otherwise a code
-// can differ only where y / scale lies within an ulp of a rounding boundary).
-// The bulk build and the per-step append use the same form.
-__device__ __forceinline__ int8_t key_code(float y, float inv_scale) {
-  float v = __builtin_rintf(y * inv_scale);
-  v = fminf(fmaxf(v, -127.0f), 127.0f);
-  return (int8_t)(int)v;
-}
-
 // Bytes of one cached K row.
 template <int DT>
 constexpr int row_bytes() {
   return DT == SKS_KV_BF16 ? 2 * D : DT == SKS_KV_I8 ? D : D / 2;
-}
-
-// First sketch row of the range handled by this (b, h): host range or append.
-__device__ __forceinline__ void sketch_range(int append, const int32_t *seq_len, int b, int T_max,
-                                             int R, int pool, int NB, int t_begin, int t_end,
-                                             int &j_lo, int &j_hi) {
-  int lo = t_begin, hi = t_end;
-  if (append) {
-    int L0 = clamp_len(seq_len[b], T_max, R);
-    lo = L0 - 1;
-    hi = L0 - 1 + R;
-    if (lo < 0) lo = 0;
-  }
-  lo = lo < 0 ? 0 : (lo > T_max ? T_max : lo);
-  hi = hi < lo ? lo : (hi > T_max ? T_max : hi);
-  j_lo = lo / pool;                       // blocks whose last token is in [lo, hi)
-  j_hi = hi / pool;
-  if (j_hi > NB) j_hi = NB;
 }
 
 // ---------------------------------------------------------------------------
@@ -334,188 +307,30 @@ __global__ __launch_bounds__(PM_THREADS) void pool_mean_kernel(
       make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Lane c's basis row (128 fp32) into registers.  The row wave and the query
-// wave issue these loads first, so that they overlap the key / query loads,
-// and then dot the row with the staged vector in the order d = 0 .. 127.
-__device__ __forceinline__ void load_basis_row(const float *__restrict__ Prow, float4 (&pr)[D / 4]) {
-#pragma unroll
-  for (int k = 0; k < D / 4; ++k) pr[k] = reinterpret_cast<const float4 *>(Prow)[k];
-}
-__device__ __forceinline__ float dot_basis_row(const float4 (&pr)[D / 4], const float *x) {
-  float y = 0.f;
-#pragma unroll
-  for (int k = 0; k < D / 4; ++k) {
-    const float4 xv = reinterpret_cast<const float4 *>(x)[k];
-    y = __builtin_fmaf(pr[k].x, xv.x, y);
-    y = __builtin_fmaf(pr[k].y, xv.y, y);
-    y = __builtin_fmaf(pr[k].z, xv.z, y);
-    y = __builtin_fmaf(pr[k].w, xv.w, y);
-  }
-  return y;
-}
-
-// Few rows per (b, h) -- the per-step append of the rows' own tokens: one
-// wave per sketch row.  The 128-element key (or pooled block) is staged in
-// LDS, lane c dots basis row c with it, so the latency is that of one row
-// instead of one lane walking all 64 x 128 products.  Appended tokens
-// (pool == 1) are read from the hot ring Kh (slot = position % W_hot; the
-// full cache itself when there is no hot tier).
+// A short range or the per-step append: one workgroup per sketch row (see
+// block_key_row).
 template <int DT>
-__device__ void sketch_row_wave(const void *__restrict__ K, const void *__restrict__ V,
-                                const uint16_t *__restrict__ Ks, const void *__restrict__ Kh,
-                                const uint16_t *__restrict__ Ksh, int W_hot,
-                                const int32_t *__restrict__ seq_len,
-                                const float *__restrict__ basis, int basis_per_head,
-                                const float *__restrict__ key_scale, int Hkv, int T_max, int R,
-                                int NB, int pool, int append, int t_begin, int t_end,
-                                int8_t *__restrict__ S, uint16_t *__restrict__ Kp,
-                                uint16_t *__restrict__ Vp, int bh, int jx) {
-  __shared__ __align__(16) float x[D];
-  const int b = bh / Hkv, h = bh % Hkv;
-  int j_lo, j_hi;
-  sketch_range(append, seq_len, b, T_max, R, pool, NB, t_begin, t_end, j_lo, j_hi);
-  const int j = j_lo + jx;
-  if (j >= j_hi) return;
-  const int lane = threadIdx.x;
-  float4 pr[D / 4];
-  load_basis_row(basis + (basis_per_head ? (size_t)h * RANK * D : 0) + (size_t)lane * D, pr);
-  if (pool == 1) {
-    if (append) {
-      K = Kh;
-      Ks = Ksh;
-    }
-    const size_t row = append ? (size_t)bh * W_hot + hot_slot(j, W_hot) : (size_t)bh * T_max + j;
-    float x0, x1;
-    if (DT == SKS_KV_BF16) {
-      const uint32_t w = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(K) + row * D)[lane];
-      x0 = bf16_lo(w);
-      x1 = bf16_hi(w);
-    } else if (DT == SKS_KV_I4) {
-      const uint32_t w = (static_cast<const uint8_t *>(K) + row * (D / 2))[lane];
-      const float sc = f16_bits_to_float(Ks[row]);
-      x0 = (float)((int32_t)(w << 28) >> 28) * sc;
-      x1 = (float)((int32_t)(w << 24) >> 28) * sc;
-    } else {
-      const uint16_t w = reinterpret_cast<const uint16_t *>(static_cast<const int8_t *>(K) + row * D)[lane];
-      const float sc = f16_bits_to_float(Ks[row]);
-      x0 = (float)(int8_t)(w & 0xff) * sc;
-      x1 = (float)(int8_t)(w >> 8) * sc;
-    }
-    x[2 * lane] = x0;
-    x[2 * lane + 1] = x1;
-  } else {
-    // pooled block: fp64 mean of `pool` rows (exact for bf16), rounded once to
-    // bf16.  The K and V rows are loaded 8 at a time, all in flight together,
-    // and summed in row order.
-    const size_t tok0 = (size_t)bh * T_max + (size_t)j * pool;
-    const size_t out_row = (size_t)bh * NB + j;
-    const double dpool = (double)pool;
-    const uint32_t *Kw = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(K) + tok0 * D) + lane;
-    const uint32_t *Vw = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(V) + tok0 * D) + lane;
-    double k0s = 0.0, k1s = 0.0, v0s = 0.0, v1s = 0.0;
-    for (int k0 = 0; k0 < pool; k0 += 8) {
-      uint32_t wk[8], wv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool in = k0 + u < pool;
-        wk[u] = in ? Kw[(size_t)(k0 + u) * (D / 2)] : 0u;
-        wv[u] = in ? Vw[(size_t)(k0 + u) * (D / 2)] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (k0 + u < pool) {
-          k0s += bf16_lo(wk[u]);
-          k1s += bf16_hi(wk[u]);
-          v0s += bf16_lo(wv[u]);
-          v1s += bf16_hi(wv[u]);
-        }
-    }
-    const uint16_t o0 = f64_to_bf16_rne(k0s / dpool), o1 = f64_to_bf16_rne(k1s / dpool);
-    const uint16_t p0 = f64_to_bf16_rne(v0s / dpool), p1 = f64_to_bf16_rne(v1s / dpool);
-    reinterpret_cast<uint32_t *>(Kp + out_row * D)[lane] = (uint32_t)o0 | ((uint32_t)o1 << 16);
-    reinterpret_cast<uint32_t *>(Vp + out_row * D)[lane] = (uint32_t)p0 | ((uint32_t)p1 << 16);
-    x[2 * lane] = __uint_as_float((uint32_t)o0 << 16);
-    x[2 * lane + 1] = __uint_as_float((uint32_t)o1 << 16);
-  }
-  __syncthreads();
-  const float y = dot_basis_row(pr, x);
-  S[((size_t)bh * NB + j) * RANK + lane] = key_code(y, 1.0f / key_scale[h]);
-}
-
-template <int DT>
-__global__ __launch_bounds__(64) void sketch_rows_small_kernel(
+__global__ __launch_bounds__(SK_THREADS) void sketch_rows_small_kernel(
     const void *__restrict__ K, const void *__restrict__ V, const uint16_t *__restrict__ Ks,
     const void *__restrict__ Kh, const uint16_t *__restrict__ Ksh, int W_hot,
     const int32_t *__restrict__ seq_len, const float *__restrict__ basis, int basis_per_head,
     const float *__restrict__ key_scale, int Hkv, int T_max, int R, int NB, int pool, int append,
     int t_begin, int t_end, int8_t *__restrict__ S, uint16_t *__restrict__ Kp,
     uint16_t *__restrict__ Vp) {
-  sketch_row_wave<DT>(K, V, Ks, Kh, Ksh, W_hot, seq_len, basis, basis_per_head, key_scale, Hkv,
-                      T_max, R, NB, pool, append, t_begin, t_end, S, Kp, Vp, blockIdx.y,
-                      blockIdx.x);
+  __shared__ SketchLds lds;
+  block_key_row<DT>(K, V, Ks, Kh, Ksh, W_hot, seq_len, basis, basis_per_head, key_scale, Hkv,
+                    T_max, R, NB, pool, append, t_begin, t_end, S, Kp, Vp, blockIdx.y, blockIdx.x,
+                    lds);
 }
 
-// Query sketch: one wave per (b, i, h).  qbar = mean of the group's queries
-// (fp32), y = P qbar by lane c, absmax over the wave, codes by lane c.
-__device__ void sketch_query_wave(const uint16_t *__restrict__ q, int R, int Hq, int Hkv,
-                                  const float *__restrict__ basis, int basis_per_head,
-                                  int8_t *__restrict__ qsk, float *__restrict__ qscale, int seg) {
-  __shared__ __align__(16) float qbar[D];     // seg = (b * R + i) * Hkv + h
-  const int h = seg % Hkv, bi = seg / Hkv;
-  const int g = Hq / Hkv;
-  const int lane = threadIdx.x;
-  float4 pr[D / 4];
-  load_basis_row(basis + (basis_per_head ? (size_t)h * RANK * D : 0) + (size_t)lane * D, pr);
-  // the group's queries, up to 8 loads in flight, summed in head order
-  const uint16_t *qg = q + ((size_t)bi * Hq + (size_t)h * g) * D;
-  float s0 = 0.f, s1 = 0.f;
-  for (int j0 = 0; j0 < g; j0 += 8) {
-    uint32_t w[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      w[u] = j0 + u < g ? *reinterpret_cast<const uint32_t *>(qg + (size_t)(j0 + u) * D + 2 * lane) : 0u;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (j0 + u < g) {
-        s0 += bf16_lo(w[u]);
-        s1 += bf16_hi(w[u]);
-      }
-  }
-  qbar[2 * lane] = s0 / (float)g;
-  qbar[2 * lane + 1] = s1 / (float)g;
-  __syncthreads();
-  const float y = dot_basis_row(pr, qbar);
-  float amax = fabsf(y);
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  float scale = amax / 127.0f;
-  int8_t code = amax > 0.f ? quant_code(y, scale) : (int8_t)0;
-  qsk[(size_t)seg * RANK + lane] = code;
-  if (lane == 0 && qscale) qscale[seg] = amax > 0.f ? scale : 0.f;
-}
-
-__global__ __launch_bounds__(64) void sketch_query_kernel(
+// Query sketch: one workgroup per (b, i, h) (see block_query_sketch).
+__global__ __launch_bounds__(SK_THREADS) void sketch_query_kernel(
     const uint16_t *__restrict__ q, int R, int Hq, int Hkv, const float *__restrict__ basis,
     int basis_per_head, int8_t *__restrict__ qsk, float *__restrict__ qscale) {
-  sketch_query_wave(q, R, Hq, Hkv, basis, basis_per_head, qsk, qscale, blockIdx.x);
-}
-
-// The step prologue in one launch: workgroups [0, nq) sketch the queries,
-// the rest the rows' own tokens (append), nrows per (b, h).
-template <int DT>
-__global__ __launch_bounds__(64) void step_prologue_kernel(
-    const uint16_t *__restrict__ q, int Hq, const void *__restrict__ K,
-    const void *__restrict__ V, const uint16_t *__restrict__ Ks, const void *__restrict__ Kh,
-    const uint16_t *__restrict__ Ksh, int W_hot, const int32_t *__restrict__ seq_len, const float *__restrict__ basis, int basis_per_head,
-    const float *__restrict__ key_scale, int Hkv, int T_max, int R, int NB, int pool, int nq,
-    int nrows, int8_t *__restrict__ qsk, float *__restrict__ qscale, int8_t *__restrict__ S,
-    uint16_t *__restrict__ Kp, uint16_t *__restrict__ Vp) {
-  if ((int)blockIdx.x < nq) {
-    sketch_query_wave(q, R, Hq, Hkv, basis, basis_per_head, qsk, qscale, blockIdx.x);
-    return;
-  }
-  const int w = blockIdx.x - nq;
-  sketch_row_wave<DT>(K, V, Ks, Kh, Ksh, W_hot, seq_len, basis, basis_per_head, key_scale, Hkv,
-                      T_max, R, NB, pool, 1, 0, 0, S, Kp, Vp, w / nrows, w % nrows);
+  __shared__ SketchLds lds;
+  const int seg = blockIdx.x;
+  block_query_sketch(q, R, Hq, Hkv, basis, basis_per_head, seg, qsk + (size_t)seg * RANK,
+                     qscale ? qscale + seg : nullptr, lds);
 }
 
 }  // namespace
@@ -535,7 +350,8 @@ hipError_t launch_sketch_keys(const sks_kv &kv, const Shape &s, const float *bas
     dim3 g2((unsigned)nrows, s.B * s.Hkv);
     const HotRows hr = hot_rows(kv);
 #define SKS_ROWS_SMALL(DT)                                                                         \
-  sketch_rows_small_kernel<DT><<<g2, 64, 0, st>>>(kv.K, kv.V, kv.K_scale, hr.K, hr.Ks, hr.W,     \
+  sketch_rows_small_kernel<DT><<<g2, SK_THREADS, 0, st>>>(kv.K, kv.V, kv.K_scale, hr.K, hr.Ks, \
+                                                          hr.W,                                  \
                                                   kv.seq_len, basis, basis_per_head, key_scale,   \
                                                   s.Hkv, s.T_max, s.R, s.NB, s.pool, append,      \
                                                   t_begin, t_end, S, Kp, Vp)
@@ -590,37 +406,11 @@ hipError_t launch_refit_amax(const sks_kv &kv, int t_begin, int t_end, const flo
   return hipGetLastError();
 }
 
-hipError_t launch_step_prologue(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
-                                const float *basis, int basis_per_head, const float *key_scale,
-                                int8_t *qsk, float *qscale, int8_t *S, uint16_t *Kp, uint16_t *Vp,
-                                hipStream_t st) {
-  // append rows per (b, h), as in launch_sketch_keys' append mode
-  long nrows = s.pool == 1 ? (long)s.R : ((long)s.R + s.pool) / s.pool + 1;
-  if (nrows > s.NB) nrows = s.NB;
-  if (nrows > SMALL_ROWS) return hipErrorInvalidValue;
-  const int nq = s.B * s.R * s.Hkv;
-  const unsigned grid = (unsigned)(nq + nrows * s.B * s.Hkv);
-  const HotRows hr = hot_rows(kv);
-#define SKS_PROLOGUE(DT)                                                                          \
-  step_prologue_kernel<DT><<<grid, 64, 0, st>>>(q, Hq, kv.K, kv.V, kv.K_scale, hr.K, hr.Ks,     \
-                                                hr.W, kv.seq_len, basis, basis_per_head,          \
-                                                key_scale, s.Hkv, s.T_max, s.R, s.NB, s.pool, nq, \
-                                                (int)nrows, qsk, qscale, S, Kp, Vp)
-  if (s.dtype == SKS_KV_BF16)
-    SKS_PROLOGUE(SKS_KV_BF16);
-  else if (s.dtype == SKS_KV_I8)
-    SKS_PROLOGUE(SKS_KV_I8);
-  else
-    SKS_PROLOGUE(SKS_KV_I4);
-#undef SKS_PROLOGUE
-  return hipGetLastError();
-}
-
 hipError_t launch_sketch_query(const uint16_t *q, int B, int R, int Hq, int Hkv,
                                const float *basis, int basis_per_head, int8_t *qsk,
                                float *qscale, hipStream_t st) {
-  sketch_query_kernel<<<B * R * Hkv, 64, 0, st>>>(q, R, Hq, Hkv, basis, basis_per_head, qsk,
-                                                  qscale);
+  sketch_query_kernel<<<B * R * Hkv, SK_THREADS, 0, st>>>(q, R, Hq, Hkv, basis, basis_per_head,
+                                                          qsk, qscale);
   return hipGetLastError();
 }
 

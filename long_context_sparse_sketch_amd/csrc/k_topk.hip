@@ -31,7 +31,7 @@
 //
 // Candidate mode (the decode step when its caller does not read the scores)
 // replaces the stored scores and the filter pass:
-//   sample: scores every 64th far entry (512 sampled rows per workgroup)
+//   sample: scores every 64th far entry (1,024 sampled rows per workgroup)
 //     into a per-segment histogram of the level-1 bins (zero at rest).
 //   the score pass: every workgroup takes as the segment's estimate E the
 //     lowest key of the sample bin holding the rho-th largest sampled key,
@@ -219,12 +219,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
 
 constexpr int TF_THREADS = 1024;
 
-constexpr int SAMPLE_THREADS = 256;
-constexpr int SAMPLE_UNROLL = 8;        // sketch loads in flight per lane
-constexpr int SAMPLE_WG_ROWS = SAMPLE_THREADS / 4 * SAMPLE_UNROLL;   // 512 sampled rows
-
 // Sample pass: workgroup x of segment y scores sampled rows j * 64,
-// j in [512x, 512x + 512), and adds their level-1 bins to the segment's
+// j in [1024x, 1024x + 1024), and adds their level-1 bins to the segment's
 // sample histogram (zero at rest; the final pass returns it to zero).
 __global__ __launch_bounds__(SAMPLE_THREADS) void topk_sample_kernel(
     const int8_t *__restrict__ qsk, const int8_t *__restrict__ S,
@@ -237,33 +233,14 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void topk_sample_kernel(
   const int m = (g.n_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;   // rows j * 64 < n_far
   const int j0 = blockIdx.x * SAMPLE_WG_ROWS;
   if (j0 >= m) return;
-  for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS) lh[k] = 0;
-  __syncthreads();
-  // a quad of lanes per sampled sketch row, 16 bytes each
-  const int part = threadIdx.x & 3, quad = threadIdx.x >> 2;
-  constexpr int QUADS = SAMPLE_THREADS / 4;
-  const int4 qv = reinterpret_cast<const int4 *>(qsk + (size_t)seg * RANK)[part];
-  const int4 *Sseg = reinterpret_cast<const int4 *>(S + ((size_t)g.b * Hkv + g.h) * NB * RANK) + part;
   int4 sv[SAMPLE_UNROLL];
-#pragma unroll
-  for (int u = 0; u < SAMPLE_UNROLL; ++u) {
-    const int j = j0 + u * QUADS + quad;
-    sv[u] = j < m ? Sseg[(size_t)j * SAMPLE_STRIDE * 4] : make_int4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int u = 0; u < SAMPLE_UNROLL; ++u) {
-    int acc = __builtin_amdgcn_sdot4(sv[u].x, qv.x, 0, false);
-    acc = __builtin_amdgcn_sdot4(sv[u].y, qv.y, acc, false);
-    acc = __builtin_amdgcn_sdot4(sv[u].z, qv.z, acc, false);
-    acc = __builtin_amdgcn_sdot4(sv[u].w, qv.w, acc, false);
-    acc = quad_sum_i(acc);
-    const int j = j0 + u * QUADS + quad;
-    if (part == 0 && j < m) atomicAdd(&lh[biased_key(acc) >> HIST2_BITS], 1);
-  }
+  sample_load(S, ((size_t)g.b * Hkv + g.h) * NB, j0, m, sv);
+  for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS) lh[k] = 0;
+  const int4 qv = reinterpret_cast<const int4 *>(qsk + (size_t)seg * RANK)[threadIdx.x & 3];
   __syncthreads();
-  int32_t *gh = hsamp + (size_t)seg * HIST1_BINS;
-  for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS)
-    if (lh[k]) atomicAdd(&gh[k], lh[k]);
+  sample_bins(sv, qv, j0, m, lh);
+  __syncthreads();
+  sample_flush(lh, hsamp + (size_t)seg * HIST1_BINS);
 }
 
 __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(FinalArgs a) {
@@ -343,7 +320,7 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
   // far entry is a candidate there, and the exact select runs in LDS.
   const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   FinalArgs a = final_args(scores, seq_len, s, idx, n_sel, w);
-  if (max_far <= TF_CACHE) {
+  if (max_far <= TF_REGS) {
     a.skip = 1;
     a.h1_ready = hist_ready;
   } else {
@@ -355,14 +332,14 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
 }
 
 // Candidate mode pays off for single-row steps where the final pass cannot
-// simply take every far entry (more than TF_CACHE of them) and the batch
+// simply take every far entry (more than TF_REGS of them) and the batch
 // streams enough sketch rows (2^20) for the saved score stores to outweigh
 // the two extra launches.  (With verify rows the candidate score pass keeps
 // more state per lane and measured slower than storing the scores.)
 bool topk_cand_preferred(const Shape &s) {
   const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   const long nseg = (long)s.B * s.R * s.Hkv;
-  return s.R == 1 && max_far > TF_CACHE && nseg * max_far >= (1L << 20);
+  return s.R == 1 && max_far > TF_REGS && nseg * max_far >= (1L << 20);
 }
 
 hipError_t launch_topk_sample(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,

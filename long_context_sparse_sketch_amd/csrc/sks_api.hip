@@ -172,27 +172,26 @@ int check_step(const sks_kv *kv, const sks_params *p, const sks_step *st, int32_
   return SKS_OK;
 }
 
-// The launches of one decode step on a carved workspace.
+// The launches of one decode step on a carved workspace: the first launch
+// (query sketch, append, candidate mode's sample pass), the score pass, the
+// selection, the attention and its merge.
 hipError_t enqueue_step(const sks_kv &kv, const sks::Shape &s, const sks_step &st, int32_t flags,
                         const sks::TopkWs &w, hipStream_t hs) {
-  hipError_t e;
-  if (flags & SKS_STEP_APPEND)
-    e = sks::launch_step_prologue(st.q, st.Hq, kv, s, st.basis, st.basis_per_head, st.key_scale,
-                                  st.qsk, st.qscale, st.S, st.Kp, st.Vp, hs);
-  else
-    e = sks::launch_sketch_query(st.q, s.B, s.R, st.Hq, s.Hkv, st.basis, st.basis_per_head,
-                                 st.qsk, st.qscale, hs);
   const bool dense = (flags & SKS_STEP_DENSE) != 0;
-  const bool cand = (flags & SKS_STEP_NO_SCORES) && sks::topk_cand_preferred(s);
-  if (!dense && cand) {
-    if (e == hipSuccess) e = sks::launch_topk_sample(st.qsk, st.S, kv.seq_len, s, w, hs);
-    if (e == hipSuccess) e = sks::launch_score(st.qsk, st.S, kv.seq_len, s, nullptr, &w, hs, true);
-    if (e == hipSuccess)
-      e = sks::launch_topk_cand(st.qsk, st.S, st.scores, kv.seq_len, s, st.idx, st.n_sel, w, hs);
-  } else if (!dense) {
-    if (e == hipSuccess) e = sks::launch_score(st.qsk, st.S, kv.seq_len, s, st.scores, &w, hs);
-    if (e == hipSuccess)
-      e = sks::launch_topk(st.scores, kv.seq_len, s, true, st.idx, st.n_sel, w, hs);
+  const bool cand = !dense && (flags & SKS_STEP_NO_SCORES) && sks::topk_cand_preferred(s);
+  hipError_t e = sks::launch_step_front(kv, s, st.q, st.Hq, st.basis, st.basis_per_head,
+                                        st.key_scale, st.qsk, st.qscale, st.S, st.Kp, st.Vp,
+                                        (flags & SKS_STEP_APPEND) != 0, cand, w, hs);
+  if (!dense) {
+    if (cand) {
+      if (e == hipSuccess) e = sks::launch_score(st.qsk, st.S, kv.seq_len, s, nullptr, &w, hs, true);
+      if (e == hipSuccess)
+        e = sks::launch_topk_cand(st.qsk, st.S, st.scores, kv.seq_len, s, st.idx, st.n_sel, w, hs);
+    } else {
+      if (e == hipSuccess) e = sks::launch_score(st.qsk, st.S, kv.seq_len, s, st.scores, &w, hs);
+      if (e == hipSuccess)
+        e = sks::launch_topk(st.scores, kv.seq_len, s, true, st.idx, st.n_sel, w, hs);
+    }
   }
   if (e == hipSuccess)
     e = sks::launch_attn(st.q, st.Hq, kv, s, st.idx, st.Kp, st.Vp, st.sm_scale, st.out, st.lse,

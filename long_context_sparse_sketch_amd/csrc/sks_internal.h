@@ -277,10 +277,12 @@ hipError_t launch_topk_cand(const int8_t *qsk, const int8_t *S, int32_t *scores,
                             const int32_t *seq_len, const Shape &s, int32_t *idx,
                             int32_t *n_sel, const TopkWs &w, hipStream_t st);
 
-hipError_t launch_step_prologue(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
-                                const float *basis, int basis_per_head, const float *key_scale,
-                                int8_t *qsk, float *qscale, int8_t *S, uint16_t *Kp, uint16_t *Vp,
-                                hipStream_t st);
+// The decode step's first launch (k_front.hip): the query sketch, the append
+// (append) and candidate mode's sample pass (cand) in one grid.
+hipError_t launch_step_front(const sks_kv &kv, const Shape &s, const uint16_t *q, int Hq,
+                             const float *basis, int basis_per_head, const float *key_scale,
+                             int8_t *qsk, float *qscale, int8_t *S, uint16_t *Kp, uint16_t *Vp,
+                             bool append, bool cand, const TopkWs &w, hipStream_t st);
 hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
                        const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp,
                        float sm_scale, float *out, float *lse, const TopkWs &w, hipStream_t st,

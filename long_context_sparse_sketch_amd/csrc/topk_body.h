@@ -9,11 +9,12 @@ namespace sks {
 namespace {
 
 constexpr int TK_THREADS = 256;
-constexpr int TF_CACHE = 8192;                     // candidates a final workgroup holds in registers
+constexpr int TF_REGS = 8192;                      // candidates a final workgroup holds in registers
+constexpr int TF_CACHE = 8192;                     // ... and in LDS for its exact path
 constexpr int FILTER_ITERS = TK_SUB / 64;          // 16 loads in flight per lane
 constexpr int HIST2_DIRECT_MAX = 4096;             // level-2 histogram built when bin b1 is this small
 static_assert(TK_CHUNK == TK_SUB * (TK_THREADS / 64), "one sub-chunk per wave");
-static_assert(TF_CACHE < 65536, "packed 16-bit counts in the emission scan");
+static_assert(TF_REGS < 65536 && TF_CACHE <= TF_REGS, "packed 16-bit counts in the emission scan");
 
 struct SegGeom {
   int b, i, h, n_far, k_eff;
@@ -104,6 +105,51 @@ __device__ int wave_threshold_bin_valid(const int *hist, int need, int n, int &a
   return wave_threshold_regs<PER>(v, need, n, above, valid);
 }
 
+// ---------------------------------------------------------------- sample pass
+// Candidate mode's sample: sampled rows j * SAMPLE_STRIDE of a segment's far
+// region, j in [j0, j0 + SAMPLE_WG_ROWS), scored against the segment's query
+// code, their level-1 bins counted in an LDS histogram and then added to the
+// segment's sample histogram (zero at rest).  A quad of lanes per sampled
+// sketch row, 16 bytes each, SAMPLE_UNROLL rows per quad in flight.
+constexpr int SAMPLE_THREADS = 256;
+constexpr int SAMPLE_UNROLL = 16;
+constexpr int SAMPLE_WG_ROWS = SAMPLE_THREADS / 4 * SAMPLE_UNROLL;   // 1024 sampled rows
+
+// Loads of this thread's sampled rows (issued before anything uses them).
+__device__ __forceinline__ void sample_load(const int8_t *__restrict__ S, size_t seg_row0, int j0,
+                                            int m, int4 (&sv)[SAMPLE_UNROLL]) {
+  const int part = threadIdx.x & 3, quad = threadIdx.x >> 2;
+  constexpr int QUADS = SAMPLE_THREADS / 4;
+  const int4 *Sseg = reinterpret_cast<const int4 *>(S + seg_row0 * RANK) + part;
+#pragma unroll
+  for (int u = 0; u < SAMPLE_UNROLL; ++u) {
+    const int j = j0 + u * QUADS + quad;
+    sv[u] = j < m ? Sseg[(size_t)j * SAMPLE_STRIDE * 4] : make_int4(0, 0, 0, 0);
+  }
+}
+
+// Their scores' level-1 bins into lh (this thread's 16 bytes of the query code: qv).
+__device__ __forceinline__ void sample_bins(const int4 (&sv)[SAMPLE_UNROLL], int4 qv, int j0, int m,
+                                            int *lh) {
+  const int part = threadIdx.x & 3, quad = threadIdx.x >> 2;
+  constexpr int QUADS = SAMPLE_THREADS / 4;
+#pragma unroll
+  for (int u = 0; u < SAMPLE_UNROLL; ++u) {
+    int acc = __builtin_amdgcn_sdot4(sv[u].x, qv.x, 0, false);
+    acc = __builtin_amdgcn_sdot4(sv[u].y, qv.y, acc, false);
+    acc = __builtin_amdgcn_sdot4(sv[u].z, qv.z, acc, false);
+    acc = __builtin_amdgcn_sdot4(sv[u].w, qv.w, acc, false);
+    acc = quad_sum_i(acc);
+    const int j = j0 + u * QUADS + quad;
+    if (part == 0 && j < m) atomicAdd(&lh[biased_key(acc) >> HIST2_BITS], 1);
+  }
+}
+
+__device__ __forceinline__ void sample_flush(const int *lh, int32_t *__restrict__ hsamp_seg) {
+  for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS)
+    if (lh[k]) atomicAdd(&hsamp_seg[k], lh[k]);
+}
+
 // Arguments of the final select pass.
 struct FinalArgs {
   const int32_t *scores, *seq_len;
@@ -112,7 +158,7 @@ struct FinalArgs {
   const int2 *cand;
   int n_sub_max, R, Hkv, T_max, NB, window, pool, topk;
   int32_t *idx, *n_sel;
-  int skip;      // no filter ran: every far entry is a candidate (n_far <= TF_CACHE)
+  int skip;      // no filter ran: every far entry is a candidate (n_far <= TF_REGS)
   int h1_ready;  // (with skip) the score pass built this step's level-1 histogram
   // Candidate mode: the score pass wrote the candidate lists (every far entry
   // at or above the segment's estimate) and the level-1 histogram, and no
@@ -128,14 +174,18 @@ struct FinalArgs {
 // and (LDS_CACHE) the candidates cached for the exact fallback path.
 template <int NT, int MAXSUB, bool LDS_CACHE>
 struct FinalLds {
-  static constexpr int PERT = TF_CACHE / NT;
+  static constexpr int PERT = TF_REGS / NT;
   int h1[hpad_size<HIST1_BINS>()];
   int h2[hpad_size<HIST2_BINS>()];
   int pre[MAXSUB + 1];
-  // sub-list start marks, one int per slot padded by one every PERT so that
-  // a thread's PERT consecutive slots fall in distinct banks across the wave
-  int marks[TF_CACHE + TF_CACHE / PERT];
-  int2 cache[LDS_CACHE ? TF_CACHE : 1];
+  union {
+    // sub-list start marks, one int per register slot padded by one every
+    // PERT so that a thread's PERT consecutive slots fall in distinct banks
+    // across the wave; read only before the candidates reach the registers
+    int marks[TF_REGS + TF_REGS / PERT];
+    // the candidates for the exact path, written only after that
+    int2 cache[LDS_CACHE ? TF_CACHE : 1];
+  };
   int sc_pre[NT / 64], sc_own[NT / 64], sc_cnt[NT / 64];
   int res[6];
 };
@@ -145,8 +195,8 @@ template <int NT, int MAXSUB, bool LDS_CACHE>
 __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS_CACHE> &L) {
   constexpr int TF_THREADS = NT;
   constexpr int TF_WAVES = NT / 64;
-  constexpr int TF_PERT = TF_CACHE / NT;
-  static_assert(TF_PERT * NT == TF_CACHE, "slots per thread");
+  constexpr int TF_PERT = TF_REGS / NT;
+  static_assert(TF_PERT * NT == TF_REGS, "slots per thread");
   const int32_t *scores = a.scores;           // written by this pass when rescoring
   const int32_t *__restrict__ seq_len = a.seq_len;
   int32_t *__restrict__ hist1 = a.hist1;
@@ -251,7 +301,7 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
     const int start = carry + incl - v;
     if (sidx < n_sub) {
       pre[sidx] = start;
-      if (v > 0 && start < TF_CACHE) marks[start + start / TF_PERT] = sidx + 1;
+      if (v > 0 && start < TF_REGS) marks[start + start / TF_PERT] = sidx + 1;
     }
     carry += tot;
   }
@@ -295,8 +345,8 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   const int m = raw || skip ? g.n_far : carry;
   const int2 *cseg = cand + (size_t)seg * n_sub_max * TK_SUB;
   const int32_t *srow = (cmode ? a.rescore : scores) + (size_t)seg * NB;
-  const bool in_regs = !raw && m <= TF_CACHE;   // the candidates fit this thread's registers
-  const bool cached = LDS_CACHE && in_regs;     // ... and the LDS cache of the exact path
+  const bool in_regs = !raw && m <= TF_REGS;    // the candidates fit the threads' registers
+  const bool cached = LDS_CACHE && in_regs && m <= TF_CACHE;   // ... and the exact path's LDS
   const int o0 = threadIdx.x * TF_PERT;          // this thread's slots [o0, o0 + TF_PERT)
 
   if (in_regs) {
@@ -401,7 +451,8 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
       }
     }
     // the guess did not hold: keep the candidates in LDS for the exact path
-    if (LDS_CACHE) {
+    // (the marks they overwrite were last read before block_excl_max's barrier)
+    if (cached) {
 #pragma unroll
       for (int q = 0; q < TF_PERT; ++q)
         if (o0 + q < m) cache[o0 + q] = c[q];

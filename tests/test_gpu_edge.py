@@ -91,11 +91,12 @@ def test_dense_and_extreme_selection(window, topk):
     compare_all(r, ref, Hq // Hkv, R)
 
 
-@pytest.mark.parametrize("topk", [8192, 8193, 20000])
+@pytest.mark.parametrize("topk", [8192, 8193, 16384, 16385, 20000])
 def test_large_k_beyond_register_cache(topk):
-    """k at and past the final pass's register cache of 8,192 candidates
-    (more candidates than it holds: the exact path over the candidate lists),
-    with far regions a few times k; two verify rows, ragged lengths."""
+    """k at and past the final pass's register slots and LDS cache (8,192
+    candidates each): more candidates than they hold take the exact path
+    over the candidate lists; with far regions a few times k; two verify
+    rows, ragged lengths."""
     flush(f"[edge] large k={topk}")
     B, R, Hq, Hkv, T = 2, 2, 8, 2, 45001
     q, K, V, Ks, Vs, basis, ks = random_arrays(B, R, Hq, Hkv, T, seed=topk)
@@ -103,6 +104,33 @@ def test_large_k_beyond_register_cache(topk):
     ref = oracle_of(q, K, V, Ks, Vs, sl, basis, ks, 1000, topk, 1)
     r = run_arrays(q, K, V, sl, basis, ks, 1000, topk, ref=ref)
     compare_all(r, ref, Hq // Hkv, R)
+
+
+def test_dirty_workspace_with_more_candidates_than_the_lds_cache():
+    """A workspace that is not zero at rest makes the final pass's threshold
+    guess fail; with more than 8,192 candidates its exact path then runs over
+    the candidate lists (not the LDS cache).  Same indices."""
+    flush("[edge] dirty workspace, k = 10000")
+    B, R, Hq, Hkv, T = 2, 1, 8, 2, 45001
+    q, K, V, Ks, Vs, basis, ks = random_arrays(B, R, Hq, Hkv, T, seed=10000)
+    sl = [T, 30123]
+    ref = oracle_of(q, K, V, Ks, Vs, sl, basis, ks, 1000, 10000, 1)
+    r = run_arrays(q, K, V, sl, basis, ks, 1000, 10000, ref=ref)
+    compare_all(r, ref, Hq // Hkv, R)
+    lay = r["layer"]
+    kc = torch.from_numpy(np.stack([np.stack([ref[(b, h)]["kcodes"][:lay.NB] for h in range(Hkv)])
+                                    for b in range(B)])).cuda()
+    qc = torch.from_numpy(np.stack([np.stack([ref[(b, h)]["qcode"][0] for h in range(Hkv)])
+                                    for b in range(B)])[:, None]).cuda()
+    for garbage in (0x01010101, 0x00000100):
+        lay.ws.view(torch.int32)[: lay.ws.numel() // 4].fill_(garbage)
+        lay.score(qsk=qc, S=kc)
+        lay.idx.fill_(-7)
+        lay.select()
+        torch.cuda.synchronize()
+        idx = lay.idx.cpu().numpy()
+        for (b, h), o in ref.items():
+            assert np.array_equal(idx[b, 0, h], o["idx"][0]), (garbage, b, h)
 
 
 def test_empty_and_short_rows():
