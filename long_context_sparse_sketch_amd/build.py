@@ -25,6 +25,9 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # no packed-FP32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments arrive preloaded in SGPRs (no argument
+    # fetch before a kernel's first loads)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -234,8 +234,14 @@ struct AttnLds {
 
 // One attention slot (see AttnArgs) of one segment, by a workgroup of
 // AT_THREADS threads, TILES tiles of AM_TILE entries per wave.
+// idx, seq_len, topk, R and Hkv are those of `a`, passed separately: the
+// kernel takes them as scalar arguments ahead of the struct, so that they
+// arrive preloaded in SGPRs and the first loads need not wait for the
+// argument fetch.
 template <int G, int DT, bool POOLED, int TILES>
-__device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
+__device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
+                          const int32_t *__restrict__ seq_len, int topk, int R, int Hkv,
+                          int seg, int slot, AttnLds &L) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head");
   constexpr int WAVE_ENTRIES = TILES * AM_TILE;
   constexpr int SPLIT = attn_split_entries<TILES>();
@@ -246,13 +252,10 @@ __device__ void attn_body(const AttnArgs &a, int seg, int slot, AttnLds &L) {
   const void *__restrict__ V = a.V;
   const uint16_t *__restrict__ Ks = a.Ks;
   const uint16_t *__restrict__ Vs = a.Vs;
-  const int32_t *__restrict__ seq_len = a.seq_len;
-  const int32_t *__restrict__ idx = a.idx;
   const uint16_t *__restrict__ Kp = a.Kp;
   const uint16_t *__restrict__ Vp = a.Vp;
   const float sm_log2 = a.sm_log2;
-  const int R = a.R, Hkv = a.Hkv, T_max = a.T_max, NB = a.NB, window = a.window, pool = a.pool,
-            topk = a.topk;
+  const int T_max = a.T_max, NB = a.NB, window = a.window, pool = a.pool;
   uint16_t (*s_v)[AM_TILE * VROW] = L.s_v;
   uint16_t (*s_p)[2][16 * AM_TILE] = L.s_p;
   float (*s_ml)[16][2] = L.s_ml;

@@ -30,21 +30,25 @@ __global__ __launch_bounds__(D * MP) void attn_merge_kernel(const float2 *__rest
 }
 
 template <int G, int DT, bool POOLED, int TILES>
-__global__ __launch_bounds__(AT_THREADS, 2) void attn_kernel(AttnArgs a, int slot0) {
+__global__ __launch_bounds__(AT_THREADS, 2) void attn_kernel(const int32_t *idx,
+                                                             const int32_t *seq_len, int topk,
+                                                             int R, int Hkv, AttnArgs a,
+                                                             int slot0) {
   __shared__ AttnLds lds;
-  attn_body<G, DT, POOLED, TILES>(a, blockIdx.y, slot0 + blockIdx.x, lds);
+  attn_body<G, DT, POOLED, TILES>(a, idx, seq_len, topk, R, Hkv, blockIdx.y, slot0 + blockIdx.x,
+                                  lds);
 }
 
 template <int G, int TILES>
 void dispatch_t(dim3 grid, hipStream_t st, const AttnArgs &a, int dtype, int pool, int slot0) {
   if (dtype == SKS_KV_I8)
-    attn_kernel<G, SKS_KV_I8, false, TILES><<<grid, AT_THREADS, 0, st>>>(a, slot0);
+    attn_kernel<G, SKS_KV_I8, false, TILES><<<grid, AT_THREADS, 0, st>>>(a.idx, a.seq_len, a.topk, a.R, a.Hkv, a, slot0);
   else if (dtype == SKS_KV_I4)
-    attn_kernel<G, SKS_KV_I4, false, TILES><<<grid, AT_THREADS, 0, st>>>(a, slot0);
+    attn_kernel<G, SKS_KV_I4, false, TILES><<<grid, AT_THREADS, 0, st>>>(a.idx, a.seq_len, a.topk, a.R, a.Hkv, a, slot0);
   else if (pool > 1)
-    attn_kernel<G, SKS_KV_BF16, true, TILES><<<grid, AT_THREADS, 0, st>>>(a, slot0);
+    attn_kernel<G, SKS_KV_BF16, true, TILES><<<grid, AT_THREADS, 0, st>>>(a.idx, a.seq_len, a.topk, a.R, a.Hkv, a, slot0);
   else
-    attn_kernel<G, SKS_KV_BF16, false, TILES><<<grid, AT_THREADS, 0, st>>>(a, slot0);
+    attn_kernel<G, SKS_KV_BF16, false, TILES><<<grid, AT_THREADS, 0, st>>>(a.idx, a.seq_len, a.topk, a.R, a.Hkv, a, slot0);
 }
 
 template <int G>

@@ -57,36 +57,44 @@ union FrontLds {
   SketchLds sk;
 };
 
+// The arguments read first (the pointers, the block counts and the shape
+// numbers the block's first loads need) come as scalar arguments ahead of
+// the struct, so that they arrive preloaded in SGPRs; they override the
+// struct's copies.
 template <int DT, bool CAND>
-__global__ __launch_bounds__(SK_THREADS) void front_kernel(FrontArgs f) {
+__global__ __launch_bounds__(SK_THREADS) void front_kernel(const uint16_t *q, const float *basis,
+                                                          const int32_t *seq_len, int8_t *S,
+                                                          int nq, int n_app, int samp_per_seg,
+                                                          int R, int Hkv, int Hq,
+                                                          int basis_per_head, FrontArgs f) {
   static_assert(SK_THREADS == SAMPLE_THREADS, "one workgroup size");
   __shared__ FrontLds lds;
   int blk = blockIdx.x;
-  if (blk < f.nq) {
-    block_query_sketch(f.q, f.R, f.Hq, f.Hkv, f.basis, f.basis_per_head, blk,
-                       f.qsk + (size_t)blk * RANK, f.qscale ? f.qscale + blk : nullptr, lds.sk);
+  if (blk < nq) {
+    block_query_sketch(q, R, Hq, Hkv, basis, basis_per_head, blk, f.qsk + (size_t)blk * RANK,
+                       f.qscale ? f.qscale + blk : nullptr, lds.sk);
     return;
   }
-  blk -= f.nq;
-  if (blk < f.n_app) {
-    block_key_row<DT>(f.K, f.V, f.Ks, f.Kh, f.Ksh, f.W_hot, f.seq_len, f.basis,
-                      f.basis_per_head, f.key_scale, f.Hkv, f.T_max, f.R, f.NB, f.pool, 1, 0, 0,
-                      f.S, f.Kp, f.Vp, blk / f.app_rows, blk % f.app_rows, lds.sk);
+  blk -= nq;
+  if (blk < n_app) {
+    block_key_row<DT>(f.K, f.V, f.Ks, f.Kh, f.Ksh, f.W_hot, seq_len, basis, basis_per_head,
+                      f.key_scale, Hkv, f.T_max, R, f.NB, f.pool, 1, 0, 0, S, f.Kp, f.Vp,
+                      blk / f.app_rows, blk % f.app_rows, lds.sk);
     return;
   }
-  blk -= f.n_app;
+  blk -= n_app;
   if (CAND && blk < f.n_samp) {
-    const int seg = blk / f.samp_per_seg;
-    const SegGeom g = seg_geom(seg, f.seq_len, f.R, f.Hkv, f.T_max, f.window, f.pool, f.topk);
+    const int seg = blk / samp_per_seg;
+    const SegGeom g = seg_geom(seg, seq_len, R, Hkv, f.T_max, f.window, f.pool, f.topk);
     if (g.k_eff >= g.n_far) return;             // uniform: no selection needed
     const int m = (g.n_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
-    const int j0 = (blk % f.samp_per_seg) * SAMPLE_WG_ROWS;
+    const int j0 = (blk % samp_per_seg) * SAMPLE_WG_ROWS;
     if (j0 >= m) return;
     int4 sv[SAMPLE_UNROLL];
-    sample_load(f.S, ((size_t)g.b * f.Hkv + g.h) * f.NB, j0, m, sv);
+    sample_load(S, ((size_t)g.b * Hkv + g.h) * f.NB, j0, m, sv);
     for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS) lds.samp.lh[k] = 0;
-    block_query_sketch(f.q, f.R, f.Hq, f.Hkv, f.basis, f.basis_per_head, seg, lds.samp.qcode,
-                       nullptr, lds.samp.sk);
+    block_query_sketch(q, R, Hq, Hkv, basis, basis_per_head, seg, lds.samp.qcode, nullptr,
+                       lds.samp.sk);
     __syncthreads();
     const int4 qv = reinterpret_cast<const int4 *>(lds.samp.qcode)[threadIdx.x & 3];
     sample_bins(sv, qv, j0, m, lds.samp.lh);
@@ -98,9 +106,13 @@ __global__ __launch_bounds__(SK_THREADS) void front_kernel(FrontArgs f) {
 template <int DT>
 void launch_front_t(const FrontArgs &f, bool cand, int grid, hipStream_t st) {
   if (cand)
-    front_kernel<DT, true><<<grid, SK_THREADS, 0, st>>>(f);
+    front_kernel<DT, true><<<grid, SK_THREADS, 0, st>>>(f.q, f.basis, f.seq_len, f.S, f.nq,
+                                                         f.n_app, f.samp_per_seg, f.R, f.Hkv,
+                                                         f.Hq, f.basis_per_head, f);
   else
-    front_kernel<DT, false><<<grid, SK_THREADS, 0, st>>>(f);
+    front_kernel<DT, false><<<grid, SK_THREADS, 0, st>>>(f.q, f.basis, f.seq_len, f.S, f.nq,
+                                                          f.n_app, f.samp_per_seg, f.R, f.Hkv,
+                                                          f.Hq, f.basis_per_head, f);
 }
 
 }  // namespace

@@ -243,9 +243,17 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void topk_sample_kernel(
   sample_flush(lh, hsamp + (size_t)seg * HIST1_BINS);
 }
 
-__global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(FinalArgs a) {
+__global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
+    const int32_t *cnt, const int32_t *thr, const int32_t *seq_len, int32_t *hist1,
+    int32_t *hist2, int n_sub_max, int R, int Hkv, FinalArgs a) {
   __shared__ FinalLds<TF_THREADS, TK_MAX_SUBS, true> lds;
-  final_body<TF_THREADS, TK_MAX_SUBS, true>(a, blockIdx.x, lds);
+  const FinalLead ld{cnt, thr, seq_len, hist1, hist2, n_sub_max, R, Hkv};
+  final_body<TF_THREADS, TK_MAX_SUBS, true>(a, ld, blockIdx.x, lds);
+}
+
+void launch_final(const FinalArgs &a, int nseg, hipStream_t st) {
+  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(a.cnt, a.thr, a.seq_len, a.hist1, a.hist2,
+                                                 a.n_sub_max, a.R, a.Hkv, a);
 }
 
 }  // namespace
@@ -327,7 +335,7 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
     hipError_t e = launch_topk_filter(scores, seq_len, s, hist_ready, w, st);
     if (e != hipSuccess) return e;
   }
-  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(a);
+  launch_final(a, nseg, st);
   return hipGetLastError();
 }
 
@@ -363,7 +371,7 @@ hipError_t launch_topk_cand(const int8_t *qsk, const int8_t *S, int32_t *scores,
   a.qsk = qsk;
   a.S = S;
   a.rescore = scores;
-  topk_final_kernel<<<nseg, TF_THREADS, 0, st>>>(a);
+  launch_final(a, nseg, st);
   return hipGetLastError();
 }
 

@@ -15,6 +15,10 @@ constexpr int FILTER_ITERS = TK_SUB / 64;          // 16 loads in flight per lan
 constexpr int HIST2_DIRECT_MAX = 4096;             // level-2 histogram built when bin b1 is this small
 static_assert(TK_CHUNK == TK_SUB * (TK_THREADS / 64), "one sub-chunk per wave");
 static_assert(TF_REGS < 65536 && TF_CACHE <= TF_REGS, "packed 16-bit counts in the emission scan");
+// A sub-list start mark packs (sub-list + 1) << MK_SHIFT | start slot: marks
+// increase with the slot, and the running maximum gives both at once.
+constexpr int MK_SHIFT = 13;
+static_assert(TF_REGS <= (1 << MK_SHIFT) && TK_MAX_SUBS < (1 << (30 - MK_SHIFT)), "packed marks");
 
 struct SegGeom {
   int b, i, h, n_far, k_eff;
@@ -174,15 +178,13 @@ struct FinalArgs {
 // and (LDS_CACHE) the candidates cached for the exact fallback path.
 template <int NT, int MAXSUB, bool LDS_CACHE>
 struct FinalLds {
-  static constexpr int PERT = TF_REGS / NT;
   int h1[hpad_size<HIST1_BINS>()];
   int h2[hpad_size<HIST2_BINS>()];
   int pre[MAXSUB + 1];
   union {
-    // sub-list start marks, one int per register slot padded by one every
-    // PERT so that a thread's PERT consecutive slots fall in distinct banks
-    // across the wave; read only before the candidates reach the registers
-    int marks[TF_REGS + TF_REGS / PERT];
+    // sub-list start marks (packed, see MK_SHIFT), one int per candidate
+    // slot; read only before the candidates reach the registers
+    int marks[TF_REGS];
     // the candidates for the exact path, written only after that
     int2 cache[LDS_CACHE ? TF_CACHE : 1];
   };
@@ -190,21 +192,31 @@ struct FinalLds {
   int res[6];
 };
 
+// The arguments of FinalArgs that the pass reads first, passed to the kernel
+// as scalar arguments ahead of the struct so that they arrive preloaded in
+// SGPRs and the first loads need not wait for the argument fetch.
+struct FinalLead {
+  const int32_t *cnt, *thr, *seq_len;
+  int32_t *hist1, *hist2;
+  int n_sub_max, R, Hkv;
+};
+
 // The final select pass of one segment by a workgroup of NT threads.
 template <int NT, int MAXSUB, bool LDS_CACHE>
-__device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS_CACHE> &L) {
+__device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
+                           FinalLds<NT, MAXSUB, LDS_CACHE> &L) {
   constexpr int TF_THREADS = NT;
   constexpr int TF_WAVES = NT / 64;
   constexpr int TF_PERT = TF_REGS / NT;
   static_assert(TF_PERT * NT == TF_REGS, "slots per thread");
   const int32_t *scores = a.scores;           // written by this pass when rescoring
-  const int32_t *__restrict__ seq_len = a.seq_len;
-  int32_t *__restrict__ hist1 = a.hist1;
-  int32_t *__restrict__ hist2 = a.hist2;
-  const int32_t *__restrict__ thr = a.thr;
-  const int32_t *__restrict__ cnt = a.cnt;
+  const int32_t *__restrict__ seq_len = ld.seq_len;
+  int32_t *__restrict__ hist1 = ld.hist1;
+  int32_t *__restrict__ hist2 = ld.hist2;
+  const int32_t *__restrict__ thr = ld.thr;
+  const int32_t *__restrict__ cnt = ld.cnt;
   const int2 *__restrict__ cand = a.cand;
-  const int n_sub_max = a.n_sub_max, R = a.R, Hkv = a.Hkv, T_max = a.T_max, NB = a.NB,
+  const int n_sub_max = ld.n_sub_max, R = ld.R, Hkv = ld.Hkv, T_max = a.T_max, NB = a.NB,
             window = a.window, pool = a.pool, topk = a.topk;
   int32_t *__restrict__ idx = a.idx;
   int32_t *__restrict__ n_sel = a.n_sel;
@@ -214,9 +226,13 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int32_t *gc = cnt + (size_t)seg * n_sub_max;
   int32_t *gh2 = hist2 + (size_t)seg * HIST2_BINS;
-  // loads first: the first round of sub-list counts, the threshold record
-  // and (wave 0) the level-2 histogram, lane l holding bins [16l, 16l+16)
-  const int cv0 = threadIdx.x < n_sub_max ? gc[threadIdx.x] : 0;
+  // loads first: every wave the first WL_SUBS sub-list counts (lane l those
+  // of sub-lists 4l .. 4l + 3), the threshold record and (wave 0) the
+  // level-2 histogram, lane l holding bins [16l, 16l+16)
+  constexpr int WL_SUBS = 4 * 64;
+  int cv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) cv[u] = 4 * lane + u < n_sub_max ? gc[4 * lane + u] : 0;
   const int4 th = reinterpret_cast<const int4 *>(thr)[seg];   // (b1, above b1, valid, in b1)
   constexpr int H2_PER = HIST2_BINS / 64;
   constexpr int H1_PER = HIST1_BINS / 64;
@@ -248,27 +264,33 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
       hv[4 * k + 3] = w.w;
     }
   }
-#pragma unroll
-  for (int q = 0; q < TF_PERT; ++q) marks[threadIdx.x * (TF_PERT + 1) + q] = 0;   // no mark
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   int32_t *out = idx + (size_t)seg * topk;
-  // the segment's level-1 histogram returns to zero (when wave 0 has read
-  // it, by the lanes that read it)
-  if (h1_ready) {
+  // The segment's histograms return to zero, and n_sel is written, on every
+  // way out.  These stores come last: a wave that waits for its loads waits
+  // for its earlier stores too, so stores issued here first would delay
+  // every load that follows them.
+  auto finish = [&]() {
+    if (h1_ready) {
+      if (wave == 0) {                           // the lanes that read it
+#pragma unroll
+        for (int k = 0; k < H1_PER / 4; ++k)
+          reinterpret_cast<int4 *>(gh1 + lane * H1_PER)[k] = make_int4(0, 0, 0, 0);
+      }
+    } else {
+      for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh1[k] = 0;
+    }
     if (wave == 0) {
 #pragma unroll
-      for (int k = 0; k < H1_PER / 4; ++k)
-        reinterpret_cast<int4 *>(gh1 + lane * H1_PER)[k] = make_int4(0, 0, 0, 0);
+      for (int k = 0; k < H2_PER / 4; ++k)
+        reinterpret_cast<int4 *>(gh2 + lane * H2_PER)[k] = make_int4(0, 0, 0, 0);
     }
-  } else {
-    for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh1[k] = 0;
-  }
-  if (threadIdx.x == 0 && n_sel) n_sel[seg] = g.k_eff;
-  if (cmode)
-    for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) a.hsamp[(size_t)seg * HIST1_BINS + k] = 0;
+    if (cmode)
+      for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) a.hsamp[(size_t)seg * HIST1_BINS + k] = 0;
+    if (threadIdx.x == 0 && n_sel) n_sel[seg] = g.k_eff;
+  };
 
-  // wave 0: the threshold guess T from the level-2 histogram (-1: none),
-  // then that histogram returns to zero (its values are consumed)
+  // wave 0: the threshold guess T from the level-2 histogram (-1: none)
   if (wave == 0) {
     int T = -1;
     if (!skip && !cmode && g.k_eff < g.n_far && th.z && th.w >= 0 && th.w <= HIST2_DIRECT_MAX &&
@@ -279,34 +301,57 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
       if (valid) T = (th.x << HIST2_BITS) | b2;
     }
     if (lane == 0) res[5] = T;
-#pragma unroll
-    for (int k = 0; k < H2_PER / 4; ++k)
-      reinterpret_cast<int4 *>(gh2 + lane * H2_PER)[k] = make_int4(0, 0, 0, 0);
   }
   if (g.k_eff >= g.n_far) {                      // every far entry is selected
     for (int j = threadIdx.x; j < topk; j += TF_THREADS) out[j] = j < g.n_far ? j : -1;
+    finish();
     return;
   }
 
-  // candidate list: exclusive prefix over the sub-list counts; every
-  // non-empty sub-list also marks its first slot with its number + 1
-  // (without a filter pass the candidates are the far entries themselves)
+  // Candidate list: sub-list s starts at slot pre[s], the exclusive prefix of
+  // the counts (without a filter pass the candidates are the far entries
+  // themselves).  Up to WL_SUBS sub-lists every wave computes the prefix from
+  // its own registers and writes the (same) pre[] values, which it then reads
+  // back itself: no workgroup barrier.  Beyond, a block-wide scan in rounds.
   const int n_sub = (g.n_far + TK_SUB - 1) / TK_SUB;
+  const bool wave_local = !skip && n_sub <= WL_SUBS;   // uniform
   int carry = 0;
-  for (int base = 0; base < (skip ? 0 : n_sub); base += TF_THREADS) {
-    const int sidx = base + threadIdx.x;
-    const int v = sidx < n_sub ? (base == 0 ? cv0 : gc[sidx]) : 0;
-    int tot;
-    const int incl = block_incl_scan<TF_WAVES, true>(v, sc_pre, tot);
-    const int start = carry + incl - v;
-    if (sidx < n_sub) {
-      pre[sidx] = start;
-      if (v > 0 && start < TF_REGS) marks[start + start / TF_PERT] = sidx + 1;
+  int st[4];                                     // wave-local: starts of sub-lists 4 lane + u
+  if (wave_local) {
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      cv[u] = 4 * lane + u < n_sub ? cv[u] : 0;
+      st[u] = sum;
+      sum += cv[u];
     }
-    carry += tot;
+    const int incl = wave_incl_add(sum);
+    carry = __builtin_amdgcn_readlane(incl, 63);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      st[u] += incl - sum;
+      if (4 * lane + u < n_sub) pre[4 * lane + u] = st[u];
+    }
+    if (lane == 0) pre[n_sub] = carry;
+  } else {
+    // every non-empty sub-list marks its first slot
+#pragma unroll
+    for (int q = 0; q < TF_PERT; ++q) marks[q * TF_THREADS + threadIdx.x] = 0;   // no mark
+    for (int base = 0; base < (skip ? 0 : n_sub); base += TF_THREADS) {
+      const int sidx = base + threadIdx.x;
+      const int v = sidx < n_sub ? gc[sidx] : 0;
+      int tot;
+      const int incl = block_incl_scan<TF_WAVES, true>(v, sc_pre, tot);
+      const int start = carry + incl - v;
+      if (sidx < n_sub) {
+        pre[sidx] = start;
+        if (v > 0 && start < TF_REGS) marks[start] = ((sidx + 1) << MK_SHIFT) | start;
+      }
+      carry += tot;
+    }
+    if (threadIdx.x == 0) pre[n_sub] = carry;
+    __syncthreads();
   }
-  if (threadIdx.x == 0) pre[n_sub] = carry;
-  __syncthreads();
   // Fewer candidates than k means the filter's histogram was not one of these
   // scores (candidate mode: the estimate lay above the k-th largest key):
   // select from the raw scores instead.
@@ -347,35 +392,74 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
   const int32_t *srow = (cmode ? a.rescore : scores) + (size_t)seg * NB;
   const bool in_regs = !raw && m <= TF_REGS;    // the candidates fit the threads' registers
   const bool cached = LDS_CACHE && in_regs && m <= TF_CACHE;   // ... and the exact path's LDS
-  const int o0 = threadIdx.x * TF_PERT;          // this thread's slots [o0, o0 + TF_PERT)
-
   if (in_regs) {
+    // Wave-major slots: wave w holds candidates [w * 64 nq, (w + 1) * 64 nq)
+    // and its register q the 64 consecutive ones from w * 64 nq + 64 q, so
+    // that every load reads 64 consecutive entries.  Slots at or past m hold
+    // the key -1, which no count or histogram below takes.
+    const int nq = (m + 64 * TF_WAVES - 1) / (64 * TF_WAVES);   // registers in use, <= TF_PERT
+    const int slot0 = wave * nq * 64 + lane;                      // slot of register 0
     int2 c[TF_PERT];
     if (skip) {
       // the far entries themselves, in index order
 #pragma unroll
       for (int q = 0; q < TF_PERT; ++q) {
-        const int o = min(o0 + q, m - 1);
-        c[q] = make_int2(o, biased_key(srow[o]));
+        const int o = slot0 + 64 * q;
+        c[q] = q < nq && o < m ? make_int2(o, biased_key(srow[o])) : make_int2(0, -1);
       }
     } else {
-      // The sub-list holding slot o is the last mark at or before o: a running
-      // maximum over the marks of this thread's slots, then across the block.
-      int mk[TF_PERT];
-      int run = 0;
+      // The sub-list holding slot o, and its start, are those of the last
+      // mark at or before o: the running maximum of the marks over the slots.
+      int run = 0;                               // uniform: the last mark before
+      if (wave_local) {
+        // this wave's marks, written and read by it alone: those of the
+        // sub-lists that start in its slot range, and as `run` the sub-list
+        // holding its first slot (the last non-empty one starting at or before)
+        const int begin = wave * nq * 64, end = begin + nq * 64;
 #pragma unroll
-      for (int q = 0; q < TF_PERT; ++q) {
-        run = max(run, marks[threadIdx.x * (TF_PERT + 1) + q]);
-        mk[q] = run;
+        for (int q = 0; q < TF_PERT; ++q)
+          if (q < nq) marks[slot0 + 64 * q] = 0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        int best = -1;                           // the last such mark
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int mark = ((4 * lane + u + 1) << MK_SHIFT) | st[u];
+          if (cv[u] > 0 && st[u] >= begin && st[u] < end) marks[st[u]] = mark;
+          if (cv[u] > 0 && st[u] <= begin) best = mark;
+        }
+        const unsigned long long bb = __ballot(best >= 0);
+        if (bb) run = __builtin_amdgcn_readlane(best, 63 - __clzll((long long)bb));
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
       }
-      const int before = block_excl_max<TF_WAVES>(run, sc_own);
+      int mk[TF_PERT];
 #pragma unroll
       for (int q = 0; q < TF_PERT; ++q) {
-        const int o = min(o0 + q, m - 1);
-        const int s = min(max(max(before, mk[q]), 1) - 1, n_sub - 1);   // clamped: always in bounds
-        c[q] = cseg[(size_t)s * TK_SUB + min(max(o - pre[s], 0), TK_SUB - 1)];
+        mk[q] = run;
+        if (q < nq) {                            // uniform
+          mk[q] = max(wave_incl_max(marks[slot0 + 64 * q]), run);
+          run = __builtin_amdgcn_readlane(mk[q], 63);
+        }
+      }
+      int before = 0;
+      if (!wave_local) {
+        // the marks of the earlier waves' ranges
+        if (lane == 0) sc_own[wave] = run;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < TF_WAVES; ++w) before = max(before, w < wave ? sc_own[w] : 0);
+      }
+#pragma unroll
+      for (int q = 0; q < TF_PERT; ++q) {
+        const int o = slot0 + 64 * q;
+        const int pk = max(before, mk[q]);
+        const int s = min(max((pk >> MK_SHIFT) - 1, 0), n_sub - 1);   // clamped: always in bounds
+        const int off = min(max(o - (pk & ((1 << MK_SHIFT) - 1)), 0), TK_SUB - 1);
+        c[q] = q < nq && o < m ? cseg[(size_t)s * TK_SUB + off] : make_int2(0, -1);
       }
     }
+    if (!h1_ready) __syncthreads();              // res[5] (wave 0) and every wave's marks read
     if (h1_ready) {
       // Guess T without a filter pass: bin b1 from the score pass's level-1
       // histogram, then a level-2 histogram of the low bits of the keys in
@@ -401,7 +485,7 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
       if (b1 >= 0) {
 #pragma unroll
         for (int q = 0; q < TF_PERT; ++q)
-          if (o0 + q < m && (c[q].y >> HIST2_BITS) == b1)
+          if ((c[q].y >> HIST2_BITS) == b1)
             atomicAdd(&h2[hpad<HIST2_BINS>(c[q].y & (HIST2_BINS - 1))], 1);
       }
       __syncthreads();
@@ -422,40 +506,46 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
       // Count, from the data, the candidates above T and equal to T.  Every
       // element with key >= T is a candidate (its bin is >= b1), so T is the
       // k-th largest key exactly when above < k <= above + equal.
-      int gt = 0, tie = 0;
+      int gt = 0, tie = 0;                       // this wave's, uniform
 #pragma unroll
       for (int q = 0; q < TF_PERT; ++q) {
-        const bool in = o0 + q < m;
-        gt += in && c[q].y > T;
-        tie += in && c[q].y == T;
+        gt += __popcll(__ballot(c[q].y > T));
+        tie += __popcll(__ballot(c[q].y == T));
       }
-      const int packed = gt | (tie << 16);
-      int tot;
-      const int ex = block_incl_scan<TF_WAVES, false>(packed, sc_cnt, tot) - packed;
-      const int gt_tot = tot & 0xffff, tie_tot = tot >> 16;
+      if (lane == 0) sc_cnt[wave] = gt | (tie << 16);
+      __syncthreads();
+      int gt_tot = 0, tie_tot = 0, gt_run = 0, tie_run = 0;
+#pragma unroll
+      for (int w = 0; w < TF_WAVES; ++w) {
+        const int v = sc_cnt[w];
+        gt_tot += v & 0xffff;
+        tie_tot += v >> 16;
+        gt_run += w < wave ? v & 0xffff : 0;
+        tie_run += w < wave ? v >> 16 : 0;
+      }
       if (gt_tot < g.k_eff && gt_tot + tie_tot >= g.k_eff) {      // uniform
         const int need = g.k_eff - gt_tot;     // ties at T to take, lowest index first
-        int gt_before = ex & 0xffff, tie_before = ex >> 16;
+        const unsigned long long lt = (1ull << lane) - 1ull;
 #pragma unroll
         for (int q = 0; q < TF_PERT; ++q) {
-          const bool in = o0 + q < m;
-          const bool is_gt = in && c[q].y > T, is_tie = in && c[q].y == T;
-          const bool sel = is_gt || (is_tie && tie_before < need);
-          const int pos = gt_before + min(tie_before, need);
-          if (sel) out[pos] = c[q].x;
-          gt_before += is_gt;
-          tie_before += is_tie;
+          const bool is_gt = c[q].y > T, is_tie = c[q].y == T;
+          const unsigned long long gb = __ballot(is_gt), tb = __ballot(is_tie);
+          const int gt_before = gt_run + __popcll(gb & lt), tie_before = tie_run + __popcll(tb & lt);
+          if (is_gt || (is_tie && tie_before < need)) out[gt_before + min(tie_before, need)] = c[q].x;
+          gt_run += __popcll(gb);
+          tie_run += __popcll(tb);
         }
         for (int j = g.k_eff + threadIdx.x; j < topk; j += TF_THREADS) out[j] = -1;
+        finish();
         return;
       }
     }
     // the guess did not hold: keep the candidates in LDS for the exact path
-    // (the marks they overwrite were last read before block_excl_max's barrier)
+    // (the marks they overwrite were last read before the barrier above)
     if (cached) {
 #pragma unroll
       for (int q = 0; q < TF_PERT; ++q)
-        if (o0 + q < m) cache[o0 + q] = c[q];
+        if (c[q].y >= 0) cache[slot0 + 64 * q] = c[q];
     }
   }
 
@@ -556,6 +646,7 @@ __device__ void final_body(const FinalArgs &a, int seg, FinalLds<NT, MAXSUB, LDS
     run_tie += tot >> 16;
   }
   for (int j = g.k_eff + threadIdx.x; j < topk; j += TF_THREADS) out[j] = -1;
+  finish();
 }
 
 
