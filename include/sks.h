@@ -222,10 +222,10 @@ int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p
  *   2. derives from that histogram an estimate E of each (b, i, h)'s k-th
  *      largest biased score (score + 2^20), set low enough that with high
  *      probability at least k entries reach it; scores every far token as
- *      sks_sketch_score does, accumulates the level-1 histogram into ws as
- *      sks_sketch_score(ws) does, and keeps in ws, instead of the scores,
- *      every far entry whose biased score is at least E (index and biased
- *      score, ascending).
+ *      sks_sketch_score does and keeps in ws, instead of the scores, every
+ *      far entry whose biased score is at least E (index and biased score,
+ *      ascending), and accumulates into ws the level-1 histogram of the
+ *      kept entries only.
  * sks_topk_select_candidates then selects as sks_topk_select, from those
  * entries.  Where fewer than k entries reached E, it recomputes that
  * segment's scores from qsk and S into `scores` ([B][R][Hkv][NB] int32,

@@ -19,13 +19,16 @@
 // chunk), so that the top-k filter reads only the chunks that can hold a
 // candidate.
 //
-// In candidate mode (CAND, with HIST) no score is stored: each row keeps,
+// In candidate mode (CAND, without HIST) no score is stored: each row keeps,
 // in its chunk's candidate list of the selection workspace, the entries
 // whose biased score reaches the row's estimate E, as (index, biased score)
 // in index order, and the list's length.  Every workgroup derives E itself
 // from the segment's sample histogram (built beforehand by the selection's
 // sample pass; see k_topk.hip for the rule), so every workgroup of a segment
-// finds the same E.  The final selection pass then needs no filter pass.
+// finds the same E.  The final selection pass then needs no filter pass and
+// no histogram from this pass: it counts the candidates' level-1 bins itself
+// (adding a few bins per workgroup into one histogram per segment, from
+// every workgroup, cost this pass 3 us at 250K in same-address atomics).
 #include "sks_internal.h"
 
 namespace sks {
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     int2 *__restrict__ cand, int32_t *__restrict__ cnt, int force) {
   static_assert(SCORE_CHUNK == TK_SUB, "one chunk maximum per top-k sub-list");
   static_assert(SCORE_CHUNK == 4 * SC_THREADS, "candidate compaction: 4 rounds of 64 per wave");
-  static_assert(!CAND || HIST, "candidate mode builds the histogram too");
+  static_assert(!(CAND && HIST), "candidate mode builds no histogram");
   __shared__ int lh[HIST ? R * HIST1_BINS : 1];
   __shared__ int lmax[HIST ? R * (SC_THREADS / 64) : 1];
   __shared__ int gcnt[CAND ? R * 16 : 1];                // candidates per 64-token group
@@ -73,15 +76,15 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int quad = lane >> 2, part = lane & 3;
   // per-row far counts (rows differ by one token each); a row whose top-k
-  // takes everything needs no histogram
+  // takes everything needs no histogram and no candidates
   int nf[R], ke[R];
-  bool need_hist[R];
+  bool need_sel[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const RowGeom rg = row_geom(L0, i, window, pool, topk);
     nf[i] = rg.n_far;
     ke[i] = rg.k_eff;
-    need_hist[i] = HIST && rg.k_eff < rg.n_far;
+    need_sel[i] = rg.k_eff < rg.n_far;
   }
   if (HIST) {
     for (int k = threadIdx.x; k < R * HIST1_BINS; k += SC_THREADS) lh[k] = 0;
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
         lsc[i * SCORE_CHUNK + (t_lo - c0)] = lo;
         lsc[i * SCORE_CHUNK + (t_hi - c0)] = hi;
       }
-      if (HIST && need_hist[i]) {
+      if (HIST && need_sel[i]) {
         const int klo = biased_key(lo), khi = biased_key(hi);
         if (t_lo < nf[i]) {
           atomicAdd(&lh[i * HIST1_BINS + (klo >> HIST2_BITS)], 1);
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     for (int i = 0; i < R; ++i) {
       const int E = e_lds[i];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) cm[i][k] = __ballot(need_hist[i] && ck[i][k] >= E);
+      for (int k = 0; k < 4; ++k) cm[i][k] = __ballot(need_sel[i] && ck[i][k] >= E);
     }
     if (lane == 0) {
       // 64-token groups in token order: g = step * 8 + wave * 2 + (lo, hi)
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     const unsigned long long before_q = (1ull << (4 * quad)) - 1ull;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      if (!need_hist[i]) continue;                 // uniform: the row selects everything
+      if (!need_sel[i]) continue;                  // uniform: the row selects everything
       const size_t seg = (size_t)(b * R + i) * Hkv + h;
       int2 *dst = cand + (seg * n_sub_max + blockIdx.x) * TK_SUB;
       int tot = 0;
@@ -334,8 +337,8 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
 #define SKS_SCORE_CASE(RR)                                                                     \
   case RR:                                                                                     \
     if (cand)                                                                                  \
-      score_kernel<RR, true, true><<<grid, SC_THREADS, 0, st>>>(                               \
-          qsk, S, seq_len, nullptr, hist1, nullptr, n_sub_max, s.Hkv, s.T_max, s.NB, s.window, \
+      score_kernel<RR, false, true><<<grid, SC_THREADS, 0, st>>>(                              \
+          qsk, S, seq_len, nullptr, nullptr, nullptr, n_sub_max, s.Hkv, s.T_max, s.NB, s.window, \
           s.pool, s.topk, w->hsamp, w->cand, w->cnt, force);                                   \
     else if (hist1)                                                                            \
       score_kernel<RR, true, false><<<grid, SC_THREADS, 0, st>>>(                              \

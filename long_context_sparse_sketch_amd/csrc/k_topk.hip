@@ -37,13 +37,13 @@
 //     lowest key of the sample bin holding the rho-th largest sampled key,
 //     rho = 2 k' + 8 where k' is the expected number of sampled entries among
 //     the k largest, keeps every far entry with key >= E in the candidate
-//     lists (see k_score.hip) and builds the level-1 histogram as usual.  E
-//     is a heuristic: only the time depends on it.
-//   final: as above, with the threshold guess taken from the level-1
-//     histogram and a level-2 histogram of the bin-b1 candidates.  If at
-//     least k entries reach E, the k largest are all candidates and the
-//     selection is exact; otherwise E was too high and the segment's scores
-//     are recomputed from the sketches and selected from in full.
+//     lists (see k_score.hip) and counts those candidates (only) into the
+//     level-1 histogram.  E is a heuristic: only the time depends on it.
+//   final: as above, with the threshold guess taken from the candidates'
+//     level-1 histogram and a level-2 histogram of the bin-b1 candidates.
+//     If at least k entries reach E, the k largest are all candidates and
+//     the selection is exact; otherwise E was too high and the segment's
+//     scores are recomputed from the sketches and selected from in full.
 #include "topk_body.h"
 
 namespace sks {

@@ -109,6 +109,48 @@ __device__ int wave_threshold_bin_valid(const int *hist, int need, int n, int &a
   return wave_threshold_regs<PER>(v, need, n, above, valid);
 }
 
+// Threshold search by all NW waves of the workgroup over a padded LDS
+// histogram of HIST1_BINS bins, wave w taking bins [w B, (w + 1) B), two per
+// lane: the bin b holding the need-th largest of n counted keys.  Writes
+// res[0] = b (-1: none, or the histogram's total is not n), res[1] = need
+// minus the count above b, res[2] = the count in b.  `scratch` holds NW ints.
+// Contains two __syncthreads().
+template <int NW>
+__device__ void block_threshold_bin(const int *hist, int need, int n, int *scratch, int *res) {
+  constexpr int B = HIST1_BINS / NW;
+  static_assert(B == 128, "two bins per lane");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b0 = wave * B + 2 * lane;            // this lane's bins b0 (lower), b0 + 1
+  const int v0 = hist[hpad<HIST1_BINS>(b0)], v1 = hist[hpad<HIST1_BINS>(b0 + 1)];
+  const bool bad = __ballot(v0 < 0 || v1 < 0 || v0 > n || v1 > n) != 0;
+  const int sum = min(v0 + v1, n + 1);
+  const int incl = wave_incl_add_sat(sum, n + 1);
+  const int wtot = __builtin_amdgcn_readlane(incl, 63);
+  if (lane == 63) scratch[wave] = bad ? n + 1 : wtot;
+  if (threadIdx.x == 0) res[0] = -1;
+  __syncthreads();
+  int above = 0, tot = 0;                        // keys in the waves above, and in all
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = scratch[w];
+    above = min(above + (w > wave ? t : 0), n + 1);
+    tot = min(tot + t, n + 1);
+  }
+  above = min(above + (wtot - incl), n + 1);     // ... and in the lanes above this one
+  if (tot == n) {
+    if (above < need && above + v1 >= need) {
+      res[0] = b0 + 1;
+      res[1] = need - above;
+      res[2] = v1;
+    } else if (above + v1 < need && above + v1 + v0 >= need) {
+      res[0] = b0;
+      res[1] = need - above - v1;
+      res[2] = v0;
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- sample pass
 // Candidate mode's sample: sampled rows j * SAMPLE_STRIDE of a segment's far
 // region, j in [j0, j0 + SAMPLE_WG_ROWS), scored against the segment's query
@@ -237,7 +279,8 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
   constexpr int H2_PER = HIST2_BINS / 64;
   constexpr int H1_PER = HIST1_BINS / 64;
   const bool skip = a.skip, cmode = a.cand_mode;   // uniform
-  const bool h1_ready = (skip && a.h1_ready) || cmode;   // this step's level-1 histogram
+  // the score pass built this step's level-1 histogram
+  const bool h1_ready = skip && a.h1_ready;
   int32_t *gh1 = hist1 + (size_t)seg * HIST1_BINS;
   int hv[H2_PER];
   int h1v[H1_PER];
@@ -254,7 +297,7 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
     }
 #pragma unroll
     for (int k = 0; k < H2_PER; ++k) hv[k] = 0;
-  } else if (wave == 0) {
+  } else if (wave == 0 && !cmode) {
 #pragma unroll
     for (int k = 0; k < H2_PER / 4; ++k) {
       const int4 w = reinterpret_cast<const int4 *>(gh2 + lane * H2_PER)[k];
@@ -264,6 +307,9 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
       hv[4 * k + 3] = w.w;
     }
   }
+  // candidate mode: the level-1 histogram of the candidates, built in LDS
+  if (cmode)
+    for (int k = threadIdx.x; k < hpad_size<HIST1_BINS>(); k += TF_THREADS) h1[k] = 0;
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   int32_t *out = idx + (size_t)seg * topk;
   // The segment's histograms return to zero, and n_sel is written, on every
@@ -459,28 +505,37 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
         c[q] = q < nq && o < m ? cseg[(size_t)s * TK_SUB + off] : make_int2(0, -1);
       }
     }
-    if (!h1_ready) __syncthreads();              // res[5] (wave 0) and every wave's marks read
-    if (h1_ready) {
-      // Guess T without a filter pass: bin b1 from the score pass's level-1
-      // histogram, then a level-2 histogram of the low bits of the keys in
-      // bin b1, which sit in registers.  The counts below check the guess
-      // against the data before it is used.
+    if (!h1_ready) __syncthreads();              // res[5] (wave 0), h1 zeroed, every wave's marks read
+    if (h1_ready || cmode) {
+      // Guess T without a filter pass: bin b1 from a level-1 histogram (the
+      // score pass's, or in candidate mode that of the candidates, counted
+      // here and searched by all waves), then a level-2 histogram of the low
+      // bits of the keys in bin b1, which sit in registers.  The counts below
+      // check the guess against the data before it is used.
       for (int k = threadIdx.x; k < hpad_size<HIST2_BINS>(); k += TF_THREADS) h2[k] = 0;
-      if (wave == 0) {
-        int above;
-        bool valid;
-        const int b1 = wave_threshold_regs<H1_PER>(h1v, g.k_eff, g.n_far, above, valid);
-        int mine = 0;
+      if (cmode) {
 #pragma unroll
-        for (int k = 0; k < H1_PER; ++k) mine = (k == (b1 & (H1_PER - 1))) ? h1v[k] : mine;
-        const int inb1 = __shfl(mine, b1 / H1_PER);
-        if (lane == 0) {
-          res[0] = valid ? b1 : -1;
-          res[1] = g.k_eff - above;
-          res[2] = inb1;
+        for (int q = 0; q < TF_PERT; ++q)
+          if (c[q].y >= 0) atomicAdd(&h1[hpad<HIST1_BINS>(c[q].y >> HIST2_BITS)], 1);
+        __syncthreads();
+        block_threshold_bin<TF_WAVES>(h1, g.k_eff, m, sc_pre, res);   // ends with a barrier
+      } else {
+        if (wave == 0) {
+          int above;
+          bool valid;
+          const int b1 = wave_threshold_regs<H1_PER>(h1v, g.k_eff, g.n_far, above, valid);
+          int mine = 0;
+#pragma unroll
+          for (int k = 0; k < H1_PER; ++k) mine = (k == (b1 & (H1_PER - 1))) ? h1v[k] : mine;
+          const int inb1 = __shfl(mine, b1 / H1_PER);
+          if (lane == 0) {
+            res[0] = valid ? b1 : -1;
+            res[1] = g.k_eff - above;
+            res[2] = inb1;
+          }
         }
+        __syncthreads();
       }
-      __syncthreads();
       const int b1 = res[0];
       if (b1 >= 0) {
 #pragma unroll
