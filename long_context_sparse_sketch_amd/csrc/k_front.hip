@@ -3,19 +3,20 @@
 // x 250K context, concurrently, on two 3090s": build the sketch, score every
 // token, pick the top ~2K -- graph-safe):
 //
-//   [0, nq)               the query sketch of every (sequence, row, KV head);
-//   [.., + n_app)         the append: the key sketch (and pooled block) of
-//                         the rows' own tokens (sketch_body.h);
-//   [.., + n_samp)        candidate mode's sample pass (topk_body.h), each
+//   [0, n_samp)           candidate mode's sample pass (topk_body.h), each
 //                         workgroup computing its segment's query sketch
-//                         itself (the same routine and bits as above), so
-//                         that it needs nothing from this launch.
+//                         itself (the same routine and bits as below), so
+//                         that it needs nothing from this launch;
+//   [.., + nq)            the query sketch of every (sequence, row, KV head);
+//   [.., + n_app)         the append: the key sketch (and pooled block) of
+//                         the rows' own tokens (sketch_body.h).
 // The three are independent chains of a few dependent loads each, so one
-// launch pays their latency once instead of three times.  The append writes
-// sketch rows of the rows' own tokens, which the sample pass reads only when
-// the window is shorter than the rows (then a sampled row may be read while
-// it is written: the sample decides only how long the selection takes, never
-// its result).
+// launch pays their latency once instead of three times.  The sample
+// workgroups have the longest chain and come first in the grid, which is
+// dispatched in order.  The append writes sketch rows of the rows' own
+// tokens, which the sample pass reads only when the window is shorter than
+// the rows (then a sampled row may be read while it is written: the sample
+// decides only how long the selection takes, never its result).
 #include "sketch_body.h"
 #include "tier.h"
 #include "topk_body.h"
@@ -70,6 +71,30 @@ __global__ __launch_bounds__(SK_THREADS) void front_kernel(const uint16_t *q, co
   static_assert(SK_THREADS == SAMPLE_THREADS, "one workgroup size");
   __shared__ FrontLds lds;
   int blk = blockIdx.x;
+  if (CAND && blk < f.n_samp) {
+    const int seg = blk / samp_per_seg;
+    const int h = seg % Hkv, b = seg / (Hkv * R);
+    const int j0 = (blk % samp_per_seg) * SAMPLE_WG_ROWS;
+    // Every load is issued at once, before the row's length is known: the
+    // sampled rows j * SAMPLE_STRIDE < NB lie in the cache whatever the
+    // length, and those past the far region are not counted.
+    int4 sv[SAMPLE_UNROLL];
+    sample_load(S, ((size_t)b * Hkv + h) * f.NB, j0, (f.NB + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE, sv);
+    for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS) lds.samp.lh[k] = 0;
+    block_query_sketch(q, R, Hq, Hkv, basis, basis_per_head, seg, lds.samp.qcode, nullptr,
+                       lds.samp.sk);
+    const SegGeom g = seg_geom(seg, seq_len, R, Hkv, f.T_max, f.window, f.pool, f.topk);
+    if (g.k_eff >= g.n_far) return;             // uniform: no selection needed
+    const int m = (g.n_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
+    if (j0 >= m) return;
+    __syncthreads();
+    const int4 qv = reinterpret_cast<const int4 *>(lds.samp.qcode)[threadIdx.x & 3];
+    sample_bins(sv, qv, j0, m, lds.samp.lh);
+    __syncthreads();
+    sample_flush(lds.samp.lh, f.hsamp + (size_t)seg * HIST1_BINS);
+    return;
+  }
+  if (CAND) blk -= f.n_samp;
   if (blk < nq) {
     block_query_sketch(q, R, Hq, Hkv, basis, basis_per_head, blk, f.qsk + (size_t)blk * RANK,
                        f.qscale ? f.qscale + blk : nullptr, lds.sk);
@@ -80,26 +105,6 @@ __global__ __launch_bounds__(SK_THREADS) void front_kernel(const uint16_t *q, co
     block_key_row<DT>(f.K, f.V, f.Ks, f.Kh, f.Ksh, f.W_hot, seq_len, basis, basis_per_head,
                       f.key_scale, Hkv, f.T_max, R, f.NB, f.pool, 1, 0, 0, S, f.Kp, f.Vp,
                       blk / f.app_rows, blk % f.app_rows, lds.sk);
-    return;
-  }
-  blk -= n_app;
-  if (CAND && blk < f.n_samp) {
-    const int seg = blk / samp_per_seg;
-    const SegGeom g = seg_geom(seg, seq_len, R, Hkv, f.T_max, f.window, f.pool, f.topk);
-    if (g.k_eff >= g.n_far) return;             // uniform: no selection needed
-    const int m = (g.n_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
-    const int j0 = (blk % samp_per_seg) * SAMPLE_WG_ROWS;
-    if (j0 >= m) return;
-    int4 sv[SAMPLE_UNROLL];
-    sample_load(S, ((size_t)g.b * Hkv + g.h) * f.NB, j0, m, sv);
-    for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS) lds.samp.lh[k] = 0;
-    block_query_sketch(q, R, Hq, Hkv, basis, basis_per_head, seg, lds.samp.qcode, nullptr,
-                       lds.samp.sk);
-    __syncthreads();
-    const int4 qv = reinterpret_cast<const int4 *>(lds.samp.qcode)[threadIdx.x & 3];
-    sample_bins(sv, qv, j0, m, lds.samp.lh);
-    __syncthreads();
-    sample_flush(lds.samp.lh, f.hsamp + (size_t)seg * HIST1_BINS);
   }
 }
 

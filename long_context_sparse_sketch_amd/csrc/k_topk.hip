@@ -31,7 +31,7 @@
 //
 // Candidate mode (the decode step when its caller does not read the scores)
 // replaces the stored scores and the filter pass:
-//   sample: scores every 64th far entry (1,024 sampled rows per workgroup)
+//   sample: scores every 64th far entry (512 sampled rows per workgroup)
 //     into a per-segment histogram of the level-1 bins (zero at rest).
 //   the score pass: every workgroup takes as the segment's estimate E the
 //     lowest key of the sample bin holding the rho-th largest sampled key,

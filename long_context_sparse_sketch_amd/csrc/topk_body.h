@@ -158,8 +158,8 @@ __device__ void block_threshold_bin(const int *hist, int need, int n, int *scrat
 // segment's sample histogram (zero at rest).  A quad of lanes per sampled
 // sketch row, 16 bytes each, SAMPLE_UNROLL rows per quad in flight.
 constexpr int SAMPLE_THREADS = 256;
-constexpr int SAMPLE_UNROLL = 16;
-constexpr int SAMPLE_WG_ROWS = SAMPLE_THREADS / 4 * SAMPLE_UNROLL;   // 1024 sampled rows
+constexpr int SAMPLE_UNROLL = 8;
+constexpr int SAMPLE_WG_ROWS = SAMPLE_THREADS / 4 * SAMPLE_UNROLL;   // 512 sampled rows
 
 // Loads of this thread's sampled rows (issued before anything uses them).
 __device__ __forceinline__ void sample_load(const int8_t *__restrict__ S, size_t seg_row0, int j0,
