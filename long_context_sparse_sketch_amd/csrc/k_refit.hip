@@ -253,24 +253,38 @@ __global__ __launch_bounds__(JB_THREADS) void jacobi_kernel(const double *__rest
         rq[tid] = q;
       }
       __syncthreads();
-      // rows p, q of A <- J^T A
-      for (int x = tid; x < (D / 2) * D; x += JB_THREADS) {
-        const int k = x / D, j = x % D;
-        const double c = rc[k], s = rs[k];
-        double *ap = A + rp[k] * JB_LDA + j, *aq = A + rq[k] * JB_LDA + j;
-        const double a = *ap, bq = *aq;
-        *ap = c * a - s * bq;
-        *aq = s * a + c * bq;
-      }
-      __syncthreads();
-      // columns p, q of A <- A J
-      for (int x = tid; x < (D / 2) * D; x += JB_THREADS) {
-        const int k = x / D, i = x % D;
-        const double c = rc[k], s = rs[k];
-        double *ap = A + i * JB_LDA + rp[k], *aq = A + i * JB_LDA + rq[k];
-        const double a = *ap, bq = *aq;
-        *ap = c * a - s * bq;
-        *aq = s * a + c * bq;
+      // A <- J^T A J, by 2 x 2 blocks: the block of rows (p_k, q_k) and columns
+      // (p_l, q_l) depends on the rotations of pairs k and l only, so each
+      // block is rotated on its rows and then on its columns in one pass
+      // (the same operations per element as a pass over rows then one over
+      // columns).  A diagonal block's off-diagonal pair is zero after its
+      // rotation and is stored as such.  Wave w takes row pairs w, w + 16,
+      // w + 32, w + 48 and lane l column pair l.
+      {
+        const int l = lane;
+        const double cl = rc[l], sl = rs[l];
+        const int pl = rp[l], ql = rq[l];
+#pragma unroll
+        for (int m = 0; m < D / 2 / (JB_THREADS / 64); ++m) {
+          const int k = wave + m * (JB_THREADS / 64);
+          const double ck = rc[k], sk = rs[k];
+          double *rowp = A + rp[k] * JB_LDA, *rowq = A + rq[k] * JB_LDA;
+          const double a_pp = rowp[pl], a_pq = rowp[ql], a_qp = rowq[pl], a_qq = rowq[ql];
+          // rows
+          const double r_pp = ck * a_pp - sk * a_qp, r_qp = sk * a_pp + ck * a_qp;
+          const double r_pq = ck * a_pq - sk * a_qq, r_qq = sk * a_pq + ck * a_qq;
+          // columns
+          double n_pp = cl * r_pp - sl * r_pq, n_pq = sl * r_pp + cl * r_pq;
+          double n_qp = cl * r_qp - sl * r_qq, n_qq = sl * r_qp + cl * r_qq;
+          if (k == l && sk != 0.0) {
+            n_pq = 0.0;
+            n_qp = 0.0;
+          }
+          rowp[pl] = n_pp;
+          rowp[ql] = n_pq;
+          rowq[pl] = n_qp;
+          rowq[ql] = n_qq;
+        }
       }
       // V <- V J on this lane's pair, then the columns move to the next
       // round's lanes (see above)
@@ -287,11 +301,6 @@ __global__ __launch_bounds__(JB_THREADS) void jacobi_kernel(const double *__rest
           vb[u] = lane == 0 ? from_next_top : from_prev_bot;
           vt[u] = t;
         }
-      }
-      __syncthreads();
-      if (tid < D / 2 && rs[tid] != 0.0) {               // the pair's entries are zero now
-        A[rp[tid] * JB_LDA + rq[tid]] = 0.0;
-        A[rq[tid] * JB_LDA + rp[tid]] = 0.0;
       }
       __syncthreads();
     }
