@@ -38,6 +38,9 @@ SCORE_SOURCES = ("k_score.hip", "sks_internal.h")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--lib", default=None,
+                    help="load this build of the library instead of libsks.so (e.g. "
+                         "libsks_attn_valu.so from `build --attn-valu`)")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="multi_agent_250k")
@@ -179,6 +182,8 @@ def main():
     import torch
 
     from long_context_sparse_sketch_amd import binding as sks
+    if args.lib:
+        sks.LIB_PATH = os.path.abspath(args.lib)
     from long_context_sparse_sketch_amd import configs as C
     from long_context_sparse_sketch_amd.runtime import (SparseDecodeLayer, StepRunner,
                                                         capture_steps, to_device)
@@ -461,7 +466,8 @@ def main():
                                 + (" (candidate mode: scores not stored)" if cand else ""))
                                + f", {args.parts} sub-batches on {args.streams} streams, "
                                + ("eager launches" if args.no_graph else
-                                  f"HIP graph replay ({spg} steps per graph)")},
+                                  f"HIP graph replay ({spg} steps per graph)")
+                               + (f", library {os.path.basename(args.lib)}" if args.lib else "")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counted_traffic(cfg.name, "candidates" if cand else "stores"),

@@ -1,9 +1,13 @@
 """Build libsks.so (HIP kernels + C ABI) for gfx950, in-tree.
 
-    python -m long_context_sparse_sketch_amd.build
+    python -m long_context_sparse_sketch_amd.build [--attn-valu]
 
 Compiles every csrc/*.hip to an object in parallel with hipcc, then links the
 shared library next to this file.  The build always recompiles.
+``--attn-valu`` builds the comparison library libsks_attn_valu.so instead,
+whose attention computes its Q.K and P.V products on the vector ALUs
+(SKS_ATTN_VALU=1; bf16 rows), for timing against the matrix-core
+attention (``bench.py --lib``).
 """
 from __future__ import annotations
 
@@ -19,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libsks.so")
+ATTN_VALU_LIB_PATH = os.path.join(PKG, "libsks_attn_valu.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -50,28 +55,31 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, attn_valu: bool = False) -> str:
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    bdir = os.path.join(BUILD_DIR, "attn_valu") if attn_valu else BUILD_DIR
+    lib = ATTN_VALU_LIB_PATH if attn_valu else LIB_PATH
+    os.makedirs(bdir, exist_ok=True)
     srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
-    objs = [os.path.join(BUILD_DIR, s[:-4] + ".o") for s in srcs]
+    objs = [os.path.join(bdir, s[:-4] + ".o") for s in srcs]
+    flags = HIP_FLAGS + (["-DSKS_ATTN_VALU=1"] if attn_valu else [])
 
     def compile_one(pair):
         src, obj = pair
-        return _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        return _run([hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
 
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16)
     with ThreadPoolExecutor(max(1, jobs)) as ex:
         outs = list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib + ".tmp"
     outs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]))
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib)
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    return LIB_PATH
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, attn_valu="--attn-valu" in sys.argv))

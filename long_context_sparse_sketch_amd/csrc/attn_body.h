@@ -11,6 +11,14 @@
 namespace sks {
 namespace {
 
+// SKS_ATTN_VALU = 1 builds the comparison variant of the attention whose Q.K
+// and P.V products run on the vector ALUs (bf16 rows; everything else --
+// gathers, tiles, splits, softmax, merge -- unchanged).  The library
+// is built with 0; `build.py --attn-valu` builds the variant beside it.
+#ifndef SKS_ATTN_VALU
+#define SKS_ATTN_VALU 0
+#endif
+
 constexpr int AT_THREADS = 256;
 constexpr int ATTN_SPLIT = 384;          // attention entries per workgroup, at most
 constexpr long ATTN_SMALL_SET = 1536;    // smaller attention sets: 128-entry slots
@@ -230,6 +238,10 @@ struct AttnLds {
   __align__(16) uint16_t s_v[4][AM_TILE * VROW];     // V tile per wave
   __align__(16) uint16_t s_p[4][2][16 * AM_TILE];    // P hi / lo [head][entry]
   float s_ml[4][16][2];
+#if SKS_ATTN_VALU
+  __align__(16) uint16_t s_q[16 * D];                // (VALU variant) Q, bf16 [head][dim]
+  float s_alpha[4][16];                              // (VALU variant) this tile's rescale per head
+#endif
 };
 
 // One attention slot (see AttnArgs) of one segment, by a workgroup of
@@ -349,6 +361,21 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
         qa[c] = u32x4_t{w.x, w.y, w.z, w.w};
     }
   }
+  constexpr bool VALU = SKS_ATTN_VALU && DT == SKS_KV_BF16;
+#if SKS_ATTN_VALU
+  // (VALU variant) every wave stages the group's Q in LDS (the same values:
+  // each wave reads back its own writes)
+  if constexpr (VALU) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (n < G)
+        *reinterpret_cast<u32x4_t *>(L.s_q + n * D + qdim(c)) = qa[c];
+    wave_lds_sync();
+  }
+  float ov[VALU ? G : 1][2];                         // (VALU variant) O[h][dims 2 lane, 2 lane + 1]
+#pragma unroll
+  for (int h = 0; h < (VALU ? G : 1); ++h) ov[h][0] = ov[h][1] = 0.f;
+#endif
   // int8 / int4 caches: each lane's entries' row scales, with the descriptors
   float ksd0 = 1.f, vsd0 = 1.f, ksd1 = 1.f, vsd1 = 1.f;
   if constexpr (DT != SKS_KV_BF16) {
@@ -474,6 +501,38 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#if SKS_ATTN_VALU
+      if constexpr (VALU) {
+        // (VALU variant) this lane's 32 dims of entry 16t + n against every
+        // head's Q (dot2 on bf16 pairs), then the four lane groups summed
+        float part[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) part[h] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4_t kv = kop(d, t, c);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const u32x4_t qv = *reinterpret_cast<const u32x4_t *>(L.s_q + h * D + qdim(c));
+#pragma unroll
+            for (int w = 0; w < 4; ++w) part[h] = dot2_bf16(qv[w], kv[w], part[h]);
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          part[h] += __shfl_xor(part[h], 16);
+          part[h] += __shfl_xor(part[h], 32);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v = 0.f;
+#pragma unroll
+          for (int h = 0; h < G; ++h) v = h == 4 * g + j ? part[h] : v;
+          sacc[t][j] = v;
+        }
+        continue;
+      }
+#endif
 #pragma unroll
       for (int c = 0; c < 4; ++c) sacc[t] = mfma_bf16(qa[c], kop(d, t, c), sacc[t]);
     }
@@ -526,14 +585,20 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float mx = row16_max_f(fmaxf(z[0][j], z[1][j]));
+      float alpha = 1.f;
       if (mx > m4[j] + RESCALE_SLACK || (m4[j] == NEG_INF && mx != NEG_INF)) {
-        const float alpha = m4[j] == NEG_INF ? 0.f : exp2_fast(m4[j] - mx);
+        alpha = m4[j] == NEG_INF ? 0.f : exp2_fast(m4[j] - mx);
         l4[j] *= alpha;
         if constexpr (I4) c4[j] *= alpha;
+        if constexpr (!VALU) {
 #pragma unroll
-        for (int blk = 0; blk < 8; ++blk) o[blk][j] *= alpha;
+          for (int blk = 0; blk < 8; ++blk) o[blk][j] *= alpha;
+        }
         m4[j] = mx;
       }
+#if SKS_ATTN_VALU
+      if (VALU && n == 0) L.s_alpha[wave][4 * g + j] = alpha;
+#endif
     }
     uint16_t *sp_hi = s_p[wave][0], *sp_lo = s_p[wave][1];
 #pragma unroll
@@ -543,6 +608,13 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
         const float pv = (z[t][j] == NEG_INF) ? 0.f : exp2_fast(z[t][j] - m4[j]);
         l4[j] += pv;
         const float pw = pv * vsc[t];                       // value scale folded in
+#if SKS_ATTN_VALU
+        if constexpr (VALU) {
+          // (VALU variant) P in fp32, [entry][16 heads] over the hi / lo area
+          reinterpret_cast<float *>(sp_hi)[(16 * t + n) * 16 + 4 * g + j] = pw;
+          continue;
+        }
+#endif
         const uint32_t hi = f32_to_bf16_rne(pw);
         const uint32_t lo = f32_to_bf16_rne(pw - __uint_as_float(hi << 16));
         if constexpr (I4) c4[j] += __uint_as_float(hi << 16) + __uint_as_float(lo << 16);
@@ -553,6 +625,32 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
     }
     wave_lds_sync();
 
+#if SKS_ATTN_VALU
+    if constexpr (VALU) {
+      // (VALU variant) this lane's two dims for every head: rescale, then
+      // the 32 entries' fp32 weights times the staged bf16 V
+      const float *pf = reinterpret_cast<const float *>(sp_hi);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float al = L.s_alpha[wave][h];
+        ov[h][0] *= al;
+        ov[h][1] *= al;
+      }
+#pragma unroll 8
+      for (int e = 0; e < AM_TILE; ++e) {
+        const uint32_t vw = *reinterpret_cast<const uint32_t *>(sv + e * VROW + 2 * lane);
+        const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xffff0000u);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pw = pf[e * 16 + h];
+          ov[h][0] = __builtin_fmaf(pw, v0, ov[h][0]);
+          ov[h][1] = __builtin_fmaf(pw, v1, ov[h][1]);
+        }
+      }
+      wave_lds_sync();                                      // before the next tile reuses LDS
+      return;
+    }
+#endif
     // ---- PV on the matrix cores: A = P (head n, entries 8g..8g+8), B = V
     const uint4 ph = *reinterpret_cast<const uint4 *>(sp_hi + n * AM_TILE + 8 * g);
     const uint4 pl = *reinterpret_cast<const uint4 *>(sp_lo + n * AM_TILE + 8 * g);
@@ -604,13 +702,22 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
     }
   }
   __syncthreads();                                          // s_v is reused as s_o below
+#if SKS_ATTN_VALU
+  if constexpr (VALU) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_o[(wave * G + h) * D + 2 * lane] = ov[h][0];
+      s_o[(wave * G + h) * D + 2 * lane + 1] = ov[h][1];
+    }
+  }
+#endif
   // wave partials to LDS: O rows 4g + j < G
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int hh = 4 * g + j;
     if (hh < G) {
 #pragma unroll
-      for (int blk = 0; blk < 8; ++blk) {
+      for (int blk = 0; blk < (VALU ? 0 : 8); ++blk) {
         // int4: V columns are in I4_ORDER within each group of 8
         const int col = 16 * blk + n;
         const int dim = I4 ? (col & ~7) + i4_slot_dim(col & 7) : col;
