@@ -116,12 +116,21 @@ __device__ int wave_threshold_bin_valid(const int *hist, int need, int n, int &a
 // minus the count above b, res[2] = the count in b.  `scratch` holds NW ints.
 // Contains two __syncthreads().
 template <int NW>
+__device__ void block_threshold_pair(int v0, int v1, int need, int n, int *scratch, int *res);
+template <int NW>
 __device__ void block_threshold_bin(const int *hist, int need, int n, int *scratch, int *res) {
+  const int b0 = 2 * (int)threadIdx.x;
+  block_threshold_pair<NW>(hist[hpad<HIST1_BINS>(b0)], hist[hpad<HIST1_BINS>(b0 + 1)], need, n,
+                           scratch, res);
+}
+// The same search with the lane's two bins (b0 = 2 threadIdx.x and b0 + 1)
+// given as values.
+template <int NW>
+__device__ void block_threshold_pair(int v0, int v1, int need, int n, int *scratch, int *res) {
   constexpr int B = HIST1_BINS / NW;
   static_assert(B == 128, "two bins per lane");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b0 = wave * B + 2 * lane;            // this lane's bins b0 (lower), b0 + 1
-  const int v0 = hist[hpad<HIST1_BINS>(b0)], v1 = hist[hpad<HIST1_BINS>(b0 + 1)];
   const bool bad = __ballot(v0 < 0 || v1 < 0 || v0 > n || v1 > n) != 0;
   const int sum = min(v0 + v1, n + 1);
   const int incl = wave_incl_add_sat(sum, n + 1);
@@ -277,24 +286,17 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
   for (int u = 0; u < 4; ++u) cv[u] = 4 * lane + u < n_sub_max ? gc[4 * lane + u] : 0;
   const int4 th = reinterpret_cast<const int4 *>(thr)[seg];   // (b1, above b1, valid, in b1)
   constexpr int H2_PER = HIST2_BINS / 64;
-  constexpr int H1_PER = HIST1_BINS / 64;
   const bool skip = a.skip, cmode = a.cand_mode;   // uniform
   // the score pass built this step's level-1 histogram
   const bool h1_ready = skip && a.h1_ready;
   int32_t *gh1 = hist1 + (size_t)seg * HIST1_BINS;
+  static_assert(HIST1_BINS == 2 * TF_THREADS, "two level-1 bins per thread");
   int hv[H2_PER];
-  int h1v[H1_PER];
-  if (wave == 0 && h1_ready) {
-    // the score pass's level-1 histogram of this segment, lane l holding bins
-    // [32l, 32l+32); the same lanes return those bins to zero afterwards
-#pragma unroll
-    for (int k = 0; k < H1_PER / 4; ++k) {
-      const int4 w = reinterpret_cast<const int4 *>(gh1 + lane * H1_PER)[k];
-      h1v[4 * k] = w.x;
-      h1v[4 * k + 1] = w.y;
-      h1v[4 * k + 2] = w.z;
-      h1v[4 * k + 3] = w.w;
-    }
+  int2 h1p = make_int2(0, 0);
+  if (h1_ready) {
+    // the score pass's level-1 histogram of this segment, thread t holding
+    // bins 2t, 2t + 1; the same threads return them to zero afterwards
+    h1p = reinterpret_cast<const int2 *>(gh1)[threadIdx.x];
 #pragma unroll
     for (int k = 0; k < H2_PER; ++k) hv[k] = 0;
   } else if (wave == 0 && !cmode) {
@@ -318,11 +320,7 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
   // every load that follows them.
   auto finish = [&]() {
     if (h1_ready) {
-      if (wave == 0) {                           // the lanes that read it
-#pragma unroll
-        for (int k = 0; k < H1_PER / 4; ++k)
-          reinterpret_cast<int4 *>(gh1 + lane * H1_PER)[k] = make_int4(0, 0, 0, 0);
-      }
+      reinterpret_cast<int2 *>(gh1)[threadIdx.x] = make_int2(0, 0);   // the threads that read it
     } else {
       for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh1[k] = 0;
     }
@@ -520,21 +518,7 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
         __syncthreads();
         block_threshold_bin<TF_WAVES>(h1, g.k_eff, m, sc_pre, res);   // ends with a barrier
       } else {
-        if (wave == 0) {
-          int above;
-          bool valid;
-          const int b1 = wave_threshold_regs<H1_PER>(h1v, g.k_eff, g.n_far, above, valid);
-          int mine = 0;
-#pragma unroll
-          for (int k = 0; k < H1_PER; ++k) mine = (k == (b1 & (H1_PER - 1))) ? h1v[k] : mine;
-          const int inb1 = __shfl(mine, b1 / H1_PER);
-          if (lane == 0) {
-            res[0] = valid ? b1 : -1;
-            res[1] = g.k_eff - above;
-            res[2] = inb1;
-          }
-        }
-        __syncthreads();
+        block_threshold_pair<TF_WAVES>(h1p.x, h1p.y, g.k_eff, g.n_far, sc_pre, res);
       }
       const int b1 = res[0];
       if (b1 >= 0) {
