@@ -33,19 +33,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Merge another online-softmax state (mo, lo, ao) into (m, l, a).
-template <int N>
-__device__ __forceinline__ void merge_state(float &m, float &l, float (&a)[N], float mo, float lo,
-                                            const float (&ao)[N]) {
-  const float M = fmaxf(m, mo);
-  const float wa = m == NEG_INF ? 0.f : exp2_fast(m - M);
-  const float wb = mo == NEG_INF ? 0.f : exp2_fast(mo - M);
-  l = l * wa + lo * wb;
-#pragma unroll
-  for (int d = 0; d < N; ++d) a[d] = a[d] * wa + ao[d] * wb;
-  m = M;
-}
-
 // ---------------------------------------------------------------------------
 // Matrix-core version.  Per wave, tiles of 32 entries:
 //   QK:  S[16 heads][16 entries] = Q x K^T with v_mfma_f32_16x16x32_bf16, two

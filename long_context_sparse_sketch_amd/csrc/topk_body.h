@@ -58,26 +58,6 @@ __device__ int block_incl_scan(int v, int *scratch, int &tot) {
   return incl + before;
 }
 
-// Exclusive block-wide running maximum of non-negative values (0 before the
-// first thread); `scratch` holds NW ints and is not reused.
-template <int NW>
-__device__ int block_excl_max(int v, int *scratch) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int incl = wave_incl_max(v);
-  if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
-  int before = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) before = max(before, w < wave ? scratch[w] : 0);
-  const int prev = __builtin_amdgcn_update_dpp(0, incl, DPP_ROW_SHR + 1, 0xF, 0xF, false);
-  // the lane before the first of a row is the last lane of the previous row
-  const int r15 = __builtin_amdgcn_readlane(incl, 15), r31 = __builtin_amdgcn_readlane(incl, 31),
-            r47 = __builtin_amdgcn_readlane(incl, 47);
-  const int row = lane >> 4;
-  const int prev_row = row == 0 ? 0 : (row == 1 ? r15 : (row == 2 ? r31 : r47));
-  return max(before, (lane & 15) ? prev : prev_row);
-}
-
 // LDS histograms are stored padded so that 64 lanes reading their contiguous
 // bins hit distinct banks.
 template <int NBINS>
