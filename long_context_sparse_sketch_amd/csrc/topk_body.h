@@ -298,13 +298,15 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
   // way out.  These stores come last: a wave that waits for its loads waits
   // for its earlier stores too, so stores issued here first would delay
   // every load that follows them.
+  // (Candidate mode writes neither histogram: a dirty one is left as it is,
+  // which costs a later storing selection time, never correctness.)
   auto finish = [&]() {
     if (h1_ready) {
       reinterpret_cast<int2 *>(gh1)[threadIdx.x] = make_int2(0, 0);   // the threads that read it
-    } else {
+    } else if (!cmode) {
       for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) gh1[k] = 0;
     }
-    if (wave == 0) {
+    if (wave == 0 && !cmode) {
 #pragma unroll
       for (int k = 0; k < H2_PER / 4; ++k)
         reinterpret_cast<int4 *>(gh2 + lane * H2_PER)[k] = make_int4(0, 0, 0, 0);
