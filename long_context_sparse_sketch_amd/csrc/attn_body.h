@@ -38,7 +38,8 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 //   QK:  S[16 heads][16 entries] = Q x K^T with v_mfma_f32_16x16x32_bf16, two
 //        sub-tiles of 16 entries (query heads padded to the 16 MFMA rows).
 //        A = Q: lane (n = lane%16, g = lane/16) holds head n, dims 32i+8g..+8;
-//        B = K^T: lane holds entry n, the same dims (16-byte gathers).
+//        B = K^T: lane holds entry n, the same dims (read from the K rows
+//        staged in wave-private LDS; int4 rows straight from the gathers).
 //        C: lane holds S[4g + j][n], j = 0..3.
 //   softmax on that layout: each lane owns 4 heads x 1 entry; row max and
 //        sums over the 16 lanes of its DPP row.  The running max is only
@@ -47,7 +48,8 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 //   PV:  O[16 heads][128] += P x V with the same MFMA, K = the 32 entries.
 //        P is split into bf16 hi + lo parts (two MFMAs) so its weights keep
 //        ~16 significant bits; V rows are staged row-major in wave-private
-//        LDS and read back per MFMA as 8 entries x 1 dim per lane.
+//        LDS and read back per MFMA as 8 entries x 1 dim per lane by two
+//        transpose reads.
 // All heads of the KV group share every gathered row; the 16-row MFMA shape
 // leaves 16 - G rows idle, which costs nothing here: the pass is bound by
 // the gathers.
@@ -59,7 +61,20 @@ constexpr int AM_TILE = 32;
 template <int TILES>
 constexpr int attn_split_entries() { return (AT_THREADS / 64) * TILES * AM_TILE; }
 static_assert(attn_split_entries<3>() == ATTN_SPLIT, "the largest split");
-constexpr int VROW = 132;                 // LDS V row stride in bf16 (264 B: conflict-free reads)
+// LDS row strides in bf16: V rows of 288 B (the four rows that a lane group
+// reads at once by transpose reads fall in disjoint banks), K rows of 272 B
+// (the 16 rows of one 16-byte operand read fall in disjoint banks).
+constexpr int VROW = 144;
+constexpr int KROW = 136;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+// LDS transpose read (gfx950): within each group of 16 lanes, the 8-byte
+// chunks that the lanes address form a 16 x 4 matrix M of 16-bit values
+// (row = addressing lane); lane j receives M[4s + j / 4][j % 4] in slot s.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t *)(p));
+  return __builtin_bit_cast(uint2, r);
+}
 constexpr float RESCALE_SLACK = 8.0f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -223,6 +238,7 @@ struct AttnArgs {
 
 struct AttnLds {
   __align__(16) uint16_t s_v[4][AM_TILE * VROW];     // V tile per wave
+  __align__(16) uint16_t s_k[4][AM_TILE * KROW];     // K tile per wave (bf16 / int8 rows as stored)
   __align__(16) uint16_t s_p[4][2][16 * AM_TILE];    // P hi / lo [head][entry]
   float s_ml[4][16][2];
 #if SKS_ATTN_VALU
@@ -411,21 +427,27 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
   const char *Vpb = reinterpret_cast<const char *>(Vp) + (POOLED ? ((size_t)b * Hkv + h) * NB * D * 2 : 0);
   uint16_t *sv = s_v[wave];
 
-  // Raw gathered data of one tile, as loaded (converted to bf16 only when the
-  // tile is consumed, so that the next tile's loads stay in flight meanwhile).
-  // bf16: K sub-tile t, lane (n, g): entry 16t + n, 16 bytes per MFMA step;
-  //       V: 16 bytes (8 dims) of chunk (x & 15) of tile row (x >> 4),
-  //       x = 64 qq + lane.
-  // int8: K: 16 bytes for steps 0-1 and 16 bytes for steps 2-3 (see qdim);
-  //       V: 16 bytes (16 dims) of chunk (x & 7) of tile row (x >> 3).
-  // int4: K: 16 bytes (dims 32g .. +32) for all four steps;
-  //       V: 16 bytes (32 dims) of chunk (x & 3) of tile row (x >> 2).
+  // Raw gathered data of one tile, as loaded (staged in LDS and converted to
+  // bf16 only when the tile is consumed, so that the next tile's loads stay
+  // in flight meanwhile).  Load qq of a tile reads 16 bytes of chunk
+  // (x & (2^VSH - 1)) of tile row (x >> VSH), x = 64 qq + lane: whole rows
+  // per load.
+  // bf16: V and K: 8 loads each (8 dims per chunk);
+  // int8: V and K: 4 loads each (16 dims per chunk);
+  // int4: V: 2 loads (32 dims per chunk); K is read in the operand layout
+  //       itself, lane (n, g) of sub-tile t taking dims 32g .. +32 of entry
+  //       16t + n (16 bytes: a 64-byte row is read whole by four lanes).
   constexpr bool I8 = DT == SKS_KV_I8, I4 = DT == SKS_KV_I4, Q = I8 || I4;
   constexpr int KLD = I4 ? 1 : I8 ? 2 : 4;           // K loads per sub-tile
   constexpr int VLD = I4 ? 2 : I8 ? 4 : 8;           // V loads per tile
   constexpr int VSH = I4 ? 2 : I8 ? 3 : 4;           // log2(V loads per row)
+  // bf16 / int8: K rows are gathered like V rows and staged in LDS, from
+  // where each lane reads its MFMA operand (read in the operand layout, a
+  // load would take 64 bytes of each of 16 rows)
+  constexpr bool KLDS = !I4;
+  uint16_t *sk = L.s_k[wave];
   struct Tile {
-    uint4 k[2][KLD];
+    uint4 k[2][KLD];       // K loads 0 .. 2 KLD - 1 (int4: sub-tile t's operand)
     uint4 v[VLD];
     int f[2];              // flags of the two K entries of this lane
     float ks[2], vs[2];    // int8 / int4 row scales of the two K entries
@@ -443,16 +465,10 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
       int r, f;
       desc(j, r, f);
       d.f[t] = f;
-      const char *kbase = (POOLED && (f & 2)) ? Kpb : (!POOLED && (f & 4)) ? Kht : Kt;
-      const size_t off = (size_t)r * RB;
+      if constexpr (I4) d.k[t][0] = ld(((f & 4) ? Kht : Kt) + (size_t)r * RB + 16 * g);
       if constexpr (Q) {
-        d.k[t][0] = ld(kbase + off + 16 * g);
-        if constexpr (I8) d.k[t][1] = ld(kbase + off + 64 + 16 * g);
         d.ks[t] = (!TWO || j < 64) ? __shfl(ksd0, j) : __shfl(ksd1, j - 64);
         d.vs[t] = (!TWO || j < 64) ? __shfl(vsd0, j) : __shfl(vsd1, j - 64);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) d.k[t][c] = ld(kbase + off + (32 * c + 8 * g) * 2);
       }
     }
 #pragma unroll
@@ -462,27 +478,75 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
       int r, f;
       desc(tile * AM_TILE + ev, r, f);
       const char *vbase = (POOLED && (f & 2)) ? Vpb : (!POOLED && (f & 4)) ? Vht : Vt;
+      if constexpr (KLDS) {
+        const char *kb = (POOLED && (f & 2)) ? Kpb : (!POOLED && (f & 4)) ? Kht : Kt;
+        d.k[qq / KLD][qq % KLD] = ld(kb + (size_t)r * RB + c * 16);
+      }
       d.v[qq] = ld(vbase + (size_t)r * RB + c * 16);
     }
   };
   // K operand of MFMA step c as 8 bf16 (int8 codes convert exactly; int4
   // codes as code + I4_BIAS, also exact)
+  // (bf16 / int8: from the staged rows, lane (n, g) reading the 16 bytes of
+  // entry 16t + n that qdim assigns to it)
   auto kop = [&](const Tile &d, int t, int c) -> u32x4_t {
     if constexpr (I4) {
       const uint4 &w = d.k[t][0];
       return i4_biased_bf16x8(c == 0 ? w.x : c == 1 ? w.y : c == 2 ? w.z : w.w);
     } else if constexpr (I8) {
-      const uint4 &w = d.k[t][c >> 1];
+      const uint4 w = *reinterpret_cast<const uint4 *>(sk + (16 * t + n) * KROW + (c >> 1) * 32 + 8 * g);
       const uint32_t a = (c & 1) ? w.z : w.x, bb = (c & 1) ? w.w : w.y;
       return u32x4_t{i8pair_to_bf16x2(a, 0), i8pair_to_bf16x2(a, 16), i8pair_to_bf16x2(bb, 0),
                      i8pair_to_bf16x2(bb, 16)};
     } else {
-      const uint4 &w = d.k[t][c];
-      return u32x4_t{w.x, w.y, w.z, w.w};
+      return *reinterpret_cast<const u32x4_t *>(sk + (16 * t + n) * KROW + 32 * c + 8 * g);
+    }
+  };
+
+  // stage V (row-major bf16, 16-byte stores)
+  auto stage_v = [&](const Tile &d) {
+#pragma unroll
+    for (int qq = 0; qq < VLD; ++qq) {
+      const int x = qq * 64 + lane;
+      const uint4 &w = d.v[qq];
+      if constexpr (I4) {
+        // 32 dims as code + I4_BIAS (the bias is removed from O at the end),
+        // each group of 8 columns in I4_ORDER (undone when O is written)
+        const int ev = x >> 2, c = x & 3;
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        uint4 *dst = reinterpret_cast<uint4 *>(sv + ev * VROW + c * 32);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x4_t bv = i4_biased_bf16x8(ws[k]);
+          dst[k] = make_uint4(bv[0], bv[1], bv[2], bv[3]);
+        }
+      } else if constexpr (I8) {
+        const int ev = x >> 3, c = x & 7;
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        uint4 *dst = reinterpret_cast<uint4 *>(sv + ev * VROW + c * 16);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          dst[k] = make_uint4(i8pair_to_bf16x2(ws[2 * k], 0), i8pair_to_bf16x2(ws[2 * k], 16),
+                              i8pair_to_bf16x2(ws[2 * k + 1], 0), i8pair_to_bf16x2(ws[2 * k + 1], 16));
+      } else {
+        const int ev = x >> 4, c = x & 15;
+        *reinterpret_cast<uint4 *>(sv + ev * VROW + c * 8) = w;
+      }
     }
   };
 
   auto consume = [&](const Tile &d) {
+    if constexpr (KLDS) {
+      // K rows as stored (16-byte stores) and V, then the operand reads
+#pragma unroll
+      for (int qq = 0; qq < VLD; ++qq) {
+        const int x = qq * 64 + lane;
+        const int ev = x >> VSH, c = x & ((1 << VSH) - 1);
+        *reinterpret_cast<uint4 *>(sk + ev * KROW + c * 8) = d.k[qq / KLD][qq % KLD];
+      }
+      stage_v(d);
+      wave_lds_sync();
+    }
     // ---- QK on the matrix cores
     f32x4_t sacc[2];
 #pragma unroll
@@ -524,37 +588,7 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
       for (int c = 0; c < 4; ++c) sacc[t] = mfma_bf16(qa[c], kop(d, t, c), sacc[t]);
     }
 
-    // stage V (row-major, 8-byte stores: the padded stride is 8-byte aligned)
-#pragma unroll
-    for (int qq = 0; qq < VLD; ++qq) {
-      const int x = qq * 64 + lane;
-      const uint4 &w = d.v[qq];
-      if constexpr (I4) {
-        // 32 dims as code + I4_BIAS (the bias is removed from O at the end),
-        // each group of 8 columns in I4_ORDER (undone when O is written)
-        const int ev = x >> 2, c = x & 3;
-        uint2 *dst = reinterpret_cast<uint2 *>(sv + ev * VROW + c * 32);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const u32x4_t bv = i4_biased_bf16x8(ws[k]);
-          dst[2 * k] = make_uint2(bv[0], bv[1]);
-          dst[2 * k + 1] = make_uint2(bv[2], bv[3]);
-        }
-      } else if constexpr (I8) {
-        const int ev = x >> 3, c = x & 7;
-        uint2 *dst = reinterpret_cast<uint2 *>(sv + ev * VROW + c * 16);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          dst[k] = make_uint2(i8pair_to_bf16x2(ws[k], 0), i8pair_to_bf16x2(ws[k], 16));
-      } else {
-        const int ev = x >> 4, c = x & 15;
-        uint2 *dst = reinterpret_cast<uint2 *>(sv + ev * VROW + c * 8);
-        dst[0] = make_uint2(w.x, w.y);
-        dst[1] = make_uint2(w.z, w.w);
-      }
-    }
+    if constexpr (!KLDS) stage_v(d);
 
     // ---- online softmax on the C layout (lane: heads 4g + j, entry n of each sub-tile)
     float ksc[2], vsc[2];
@@ -645,11 +679,12 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
     const u32x4_t pa_lo = u32x4_t{pl.x, pl.y, pl.z, pl.w};
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
-      const uint16_t *col = sv + (8 * g) * VROW + 16 * blk + n;
-      u32x4_t vb;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        vb[k] = (uint32_t)col[(2 * k) * VROW] | ((uint32_t)col[(2 * k + 1) * VROW] << 16);
+      // lane n of group g addresses dims 16 blk + 4 (n % 4) .. +4 of entry
+      // 8g + n / 4 (and of entry 8g + 4 + n / 4); transposed, lane n holds
+      // dim 16 blk + n of entries 8g .. 8g + 8: the MFMA's B layout
+      const uint16_t *p0 = sv + (8 * g + (n >> 2)) * VROW + 16 * blk + 4 * (n & 3);
+      const uint2 r0 = lds_read_tr16(p0), r1 = lds_read_tr16(p0 + 4 * VROW);
+      const u32x4_t vb = u32x4_t{r0.x, r0.y, r1.x, r1.y};
       o[blk] = mfma_bf16(pa_hi, vb, o[blk]);
       o[blk] = mfma_bf16(pa_lo, vb, o[blk]);
     }
