@@ -94,10 +94,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
 
 // int8 codes -> bf16 (exact: |code| <= 127 needs 7 significant bits)
 __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int sh) {
@@ -124,12 +120,28 @@ __device__ __forceinline__ u32x4_t i4_biased_bf16x8(uint32_t w) {
 // dim held by slot s (0..7) of a group of 8 in I4_ORDER
 __device__ __forceinline__ int i4_slot_dim(int s) { return s < 4 ? 2 * s : 2 * (s - 4) + 1; }
 
-__device__ __forceinline__ float row16_max_f(float x) {
-  x = fmaxf(x, dpp_f<DPP_ROW_MIRROR>(x));
-  x = fmaxf(x, dpp_f<DPP_ROW_HMIRROR>(x));
-  x = fmaxf(x, dpp_f<DPP_QUAD_XOR1>(x));
-  x = fmaxf(x, dpp_f<DPP_QUAD_XOR2>(x));
+// Max over the 16 lanes of each DPP row of values that are never NaN, each
+// step as the median of (x, permuted x, +inf): one instruction, where fmaxf
+// would first quiet the permuted operand.  `inf` must be +inf and opaque to
+// the compiler (see opaque_inf), which would otherwise turn the median back
+// into fmaxf.
+__device__ __forceinline__ float row16_max_f(float x, float inf) {
+  x = __builtin_amdgcn_fmed3f(x, dpp_f<DPP_ROW_MIRROR>(x), inf);
+  x = __builtin_amdgcn_fmed3f(x, dpp_f<DPP_ROW_HMIRROR>(x), inf);
+  x = __builtin_amdgcn_fmed3f(x, dpp_f<DPP_QUAD_XOR1>(x), inf);
+  x = __builtin_amdgcn_fmed3f(x, dpp_f<DPP_QUAD_XOR2>(x), inf);
   return x;
+}
+// +inf in a register, produced by a move the compiler cannot see through
+__device__ __forceinline__ float opaque_inf() {
+  float v;
+  asm("v_mov_b32 %0, 0x7f800000" : "=v"(v));
+  return v;
+}
+// two floats -> bf16 pair (round to nearest even), a in the low half
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const bf16x2_t h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 // Merge of the partials of one (segment, query head j, dim d) over all
@@ -239,7 +251,7 @@ struct AttnArgs {
 struct AttnLds {
   __align__(16) uint16_t s_v[4][AM_TILE * VROW];     // V tile per wave
   __align__(16) uint16_t s_k[4][AM_TILE * KROW];     // K tile per wave (bf16 / int8 rows as stored)
-  __align__(16) uint16_t s_p[4][2][16 * AM_TILE];    // P hi / lo [head][entry]
+  __align__(16) uint16_t s_p[4][2][AM_TILE * 16];    // P hi / lo [entry][head]
   float s_ml[4][16][2];
 #if SKS_ATTN_VALU
   __align__(16) uint16_t s_q[16 * D];                // (VALU variant) Q, bf16 [head][dim]
@@ -272,7 +284,7 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
   const float sm_log2 = a.sm_log2;
   const int T_max = a.T_max, NB = a.NB, window = a.window, pool = a.pool;
   uint16_t (*s_v)[AM_TILE * VROW] = L.s_v;
-  uint16_t (*s_p)[2][16 * AM_TILE] = L.s_p;
+  uint16_t (*s_p)[2][AM_TILE * 16] = L.s_p;
   float (*s_ml)[16][2] = L.s_ml;
   float *s_o = reinterpret_cast<float *>(&s_v[0][0]);          // reused after the loop
 
@@ -458,25 +470,32 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
     return make_uint4(v[0], v[1], v[2], v[3]);
   };
+  // Every descriptor of the tile is fetched first (lane permutes through the
+  // LDS unit: one round trip for all of them), then every load is issued.
+  // Interleaved, each load would wait for its own permute.
   auto gather = [&](int tile, Tile &d) {
+    int kr[2], kf[2], vr[VLD], vf[VLD];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int j = tile * AM_TILE + 16 * t + n;
-      int r, f;
-      desc(j, r, f);
-      d.f[t] = f;
-      if constexpr (I4) d.k[t][0] = ld(((f & 4) ? Kht : Kt) + (size_t)r * RB + 16 * g);
+      desc(j, kr[t], kf[t]);
+      d.f[t] = kf[t];
       if constexpr (Q) {
         d.ks[t] = (!TWO || j < 64) ? __shfl(ksd0, j) : __shfl(ksd1, j - 64);
         d.vs[t] = (!TWO || j < 64) ? __shfl(vsd0, j) : __shfl(vsd1, j - 64);
       }
     }
 #pragma unroll
+    for (int qq = 0; qq < VLD; ++qq) desc(tile * AM_TILE + ((qq * 64 + lane) >> VSH), vr[qq], vf[qq]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (I4) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) d.k[t][0] = ld(((kf[t] & 4) ? Kht : Kt) + (size_t)kr[t] * RB + 16 * g);
+    }
+#pragma unroll
     for (int qq = 0; qq < VLD; ++qq) {
-      const int x = qq * 64 + lane;
-      const int ev = x >> VSH, c = x & ((1 << VSH) - 1);
-      int r, f;
-      desc(tile * AM_TILE + ev, r, f);
+      const int c = (qq * 64 + lane) & ((1 << VSH) - 1);
+      const int r = vr[qq], f = vf[qq];
       const char *vbase = (POOLED && (f & 2)) ? Vpb : (!POOLED && (f & 4)) ? Vht : Vt;
       if constexpr (KLDS) {
         const char *kb = (POOLED && (f & 2)) ? Kpb : (!POOLED && (f & 4)) ? Kht : Kt;
@@ -535,6 +554,7 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
     }
   };
 
+  const float pinf = opaque_inf();
   auto consume = [&](const Tile &d) {
     if constexpr (KLDS) {
       // K rows as stored (16-byte stores) and V, then the operand reads
@@ -581,11 +601,21 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
           for (int h = 0; h < G; ++h) v = h == 4 * g + j ? part[h] : v;
           sacc[t][j] = v;
         }
-        continue;
       }
 #endif
+    }
+    if constexpr (!VALU) {
+      // all eight K operands first (LDS reads in flight together), then the products
+      u32x4_t kb[2][4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sacc[t] = mfma_bf16(qa[c], kop(d, t, c), sacc[t]);
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kb[t][c] = kop(d, t, c);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sacc[t] = mfma_bf16(qa[c], kb[t][c], sacc[t]);
     }
 
     if constexpr (!KLDS) stage_v(d);
@@ -605,7 +635,7 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
         z[t][j] = (d.f[t] & 1) ? (sacc[t][j] - kb4[j]) * ksc[t] * sm_log2 : NEG_INF;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float mx = row16_max_f(fmaxf(z[0][j], z[1][j]));
+      const float mx = row16_max_f(fmaxf(z[0][j], z[1][j]), pinf);
       float alpha = 1.f;
       if (mx > m4[j] + RESCALE_SLACK || (m4[j] == NEG_INF && mx != NEG_INF)) {
         alpha = m4[j] == NEG_INF ? 0.f : exp2_fast(m4[j] - mx);
@@ -624,24 +654,34 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
     uint16_t *sp_hi = s_p[wave][0], *sp_lo = s_p[wave][1];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      float pw[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float pv = (z[t][j] == NEG_INF) ? 0.f : exp2_fast(z[t][j] - m4[j]);
         l4[j] += pv;
-        const float pw = pv * vsc[t];                       // value scale folded in
+        pw[j] = pv * vsc[t];                                // value scale folded in
 #if SKS_ATTN_VALU
-        if constexpr (VALU) {
-          // (VALU variant) P in fp32, [entry][16 heads] over the hi / lo area
-          reinterpret_cast<float *>(sp_hi)[(16 * t + n) * 16 + 4 * g + j] = pw;
-          continue;
-        }
+        // (VALU variant) P in fp32, [entry][16 heads] over the hi / lo area
+        if constexpr (VALU) reinterpret_cast<float *>(sp_hi)[(16 * t + n) * 16 + 4 * g + j] = pw[j];
 #endif
-        const uint32_t hi = f32_to_bf16_rne(pw);
-        const uint32_t lo = f32_to_bf16_rne(pw - __uint_as_float(hi << 16));
-        if constexpr (I4) c4[j] += __uint_as_float(hi << 16) + __uint_as_float(lo << 16);
-        const int at = (4 * g + j) * AM_TILE + 16 * t + n;
-        sp_hi[at] = (uint16_t)hi;
-        sp_lo[at] = (uint16_t)lo;
+      }
+      if constexpr (!VALU) {
+        // bf16 hi + lo parts, two heads per conversion, stored as P^T
+        // [entry][16 heads]: this lane's four heads of entry 16t + n
+        const uint32_t h01 = bf16x2_rne(pw[0], pw[1]), h23 = bf16x2_rne(pw[2], pw[3]);
+        const float hf[4] = {__uint_as_float(h01 << 16), __uint_as_float(h01 & 0xffff0000u),
+                             __uint_as_float(h23 << 16), __uint_as_float(h23 & 0xffff0000u)};
+        const uint32_t l01 = bf16x2_rne(pw[0] - hf[0], pw[1] - hf[1]);
+        const uint32_t l23 = bf16x2_rne(pw[2] - hf[2], pw[3] - hf[3]);
+        if constexpr (I4) {
+          const float lf[4] = {__uint_as_float(l01 << 16), __uint_as_float(l01 & 0xffff0000u),
+                               __uint_as_float(l23 << 16), __uint_as_float(l23 & 0xffff0000u)};
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) c4[jj] += hf[jj] + lf[jj];
+        }
+        const int at = (16 * t + n) * 16 + 4 * g;
+        *reinterpret_cast<uint2 *>(sp_hi + at) = make_uint2(h01, h23);
+        *reinterpret_cast<uint2 *>(sp_lo + at) = make_uint2(l01, l23);
       }
     }
     wave_lds_sync();
@@ -673,10 +713,14 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
     }
 #endif
     // ---- PV on the matrix cores: A = P (head n, entries 8g..8g+8), B = V
-    const uint4 ph = *reinterpret_cast<const uint4 *>(sp_hi + n * AM_TILE + 8 * g);
-    const uint4 pl = *reinterpret_cast<const uint4 *>(sp_lo + n * AM_TILE + 8 * g);
-    const u32x4_t pa_hi = u32x4_t{ph.x, ph.y, ph.z, ph.w};
-    const u32x4_t pa_lo = u32x4_t{pl.x, pl.y, pl.z, pl.w};
+    // (P^T read back by transpose reads: lane n of group g addressing heads
+    // 4 (n % 4) .. +4 of entry 8g + n / 4 ends up with head n of entries
+    // 8g .. 8g + 4, and with the second read of 8g + 4 .. 8g + 8)
+    const int pat = (8 * g + (n >> 2)) * 16 + 4 * (n & 3);
+    const uint2 h0 = lds_read_tr16(sp_hi + pat), h1 = lds_read_tr16(sp_hi + pat + 64);
+    const uint2 l0 = lds_read_tr16(sp_lo + pat), l1 = lds_read_tr16(sp_lo + pat + 64);
+    const u32x4_t pa_hi = u32x4_t{h0.x, h0.y, h1.x, h1.y};
+    const u32x4_t pa_lo = u32x4_t{l0.x, l0.y, l1.x, l1.y};
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       // lane n of group g addresses dims 16 blk + 4 (n % 4) .. +4 of entry
