@@ -20,13 +20,23 @@ namespace sks {
 namespace {
 
 // One workgroup of D x merge_parts(nsplit) threads per (segment, query head
-// of the group).
+// of the group).  With `zero`, the workgroups also clear zero[0, nzero)
+// between them, after their merge (stores issued before the loads would
+// delay them).
 __global__ __launch_bounds__(D * MP) void attn_merge_kernel(const float2 *__restrict__ part_ml,
                                                             const float *__restrict__ part_acc,
                                                             int nsplit, int G, int Hkv,
                                                             float *__restrict__ out,
-                                                            float *__restrict__ lse) {
+                                                            float *__restrict__ lse,
+                                                            int32_t *__restrict__ zero,
+                                                            long nzero) {
   merge_splits(part_ml, part_acc, blockIdx.x, blockIdx.y, nsplit, G, Hkv, out, lse);
+  if (zero) {
+    const long nb = (long)gridDim.x * gridDim.y, blk = (long)blockIdx.y * gridDim.x + blockIdx.x;
+    const long per = (nzero + nb - 1) / nb, end = min(nzero, (blk + 1) * per);
+    const int nt = blockDim.x * blockDim.y, t = threadIdx.y * blockDim.x + threadIdx.x;
+    for (long i = blk * per + t; i < end; i += nt) zero[i] = 0;
+  }
 }
 
 template <int G, int DT, bool POOLED, int TILES>
@@ -126,16 +136,16 @@ hipError_t launch_attn_slots(const AttnArgs &a, int G, int dtype, int nseg, int 
 }
 
 hipError_t launch_attn_merge(const AttnArgs &a, int G, int nseg, float *out, float *lse,
-                             hipStream_t st) {
-  attn_merge_kernel<<<dim3(nseg, G), dim3(D, merge_parts(a.nsplit)), 0, st>>>(a.part_ml, a.part_acc, a.nsplit, G,
-                                                            a.Hkv, out, lse);
+                             hipStream_t st, int32_t *zero, long nzero) {
+  attn_merge_kernel<<<dim3(nseg, G), dim3(D, merge_parts(a.nsplit)), 0, st>>>(
+      a.part_ml, a.part_acc, a.nsplit, G, a.Hkv, out, lse, zero, nzero);
   return hipGetLastError();
 }
 
 hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
                        const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp,
                        float sm_scale, float *out, float *lse, const TopkWs &w, hipStream_t st,
-                       bool dense) {
+                       bool dense, int32_t *zero, long nzero) {
   const int G = Hq / s.Hkv;
   const int nseg = s.B * s.R * s.Hkv;
   AttnArgs a = attn_args(q, Hq, kv, s, idx, Kp, Vp, sm_scale, w);
@@ -149,7 +159,7 @@ hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape 
   }
   hipError_t e = launch_attn_slots(a, G, s.dtype, nseg, 0, a.nsplit, st);
   if (e != hipSuccess) return e;
-  return launch_attn_merge(a, G, nseg, out, lse, st);
+  return launch_attn_merge(a, G, nseg, out, lse, st, zero, nzero);
 }
 
 }  // namespace sks

@@ -363,11 +363,12 @@ hipError_t launch_topk_sample(const int8_t *qsk, const int8_t *S, const int32_t 
 
 hipError_t launch_topk_cand(const int8_t *qsk, const int8_t *S, int32_t *scores,
                             const int32_t *seq_len, const Shape &s, int32_t *idx,
-                            int32_t *n_sel, const TopkWs &w, hipStream_t st) {
+                            int32_t *n_sel, const TopkWs &w, hipStream_t st, bool zero_hsamp) {
   const int nseg = s.B * s.R * s.Hkv;
   FinalArgs a = final_args(scores, seq_len, s, idx, n_sel, w);
   a.cand_mode = 1;
   a.hsamp = w.hsamp;
+  a.zero_hsamp = zero_hsamp ? 1 : 0;
   a.qsk = qsk;
   a.S = S;
   a.rescore = scores;

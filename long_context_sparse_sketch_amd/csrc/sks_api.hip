@@ -185,8 +185,11 @@ hipError_t enqueue_step(const sks_kv &kv, const sks::Shape &s, const sks_step &s
   if (!dense) {
     if (cand) {
       if (e == hipSuccess) e = sks::launch_score(st.qsk, st.S, kv.seq_len, s, nullptr, &w, hs, true);
+      // (the sample histograms are cleared by the attention's merge launch,
+      // off the selection's critical path)
       if (e == hipSuccess)
-        e = sks::launch_topk_cand(st.qsk, st.S, st.scores, kv.seq_len, s, st.idx, st.n_sel, w, hs);
+        e = sks::launch_topk_cand(st.qsk, st.S, st.scores, kv.seq_len, s, st.idx, st.n_sel, w, hs,
+                                  false);
     } else {
       if (e == hipSuccess) e = sks::launch_score(st.qsk, st.S, kv.seq_len, s, st.scores, &w, hs);
       if (e == hipSuccess)
@@ -195,7 +198,8 @@ hipError_t enqueue_step(const sks_kv &kv, const sks::Shape &s, const sks_step &s
   }
   if (e == hipSuccess)
     e = sks::launch_attn(st.q, st.Hq, kv, s, st.idx, st.Kp, st.Vp, st.sm_scale, st.out, st.lse,
-                         w, hs, dense);
+                         w, hs, dense, cand ? w.hsamp : nullptr,
+                         cand ? (long)s.B * s.R * s.Hkv * sks::HIST1_BINS : 0);
   return e;
 }
 

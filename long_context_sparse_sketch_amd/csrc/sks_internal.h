@@ -269,13 +269,15 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
                        hipStream_t st);
 // Candidate mode: the sample pass (per-segment sample histograms), and the
 // final pass over the score pass's candidates, which rescores a segment into
-// `scores` when its estimate was too high.
+// `scores` when its estimate was too high and returns the sample histograms
+// to zero (with zero_hsamp; else a later launch must).
 bool topk_cand_preferred(const Shape &s);
 hipError_t launch_topk_sample(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
                               const Shape &s, const TopkWs &w, hipStream_t st);
 hipError_t launch_topk_cand(const int8_t *qsk, const int8_t *S, int32_t *scores,
                             const int32_t *seq_len, const Shape &s, int32_t *idx,
-                            int32_t *n_sel, const TopkWs &w, hipStream_t st);
+                            int32_t *n_sel, const TopkWs &w, hipStream_t st,
+                            bool zero_hsamp = true);
 
 // The decode step's first launch (k_front.hip): the query sketch, the append
 // (append) and candidate mode's sample pass (cand) in one grid.
@@ -283,10 +285,12 @@ hipError_t launch_step_front(const sks_kv &kv, const Shape &s, const uint16_t *q
                              const float *basis, int basis_per_head, const float *key_scale,
                              int8_t *qsk, float *qscale, int8_t *S, uint16_t *Kp, uint16_t *Vp,
                              bool append, bool cand, const TopkWs &w, hipStream_t st);
+// The attention pass and its merge; the merge also clears zero[0, nzero)
+// when `zero` is given.
 hipError_t launch_attn(const uint16_t *q, int Hq, const sks_kv &kv, const Shape &s,
                        const int32_t *idx, const uint16_t *Kp, const uint16_t *Vp,
                        float sm_scale, float *out, float *lse, const TopkWs &w, hipStream_t st,
-                       bool dense = false);
+                       bool dense = false, int32_t *zero = nullptr, long nzero = 0);
 
 hipError_t launch_gather(const sks_kv &kv, const Shape &s, const int32_t *idx,
                          const uint16_t *Kp, const uint16_t *Vp, void *K_out, void *V_out,

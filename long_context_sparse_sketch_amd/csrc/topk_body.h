@@ -201,6 +201,7 @@ struct FinalArgs {
   // S into `rescore` (the scores buffer) and selected from there.
   int cand_mode;
   int32_t *hsamp;   // candidate mode: the sample histograms, returned to zero here
+  int zero_hsamp;   // ... unless 0: then a later launch of the step clears them
   const int8_t *qsk, *S;
   int32_t *rescore;
 };
@@ -311,7 +312,7 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
       for (int k = 0; k < H2_PER / 4; ++k)
         reinterpret_cast<int4 *>(gh2 + lane * H2_PER)[k] = make_int4(0, 0, 0, 0);
     }
-    if (cmode)
+    if (cmode && a.zero_hsamp)
       for (int k = threadIdx.x; k < HIST1_BINS; k += TF_THREADS) a.hsamp[(size_t)seg * HIST1_BINS + k] = 0;
     if (threadIdx.x == 0 && n_sel) n_sel[seg] = g.k_eff;
   };
@@ -695,6 +696,7 @@ inline FinalArgs final_args(const int32_t *scores, const int32_t *seq_len, const
   a.h1_ready = 0;
   a.cand_mode = 0;
   a.hsamp = nullptr;
+  a.zero_hsamp = 1;
   a.qsk = nullptr;
   a.S = nullptr;
   a.rescore = nullptr;
