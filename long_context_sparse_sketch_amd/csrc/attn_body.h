@@ -248,9 +248,15 @@ struct AttnArgs {
   float *part_acc;
 };
 
+// K rows are staged in LDS for bf16 rows only (see attn_body): int8 and int4
+// rows go from the loads to the products, and their workgroups, at 45 KB of
+// LDS, fit three to a CU.
+template <int DT>
+constexpr bool attn_kstage() { return DT == SKS_KV_BF16; }
+template <bool KSTAGE>
 struct AttnLds {
   __align__(16) uint16_t s_v[4][AM_TILE * VROW];     // V tile per wave
-  __align__(16) uint16_t s_k[4][AM_TILE * KROW];     // K tile per wave (bf16 / int8 rows as stored)
+  __align__(16) uint16_t s_k[KSTAGE ? 4 : 1][KSTAGE ? AM_TILE * KROW : 8];   // K tile per wave
   __align__(16) uint16_t s_p[4][2][AM_TILE * 16];    // P hi / lo [entry][head]
   float s_ml[4][16][2];
 #if SKS_ATTN_VALU
@@ -268,7 +274,7 @@ struct AttnLds {
 template <int G, int DT, bool POOLED, int TILES>
 __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
                           const int32_t *__restrict__ seq_len, int topk, int R, int Hkv,
-                          int seg, int slot, AttnLds &L) {
+                          int seg, int slot, AttnLds<attn_kstage<DT>()> &L) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head");
   constexpr int WAVE_ENTRIES = TILES * AM_TILE;
   constexpr int SPLIT = attn_split_entries<TILES>();
@@ -445,7 +451,9 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
   // (x & (2^VSH - 1)) of tile row (x >> VSH), x = 64 qq + lane: whole rows
   // per load.
   // bf16: V and K: 8 loads each (8 dims per chunk);
-  // int8: V and K: 4 loads each (16 dims per chunk);
+  // int8: V: 4 loads (16 dims per chunk); K is read in the operand layout,
+  //       lane (n, g) of sub-tile t taking bytes 16g and 64 + 16g of entry
+  //       16t + n (two loads);
   // int4: V: 2 loads (32 dims per chunk); K is read in the operand layout
   //       itself, lane (n, g) of sub-tile t taking dims 32g .. +32 of entry
   //       16t + n (16 bytes: a 64-byte row is read whole by four lanes).
@@ -453,13 +461,15 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
   constexpr int KLD = I4 ? 1 : I8 ? 2 : 4;           // K loads per sub-tile
   constexpr int VLD = I4 ? 2 : I8 ? 4 : 8;           // V loads per tile
   constexpr int VSH = I4 ? 2 : I8 ? 3 : 4;           // log2(V loads per row)
-  // bf16 / int8: K rows are gathered like V rows and staged in LDS, from
-  // where each lane reads its MFMA operand (read in the operand layout, a
-  // load would take 64 bytes of each of 16 rows)
-  constexpr bool KLDS = !I4;
-  uint16_t *sk = L.s_k[wave];
+  // bf16: K rows are gathered like V rows and staged in LDS, from where each
+  // lane reads its MFMA operand (read in the operand layout, a load would
+  // take 64 bytes of each of 16 rows).  int8 rows are read in the operand
+  // layout (64 bytes of each of 16 rows per load): staging them too measured
+  // slower, its LDS leaving room for two workgroups per CU instead of three.
+  constexpr bool KLDS = attn_kstage<DT>();
+  uint16_t *sk = L.s_k[KLDS ? wave : 0];
   struct Tile {
-    uint4 k[2][KLD];       // K loads 0 .. 2 KLD - 1 (int4: sub-tile t's operand)
+    uint4 k[2][KLD];       // bf16: K loads 0 .. 2 KLD - 1; int8 / int4: sub-tile t's operand
     uint4 v[VLD];
     int f[2];              // flags of the two K entries of this lane
     float ks[2], vs[2];    // int8 / int4 row scales of the two K entries
@@ -492,6 +502,15 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
 #pragma unroll
       for (int t = 0; t < 2; ++t) d.k[t][0] = ld(((kf[t] & 4) ? Kht : Kt) + (size_t)kr[t] * RB + 16 * g);
     }
+    if constexpr (I8) {
+      // int8 rows in the operand layout (lane (n, g): bytes 16g and 64 + 16g)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const char *kb = ((kf[t] & 4) ? Kht : Kt) + (size_t)kr[t] * RB + 16 * g;
+        d.k[t][0] = ld(kb);
+        d.k[t][1] = ld(kb + 64);
+      }
+    }
 #pragma unroll
     for (int qq = 0; qq < VLD; ++qq) {
       const int c = (qq * 64 + lane) & ((1 << VSH) - 1);
@@ -506,14 +525,14 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
   };
   // K operand of MFMA step c as 8 bf16 (int8 codes convert exactly; int4
   // codes as code + I4_BIAS, also exact)
-  // (bf16 / int8: from the staged rows, lane (n, g) reading the 16 bytes of
-  // entry 16t + n that qdim assigns to it)
+  // (bf16: from the staged rows, lane (n, g) reading the 16 bytes of entry
+  // 16t + n that qdim assigns to it)
   auto kop = [&](const Tile &d, int t, int c) -> u32x4_t {
     if constexpr (I4) {
       const uint4 &w = d.k[t][0];
       return i4_biased_bf16x8(c == 0 ? w.x : c == 1 ? w.y : c == 2 ? w.z : w.w);
     } else if constexpr (I8) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(sk + (16 * t + n) * KROW + (c >> 1) * 32 + 8 * g);
+      const uint4 &w = d.k[t][c >> 1];
       const uint32_t a = (c & 1) ? w.z : w.x, bb = (c & 1) ? w.w : w.y;
       return u32x4_t{i8pair_to_bf16x2(a, 0), i8pair_to_bf16x2(a, 16), i8pair_to_bf16x2(bb, 0),
                      i8pair_to_bf16x2(bb, 16)};
@@ -714,20 +733,26 @@ __device__ void attn_body(const AttnArgs &a, const int32_t *__restrict__ idx,
 #endif
     // ---- PV on the matrix cores: A = P (head n, entries 8g..8g+8), B = V
     // (P^T read back by transpose reads: lane n of group g addressing heads
-    // 4 (n % 4) .. +4 of entry 8g + n / 4 ends up with head n of entries
-    // 8g .. 8g + 4, and with the second read of 8g + 4 .. 8g + 8)
-    const int pat = (8 * g + (n >> 2)) * 16 + 4 * (n & 3);
-    const uint2 h0 = lds_read_tr16(sp_hi + pat), h1 = lds_read_tr16(sp_hi + pat + 64);
-    const uint2 l0 = lds_read_tr16(sp_lo + pat), l1 = lds_read_tr16(sp_lo + pat + 64);
+    // 4 (n % 4) .. +4 of entry e0 + n / 4 ends up with head n of entries
+    // e0 .. e0 + 4, and with the second read of e1 .. e1 + 4.  Lane group g
+    // takes the MFMA's k-slots 8g .. 8g + 8, here entries e0 = 8g, e1 = 8g + 4
+    // for even g and e0 = 8g + 4, e1 = 8g for odd g: P and V take the same
+    // order, the product is the same sum, and the two lane groups of each
+    // half-wave read rows 32 banks apart instead of the same banks.)
+    const int e0 = 8 * g + 4 * (g & 1), e1 = 8 * g + 4 * (~g & 1);
+    const int pat0 = (e0 + (n >> 2)) * 16 + 4 * (n & 3), pat1 = (e1 + (n >> 2)) * 16 + 4 * (n & 3);
+    const uint2 h0 = lds_read_tr16(sp_hi + pat0), h1 = lds_read_tr16(sp_hi + pat1);
+    const uint2 l0 = lds_read_tr16(sp_lo + pat0), l1 = lds_read_tr16(sp_lo + pat1);
     const u32x4_t pa_hi = u32x4_t{h0.x, h0.y, h1.x, h1.y};
     const u32x4_t pa_lo = u32x4_t{l0.x, l0.y, l1.x, l1.y};
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       // lane n of group g addresses dims 16 blk + 4 (n % 4) .. +4 of entry
-      // 8g + n / 4 (and of entry 8g + 4 + n / 4); transposed, lane n holds
-      // dim 16 blk + n of entries 8g .. 8g + 8: the MFMA's B layout
-      const uint16_t *p0 = sv + (8 * g + (n >> 2)) * VROW + 16 * blk + 4 * (n & 3);
-      const uint2 r0 = lds_read_tr16(p0), r1 = lds_read_tr16(p0 + 4 * VROW);
+      // e0 + n / 4 (and of entry e1 + n / 4); transposed, lane n holds dim
+      // 16 blk + n of the entries of k-slots 8g .. 8g + 8: the MFMA's B layout
+      const uint16_t *p0 = sv + (e0 + (n >> 2)) * VROW + 16 * blk + 4 * (n & 3);
+      const uint16_t *p1 = sv + (e1 + (n >> 2)) * VROW + 16 * blk + 4 * (n & 3);
+      const uint2 r0 = lds_read_tr16(p0), r1 = lds_read_tr16(p1);
       const u32x4_t vb = u32x4_t{r0.x, r0.y, r1.x, r1.y};
       o[blk] = mfma_bf16(pa_hi, vb, o[blk]);
       o[blk] = mfma_bf16(pa_lo, vb, o[blk]);

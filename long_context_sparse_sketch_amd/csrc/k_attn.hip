@@ -44,7 +44,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_kernel(const int32_t *idx,
                                                              const int32_t *seq_len, int topk,
                                                              int R, int Hkv, AttnArgs a,
                                                              int slot0) {
-  __shared__ AttnLds lds;
+  __shared__ AttnLds<attn_kstage<DT>()> lds;
   attn_body<G, DT, POOLED, TILES>(a, idx, seq_len, topk, R, Hkv, blockIdx.y, slot0 + blockIdx.x,
                                   lds);
 }
