@@ -49,26 +49,37 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_kernel(const int32_t *idx,
                                   lds);
 }
 
+// The splits attn_split() gives: one tile per wave for small attention sets,
+// else three for bf16 rows and two for int8 / int4 rows; only these kernels
+// are built.
 template <int G, int TILES>
-void dispatch_t(dim3 grid, hipStream_t st, const AttnArgs &a, int dtype, int pool, int slot0) {
-  if (dtype == SKS_KV_I8)
-    attn_kernel<G, SKS_KV_I8, false, TILES><<<grid, AT_THREADS, 0, st>>>(a.idx, a.seq_len, a.topk, a.R, a.Hkv, a, slot0);
-  else if (dtype == SKS_KV_I4)
-    attn_kernel<G, SKS_KV_I4, false, TILES><<<grid, AT_THREADS, 0, st>>>(a.idx, a.seq_len, a.topk, a.R, a.Hkv, a, slot0);
-  else if (pool > 1)
+hipError_t dispatch_t(dim3 grid, hipStream_t st, const AttnArgs &a, int dtype, int pool, int slot0) {
+  if (dtype == SKS_KV_I8 || dtype == SKS_KV_I4) {
+    if constexpr (TILES == 3) {
+      return hipErrorInvalidValue;
+    } else if (dtype == SKS_KV_I8) {
+      attn_kernel<G, SKS_KV_I8, false, TILES><<<grid, AT_THREADS, 0, st>>>(a.idx, a.seq_len, a.topk, a.R, a.Hkv, a, slot0);
+    } else {
+      attn_kernel<G, SKS_KV_I4, false, TILES><<<grid, AT_THREADS, 0, st>>>(a.idx, a.seq_len, a.topk, a.R, a.Hkv, a, slot0);
+    }
+  } else if constexpr (TILES == 2) {
+    return hipErrorInvalidValue;
+  } else if (pool > 1) {
     attn_kernel<G, SKS_KV_BF16, true, TILES><<<grid, AT_THREADS, 0, st>>>(a.idx, a.seq_len, a.topk, a.R, a.Hkv, a, slot0);
-  else
+  } else {
     attn_kernel<G, SKS_KV_BF16, false, TILES><<<grid, AT_THREADS, 0, st>>>(a.idx, a.seq_len, a.topk, a.R, a.Hkv, a, slot0);
+  }
+  return hipSuccess;
 }
 
 template <int G>
-void dispatch_g(dim3 grid, hipStream_t st, const AttnArgs &a, int dtype, int pool, int slot0) {
+hipError_t dispatch_g(dim3 grid, hipStream_t st, const AttnArgs &a, int dtype, int pool, int slot0) {
   if (a.split == attn_split_entries<1>())
-    dispatch_t<G, 1>(grid, st, a, dtype, pool, slot0);
+    return dispatch_t<G, 1>(grid, st, a, dtype, pool, slot0);
   else if (a.split == attn_split_entries<2>())
-    dispatch_t<G, 2>(grid, st, a, dtype, pool, slot0);
+    return dispatch_t<G, 2>(grid, st, a, dtype, pool, slot0);
   else
-    dispatch_t<G, 3>(grid, st, a, dtype, pool, slot0);
+    return dispatch_t<G, 3>(grid, st, a, dtype, pool, slot0);
 }
 
 }  // namespace
@@ -121,18 +132,19 @@ hipError_t launch_attn_slots(const AttnArgs &a, int G, int dtype, int nseg, int 
                              hipStream_t st) {
   if (nslots <= 0) return hipSuccess;
   dim3 grid(nslots, nseg);
+  hipError_t e;
   switch (G) {
-    case 1: dispatch_g<1>(grid, st, a, dtype, a.pool, slot0); break;
-    case 2: dispatch_g<2>(grid, st, a, dtype, a.pool, slot0); break;
-    case 3: dispatch_g<3>(grid, st, a, dtype, a.pool, slot0); break;
-    case 4: dispatch_g<4>(grid, st, a, dtype, a.pool, slot0); break;
-    case 5: dispatch_g<5>(grid, st, a, dtype, a.pool, slot0); break;
-    case 6: dispatch_g<6>(grid, st, a, dtype, a.pool, slot0); break;
-    case 7: dispatch_g<7>(grid, st, a, dtype, a.pool, slot0); break;
-    case 8: dispatch_g<8>(grid, st, a, dtype, a.pool, slot0); break;
+    case 1: e = dispatch_g<1>(grid, st, a, dtype, a.pool, slot0); break;
+    case 2: e = dispatch_g<2>(grid, st, a, dtype, a.pool, slot0); break;
+    case 3: e = dispatch_g<3>(grid, st, a, dtype, a.pool, slot0); break;
+    case 4: e = dispatch_g<4>(grid, st, a, dtype, a.pool, slot0); break;
+    case 5: e = dispatch_g<5>(grid, st, a, dtype, a.pool, slot0); break;
+    case 6: e = dispatch_g<6>(grid, st, a, dtype, a.pool, slot0); break;
+    case 7: e = dispatch_g<7>(grid, st, a, dtype, a.pool, slot0); break;
+    case 8: e = dispatch_g<8>(grid, st, a, dtype, a.pool, slot0); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 hipError_t launch_attn_merge(const AttnArgs &a, int G, int nseg, float *out, float *lse,
