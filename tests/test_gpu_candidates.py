@@ -96,6 +96,40 @@ def test_step_without_scores_equals_step(ctx):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (cfg.name, name)
 
 
+def histogram_regions(lay):
+    """The per-segment histograms at the start of the workspace that must be
+    zero at rest: level-1, level-2 and the sample histograms (the layout of
+    the selection's workspace: level-1 [nseg][2048], level-2 [nseg][1024],
+    thresholds [nseg][4], sub-list maxima [nseg][ceil(NB / 1024)], sample
+    [nseg][2048] int32, each region 256-byte aligned)."""
+    def align(x):
+        return (x + 255) // 256 * 256
+    nseg = lay.B * lay.R * lay.Hkv
+    n_sub = (lay.NB + 1023) // 1024
+    h1, h2 = nseg * 2048 * 4, nseg * 1024 * 4
+    samp = align(h1) + align(h2) + align(nseg * 16) + align(nseg * n_sub * 4)
+    ws = lay.ws
+    return {"level-1": ws[:h1], "level-2": ws[align(h1):align(h1) + h2], "sample": ws[samp:samp + h1]}
+
+
+def test_histograms_return_to_zero(ctx):
+    """After the candidate selection and after a step (in candidate mode for
+    the shapes that take it: the attention's merge launch clears the sample
+    histograms there), every histogram of the workspace is zero again, so
+    that the next selection's estimate and thresholds start clean."""
+    cfg, case, g, ref, arr = ctx
+    lay = g.layer
+    sks.workspace_init(lay.ws)
+    select_candidates(g, arr, 0)
+    for name, r in histogram_regions(lay).items():
+        assert int(torch.count_nonzero(r)) == 0, (cfg.name, "candidate selection", name)
+    for keep in (False, True, False):
+        lay.step(g.q, keep_scores=keep)
+        torch.cuda.synchronize()
+        for name, r in histogram_regions(lay).items():
+            assert int(torch.count_nonzero(r)) == 0, (cfg.name, "step", keep, name)
+
+
 @pytest.mark.parametrize("seed", list(range(60)))
 def test_candidates_random_shape(seed):
     """Ragged lengths (empty rows included), verify rows, pooling, k = 1 and
@@ -111,3 +145,31 @@ def test_candidates_random_shape(seed):
         idx, n_sel = select_candidates(g, arr, flags)
         assert np.array_equal(idx, arr["idx"]), (seed, mode)
         assert np.array_equal(n_sel, arr["n_sel"]), (seed, mode)
+
+
+def test_step_in_candidate_mode_clears_histograms():
+    """A shape that takes candidate mode in the step (one row, 8 segments of
+    ~136K far entries: more than 2^20 in all): the step without scores gives
+    the stored-score step's bits, and after each such step every histogram of
+    the workspace is zero again (the sample histograms are cleared by the
+    attention's merge launch there)."""
+    cfg = C.C3.scaled(name="candidate_step", B=2, L=140000, needle_count=16)
+    flush(f"[candidates] {cfg.name}: B={cfg.B} Hkv={cfg.Hkv} L={cfg.L}")
+    case = make_case(cfg)
+    g = GpuCase(case)
+    lay = g.layer
+    lay.build_sketch(0, g.T)
+    lay.step(g.q)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (lay.idx, lay.n_sel, lay.out, lay.lse)]
+    for _ in range(3):
+        for t in (lay.idx, lay.n_sel):
+            t.fill_(-7)
+        lay.out.fill_(float("nan"))
+        lay.step(g.q, keep_scores=False)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("idx", "n_sel", "out", "lse"), want,
+                              (lay.idx, lay.n_sel, lay.out, lay.lse)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
+        for name, r in histogram_regions(lay).items():
+            assert int(torch.count_nonzero(r)) == 0, name
