@@ -38,8 +38,9 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 //   QK:  S[16 heads][16 entries] = Q x K^T with v_mfma_f32_16x16x32_bf16, two
 //        sub-tiles of 16 entries (query heads padded to the 16 MFMA rows).
 //        A = Q: lane (n = lane%16, g = lane/16) holds head n, dims 32i+8g..+8;
-//        B = K^T: lane holds entry n, the same dims (read from the K rows
-//        staged in wave-private LDS; int4 rows straight from the gathers).
+//        B = K^T: lane holds entry n, the same dims (bf16: read from the K
+//        rows staged in wave-private LDS; int8 / int4: straight from the
+//        gathers).
 //        C: lane holds S[4g + j][n], j = 0..3.
 //   softmax on that layout: each lane owns 4 heads x 1 entry; row max and
 //        sums over the 16 lanes of its DPP row.  The running max is only
@@ -93,7 +94,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-
 
 // int8 codes -> bf16 (exact: |code| <= 127 needs 7 significant bits)
 __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int sh) {
