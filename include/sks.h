@@ -221,19 +221,20 @@ int sks_topk_select(const int32_t *scores, const sks_kv *kv, const sks_params *p
  *      (b, i, h) into a sample histogram in ws;
  *   2. derives from that histogram an estimate E of each (b, i, h)'s k-th
  *      largest biased score (score + 2^20), set low enough that with high
- *      probability at least k entries reach it; scores every far token as
- *      sks_sketch_score does and keeps in ws, instead of the scores, every
- *      far entry whose biased score is at least E (index and biased score,
- *      ascending), and accumulates into ws the level-1 histogram of the
- *      kept entries only.
+ *      probability at least k entries reach it (where a (b, i, h) has at most
+ *      1,024 sampled entries, step 1 derives E at once and keeps E in ws
+ *      instead of the histogram); scores every far token as sks_sketch_score
+ *      does and keeps in ws, instead of the scores, every far entry whose
+ *      biased score is at least E (index and biased score, ascending).
  * sks_topk_select_candidates then selects as sks_topk_select, from those
  * entries.  Where fewer than k entries reached E, it recomputes that
  * segment's scores from qsk and S into `scores` ([B][R][Hkv][NB] int32,
  * scratch: its contents afterwards are unspecified) and selects from them.
  * E only decides the time taken, never the result.
  * Flags of sks_score_candidates:
- *   SKS_CAND_KEEP_ESTIMATE  reuse the sample histograms already in ws (step
- *                           2 only; sks_topk_select_candidates returns them
+ *   SKS_CAND_KEEP_ESTIMATE  reuse the sample histograms (or estimates)
+ *                           already in ws (step 2 only;
+ *                           sks_topk_select_candidates returns histograms
  *                           to zero, after which E is 0);
  *   SKS_CAND_TEST_HIGH      (tests) E above every score: every segment with
  *                           k_eff < n_far takes the recomputing path;
@@ -303,9 +304,9 @@ int sks_sparse_decode_attn(const uint16_t *q, int32_t Hq, const sks_kv *kv,
  * the sketch current.  Which mode a step takes is the caller's choice (it
  * knows its lengths); the workspace of the sparse step serves both.
  * With SKS_STEP_NO_SCORES the caller does not read `scores` after the step:
- * where it pays (one row per sequence, rows of more than 8,192 far entries
- * and at least 2^20 far entries over all (b, h)), the step scores and
- * selects in candidate
+ * where it pays (rows of more than 8,192 far entries, at least 2^20 far
+ * entries over all (b, i, h), and either one row per sequence or at most
+ * 65,536 far entries per row), the step scores and selects in candidate
  * mode (sks_score_candidates + sks_topk_select_candidates), which stores no
  * scores; idx, n_sel, out and lse are the same bit for bit, and `scores` is
  * then scratch with unspecified contents.

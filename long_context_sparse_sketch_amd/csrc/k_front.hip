@@ -6,7 +6,10 @@
 //   [0, n_samp)           candidate mode's sample pass (topk_body.h), each
 //                         workgroup computing its segment's query sketch
 //                         itself (the same routine and bits as below), so
-//                         that it needs nothing from this launch;
+//                         that it needs nothing from this launch; when one
+//                         workgroup samples a whole segment (EST), it also
+//                         derives the segment's estimate E for the score
+//                         pass instead of publishing its histogram;
 //   [.., + nq)            the query sketch of every (sequence, row, KV head);
 //   [.., + n_app)         the append: the key sketch (and pooled block) of
 //                         the rows' own tokens (sketch_body.h).
@@ -26,7 +29,7 @@ namespace {
 
 struct FrontArgs {
   int R, Hkv, T_max, NB, window, pool, topk;
-  int n_samp, samp_per_seg, nq, n_app, app_rows;
+  int n_samp, samp_per_seg, samp_stride, nq, n_app, app_rows;
   const int32_t *seq_len;
   // the query sketch and the append
   const uint16_t *q;
@@ -45,11 +48,13 @@ struct FrontArgs {
   uint16_t *Kp, *Vp;
   // the sample pass
   int32_t *hsamp;
+  int32_t *est;
 };
 
 struct SampleLds {
   int lh[HIST1_BINS];
   __align__(16) int8_t qcode[RANK];
+  SampleEstLds est;
   SketchLds sk;
 };
 
@@ -62,35 +67,45 @@ union FrontLds {
 // numbers the block's first loads need) come as scalar arguments ahead of
 // the struct, so that they arrive preloaded in SGPRs; they override the
 // struct's copies.
-template <int DT, bool CAND>
+template <int DT, bool CAND, bool EST>
 __global__ __launch_bounds__(SK_THREADS) void front_kernel(const uint16_t *q, const float *basis,
                                                           const int32_t *seq_len, int8_t *S,
                                                           int nq, int n_app, int samp_per_seg,
                                                           int R, int Hkv, int Hq,
                                                           int basis_per_head, FrontArgs f) {
   static_assert(SK_THREADS == SAMPLE_THREADS, "one workgroup size");
+  static_assert(!EST || CAND, "the estimate is candidate mode's");
   __shared__ FrontLds lds;
   int blk = blockIdx.x;
   if (CAND && blk < f.n_samp) {
     const int seg = blk / samp_per_seg;
     const int h = seg % Hkv, b = seg / (Hkv * R);
-    const int j0 = (blk % samp_per_seg) * SAMPLE_WG_ROWS;
+    const int j0 = (blk % samp_per_seg) * SAMPLE_WG_ROWS;   // EST: one workgroup per segment, 0
     // Every load is issued at once, before the row's length is known: the
-    // sampled rows j * SAMPLE_STRIDE < NB lie in the cache whatever the
-    // length, and those past the far region are not counted.
+    // sampled rows j * stride < NB lie in the cache whatever the length, and
+    // those past the far region are not counted.
+    const int stride = f.samp_stride;
     int4 sv[SAMPLE_UNROLL];
-    sample_load(S, ((size_t)b * Hkv + h) * f.NB, j0, (f.NB + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE, sv);
+    sample_load(S, ((size_t)b * Hkv + h) * f.NB, j0, (f.NB + stride - 1) / stride, stride, sv);
     for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS) lds.samp.lh[k] = 0;
+    if (EST)
+      for (int k = threadIdx.x; k < HIST2_BINS; k += SAMPLE_THREADS) lds.samp.est.h2[k] = 0;
     block_query_sketch(q, R, Hq, Hkv, basis, basis_per_head, seg, lds.samp.qcode, nullptr,
                        lds.samp.sk);
     const SegGeom g = seg_geom(seg, seq_len, R, Hkv, f.T_max, f.window, f.pool, f.topk);
     if (g.k_eff >= g.n_far) return;             // uniform: no selection needed
-    const int m = (g.n_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
+    const int m = (g.n_far + stride - 1) / stride;
     if (j0 >= m) return;
     __syncthreads();
     const int4 qv = reinterpret_cast<const int4 *>(lds.samp.qcode)[threadIdx.x & 3];
-    sample_bins(sv, qv, j0, m, lds.samp.lh);
+    int keys[SAMPLE_UNROLL];
+    sample_bins(sv, qv, j0, m, lds.samp.lh, keys);
     __syncthreads();
+    if (EST) {                                   // the whole segment's sample is here
+      const int E = sample_estimate(lds.samp.lh, keys, g.n_far, g.k_eff, stride, lds.samp.est);
+      if (threadIdx.x == 0) f.est[seg] = E;
+      return;
+    }
     sample_flush(lds.samp.lh, f.hsamp + (size_t)seg * HIST1_BINS);
     return;
   }
@@ -110,14 +125,19 @@ __global__ __launch_bounds__(SK_THREADS) void front_kernel(const uint16_t *q, co
 
 template <int DT>
 void launch_front_t(const FrontArgs &f, bool cand, int grid, hipStream_t st) {
-  if (cand)
-    front_kernel<DT, true><<<grid, SK_THREADS, 0, st>>>(f.q, f.basis, f.seq_len, f.S, f.nq,
-                                                         f.n_app, f.samp_per_seg, f.R, f.Hkv,
-                                                         f.Hq, f.basis_per_head, f);
+  if (cand && f.est)
+    front_kernel<DT, true, true><<<grid, SK_THREADS, 0, st>>>(f.q, f.basis, f.seq_len, f.S, f.nq,
+                                                               f.n_app, f.samp_per_seg, f.R,
+                                                               f.Hkv, f.Hq, f.basis_per_head, f);
+  else if (cand)
+    front_kernel<DT, true, false><<<grid, SK_THREADS, 0, st>>>(f.q, f.basis, f.seq_len, f.S, f.nq,
+                                                                f.n_app, f.samp_per_seg, f.R,
+                                                                f.Hkv, f.Hq, f.basis_per_head, f);
   else
-    front_kernel<DT, false><<<grid, SK_THREADS, 0, st>>>(f.q, f.basis, f.seq_len, f.S, f.nq,
-                                                          f.n_app, f.samp_per_seg, f.R, f.Hkv,
-                                                          f.Hq, f.basis_per_head, f);
+    front_kernel<DT, false, false><<<grid, SK_THREADS, 0, st>>>(f.q, f.basis, f.seq_len, f.S,
+                                                                 f.nq, f.n_app, f.samp_per_seg,
+                                                                 f.R, f.Hkv, f.Hq,
+                                                                 f.basis_per_head, f);
 }
 
 }  // namespace
@@ -137,11 +157,17 @@ hipError_t launch_step_front(const sks_kv &kv, const Shape &s, const uint16_t *q
   f.seq_len = kv.seq_len;
   const int nseg = s.B * s.R * s.Hkv;
   f.samp_per_seg = 1;
+  f.samp_stride = SAMPLE_STRIDE;
   f.n_samp = 0;
+  f.est = nullptr;
   if (cand) {
     const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
-    const long max_m = (max_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
-    f.samp_per_seg = std::max(1, ceil_div(max_m, SAMPLE_WG_ROWS));
+    if (topk_cand_est_early(s)) {
+      f.est = w.est;                             // one workgroup per segment
+      f.samp_stride = topk_cand_est_stride(s);
+    } else {
+      f.samp_per_seg = std::max(1, ceil_div((max_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE, SAMPLE_WG_ROWS));
+    }
     f.n_samp = f.samp_per_seg * nseg;
   }
   f.nq = nseg;

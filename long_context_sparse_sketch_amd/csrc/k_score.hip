@@ -22,10 +22,12 @@
 // In candidate mode (CAND, without HIST) no score is stored: each row keeps,
 // in its chunk's candidate list of the selection workspace, the entries
 // whose biased score reaches the row's estimate E, as (index, biased score)
-// in index order, and the list's length.  Every workgroup derives E itself
-// from the segment's sample histogram (built beforehand by the selection's
-// sample pass; see k_topk.hip for the rule), so every workgroup of a segment
-// finds the same E.  The final selection pass then needs no filter pass and
+// in index order, and the list's length.  `samp` holds the segments' sample
+// histograms (built beforehand by the selection's sample pass), from which
+// every workgroup derives E itself (block_estimate), so every workgroup of a
+// segment finds the same E; or (EST) the segments' estimates themselves,
+// derived by the step's first launch when one workgroup sampled the whole
+// segment.  The final selection pass then needs no filter pass and
 // no histogram from this pass: it counts the candidates' level-1 bins itself
 // (adding a few bins per workgroup into one histogram per segment, from
 // every workgroup, cost this pass 3 us at 250K in same-address atomics).
@@ -49,16 +51,17 @@ constexpr int SC_UNROLL = 8;                        // rows per lane-quad per st
 constexpr int SC_WAVE_STEP = 16 * SC_UNROLL;        // 128 rows per wave step
 constexpr int SC_BLOCK_STEP = SC_WAVE_STEP * (SC_THREADS / 64);   // 512
 
-template <int R, bool HIST, bool CAND>
+template <int R, bool HIST, bool CAND, bool EST = false>
 __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     const int8_t *__restrict__ qsk, const int8_t *__restrict__ S,
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ scores,
     int32_t *__restrict__ hist1, int32_t *__restrict__ cmax, int n_sub_max, int Hkv, int T_max,
-    int NB, int window, int pool, int topk, const int32_t *__restrict__ hsamp,
+    int NB, int window, int pool, int topk, const int32_t *__restrict__ samp,
     int2 *__restrict__ cand, int32_t *__restrict__ cnt, int force) {
   static_assert(SCORE_CHUNK == TK_SUB, "one chunk maximum per top-k sub-list");
   static_assert(SCORE_CHUNK == 4 * SC_THREADS, "candidate compaction: 4 rounds of 64 per wave");
   static_assert(!(CAND && HIST), "candidate mode builds no histogram");
+  static_assert(!EST || CAND, "a given estimate is candidate mode's");
   __shared__ int lh[HIST ? R * HIST1_BINS : 1];
   __shared__ int lmax[HIST ? R * (SC_THREADS / 64) : 1];
   __shared__ int gcnt[CAND ? R * 16 : 1];                // candidates per 64-token group
@@ -96,25 +99,27 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   for (int i = 0; i < R; ++i)
     qv[i] = *reinterpret_cast<const int4 *>(qsk + ((size_t)(b * R + i) * Hkv + h) * RANK + part * 16);
   // candidate mode: thread t's 8 bins of each row's sample histogram, from
-  // the top bin down (bins 2047 - 8t ... 2040 - 8t), loaded ahead of the stream
-  constexpr int EPER = HIST1_BINS / SC_THREADS;
-  int hsv[CAND ? R : 1][EPER];
-  if (CAND) {
+  // the top bin down (bins 2047 - 8t ... 2040 - 8t), loaded ahead of the
+  // stream -- or (EST) the row's estimate, derived by the step's first launch.
+  // Every workgroup of a segment must use the same E (the final pass relies
+  // on one E per segment): block_estimate gives every workgroup reading the
+  // same bins the same E, even for a workspace that held garbage.
+  static_assert(HIST1_BINS == 8 * SC_THREADS, "eight sample bins per thread");
+  int hsv[CAND && !EST ? R : 1][8];
+  int e_pre[EST ? R : 1];
+  if (EST) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) e_pre[i] = samp[(size_t)(b * R + i) * Hkv + h];
+  } else if (CAND) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int4 *src = reinterpret_cast<const int4 *>(
-          hsamp + ((size_t)(b * R + i) * Hkv + h) * HIST1_BINS + HIST1_BINS - EPER * (threadIdx.x + 1));
+          samp + ((size_t)(b * R + i) * Hkv + h) * HIST1_BINS + HIST1_BINS - 8 * (threadIdx.x + 1));
       const int4 lo4 = src[0], hi4 = src[1];     // ascending bins
       hsv[i][0] = hi4.w; hsv[i][1] = hi4.z; hsv[i][2] = hi4.y; hsv[i][3] = hi4.x;
       hsv[i][4] = lo4.w; hsv[i][5] = lo4.z; hsv[i][6] = lo4.y; hsv[i][7] = lo4.x;
     }
   }
-  // Every workgroup of a segment must derive the same E (the final pass
-  // relies on one E per segment): bins are clamped to [0, 2^18] -- a real
-  // sample never exceeds 2^17 per bin -- so that no sum below can overflow
-  // and the running counts stay monotone even for a workspace that held
-  // garbage.
-  constexpr int HS_MAX = 1 << 18;
 
   const int4 *Sbh = reinterpret_cast<const int4 *>(S + (size_t)bh * NB * RANK) + part;
   int32_t *out[R];
@@ -201,45 +206,18 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     }
   }
   if (CAND) {
-    // Each row's estimate E: the lowest key of the sample histogram's bin
-    // holding the rho-th largest sampled key, rho = 2 k' + 8 with k' the
-    // expected number of sampled entries among the k largest; 0 when fewer
-    // than rho entries were sampled.  force 1: above every key; 2: 0.
+    // Each row's estimate E (block_estimate: the lowest key of the sample
+    // histogram's bin holding the rho-th largest sampled key).
+    if (!EST) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      int sum = 0;
-#pragma unroll
-      for (int k = 0; k < EPER; ++k) sum += min(max(hsv[i][k], 0), HS_MAX);
-      const int incl = wave_incl_add(sum);
-      if (lane == 63) escan[wave] = incl;
-      __syncthreads();
-      int before = 0, tot = 0;
-#pragma unroll
-      for (int w = 0; w < SC_THREADS / 64; ++w) {
-        before += w < wave ? escan[w] : 0;
-        tot += escan[w];
-      }
-      const int m = (nf[i] + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
-      const int kp = nf[i] > 0 ? (int)(((long)ke[i] * m + nf[i] - 1) / nf[i]) : 0;
-      const int rho = 2 * kp + 8;
-      int run = before + incl - sum;             // sampled keys in higher bins
-      const int top = HIST1_BINS - 1 - EPER * (int)threadIdx.x;
-      if (threadIdx.x == 0 && (tot < rho || force)) e_lds[i] = force == 1 ? (1 << 30) : 0;
-      if (!force && tot >= rho && run < rho && run + sum >= rho) {
-        int bin = top - (EPER - 1);
-#pragma unroll
-        for (int k = 0; k < EPER; ++k) {
-          const int c = min(max(hsv[i][k], 0), HS_MAX);
-          if (run < rho && run + c >= rho) bin = top - k;
-          run += c;
-        }
-        e_lds[i] = bin << HIST2_BITS;
-      }
-      __syncthreads();                           // escan is reused by the next row
+      for (int i = 0; i < R; ++i)
+        block_estimate<SC_THREADS>(hsv[i], nf[i], ke[i], SAMPLE_STRIDE, force, escan, &e_lds[i]);
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int E = e_lds[i];
+      // (a given estimate is clamped at 0, so that garbage in the workspace
+      // can never admit the key -1 of a slot without a token)
+      const int E = !EST ? e_lds[i] : force == 1 ? (1 << 30) : force == 2 ? 0 : max(e_pre[i], 0);
 #pragma unroll
       for (int k = 0; k < 4; ++k) cm[i][k] = __ballot(need_sel[i] && ck[i][k] >= E);
     }
@@ -324,7 +302,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
                         const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st,
-                        bool cand, int force) {
+                        bool cand, int force, const int32_t *est) {
   if (cand && !w) return hipErrorInvalidValue;
   int32_t *hist1 = w ? w->hist1 : nullptr;
   int32_t *cmax = w ? w->cmax : nullptr;
@@ -336,7 +314,11 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
   switch (s.R) {
 #define SKS_SCORE_CASE(RR)                                                                     \
   case RR:                                                                                     \
-    if (cand)                                                                                  \
+    if (cand && est)                                                                           \
+      score_kernel<RR, false, true, true><<<grid, SC_THREADS, 0, st>>>(                        \
+          qsk, S, seq_len, nullptr, nullptr, nullptr, n_sub_max, s.Hkv, s.T_max, s.NB, s.window, \
+          s.pool, s.topk, est, w->cand, w->cnt, force);                                        \
+    else if (cand)                                                                             \
       score_kernel<RR, false, true><<<grid, SC_THREADS, 0, st>>>(                              \
           qsk, S, seq_len, nullptr, nullptr, nullptr, n_sub_max, s.Hkv, s.T_max, s.NB, s.window, \
           s.pool, s.topk, w->hsamp, w->cand, w->cnt, force);                                   \

@@ -219,28 +219,40 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(
 
 constexpr int TF_THREADS = 1024;
 
-// Sample pass: workgroup x of segment y scores sampled rows j * 64,
-// j in [1024x, 1024x + 1024), and adds their level-1 bins to the segment's
-// sample histogram (zero at rest; the final pass returns it to zero).
+// Sample pass: workgroup x of segment y scores sampled rows j * stride,
+// j in [512x, 512x + 512), and adds their level-1 bins to the segment's
+// sample histogram (`out`, zero at rest; the final pass returns it to zero).
+// With EST one workgroup takes a segment's whole sample and writes the
+// segment's estimate E to out[seg] instead (sample_estimate).
+template <bool EST>
 __global__ __launch_bounds__(SAMPLE_THREADS) void topk_sample_kernel(
     const int8_t *__restrict__ qsk, const int8_t *__restrict__ S,
-    const int32_t *__restrict__ seq_len, int32_t *__restrict__ hsamp, int R, int Hkv, int T_max,
-    int NB, int window, int pool, int topk) {
+    const int32_t *__restrict__ seq_len, int32_t *__restrict__ out, int R, int Hkv, int T_max,
+    int NB, int window, int pool, int topk, int stride) {
   __shared__ int lh[HIST1_BINS];
+  __shared__ SampleEstLds est;
   const int seg = blockIdx.y;
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
   if (g.k_eff >= g.n_far) return;               // uniform: no selection needed
-  const int m = (g.n_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;   // rows j * 64 < n_far
+  const int m = (g.n_far + stride - 1) / stride;   // rows j * stride < n_far
   const int j0 = blockIdx.x * SAMPLE_WG_ROWS;
   if (j0 >= m) return;
   int4 sv[SAMPLE_UNROLL];
-  sample_load(S, ((size_t)g.b * Hkv + g.h) * NB, j0, m, sv);
+  sample_load(S, ((size_t)g.b * Hkv + g.h) * NB, j0, m, stride, sv);
   for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS) lh[k] = 0;
+  if (EST)
+    for (int k = threadIdx.x; k < HIST2_BINS; k += SAMPLE_THREADS) est.h2[k] = 0;
   const int4 qv = reinterpret_cast<const int4 *>(qsk + (size_t)seg * RANK)[threadIdx.x & 3];
   __syncthreads();
-  sample_bins(sv, qv, j0, m, lh);
+  int keys[SAMPLE_UNROLL];
+  sample_bins(sv, qv, j0, m, lh, keys);
   __syncthreads();
-  sample_flush(lh, hsamp + (size_t)seg * HIST1_BINS);
+  if (EST) {
+    const int E = sample_estimate(lh, keys, g.n_far, g.k_eff, stride, est);
+    if (threadIdx.x == 0) out[seg] = E;
+    return;
+  }
+  sample_flush(lh, out + (size_t)seg * HIST1_BINS);
 }
 
 __global__ __launch_bounds__(TF_THREADS) void topk_final_kernel(
@@ -268,7 +280,8 @@ size_t hist_region_bytes(const Shape &s) {
 size_t topk_scratch_bytes(const Shape &s) {
   const size_t nseg = (size_t)s.B * s.R * s.Hkv;
   const size_t n_sub = (size_t)ceil_div(s.NB, TK_SUB);
-  return align_up(nseg * n_sub * 4, 256) + align_up(nseg * n_sub * TK_SUB * sizeof(int2), 256);
+  return align_up(nseg * n_sub * 4, 256) + align_up(nseg * n_sub * TK_SUB * sizeof(int2), 256) +
+         align_up(nseg * 4, 256);
 }
 
 TopkWs topk_ws_carve(const Shape &s, void *ws) {
@@ -291,6 +304,8 @@ TopkWs topk_ws_carve(const Shape &s, void *ws) {
   w.cnt = reinterpret_cast<int32_t *>(p);
   p += align_up(nseg * n_sub * 4, 256);
   w.cand = reinterpret_cast<int2 *>(p);
+  p += align_up(nseg * n_sub * TK_SUB * sizeof(int2), 256);
+  w.est = reinterpret_cast<int32_t *>(p);
   w.nchunk = (int)n_sub;
   w.attn = base + hist_region_bytes(s) + topk_scratch_bytes(s);
   return w;
@@ -339,15 +354,27 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
   return hipGetLastError();
 }
 
-// Candidate mode pays off for single-row steps where the final pass cannot
-// simply take every far entry (more than TF_REGS of them) and the batch
-// streams enough sketch rows (2^20) for the saved score stores to outweigh
-// the two extra launches.  (With verify rows the candidate score pass keeps
-// more state per lane and measured slower than storing the scores.)
+// Candidate mode pays off where the final pass cannot simply take every far
+// entry (more than TF_REGS of them) and the batch streams enough sketch rows
+// (2^20) for the saved score stores to outweigh the sample work.  With verify
+// rows it pays only when the step's first launch derives the estimates (one
+// sample workgroup per segment): a score pass that derives three rows'
+// estimates in every workgroup measured slower than storing the scores.
 bool topk_cand_preferred(const Shape &s) {
   const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   const long nseg = (long)s.B * s.R * s.Hkv;
-  return s.R == 1 && max_far > TF_REGS && nseg * max_far >= (1L << 20);
+  return max_far > TF_REGS && nseg * max_far >= (1L << 20) &&
+         (s.R == 1 || topk_cand_est_early(s));
+}
+
+bool topk_cand_est_early(const Shape &s) {
+  const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
+  return max_far <= (long)SAMPLE_WG_ROWS * SAMPLE_EST_STRIDE;
+}
+
+int topk_cand_est_stride(const Shape &s) {
+  const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
+  return max_far <= (long)SAMPLE_WG_ROWS * SAMPLE_STRIDE ? SAMPLE_STRIDE : SAMPLE_EST_STRIDE;
 }
 
 hipError_t launch_topk_sample(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
@@ -355,9 +382,14 @@ hipError_t launch_topk_sample(const int8_t *qsk, const int8_t *S, const int32_t 
   const int nseg = s.B * s.R * s.Hkv;
   const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   const long max_m = (max_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
-  if (max_m > 0)
-    topk_sample_kernel<<<dim3(ceil_div(max_m, SAMPLE_WG_ROWS), nseg), SAMPLE_THREADS, 0, st>>>(
-        qsk, S, seq_len, w.hsamp, s.R, s.Hkv, s.T_max, s.NB, s.window, s.pool, s.topk);
+  if (max_m > 0 && topk_cand_est_early(s))
+    topk_sample_kernel<true><<<dim3(1, nseg), SAMPLE_THREADS, 0, st>>>(
+        qsk, S, seq_len, w.est, s.R, s.Hkv, s.T_max, s.NB, s.window, s.pool, s.topk,
+        topk_cand_est_stride(s));
+  else if (max_m > 0)
+    topk_sample_kernel<false><<<dim3(ceil_div(max_m, SAMPLE_WG_ROWS), nseg), SAMPLE_THREADS, 0, st>>>(
+        qsk, S, seq_len, w.hsamp, s.R, s.Hkv, s.T_max, s.NB, s.window, s.pool, s.topk,
+        SAMPLE_STRIDE);
   return hipGetLastError();
 }
 

@@ -179,14 +179,19 @@ hipError_t enqueue_step(const sks_kv &kv, const sks::Shape &s, const sks_step &s
                         const sks::TopkWs &w, hipStream_t hs) {
   const bool dense = (flags & SKS_STEP_DENSE) != 0;
   const bool cand = !dense && (flags & SKS_STEP_NO_SCORES) && sks::topk_cand_preferred(s);
+  // the first launch derives the estimates itself when one workgroup samples
+  // each segment; otherwise it leaves sample histograms for the score pass
+  const bool est = cand && sks::topk_cand_est_early(s);
   hipError_t e = sks::launch_step_front(kv, s, st.q, st.Hq, st.basis, st.basis_per_head,
                                         st.key_scale, st.qsk, st.qscale, st.S, st.Kp, st.Vp,
                                         (flags & SKS_STEP_APPEND) != 0, cand, w, hs);
   if (!dense) {
     if (cand) {
-      if (e == hipSuccess) e = sks::launch_score(st.qsk, st.S, kv.seq_len, s, nullptr, &w, hs, true);
-      // (the sample histograms are cleared by the attention's merge launch,
-      // off the selection's critical path)
+      if (e == hipSuccess)
+        e = sks::launch_score(st.qsk, st.S, kv.seq_len, s, nullptr, &w, hs, true, 0,
+                              est ? w.est : nullptr);
+      // (sample histograms are cleared by the attention's merge launch, off
+      // the selection's critical path)
       if (e == hipSuccess)
         e = sks::launch_topk_cand(st.qsk, st.S, st.scores, kv.seq_len, s, st.idx, st.n_sel, w, hs,
                                   false);
@@ -198,8 +203,8 @@ hipError_t enqueue_step(const sks_kv &kv, const sks::Shape &s, const sks_step &s
   }
   if (e == hipSuccess)
     e = sks::launch_attn(st.q, st.Hq, kv, s, st.idx, st.Kp, st.Vp, st.sm_scale, st.out, st.lse,
-                         w, hs, dense, cand ? w.hsamp : nullptr,
-                         cand ? (long)s.B * s.R * s.Hkv * sks::HIST1_BINS : 0);
+                         w, hs, dense, cand && !est ? w.hsamp : nullptr,
+                         cand && !est ? (long)s.B * s.R * s.Hkv * sks::HIST1_BINS : 0);
   return e;
 }
 
@@ -387,7 +392,9 @@ int sks_score_candidates(const int8_t *qsk, const int8_t *S, const sks_kv *kv,
   const int force = (flags & SKS_CAND_TEST_HIGH) ? 1 : (flags & SKS_CAND_TEST_ZERO) ? 2 : 0;
   if (!(flags & SKS_CAND_KEEP_ESTIMATE) && !force)
     e = sks::launch_topk_sample(qsk, S, kv->seq_len, s, w, hs);
-  if (e == hipSuccess) e = sks::launch_score(qsk, S, kv->seq_len, s, nullptr, &w, hs, true, force);
+  if (e == hipSuccess)
+    e = sks::launch_score(qsk, S, kv->seq_len, s, nullptr, &w, hs, true, force,
+                          sks::topk_cand_est_early(s) ? w.est : nullptr);
   return hip_status(e, "sks_score_candidates");
 }
 
@@ -407,8 +414,9 @@ int sks_topk_select_candidates(const int8_t *qsk, const int8_t *S, const sks_kv 
                 sks::TK_MAX_SUBS * sks::TK_SUB);
   TRY(check_ws(ws, ws_bytes_given, topk_need(s)));
   const sks::TopkWs w = sks::topk_ws_carve(s, ws);
+  // (sample histograms are left only where no estimate was derived at once)
   return hip_status(sks::launch_topk_cand(qsk, S, scores, kv->seq_len, s, idx, n_sel, w,
-                                          (hipStream_t)stream),
+                                          (hipStream_t)stream, !sks::topk_cand_est_early(s)),
                     "sks_topk_select_candidates");
 }
 

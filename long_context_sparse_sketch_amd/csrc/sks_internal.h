@@ -25,7 +25,8 @@ constexpr int TK_CHUNK = 4096;           // tokens per top-k filter workgroup
 constexpr int TK_SUB = 1024;             // tokens per filter wave (one candidate sub-list)
 constexpr int TK_MAX_SUBS = 8192;        // sub-lists per segment the final pass can index
 constexpr int ATTN_MAX_G = 8;            // query heads per KV head supported
-constexpr int SAMPLE_STRIDE = 64;        // candidate mode samples one far entry in 64
+constexpr int SAMPLE_STRIDE = 64;        // candidate mode samples one far entry in 64 ...
+constexpr int SAMPLE_EST_STRIDE = 128;   // ... or in 128 where one workgroup samples a segment
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
@@ -169,6 +170,101 @@ __device__ __forceinline__ int wave_incl_max(int x) {
   return max(x, max(row > 0 ? r0 : 0, max(row > 1 ? r1 : 0, row > 2 ? r2 : 0)));
 }
 
+// ---------------------------------------------------------------- candidate estimate
+// Candidate mode's estimate E of a row's k-th largest biased key, from the
+// row's sample histogram (every stride-th far entry scored and counted by
+// level-1 bin).  With m = ceil(n_far / stride) sampled entries and
+// k' = ceil(k_eff m / n_far) the expected number of them among the k largest,
+// E is the lowest key of the bin holding the rho-th largest sampled key,
+// rho = 2 k' + 8; E = 0 when fewer than rho entries were sampled.  force 1
+// gives E above every key, 2 gives 0.  E decides only how much work the
+// selection does, never its result.
+//
+// NT threads (8 bins each) hold the histogram, thread t bins 2047 - 8t down to
+// 2040 - 8t in hv.  Bins are clamped to [0, 2^18] (a real sample never
+// exceeds 2^17 per bin), so that a histogram holding garbage cannot overflow
+// the sums and every workgroup reading the same bins finds the same E.
+// escan holds NT / 64 ints; *e_out (LDS) receives E and, when given,
+// *rank_out (LDS) the rank of the rho-th largest sampled key inside E's bin,
+// counted from the top of the bin (1 ..), or 0 when E is not a bin's lower
+// edge found this way.  Two barriers: the results are readable after the
+// call, and escan may be used again.
+template <int NT>
+__device__ void block_estimate(const int (&hv)[8], int n_far, int k_eff, int stride, int force,
+                               int *escan, int *e_out, int *rank_out = nullptr) {
+  static_assert(NT * 8 == HIST1_BINS, "eight bins per thread");
+  constexpr int HS_MAX = 1 << 18;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sum += min(max(hv[k], 0), HS_MAX);
+  const int incl = wave_incl_add(sum);
+  if (lane == 63) escan[wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    before += w < wave ? escan[w] : 0;
+    tot += escan[w];
+  }
+  const int m = (n_far + stride - 1) / stride;
+  const int kp = n_far > 0 ? (int)(((long)k_eff * m + n_far - 1) / n_far) : 0;
+  const int rho = 2 * kp + 8;
+  int run = before + incl - sum;                 // sampled keys in higher bins
+  const int top = HIST1_BINS - 1 - 8 * (int)threadIdx.x;
+  if (threadIdx.x == 0 && (tot < rho || force)) {
+    *e_out = force == 1 ? (1 << 30) : 0;
+    if (rank_out) *rank_out = 0;
+  }
+  if (!force && tot >= rho && run < rho && run + sum >= rho) {
+    int bin = top - 7, rank = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = min(max(hv[k], 0), HS_MAX);
+      if (run < rho && run + c >= rho) {
+        bin = top - k;
+        rank = rho - run;
+      }
+      run += c;
+    }
+    *e_out = bin << HIST2_BITS;
+    if (rank_out) *rank_out = rank;
+  }
+  __syncthreads();
+}
+
+// Top-down rank search over a histogram that NT threads hold PER bins each,
+// thread t the bins at positions PER t .. PER t + PER - 1 counted from the
+// top (position 0: the highest bin): writes *pos_out = the position at which
+// the running count from the top first reaches need (1 <= need), or -1 when
+// the total stays below need.  Counts are non-negative and sum below 2^31.
+// Two barriers: *pos_out is readable after the call, and escan (NT / 64
+// ints) may be used again.
+template <int NT, int PER>
+__device__ void block_top_rank(const int (&v)[PER], int need, int *escan, int *pos_out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) sum += v[k];
+  const int incl = wave_incl_add(sum);
+  if (lane == 63) escan[wave] = incl;
+  if (threadIdx.x == 0) *pos_out = -1;
+  __syncthreads();
+  int run = incl - sum;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) run += w < wave ? escan[w] : 0;
+  if (run < need && run + sum >= need) {
+    int pos = PER * (int)threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if (run < need && run + v[k] >= need) pos = PER * (int)threadIdx.x + k;
+      run += v[k];
+    }
+    *pos_out = pos;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- selection threshold
 // Threshold search over a histogram held in registers, lane l holding bins
 // [l*PER, (l+1)*PER) in v[].  No barriers.  The histogram is validated first
@@ -247,7 +343,7 @@ hipError_t launch_fill(int32_t *p, size_t n, hipStream_t st);
 struct TopkWs;
 hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
                         const Shape &s, int32_t *scores, const TopkWs *w, hipStream_t st,
-                        bool cand = false, int force = 0);
+                        bool cand = false, int force = 0, const int32_t *est = nullptr);
 
 struct TopkWs {
   int32_t *hist1;     // [nseg][HIST1_BINS], zero at rest
@@ -259,6 +355,7 @@ struct TopkWs {
   char *attn;         // start of the attention partials (after the selection scratch)
   int32_t *cnt;       // [nseg][nchunk]
   int2 *cand;         // [nseg][nchunk * TK_SUB]
+  int32_t *est;       // [nseg]: candidate mode's estimate E, when the step's first launch derives it
   int nchunk;         // sub-lists per segment
 };
 TopkWs topk_ws_carve(const Shape &s, void *ws);
@@ -272,6 +369,12 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
 // `scores` when its estimate was too high and returns the sample histograms
 // to zero (with zero_hsamp; else a later launch must).
 bool topk_cand_preferred(const Shape &s);
+// Whether one sample workgroup covers each segment's whole sample (at most
+// SAMPLE_WG_ROWS entries at a stride of 64, or else 128), so that the sample
+// pass derives the estimate E itself and the score pass reads it from
+// TopkWs::est; and that stride.
+bool topk_cand_est_early(const Shape &s);
+int topk_cand_est_stride(const Shape &s);
 hipError_t launch_topk_sample(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,
                               const Shape &s, const TopkWs &w, hipStream_t st);
 hipError_t launch_topk_cand(const int8_t *qsk, const int8_t *S, int32_t *scores,

@@ -141,10 +141,11 @@ __device__ void block_threshold_pair(int v0, int v1, int need, int n, int *scrat
 }
 
 // ---------------------------------------------------------------- sample pass
-// Candidate mode's sample: sampled rows j * SAMPLE_STRIDE of a segment's far
-// region, j in [j0, j0 + SAMPLE_WG_ROWS), scored against the segment's query
-// code, their level-1 bins counted in an LDS histogram and then added to the
-// segment's sample histogram (zero at rest).  A quad of lanes per sampled
+// Candidate mode's sample: sampled rows j * stride of a segment's far region,
+// j in [j0, j0 + SAMPLE_WG_ROWS), scored against the segment's query code,
+// their level-1 bins counted in an LDS histogram and then added to the
+// segment's sample histogram (zero at rest), or (one workgroup per segment)
+// turned into the segment's estimate at once.  A quad of lanes per sampled
 // sketch row, 16 bytes each, SAMPLE_UNROLL rows per quad in flight.
 constexpr int SAMPLE_THREADS = 256;
 constexpr int SAMPLE_UNROLL = 8;
@@ -152,20 +153,22 @@ constexpr int SAMPLE_WG_ROWS = SAMPLE_THREADS / 4 * SAMPLE_UNROLL;   // 512 samp
 
 // Loads of this thread's sampled rows (issued before anything uses them).
 __device__ __forceinline__ void sample_load(const int8_t *__restrict__ S, size_t seg_row0, int j0,
-                                            int m, int4 (&sv)[SAMPLE_UNROLL]) {
+                                            int m, int stride, int4 (&sv)[SAMPLE_UNROLL]) {
   const int part = threadIdx.x & 3, quad = threadIdx.x >> 2;
   constexpr int QUADS = SAMPLE_THREADS / 4;
   const int4 *Sseg = reinterpret_cast<const int4 *>(S + seg_row0 * RANK) + part;
 #pragma unroll
   for (int u = 0; u < SAMPLE_UNROLL; ++u) {
     const int j = j0 + u * QUADS + quad;
-    sv[u] = j < m ? Sseg[(size_t)j * SAMPLE_STRIDE * 4] : make_int4(0, 0, 0, 0);
+    sv[u] = j < m ? Sseg[(size_t)j * stride * 4] : make_int4(0, 0, 0, 0);
   }
 }
 
-// Their scores' level-1 bins into lh (this thread's 16 bytes of the query code: qv).
+// Their scores' level-1 bins into lh (this thread's 16 bytes of the query
+// code: qv); keys[u] receives the biased key of the thread's row u (lane 0 of
+// each quad only; -1 for the other lanes and for rows past m).
 __device__ __forceinline__ void sample_bins(const int4 (&sv)[SAMPLE_UNROLL], int4 qv, int j0, int m,
-                                            int *lh) {
+                                            int *lh, int (&keys)[SAMPLE_UNROLL]) {
   const int part = threadIdx.x & 3, quad = threadIdx.x >> 2;
   constexpr int QUADS = SAMPLE_THREADS / 4;
 #pragma unroll
@@ -176,8 +179,46 @@ __device__ __forceinline__ void sample_bins(const int4 (&sv)[SAMPLE_UNROLL], int
     acc = __builtin_amdgcn_sdot4(sv[u].w, qv.w, acc, false);
     acc = quad_sum_i(acc);
     const int j = j0 + u * QUADS + quad;
-    if (part == 0 && j < m) atomicAdd(&lh[biased_key(acc) >> HIST2_BITS], 1);
+    keys[u] = part == 0 && j < m ? biased_key(acc) : -1;
+    if (keys[u] >= 0) atomicAdd(&lh[keys[u] >> HIST2_BITS], 1);
   }
+}
+
+// LDS of a sample workgroup that derives its segment's estimate itself.
+struct SampleEstLds {
+  int h2[HIST2_BINS];
+  int escan[SAMPLE_THREADS / 64];
+  int e, rank, pos;
+};
+
+// A segment's estimate E from its whole sample, held by one workgroup: the
+// level-1 histogram lh (complete) and the sampled keys (sample_bins).  E is
+// the rho-th largest sampled key itself (block_estimate's rule without its
+// rounding down to the lower edge of that key's level-1 bin): block_estimate
+// finds the bin and the key's rank in it, and a level-2 histogram of the low
+// bits of the bin's sampled keys finds the key.  L.h2 must be zero on entry.
+// Returns E in every thread.
+__device__ int sample_estimate(const int *lh, const int (&keys)[SAMPLE_UNROLL], int n_far,
+                               int k_eff, int stride, SampleEstLds &L) {
+  int hv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) hv[k] = lh[HIST1_BINS - 1 - 8 * (int)threadIdx.x - k];
+  block_estimate<SAMPLE_THREADS>(hv, n_far, k_eff, stride, 0, L.escan, &L.e, &L.rank);
+  const int e1 = L.e, rank = L.rank;
+  if (rank <= 0) return e1;                      // uniform: no sampled key to refine to
+  const int b1 = e1 >> HIST2_BITS;
+#pragma unroll
+  for (int u = 0; u < SAMPLE_UNROLL; ++u)
+    if (keys[u] >= 0 && (keys[u] >> HIST2_BITS) == b1) atomicAdd(&L.h2[keys[u] & (HIST2_BINS - 1)], 1);
+  __syncthreads();
+  constexpr int PER2 = HIST2_BINS / SAMPLE_THREADS;
+  int v[PER2];
+#pragma unroll
+  for (int k = 0; k < PER2; ++k) v[k] = L.h2[HIST2_BINS - 1 - PER2 * (int)threadIdx.x - k];
+  block_top_rank<SAMPLE_THREADS, PER2>(v, rank, L.escan, &L.pos);
+  const int pos = L.pos;
+  // (the bin holds at least `rank` sampled keys, so pos >= 0)
+  return pos >= 0 ? e1 | (HIST2_BINS - 1 - pos) : e1;
 }
 
 __device__ __forceinline__ void sample_flush(const int *lh, int32_t *__restrict__ hsamp_seg) {

@@ -1,6 +1,7 @@
 """GPU parity of whole decode steps on seeded random long-context shapes:
 far regions of 8K to 320K entries per row and at least 2^20 in all, so that
-single-row steps without stored scores take the selection's candidate mode
+steps without stored scores take the selection's candidate mode (single-row
+steps, and verify-row steps of at most 65,536 far entries per row)
 ("What it took" on the page "8 agents x 250K context, concurrently, on two
 3090s": score every token, pick the top ~2K).  Each case draws the batch, the
 verify rows, the query group, pooling, KV storage, window, top-k (up to
@@ -43,7 +44,7 @@ def draw(seed):
         B = int(rng.integers(1, 5))
         nseg = B * R * Hkv
         # the step's candidate mode: more than 8,192 far entries per row and
-        # at least 2^20 over the batch's segments (for single-row steps)
+        # at least 2^20 over the batch's segments
         need_far = max(8193, -(-(1 << 20) // nseg))
         L_min = window + pool * need_far + 1
         L = int(rng.integers(L_min, L_min + 60000))
