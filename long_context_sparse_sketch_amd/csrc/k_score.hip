@@ -233,22 +233,35 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   if (CAND) {
     // Lane 4q + p holds token 16p + q of each group: its rank among the
     // group's candidates counts the set bits of parts p' < p, then those of
-    // part p below quad q.
+    // part p below quad q.  The groups' offsets in the chunk's list: lane
+    // 16 (i % 4) + g of every wave scans group g of row i inside its row of
+    // 16 lanes, and the offsets are read back by lane index.
     constexpr unsigned long long PART0 = 0x1111111111111111ull;
     const unsigned long long before_q = (1ull << (4 * quad)) - 1ull;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int gincl[(R + 3) / 4], gv[(R + 3) / 4];
+#pragma unroll
+    for (int r4 = 0; r4 < (R + 3) / 4; ++r4) {
+      const int ii = 4 * r4 + (lane >> 4);
+      gv[r4] = ii < R ? gcnt[ii * 16 + (lane & 15)] : 0;
+      int x = gv[r4];
+      x += dpp_shr<1>(x);
+      x += dpp_shr<2>(x);
+      x += dpp_shr<4>(x);
+      x += dpp_shr<8>(x);
+      gincl[r4] = x;
+    }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       if (!need_sel[i]) continue;                  // uniform: the row selects everything
       const size_t seg = (size_t)(b * R + i) * Hkv + h;
       int2 *dst = cand + (seg * n_sub_max + blockIdx.x) * TK_SUB;
-      int tot = 0;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) tot += gcnt[i * 16 + k];
+      const int tot = __builtin_amdgcn_readlane(gincl[i / 4], 16 * (i % 4) + 15);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int g = (k >> 1) * 8 + wave * 2 + (k & 1);
-        int off = 0;
-        for (int j = 0; j < g; ++j) off += gcnt[i * 16 + j];
+        const int g = (k >> 1) * 8 + wv * 2 + (k & 1);
+        const int off = __builtin_amdgcn_readlane(gincl[i / 4], 16 * (i % 4) + g) -
+                        __builtin_amdgcn_readlane(gv[i / 4], 16 * (i % 4) + g);
         const unsigned long long M = cm[i][k];
         if ((M >> lane) & 1ull) {
           int rank = __popcll(M & (PART0 << part) & before_q);
