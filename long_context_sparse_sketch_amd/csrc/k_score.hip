@@ -145,11 +145,15 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   int it = 0;
   for (int base = c0 + wave * SC_WAVE_STEP; base < c1; base += SC_BLOCK_STEP, ++it) {
     int4 sv[SC_UNROLL];
+    // Every load is issued, and all of them before any use: a load under a
+    // branch, or one the scheduler moves next to its use, is waited for
+    // before the next one is issued.  Rows past the chunk's end read its last
+    // row instead; their results are never used (keys, histogram counts and
+    // stored scores all stop at the row's far count).
 #pragma unroll
-    for (int u = 0; u < SC_UNROLL; ++u) {
-      const int t = base + u * 16 + quad;
-      sv[u] = t < c1 ? load_stream(&Sbh[(size_t)t * 4]) : make_int4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < SC_UNROLL; ++u)
+      sv[u] = load_stream(&Sbh[(size_t)min(base + u * 16 + quad, c1 - 1) * 4]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       int acc[SC_UNROLL];
