@@ -57,7 +57,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     const int32_t *__restrict__ seq_len, int32_t *__restrict__ scores,
     int32_t *__restrict__ hist1, int32_t *__restrict__ cmax, int n_sub_max, int Hkv, int T_max,
     int NB, int window, int pool, int topk, const int32_t *__restrict__ samp,
-    int2 *__restrict__ cand, int32_t *__restrict__ cnt, int force) {
+    int2 *__restrict__ cand, int32_t *__restrict__ cnt, int force, int32_t *__restrict__ est_out) {
   static_assert(SCORE_CHUNK == TK_SUB, "one chunk maximum per top-k sub-list");
   static_assert(SCORE_CHUNK == 4 * SC_THREADS, "candidate compaction: 4 rounds of 64 per wave");
   static_assert(!(CAND && HIST), "candidate mode builds no histogram");
@@ -216,6 +216,9 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 #pragma unroll
       for (int i = 0; i < R; ++i)
         block_estimate<SC_THREADS>(hsv[i], nf[i], ke[i], SAMPLE_STRIDE, force, escan, &e_lds[i]);
+      // the segment's E for the final pass (every workgroup derived the same)
+      if (est_out && blockIdx.x == 0 && threadIdx.x < R)
+        est_out[(size_t)(b * R + threadIdx.x) * Hkv + h] = e_lds[threadIdx.x];
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -334,19 +337,19 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
     if (cand && est)                                                                           \
       score_kernel<RR, false, true, true><<<grid, SC_THREADS, 0, st>>>(                        \
           qsk, S, seq_len, nullptr, nullptr, nullptr, n_sub_max, s.Hkv, s.T_max, s.NB, s.window, \
-          s.pool, s.topk, est, w->cand, w->cnt, force);                                        \
+          s.pool, s.topk, est, w->cand, w->cnt, force, nullptr);                               \
     else if (cand)                                                                             \
       score_kernel<RR, false, true><<<grid, SC_THREADS, 0, st>>>(                              \
           qsk, S, seq_len, nullptr, nullptr, nullptr, n_sub_max, s.Hkv, s.T_max, s.NB, s.window, \
-          s.pool, s.topk, w->hsamp, w->cand, w->cnt, force);                                   \
+          s.pool, s.topk, w->hsamp, w->cand, w->cnt, force, w->est);                           \
     else if (hist1)                                                                            \
       score_kernel<RR, true, false><<<grid, SC_THREADS, 0, st>>>(                              \
           qsk, S, seq_len, scores, hist1, cmax, n_sub_max, s.Hkv, s.T_max, s.NB, s.window,     \
-          s.pool, s.topk, nullptr, nullptr, nullptr, 0);                                       \
+          s.pool, s.topk, nullptr, nullptr, nullptr, 0, nullptr);                              \
     else                                                                                       \
       score_kernel<RR, false, false><<<grid, SC_THREADS, 0, st>>>(                             \
           qsk, S, seq_len, scores, nullptr, nullptr, 0, s.Hkv, s.T_max, s.NB, s.window,        \
-          s.pool, s.topk, nullptr, nullptr, nullptr, 0);                                       \
+          s.pool, s.topk, nullptr, nullptr, nullptr, 0, nullptr);                              \
     break;
     SKS_SCORE_CASE(1)
     SKS_SCORE_CASE(2)

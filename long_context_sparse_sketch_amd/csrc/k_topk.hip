@@ -400,6 +400,7 @@ hipError_t launch_topk_cand(const int8_t *qsk, const int8_t *S, int32_t *scores,
   FinalArgs a = final_args(scores, seq_len, s, idx, n_sel, w);
   a.cand_mode = 1;
   a.hsamp = w.hsamp;
+  a.est = w.est;
   a.zero_hsamp = zero_hsamp ? 1 : 0;
   a.qsk = qsk;
   a.S = S;

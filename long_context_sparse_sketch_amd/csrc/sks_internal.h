@@ -27,6 +27,7 @@ constexpr int TK_MAX_SUBS = 8192;        // sub-lists per segment the final pass
 constexpr int ATTN_MAX_G = 8;            // query heads per KV head supported
 constexpr int SAMPLE_STRIDE = 64;        // candidate mode samples one far entry in 64 ...
 constexpr int SAMPLE_EST_STRIDE = 128;   // ... or in 128 where one workgroup samples a segment
+constexpr int CAND_FINE_BITS = 5;        // candidate mode's final pass: bins of 32 keys above E
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }

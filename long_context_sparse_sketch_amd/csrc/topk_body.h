@@ -243,6 +243,8 @@ struct FinalArgs {
   int cand_mode;
   int32_t *hsamp;   // candidate mode: the sample histograms, returned to zero here
   int zero_hsamp;   // ... unless 0: then a later launch of the step clears them
+  const int32_t *est;   // candidate mode: each segment's estimate E (written by the score pass
+                        // or, early estimates, by the sample pass)
   const int8_t *qsk, *S;
   int32_t *rescore;
 };
@@ -331,7 +333,9 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
       hv[4 * k + 3] = w.w;
     }
   }
-  // candidate mode: the level-1 histogram of the candidates, built in LDS
+  // candidate mode: the estimate the candidates were kept with (clamped as
+  // the score pass clamps it), and the candidates' histogram, built in LDS
+  const int e_cand = cmode && a.est ? max(a.est[seg], 0) : 0;
   if (cmode)
     for (int k = threadIdx.x; k < hpad_size<HIST1_BINS>(); k += TF_THREADS) h1[k] = 0;
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
@@ -534,18 +538,37 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
       // here and searched by all waves), then a level-2 histogram of the low
       // bits of the keys in bin b1, which sit in registers.  The counts below
       // check the guess against the data before it is used.
+      // Candidate mode bins the keys relative to the estimate E instead, in
+      // bins of 2^CAND_FINE_BITS (the top bin takes every key from
+      // E + 2047 * 2^CAND_FINE_BITS up): the candidates then spread over
+      // many bins instead of a few dozen, so that the histogram's atomics
+      // rarely collide, and the second level is 2^CAND_FINE_BITS bins that
+      // one wave searches.  A key below E (an estimate that is not the one
+      // the candidates were kept with) lands in bin 0 and fails the check.
       for (int k = threadIdx.x; k < hpad_size<HIST2_BINS>(); k += TF_THREADS) h2[k] = 0;
+      auto fbin = [&](int key) {
+        return min(max(key - e_cand, 0) >> CAND_FINE_BITS, HIST1_BINS - 1);
+      };
       if (cmode) {
 #pragma unroll
         for (int q = 0; q < TF_PERT; ++q)
-          if (c[q].y >= 0) atomicAdd(&h1[hpad<HIST1_BINS>(c[q].y >> HIST2_BITS)], 1);
+          if (c[q].y >= 0) atomicAdd(&h1[hpad<HIST1_BINS>(fbin(c[q].y))], 1);
         __syncthreads();
         block_threshold_bin<TF_WAVES>(h1, g.k_eff, m, sc_pre, res);   // ends with a barrier
       } else {
         block_threshold_pair<TF_WAVES>(h1p.x, h1p.y, g.k_eff, g.n_far, sc_pre, res);
       }
       const int b1 = res[0];
-      if (b1 >= 0) {
+      constexpr int FINE = 1 << CAND_FINE_BITS;
+      static_assert(FINE <= 64, "one bin per lane");
+      const bool fine_ok = b1 >= 0 && b1 < HIST1_BINS - 1;   // uniform
+      if (cmode) {
+        if (fine_ok) {
+#pragma unroll
+          for (int q = 0; q < TF_PERT; ++q)
+            if (c[q].y >= 0 && fbin(c[q].y) == b1) atomicAdd(&h2[(c[q].y - e_cand) & (FINE - 1)], 1);
+        }
+      } else if (b1 >= 0) {
 #pragma unroll
         for (int q = 0; q < TF_PERT; ++q)
           if ((c[q].y >> HIST2_BITS) == b1)
@@ -554,9 +577,15 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
       __syncthreads();
       if (wave == 0) {
         int T = -1;
-        if (b1 >= 0) {
-          int above;
-          bool valid;
+        int above;
+        bool valid;
+        if (cmode) {
+          if (fine_ok) {
+            int v[1] = {lane < FINE ? h2[lane] : 0};
+            const int b2 = wave_threshold_regs<1>(v, res[1], res[2], above, valid);
+            if (valid) T = e_cand + (b1 << CAND_FINE_BITS) + b2;
+          }
+        } else if (b1 >= 0) {
           const int b2 = wave_threshold_bin_valid<HIST2_BINS>(h2, res[1], res[2], above, valid);
           if (valid) T = (b1 << HIST2_BITS) | b2;
         }
@@ -738,6 +767,7 @@ inline FinalArgs final_args(const int32_t *scores, const int32_t *seq_len, const
   a.cand_mode = 0;
   a.hsamp = nullptr;
   a.zero_hsamp = 1;
+  a.est = nullptr;
   a.qsk = nullptr;
   a.S = nullptr;
   a.rescore = nullptr;
