@@ -48,7 +48,7 @@ struct FrontArgs {
   uint16_t *Kp, *Vp;
   // the sample pass
   int32_t *hsamp;
-  int32_t *est;
+  int32_t *est;   // (EST) the segments' selection records: E in the first int of each
 };
 
 struct SampleLds {
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(SK_THREADS) void front_kernel(const uint16_t *q, co
     __syncthreads();
     if (EST) {                                   // the whole segment's sample is here
       const int E = sample_estimate(lds.samp.lh, keys, g.n_far, g.k_eff, stride, lds.samp.est);
-      if (threadIdx.x == 0) f.est[seg] = E;
+      if (threadIdx.x == 0) f.est[4 * seg] = E;
       return;
     }
     sample_flush(lds.samp.lh, f.hsamp + (size_t)seg * HIST1_BINS);
@@ -163,7 +163,7 @@ hipError_t launch_step_front(const sks_kv &kv, const Shape &s, const uint16_t *q
   if (cand) {
     const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
     if (topk_cand_est_early(s)) {
-      f.est = w.est;                             // one workgroup per segment
+      f.est = w.counters;                        // one workgroup per segment
       f.samp_stride = topk_cand_est_stride(s);
     } else {
       f.samp_per_seg = std::max(1, ceil_div((max_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE, SAMPLE_WG_ROWS));

@@ -25,9 +25,10 @@
 // in index order, and the list's length.  `samp` holds the segments' sample
 // histograms (built beforehand by the selection's sample pass), from which
 // every workgroup derives E itself (block_estimate), so every workgroup of a
-// segment finds the same E; or (EST) the segments' estimates themselves,
-// derived by the step's first launch when one workgroup sampled the whole
-// segment.  The final selection pass then needs no filter pass and
+// segment finds the same E; or (EST) the segments' selection records, whose
+// first int holds the estimate derived by the sample pass when one workgroup
+// sampled the whole segment (a derived E is recorded there as well, for the
+// final pass).  The final selection pass then needs no filter pass and
 // no histogram from this pass: it counts the candidates' level-1 bins itself
 // (adding a few bins per workgroup into one histogram per segment, from
 // every workgroup, cost this pass 3 us at 250K in same-address atomics).
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   int e_pre[EST ? R : 1];
   if (EST) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) e_pre[i] = samp[(size_t)(b * R + i) * Hkv + h];
+    for (int i = 0; i < R; ++i) e_pre[i] = samp[4 * ((size_t)(b * R + i) * Hkv + h)];
   } else if (CAND) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -216,9 +217,10 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 #pragma unroll
       for (int i = 0; i < R; ++i)
         block_estimate<SC_THREADS>(hsv[i], nf[i], ke[i], SAMPLE_STRIDE, force, escan, &e_lds[i]);
-      // the segment's E for the final pass (every workgroup derived the same)
+      // the segment's E for the final pass, in its counters record (every
+      // workgroup derived the same)
       if (est_out && blockIdx.x == 0 && threadIdx.x < R)
-        est_out[(size_t)(b * R + threadIdx.x) * Hkv + h] = e_lds[threadIdx.x];
+        est_out[4 * ((size_t)(b * R + threadIdx.x) * Hkv + h)] = e_lds[threadIdx.x];
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -341,7 +343,7 @@ hipError_t launch_score(const int8_t *qsk, const int8_t *S, const int32_t *seq_l
     else if (cand)                                                                             \
       score_kernel<RR, false, true><<<grid, SC_THREADS, 0, st>>>(                              \
           qsk, S, seq_len, nullptr, nullptr, nullptr, n_sub_max, s.Hkv, s.T_max, s.NB, s.window, \
-          s.pool, s.topk, w->hsamp, w->cand, w->cnt, force, w->est);                           \
+          s.pool, s.topk, w->hsamp, w->cand, w->cnt, force, w->counters);                      \
     else if (hist1)                                                                            \
       score_kernel<RR, true, false><<<grid, SC_THREADS, 0, st>>>(                              \
           qsk, S, seq_len, scores, hist1, cmax, n_sub_max, s.Hkv, s.T_max, s.NB, s.window,     \

@@ -223,7 +223,8 @@ constexpr int TF_THREADS = 1024;
 // j in [512x, 512x + 512), and adds their level-1 bins to the segment's
 // sample histogram (`out`, zero at rest; the final pass returns it to zero).
 // With EST one workgroup takes a segment's whole sample and writes the
-// segment's estimate E to out[seg] instead (sample_estimate).
+// segment's estimate E to out[4 seg] instead (sample_estimate; `out` is the
+// counters record of TopkWs then).
 template <bool EST>
 __global__ __launch_bounds__(SAMPLE_THREADS) void topk_sample_kernel(
     const int8_t *__restrict__ qsk, const int8_t *__restrict__ S,
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void topk_sample_kernel(
   __syncthreads();
   if (EST) {
     const int E = sample_estimate(lh, keys, g.n_far, g.k_eff, stride, est);
-    if (threadIdx.x == 0) out[seg] = E;
+    if (threadIdx.x == 0) out[4 * seg] = E;
     return;
   }
   sample_flush(lh, out + (size_t)seg * HIST1_BINS);
@@ -280,8 +281,7 @@ size_t hist_region_bytes(const Shape &s) {
 size_t topk_scratch_bytes(const Shape &s) {
   const size_t nseg = (size_t)s.B * s.R * s.Hkv;
   const size_t n_sub = (size_t)ceil_div(s.NB, TK_SUB);
-  return align_up(nseg * n_sub * 4, 256) + align_up(nseg * n_sub * TK_SUB * sizeof(int2), 256) +
-         align_up(nseg * 4, 256);
+  return align_up(nseg * n_sub * 4, 256) + align_up(nseg * n_sub * TK_SUB * sizeof(int2), 256);
 }
 
 TopkWs topk_ws_carve(const Shape &s, void *ws) {
@@ -304,8 +304,6 @@ TopkWs topk_ws_carve(const Shape &s, void *ws) {
   w.cnt = reinterpret_cast<int32_t *>(p);
   p += align_up(nseg * n_sub * 4, 256);
   w.cand = reinterpret_cast<int2 *>(p);
-  p += align_up(nseg * n_sub * TK_SUB * sizeof(int2), 256);
-  w.est = reinterpret_cast<int32_t *>(p);
   w.nchunk = (int)n_sub;
   w.attn = base + hist_region_bytes(s) + topk_scratch_bytes(s);
   return w;
@@ -384,7 +382,7 @@ hipError_t launch_topk_sample(const int8_t *qsk, const int8_t *S, const int32_t 
   const long max_m = (max_far + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
   if (max_m > 0 && topk_cand_est_early(s))
     topk_sample_kernel<true><<<dim3(1, nseg), SAMPLE_THREADS, 0, st>>>(
-        qsk, S, seq_len, w.est, s.R, s.Hkv, s.T_max, s.NB, s.window, s.pool, s.topk,
+        qsk, S, seq_len, w.counters, s.R, s.Hkv, s.T_max, s.NB, s.window, s.pool, s.topk,
         topk_cand_est_stride(s));
   else if (max_m > 0)
     topk_sample_kernel<false><<<dim3(ceil_div(max_m, SAMPLE_WG_ROWS), nseg), SAMPLE_THREADS, 0, st>>>(
@@ -400,7 +398,6 @@ hipError_t launch_topk_cand(const int8_t *qsk, const int8_t *S, int32_t *scores,
   FinalArgs a = final_args(scores, seq_len, s, idx, n_sel, w);
   a.cand_mode = 1;
   a.hsamp = w.hsamp;
-  a.est = w.est;
   a.zero_hsamp = zero_hsamp ? 1 : 0;
   a.qsk = qsk;
   a.S = S;

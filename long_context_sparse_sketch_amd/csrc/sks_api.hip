@@ -189,7 +189,7 @@ hipError_t enqueue_step(const sks_kv &kv, const sks::Shape &s, const sks_step &s
     if (cand) {
       if (e == hipSuccess)
         e = sks::launch_score(st.qsk, st.S, kv.seq_len, s, nullptr, &w, hs, true, 0,
-                              est ? w.est : nullptr);
+                              est ? w.counters : nullptr);
       // (sample histograms are cleared by the attention's merge launch, off
       // the selection's critical path)
       if (e == hipSuccess)
@@ -394,7 +394,7 @@ int sks_score_candidates(const int8_t *qsk, const int8_t *S, const sks_kv *kv,
     e = sks::launch_topk_sample(qsk, S, kv->seq_len, s, w, hs);
   if (e == hipSuccess)
     e = sks::launch_score(qsk, S, kv->seq_len, s, nullptr, &w, hs, true, force,
-                          sks::topk_cand_est_early(s) ? w.est : nullptr);
+                          sks::topk_cand_est_early(s) ? w.counters : nullptr);
   return hip_status(e, "sks_score_candidates");
 }
 

@@ -351,12 +351,12 @@ struct TopkWs {
   int32_t *hist2;     // [nseg][HIST2_BINS], zero at rest
   int32_t *cmax;      // [nseg][nchunk]: largest biased score of each sub-list + 1 (0: empty)
   int32_t *hsamp;     // [nseg][HIST1_BINS]: candidate mode's sample histogram, zero at rest
-  int32_t *counters;  // [nseg][4]: threshold bin b1, count above it, valid, count in b1
+  int32_t *counters;  // [nseg][4]: threshold bin b1, count above it, valid, count in b1;
+                      // in candidate mode the estimate E, in the first int
   char *scratch;      // start of the selection scratch (cnt, cand)
   char *attn;         // start of the attention partials (after the selection scratch)
   int32_t *cnt;       // [nseg][nchunk]
   int2 *cand;         // [nseg][nchunk * TK_SUB]
-  int32_t *est;       // [nseg]: candidate mode's estimate E, when the step's first launch derives it
   int nchunk;         // sub-lists per segment
 };
 TopkWs topk_ws_carve(const Shape &s, void *ws);
@@ -372,8 +372,8 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
 bool topk_cand_preferred(const Shape &s);
 // Whether one sample workgroup covers each segment's whole sample (at most
 // SAMPLE_WG_ROWS entries at a stride of 64, or else 128), so that the sample
-// pass derives the estimate E itself and the score pass reads it from
-// TopkWs::est; and that stride.
+// pass derives the estimate E itself and the score pass reads it from the
+// segment's TopkWs::counters record; and that stride.
 bool topk_cand_est_early(const Shape &s);
 int topk_cand_est_stride(const Shape &s);
 hipError_t launch_topk_sample(const int8_t *qsk, const int8_t *S, const int32_t *seq_len,

@@ -243,8 +243,6 @@ struct FinalArgs {
   int cand_mode;
   int32_t *hsamp;   // candidate mode: the sample histograms, returned to zero here
   int zero_hsamp;   // ... unless 0: then a later launch of the step clears them
-  const int32_t *est;   // candidate mode: each segment's estimate E (written by the score pass
-                        // or, early estimates, by the sample pass)
   const int8_t *qsk, *S;
   int32_t *rescore;
 };
@@ -333,9 +331,10 @@ __device__ void final_body(const FinalArgs &a, const FinalLead &ld, int seg,
       hv[4 * k + 3] = w.w;
     }
   }
-  // candidate mode: the estimate the candidates were kept with (clamped as
-  // the score pass clamps it), and the candidates' histogram, built in LDS
-  const int e_cand = cmode && a.est ? max(a.est[seg], 0) : 0;
+  // candidate mode: the candidates' histogram, built in LDS, and the
+  // estimate the candidates were kept with, from the segment's record
+  // (clamped as the score pass clamps it)
+  const int e_cand = cmode ? max(th.x, 0) : 0;
   if (cmode)
     for (int k = threadIdx.x; k < hpad_size<HIST1_BINS>(); k += TF_THREADS) h1[k] = 0;
   const SegGeom g = seg_geom(seg, seq_len, R, Hkv, T_max, window, pool, topk);
@@ -767,7 +766,6 @@ inline FinalArgs final_args(const int32_t *scores, const int32_t *seq_len, const
   a.cand_mode = 0;
   a.hsamp = nullptr;
   a.zero_hsamp = 1;
-  a.est = nullptr;
   a.qsk = nullptr;
   a.S = nullptr;
   a.rescore = nullptr;
