@@ -262,12 +262,11 @@ def main():
                           dense=args.dense, keep_scores=args.keep_scores)
                for lay in layers]
     # the step's own rule (sks.h, SKS_STEP_NO_SCORES): candidate mode for rows
-    # of more than 8,192 far entries and at least 2^20 far entries in all,
-    # with one row per sequence or at most 65,536 far entries per row
+    # of more than 8,192 far entries, with at most 65,536 far entries per row,
+    # or one row per sequence and at least 2^20 far entries in all
     max_far = max(0, cfg.T_max - cfg.window) // cfg.pool
-    cand = (not args.keep_scores and not args.dense and not args.five_calls
-            and max_far > 8192 and cfg.B * cfg.R * cfg.Hkv * max_far >= 1 << 20
-            and (cfg.R == 1 or -(-max_far // 64) <= 1024))
+    cand = (not args.keep_scores and not args.dense and not args.five_calls and max_far > 8192
+            and (max_far <= 65536 or (cfg.R == 1 and cfg.B * cfg.Hkv * max_far >= 1 << 20)))
     R_ = len(runners)
     spg = args.steps_per_graph or R_
     if R_ % spg:

@@ -304,9 +304,9 @@ int sks_sparse_decode_attn(const uint16_t *q, int32_t Hq, const sks_kv *kv,
  * the sketch current.  Which mode a step takes is the caller's choice (it
  * knows its lengths); the workspace of the sparse step serves both.
  * With SKS_STEP_NO_SCORES the caller does not read `scores` after the step:
- * where it pays (rows of more than 8,192 far entries, at least 2^20 far
- * entries over all (b, i, h), and either one row per sequence or at most
- * 65,536 far entries per row), the step scores and selects in candidate
+ * where it pays (rows of more than 8,192 far entries, and either at most
+ * 65,536 far entries per row, or one row per sequence and at least 2^20 far
+ * entries over all (b, h)), the step scores and selects in candidate
  * mode (sks_score_candidates + sks_topk_select_candidates), which stores no
  * scores; idx, n_sel, out and lse are the same bit for bit, and `scores` is
  * then scratch with unspecified contents.

@@ -353,16 +353,16 @@ hipError_t launch_topk(const int32_t *scores, const int32_t *seq_len, const Shap
 }
 
 // Candidate mode pays off where the final pass cannot simply take every far
-// entry (more than TF_REGS of them) and the batch streams enough sketch rows
-// (2^20) for the saved score stores to outweigh the sample work.  With verify
-// rows it pays only when the step's first launch derives the estimates (one
-// sample workgroup per segment): a score pass that derives three rows'
-// estimates in every workgroup measured slower than storing the scores.
+// entry (more than TF_REGS of them), and either the sample workgroups derive
+// the estimates themselves (one per segment: rows of at most 65,536 far
+// entries) or single-row steps stream enough sketch rows (2^20) for the
+// saved score stores to outweigh the per-workgroup estimate.  (A verify-row
+// score pass that derives three rows' estimates in every workgroup measured
+// slower than storing the scores.)
 bool topk_cand_preferred(const Shape &s) {
   const long max_far = s.T_max > s.window ? (long)(s.T_max - s.window) / s.pool : 0;
   const long nseg = (long)s.B * s.R * s.Hkv;
-  return max_far > TF_REGS && nseg * max_far >= (1L << 20) &&
-         (s.R == 1 || topk_cand_est_early(s));
+  return max_far > TF_REGS && (topk_cand_est_early(s) || (s.R == 1 && nseg * max_far >= (1L << 20)));
 }
 
 bool topk_cand_est_early(const Shape &s) {

@@ -78,9 +78,9 @@ def test_candidates_with_dirty_workspace(ctx):
 
 def test_step_without_scores_equals_step(ctx):
     """SKS_STEP_NO_SCORES: the same idx, n_sel, out and lse bit for bit
-    (shapes with more than 8,192 far entries per row and 2^20 in all take the
-    candidate mode, verify rows only at 65,536 far entries per row or fewer;
-    the others store the scores as before)."""
+    (rows of more than 8,192 far entries take the candidate mode: at 65,536
+    far entries per row or fewer, or single rows with 2^20 far entries in
+    all; the others store the scores as before)."""
     cfg, case, g, ref, arr = ctx
     lay = g.layer
     lay.step(g.q)
