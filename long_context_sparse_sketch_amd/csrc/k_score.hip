@@ -143,18 +143,38 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
       cm[i][k] = 0ull;
     }
   static_assert(SCORE_CHUNK == 2 * SC_BLOCK_STEP, "two steps per wave and chunk");
-  int it = 0;
-  for (int base = c0 + wave * SC_WAVE_STEP; base < c1; base += SC_BLOCK_STEP, ++it) {
-    int4 sv[SC_UNROLL];
-    // Every load is issued, and all of them before any use: a load under a
-    // branch, or one the scheduler moves next to its use, is waited for
-    // before the next one is issued.  Rows past the chunk's end read its last
-    // row instead; their results are never used (keys, histogram counts and
-    // stored scores all stop at the row's far count).
+  // A step's stream loads: every load is issued, and all of them before any
+  // use (a load under a branch, or one the scheduler moves next to its use,
+  // is waited for before the next one is issued).  Rows past the chunk's end
+  // read its last row instead; their results are never used (keys, histogram
+  // counts and stored scores all stop at the row's far count).
+  auto stream = [&](int base, int4 (&sv)[SC_UNROLL]) {
 #pragma unroll
     for (int u = 0; u < SC_UNROLL; ++u)
       sv[u] = load_stream(&Sbh[(size_t)min(base + u * 16 + quad, c1 - 1) * 4]);
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // Candidate mode derives each row's estimate E (block_estimate: the lowest
+  // key of the sample histogram's bin holding the rho-th largest sampled
+  // key) while the first step's loads are in flight.  Its barriers stay out
+  // of the loop below, whose trip count differs between waves at a row's
+  // last chunk.
+  int4 sv0[SC_UNROLL];
+  if (CAND && !EST) {
+    stream(c0 + wave * SC_WAVE_STEP, sv0);
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      block_estimate<SC_THREADS>(hsv[i], nf[i], ke[i], SAMPLE_STRIDE, force, escan, &e_lds[i]);
+  }
+  int it = 0;
+  for (int base = c0 + wave * SC_WAVE_STEP; base < c1; base += SC_BLOCK_STEP, ++it) {
+    int4 sv[SC_UNROLL];
+    if (CAND && !EST && it == 0) {
+#pragma unroll
+      for (int u = 0; u < SC_UNROLL; ++u) sv[u] = sv0[u];
+    } else {
+      stream(base, sv);
+    }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       int acc[SC_UNROLL];
@@ -211,12 +231,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     }
   }
   if (CAND) {
-    // Each row's estimate E (block_estimate: the lowest key of the sample
-    // histogram's bin holding the rho-th largest sampled key).
     if (!EST) {
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-        block_estimate<SC_THREADS>(hsv[i], nf[i], ke[i], SAMPLE_STRIDE, force, escan, &e_lds[i]);
       // the segment's E for the final pass, in its counters record (every
       // workgroup derived the same)
       if (est_out && blockIdx.x == 0 && threadIdx.x < R)
