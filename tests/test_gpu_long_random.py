@@ -1,7 +1,9 @@
-"""GPU parity of whole decode steps on seeded random long-context shapes:
-far regions of 8K to 320K entries per row and at least 2^20 in all, so that
-steps without stored scores take the selection's candidate mode (single-row
-steps, and verify-row steps of at most 65,536 far entries per row)
+"""GPU parity of whole decode steps on seeded random long-context shapes that
+take the selection's candidate mode when they store no scores: far regions of
+8K to 320K entries per row and at least 2^20 in all (the estimate from the
+sample histograms, single-row steps), and far regions of 8,193 to 65,536
+entries per row with one to three verify rows (the estimate from one sample
+workgroup per segment)
 ("What it took" on the page "8 agents x 250K context, concurrently, on two
 3090s": score every token, pick the top ~2K).  Each case draws the batch, the
 verify rows, the query group, pooling, KV storage, window, top-k (up to
@@ -29,6 +31,7 @@ from tests.test_gpu_candidates import histogram_regions
 pytestmark = pytest.mark.gpu
 
 SEEDS = list(range(40))
+EST_SEEDS = list(range(24))
 
 
 def draw(seed):
@@ -64,10 +67,44 @@ def draw(seed):
     return cfg, lengths
 
 
+def draw_early(seed):
+    rng = np.random.default_rng(77000 + seed)
+    R = int(rng.choice([1, 1, 2, 3, 3]))
+    Hkv = int(rng.integers(1, 9))
+    G = int(rng.integers(1, 9))
+    pool = int(rng.choice([1, 1, 1, 2, 4]))
+    kv = C.KV_BF16 if pool > 1 else int(rng.choice([C.KV_BF16, C.KV_I8, C.KV_I4]))
+    window = int(rng.choice([0, 17, 4096, int(rng.integers(0, 6000))]))
+    topk = int(rng.choice([1, 3, 2048, int(rng.integers(1, 8000))]))
+    B = int(rng.integers(1, 7))
+    far = int(rng.integers(8193, 65537))        # far entries of a full-length row
+    L = window + pool * far + R
+    kind = str(rng.choice(["random", "clusters"]))
+    cfg = C.Config(f"early{seed}", 500 + seed, B=B, R=R, Hq=Hkv * G, Hkv=Hkv, L=L, window=window,
+                   topk=topk, pool=pool, kv_dtype=kv, needle_kind=kind,
+                   needle_count=(L // 100 if kind == "clusters" else 64), needle_amp=2.5,
+                   needle_noise=0.5)
+    lengths = rng.integers(0, L + 1, B).astype(np.int32)
+    lengths[0] = L
+    if B > 1 and rng.random() < 0.4:
+        lengths[1] = int(rng.integers(0, window + topk + 2))
+    if B > 2 and rng.random() < 0.4:
+        lengths[2] = 0
+    return cfg, lengths
+
+
 @pytest.mark.parametrize("seed", SEEDS)
 def test_long_random_step(seed):
-    cfg, sl = draw(seed)
-    flush(f"[long random] seed {seed}: B={cfg.B} R={cfg.R} Hq/Hkv={cfg.Hq}/{cfg.Hkv} "
+    check_step(seed, *draw(seed))
+
+
+@pytest.mark.parametrize("seed", EST_SEEDS)
+def test_early_estimate_random_step(seed):
+    check_step(seed, *draw_early(seed))
+
+
+def check_step(seed, cfg, sl):
+    flush(f"[long random] {cfg.name}: B={cfg.B} R={cfg.R} Hq/Hkv={cfg.Hq}/{cfg.Hkv} "
           f"L={sl.tolist()} W={cfg.window} k={cfg.topk} r={cfg.pool} "
           f"kv={C.KV_NAMES[cfg.kv_dtype]} needles={cfg.needle_kind}")
     case = make_case(cfg)
