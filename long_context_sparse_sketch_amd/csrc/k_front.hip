@@ -81,17 +81,23 @@ __global__ __launch_bounds__(SK_THREADS) void front_kernel(const uint16_t *q, co
     const int seg = blk / samp_per_seg;
     const int h = seg % Hkv, b = seg / (Hkv * R);
     const int j0 = (blk % samp_per_seg) * SAMPLE_WG_ROWS;   // EST: one workgroup per segment, 0
-    // Every load is issued at once, before the row's length is known: the
-    // sampled rows j * stride < NB lie in the cache whatever the length, and
-    // those past the far region are not counted.
+    // Every load is issued before the row's length is known: the sampled
+    // rows j * stride < NB lie in the cache whatever the length, and those
+    // past the far region are not counted.
     const int stride = f.samp_stride;
+    // The query sketch's own loads go first (its chain is the longer one);
+    // the sampled rows load behind them.
     int4 sv[SAMPLE_UNROLL];
-    sample_load(S, ((size_t)b * Hkv + h) * f.NB, j0, (f.NB + stride - 1) / stride, stride, sv);
-    for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS) lds.samp.lh[k] = 0;
-    if (EST)
-      for (int k = threadIdx.x; k < HIST2_BINS; k += SAMPLE_THREADS) lds.samp.est.h2[k] = 0;
     block_query_sketch(q, R, Hq, Hkv, basis, basis_per_head, seg, lds.samp.qcode, nullptr,
-                       lds.samp.sk);
+                       lds.samp.sk, [&] {
+                         sample_load(S, ((size_t)b * Hkv + h) * f.NB, j0,
+                                     (f.NB + stride - 1) / stride, stride, sv);
+                         for (int k = threadIdx.x; k < HIST1_BINS; k += SAMPLE_THREADS)
+                           lds.samp.lh[k] = 0;
+                         if (EST)
+                           for (int k = threadIdx.x; k < HIST2_BINS; k += SAMPLE_THREADS)
+                             lds.samp.est.h2[k] = 0;
+                       });
     const SegGeom g = seg_geom(seg, seq_len, R, Hkv, f.T_max, f.window, f.pool, f.topk);
     if (g.k_eff >= g.n_far) return;             // uniform: no selection needed
     const int m = (g.n_far + stride - 1) / stride;

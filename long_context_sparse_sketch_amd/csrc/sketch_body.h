@@ -88,24 +88,38 @@ __device__ __forceinline__ float dot_basis_part(const float4 (&pr)[8], const flo
 // order), y = P_h qbar, qscale = max|y| / 127, codes = clamp(rne(y / qscale))
 // (all zero, scale 0, when y == 0).  Writes the 64 codes to `codes` (global
 // memory or LDS) and the scale to *qscale when qscale is not NULL.  Contains
-// two __syncthreads().
+// two __syncthreads().  `between` runs (in every thread) once the basis and
+// the first eight query heads are loading and before they are used: loads it
+// issues complete behind them.
+template <typename F>
 __device__ void block_query_sketch(const uint16_t *__restrict__ q, int R, int Hq, int Hkv,
                                    const float *__restrict__ basis, int basis_per_head, int seg,
-                                   int8_t *codes, float *qscale, SketchLds &L) {
+                                   int8_t *codes, float *qscale, SketchLds &L, F &&between) {
   const int h = seg % Hkv, bi = seg / Hkv;
   const int g = Hq / Hkv;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   float4 pr[8];
   load_basis_part(basis + (basis_per_head ? (size_t)h * RANK * D : 0), pr);
-  if (t < D / 2) {
-    // dims 2t, 2t + 1 of the group's queries, up to 8 loads in flight, summed in head order
-    const uint16_t *qg = q + ((size_t)bi * Hq + (size_t)h * g) * D;
+  // dims 2t, 2t + 1 of the group's queries (threads t < 64), eight heads in
+  // flight, loaded unconditionally (past the group: its last head again, not
+  // summed)
+  const uint16_t *qg = q + ((size_t)bi * Hq + (size_t)h * g) * D;
+  const bool qt = t < D / 2;
+  uint32_t w[8];
+  if (qt) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      w[u] = *reinterpret_cast<const uint32_t *>(qg + (size_t)min(u, g - 1) * D + 2 * t);
+  }
+  between();
+  if (qt) {
     float s0 = 0.f, s1 = 0.f;
     for (int j0 = 0; j0 < g; j0 += 8) {
-      uint32_t w[8];
+      if (j0 > 0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        w[u] = j0 + u < g ? *reinterpret_cast<const uint32_t *>(qg + (size_t)(j0 + u) * D + 2 * t) : 0u;
+        for (int u = 0; u < 8; ++u)
+          w[u] = *reinterpret_cast<const uint32_t *>(qg + (size_t)min(j0 + u, g - 1) * D + 2 * t);
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (j0 + u < g) {
@@ -127,6 +141,12 @@ __device__ void block_query_sketch(const uint16_t *__restrict__ q, int R, int Hq
   const float scale = amax / 127.0f;
   if ((t & 3) == 0) codes[t >> 2] = amax > 0.f ? quant_code(y, scale) : (int8_t)0;
   if (t == 0 && qscale) *qscale = amax > 0.f ? scale : 0.f;
+}
+__device__ __forceinline__ void block_query_sketch(const uint16_t *__restrict__ q, int R, int Hq,
+                                                   int Hkv, const float *__restrict__ basis,
+                                                   int basis_per_head, int seg, int8_t *codes,
+                                                   float *qscale, SketchLds &L) {
+  block_query_sketch(q, R, Hq, Hkv, basis, basis_per_head, seg, codes, qscale, L, [] {});
 }
 
 // Key sketch of sketch row j_lo + jx of (b, h) = (bh / Hkv, bh % Hkv), by the

@@ -151,16 +151,22 @@ constexpr int SAMPLE_THREADS = 256;
 constexpr int SAMPLE_UNROLL = 8;
 constexpr int SAMPLE_WG_ROWS = SAMPLE_THREADS / 4 * SAMPLE_UNROLL;   // 512 sampled rows
 
-// Loads of this thread's sampled rows (issued before anything uses them).
+// Loads of this thread's sampled rows j * stride, j < m (issued before
+// anything uses them); m, the cache's sampled rows, is at least 1 (a cache
+// holds at least one sketch row).  The loads are unconditional, rows past m
+// reading row (m - 1) * stride instead (sample_bins masks them): a load under
+// a per-lane condition, or one of two definitions of sv, becomes a branch at
+// whose join the compiler waits for the loads before it.
 __device__ __forceinline__ void sample_load(const int8_t *__restrict__ S, size_t seg_row0, int j0,
                                             int m, int stride, int4 (&sv)[SAMPLE_UNROLL]) {
   const int part = threadIdx.x & 3, quad = threadIdx.x >> 2;
   constexpr int QUADS = SAMPLE_THREADS / 4;
   const int4 *Sseg = reinterpret_cast<const int4 *>(S + seg_row0 * RANK) + part;
+  const int last = max(m - 1, 0);
 #pragma unroll
   for (int u = 0; u < SAMPLE_UNROLL; ++u) {
-    const int j = j0 + u * QUADS + quad;
-    sv[u] = j < m ? Sseg[(size_t)j * stride * 4] : make_int4(0, 0, 0, 0);
+    const int j = min(j0 + u * QUADS + quad, last);
+    sv[u] = Sseg[(size_t)j * stride * 4];
   }
 }
 
